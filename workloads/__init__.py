@@ -1,0 +1,251 @@
+"""Seeded synthetic workloads for one Medusa verify step.
+
+This module only draws random tensors of the right shapes and distributions.
+It holds none of the method's arithmetic: no heads, no tree, no attention, no
+acceptance rule. Both the CPU oracle (``oracle/``) and the HIP path take their
+inputs from here, so that the two sides see identical bytes.
+
+The shapes follow the pages' workloads: batch 1, prefix KV up to 4096, five
+Medusa heads, trees of a few dozen nodes, temperature 0.7 for typical
+acceptance ("Medusa: Faster LLM text generation", Results; "Medusa 深读", §7.1
+Table 1 and §7.2). The pages measure on MT-Bench with Vicuna weights and
+trained heads; none of that exists here, so seeded Gaussian tensors of the same
+shapes stand in for them.
+
+Conventions
+-----------
+* bf16 tensors are numpy ``uint16`` arrays holding bf16 bit patterns
+  (fp32 draws rounded to nearest-even). fp32 workloads keep ``float32``.
+* Every tensor has its own generator ``np.random.default_rng([seed, tid])``
+  with a fixed tensor id, so adding a tensor never shifts another one.
+* Weights are stored row-major ``[out][in]`` (``W1[k]`` is d x d, ``W2[k]``
+  is V x d, ``W_qkv`` is 3d x d with the q, k, v blocks stacked, ``W_lm`` is
+  V x d, the embedding ``E`` is V x d).
+* The KV cache is ``[B][H][Lmax][Dh]``; rows at or past a sequence's prefix
+  length are zero.
+"""
+
+from __future__ import annotations
+
+import dataclasses
+from typing import Dict, Optional, Tuple
+
+import numpy as np
+
+# Tensor ids: one independent stream per tensor.
+TID = dict(h=0, W1=1, b1=2, W2=3, E=4, W_qkv=5, W_o=6, W_lm=7, K=8, V=9,
+           kv_len=10, root=11, u_draft=12, u_accept=13, u_resample=14)
+
+
+@dataclasses.dataclass(frozen=True)
+class Workload:
+    """Shape, tree, acceptance rule and value distributions of one workload."""
+
+    name: str
+    dtype: str                 # "f32" or "bf16": storage type of weights, E, KV
+    B: int                     # sequences
+    d: int                     # hidden width
+    V: int                     # vocabulary
+    K: int                     # Medusa heads = tree depth
+    s: Tuple[int, ...]         # per-depth top-s of the Cartesian tree
+    H: int                     # attention heads of the verifier layer
+    Dh: int                    # head dimension
+    L: Optional[int]           # prefix length (None: ragged, drawn per sequence)
+    L_range: Tuple[int, int]   # inclusive range for ragged prefix lengths
+    mode: str                  # "greedy", "typical" or "exact"
+    tau: float                 # verifier temperature
+    eps: float                 # typical acceptance hard threshold
+    delta: float               # typical acceptance entropy factor
+    w1_std: Optional[float]    # std of W1 entries (None: 1/sqrt(d))
+    entropy_target: Optional[float]  # scale W_lm so LM logits on h have this entropy (nats)
+    seed: int
+    rope_theta: float = 10000.0
+
+    @property
+    def s_max(self) -> int:
+        return max(self.s)
+
+
+WORKLOADS: Dict[str, Workload] = {
+    # Tiny fp32 case the oracle finishes in well under a second.
+    "tiny_fp32": Workload(
+        name="tiny_fp32", dtype="f32", B=1, d=256, V=1000, K=3, s=(2, 2, 2),
+        H=4, Dh=64, L=64, L_range=(64, 64), mode="greedy", tau=1.0,
+        eps=0.09, delta=0.3, w1_std=0.02, entropy_target=2.0, seed=1001),
+    # Vicuna-7B-shaped step, typical acceptance: the throughput workload.
+    "vicuna7b_typical": Workload(
+        name="vicuna7b_typical", dtype="bf16", B=1, d=4096, V=32000, K=5,
+        s=(3, 2, 2, 1, 1), H=32, Dh=128, L=2048, L_range=(2048, 2048),
+        mode="typical", tau=0.7, eps=0.09, delta=0.3, w1_std=None,
+        entropy_target=None, seed=1002),
+    # Vicuna-13B-shaped step, wider 136-node tree, 4k prefix.
+    "vicuna13b_typical": Workload(
+        name="vicuna13b_typical", dtype="bf16", B=1, d=5120, V=32000, K=5,
+        s=(4, 3, 2, 2, 1), H=40, Dh=128, L=4096, L_range=(4096, 4096),
+        mode="typical", tau=0.7, eps=0.09, delta=0.3, w1_std=0.02,
+        entropy_target=2.0, seed=1003),
+    # Eight independent 7B-shaped sequences with ragged prefixes, greedy.
+    "vicuna7b_batch8_ragged": Workload(
+        name="vicuna7b_batch8_ragged", dtype="bf16", B=8, d=4096, V=32000, K=5,
+        s=(3, 2, 2, 1, 1), H=32, Dh=128, L=None, L_range=(512, 4096),
+        mode="greedy", tau=1.0, eps=0.09, delta=0.3, w1_std=None,
+        entropy_target=None, seed=1004),
+    # 7B shapes with exact p/q rejection sampling, 4k prefix.
+    "vicuna7b_exact": Workload(
+        name="vicuna7b_exact", dtype="bf16", B=1, d=4096, V=32000, K=5,
+        s=(3, 2, 2, 1, 1), H=32, Dh=128, L=4096, L_range=(4096, 4096),
+        mode="exact", tau=1.0, eps=0.09, delta=0.3, w1_std=None,
+        entropy_target=None, seed=1005),
+}
+
+
+def scaled(w: Workload, **overrides) -> Workload:
+    """A copy of ``w`` with some fields replaced (for small parity shapes)."""
+    return dataclasses.replace(w, **overrides)
+
+
+# --------------------------------------------------------------------------
+# bf16 storage helpers (data preparation only)
+# --------------------------------------------------------------------------
+
+def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """Round float32 to bf16 (nearest, ties to even); return uint16 bit patterns."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    b = x.view(np.uint32).astype(np.uint64)
+    b = (b + 0x7FFF + ((b >> 16) & 1)) >> 16
+    return b.astype(np.uint16)
+
+
+def bf16_bits_to_f32(u: np.ndarray) -> np.ndarray:
+    """Exact widening of bf16 bit patterns to float32."""
+    u = np.ascontiguousarray(u, dtype=np.uint16)
+    return (u.astype(np.uint32) << 16).view(np.float32)
+
+
+def _rng(w: Workload, name: str) -> np.random.Generator:
+    return np.random.default_rng([w.seed, TID[name]])
+
+
+def _normal(rng: np.random.Generator, shape, std: float, store: str,
+            chunk_rows: int = 4096) -> np.ndarray:
+    """N(0, std^2) draws, produced in row chunks to bound peak memory."""
+    shape = tuple(int(x) for x in shape)
+    rows = int(np.prod(shape[:-1])) if len(shape) > 1 else 1
+    cols = shape[-1]
+    out = np.empty((rows, cols), dtype=np.uint16 if store == "bf16" else np.float32)
+    for r0 in range(0, rows, chunk_rows):
+        r1 = min(rows, r0 + chunk_rows)
+        x = rng.standard_normal((r1 - r0, cols), dtype=np.float32)
+        if std != 1.0:
+            x *= np.float32(std)
+        out[r0:r1] = f32_to_bf16_bits(x) if store == "bf16" else x
+    return out.reshape(shape)
+
+
+def _entropy_nats(logits: np.ndarray) -> float:
+    # Plain entropy of a softmax, used only to size the LM-head scale of the
+    # synthetic input (the input distribution, not a step of the method).
+    z = logits - logits.max()
+    e = np.exp(z)
+    p = e / e.sum()
+    nz = p > 0
+    return float(-(p[nz] * np.log(p[nz])).sum())
+
+
+def _lm_scale_for_entropy(W_lm_f32: np.ndarray, h: np.ndarray, target: float) -> float:
+    """Bisect alpha so that softmax(alpha * W_lm h) has entropy ``target`` nats."""
+    base = W_lm_f32.astype(np.float64) @ h.astype(np.float64)
+    lo, hi = 1e-3, 1e3
+    for _ in range(200):
+        mid = np.sqrt(lo * hi)
+        if _entropy_nats(mid * base) > target:
+            lo = mid   # entropy too high: logits need more spread
+        else:
+            hi = mid
+        if hi / lo < 1 + 1e-9:
+            break
+    return float(np.sqrt(lo * hi))
+
+
+def cartesian_ranks(s) -> np.ndarray:
+    """Rank tuples (0-based, -1 padded) of the Cartesian top-s tree, one row per
+    non-root node, depth-major then lexicographic. This lists the tree the
+    pages describe ("Medusa 深读", §6.1): every combination of per-head ranks,
+    with shared prefixes stored once."""
+    K = len(s)
+    rows = []
+    frontier = [()]
+    for k in range(K):
+        nxt = []
+        for t in frontier:
+            for r in range(s[k]):
+                nxt.append(t + (r,))
+        rows.extend(nxt)
+        frontier = nxt
+    out = np.full((len(rows), K), -1, dtype=np.int32)
+    for i, t in enumerate(rows):
+        out[i, :len(t)] = t
+    return out
+
+
+def lmax_for(w: Workload) -> int:
+    """KV capacity: room for the longest prefix plus a full commit (K+1 rows),
+    rounded up to a multiple of 64."""
+    Lmax = w.L_range[1] + w.K + 1
+    return (Lmax + 63) // 64 * 64
+
+
+def make_inputs(w: Workload, with_weights: bool = True) -> Dict[str, np.ndarray]:
+    """Draw every input of one verify step for workload ``w``.
+
+    Returns a dict of numpy arrays (see the module docstring for layouts):
+    h [B,d] f32; W1 [K,d,d]; W2 [K,V,d]; E [V,d]; W_qkv [3d,d]; W_o [d,d];
+    W_lm [V,d]; k_cache, v_cache [B,H,Lmax,Dh]; kv_len [B] int32;
+    root [B] int32; ranks [N,K] int32; u_draft, u_accept, u_resample [B,T] f32.
+    """
+    store = w.dtype
+    d, V, K, B, H, Dh = w.d, w.V, w.K, w.B, w.H, w.Dh
+    ranks = cartesian_ranks(w.s)
+    N = ranks.shape[0]
+    T = N + 1
+    Lmax = lmax_for(w)
+    out: Dict[str, np.ndarray] = {"ranks": ranks}
+
+    out["h"] = _rng(w, "h").standard_normal((B, d), dtype=np.float32)
+
+    if w.L is not None:
+        kv_len = np.full(B, w.L, dtype=np.int32)
+    else:
+        kv_len = _rng(w, "kv_len").integers(w.L_range[0], w.L_range[1],
+                                            endpoint=True, size=B).astype(np.int32)
+    out["kv_len"] = kv_len
+    out["root"] = _rng(w, "root").integers(0, V, size=B).astype(np.int32)
+
+    if with_weights:
+        inv = 1.0 / np.sqrt(d)
+        w1_std = w.w1_std if w.w1_std is not None else inv
+        out["W1"] = _normal(_rng(w, "W1"), (K, d, d), w1_std, store)
+        out["W2"] = _normal(_rng(w, "W2"), (K, V, d), inv, store)
+        out["E"] = _normal(_rng(w, "E"), (V, d), 1.0, store)
+        out["W_qkv"] = _normal(_rng(w, "W_qkv"), (3 * d, d), inv, store)
+        out["W_o"] = _normal(_rng(w, "W_o"), (d, d), inv, store)
+        if w.entropy_target is None:
+            out["W_lm"] = _normal(_rng(w, "W_lm"), (V, d), inv, store)
+        else:
+            raw = _rng(w, "W_lm").standard_normal((V, d), dtype=np.float32)
+            raw *= np.float32(inv)
+            alpha = _lm_scale_for_entropy(raw, out["h"][0], w.entropy_target)
+            raw *= np.float32(alpha)
+            out["W_lm"] = f32_to_bf16_bits(raw) if store == "bf16" else raw
+        for name in ("K", "V"):
+            rng = _rng(w, name)
+            cache = np.zeros((B, H, Lmax, Dh),
+                             dtype=np.uint16 if store == "bf16" else np.float32)
+            for b in range(B):
+                L = int(kv_len[b])
+                cache[b, :, :L, :] = _normal(rng, (H, L, Dh), 1.0, store)
+            out["k_cache" if name == "K" else "v_cache"] = cache
+
+    for name in ("u_draft", "u_accept", "u_resample"):
+        out[name] = _rng(w, name).random((B, T), dtype=np.float32)
+    return out
