@@ -1,0 +1,11 @@
+"""MI355X-native Medusa verify step: Python binding of the gfx950 HIP library.
+
+The library (``libmedusa_mi355x.so``, built from ``csrc/``) does all the
+work; this package marshals arguments (``_lib``) and allocates the device
+buffers of one step (``step``). Importing it without the built library raises.
+"""
+
+from ._lib import (  # noqa: F401
+    BF16, DRAFT_SAMPLE, DRAFT_TOPK, EXACT, F32, GREEDY, LIB_PATH, MODES, TYPICAL, MedusaError,
+    Shape, build_tree, commit, evaluate_posterior, exported_symbols, heads_forward, last_error,
+    make_shape, tree_attention, verify_forward, version, workspace_bytes)

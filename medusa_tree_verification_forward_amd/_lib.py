@@ -1,0 +1,193 @@
+"""ctypes binding of ``libmedusa_mi355x.so`` (argument marshalling only).
+
+Every function here converts its arguments (torch tensors on the GPU,
+numpy arrays for host inputs) into the C ABI's plain pointers and sizes,
+calls the library, and raises ``MedusaError`` on a nonzero return. No step
+of the method runs in Python. The library must have been built (see
+``build.py``); importing the package without it raises immediately.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmedusa_mi355x.so")
+
+OK = 0
+ERR_ARG = -1
+ERR_UNSUPPORTED = -2
+ERR_WORKSPACE = -3
+ERR_CAPACITY = -4
+ERR_HIP = -5
+
+BF16 = 0
+F32 = 1
+GREEDY = 0
+TYPICAL = 1
+EXACT = 2
+DRAFT_TOPK = 0
+DRAFT_SAMPLE = 1
+MODES = {"greedy": GREEDY, "typical": TYPICAL, "exact": EXACT}
+
+
+class MedusaError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"medusa error {code}: {msg}")
+        self.code = code
+
+
+class Shape(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in
+                ("B", "d", "V", "K", "H", "Dh", "Lmax", "N", "P", "s_max", "dtype")]
+
+    def as_dict(self):
+        return {n: getattr(self, n) for n, _ in self._fields_}
+
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(
+        f"{LIB_PATH} is missing: build it with `python -m medusa_tree_verification_forward_amd.build` "
+        "or `__graft_entry__.build()`. There is no fallback path.")
+
+_lib = ctypes.CDLL(LIB_PATH)
+
+_P = ctypes.c_void_p
+_I = ctypes.c_int
+_F = ctypes.c_float
+_SZ = ctypes.c_size_t
+_SP = ctypes.POINTER(Shape)
+
+_SIGS = {
+    "medusa_last_error": ([], ctypes.c_char_p),
+    "medusa_version": ([], ctypes.c_char_p),
+    "medusa_workspace_bytes": ([_SP], _SZ),
+    "medusa_heads_forward": ([_SP, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P], _I),
+    "medusa_build_tree": ([_SP, _P, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P], _I),
+    "medusa_tree_attention": ([_SP, _P, _P, _P, _P, _P, _P, _P, _F, _P, _P, _SZ, _P], _I),
+    "medusa_verify_forward": ([_SP, _P, _P, _P, _P, _F, _P, _P, _P, _P, _P, _P, _P, _F,
+                               _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P], _I),
+    "medusa_evaluate_posterior": ([_SP, _I, _F, _F, _F, _P, _P, _P, _P, _P, _P, _P, _P, _P,
+                                   _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P], _I),
+    "medusa_commit": ([_SP, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P], _I),
+}
+for _name, (_args, _res) in _SIGS.items():
+    _fn = getattr(_lib, _name, None)
+    if _fn is not None:
+        _fn.argtypes = _args
+        _fn.restype = _res
+
+
+def exported_symbols():
+    """Names of the C ABI functions the loaded library exports."""
+    return [n for n in _SIGS if getattr(_lib, n, None) is not None]
+
+
+def last_error() -> str:
+    return _lib.medusa_last_error().decode()
+
+
+def version() -> str:
+    return _lib.medusa_version().decode()
+
+
+def _check(rc: int):
+    if rc != OK:
+        raise MedusaError(rc, last_error())
+
+
+def _ptr(t) -> Optional[int]:
+    """Device pointer of a torch tensor (None -> NULL)."""
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def make_shape(B, d, V, K, H, Dh, Lmax, N, P, s_max, dtype) -> Shape:
+    return Shape(B, d, V, K, H, Dh, Lmax, N, P, s_max,
+                 dtype if isinstance(dtype, int) else (F32 if dtype == "f32" else BF16))
+
+
+def workspace_bytes(shape: Shape) -> int:
+    n = _lib.medusa_workspace_bytes(ctypes.byref(shape))
+    if n == 0:
+        raise MedusaError(ERR_ARG, last_error())
+    return int(n)
+
+
+def heads_forward(shape, h, W1, W2, topk_ids, topk_logits, workspace, *, b1=None,
+                  head_lse=None, head_logits=None, z=None, stream=None):
+    _check(_lib.medusa_heads_forward(
+        ctypes.byref(shape), _ptr(h), _ptr(W1), _ptr(b1), _ptr(W2), _ptr(topk_ids),
+        _ptr(topk_logits), _ptr(head_lse), _ptr(head_logits), _ptr(z), _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _stream(stream)))
+
+
+def build_tree(shape, tree_ranks: np.ndarray, root_tok, kv_len, tree_tokens, tree_mask,
+               position_ids, retrieve, parent, depth, *, draft_mode=DRAFT_TOPK, topk_ids=None,
+               head_logits=None, head_lse=None, u_draft=None, stream=None):
+    ranks = np.ascontiguousarray(tree_ranks, dtype=np.int32)
+    rp = ranks.ctypes.data if ranks.size else None
+    _check(_lib.medusa_build_tree(
+        ctypes.byref(shape), rp, int(draft_mode), _ptr(root_tok), _ptr(topk_ids),
+        _ptr(head_logits), _ptr(head_lse), _ptr(u_draft), _ptr(kv_len), _ptr(tree_tokens),
+        _ptr(tree_mask), _ptr(position_ids), _ptr(retrieve), _ptr(parent), _ptr(depth),
+        _stream(stream)))
+
+
+def tree_attention(shape, q, k_tree, v_tree, k_cache, v_cache, kv_len, tree_mask, scale, out,
+                   workspace, *, stream=None):
+    _check(_lib.medusa_tree_attention(
+        ctypes.byref(shape), _ptr(q), _ptr(k_tree), _ptr(v_tree), _ptr(k_cache), _ptr(v_cache),
+        _ptr(kv_len), _ptr(tree_mask), float(scale), _ptr(out), _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _stream(stream)))
+
+
+def verify_forward(shape, E, W_qkv, W_o, W_lm, rope_theta, tree_tokens, position_ids,
+                   tree_mask, parent, k_cache, v_cache, kv_len, temperature, k_tree_out,
+                   v_tree_out, y_out, row_stats, row_argmax, child_logit, workspace, *,
+                   verify_logits=None, stream=None):
+    _check(_lib.medusa_verify_forward(
+        ctypes.byref(shape), _ptr(E), _ptr(W_qkv), _ptr(W_o), _ptr(W_lm), float(rope_theta),
+        _ptr(tree_tokens), _ptr(position_ids), _ptr(tree_mask), _ptr(parent), _ptr(k_cache),
+        _ptr(v_cache), _ptr(kv_len), float(temperature), _ptr(k_tree_out), _ptr(v_tree_out),
+        _ptr(y_out), _ptr(row_stats), _ptr(row_argmax), _ptr(child_logit),
+        _ptr(verify_logits), _ptr(workspace), workspace.numel() * workspace.element_size(),
+        _stream(stream)))
+
+
+def evaluate_posterior(shape, mode, temperature, eps, delta, row_stats, row_argmax,
+                       child_logit, tree_tokens, parent, retrieve, accept_len, best_path,
+                       last_node, out_tokens, next_root, workspace, *, verify_logits=None,
+                       head_logits=None, head_lse=None, u_accept=None, u_resample=None,
+                       stream=None):
+    m = MODES[mode] if isinstance(mode, str) else int(mode)
+    _check(_lib.medusa_evaluate_posterior(
+        ctypes.byref(shape), m, float(temperature), float(eps), float(delta), _ptr(row_stats),
+        _ptr(row_argmax), _ptr(child_logit), _ptr(verify_logits), _ptr(tree_tokens),
+        _ptr(parent), _ptr(retrieve), _ptr(head_logits), _ptr(head_lse), _ptr(u_accept),
+        _ptr(u_resample), _ptr(accept_len), _ptr(best_path), _ptr(last_node),
+        _ptr(out_tokens), _ptr(next_root), _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _stream(stream)))
+
+
+def commit(shape, last_node, parent, k_tree, v_tree, y, k_cache, v_cache, kv_len, h_next, *,
+           stream=None):
+    _check(_lib.medusa_commit(
+        ctypes.byref(shape), _ptr(last_node), _ptr(parent), _ptr(k_tree), _ptr(v_tree), _ptr(y),
+        _ptr(k_cache), _ptr(v_cache), _ptr(kv_len), _ptr(h_next), _stream(stream)))

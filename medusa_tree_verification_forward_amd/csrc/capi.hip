@@ -1,0 +1,307 @@
+// C ABI of the Medusa verify-step library: host-side validation, workspace
+// layout and dispatch to the gfx950 kernels. See include/medusa.h for the
+// contract of every entry point.
+#include "medusa.h"
+
+#include <stdarg.h>
+#include <stdio.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include <algorithm>
+#include <string>
+#include <vector>
+
+#include "kernels.h"
+
+using namespace medusa;
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return code;
+}
+
+int ok() {
+  g_err.clear();
+  return MEDUSA_OK;
+}
+
+int hip_fail(hipError_t e, const char* what) {
+  return fail(MEDUSA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+#define REQUIRE_PTR(p)                                                         \
+  do {                                                                         \
+    if (!(p)) return fail(MEDUSA_ERR_ARG, "%s: null pointer", #p);             \
+    if (!aligned16(p)) return fail(MEDUSA_ERR_ARG, "%s: not 16-byte aligned", #p); \
+  } while (0)
+#define OPTIONAL_PTR(p)                                                        \
+  do {                                                                         \
+    if ((p) && !aligned16(p)) return fail(MEDUSA_ERR_ARG, "%s: not 16-byte aligned", #p); \
+  } while (0)
+
+int env_int(const char* name, int dflt, int lo, int hi) {
+  const char* s = getenv(name);
+  if (!s || !*s) return dflt;
+  int v = atoi(s);
+  return std::min(hi, std::max(lo, v));
+}
+
+// Tuning knobs (rows per workgroup of the head streams). Workspace sizes are
+// computed for the smallest allowed value, so any setting fits.
+constexpr int kMinW2Rows = 16;
+int w1_rows() { static int v = env_int("MEDUSA_W1_ROWS", 64, 4, 4096); return v; }
+int w2_rows() { static int v = env_int("MEDUSA_W2_ROWS", 128, kMinW2Rows, 65536); return v; }
+
+int check_shape(const medusa_shape* s) {
+  if (!s) return fail(MEDUSA_ERR_ARG, "shape: null pointer");
+  if (s->dtype != MEDUSA_BF16 && s->dtype != MEDUSA_F32)
+    return fail(MEDUSA_ERR_ARG, "dtype %d is neither MEDUSA_BF16 nor MEDUSA_F32", s->dtype);
+  if (s->B < 1 || s->d < 1 || s->V < 1 || s->K < 1 || s->H < 1 || s->Dh < 1 || s->Lmax < 1 ||
+      s->N < 0 || s->P < 1 || s->s_max < 1)
+    return fail(MEDUSA_ERR_ARG, "shape has a non-positive size");
+  if (s->H * s->Dh != s->d) return fail(MEDUSA_ERR_ARG, "H*Dh (%d) != d (%d)", s->H * s->Dh, s->d);
+  if (s->V < s->s_max) return fail(MEDUSA_ERR_ARG, "V (%d) < s_max (%d)", s->V, s->s_max);
+  if (s->B > MEDUSA_MAX_B) return fail(MEDUSA_ERR_UNSUPPORTED, "B=%d > %d", s->B, MEDUSA_MAX_B);
+  if (s->K > MEDUSA_MAX_K) return fail(MEDUSA_ERR_UNSUPPORTED, "K=%d > %d", s->K, MEDUSA_MAX_K);
+  if (s->s_max > MEDUSA_MAX_S)
+    return fail(MEDUSA_ERR_UNSUPPORTED, "s_max=%d > %d", s->s_max, MEDUSA_MAX_S);
+  if (s->N + 1 > MEDUSA_MAX_T)
+    return fail(MEDUSA_ERR_UNSUPPORTED, "T=%d > %d", s->N + 1, MEDUSA_MAX_T);
+  if (s->P > s->N + 1) return fail(MEDUSA_ERR_ARG, "P=%d > T=%d", s->P, s->N + 1);
+  if (s->d % 64 != 0) return fail(MEDUSA_ERR_UNSUPPORTED, "d=%d is not a multiple of 64", s->d);
+  if (s->Dh != 64 && s->Dh != 128)
+    return fail(MEDUSA_ERR_UNSUPPORTED, "Dh=%d is not 64 or 128", s->Dh);
+  return MEDUSA_OK;
+}
+
+// ---- workspace layout ----------------------------------------------------------
+constexpr size_t kCounterBytes = 64 * 1024;   // reserved at offset 0 for counters
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+struct Layout {
+  size_t counters = 0;
+  // heads
+  size_t z = 0, part_val = 0, part_id = 0, part_m = 0, part_s = 0;
+  int G = 0;
+  size_t total = 0;
+};
+
+Layout layout_for(const medusa_shape* s) {
+  Layout L;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    size_t o = off;
+    off = align256(off + bytes);
+    return o;
+  };
+  L.counters = take(kCounterBytes);
+  const size_t B = s->B, K = s->K, d = s->d, S = s->s_max;
+  const int Gmax = (s->V + kMinW2Rows - 1) / kMinW2Rows;
+  L.G = (s->V + w2_rows() - 1) / w2_rows();
+  L.z = take(B * K * d * 4);
+  L.part_val = take(B * K * Gmax * S * 4);
+  L.part_id = take(B * K * Gmax * S * 4);
+  L.part_m = take(B * K * Gmax * 4);
+  L.part_s = take(B * K * Gmax * 4);
+  L.total = off;
+  return L;
+}
+
+template <class T>
+T* at(void* ws, size_t off) {
+  return reinterpret_cast<T*>(static_cast<char*>(ws) + off);
+}
+
+int check_workspace(const medusa_shape* s, void* ws, size_t bytes, Layout* L) {
+  *L = layout_for(s);
+  if (!ws) return fail(MEDUSA_ERR_WORKSPACE, "workspace: null pointer");
+  if ((reinterpret_cast<uintptr_t>(ws) & 255u) != 0)
+    return fail(MEDUSA_ERR_WORKSPACE, "workspace: not 256-byte aligned");
+  if (bytes < L->total)
+    return fail(MEDUSA_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", bytes, L->total);
+  return MEDUSA_OK;
+}
+
+// ---- tree spec ------------------------------------------------------------------
+// Validates the host rank table and reduces it to (parent, own rank) per node.
+int make_plan(const medusa_shape* s, const int32_t* ranks, TreePlan* plan, int* P_out) {
+  const int N = s->N, K = s->K, T = N + 1;
+  if (N > 0 && !ranks) return fail(MEDUSA_ERR_ARG, "tree_ranks: null pointer");
+  std::vector<std::vector<int>> tup(N);
+  for (int n = 0; n < N; ++n) {
+    bool ended = false;
+    for (int j = 0; j < K; ++j) {
+      const int r = ranks[(size_t)n * K + j];
+      if (r < 0) {
+        ended = true;
+        continue;
+      }
+      if (ended) return fail(MEDUSA_ERR_ARG, "tree_ranks row %d: rank after -1 padding", n);
+      if (r >= s->s_max)
+        return fail(MEDUSA_ERR_ARG, "tree_ranks row %d: rank %d >= s_max %d", n, r, s->s_max);
+      tup[n].push_back(r);
+    }
+    if (tup[n].empty()) return fail(MEDUSA_ERR_ARG, "tree_ranks row %d: empty rank path", n);
+  }
+  auto canon_less = [](const std::vector<int>& a, const std::vector<int>& b) {
+    if (a.size() != b.size()) return a.size() < b.size();
+    return a < b;
+  };
+  for (int n = 1; n < N; ++n)
+    if (!canon_less(tup[n - 1], tup[n]))
+      return fail(MEDUSA_ERR_ARG,
+                  "tree_ranks rows %d,%d: not in canonical order (depth, then lexicographic) "
+                  "or duplicated",
+                  n - 1, n);
+  memset(plan, 0, sizeof(*plan));
+  plan->T = T;
+  plan->K = K;
+  std::vector<char> has_child(T, 0);
+  for (int n = 0; n < N; ++n) {
+    int par = 0;
+    if (tup[n].size() > 1) {
+      std::vector<int> pre(tup[n].begin(), tup[n].end() - 1);
+      // canonical order sorts parents before children: binary search
+      auto it = std::lower_bound(tup.begin(), tup.begin() + n, pre, canon_less);
+      if (it == tup.begin() + n || *it != pre)
+        return fail(MEDUSA_ERR_ARG, "tree_ranks row %d: not prefix-closed", n);
+      par = (int)(it - tup.begin()) + 1;
+    }
+    plan->parent[n + 1] = (uint8_t)par;
+    plan->last_rank[n + 1] = (uint8_t)tup[n].back();
+    has_child[par] = 1;
+  }
+  int P = 0;
+  for (int n = 1; n < T; ++n) P += !has_child[n];
+  if (T == 1) P = 1;
+  *P_out = P;
+  return MEDUSA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* medusa_last_error(void) { return g_err.c_str(); }
+
+const char* medusa_version(void) { return "medusa-mi355x 0.1 (gfx950)"; }
+
+size_t medusa_workspace_bytes(const medusa_shape* shape) {
+  if (check_shape(shape) != MEDUSA_OK) return 0;
+  return layout_for(shape).total;
+}
+
+int medusa_heads_forward(const medusa_shape* shape, const float* h, const void* W1,
+                         const float* b1_or_null, const void* W2, int32_t* topk_ids,
+                         float* topk_logits, float* head_lse_or_null,
+                         float* head_logits_or_null, float* z_or_null, void* workspace,
+                         size_t workspace_bytes, void* stream) {
+  int rc = check_shape(shape);
+  if (rc) return rc;
+  REQUIRE_PTR(h);
+  REQUIRE_PTR(W1);
+  REQUIRE_PTR(W2);
+  REQUIRE_PTR(topk_ids);
+  REQUIRE_PTR(topk_logits);
+  OPTIONAL_PTR(b1_or_null);
+  OPTIONAL_PTR(head_lse_or_null);
+  OPTIONAL_PTR(head_logits_or_null);
+  OPTIONAL_PTR(z_or_null);
+  Layout L;
+  rc = check_workspace(shape, workspace, workspace_bytes, &L);
+  if (rc) return rc;
+  HeadsArgs a{};
+  a.f32 = shape->dtype == MEDUSA_F32;
+  a.B = shape->B;
+  a.d = shape->d;
+  a.V = shape->V;
+  a.K = shape->K;
+  a.S = shape->s_max;
+  a.h = h;
+  a.W1 = W1;
+  a.b1 = b1_or_null;
+  a.W2 = W2;
+  a.z = z_or_null ? z_or_null : at<float>(workspace, L.z);
+  a.head_logits = head_logits_or_null;
+  a.topk_ids = topk_ids;
+  a.topk_logits = topk_logits;
+  a.lse = head_lse_or_null;
+  a.part_val = at<float>(workspace, L.part_val);
+  a.part_id = at<int>(workspace, L.part_id);
+  a.part_m = at<float>(workspace, L.part_m);
+  a.part_s = at<float>(workspace, L.part_s);
+  a.G = L.G;
+  a.w1_rows_per_wg = w1_rows();
+  a.w2_rows_per_wg = w2_rows();
+  hipError_t e = launch_heads(a, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "heads launch");
+  return ok();
+}
+
+int medusa_build_tree(const medusa_shape* shape, const int32_t* tree_ranks_host,
+                      int draft_mode, const int32_t* root_tok, const int32_t* topk_ids,
+                      const float* head_logits_or_null, const float* head_lse_or_null,
+                      const float* u_draft_or_null, const int32_t* kv_len,
+                      int32_t* tree_tokens, uint8_t* tree_mask, int32_t* position_ids,
+                      int32_t* retrieve, int32_t* parent, int32_t* depth, void* stream) {
+  int rc = check_shape(shape);
+  if (rc) return rc;
+  if (draft_mode != MEDUSA_DRAFT_TOPK && draft_mode != MEDUSA_DRAFT_SAMPLE)
+    return fail(MEDUSA_ERR_ARG, "draft_mode %d unknown", draft_mode);
+  REQUIRE_PTR(root_tok);
+  REQUIRE_PTR(kv_len);
+  REQUIRE_PTR(tree_tokens);
+  REQUIRE_PTR(tree_mask);
+  REQUIRE_PTR(position_ids);
+  REQUIRE_PTR(retrieve);
+  REQUIRE_PTR(parent);
+  REQUIRE_PTR(depth);
+  if (draft_mode == MEDUSA_DRAFT_TOPK) {
+    REQUIRE_PTR(topk_ids);
+  } else {
+    REQUIRE_PTR(head_logits_or_null);
+    REQUIRE_PTR(head_lse_or_null);
+    REQUIRE_PTR(u_draft_or_null);
+  }
+  TreeArgs a{};
+  int P = 0;
+  rc = make_plan(shape, tree_ranks_host, &a.plan, &P);
+  if (rc) return rc;
+  if (P != shape->P)
+    return fail(MEDUSA_ERR_ARG, "tree has %d root-to-leaf paths, shape.P is %d", P, shape->P);
+  a.B = shape->B;
+  a.V = shape->V;
+  a.S = shape->s_max;
+  a.P = P;
+  a.sample = draft_mode == MEDUSA_DRAFT_SAMPLE;
+  a.root_tok = root_tok;
+  a.topk_ids = topk_ids;
+  a.head_logits = head_logits_or_null;
+  a.head_lse = head_lse_or_null;
+  a.u_draft = u_draft_or_null;
+  a.kv_len = kv_len;
+  a.tokens = tree_tokens;
+  a.mask = tree_mask;
+  a.position_ids = position_ids;
+  a.retrieve = retrieve;
+  a.parent = parent;
+  a.depth = depth;
+  hipError_t e = launch_tree(a, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "tree launch");
+  return ok();
+}
+
+}  // extern "C"

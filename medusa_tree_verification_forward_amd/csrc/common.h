@@ -1,0 +1,160 @@
+// Device helpers shared by the gfx950 kernels of the Medusa verify step.
+//
+// Wavefronts are 64 lanes. Cross-lane reductions use DPP inside 16-lane rows
+// (quad permutes and row rotations) and DPP row broadcasts across rows, the
+// GFX9-family forms that gfx950 keeps.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace medusa {
+
+constexpr int kWave = 64;
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float floatx4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+// ---- bf16 <-> fp32 ----------------------------------------------------------
+
+// Low / high bf16 of a packed pair, widened exactly to fp32.
+__device__ __forceinline__ float bf16lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// fp32 -> bf16 bits, round to nearest, ties to even (finite inputs).
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
+}
+__device__ __forceinline__ float round_to_bf16(float f) {
+  return __uint_as_float(f32_to_bf16_bits(f) << 16);
+}
+
+// ---- element type traits ----------------------------------------------------
+// Weights, embeddings and the KV cache are stored as bf16 (uint16 bits) or
+// fp32. A 16-byte vector load carries 8 bf16 or 4 fp32 elements.
+
+struct BF16 {
+  typedef uint16_t storage;
+  static constexpr int kPerVec = 8;
+  __device__ __forceinline__ static void widen(const u32x4_t& v, float* out) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      out[2 * i] = bf16lo(v[i]);
+      out[2 * i + 1] = bf16hi(v[i]);
+    }
+  }
+  __device__ __forceinline__ static float load1(const storage* p) {
+    return __uint_as_float(((uint32_t)*p) << 16);
+  }
+  __device__ __forceinline__ static storage from_float(float f) {
+    return (storage)f32_to_bf16_bits(f);
+  }
+  __device__ __forceinline__ static float round(float f) { return round_to_bf16(f); }
+};
+
+struct F32 {
+  typedef float storage;
+  static constexpr int kPerVec = 4;
+  __device__ __forceinline__ static void widen(const u32x4_t& v, float* out) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) out[i] = __uint_as_float(v[i]);
+  }
+  __device__ __forceinline__ static float load1(const storage* p) { return *p; }
+  __device__ __forceinline__ static storage from_float(float f) { return f; }
+  __device__ __forceinline__ static float round(float f) { return f; }
+};
+
+// 16-byte global load that bypasses nothing special (plain vector load).
+__device__ __forceinline__ u32x4_t load16(const void* p) {
+  return *reinterpret_cast<const u32x4_t*>(p);
+}
+// Streaming (read-once) 16-byte load: non-temporal hint so the stream does
+// not evict reused data from the caches.
+__device__ __forceinline__ u32x4_t load16_stream(const void* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+}
+
+// ---- DPP wave reductions ----------------------------------------------------
+// DPP control codes (GFX9 encoding).
+constexpr int kDppQuadXor1 = 0xB1;   // quad_perm [1,0,3,2]
+constexpr int kDppQuadXor2 = 0x4E;   // quad_perm [2,3,0,1]
+constexpr int kDppRowRor4 = 0x124;   // row_ror:4
+constexpr int kDppRowRor8 = 0x128;   // row_ror:8
+constexpr int kDppRowBcast15 = 0x142;
+constexpr int kDppRowBcast31 = 0x143;
+
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xf, 0xf, false));
+}
+template <int CTRL>
+__device__ __forceinline__ int dppi(int v) {
+  return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xf, 0xf, false);
+}
+
+// Sum over each 16-lane row; every lane of the row gets the row's sum.
+__device__ __forceinline__ float row16_sum(float v) {
+  v += dpp<kDppQuadXor1>(v);
+  v += dpp<kDppQuadXor2>(v);
+  v += dpp<kDppRowRor4>(v);
+  v += dpp<kDppRowRor8>(v);
+  return v;
+}
+__device__ __forceinline__ float row16_max(float v) {
+  v = fmaxf(v, dpp<kDppQuadXor1>(v));
+  v = fmaxf(v, dpp<kDppQuadXor2>(v));
+  v = fmaxf(v, dpp<kDppRowRor4>(v));
+  v = fmaxf(v, dpp<kDppRowRor8>(v));
+  return v;
+}
+
+__device__ __forceinline__ float readlane_f(float v, int lane) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), lane));
+}
+
+// Sum over the whole wave, returned to every lane (uniform). Rows are
+// combined in a fixed order, so the result does not depend on timing.
+__device__ __forceinline__ float wave_sum(float v) {
+  v = row16_sum(v);
+  return (readlane_f(v, 0) + readlane_f(v, 16)) + (readlane_f(v, 32) + readlane_f(v, 48));
+}
+__device__ __forceinline__ float wave_max(float v) {
+  v = row16_max(v);
+  return fmaxf(fmaxf(readlane_f(v, 0), readlane_f(v, 16)),
+               fmaxf(readlane_f(v, 32), readlane_f(v, 48)));
+}
+
+// ---- ordering of (logit, token id) candidates --------------------------------
+// Higher logit first; equal logits: lower id first.
+__device__ __forceinline__ bool better(float va, int ia, float vb, int ib) {
+  return va > vb || (va == vb && ia < ib);
+}
+
+// ---- MFMA ---------------------------------------------------------------------
+// v_mfma_f32_16x16x32_bf16: A 16x32, B 32x16, C 16x16 fp32.
+// Lane l holds A[l%16][8*(l/16) .. +7], B[8*(l/16) .. +7][l%16] and
+// C[4*(l/16) + j][l%16] for j = 0..3.
+__device__ __forceinline__ floatx4_t mfma16x16x32_bf16(const u32x4_t& a, const u32x4_t& b,
+                                                       floatx4_t c) {
+  bf16x8_t av, bv;
+  __builtin_memcpy(&av, &a, 16);
+  __builtin_memcpy(&bv, &b, 16);
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bv, c, 0, 0, 0);
+}
+// v_mfma_f32_16x16x4_f32: lane l holds A[l%16][l/16], B[l/16][l%16].
+__device__ __forceinline__ floatx4_t mfma16x16x4_f32(float a, float b, floatx4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+// e^x through the hardware base-2 exponential.
+__device__ __forceinline__ float exp_e(float x) {
+  return __builtin_amdgcn_exp2f(x * 1.4426950408889634f);
+}
+
+}  // namespace medusa

@@ -1,0 +1,179 @@
+// Candidate tree on gfx950 ("Medusa 深读", §6.1): topology, mask, position
+// ids, root-to-leaf paths and node tokens.
+//
+// The host has validated the rank-path spec and reduced it to (parent, own
+// rank) per node; one workgroup per sequence rebuilds the rest on the device
+// with one thread per node (T <= 256):
+//   depth      by walking parents,
+//   mask[i][j] = 1 iff j is i or an ancestor of i,
+//   positions  = kv_len[b] + depth (one index per depth),
+//   paths      = the leaves in lexicographic rank-path order,
+//   tokens     = the root token, or head (depth-1)'s token of the node's rank.
+// In sampling mode a second kernel draws each node's token from its depth's
+// head softmax by inverse CDF.
+#include "common.h"
+#include "kernels.h"
+
+namespace medusa {
+namespace {
+
+__device__ __forceinline__ bool lex_less(const uint8_t* a, int da, const uint8_t* b, int db) {
+  const int n = da < db ? da : db;
+  for (int j = 0; j < n; ++j)
+    if (a[j] != b[j]) return a[j] < b[j];
+  return da < db;
+}
+
+__global__ __launch_bounds__(256) void tree_kernel(TreeArgs a) {
+  const int b = blockIdx.x;
+  const int n = threadIdx.x;
+  const int T = a.plan.T, K = a.plan.K;
+  __shared__ uint8_t tup[MAXT][MAXK];
+  __shared__ int dep[MAXT];
+  __shared__ int has_child[MAXT];
+  if (n < T) {
+    int d = 0;
+    for (int x = n; x != 0; x = a.plan.parent[x]) ++d;
+    dep[n] = d;
+    int x = n;
+    for (int j = d - 1; j >= 0; --j) {
+      tup[n][j] = a.plan.last_rank[x];
+      x = a.plan.parent[x];
+    }
+    has_child[n] = 0;
+  }
+  __syncthreads();
+  if (n >= 1 && n < T) has_child[a.plan.parent[n]] = 1;
+  __syncthreads();
+  if (n >= T) return;
+  const int d = dep[n];
+
+  int tok;
+  if (n == 0)
+    tok = a.root_tok[b];
+  else if (a.sample)
+    tok = -1;   // drawn by tree_sample_kernel
+  else
+    tok = a.topk_ids[((size_t)b * K + (d - 1)) * a.S + a.plan.last_rank[n]];
+  a.tokens[(size_t)b * T + n] = tok;
+  a.position_ids[(size_t)b * T + n] = a.kv_len[b] + d;
+
+  if (b != 0) return;   // the topology is shared by every sequence
+  a.parent[n] = n == 0 ? -1 : (int)a.plan.parent[n];
+  a.depth[n] = d;
+  uint8_t* row = a.mask + (size_t)n * T;
+  for (int j = 0; j < T; ++j) row[j] = 0;
+  for (int x = n;; x = a.plan.parent[x]) {
+    row[x] = 1;
+    if (x == 0) break;
+  }
+  const bool leaf = T == 1 ? true : (n >= 1 && !has_child[n]);
+  if (!leaf) return;
+  int p = 0;
+  for (int m = 1; m < T; ++m)
+    if (m != n && !has_child[m] && lex_less(tup[m], dep[m], tup[n], d)) ++p;
+  int32_t* r = a.retrieve + (size_t)p * (K + 1);
+  int x = n;
+  for (int j = d; j >= 0; --j) {
+    r[j] = x;
+    x = a.plan.parent[x];
+  }
+  for (int j = d + 1; j <= K; ++j) r[j] = -1;
+}
+
+// Inverse-CDF draws for sampling mode. One 1024-thread block per
+// (depth k, sequence b); weights w_v = exp(l_v - lse) of head k.
+// The CDF is a fixed two-level sum: thread t sums chunk t sequentially (cs),
+// 64 groups of 16 chunks are combined sequentially (F inside a group, E
+// across groups), so C(x) = E_g + (F_j + local(x)) is monotone and every
+// search below evaluates exactly that function. A node draws the smallest
+// x with C(x) > u * C(V-1), clamped to the last token of nonzero weight.
+__global__ __launch_bounds__(1024) void tree_sample_kernel(TreeArgs a) {
+  const int kd = blockIdx.x;     // 0-based head = depth - 1
+  const int b = blockIdx.y;
+  const int t = threadIdx.x;
+  const int T = a.plan.T, K = a.plan.K, V = a.V;
+  const float* l = a.head_logits + ((size_t)b * K + kd) * V;
+  const float lse = a.head_lse[(size_t)b * K + kd];
+  const int csz = (V + 1023) / 1024;
+  __shared__ float cs[1024];
+  __shared__ float F[1024];
+  __shared__ float E[65];
+  __shared__ int last_nz;
+  float s = 0.f;
+  int my_last = -1;
+  for (int i = 0; i < csz; ++i) {
+    const int v = t * csz + i;
+    if (v < V) {
+      const float w = exp_e(l[v] - lse);
+      s += w;
+      if (w > 0.f) my_last = v;
+    }
+  }
+  cs[t] = s;
+  if (t == 0) last_nz = -1;
+  __syncthreads();
+  atomicMax(&last_nz, my_last);
+  if (t < 64) {
+    float f = 0.f;
+    for (int j = 0; j < 16; ++j) {
+      F[t * 16 + j] = f;
+      f = f + cs[t * 16 + j];
+    }
+    E[t + 1] = f;                         // temporarily the group total
+  }
+  __syncthreads();
+  if (t == 0) {
+    float e = 0.f;
+    for (int g = 0; g < 64; ++g) {
+      const float gt = E[g + 1];
+      E[g] = e;
+      e = e + gt;
+    }
+    E[64] = e;
+  }
+  __syncthreads();
+  // nodes of this depth, one per thread
+  int count = 0;
+  for (int n = 1; n < T; ++n) {
+    int dd = 0;
+    for (int x = n; x != 0; x = a.plan.parent[x]) ++dd;
+    if (dd != kd + 1) continue;
+    if (count++ % 1024 != t) continue;
+    const float target = a.u_draft[(size_t)b * T + n] * E[64];
+    int tok = -1;
+    for (int g = 0; g < 64 && tok < 0; ++g) {
+      const float eg = E[g];
+      const float gend = eg + (F[g * 16 + 15] + cs[g * 16 + 15]);
+      if (!(gend > target)) continue;
+      for (int j = g * 16; j < g * 16 + 16 && tok < 0; ++j) {
+        if (!(eg + (F[j] + cs[j]) > target)) continue;
+        float local = 0.f;
+        for (int i = 0; i < csz; ++i) {
+          const int v = j * csz + i;
+          if (v >= V) break;
+          local += exp_e(l[v] - lse);
+          if (eg + (F[j] + local) > target) {
+            tok = v;
+            break;
+          }
+        }
+        if (tok < 0) tok = min(V - 1, j * csz + csz - 1);
+      }
+    }
+    if (tok < 0 || tok > last_nz) tok = last_nz < 0 ? V - 1 : last_nz;
+    a.tokens[(size_t)b * T + n] = tok;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_tree(const TreeArgs& a, hipStream_t st) {
+  hipLaunchKernelGGL(tree_kernel, dim3(a.B), dim3(256), 0, st, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || !a.sample) return e;
+  hipLaunchKernelGGL(tree_sample_kernel, dim3(a.plan.K, a.B), dim3(1024), 0, st, a);
+  return hipGetLastError();
+}
+
+}  // namespace medusa

@@ -1,0 +1,119 @@
+"""Host-side checks of the C ABI: the library loads, exports every function
+include/medusa.h declares, and rejects bad arguments before touching the GPU
+(no compute is launched here)."""
+
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _lib():
+    try:
+        import medusa_tree_verification_forward_amd as M
+    except ImportError as e:
+        pytest.fail(f"library not built: {e}")
+    return M
+
+
+def _declared():
+    src = open(os.path.join(ROOT, "include", "medusa.h")).read()
+    return sorted(set(re.findall(r"\b(medusa_[a-z_]+)\s*\(", src)))
+
+
+def test_exports_every_declared_symbol():
+    M = _lib()
+    lib = ctypes.CDLL(M.LIB_PATH)
+    missing = [n for n in _declared() if not hasattr(lib, n)]
+    assert not missing, missing
+    assert set(_declared()) <= set(M.exported_symbols()) | {"medusa_last_error", "medusa_version"}
+
+
+def _shape(M, **kw):
+    base = dict(B=1, d=4096, V=32000, K=5, H=32, Dh=128, Lmax=2112, N=45, P=12, s_max=3,
+                dtype="bf16")
+    base.update(kw)
+    return M.make_shape(**base)
+
+
+def test_workspace_bytes_and_shape_validation():
+    M = _lib()
+    n = M.workspace_bytes(_shape(M))
+    assert n > 0 and n % 256 == 0
+    for bad, code in [(dict(Dh=100), M._lib.ERR_ARG), (dict(d=4000, H=40, Dh=100), M._lib.ERR_ARG),
+                      (dict(K=9), M._lib.ERR_UNSUPPORTED), (dict(s_max=17), M._lib.ERR_UNSUPPORTED),
+                      (dict(N=256, P=1), M._lib.ERR_UNSUPPORTED), (dict(B=0), M._lib.ERR_ARG),
+                      (dict(dtype=7), M._lib.ERR_ARG), (dict(V=2), M._lib.ERR_ARG),
+                      (dict(H=64, Dh=64, d=4096, Lmax=0), M._lib.ERR_ARG)]:
+        with pytest.raises(M.MedusaError) as ei:
+            M.workspace_bytes(_shape(M, **bad))
+        assert ei.value.code in (M._lib.ERR_ARG, code), bad
+
+
+class _FakePtr:
+    """A non-null, aligned fake device pointer: validation must fail before
+    any launch, so it is never dereferenced."""
+
+
+FAKE = 1 << 20
+
+
+def _call_tree(M, shape, ranks, **kw):
+    args = dict(root_tok=FAKE, kv_len=FAKE, tree_tokens=FAKE, tree_mask=FAKE, position_ids=FAKE,
+                retrieve=FAKE, parent=FAKE, depth=FAKE, topk_ids=FAKE)
+    args.update(kw)
+    lib = M._lib._lib
+    return lib.medusa_build_tree(ctypes.byref(shape), ranks.ctypes.data if ranks.size else None,
+                                 0, args["root_tok"], args["topk_ids"], None, None, None,
+                                 args["kv_len"], args["tree_tokens"], args["tree_mask"],
+                                 args["position_ids"], args["retrieve"], args["parent"],
+                                 args["depth"], None)
+
+
+@pytest.mark.parametrize("rows,why", [
+    ([[0, -1], [0, 0], [1, -1]], "canonical"),      # depth-2 row before a depth-1 row
+    ([[0, -1], [1, 0]], "prefix"),                  # (1,0) without (1,)
+    ([[0, -1], [0, -1]], "canonical"),              # duplicate
+    ([[0, -1], [3, -1]], "s_max"),                  # rank beyond the pool
+    ([[-1, 0]], "padding"),                         # rank after padding
+])
+def test_tree_spec_rejected_on_host(rows, why):
+    M = _lib()
+    ranks = np.array(rows, dtype=np.int32)
+    shape = _shape(M, K=2, N=len(rows), P=1, s_max=2)
+    rc = _call_tree(M, shape, ranks)
+    assert rc == M._lib.ERR_ARG
+    assert M.last_error() != ""
+
+
+def test_tree_path_count_must_match():
+    M = _lib()
+    from workloads import cartesian_ranks
+    ranks = cartesian_ranks((2, 2))
+    shape = _shape(M, K=2, N=6, P=3, s_max=2)
+    assert _call_tree(M, shape, ranks) == M._lib.ERR_ARG
+    assert "paths" in M.last_error()
+
+
+def test_null_and_misaligned_pointers_rejected():
+    M = _lib()
+    from workloads import cartesian_ranks
+    ranks = cartesian_ranks((2, 2))
+    shape = _shape(M, K=2, N=6, P=4, s_max=2)
+    assert _call_tree(M, shape, ranks, tree_mask=None) == M._lib.ERR_ARG
+    assert "tree_mask" in M.last_error()
+    assert _call_tree(M, shape, ranks, retrieve=FAKE + 4) == M._lib.ERR_ARG
+    assert "aligned" in M.last_error()
+
+
+def test_heads_workspace_too_small():
+    M = _lib()
+    shape = _shape(M)
+    lib = M._lib._lib
+    rc = lib.medusa_heads_forward(ctypes.byref(shape), FAKE, FAKE, None, FAKE, FAKE, FAKE, None,
+                                  None, None, FAKE, 16, None)
+    assert rc == M._lib.ERR_WORKSPACE

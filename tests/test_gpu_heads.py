@@ -1,0 +1,140 @@
+"""GPU parity of medusa_heads_forward against the oracle's heads."""
+
+import numpy as np
+import pytest
+
+from oracle import heads as OH
+from oracle import numerics as ON
+from workloads import WORKLOADS, cartesian_ranks, make_inputs, scaled
+
+from gpu_helpers import assert_close, dev, host, poisoned, require_gpu, workspace
+
+pytestmark = pytest.mark.gpu
+
+
+def _run_heads(w, inp, with_logits=True):
+    import torch
+    import medusa_tree_verification_forward_amd as M
+    require_gpu()
+    B, K, S = w.B, w.K, w.s_max
+    N = cartesian_ranks(w.s).shape[0]
+    shape = M.make_shape(w.B, w.d, w.V, w.K, w.H, w.Dh, 64, N, int(np.prod(w.s)), S, w.dtype)
+    ws = workspace(M.workspace_bytes(shape))
+    ids = poisoned((B, K, S), torch.int32)
+    vals = poisoned((B, K, S), torch.float32)
+    lse = poisoned((B, K), torch.float32)
+    logits = poisoned((B, K, w.V), torch.float32) if with_logits else None
+    z = poisoned((B, K, w.d), torch.float32)
+    M.heads_forward(shape, dev(inp["h"]), dev(inp["W1"]), dev(inp["W2"]), ids, vals, ws,
+                    head_lse=lse, head_logits=logits, z=z)
+    torch.cuda.synchronize()
+    out = dict(ids=host(ids), vals=host(vals), lse=host(lse), z=host(z))
+    if with_logits:
+        out["logits"] = host(logits)
+    return out
+
+
+def _check_topk_on_own_logits(g):
+    # the fused top-s must equal a stable sort of the kernel's own logits
+    B, K, S = g["ids"].shape
+    for b in range(B):
+        for k in range(K):
+            row = g["logits"][b, k].astype(np.float64)
+            ref = np.lexsort((np.arange(row.shape[0]), -row))[:S]
+            assert list(g["ids"][b, k]) == list(ref), (b, k)
+            assert np.array_equal(g["vals"][b, k], g["logits"][b, k][ref])
+
+
+def _check_against_oracle(w, inp, g):
+    z, logits = OH.heads_forward(inp["h"], inp["W1"], inp["W2"])
+    ids, vals, lse = OH.heads_topk(logits, w.s_max)
+    assert_close(g["z"], z, 1e-5, "z")
+    assert_close(g["logits"], logits, 1e-5, "head logits")
+    err = float(np.max(np.abs(g["logits"] - logits)))
+    ambiguous = 0
+    for b in range(w.B):
+        for k in range(w.K):
+            if OH.topk_margin(logits[b, k], w.s_max) < 4 * err:
+                ambiguous += 1
+                continue
+            assert list(g["ids"][b, k]) == list(ids[b, k]), (b, k)
+    assert ambiguous == 0 or ambiguous < w.B * w.K // 4
+    assert np.allclose(g["lse"], lse, rtol=1e-5, atol=1e-5)
+    return ambiguous
+
+
+SMALL = [
+    WORKLOADS["tiny_fp32"],
+    # bf16, several row blocks with a ragged tail, 5 heads, d spanning many vectors
+    scaled(WORKLOADS["vicuna7b_typical"], d=512, V=2999, H=4, Dh=128),
+    # batch of 3 (ragged batch tile), fp32
+    scaled(WORKLOADS["tiny_fp32"], B=3, V=777),
+    # batch of 8 bf16
+    scaled(WORKLOADS["vicuna7b_batch8_ragged"], d=256, V=1500, H=2, Dh=128),
+    # wide pools (s_max = 16)
+    scaled(WORKLOADS["tiny_fp32"], s=(16, 2), K=2, V=4000),
+]
+
+
+@pytest.mark.parametrize("w", SMALL, ids=lambda w: f"{w.name}-d{w.d}-V{w.V}-B{w.B}")
+def test_heads_small_shapes(w):
+    inp = make_inputs(w, only=("W1", "W2"))
+    g = _run_heads(w, inp)
+    _check_topk_on_own_logits(g)
+    _check_against_oracle(w, inp, g)
+
+
+def test_heads_bias_and_identity_init():
+    # W1 = 0, b1 = 0, W2_k = W_lm: every head reproduces the LM head on h.
+    import torch
+    import medusa_tree_verification_forward_amd as M
+    require_gpu()
+    w = scaled(WORKLOADS["tiny_fp32"], V=1200)
+    inp = make_inputs(w, only=("W_lm",))
+    K, d = w.K, w.d
+    W1 = np.zeros((K, d, d), dtype=np.float32)
+    W2 = np.stack([inp["W_lm"]] * K)
+    shape = M.make_shape(1, d, w.V, K, w.H, w.Dh, 64, 14, 8, w.s_max, "f32")
+    ws = workspace(M.workspace_bytes(shape))
+    ids = poisoned((1, K, w.s_max), torch.int32)
+    vals = poisoned((1, K, w.s_max), torch.float32)
+    z = poisoned((1, K, d), torch.float32)
+    logits = poisoned((1, K, w.V), torch.float32)
+    b1 = torch.zeros((K, d), dtype=torch.float32, device="cuda")
+    M.heads_forward(shape, dev(inp["h"]), dev(W1), dev(W2), ids, vals, ws, b1=b1, z=z,
+                    head_logits=logits)
+    torch.cuda.synchronize()
+    zh = host(z)
+    lg = host(logits)
+    for k in range(K):
+        assert np.array_equal(zh[0, k], inp["h"][0])       # exact residual identity
+        assert np.array_equal(lg[0, k], lg[0, 0])          # identical heads, identical logits
+    ref = OH.lm_head(inp["W_lm"], inp["h"].astype(np.float64))
+    assert_close(lg[0, 0], ref[0], 1e-5, "identity logits")
+
+
+def test_heads_full_size_7b():
+    # Full 7B shapes, the launch configuration the throughput run uses.
+    w = WORKLOADS["vicuna7b_typical"]
+    inp = make_inputs(w, only=("W1", "W2"))
+    g = _run_heads(w, inp)
+    _check_topk_on_own_logits(g)
+    # oracle, head by head, in float64
+    z = np.empty((1, w.K, w.d))
+    for k in range(w.K):
+        z[:, k] = OH.residual_block(inp["W1"][k], inp["h"].astype(np.float64))
+    assert_close(g["z"], z, 1e-5, "z")
+    rng = np.random.default_rng(0)
+    for k in range(w.K):
+        W2k = ON.widen(inp["W2"][k])
+        logits = W2k @ z[0, k]
+        assert_close(g["logits"][0, k], logits, 1e-5, f"head {k} logits")
+        ids, vals = OH.top_s(logits, w.s_max)
+        err = float(np.max(np.abs(g["logits"][0, k] - logits)))
+        if OH.topk_margin(logits, w.s_max) >= 4 * err:
+            assert list(g["ids"][0, k]) == list(ids)
+        assert abs(g["lse"][0, k] - OH.log_sum_exp(logits)) < 1e-4
+        # spot rows one by one
+        rows = rng.integers(0, w.V, size=64)
+        for r in rows:
+            assert abs(g["logits"][0, k, r] - float(W2k[r] @ z[0, k])) < 1e-4

@@ -195,14 +195,21 @@ def lmax_for(w: Workload) -> int:
     return (Lmax + 63) // 64 * 64
 
 
-def make_inputs(w: Workload, with_weights: bool = True) -> Dict[str, np.ndarray]:
+def make_inputs(w: Workload, with_weights: bool = True,
+                only: Optional[Tuple[str, ...]] = None) -> Dict[str, np.ndarray]:
     """Draw every input of one verify step for workload ``w``.
 
     Returns a dict of numpy arrays (see the module docstring for layouts):
     h [B,d] f32; W1 [K,d,d]; W2 [K,V,d]; E [V,d]; W_qkv [3d,d]; W_o [d,d];
     W_lm [V,d]; k_cache, v_cache [B,H,Lmax,Dh]; kv_len [B] int32;
     root [B] int32; ranks [N,K] int32; u_draft, u_accept, u_resample [B,T] f32.
+    ``only`` restricts the weight tensors drawn (names as in the dict); every
+    tensor has its own stream, so a partial draw gives the same values.
     """
+
+    def want(name):
+        return with_weights and (only is None or name in only)
+
     store = w.dtype
     d, V, K, B, H, Dh = w.d, w.V, w.K, w.B, w.H, w.Dh
     ranks = cartesian_ranks(w.s)
@@ -221,14 +228,19 @@ def make_inputs(w: Workload, with_weights: bool = True) -> Dict[str, np.ndarray]
     out["kv_len"] = kv_len
     out["root"] = _rng(w, "root").integers(0, V, size=B).astype(np.int32)
 
-    if with_weights:
-        inv = 1.0 / np.sqrt(d)
-        w1_std = w.w1_std if w.w1_std is not None else inv
+    inv = 1.0 / np.sqrt(d)
+    w1_std = w.w1_std if w.w1_std is not None else inv
+    if want("W1"):
         out["W1"] = _normal(_rng(w, "W1"), (K, d, d), w1_std, store)
+    if want("W2"):
         out["W2"] = _normal(_rng(w, "W2"), (K, V, d), inv, store)
+    if want("E"):
         out["E"] = _normal(_rng(w, "E"), (V, d), 1.0, store)
+    if want("W_qkv"):
         out["W_qkv"] = _normal(_rng(w, "W_qkv"), (3 * d, d), inv, store)
+    if want("W_o"):
         out["W_o"] = _normal(_rng(w, "W_o"), (d, d), inv, store)
+    if want("W_lm"):
         if w.entropy_target is None:
             out["W_lm"] = _normal(_rng(w, "W_lm"), (V, d), inv, store)
         else:
@@ -237,7 +249,8 @@ def make_inputs(w: Workload, with_weights: bool = True) -> Dict[str, np.ndarray]
             alpha = _lm_scale_for_entropy(raw, out["h"][0], w.entropy_target)
             raw *= np.float32(alpha)
             out["W_lm"] = f32_to_bf16_bits(raw) if store == "bf16" else raw
-        for name in ("K", "V"):
+    for name in ("K", "V"):
+        if want("k_cache" if name == "K" else "v_cache"):
             rng = _rng(w, name)
             cache = np.zeros((B, H, Lmax, Dh),
                              dtype=np.uint16 if store == "bf16" else np.float32)
