@@ -1,0 +1,158 @@
+"""Throughput of one Medusa verify step on one MI355X.
+
+A step is one pass of the whole hot path over one batch: heads (residual
+block + vocabulary projection with fused top-s) -> candidate tree -> verify
+forward (QKV + RoPE, split-KV tree attention, output projection, LM head
+with row statistics) -> posterior (typical acceptance) -> commit. The
+workload is the Vicuna-7B-shaped step (d 4096, V 32000, 5 heads, 45-node
+top-(3,2,2,1,1) tree, 2048-token prefix, typical acceptance eps 0.09,
+delta 0.3, tau 0.7) on seeded synthetic inputs resident in HBM.
+
+Prints one JSON line: steps/s, the roofline of the dominant kernel (the
+W2 vocabulary projection with the fused top-s, timed with HIP events on its
+own stream inside the timed region) and the CPU oracle timed on a bounded
+sample of the same workload.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+WORKLOAD = "vicuna7b_typical"
+HBM_PEAK_GBS = 8000.0   # MI355X published HBM3E bandwidth
+
+
+def algorithmic_bytes(w, T, L_total):
+    """Bytes the step must move (bf16 weights and KV, fp32 activations)."""
+    d, V, K, B, H, Dh = w.d, w.V, w.K, w.B, w.H, w.Dh
+    wb = 2
+    weights = wb * (K * d * d + K * V * d + V * d + 4 * d * d)
+    kv = wb * 2 * H * Dh * L_total
+    emb = wb * d * B * T
+    act = 4 * d * B
+    return weights + kv + emb + act
+
+
+def w2_kernel_bytes(w):
+    """Algorithmic bytes of one vocabulary-projection launch: the K*V*d bf16
+    weights plus the K fp32 input vectors per sequence."""
+    return 2 * w.K * w.V * w.d + 4 * w.B * w.K * w.d
+
+
+def cpu_baseline(w, inp):
+    """The oracle, as it stands, on one full step of the same workload."""
+    from threadpoolctl import threadpool_info
+    from oracle import step as OSTEP
+    threads = max([t.get("num_threads", 1) for t in threadpool_info()] + [1])
+    t0 = time.perf_counter()
+    OSTEP.verify_step(inp, H=w.H, Dh=w.Dh, s_max=w.s_max, mode=w.mode, tau=w.tau, eps=w.eps,
+                      delta=w.delta, theta=w.rope_theta, bf16=True, want_margins=False)
+    dt = time.perf_counter() - t0
+    return {"value": 1.0 / dt, "unit": "steps/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"1 full {w.name} step (float64 NumPy, BLAS threads {threads}, "
+                      f"affinity cores {len(os.sched_getaffinity(0))}), {dt:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only: this build runs the verify step on a single "
+              f"MI355X; --gpus {args.gpus} is not supported.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import medusa_tree_verification_forward_amd as M
+    from medusa_tree_verification_forward_amd.step import VerifyStep
+    from workloads import WORKLOADS, make_inputs
+
+    w = WORKLOADS[WORKLOAD]
+    inp = make_inputs(w)
+    st = VerifyStep(inp, H=w.H, Dh=w.Dh, s_max=w.s_max, mode=w.mode, tau=w.tau, eps=w.eps,
+                    delta=w.delta, theta=w.rope_theta)
+    stream = torch.cuda.current_stream()
+    T = st.T
+    L_total = int(np.sum(inp["kv_len"]))
+
+    def step():
+        st.reset_kv_len()
+        st.run(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # per-step events around the dominant kernel (same stream as the kernel)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    for a, b in evs:       # create the underlying events before handing them over
+        a.record(stream)
+        b.record(stream)
+    torch.cuda.synchronize()
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_stop = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record(stream)
+    for i in range(args.steps):
+        M.set_profile_events(evs[i][0], evs[i][1])
+        step()
+    t_stop.record(stream)
+    torch.cuda.synchronize()
+    M.set_profile_events(None, None)
+    ms_total = t_start.elapsed_time(t_stop)
+    ms_step = ms_total / args.steps
+    w2_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+
+    alg = algorithmic_bytes(w, T, L_total)
+    w2b = w2_kernel_bytes(w)
+    achieved = w2b / (w2_ms * 1e-3) / 1e9
+    res = st.results()
+    line = {
+        "metric": "Medusa verify-steps/sec at 7B shapes (K=5, 45-node tree, 2k KV); "
+                  "% HBM roofline",
+        "value": 1000.0 / ms_step,
+        "unit": "steps/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded Gaussian weights and KV of Vicuna-7B shapes)",
+        "config": {"workload": w.name, "batch": w.B, "d": w.d, "V": w.V, "heads": w.K,
+                   "tree": "top-(3,2,2,1,1)", "tree_nodes": T - 1, "prefix_kv": L_total,
+                   "attn": f"{w.H}x{w.Dh}", "accept": f"typical eps={w.eps} delta={w.delta} "
+                                                    f"tau={w.tau}"},
+        "step_roofline": {"bound": "hbm", "algorithmic_bytes": alg,
+                          "achieved_GBs": alg / (ms_step * 1e-3) / 1e9, "peak": HBM_PEAK_GBS,
+                          "frac": alg / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS},
+        "roofline": {"kernel": "heads_w2 (vocabulary projection + fused top-s)",
+                     "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "avg_us": w2_ms * 1e3, "bytes_per_launch": w2b},
+        "accept_len": [int(x) for x in res["accept_len"]],
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(w, inp)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -93,6 +93,17 @@ const char* medusa_last_error(void);
 const char* medusa_version(void);
 
 /*
+ * Benchmark hook. When both handles are non-NULL hipEvent_t values, every
+ * later medusa_heads_forward call records `before` and `after` on its own
+ * stream immediately around its vocabulary-projection kernel (l_k = W2_k z_k
+ * with the fused top-s, the step's dominant HBM stream), so a caller can
+ * time that kernel alone. NULL, NULL turns the hook off. Process-wide, not
+ * thread-safe; meant for single-threaded benchmark drivers. Returns
+ * MEDUSA_OK.
+ */
+int medusa_set_profile_events(void* before, void* after);
+
+/*
  * Workspace bytes that one call sequence of this shape needs (the largest
  * need of any call below, plus a counter block). Zero-fill a new workspace
  * once before its first use; every call leaves its counters at zero again,

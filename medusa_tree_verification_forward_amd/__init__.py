@@ -8,4 +8,4 @@ buffers of one step (``step``). Importing it without the built library raises.
 from ._lib import (  # noqa: F401
     BF16, DRAFT_SAMPLE, DRAFT_TOPK, EXACT, F32, GREEDY, LIB_PATH, MODES, TYPICAL, MedusaError,
     Shape, build_tree, commit, evaluate_posterior, exported_symbols, heads_forward, last_error,
-    make_shape, tree_attention, verify_forward, version, workspace_bytes)
+    make_shape, set_profile_events, tree_attention, verify_forward, version, workspace_bytes)

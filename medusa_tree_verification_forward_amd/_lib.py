@@ -66,6 +66,7 @@ _SIGS = {
     "medusa_last_error": ([], ctypes.c_char_p),
     "medusa_version": ([], ctypes.c_char_p),
     "medusa_workspace_bytes": ([_SP], _SZ),
+    "medusa_set_profile_events": ([_P, _P], _I),
     "medusa_heads_forward": ([_SP, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P], _I),
     "medusa_build_tree": ([_SP, _P, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P], _I),
     "medusa_tree_attention": ([_SP, _P, _P, _P, _P, _P, _P, _P, _F, _P, _P, _SZ, _P], _I),
@@ -121,6 +122,16 @@ def _stream(stream) -> Optional[int]:
 def make_shape(B, d, V, K, H, Dh, Lmax, N, P, s_max, dtype) -> Shape:
     return Shape(B, d, V, K, H, Dh, Lmax, N, P, s_max,
                  dtype if isinstance(dtype, int) else (F32 if dtype == "f32" else BF16))
+
+
+def set_profile_events(before=None, after=None):
+    """Record `before`/`after` (torch.cuda.Event or raw handles) around the
+    vocabulary-projection kernel of later heads calls; None, None disables."""
+    def h(e):
+        if e is None:
+            return None
+        return e if isinstance(e, int) else e.cuda_event
+    _check(_lib.medusa_set_profile_events(h(before), h(after)))
 
 
 def workspace_bytes(shape: Shape) -> int:

@@ -12,6 +12,8 @@
 #include <string>
 #include <vector>
 
+#include <math.h>
+
 #include "kernels.h"
 
 using namespace medusa;
@@ -19,6 +21,7 @@ using namespace medusa;
 namespace {
 
 thread_local std::string g_err;
+hipEvent_t g_ev_before = nullptr, g_ev_after = nullptr;   // benchmark hook
 
 int fail(int code, const char* fmt, ...) {
   char buf[512];
@@ -96,6 +99,13 @@ struct Layout {
   // heads
   size_t z = 0, part_val = 0, part_id = 0, part_m = 0, part_s = 0;
   int G = 0;
+  // attention
+  size_t att_o = 0, att_ml = 0;
+  int NS = 0;
+  // verify
+  size_t q = 0, o_elem = 0, y_elem = 0, lm_part = 0;
+  // posterior (exact)
+  size_t pw = 0;
   size_t total = 0;
 };
 
@@ -116,6 +126,16 @@ Layout layout_for(const medusa_shape* s) {
   L.part_id = take(B * K * Gmax * S * 4);
   L.part_m = take(B * K * Gmax * 4);
   L.part_s = take(B * K * Gmax * 4);
+  const size_t T = s->N + 1, H = s->H, Dh = s->Dh, V = s->V;
+  const size_t es = s->dtype == MEDUSA_F32 ? 4 : 2;
+  L.NS = attn_splits(s->Lmax);
+  L.att_o = take(B * H * L.NS * T * Dh * 4);
+  L.att_ml = take(B * H * L.NS * T * 2 * 4);
+  L.q = take(B * T * d * es);
+  L.o_elem = take(B * T * d * es);
+  L.y_elem = take(B * T * d * es);
+  L.lm_part = take(B * T * lm_head_blocks(s->V) * 4 * 4);
+  L.pw = take(B * V * 4);
   L.total = off;
   return L;
 }
@@ -199,6 +219,16 @@ const char* medusa_last_error(void) { return g_err.c_str(); }
 
 const char* medusa_version(void) { return "medusa-mi355x 0.1 (gfx950)"; }
 
+int medusa_set_profile_events(void* before, void* after) {
+  if (before && after) {
+    g_ev_before = static_cast<hipEvent_t>(before);
+    g_ev_after = static_cast<hipEvent_t>(after);
+  } else {
+    g_ev_before = g_ev_after = nullptr;
+  }
+  return ok();
+}
+
 size_t medusa_workspace_bytes(const medusa_shape* shape) {
   if (check_shape(shape) != MEDUSA_OK) return 0;
   return layout_for(shape).total;
@@ -246,6 +276,8 @@ int medusa_heads_forward(const medusa_shape* shape, const float* h, const void* 
   a.G = L.G;
   a.w1_rows_per_wg = w1_rows();
   a.w2_rows_per_wg = w2_rows();
+  a.ev_before = g_ev_before;
+  a.ev_after = g_ev_after;
   hipError_t e = launch_heads(a, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "heads launch");
   return ok();
@@ -301,6 +333,274 @@ int medusa_build_tree(const medusa_shape* shape, const int32_t* tree_ranks_host,
   a.depth = depth;
   hipError_t e = launch_tree(a, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "tree launch");
+  return ok();
+}
+
+int medusa_tree_attention(const medusa_shape* shape, const void* q, const void* k_tree,
+                          const void* v_tree, const void* k_cache, const void* v_cache,
+                          const int32_t* kv_len, const uint8_t* tree_mask, float scale,
+                          float* out, void* workspace, size_t workspace_bytes, void* stream) {
+  int rc = check_shape(shape);
+  if (rc) return rc;
+  REQUIRE_PTR(q);
+  REQUIRE_PTR(k_tree);
+  REQUIRE_PTR(v_tree);
+  REQUIRE_PTR(k_cache);
+  REQUIRE_PTR(v_cache);
+  REQUIRE_PTR(kv_len);
+  REQUIRE_PTR(tree_mask);
+  REQUIRE_PTR(out);
+  if (!(scale > 0.f) || !isfinite(scale)) return fail(MEDUSA_ERR_ARG, "scale must be positive");
+  Layout L;
+  rc = check_workspace(shape, workspace, workspace_bytes, &L);
+  if (rc) return rc;
+  AttnArgs a{};
+  a.f32 = shape->dtype == MEDUSA_F32;
+  a.B = shape->B;
+  a.T = shape->N + 1;
+  a.H = shape->H;
+  a.Dh = shape->Dh;
+  a.Lmax = shape->Lmax;
+  a.q = q;
+  a.k_tree = k_tree;
+  a.v_tree = v_tree;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.kv_len = kv_len;
+  a.mask = tree_mask;
+  a.scale = scale;
+  a.NS = L.NS;
+  a.part_o = at<float>(workspace, L.att_o);
+  a.part_ml = at<float>(workspace, L.att_ml);
+  a.out = out;
+  a.out_elem = nullptr;
+  hipError_t e = launch_tree_attention(a, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "tree attention launch");
+  return ok();
+}
+
+int medusa_verify_forward(const medusa_shape* shape, const void* E, const void* W_qkv,
+                          const void* W_o, const void* W_lm, float rope_theta,
+                          const int32_t* tree_tokens, const int32_t* position_ids,
+                          const uint8_t* tree_mask, const int32_t* parent,
+                          const void* k_cache, const void* v_cache, const int32_t* kv_len,
+                          float temperature, void* k_tree_out, void* v_tree_out,
+                          float* y_out, float* row_stats, int32_t* row_argmax,
+                          float* child_logit, float* verify_logits_or_null,
+                          void* workspace, size_t workspace_bytes, void* stream) {
+  int rc = check_shape(shape);
+  if (rc) return rc;
+  REQUIRE_PTR(E);
+  REQUIRE_PTR(W_qkv);
+  REQUIRE_PTR(W_o);
+  REQUIRE_PTR(W_lm);
+  REQUIRE_PTR(tree_tokens);
+  REQUIRE_PTR(position_ids);
+  REQUIRE_PTR(tree_mask);
+  REQUIRE_PTR(parent);
+  REQUIRE_PTR(k_cache);
+  REQUIRE_PTR(v_cache);
+  REQUIRE_PTR(kv_len);
+  REQUIRE_PTR(k_tree_out);
+  REQUIRE_PTR(v_tree_out);
+  REQUIRE_PTR(y_out);
+  REQUIRE_PTR(row_stats);
+  REQUIRE_PTR(row_argmax);
+  REQUIRE_PTR(child_logit);
+  OPTIONAL_PTR(verify_logits_or_null);
+  if (!(rope_theta > 1.f) || !isfinite(rope_theta))
+    return fail(MEDUSA_ERR_ARG, "rope_theta must be > 1");
+  if (!(temperature > 0.f) || !isfinite(temperature))
+    return fail(MEDUSA_ERR_ARG, "temperature must be positive");
+  Layout L;
+  rc = check_workspace(shape, workspace, workspace_bytes, &L);
+  if (rc) return rc;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const bool f32 = shape->dtype == MEDUSA_F32;
+  const int T = shape->N + 1, M = shape->B * T, d = shape->d;
+
+  GemmParams g{};
+  g.f32 = f32;
+  g.T = T;
+  g.H = shape->H;
+  g.Dh = shape->Dh;
+  // 1. q, k, v = RoPE(E[tok] Wq^T), RoPE(E[tok] Wk^T), E[tok] Wv^T
+  g.M = M;
+  g.N = 3 * d;
+  g.K = d;
+  g.A = E;
+  g.lda = d;
+  g.a_rows = tree_tokens;
+  g.a_nrows = shape->V;
+  g.W = W_qkv;
+  g.pos = position_ids;
+  g.log_theta = log((double)rope_theta);
+  g.q_out = at<char>(workspace, L.q);
+  g.k_out = k_tree_out;
+  g.v_out = v_tree_out;
+  hipError_t e = launch_qkv(g, st);
+  if (e != hipSuccess) return hip_fail(e, "qkv launch");
+  // 2. tree attention, output rounded to the storage type
+  AttnArgs a{};
+  a.f32 = f32;
+  a.B = shape->B;
+  a.T = T;
+  a.H = shape->H;
+  a.Dh = shape->Dh;
+  a.Lmax = shape->Lmax;
+  a.q = g.q_out;
+  a.k_tree = k_tree_out;
+  a.v_tree = v_tree_out;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.kv_len = kv_len;
+  a.mask = tree_mask;
+  a.scale = 1.0f / sqrtf((float)shape->Dh);
+  a.NS = L.NS;
+  a.part_o = at<float>(workspace, L.att_o);
+  a.part_ml = at<float>(workspace, L.att_ml);
+  a.out = nullptr;
+  a.out_elem = at<char>(workspace, L.o_elem);
+  e = launch_tree_attention(a, st);
+  if (e != hipSuccess) return hip_fail(e, "attention launch");
+  // 3. y = x + o Wo^T
+  GemmParams go = g;
+  go.N = d;
+  go.A = a.out_elem;
+  go.a_rows = nullptr;
+  go.a_nrows = shape->V;   // rows of E for the residual
+  go.W = W_o;
+  go.E = E;
+  go.tokens = tree_tokens;
+  go.y_out = y_out;
+  go.y_elem = at<char>(workspace, L.y_elem);
+  e = launch_oproj(go, st);
+  if (e != hipSuccess) return hip_fail(e, "output projection launch");
+  // 4. logits = y W_lm^T with row statistics and child logits
+  GemmParams gl = g;
+  gl.N = shape->V;
+  gl.A = go.y_elem;
+  gl.a_rows = nullptr;
+  gl.W = W_lm;
+  gl.tokens = tree_tokens;
+  gl.parent = parent;
+  gl.inv_tau = 1.0f / temperature;
+  gl.part = at<float>(workspace, L.lm_part);
+  gl.child_logit = child_logit;
+  gl.logits_out = verify_logits_or_null;
+  e = launch_lm_head(gl, row_stats, row_argmax, st);
+  if (e != hipSuccess) return hip_fail(e, "lm head launch");
+  return ok();
+}
+
+int medusa_evaluate_posterior(const medusa_shape* shape, int mode, float temperature,
+                              float eps, float delta, const float* row_stats,
+                              const int32_t* row_argmax, const float* child_logit,
+                              const float* verify_logits_or_null,
+                              const int32_t* tree_tokens, const int32_t* parent,
+                              const int32_t* retrieve, const float* head_logits_or_null,
+                              const float* head_lse_or_null, const float* u_accept_or_null,
+                              const float* u_resample_or_null, int32_t* accept_len,
+                              int32_t* best_path, int32_t* last_node, int32_t* out_tokens,
+                              int32_t* next_root, void* workspace, size_t workspace_bytes,
+                              void* stream) {
+  int rc = check_shape(shape);
+  if (rc) return rc;
+  if (mode != MEDUSA_GREEDY && mode != MEDUSA_TYPICAL && mode != MEDUSA_EXACT)
+    return fail(MEDUSA_ERR_ARG, "mode %d unknown", mode);
+  if (!(temperature > 0.f) || !isfinite(temperature))
+    return fail(MEDUSA_ERR_ARG, "temperature must be positive");
+  REQUIRE_PTR(tree_tokens);
+  REQUIRE_PTR(parent);
+  REQUIRE_PTR(retrieve);
+  REQUIRE_PTR(accept_len);
+  REQUIRE_PTR(best_path);
+  REQUIRE_PTR(last_node);
+  REQUIRE_PTR(out_tokens);
+  REQUIRE_PTR(next_root);
+  if (mode == MEDUSA_GREEDY) {
+    REQUIRE_PTR(row_argmax);
+  } else if (mode == MEDUSA_TYPICAL) {
+    REQUIRE_PTR(row_argmax);
+    REQUIRE_PTR(row_stats);
+    REQUIRE_PTR(child_logit);
+    if (!(eps >= 0.f) || !(delta >= 0.f)) return fail(MEDUSA_ERR_ARG, "eps, delta must be >= 0");
+  } else {
+    REQUIRE_PTR(verify_logits_or_null);
+    REQUIRE_PTR(head_logits_or_null);
+    REQUIRE_PTR(head_lse_or_null);
+    REQUIRE_PTR(u_accept_or_null);
+    REQUIRE_PTR(u_resample_or_null);
+  }
+  Layout L;
+  rc = check_workspace(shape, workspace, workspace_bytes, &L);
+  if (rc) return rc;
+  PostArgs a{};
+  a.mode = mode;
+  a.B = shape->B;
+  a.T = shape->N + 1;
+  a.K = shape->K;
+  a.P = shape->P;
+  a.V = shape->V;
+  a.inv_tau = 1.0f / temperature;
+  a.eps = eps;
+  a.delta = delta;
+  a.row_stats = row_stats;
+  a.row_argmax = row_argmax;
+  a.child_logit = child_logit;
+  a.verify_logits = verify_logits_or_null;
+  a.tokens = tree_tokens;
+  a.parent = parent;
+  a.retrieve = retrieve;
+  a.head_logits = head_logits_or_null;
+  a.head_lse = head_lse_or_null;
+  a.u_accept = u_accept_or_null;
+  a.u_resample = u_resample_or_null;
+  a.pw = at<float>(workspace, L.pw);
+  a.accept_len = accept_len;
+  a.best_path = best_path;
+  a.last_node = last_node;
+  a.out_tokens = out_tokens;
+  a.next_root = next_root;
+  hipError_t e = launch_posterior(a, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "posterior launch");
+  return ok();
+}
+
+int medusa_commit(const medusa_shape* shape, const int32_t* last_node, const int32_t* parent,
+                  const void* k_tree, const void* v_tree, const float* y, void* k_cache,
+                  void* v_cache, int32_t* kv_len, float* h_next, void* stream) {
+  int rc = check_shape(shape);
+  if (rc) return rc;
+  REQUIRE_PTR(last_node);
+  REQUIRE_PTR(parent);
+  REQUIRE_PTR(k_tree);
+  REQUIRE_PTR(v_tree);
+  REQUIRE_PTR(y);
+  REQUIRE_PTR(k_cache);
+  REQUIRE_PTR(v_cache);
+  REQUIRE_PTR(kv_len);
+  REQUIRE_PTR(h_next);
+  CommitArgs a{};
+  a.f32 = shape->dtype == MEDUSA_F32;
+  a.B = shape->B;
+  a.T = shape->N + 1;
+  a.K = shape->K;
+  a.H = shape->H;
+  a.Dh = shape->Dh;
+  a.d = shape->d;
+  a.Lmax = shape->Lmax;
+  a.last_node = last_node;
+  a.parent = parent;
+  a.k_tree = k_tree;
+  a.v_tree = v_tree;
+  a.y = y;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.kv_len = kv_len;
+  a.h_next = h_next;
+  hipError_t e = launch_commit(a, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "commit launch");
   return ok();
 }
 

@@ -341,11 +341,18 @@ hipError_t launch_heads_nb(const HeadsArgs& a, int b0, hipStream_t st) {
   if (e != hipSuccess) return e;
   const size_t lds_list = (size_t)WAVES * NB * (2 * MAXS_LDS + 2) * sizeof(float);
   const size_t lds2 = lds_x > lds_list ? lds_x : lds_list;
+  if (a.ev_before) {
+    e = hipEventRecord(a.ev_before, st);
+    if (e != hipSuccess) return e;
+  }
   hipLaunchKernelGGL((heads_w2_kernel<ET, NB, ROWS, WAVES>), dim3(a.G, a.K), dim3(WAVES * 64),
                      lds2, st, a.z, a.B, b0, a.K, a.V, a.d,
                      reinterpret_cast<const typename ET::storage*>(a.W2), a.w2_rows_per_wg,
                      a.S, a.head_logits, a.part_val, a.part_id, a.part_m, a.part_s, a.G);
-  return hipGetLastError();
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  if (a.ev_after) e = hipEventRecord(a.ev_after, st);
+  return e;
 }
 
 template <class ET>

@@ -32,6 +32,8 @@ struct HeadsArgs {
   int G;                  // row blocks per head
   int w1_rows_per_wg;
   int w2_rows_per_wg;
+  hipEvent_t ev_before;   // optional: recorded around the W2 kernel
+  hipEvent_t ev_after;
 };
 hipError_t launch_heads(const HeadsArgs& a, hipStream_t st);
 
@@ -63,5 +65,102 @@ struct TreeArgs {
   int32_t* depth;                // [T]
 };
 hipError_t launch_tree(const TreeArgs& a, hipStream_t st);
+
+// ---- node GEMMs (verify pass) ---------------------------------------------------
+enum { EPI_QKV = 0, EPI_OPROJ = 1, EPI_LM = 2 };
+struct GemmParams {
+  bool f32;
+  int M, N, K;                 // C[M][N] = A[M][K] * W[N][K]^T
+  const void* A;
+  int lda;
+  const int32_t* a_rows;       // optional: A row of output row m is a_rows[m]
+  int a_nrows;                 // rows of A (gathered indices are clamped into range)
+  const void* W;
+  // QKV epilogue
+  int T, H, Dh;
+  const int32_t* pos;          // [M] position ids
+  double log_theta;
+  void* q_out;
+  void* k_out;
+  void* v_out;                 // [M][H][Dh] storage type
+  // OPROJ epilogue (and LM child logits)
+  const void* E;
+  const int32_t* tokens;       // [M]
+  float* y_out;                // [M][N] fp32
+  void* y_elem;                // [M][N] storage type
+  // LM epilogue
+  float inv_tau;
+  float* part;                 // [M][blocks][4]
+  const int32_t* parent;       // [T]
+  float* child_logit;          // [M]
+  float* logits_out;           // [M][N] or null
+};
+int lm_head_blocks(int N);
+hipError_t launch_qkv(const GemmParams& p, hipStream_t st);
+hipError_t launch_oproj(const GemmParams& p, hipStream_t st);
+hipError_t launch_lm_head(const GemmParams& p, float* row_stats, int* row_argmax,
+                          hipStream_t st);
+
+// ---- tree attention ---------------------------------------------------------------
+constexpr int kAttnChunk = 256;   // prefix keys per split
+struct AttnArgs {
+  bool f32;
+  int B, T, H, Dh, Lmax;
+  const void* q;
+  const void* k_tree;
+  const void* v_tree;          // [B][T][H][Dh]
+  const void* k_cache;
+  const void* v_cache;         // [B][H][Lmax][Dh]
+  const int32_t* kv_len;       // [B]
+  const uint8_t* mask;         // [T][T]
+  float scale;
+  int NS;                      // splits per (b, h): 1 tree split + prefix splits
+  float* part_o;               // [B][H][NS][T][Dh]
+  float* part_ml;              // [B][H][NS][T][2]
+  float* out;                  // [B][T][H][Dh] fp32 (or null)
+  void* out_elem;              // [B][T][H][Dh] storage type (or null)
+};
+int attn_splits(int Lmax);
+hipError_t launch_tree_attention(const AttnArgs& a, hipStream_t st);
+
+// ---- posterior and commit -------------------------------------------------------------
+struct PostArgs {
+  int mode;                    // 0 greedy, 1 typical, 2 exact
+  int B, T, K, P, V;
+  float inv_tau, eps, delta;
+  const float* row_stats;      // [B][T][3]
+  const int32_t* row_argmax;   // [B][T]
+  const float* child_logit;    // [B][T]
+  const float* verify_logits;  // [B][T][V] (exact)
+  const int32_t* tokens;       // [B][T]
+  const int32_t* parent;       // [T]
+  const int32_t* retrieve;     // [P][K+1]
+  const float* head_logits;    // [B][K][V] (exact)
+  const float* head_lse;       // [B][K] (exact)
+  const float* u_accept;       // [B][T] (exact)
+  const float* u_resample;     // [B][T] (exact)
+  float* pw;                   // [B][V] workspace (exact)
+  int32_t* accept_len;
+  int32_t* best_path;
+  int32_t* last_node;
+  int32_t* out_tokens;         // [B][K+1]
+  int32_t* next_root;
+};
+hipError_t launch_posterior(const PostArgs& a, hipStream_t st);
+
+struct CommitArgs {
+  bool f32;
+  int B, T, K, H, Dh, d, Lmax;
+  const int32_t* last_node;
+  const int32_t* parent;
+  const void* k_tree;
+  const void* v_tree;
+  const float* y;
+  void* k_cache;
+  void* v_cache;
+  int32_t* kv_len;
+  float* h_next;
+};
+hipError_t launch_commit(const CommitArgs& a, hipStream_t st);
 
 }  // namespace medusa

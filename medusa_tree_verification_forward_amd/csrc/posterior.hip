@@ -1,0 +1,360 @@
+// Posterior evaluation, longest accepted prefix and commit on gfx950.
+//
+// Rules ("Medusa 深读", §5, acceptance equation and rule table; "Medusa Part
+// I", Part 2; "Medusa: Faster LLM text generation", Acceptance rules):
+//   greedy : child c accepted iff tok(c) == argmax of its parent's logits;
+//   typical: p(tok(c)) > min(eps, delta * exp(-H)) with p, H of the parent's
+//            tempered distribution, from its row statistics
+//            (p = e^{(l-m)/tau}/S, H = log S - W/S);
+//   exact  : children of an accepted node are tried in order, accepted iff
+//            u*q(x) < p(x), else p <- norm((p - q)+); with no child accepted
+//            (or at a leaf) the next root is an inverse-CDF draw from p.
+// The root is always accepted; a node needs its parent accepted; the
+// committed node is the deepest accepted node with the lowest index.
+//
+// Greedy/typical: one workgroup per sequence, one thread per node; the
+// accepted-prefix flags are ANDed along each node's ancestor chain and the
+// (depth, -index) maximum is found with DPP wave reductions.
+// Exact: one 1024-thread workgroup per sequence walks the tree; each p/q
+// step is a block-wide pass over the vocabulary.
+#include "common.h"
+#include "kernels.h"
+
+namespace medusa {
+namespace {
+
+constexpr float kNegInf = -__builtin_huge_valf();
+
+// Parent of node x, clamped into [0, T); walks below stop after K steps, so
+// a malformed parent array can neither fault nor loop.
+__device__ __forceinline__ int parent_of(const int32_t* parent, int x, int T) {
+  return min(max(parent[x], 0), T - 1);
+}
+
+__device__ __forceinline__ int wave_max_i(int v) {
+  v = max(v, dppi<kDppQuadXor1>(v));
+  v = max(v, dppi<kDppQuadXor2>(v));
+  v = max(v, dppi<kDppRowRor4>(v));
+  v = max(v, dppi<kDppRowRor8>(v));
+  return max(max(__builtin_amdgcn_readlane(v, 0), __builtin_amdgcn_readlane(v, 16)),
+             max(__builtin_amdgcn_readlane(v, 32), __builtin_amdgcn_readlane(v, 48)));
+}
+
+__global__ __launch_bounds__(256) void posterior_kernel(PostArgs a) {
+  const int b = blockIdx.x, c = threadIdx.x;
+  const int T = a.T;
+  __shared__ uint8_t acc[MAXT];
+  __shared__ int wmax[4];
+  const int* tok = a.tokens + (size_t)b * T;
+  if (c < T) {
+    bool ok = true;
+    if (c > 0) {
+      const int v = parent_of(a.parent, c, T);
+      const size_t pr = (size_t)b * T + v;
+      if (a.mode == 0) {
+        ok = tok[c] == a.row_argmax[pr];
+      } else {
+        const float m = a.row_stats[pr * 3 + 0];
+        const float S = a.row_stats[pr * 3 + 1];
+        const float W = a.row_stats[pr * 3 + 2];
+        const float p = exp_e((a.child_logit[(size_t)b * T + c] - m) * a.inv_tau) / S;
+        const float H = __logf(S) - W / S;
+        const float thr = fminf(a.eps, a.delta * exp_e(-H));
+        ok = p > thr;
+      }
+    }
+    acc[c] = ok;
+  }
+  __syncthreads();
+  int key = -1;
+  int dep = 0;
+  if (c < T) {
+    bool ok = true;
+    for (int x = c; x != 0 && dep < a.K; x = parent_of(a.parent, x, T)) {
+      ok = ok && acc[x];
+      ++dep;
+    }
+    if (ok) key = (dep << 16) | (0xffff - c);
+  }
+  key = wave_max_i(key);
+  if ((threadIdx.x & 63) == 0) wmax[threadIdx.x >> 6] = key;
+  __syncthreads();
+  if (c != 0) return;
+  key = max(max(wmax[0], wmax[1]), max(wmax[2], wmax[3]));
+  const int best = 0xffff - (key & 0xffff);
+  const int depth = key >> 16;
+  a.accept_len[b] = depth;
+  a.last_node[b] = best;
+  int* out = a.out_tokens + (size_t)b * (a.K + 1);
+  for (int j = depth + 1; j <= a.K; ++j) out[j] = -1;
+  int x = best;
+  for (int j = depth; j >= 0; --j) {
+    out[j] = tok[x];
+    x = parent_of(a.parent, x, T);
+  }
+  a.next_root[b] = a.row_argmax[(size_t)b * T + best];
+  int bp = 0;
+  for (int p = 0; p < a.P; ++p)
+    if (a.retrieve[(size_t)p * (a.K + 1) + depth] == best) {
+      bp = p;
+      break;
+    }
+  a.best_path[b] = bp;
+}
+
+// ---- exact mode ----------------------------------------------------------------
+// Block-wide helpers over a 1024-thread workgroup.
+__device__ float block_sum(float v, float* red) {
+  v = wave_sum(v);
+  const int w = threadIdx.x >> 6;
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) red[w] = v;
+  __syncthreads();
+  float s = 0.f;
+  for (int i = 0; i < 16; ++i) s += red[i];
+  return s;
+}
+__device__ float block_max(float v, float* red) {
+  v = wave_max(v);
+  const int w = threadIdx.x >> 6;
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) red[w] = v;
+  __syncthreads();
+  float s = kNegInf;
+  for (int i = 0; i < 16; ++i) s = fmaxf(s, red[i]);
+  return s;
+}
+
+// Inverse-CDF draw from the non-negative weights w[0..V): the same fixed
+// two-level sum as the tree sampler (chunk per thread, 64 groups of 16
+// chunks, groups combined in order); smallest x with C(x) > u * C(V-1),
+// clamped to the last positive weight.
+__device__ int block_inverse_cdf(const float* w, int V, float u, float* cs, float* F, float* E,
+                                 int* last_nz) {
+  const int t = threadIdx.x;
+  const int csz = (V + 1023) / 1024;
+  float s = 0.f;
+  int my_last = -1;
+  for (int i = 0; i < csz; ++i) {
+    const int v = t * csz + i;
+    if (v < V) {
+      s += w[v];
+      if (w[v] > 0.f) my_last = v;
+    }
+  }
+  __syncthreads();
+  cs[t] = s;
+  if (t == 0) *last_nz = -1;
+  __syncthreads();
+  atomicMax(last_nz, my_last);
+  if (t < 64) {
+    float f = 0.f;
+    for (int j = 0; j < 16; ++j) {
+      F[t * 16 + j] = f;
+      f = f + cs[t * 16 + j];
+    }
+    E[t + 1] = f;
+  }
+  __syncthreads();
+  if (t == 0) {
+    float e = 0.f;
+    for (int g = 0; g < 64; ++g) {
+      const float gt = E[g + 1];
+      E[g] = e;
+      e = e + gt;
+    }
+    E[64] = e;
+  }
+  __syncthreads();
+  // thread t tests whether the draw falls in its chunk
+  const float target = u * E[64];
+  const int g = t >> 4;
+  const float eg = E[g];
+  const float lo = eg + F[t];
+  const float hi = eg + (F[t] + cs[t]);
+  __shared__ int found;
+  if (t == 0) found = 0x7fffffff;
+  __syncthreads();
+  if (!(lo > target) && hi > target) {
+    float local = 0.f;
+    int x = -1;
+    for (int i = 0; i < csz; ++i) {
+      const int v = t * csz + i;
+      if (v >= V) break;
+      local += w[v];
+      if (eg + (F[t] + local) > target) {
+        x = v;
+        break;
+      }
+    }
+    if (x < 0) x = min(V - 1, t * csz + csz - 1);
+    atomicMin(&found, x);
+  }
+  __syncthreads();
+  int x = found;
+  if (x == 0x7fffffff || x > *last_nz) x = *last_nz < 0 ? V - 1 : *last_nz;
+  __syncthreads();
+  return x;
+}
+
+__global__ __launch_bounds__(1024) void posterior_exact_kernel(PostArgs a) {
+  const int b = blockIdx.x, t = threadIdx.x;
+  const int T = a.T, V = a.V, K = a.K;
+  __shared__ float red[16];
+  __shared__ float cs[1024], F[1024], E[65];
+  __shared__ int last_nz;
+  __shared__ int sh_taken;
+  float* pw = a.pw + (size_t)b * V;   // current target distribution p
+  const int* tok = a.tokens + (size_t)b * T;
+  const float* ur = a.u_resample + (size_t)b * T;
+  const float* ua = a.u_accept + (size_t)b * T;
+
+  // p = softmax(l_v / tau) into pw
+  auto load_p = [&](int v) {
+    const float* l = a.verify_logits + ((size_t)b * T + v) * V;
+    float mx = kNegInf;
+    for (int x = t; x < V; x += 1024) mx = fmaxf(mx, l[x] * a.inv_tau);
+    mx = block_max(mx, red);
+    float s = 0.f;
+    for (int x = t; x < V; x += 1024) {
+      const float e = exp_e(l[x] * a.inv_tau - mx);
+      pw[x] = e;
+      s += e;
+    }
+    s = block_sum(s, red);
+    const float inv = 1.f / s;
+    for (int x = t; x < V; x += 1024) pw[x] *= inv;
+    __syncthreads();
+  };
+
+  int v = 0;
+  int next = -1;
+  load_p(0);
+  while (true) {
+    const int dv = [&] {
+      int d = 0;
+      for (int x = v; x != 0 && d < K; x = parent_of(a.parent, x, T)) ++d;
+      return d;
+    }();
+    int taken = -1;
+    bool has_kids = false;
+    if (dv < K) {
+      const float* hl = a.head_logits + ((size_t)b * K + dv) * V;
+      const float lse = a.head_lse[(size_t)b * K + dv];
+      for (int c = v + 1; c < T; ++c) {
+        if (a.parent[c] != v) continue;
+        has_kids = true;
+        const int x = min(max(tok[c], 0), V - 1);
+        const float qx = exp_e(hl[x] - lse);
+        if (t == 0) sh_taken = (ua[c] * qx < pw[x]) ? 1 : 0;
+        __syncthreads();
+        const int acc = sh_taken;
+        __syncthreads();
+        if (acc) {
+          taken = c;
+          break;
+        }
+        // residual p <- norm(max(0, p - q)); kept when all zero
+        float s = 0.f;
+        for (int y = t; y < V; y += 1024) s += fmaxf(pw[y] - exp_e(hl[y] - lse), 0.f);
+        s = block_sum(s, red);
+        if (s > 0.f) {
+          const float inv = 1.f / s;
+          for (int y = t; y < V; y += 1024) pw[y] = fmaxf(pw[y] - exp_e(hl[y] - lse), 0.f) * inv;
+        }
+        __syncthreads();
+      }
+    }
+    if (taken < 0) {
+      next = block_inverse_cdf(pw, V, ur[v], cs, F, E, &last_nz);
+      break;
+    }
+    v = taken;
+    load_p(v);
+  }
+  if (t != 0) return;
+  int depth = 0;
+  for (int x = v; x != 0 && depth < K; x = parent_of(a.parent, x, T)) ++depth;
+  a.accept_len[b] = depth;
+  a.last_node[b] = v;
+  int* out = a.out_tokens + (size_t)b * (K + 1);
+  for (int j = depth + 1; j <= K; ++j) out[j] = -1;
+  int x = v;
+  for (int j = depth; j >= 0; --j) {
+    out[j] = tok[x];
+    x = parent_of(a.parent, x, T);
+  }
+  a.next_root[b] = next;
+  int bp = 0;
+  for (int p = 0; p < a.P; ++p)
+    if (a.retrieve[(size_t)p * (K + 1) + depth] == v) {
+      bp = p;
+      break;
+    }
+  a.best_path[b] = bp;
+}
+
+// ---- commit ----------------------------------------------------------------------
+template <class ET>
+__global__ __launch_bounds__(256) void commit_kernel(CommitArgs a) {
+  using S = typename ET::storage;
+  const int b = blockIdx.x;
+  const int T = a.T, H = a.H, Dh = a.Dh;
+  __shared__ int path[MAXK + 1];
+  __shared__ int sh_L, sh_depth;
+  if (threadIdx.x == 0) {
+    const int last = min(max(a.last_node[b], 0), T - 1);
+    int d = 0;
+    for (int x = last; x != 0 && d < a.K; x = parent_of(a.parent, x, T)) ++d;
+    int x = last;
+    for (int j = d; j >= 0; --j) {
+      path[j] = x;
+      x = parent_of(a.parent, x, T);
+    }
+    sh_depth = d;
+    sh_L = a.kv_len[b];
+  }
+  __syncthreads();
+  const int L = sh_L, d = sh_depth;
+  const bool room = L >= 0 && L + d + 1 <= a.Lmax;
+  if (room) {
+    const S* kt = reinterpret_cast<const S*>(a.k_tree);
+    const S* vt = reinterpret_cast<const S*>(a.v_tree);
+    S* kc = reinterpret_cast<S*>(a.k_cache);
+    S* vc = reinterpret_cast<S*>(a.v_cache);
+    const int per_row = H * Dh;
+    const int total = (d + 1) * per_row;
+    for (int e = threadIdx.x; e < total; e += blockDim.x) {
+      const int i = e / per_row, rem = e - i * per_row;
+      const int hh = rem / Dh, x = rem - hh * Dh;
+      const size_t src = (((size_t)b * T + path[i]) * H + hh) * Dh + x;
+      const size_t dst = (((size_t)b * H + hh) * a.Lmax + L + i) * Dh + x;
+      kc[dst] = kt[src];
+      vc[dst] = vt[src];
+    }
+  }
+  const float* y = a.y + ((size_t)b * T + path[d]) * a.d;
+  for (int e = threadIdx.x; e < a.d; e += blockDim.x) a.h_next[(size_t)b * a.d + e] = y[e];
+  __syncthreads();
+  if (threadIdx.x == 0) a.kv_len[b] = room ? L + d + 1 : -1;
+}
+
+}  // namespace
+
+hipError_t launch_posterior(const PostArgs& a, hipStream_t st) {
+  if (a.mode == 2)
+    hipLaunchKernelGGL(posterior_exact_kernel, dim3(a.B), dim3(1024), 0, st, a);
+  else
+    hipLaunchKernelGGL(posterior_kernel, dim3(a.B), dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_commit(const CommitArgs& a, hipStream_t st) {
+  if (a.f32)
+    hipLaunchKernelGGL(commit_kernel<F32>, dim3(a.B), dim3(256), 0, st, a);
+  else
+    hipLaunchKernelGGL(commit_kernel<BF16>, dim3(a.B), dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+}  // namespace medusa

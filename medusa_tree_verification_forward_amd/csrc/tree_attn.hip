@@ -1,0 +1,284 @@
+// Tree attention on gfx950 ("Medusa: Faster LLM text generation", Tree
+// attention; "Medusa 深读", §6.1): every tree node attends to the whole
+// prefix KV cache and to its own ancestors (and itself) among the tree nodes.
+//
+// Split-KV (flash-decoding) layout: workgroup (s, h, b) handles one key
+// range -- split 0 is the tree block (T keys under the ancestor mask), split
+// s >= 1 covers prefix keys [(s-1)*C, s*C) -- for all T queries of (b, h),
+// and leaves an unnormalised partial (m, l, O) per query. A merge kernel
+// combines the splits in a fixed order.
+//
+// Inside a workgroup everything is computed transposed, so that no lane
+// shuffles are needed between the two products:
+//   S^T = K Q^T     (A = K rows, loaded straight from HBM; B = Q rows),
+//   P^T = 2^(S^T * scale*log2e - m),
+//   O^T += V^T P^T  (A = V^T from LDS, where the workgroup stores the V
+//                    sub-chunk transposed; B = P^T straight from the S^T
+//                    accumulators, since the MFMA result layout puts the 4
+//                    keys of a lane exactly where the next MFMA's B operand
+//                    expects its k slots, up to a permutation shared with A).
+// In every accumulator a lane's column is one query, so the online-softmax
+// statistics (m, l, rescale factor) of a query live in that lane alone.
+// Waves split the query tiles (16 queries each).
+#include "common.h"
+#include "kernels.h"
+
+namespace medusa {
+namespace {
+
+constexpr float kNegInf = -__builtin_huge_valf();
+constexpr int SUB = 64;        // keys per sub-chunk
+constexpr int VPAD = 8;        // LDS row padding (elements) of V^T
+
+template <class ET, int DH, int QT>
+__global__ __launch_bounds__(256) void tree_attn_kernel(AttnArgs a) {
+  using S = typename ET::storage;
+  constexpr int PV = ET::kPerVec;
+  constexpr bool BF = PV == 8;
+  constexpr int DS = DH / (4 * PV);   // 16-byte steps along Dh per lane group
+  constexpr int DT = DH / 16;         // dh tiles of the output
+  const int s = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int T = a.T, H = a.H;
+  const int L = min(max(a.kv_len[b], 0), a.Lmax);
+  const bool tree = s == 0;
+  int kbeg, kend;
+  if (tree) {
+    kbeg = 0;
+    kend = T;
+  } else {
+    kbeg = (s - 1) * kAttnChunk;
+    kend = min(L, s * kAttnChunk);
+    if (kbeg >= kend) return;
+  }
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int li = lane & 15, lq = lane >> 4;
+  const int MQ = (T + 15) / 16;
+  const float sl2 = a.scale * 1.4426950408889634f;
+
+  const S* __restrict__ q = reinterpret_cast<const S*>(a.q);
+  const S* __restrict__ kt_src;
+  const S* __restrict__ vt_src;
+  size_t krow_stride;   // elements between consecutive keys
+  if (tree) {
+    kt_src = reinterpret_cast<const S*>(a.k_tree) + ((size_t)b * T * H + h) * DH;
+    vt_src = reinterpret_cast<const S*>(a.v_tree) + ((size_t)b * T * H + h) * DH;
+    krow_stride = (size_t)H * DH;
+  } else {
+    kt_src = reinterpret_cast<const S*>(a.k_cache) + ((size_t)b * H + h) * a.Lmax * DH;
+    vt_src = reinterpret_cast<const S*>(a.v_cache) + ((size_t)b * H + h) * a.Lmax * DH;
+    krow_stride = DH;
+  }
+
+  __shared__ S vt[DH][SUB + VPAD];
+
+  // Q fragments of my query tiles (B operand: lane = query, 16 B along Dh)
+  u32x4_t qf[QT][DS];
+  floatx4_t o[QT][DT];
+  float m_run[QT], l_run[QT];
+#pragma unroll
+  for (int u = 0; u < QT; ++u) {
+    const int qt = wave + 4 * u;
+    const int qi = min(16 * qt + li, T - 1);
+    const S* qp = q + (((size_t)b * T + qi) * H + h) * DH + PV * lq;
+#pragma unroll
+    for (int ds = 0; ds < DS; ++ds) qf[u][ds] = load16(qp + 4 * PV * ds);
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) o[u][dt] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+    m_run[u] = kNegInf;
+    l_run[u] = 0.f;
+  }
+
+  for (int kb = kbeg; kb < kend; kb += SUB) {
+    // ---- stage V^T of this sub-chunk (keys past the range read a valid row) ----
+    {
+      constexpr int VEC_PER_KEY = DH / PV;
+      for (int c = threadIdx.x; c < SUB * VEC_PER_KEY; c += 256) {
+        const int kk = c / VEC_PER_KEY, part = c - kk * VEC_PER_KEY;
+        const int key = min(kb + kk, kend - 1);
+        const u32x4_t v = load16(vt_src + (size_t)key * krow_stride + PV * part);
+        if constexpr (BF) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            vt[PV * part + 2 * e][kk] = (S)(v[e] & 0xffffu);
+            vt[PV * part + 2 * e + 1][kk] = (S)(v[e] >> 16);
+          }
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) vt[PV * part + e][kk] = __uint_as_float(v[e]);
+        }
+      }
+    }
+    __syncthreads();
+
+#pragma unroll
+    for (int u = 0; u < QT; ++u) {
+      const int qt = wave + 4 * u;
+      if (qt >= MQ) break;
+      const int query = 16 * qt + li;
+      // ---- S^T = K Q^T over 4 key tiles ----
+      floatx4_t st[4];
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt) {
+        st[kt] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+        const int key = min(kb + 16 * kt + li, kend - 1);
+        const S* kp = kt_src + (size_t)key * krow_stride + PV * lq;
+#pragma unroll
+        for (int ds = 0; ds < DS; ++ds) {
+          const u32x4_t kf = load16(kp + 4 * PV * ds);
+          if constexpr (BF) {
+            st[kt] = mfma16x16x32_bf16(kf, qf[u][ds], st[kt]);
+          } else {
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+              st[kt] = mfma16x16x4_f32(__uint_as_float(kf[j]), __uint_as_float(qf[u][ds][j]),
+                                       st[kt]);
+          }
+        }
+      }
+      // ---- scale, mask, online softmax (lane = query) ----
+      const uint8_t* mrow = a.mask + (size_t)min(query, T - 1) * T;
+      float mx = kNegInf;
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int key = kb + 16 * kt + 4 * lq + r;
+          bool ok = key < kend;
+          if (tree && ok && query < T) ok = mrow[key] != 0;
+          const float v = ok ? st[kt][r] * sl2 : kNegInf;
+          st[kt][r] = v;
+          mx = fmaxf(mx, v);
+        }
+      mx = fmaxf(mx, __shfl_xor(mx, 16));
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      const float m_new = fmaxf(m_run[u], mx);
+      const float alpha = m_new == kNegInf ? 1.f : __builtin_amdgcn_exp2f(m_run[u] - m_new);
+      float ls = 0.f;
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float pv = m_new == kNegInf ? 0.f : __builtin_amdgcn_exp2f(st[kt][r] - m_new);
+          st[kt][r] = pv;
+          ls += pv;
+        }
+      ls += __shfl_xor(ls, 16);
+      ls += __shfl_xor(ls, 32);
+      l_run[u] = l_run[u] * alpha + ls;
+      m_run[u] = m_new;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) o[u][dt][j] *= alpha;
+      // ---- O^T += V^T P^T ----
+      if constexpr (BF) {
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          u32x4_t pf;
+          pf[0] = pack_bf16x2(st[2 * t][0], st[2 * t][1]);
+          pf[1] = pack_bf16x2(st[2 * t][2], st[2 * t][3]);
+          pf[2] = pack_bf16x2(st[2 * t + 1][0], st[2 * t + 1][1]);
+          pf[3] = pack_bf16x2(st[2 * t + 1][2], st[2 * t + 1][3]);
+#pragma unroll
+          for (int dt = 0; dt < DT; ++dt) {
+            const S* vr = &vt[16 * dt + li][32 * t + 4 * lq];
+            const uint2 lo = *reinterpret_cast<const uint2*>(vr);
+            const uint2 hi = *reinterpret_cast<const uint2*>(vr + 16);
+            u32x4_t vf;
+            vf[0] = lo.x;
+            vf[1] = lo.y;
+            vf[2] = hi.x;
+            vf[3] = hi.y;
+            o[u][dt] = mfma16x16x32_bf16(vf, pf, o[u][dt]);
+          }
+        }
+      } else {
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+          for (int dt = 0; dt < DT; ++dt) {
+            const float4 vr = *reinterpret_cast<const float4*>(&vt[16 * dt + li][16 * kt + 4 * lq]);
+            o[u][dt] = mfma16x16x4_f32(vr.x, st[kt][0], o[u][dt]);
+            o[u][dt] = mfma16x16x4_f32(vr.y, st[kt][1], o[u][dt]);
+            o[u][dt] = mfma16x16x4_f32(vr.z, st[kt][2], o[u][dt]);
+            o[u][dt] = mfma16x16x4_f32(vr.w, st[kt][3], o[u][dt]);
+          }
+      }
+    }
+    __syncthreads();
+  }
+
+  // ---- partial (m, l, O) per query ----
+  const size_t base = (((size_t)b * H + h) * a.NS + s) * T;
+#pragma unroll
+  for (int u = 0; u < QT; ++u) {
+    const int qt = wave + 4 * u;
+    if (qt >= MQ) break;
+    const int query = 16 * qt + li;
+    if (query >= T) continue;
+    if (lq == 0) {
+      a.part_ml[(base + query) * 2 + 0] = m_run[u];
+      a.part_ml[(base + query) * 2 + 1] = l_run[u];
+    }
+    float* op = a.part_o + (base + query) * DH;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+      *reinterpret_cast<float4*>(op + 16 * dt + 4 * lq) =
+          make_float4(o[u][dt][0], o[u][dt][1], o[u][dt][2], o[u][dt][3]);
+  }
+}
+
+// Combine the splits of every (b, query, h): fixed order, tree split first.
+template <class ET>
+__global__ void attn_merge_kernel(AttnArgs a) {
+  using S = typename ET::storage;
+  const int i = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int x = threadIdx.x;   // one dh element per thread
+  const int T = a.T, H = a.H, DH = a.Dh;
+  const int L = min(max(a.kv_len[b], 0), a.Lmax);
+  const int ns = 1 + (L + kAttnChunk - 1) / kAttnChunk;
+  const size_t base = ((size_t)b * H + h) * a.NS * T;
+  float M = kNegInf;
+  for (int s = 0; s < ns; ++s) M = fmaxf(M, a.part_ml[(base + (size_t)s * T + i) * 2]);
+  float l = 0.f, acc = 0.f;
+  for (int s = 0; s < ns; ++s) {
+    const size_t r = base + (size_t)s * T + i;
+    const float ms = a.part_ml[r * 2];
+    if (ms == kNegInf) continue;
+    const float w = __builtin_amdgcn_exp2f(ms - M);
+    l += w * a.part_ml[r * 2 + 1];
+    acc += w * a.part_o[r * DH + x];
+  }
+  const float ov = acc / l;
+  const size_t out = (((size_t)b * T + i) * H + h) * DH + x;
+  if (a.out) a.out[out] = ov;
+  if (a.out_elem) reinterpret_cast<S*>(a.out_elem)[out] = ET::from_float(ov);
+}
+
+template <class ET, int DH>
+hipError_t launch_dh(const AttnArgs& a, hipStream_t st) {
+  const int MQ = (a.T + 15) / 16;
+  const int QT = (MQ + 3) / 4;
+  dim3 grid(a.NS, a.H, a.B), block(256);
+  switch (QT) {
+    case 1: hipLaunchKernelGGL((tree_attn_kernel<ET, DH, 1>), grid, block, 0, st, a); break;
+    case 2: hipLaunchKernelGGL((tree_attn_kernel<ET, DH, 2>), grid, block, 0, st, a); break;
+    case 3: hipLaunchKernelGGL((tree_attn_kernel<ET, DH, 3>), grid, block, 0, st, a); break;
+    default: hipLaunchKernelGGL((tree_attn_kernel<ET, DH, 4>), grid, block, 0, st, a); break;
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(attn_merge_kernel<ET>, dim3(a.T, a.H, a.B), dim3(DH), 0, st, a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+int attn_splits(int Lmax) { return 1 + (Lmax + kAttnChunk - 1) / kAttnChunk; }
+
+hipError_t launch_tree_attention(const AttnArgs& a, hipStream_t st) {
+  if (a.f32) return a.Dh == 64 ? launch_dh<F32, 64>(a, st) : launch_dh<F32, 128>(a, st);
+  return a.Dh == 64 ? launch_dh<BF16, 64>(a, st) : launch_dh<BF16, 128>(a, st);
+}
+
+}  // namespace medusa

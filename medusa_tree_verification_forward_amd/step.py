@@ -1,0 +1,151 @@
+"""Device buffers and call sequence of one verify step (marshalling only).
+
+``VerifyStep`` allocates, with PyTorch on the GPU, every buffer the five C
+ABI calls of one step read or write, then issues them in order on one
+stream: heads -> tree -> verify forward -> posterior -> commit. All
+arithmetic happens in the HIP library.
+"""
+
+from __future__ import annotations
+
+from typing import Dict, Optional
+
+import numpy as np
+
+from . import _lib as L
+
+
+def to_device(x: np.ndarray, device="cuda"):
+    """numpy -> torch tensor on the GPU; uint16 arrays hold bf16 bit patterns."""
+    import torch
+    x = np.ascontiguousarray(x)
+    if x.dtype == np.uint16:
+        return torch.from_numpy(x.view(np.int16)).to(device).view(torch.bfloat16)
+    return torch.from_numpy(x).to(device)
+
+
+def to_host(t) -> np.ndarray:
+    import torch
+    t = t.detach()
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).cpu().numpy().view(np.uint16)
+    return t.cpu().numpy()
+
+
+class VerifyStep:
+    """One Medusa verify step on the GPU for fixed shapes.
+
+    inputs: dict of numpy arrays as produced by the workload generator
+    (h, W1, W2, E, W_qkv, W_o, W_lm, k_cache, v_cache, kv_len, root, ranks,
+    u_draft, u_accept, u_resample).
+    """
+
+    def __init__(self, inputs: Dict[str, np.ndarray], *, H: int, Dh: int, s_max: int,
+                 mode: str, tau: float, eps: float, delta: float, theta: float,
+                 want_logits: bool = False):
+        import torch
+        self.torch = torch
+        f32 = inputs["W2"].dtype == np.float32
+        K, V, d = inputs["W2"].shape
+        B = inputs["h"].shape[0]
+        ranks = np.ascontiguousarray(inputs["ranks"], dtype=np.int32)
+        N = ranks.shape[0]
+        T = N + 1
+        P = self._count_paths(ranks)
+        Lmax = inputs["k_cache"].shape[2]
+        self.shape = L.make_shape(B, d, V, K, H, Dh, Lmax, N, P, s_max, "f32" if f32 else "bf16")
+        self.B, self.T, self.K, self.V, self.d, self.P = B, T, K, V, d, P
+        self.mode, self.tau, self.eps, self.delta, self.theta = mode, tau, eps, delta, theta
+        self.ranks = ranks
+        dev = {k: to_device(v) for k, v in inputs.items()
+               if k not in ("ranks",) and isinstance(v, np.ndarray)}
+        self.inp = dev
+        self.kv_len0 = dev["kv_len"].clone()
+        i32, f = torch.int32, torch.float32
+        z = lambda shape, dt: torch.zeros(shape, dtype=dt, device="cuda")  # noqa: E731
+        exact = mode == "exact"
+        elem = torch.float32 if f32 else torch.bfloat16
+        self.out = dict(
+            topk_ids=z((B, K, s_max), i32), topk_logits=z((B, K, s_max), f),
+            head_lse=z((B, K), f),
+            head_logits=z((B, K, V), f) if (exact or want_logits) else None,
+            z=z((B, K, d), f),
+            tree_tokens=z((B, T), i32), tree_mask=z((T, T), torch.uint8),
+            position_ids=z((B, T), i32), retrieve=z((P, K + 1), i32), parent=z((T,), i32),
+            depth=z((T,), i32), k_tree=z((B, T, H, Dh), elem), v_tree=z((B, T, H, Dh), elem),
+            y=z((B, T, d), f), row_stats=z((B, T, 3), f), row_argmax=z((B, T), i32),
+            child_logit=z((B, T), f),
+            verify_logits=z((B, T, V), f) if (exact or want_logits) else None,
+            accept_len=z((B,), i32), best_path=z((B,), i32), last_node=z((B,), i32),
+            out_tokens=z((B, K + 1), i32), next_root=z((B,), i32), h_next=z((B, d), f),
+        )
+        self.ws = torch.zeros(L.workspace_bytes(self.shape), dtype=torch.uint8, device="cuda")
+
+    @staticmethod
+    def _count_paths(ranks: np.ndarray) -> int:
+        tuples = set()
+        for row in ranks:
+            t = tuple(int(r) for r in row if r >= 0)
+            tuples.add(t)
+        if not tuples:
+            return 1
+        parents = {t[:-1] for t in tuples}
+        return sum(1 for t in tuples if t not in parents)
+
+    # -- the five calls -------------------------------------------------------------
+    def heads(self, stream=None):
+        o, i = self.out, self.inp
+        L.heads_forward(self.shape, i["h"], i["W1"], i["W2"], o["topk_ids"], o["topk_logits"],
+                        self.ws, head_lse=o["head_lse"], head_logits=o["head_logits"], z=o["z"],
+                        stream=stream)
+
+    def tree(self, stream=None):
+        o, i = self.out, self.inp
+        sample = self.mode == "exact"
+        L.build_tree(self.shape, self.ranks, i["root"], i["kv_len"], o["tree_tokens"],
+                     o["tree_mask"], o["position_ids"], o["retrieve"], o["parent"], o["depth"],
+                     draft_mode=L.DRAFT_SAMPLE if sample else L.DRAFT_TOPK,
+                     topk_ids=o["topk_ids"], head_logits=o["head_logits"],
+                     head_lse=o["head_lse"], u_draft=i.get("u_draft") if sample else None,
+                     stream=stream)
+
+    def verify(self, stream=None):
+        o, i = self.out, self.inp
+        L.verify_forward(self.shape, i["E"], i["W_qkv"], i["W_o"], i["W_lm"], self.theta,
+                         o["tree_tokens"], o["position_ids"], o["tree_mask"], o["parent"],
+                         i["k_cache"], i["v_cache"], i["kv_len"], self.tau, o["k_tree"],
+                         o["v_tree"], o["y"], o["row_stats"], o["row_argmax"], o["child_logit"],
+                         self.ws, verify_logits=o["verify_logits"], stream=stream)
+
+    def posterior(self, stream=None):
+        o, i = self.out, self.inp
+        exact = self.mode == "exact"
+        L.evaluate_posterior(self.shape, self.mode, self.tau, self.eps, self.delta,
+                             o["row_stats"], o["row_argmax"], o["child_logit"],
+                             o["tree_tokens"], o["parent"], o["retrieve"], o["accept_len"],
+                             o["best_path"], o["last_node"], o["out_tokens"], o["next_root"],
+                             self.ws, verify_logits=o["verify_logits"] if exact else None,
+                             head_logits=o["head_logits"] if exact else None,
+                             head_lse=o["head_lse"] if exact else None,
+                             u_accept=i.get("u_accept") if exact else None,
+                             u_resample=i.get("u_resample") if exact else None, stream=stream)
+
+    def commit(self, stream=None):
+        o, i = self.out, self.inp
+        L.commit(self.shape, o["last_node"], o["parent"], o["k_tree"], o["v_tree"], o["y"],
+                 i["k_cache"], i["v_cache"], i["kv_len"], o["h_next"], stream=stream)
+
+    def reset_kv_len(self):
+        self.inp["kv_len"].copy_(self.kv_len0)
+
+    def run(self, stream=None, commit: bool = True):
+        """The whole step: heads, tree, verify forward, posterior, commit."""
+        self.heads(stream)
+        self.tree(stream)
+        self.verify(stream)
+        self.posterior(stream)
+        if commit:
+            self.commit(stream)
+
+    def results(self) -> Dict[str, np.ndarray]:
+        return {k: to_host(v) for k, v in self.out.items() if v is not None}

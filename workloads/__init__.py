@@ -16,8 +16,11 @@ Conventions
 -----------
 * bf16 tensors are numpy ``uint16`` arrays holding bf16 bit patterns
   (fp32 draws rounded to nearest-even). fp32 workloads keep ``float32``.
-* Every tensor has its own generator ``np.random.default_rng([seed, tid])``
-  with a fixed tensor id, so adding a tensor never shifts another one.
+* Every tensor has its own generators: ``np.random.default_rng([seed, tid,
+  sub, chunk])`` for each 2^20-element chunk of a Gaussian tensor (``sub``
+  is the sequence index for the KV cache, else 0), ``default_rng([seed,
+  tid])`` for the small integer and uniform draws; adding a tensor never
+  shifts another one, and the values do not depend on the thread count.
 * Weights are stored row-major ``[out][in]`` (``W1[k]`` is d x d, ``W2[k]``
   is V x d, ``W_qkv`` is 3d x d with the q, k, v blocks stacked, ``W_lm`` is
   V x d, the embedding ``E`` is V x d).
@@ -28,6 +31,8 @@ Conventions
 from __future__ import annotations
 
 import dataclasses
+import os
+from concurrent.futures import ThreadPoolExecutor
 from typing import Dict, Optional, Tuple
 
 import numpy as np
@@ -109,11 +114,16 @@ def scaled(w: Workload, **overrides) -> Workload:
 # --------------------------------------------------------------------------
 
 def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
-    """Round float32 to bf16 (nearest, ties to even); return uint16 bit patterns."""
+    """Round float32 to bf16 (nearest, ties to even); return uint16 bit patterns.
+
+    Finite inputs only (the sum below cannot wrap for them)."""
     x = np.ascontiguousarray(x, dtype=np.float32)
-    b = x.view(np.uint32).astype(np.uint64)
-    b = (b + 0x7FFF + ((b >> 16) & 1)) >> 16
-    return b.astype(np.uint16)
+    b = x.view(np.uint32)
+    r = (b >> 16) & np.uint32(1)
+    r += np.uint32(0x7FFF)
+    r += b
+    r >>= 16
+    return r.astype(np.uint16)
 
 
 def bf16_bits_to_f32(u: np.ndarray) -> np.ndarray:
@@ -126,19 +136,33 @@ def _rng(w: Workload, name: str) -> np.random.Generator:
     return np.random.default_rng([w.seed, TID[name]])
 
 
-def _normal(rng: np.random.Generator, shape, std: float, store: str,
-            chunk_rows: int = 4096) -> np.ndarray:
-    """N(0, std^2) draws, produced in row chunks to bound peak memory."""
+_CHUNK = 1 << 20   # elements per independent stream
+
+
+def _normal(w: Workload, name: str, shape, std: float, store: str, sub: int = 0) -> np.ndarray:
+    """N(0, std^2) draws for tensor `name`. The tensor is cut into fixed
+    chunks of 2^20 elements; chunk c uses its own stream
+    default_rng([seed, tensor id, sub, c]), so the values do not depend on
+    how many threads produce them."""
     shape = tuple(int(x) for x in shape)
-    rows = int(np.prod(shape[:-1])) if len(shape) > 1 else 1
-    cols = shape[-1]
-    out = np.empty((rows, cols), dtype=np.uint16 if store == "bf16" else np.float32)
-    for r0 in range(0, rows, chunk_rows):
-        r1 = min(rows, r0 + chunk_rows)
-        x = rng.standard_normal((r1 - r0, cols), dtype=np.float32)
+    total = int(np.prod(shape)) if shape else 1
+    out = np.empty(total, dtype=np.uint16 if store == "bf16" else np.float32)
+    nchunks = (total + _CHUNK - 1) // _CHUNK
+
+    def work(c):
+        lo, hi = c * _CHUNK, min(total, (c + 1) * _CHUNK)
+        x = np.random.default_rng([w.seed, TID[name], sub, c]).standard_normal(
+            hi - lo, dtype=np.float32)
         if std != 1.0:
             x *= np.float32(std)
-        out[r0:r1] = f32_to_bf16_bits(x) if store == "bf16" else x
+        out[lo:hi] = f32_to_bf16_bits(x) if store == "bf16" else x
+
+    if nchunks <= 1:
+        for c in range(nchunks):
+            work(c)
+    else:
+        with ThreadPoolExecutor(max_workers=min(16, os.cpu_count() or 1)) as ex:
+            list(ex.map(work, range(nchunks)))
     return out.reshape(shape)
 
 
@@ -231,32 +255,31 @@ def make_inputs(w: Workload, with_weights: bool = True,
     inv = 1.0 / np.sqrt(d)
     w1_std = w.w1_std if w.w1_std is not None else inv
     if want("W1"):
-        out["W1"] = _normal(_rng(w, "W1"), (K, d, d), w1_std, store)
+        out["W1"] = _normal(w, "W1", (K, d, d), w1_std, store)
     if want("W2"):
-        out["W2"] = _normal(_rng(w, "W2"), (K, V, d), inv, store)
+        out["W2"] = _normal(w, "W2", (K, V, d), inv, store)
     if want("E"):
-        out["E"] = _normal(_rng(w, "E"), (V, d), 1.0, store)
+        out["E"] = _normal(w, "E", (V, d), 1.0, store)
     if want("W_qkv"):
-        out["W_qkv"] = _normal(_rng(w, "W_qkv"), (3 * d, d), inv, store)
+        out["W_qkv"] = _normal(w, "W_qkv", (3 * d, d), inv, store)
     if want("W_o"):
-        out["W_o"] = _normal(_rng(w, "W_o"), (d, d), inv, store)
+        out["W_o"] = _normal(w, "W_o", (d, d), inv, store)
     if want("W_lm"):
         if w.entropy_target is None:
-            out["W_lm"] = _normal(_rng(w, "W_lm"), (V, d), inv, store)
+            out["W_lm"] = _normal(w, "W_lm", (V, d), inv, store)
         else:
-            raw = _rng(w, "W_lm").standard_normal((V, d), dtype=np.float32)
-            raw *= np.float32(inv)
+            raw = _normal(w, "W_lm", (V, d), inv, "f32")
             alpha = _lm_scale_for_entropy(raw, out["h"][0], w.entropy_target)
             raw *= np.float32(alpha)
             out["W_lm"] = f32_to_bf16_bits(raw) if store == "bf16" else raw
     for name in ("K", "V"):
         if want("k_cache" if name == "K" else "v_cache"):
-            rng = _rng(w, name)
             cache = np.zeros((B, H, Lmax, Dh),
                              dtype=np.uint16 if store == "bf16" else np.float32)
             for b in range(B):
                 L = int(kv_len[b])
-                cache[b, :, :L, :] = _normal(rng, (H, L, Dh), 1.0, store)
+                if L > 0:
+                    cache[b, :, :L, :] = _normal(w, name, (H, L, Dh), 1.0, store, sub=b)
             out["k_cache" if name == "K" else "v_cache"] = cache
 
     for name in ("u_draft", "u_accept", "u_resample"):
