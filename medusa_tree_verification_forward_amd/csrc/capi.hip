@@ -64,7 +64,7 @@ int env_int(const char* name, int dflt, int lo, int hi) {
 // Tuning knobs (rows per workgroup of the head streams). Workspace sizes are
 // computed for the smallest allowed value, so any setting fits.
 constexpr int kMinW2Rows = 16;
-int w1_rows() { static int v = env_int("MEDUSA_W1_ROWS", 64, 4, 4096); return v; }
+int w1_rows() { static int v = env_int("MEDUSA_W1_ROWS", 16, 4, 4096); return v; }
 int w2_rows() { static int v = env_int("MEDUSA_W2_ROWS", 128, kMinW2Rows, 65536); return v; }
 
 int check_shape(const medusa_shape* s) {
@@ -103,7 +103,7 @@ struct Layout {
   size_t att_o = 0, att_ml = 0;
   int NS = 0;
   // verify
-  size_t q = 0, o_elem = 0, y_elem = 0, lm_part = 0;
+  size_t q = 0, o_elem = 0, y_elem = 0, lm_part = 0, gemm_part = 0;
   // posterior (exact)
   size_t pw = 0;
   size_t total = 0;
@@ -135,6 +135,12 @@ Layout layout_for(const medusa_shape* s) {
   L.o_elem = take(B * T * d * es);
   L.y_elem = take(B * T * d * es);
   L.lm_part = take(B * T * lm_head_blocks(s->V) * 4 * 4);
+  {
+    const bool f32 = s->dtype == MEDUSA_F32;
+    const size_t q_need = (size_t)gemm_splits(3 * s->d, s->d, f32) * B * T * 3 * d;
+    const size_t o_need = (size_t)gemm_splits(s->d, s->d, f32) * B * T * d;
+    L.gemm_part = take((q_need > o_need ? q_need : o_need) * 4);
+  }
   L.pw = take(B * V * 4);
   L.total = off;
   return L;
@@ -438,6 +444,7 @@ int medusa_verify_forward(const medusa_shape* shape, const void* E, const void* 
   g.q_out = at<char>(workspace, L.q);
   g.k_out = k_tree_out;
   g.v_out = v_tree_out;
+  g.part = at<float>(workspace, L.gemm_part);
   hipError_t e = launch_qkv(g, st);
   if (e != hipSuccess) return hip_fail(e, "qkv launch");
   // 2. tree attention, output rounded to the storage type

@@ -80,6 +80,57 @@ __device__ __forceinline__ u32x4_t load16_stream(const void* p) {
   return __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
 }
 
+// ---- direct global -> LDS loads (gfx950) ---------------------------------------
+// Each lane names one 16-byte piece in global memory; the wave's 64 pieces
+// land in LDS contiguously at `lds` (lane-major), without passing through
+// VGPRs. Completion is tracked by the vector-memory counter, so a reader of
+// that LDS must first wait with vmcnt() below.
+typedef __attribute__((address_space(3))) void lds_void_t;
+__device__ __forceinline__ void dma16(const void* g, void* lds) {
+  __builtin_amdgcn_global_load_lds(const_cast<void*>(g), (lds_void_t*)lds, 16, 0, 0);
+}
+// Wait until at most N vector-memory operations of this wave are in flight
+// (GFX9 s_waitcnt encoding: vmcnt low bits [3:0] and high bits [15:14];
+// expcnt and lgkmcnt left at their maxima, i.e. not waited on).
+template <int N>
+__device__ __forceinline__ void vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
+// vmcnt() with a run-time count (0..63), for pipelines whose tail issues
+// fewer loads than their steady state.
+__device__ __forceinline__ void vmcnt_rt(int n) {
+  switch (n) {
+#define MEDUSA_VMCNT_CASE(N) \
+  case N:                    \
+    vmcnt<N>();              \
+    break;
+    MEDUSA_VMCNT_CASE(0) MEDUSA_VMCNT_CASE(1) MEDUSA_VMCNT_CASE(2) MEDUSA_VMCNT_CASE(3)
+    MEDUSA_VMCNT_CASE(4) MEDUSA_VMCNT_CASE(5) MEDUSA_VMCNT_CASE(6) MEDUSA_VMCNT_CASE(7)
+    MEDUSA_VMCNT_CASE(8) MEDUSA_VMCNT_CASE(9) MEDUSA_VMCNT_CASE(10) MEDUSA_VMCNT_CASE(11)
+    MEDUSA_VMCNT_CASE(12) MEDUSA_VMCNT_CASE(13) MEDUSA_VMCNT_CASE(14) MEDUSA_VMCNT_CASE(15)
+    MEDUSA_VMCNT_CASE(16) MEDUSA_VMCNT_CASE(17) MEDUSA_VMCNT_CASE(18) MEDUSA_VMCNT_CASE(19)
+    MEDUSA_VMCNT_CASE(20) MEDUSA_VMCNT_CASE(21) MEDUSA_VMCNT_CASE(22) MEDUSA_VMCNT_CASE(23)
+    MEDUSA_VMCNT_CASE(24) MEDUSA_VMCNT_CASE(25) MEDUSA_VMCNT_CASE(26) MEDUSA_VMCNT_CASE(27)
+    MEDUSA_VMCNT_CASE(28) MEDUSA_VMCNT_CASE(29) MEDUSA_VMCNT_CASE(30) MEDUSA_VMCNT_CASE(31)
+#undef MEDUSA_VMCNT_CASE
+    default:
+      vmcnt<0>();   // conservative: wait for everything
+      break;
+  }
+}
+
+// Workgroup barrier for LDS-DMA pipelines: s_barrier without the release /
+// acquire fence of __syncthreads(), which would drain every outstanding
+// direct-to-LDS load (vmcnt 0). The caller waits for its own loads first
+// (vmcnt); the compiler-only fences keep LDS accesses on their side.
+__device__ __forceinline__ void stage_barrier() {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_barrier();
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
 // ---- DPP wave reductions ----------------------------------------------------
 // DPP control codes (GFX9 encoding).
 constexpr int kDppQuadXor1 = 0xB1;   // quad_perm [1,0,3,2]

@@ -277,7 +277,28 @@ __global__ __launch_bounds__(WAVES * 64) void heads_w2_kernel(
 
 // ---------------------------------------------------------------------------
 // Merge the G partial records of one (sequence, head): one wavefront.
-// grid = (K, B).
+// grid = (K, B). Each lane keeps a private sorted list of its candidates in
+// registers (a candidate that does not beat the lane's S-th entry costs one
+// compare); then S selection rounds take the best lane head with a DPP
+// (value desc, id asc) reduction and pop it from its lane.
+template <int SMAX>
+__device__ __forceinline__ void reg_insert(float (&lv)[SMAX], int (&li)[SMAX], float v, int id,
+                                           int S) {
+#pragma unroll
+  for (int j = SMAX - 1; j >= 0; --j) {
+    if (j >= S) continue;
+    if (!better(v, id, lv[j], li[j])) continue;
+    if (j > 0 && better(v, id, lv[j - 1], li[j - 1])) {
+      lv[j] = lv[j - 1];
+      li[j] = li[j - 1];
+    } else {
+      lv[j] = v;
+      li[j] = id;
+    }
+  }
+}
+
+template <int SMAX>
 __global__ __launch_bounds__(64) void heads_merge_kernel(
     int K, int G, int S, const float* __restrict__ part_val, const int* __restrict__ part_id,
     const float* __restrict__ part_m, const float* __restrict__ part_s,
@@ -285,32 +306,76 @@ __global__ __launch_bounds__(64) void heads_merge_kernel(
   const int k = blockIdx.x, b = blockIdx.y;
   const int lane = threadIdx.x;
   const size_t rec0 = ((size_t)b * K + k) * G;
-  float tv = kNegInf;
-  int ti = kNoId;
+  float lv[SMAX];
+  int li[SMAX];
+#pragma unroll
+  for (int j = 0; j < SMAX; ++j) {
+    lv[j] = kNegInf;
+    li[j] = kNoId;
+  }
   const int ncand = G * S;
-  for (int c0 = 0; c0 < ncand; c0 += 64) {
-    const int c = c0 + lane;
-    const float v = c < ncand ? part_val[rec0 * S + c] : kNegInf;
-    const int id = c < ncand ? part_id[rec0 * S + c] : kNoId;
-    float thv = readlane_f(tv, S - 1);
-    int thi = __builtin_amdgcn_readlane(ti, S - 1);
-    uint64_t mask = __ballot(better(v, id, thv, thi));
-    while (mask) {
-      const int j = __ffsll((unsigned long long)mask) - 1;
-      mask &= mask - 1;
-      const float cv = readlane_f(v, j);
-      const int ci = __builtin_amdgcn_readlane(id, j);
-      if (better(cv, ci, thv, thi)) {
-        list_insert(tv, ti, cv, ci, S);
-        thv = readlane_f(tv, S - 1);
-        thi = __builtin_amdgcn_readlane(ti, S - 1);
+  for (int c = lane; c < ncand; c += 64) {
+    const float v = part_val[rec0 * S + c];
+    const int id = part_id[rec0 * S + c];
+    // the S-th entry sits at a runtime index: select it with an unrolled scan
+    float tv = kNegInf;
+    int ti = kNoId;
+#pragma unroll
+    for (int j = 0; j < SMAX; ++j)
+      if (j == S - 1) {
+        tv = lv[j];
+        ti = li[j];
       }
+    if (better(v, id, tv, ti)) reg_insert<SMAX>(lv, li, v, id, S);
+  }
+  float out_v = kNegInf;
+  int out_i = kNoId;
+  for (int r = 0; r < S; ++r) {
+    float bv = lv[0];
+    int bi = li[0];
+#pragma unroll
+    for (int step = 0; step < 4; ++step) {
+      float ov;
+      int oi;
+      if (step == 0) { ov = dpp<kDppQuadXor1>(bv); oi = dppi<kDppQuadXor1>(bi); }
+      else if (step == 1) { ov = dpp<kDppQuadXor2>(bv); oi = dppi<kDppQuadXor2>(bi); }
+      else if (step == 2) { ov = dpp<kDppRowRor4>(bv); oi = dppi<kDppRowRor4>(bi); }
+      else { ov = dpp<kDppRowRor8>(bv); oi = dppi<kDppRowRor8>(bi); }
+      if (better(ov, oi, bv, bi)) { bv = ov; bi = oi; }
+    }
+    // best of the four 16-lane rows (uniform)
+    float wv = readlane_f(bv, 0);
+    int wi = __builtin_amdgcn_readlane(bi, 0);
+#pragma unroll
+    for (int row = 16; row < 64; row += 16) {
+      const float ov = readlane_f(bv, row);
+      const int oi = __builtin_amdgcn_readlane(bi, row);
+      if (better(ov, oi, wv, wi)) {
+        wv = ov;
+        wi = oi;
+      }
+    }
+    bv = wv;
+    bi = wi;
+    if (lane == r) {
+      out_v = bv;
+      out_i = bi;
+    }
+    // pop the winner from the lane that holds it (ids are unique)
+    if (li[0] == bi) {
+#pragma unroll
+      for (int j = 0; j < SMAX - 1; ++j) {
+        lv[j] = lv[j + 1];
+        li[j] = li[j + 1];
+      }
+      lv[SMAX - 1] = kNegInf;
+      li[SMAX - 1] = kNoId;
     }
   }
   const size_t out = ((size_t)b * K + k) * S;
   if (lane < S) {
-    topk_ids[out + lane] = ti;
-    topk_logits[out + lane] = tv;
+    topk_ids[out + lane] = out_i;
+    topk_logits[out + lane] = out_v;
   }
   if (lse) {
     float mm = kNegInf;
@@ -370,9 +435,17 @@ hipError_t launch_heads_et(const HeadsArgs& a, hipStream_t st) {
       e = launch_heads_nb<ET, 8>(a, b0, st);
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL(heads_merge_kernel, dim3(a.K, a.B), dim3(64), 0, st, a.K, a.G, a.S,
-                     a.part_val, a.part_id, a.part_m, a.part_s, a.topk_ids, a.topk_logits,
-                     a.lse);
+#define MERGE_LAUNCH(SM)                                                                    \
+  hipLaunchKernelGGL(heads_merge_kernel<SM>, dim3(a.K, a.B), dim3(64), 0, st, a.K, a.G, a.S, \
+                     a.part_val, a.part_id, a.part_m, a.part_s, a.topk_ids, a.topk_logits,   \
+                     a.lse)
+  if (a.S <= 4)
+    MERGE_LAUNCH(4);
+  else if (a.S <= 8)
+    MERGE_LAUNCH(8);
+  else
+    MERGE_LAUNCH(16);
+#undef MERGE_LAUNCH
   return hipGetLastError();
 }
 

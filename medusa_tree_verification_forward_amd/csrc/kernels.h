@@ -90,19 +90,20 @@ struct GemmParams {
   void* y_elem;                // [M][N] storage type
   // LM epilogue
   float inv_tau;
-  float* part;                 // [M][blocks][4]
+  float* part;                 // LM: [M][blocks][4]; QKV/OPROJ: [KS][M][N] partials
   const int32_t* parent;       // [T]
   float* child_logit;          // [M]
   float* logits_out;           // [M][N] or null
 };
 int lm_head_blocks(int N);
+int gemm_splits(int N, int K, bool f32);   // K slices of the QKV / output projection GEMMs
 hipError_t launch_qkv(const GemmParams& p, hipStream_t st);
 hipError_t launch_oproj(const GemmParams& p, hipStream_t st);
 hipError_t launch_lm_head(const GemmParams& p, float* row_stats, int* row_argmax,
                           hipStream_t st);
 
 // ---- tree attention ---------------------------------------------------------------
-constexpr int kAttnChunk = 256;   // prefix keys per split
+constexpr int kAttnChunk = 128;   // prefix keys per split
 struct AttnArgs {
   bool f32;
   int B, T, H, Dh, Lmax;

@@ -295,9 +295,15 @@ __global__ __launch_bounds__(1024) void posterior_exact_kernel(PostArgs a) {
 }
 
 // ---- commit ----------------------------------------------------------------------
+// One 1024-thread workgroup per sequence; the path's K/V rows are copied as
+// 16-byte vectors (a node's row [H][Dh] is contiguous in the tree buffers, a
+// head's row Dh is contiguous in the cache), so each thread moves a few
+// vectors and the copy is bound by one round trip to memory, not by a chain
+// of dependent element copies.
 template <class ET>
-__global__ __launch_bounds__(256) void commit_kernel(CommitArgs a) {
+__global__ __launch_bounds__(1024) void commit_kernel(CommitArgs a) {
   using S = typename ET::storage;
+  constexpr int PV = ET::kPerVec;
   const int b = blockIdx.x;
   const int T = a.T, H = a.H, Dh = a.Dh;
   __shared__ int path[MAXK + 1];
@@ -318,23 +324,26 @@ __global__ __launch_bounds__(256) void commit_kernel(CommitArgs a) {
   const int L = sh_L, d = sh_depth;
   const bool room = L >= 0 && L + d + 1 <= a.Lmax;
   if (room) {
-    const S* kt = reinterpret_cast<const S*>(a.k_tree);
-    const S* vt = reinterpret_cast<const S*>(a.v_tree);
-    S* kc = reinterpret_cast<S*>(a.k_cache);
-    S* vc = reinterpret_cast<S*>(a.v_cache);
-    const int per_row = H * Dh;
-    const int total = (d + 1) * per_row;
+    const int vec_row = H * Dh / PV;          // 16-byte vectors per node row
+    const int vec_head = Dh / PV;             // per head
+    const int total = (d + 1) * vec_row;
+    const u32x4_t* kt = reinterpret_cast<const u32x4_t*>(a.k_tree);
+    const u32x4_t* vt = reinterpret_cast<const u32x4_t*>(a.v_tree);
+    u32x4_t* kc = reinterpret_cast<u32x4_t*>(a.k_cache);
+    u32x4_t* vc = reinterpret_cast<u32x4_t*>(a.v_cache);
     for (int e = threadIdx.x; e < total; e += blockDim.x) {
-      const int i = e / per_row, rem = e - i * per_row;
-      const int hh = rem / Dh, x = rem - hh * Dh;
-      const size_t src = (((size_t)b * T + path[i]) * H + hh) * Dh + x;
-      const size_t dst = (((size_t)b * H + hh) * a.Lmax + L + i) * Dh + x;
-      kc[dst] = kt[src];
-      vc[dst] = vt[src];
+      const int i = e / vec_row, rem = e - i * vec_row;
+      const int hh = rem / vec_head, x = rem - hh * vec_head;
+      const size_t src = ((size_t)b * T + path[i]) * vec_row + rem;
+      const size_t dst = (((size_t)b * H + hh) * a.Lmax + L + i) * vec_head + x;
+      const u32x4_t kv = kt[src], vv = vt[src];
+      kc[dst] = kv;
+      vc[dst] = vv;
     }
   }
-  const float* y = a.y + ((size_t)b * T + path[d]) * a.d;
-  for (int e = threadIdx.x; e < a.d; e += blockDim.x) a.h_next[(size_t)b * a.d + e] = y[e];
+  const float4* y = reinterpret_cast<const float4*>(a.y + ((size_t)b * T + path[d]) * a.d);
+  float4* hn = reinterpret_cast<float4*>(a.h_next + (size_t)b * a.d);
+  for (int e = threadIdx.x; e < a.d / 4; e += blockDim.x) hn[e] = y[e];
   __syncthreads();
   if (threadIdx.x == 0) a.kv_len[b] = room ? L + d + 1 : -1;
 }
@@ -351,9 +360,9 @@ hipError_t launch_posterior(const PostArgs& a, hipStream_t st) {
 
 hipError_t launch_commit(const CommitArgs& a, hipStream_t st) {
   if (a.f32)
-    hipLaunchKernelGGL(commit_kernel<F32>, dim3(a.B), dim3(256), 0, st, a);
+    hipLaunchKernelGGL(commit_kernel<F32>, dim3(a.B), dim3(1024), 0, st, a);
   else
-    hipLaunchKernelGGL(commit_kernel<BF16>, dim3(a.B), dim3(256), 0, st, a);
+    hipLaunchKernelGGL(commit_kernel<BF16>, dim3(a.B), dim3(1024), 0, st, a);
   return hipGetLastError();
 }
 

@@ -28,56 +28,57 @@ __global__ __launch_bounds__(256) void tree_kernel(TreeArgs a) {
   const int b = blockIdx.x;
   const int n = threadIdx.x;
   const int T = a.plan.T, K = a.plan.K;
-  __shared__ uint8_t tup[MAXT][MAXK];
-  __shared__ int dep[MAXT];
-  __shared__ int has_child[MAXT];
+  __shared__ uint8_t par[MAXT], lrank[MAXT], dep[MAXT], has_child[MAXT];
+  __shared__ uint8_t anc[MAXT][MAXK + 1];   // anc[n][k]: n's ancestor at depth k (k <= depth)
+  __shared__ uint8_t tup[MAXT][MAXK];       // n's rank path
   if (n < T) {
-    int d = 0;
-    for (int x = n; x != 0; x = a.plan.parent[x]) ++d;
-    dep[n] = d;
-    int x = n;
-    for (int j = d - 1; j >= 0; --j) {
-      tup[n][j] = a.plan.last_rank[x];
-      x = a.plan.parent[x];
-    }
+    par[n] = a.plan.parent[n];
+    lrank[n] = a.plan.last_rank[n];
     has_child[n] = 0;
   }
   __syncthreads();
-  if (n >= 1 && n < T) has_child[a.plan.parent[n]] = 1;
-  __syncthreads();
-  if (n >= T) return;
-  const int d = dep[n];
-
-  int tok;
-  if (n == 0)
-    tok = a.root_tok[b];
-  else if (a.sample)
-    tok = -1;   // drawn by tree_sample_kernel
-  else
-    tok = a.topk_ids[((size_t)b * K + (d - 1)) * a.S + a.plan.last_rank[n]];
-  a.tokens[(size_t)b * T + n] = tok;
-  a.position_ids[(size_t)b * T + n] = a.kv_len[b] + d;
-
-  if (b != 0) return;   // the topology is shared by every sequence
-  a.parent[n] = n == 0 ? -1 : (int)a.plan.parent[n];
-  a.depth[n] = d;
-  uint8_t* row = a.mask + (size_t)n * T;
-  for (int j = 0; j < T; ++j) row[j] = 0;
-  for (int x = n;; x = a.plan.parent[x]) {
-    row[x] = 1;
-    if (x == 0) break;
+  if (n < T) {
+    int d = 0;
+    for (int x = n; x != 0 && d < K; x = par[x]) ++d;
+    dep[n] = (uint8_t)d;
+    int x = n;
+    anc[n][d] = (uint8_t)n;
+    for (int j = d - 1; j >= 0; --j) {
+      tup[n][j] = lrank[x];
+      x = par[x];
+      anc[n][j] = (uint8_t)x;
+    }
+    if (n >= 1) has_child[par[n]] = 1;
   }
+  __syncthreads();
+  const int d = n < T ? dep[n] : 0;
+  if (n < T) {
+    int tok;
+    if (n == 0)
+      tok = a.root_tok[b];
+    else if (a.sample)
+      tok = -1;   // drawn by tree_sample_kernel
+    else
+      tok = a.topk_ids[((size_t)b * K + (d - 1)) * a.S + lrank[n]];
+    a.tokens[(size_t)b * T + n] = tok;
+    a.position_ids[(size_t)b * T + n] = a.kv_len[b] + d;
+  }
+  if (b != 0) return;   // the topology is shared by every sequence
+  // mask[i][j] = j is i or an ancestor of i, written cooperatively
+  for (int e = n; e < T * T; e += blockDim.x) {
+    const int i = e / T, j = e - i * T;
+    a.mask[e] = (dep[j] <= dep[i] && anc[i][dep[j]] == j) ? 1 : 0;
+  }
+  if (n >= T) return;
+  a.parent[n] = n == 0 ? -1 : (int)par[n];
+  a.depth[n] = d;
   const bool leaf = T == 1 ? true : (n >= 1 && !has_child[n]);
   if (!leaf) return;
   int p = 0;
   for (int m = 1; m < T; ++m)
     if (m != n && !has_child[m] && lex_less(tup[m], dep[m], tup[n], d)) ++p;
   int32_t* r = a.retrieve + (size_t)p * (K + 1);
-  int x = n;
-  for (int j = d; j >= 0; --j) {
-    r[j] = x;
-    x = a.plan.parent[x];
-  }
+  for (int j = 0; j <= d; ++j) r[j] = anc[n][j];
   for (int j = d + 1; j <= K; ++j) r[j] = -1;
 }
 

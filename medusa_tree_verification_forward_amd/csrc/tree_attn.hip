@@ -27,16 +27,21 @@ namespace medusa {
 namespace {
 
 constexpr float kNegInf = -__builtin_huge_valf();
-constexpr int SUB = 64;        // keys per sub-chunk
-constexpr int VPAD = 8;        // LDS row padding (elements) of V^T
 
-template <class ET, int DH, int QT>
+// SC keys are staged per round: all K rows (row-major, padded by 16 bytes)
+// and V transposed (padded) go to LDS with every global load of the round
+// in flight at once, then the waves compute from LDS.
+template <class ET, int DH, int QT, int SC>
 __global__ __launch_bounds__(256) void tree_attn_kernel(AttnArgs a) {
   using S = typename ET::storage;
   constexpr int PV = ET::kPerVec;
   constexpr bool BF = PV == 8;
   constexpr int DS = DH / (4 * PV);   // 16-byte steps along Dh per lane group
   constexpr int DT = DH / 16;         // dh tiles of the output
+  constexpr int KT = SC / 16;         // key tiles per round
+  constexpr int PAD = 16 / sizeof(S); // 16 bytes of padding per LDS row
+  constexpr int VEC_PER_KEY = DH / PV;
+  constexpr int LOADS = SC * VEC_PER_KEY / 256;   // 16-byte loads per thread per tensor
   const int s = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const int T = a.T, H = a.H;
   const int L = min(max(a.kv_len[b], 0), a.Lmax);
@@ -56,20 +61,21 @@ __global__ __launch_bounds__(256) void tree_attn_kernel(AttnArgs a) {
   const float sl2 = a.scale * 1.4426950408889634f;
 
   const S* __restrict__ q = reinterpret_cast<const S*>(a.q);
-  const S* __restrict__ kt_src;
-  const S* __restrict__ vt_src;
-  size_t krow_stride;   // elements between consecutive keys
+  const S* __restrict__ k_src;
+  const S* __restrict__ v_src;
+  size_t krow;   // elements between consecutive keys
   if (tree) {
-    kt_src = reinterpret_cast<const S*>(a.k_tree) + ((size_t)b * T * H + h) * DH;
-    vt_src = reinterpret_cast<const S*>(a.v_tree) + ((size_t)b * T * H + h) * DH;
-    krow_stride = (size_t)H * DH;
+    k_src = reinterpret_cast<const S*>(a.k_tree) + ((size_t)b * T * H + h) * DH;
+    v_src = reinterpret_cast<const S*>(a.v_tree) + ((size_t)b * T * H + h) * DH;
+    krow = (size_t)H * DH;
   } else {
-    kt_src = reinterpret_cast<const S*>(a.k_cache) + ((size_t)b * H + h) * a.Lmax * DH;
-    vt_src = reinterpret_cast<const S*>(a.v_cache) + ((size_t)b * H + h) * a.Lmax * DH;
-    krow_stride = DH;
+    k_src = reinterpret_cast<const S*>(a.k_cache) + ((size_t)b * H + h) * a.Lmax * DH;
+    v_src = reinterpret_cast<const S*>(a.v_cache) + ((size_t)b * H + h) * a.Lmax * DH;
+    krow = DH;
   }
 
-  __shared__ S vt[DH][SUB + VPAD];
+  __shared__ S ks[SC][DH + PAD];
+  __shared__ S vt[DH][SC + PAD];
 
   // Q fragments of my query tiles (B operand: lane = query, 16 B along Dh)
   u32x4_t qf[QT][DS];
@@ -88,23 +94,33 @@ __global__ __launch_bounds__(256) void tree_attn_kernel(AttnArgs a) {
     l_run[u] = 0.f;
   }
 
-  for (int kb = kbeg; kb < kend; kb += SUB) {
-    // ---- stage V^T of this sub-chunk (keys past the range read a valid row) ----
+  for (int kb = kbeg; kb < kend; kb += SC) {
+    if (kb > kbeg) __syncthreads();   // previous round's readers are done
+    // ---- stage K and V^T (keys past the range read a valid row; masked later) ----
     {
-      constexpr int VEC_PER_KEY = DH / PV;
-      for (int c = threadIdx.x; c < SUB * VEC_PER_KEY; c += 256) {
+      u32x4_t kv[LOADS], vv[LOADS];
+#pragma unroll
+      for (int i = 0; i < LOADS; ++i) {
+        const int c = threadIdx.x + 256 * i;
         const int kk = c / VEC_PER_KEY, part = c - kk * VEC_PER_KEY;
-        const int key = min(kb + kk, kend - 1);
-        const u32x4_t v = load16(vt_src + (size_t)key * krow_stride + PV * part);
+        const size_t off = (size_t)min(kb + kk, kend - 1) * krow + PV * part;
+        kv[i] = load16(k_src + off);
+        vv[i] = load16(v_src + off);
+      }
+#pragma unroll
+      for (int i = 0; i < LOADS; ++i) {
+        const int c = threadIdx.x + 256 * i;
+        const int kk = c / VEC_PER_KEY, part = c - kk * VEC_PER_KEY;
+        *reinterpret_cast<u32x4_t*>(&ks[kk][PV * part]) = kv[i];
         if constexpr (BF) {
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            vt[PV * part + 2 * e][kk] = (S)(v[e] & 0xffffu);
-            vt[PV * part + 2 * e + 1][kk] = (S)(v[e] >> 16);
+            vt[PV * part + 2 * e][kk] = (S)(vv[i][e] & 0xffffu);
+            vt[PV * part + 2 * e + 1][kk] = (S)(vv[i][e] >> 16);
           }
         } else {
 #pragma unroll
-          for (int e = 0; e < 4; ++e) vt[PV * part + e][kk] = __uint_as_float(v[e]);
+          for (int e = 0; e < 4; ++e) vt[PV * part + e][kk] = __uint_as_float(vv[i][e]);
         }
       }
     }
@@ -115,16 +131,15 @@ __global__ __launch_bounds__(256) void tree_attn_kernel(AttnArgs a) {
       const int qt = wave + 4 * u;
       if (qt >= MQ) break;
       const int query = 16 * qt + li;
-      // ---- S^T = K Q^T over 4 key tiles ----
-      floatx4_t st[4];
+      // ---- S^T = K Q^T over the round's key tiles ----
+      floatx4_t st[KT];
 #pragma unroll
-      for (int kt = 0; kt < 4; ++kt) {
+      for (int kt = 0; kt < KT; ++kt) {
         st[kt] = floatx4_t{0.f, 0.f, 0.f, 0.f};
-        const int key = min(kb + 16 * kt + li, kend - 1);
-        const S* kp = kt_src + (size_t)key * krow_stride + PV * lq;
+        const S* kp = &ks[16 * kt + li][PV * lq];
 #pragma unroll
         for (int ds = 0; ds < DS; ++ds) {
-          const u32x4_t kf = load16(kp + 4 * PV * ds);
+          const u32x4_t kf = *reinterpret_cast<const u32x4_t*>(kp + 4 * PV * ds);
           if constexpr (BF) {
             st[kt] = mfma16x16x32_bf16(kf, qf[u][ds], st[kt]);
           } else {
@@ -139,7 +154,7 @@ __global__ __launch_bounds__(256) void tree_attn_kernel(AttnArgs a) {
       const uint8_t* mrow = a.mask + (size_t)min(query, T - 1) * T;
       float mx = kNegInf;
 #pragma unroll
-      for (int kt = 0; kt < 4; ++kt)
+      for (int kt = 0; kt < KT; ++kt)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int key = kb + 16 * kt + 4 * lq + r;
@@ -155,7 +170,7 @@ __global__ __launch_bounds__(256) void tree_attn_kernel(AttnArgs a) {
       const float alpha = m_new == kNegInf ? 1.f : __builtin_amdgcn_exp2f(m_run[u] - m_new);
       float ls = 0.f;
 #pragma unroll
-      for (int kt = 0; kt < 4; ++kt)
+      for (int kt = 0; kt < KT; ++kt)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const float pv = m_new == kNegInf ? 0.f : __builtin_amdgcn_exp2f(st[kt][r] - m_new);
@@ -173,7 +188,7 @@ __global__ __launch_bounds__(256) void tree_attn_kernel(AttnArgs a) {
       // ---- O^T += V^T P^T ----
       if constexpr (BF) {
 #pragma unroll
-        for (int t = 0; t < 2; ++t) {
+        for (int t = 0; t < KT / 2; ++t) {
           u32x4_t pf;
           pf[0] = pack_bf16x2(st[2 * t][0], st[2 * t][1]);
           pf[1] = pack_bf16x2(st[2 * t][2], st[2 * t][3]);
@@ -194,7 +209,7 @@ __global__ __launch_bounds__(256) void tree_attn_kernel(AttnArgs a) {
         }
       } else {
 #pragma unroll
-        for (int kt = 0; kt < 4; ++kt)
+        for (int kt = 0; kt < KT; ++kt)
 #pragma unroll
           for (int dt = 0; dt < DT; ++dt) {
             const float4 vr = *reinterpret_cast<const float4*>(&vt[16 * dt + li][16 * kt + 4 * lq]);
@@ -205,7 +220,6 @@ __global__ __launch_bounds__(256) void tree_attn_kernel(AttnArgs a) {
           }
       }
     }
-    __syncthreads();
   }
 
   // ---- partial (m, l, O) per query ----
@@ -229,6 +243,10 @@ __global__ __launch_bounds__(256) void tree_attn_kernel(AttnArgs a) {
 }
 
 // Combine the splits of every (b, query, h): fixed order, tree split first.
+// The (m, l) pairs of up to kMaxSplitsFast splits are loaded together, then
+// the O rows, so each thread waits for two rounds of loads, not one per
+// split.
+constexpr int kMaxSplitsFast = 48;
 template <class ET>
 __global__ void attn_merge_kernel(AttnArgs a) {
   using S = typename ET::storage;
@@ -237,17 +255,36 @@ __global__ void attn_merge_kernel(AttnArgs a) {
   const int T = a.T, H = a.H, DH = a.Dh;
   const int L = min(max(a.kv_len[b], 0), a.Lmax);
   const int ns = 1 + (L + kAttnChunk - 1) / kAttnChunk;
-  const size_t base = ((size_t)b * H + h) * a.NS * T;
-  float M = kNegInf;
-  for (int s = 0; s < ns; ++s) M = fmaxf(M, a.part_ml[(base + (size_t)s * T + i) * 2]);
-  float l = 0.f, acc = 0.f;
-  for (int s = 0; s < ns; ++s) {
-    const size_t r = base + (size_t)s * T + i;
-    const float ms = a.part_ml[r * 2];
-    if (ms == kNegInf) continue;
-    const float w = __builtin_amdgcn_exp2f(ms - M);
-    l += w * a.part_ml[r * 2 + 1];
-    acc += w * a.part_o[r * DH + x];
+  const size_t base = ((size_t)b * H + h) * a.NS * T + i;
+  float M = kNegInf, l = 0.f, acc = 0.f;
+  for (int s0 = 0; s0 < ns; s0 += kMaxSplitsFast) {
+    const int n = min(kMaxSplitsFast, ns - s0);
+    float ms[kMaxSplitsFast], lsv[kMaxSplitsFast], os[kMaxSplitsFast];
+#pragma unroll
+    for (int j = 0; j < kMaxSplitsFast; ++j) {
+      if (j < n) {
+        const size_t r = base + (size_t)(s0 + j) * T;
+        ms[j] = a.part_ml[r * 2];
+        lsv[j] = a.part_ml[r * 2 + 1];
+        os[j] = a.part_o[r * DH + x];
+      }
+    }
+    float Mn = M;
+#pragma unroll
+    for (int j = 0; j < kMaxSplitsFast; ++j)
+      if (j < n) Mn = fmaxf(Mn, ms[j]);
+    const float c = M == kNegInf ? 0.f : __builtin_amdgcn_exp2f(M - Mn);
+    l *= c;
+    acc *= c;
+#pragma unroll
+    for (int j = 0; j < kMaxSplitsFast; ++j) {
+      if (j < n && ms[j] != kNegInf) {
+        const float w = __builtin_amdgcn_exp2f(ms[j] - Mn);
+        l += w * lsv[j];
+        acc += w * os[j];
+      }
+    }
+    M = Mn;
   }
   const float ov = acc / l;
   const size_t out = (((size_t)b * T + i) * H + h) * DH + x;
@@ -257,14 +294,16 @@ __global__ void attn_merge_kernel(AttnArgs a) {
 
 template <class ET, int DH>
 hipError_t launch_dh(const AttnArgs& a, hipStream_t st) {
+  // fp32 with 128-wide heads stages 64 keys per round to keep LDS below 68 KB
+  constexpr int SC = (sizeof(typename ET::storage) == 4 && DH == 128) ? 64 : 128;
   const int MQ = (a.T + 15) / 16;
   const int QT = (MQ + 3) / 4;
   dim3 grid(a.NS, a.H, a.B), block(256);
   switch (QT) {
-    case 1: hipLaunchKernelGGL((tree_attn_kernel<ET, DH, 1>), grid, block, 0, st, a); break;
-    case 2: hipLaunchKernelGGL((tree_attn_kernel<ET, DH, 2>), grid, block, 0, st, a); break;
-    case 3: hipLaunchKernelGGL((tree_attn_kernel<ET, DH, 3>), grid, block, 0, st, a); break;
-    default: hipLaunchKernelGGL((tree_attn_kernel<ET, DH, 4>), grid, block, 0, st, a); break;
+    case 1: hipLaunchKernelGGL((tree_attn_kernel<ET, DH, 1, SC>), grid, block, 0, st, a); break;
+    case 2: hipLaunchKernelGGL((tree_attn_kernel<ET, DH, 2, SC>), grid, block, 0, st, a); break;
+    case 3: hipLaunchKernelGGL((tree_attn_kernel<ET, DH, 3, SC>), grid, block, 0, st, a); break;
+    default: hipLaunchKernelGGL((tree_attn_kernel<ET, DH, 4, SC>), grid, block, 0, st, a); break;
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;

@@ -61,6 +61,8 @@ class VerifyStep:
                if k not in ("ranks",) and isinstance(v, np.ndarray)}
         self.inp = dev
         self.kv_len0 = dev["kv_len"].clone()
+        kv = np.asarray(inputs["kv_len"])
+        self._uniform_kv = int(kv[0]) if np.all(kv == kv[0]) else None
         i32, f = torch.int32, torch.float32
         z = lambda shape, dt: torch.zeros(shape, dtype=dt, device="cuda")  # noqa: E731
         exact = mode == "exact"
@@ -136,7 +138,12 @@ class VerifyStep:
                  i["k_cache"], i["v_cache"], i["kv_len"], o["h_next"], stream=stream)
 
     def reset_kv_len(self):
-        self.inp["kv_len"].copy_(self.kv_len0)
+        """Restore the prefix lengths (one small fill kernel when they are all
+        equal, else a device copy)."""
+        if self._uniform_kv is not None:
+            self.inp["kv_len"].fill_(self._uniform_kv)
+        else:
+            self.inp["kv_len"].copy_(self.kv_len0)
 
     def run(self, stream=None, commit: bool = True):
         """The whole step: heads, tree, verify forward, posterior, commit."""
