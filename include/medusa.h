@@ -179,6 +179,32 @@ int medusa_tree_attention(const medusa_shape* shape, const void* q, const void* 
                           float* out, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Weight packing for the verification GEMMs (an MI355X layout, not a step of
+ * the method). The verifier's projections read their weights as MFMA
+ * operand tiles: tile (nt, kt) holds packed rows 16*nt .. 16*nt+15 and
+ * columns c*kt .. c*kt+c-1 (c = 32 for bf16, 16 for fp32) of a row-major
+ * [rows][d] matrix, stored as 64 consecutive 16-byte pieces, piece l =
+ * packed row 16*nt + l%16, columns c*kt + (c/4)*(l/16) .. +c/4-1; tiles are
+ * ordered nt-major, kt-minor, so 16 rows stream contiguously along d. Packed
+ * rows past `rows` (up to the next multiple of 16) are zero.
+ * kind MEDUSA_PACK_PLAIN: packed row n is row n (W_o, W_lm).
+ * kind MEDUSA_PACK_QKV (W_qkv, rows = 3d): within every block of Dh rows
+ *   (one head of q, k or v) packed row 16*t + j is row 8*t + j for j < 8 and
+ *   row Dh/2 + 8*t + j - 8 for j >= 8, so each tile holds 8 whole RoPE
+ *   rotation pairs (i, i + Dh/2).
+ *   W        [rows][d] elem, row-major (input, not modified)
+ *   W_packed medusa_packed_weight_bytes(shape, rows) bytes, 16-byte aligned,
+ *            not overlapping W (out)
+ * Pack W_qkv, W_o and W_lm once, before the first medusa_verify_forward.
+ * medusa_packed_weight_bytes returns 0 on an invalid shape or rows < 1.
+ */
+#define MEDUSA_PACK_PLAIN 0
+#define MEDUSA_PACK_QKV 1
+size_t medusa_packed_weight_bytes(const medusa_shape* shape, int rows);
+int medusa_pack_weight(const medusa_shape* shape, int kind, const void* W, int rows,
+                       void* W_packed, void* stream);
+
+/*
  * Verification forward: one target layer over the T tree rows of every
  * sequence, then the verification LM head (the target scores the whole tree
  * in one pass, "Medusa: Faster LLM text generation", Tree attention). The
@@ -195,7 +221,9 @@ int medusa_tree_attention(const medusa_shape* shape, const void* q, const void* 
  *   child_logit[b][t] = l at row parent(t), column tree_tokens[b][t]
  *   (t >= 1; child_logit[b][0] = 0).
  *
- *   E [V][d], W_qkv [3d][d] (q, k, v blocks), W_o [d][d], W_lm [V][d]: elem
+ *   E [V][d] elem, row-major; W_qkv (3d rows: q, k, v blocks, packed with
+ *   MEDUSA_PACK_QKV), W_o (d rows) and W_lm (V rows, both MEDUSA_PACK_PLAIN):
+ *   elem, packed by medusa_pack_weight
  *   k_tree_out, v_tree_out [B][T][H][Dh] elem (out; rows to commit)
  *   y_out [B][T][d] fp32 (out); row_stats [B][T][3] fp32 (out);
  *   row_argmax [B][T] int32 (out); child_logit [B][T] fp32 (out);

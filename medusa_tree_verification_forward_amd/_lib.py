@@ -70,6 +70,8 @@ _SIGS = {
     "medusa_heads_forward": ([_SP, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P], _I),
     "medusa_build_tree": ([_SP, _P, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P], _I),
     "medusa_tree_attention": ([_SP, _P, _P, _P, _P, _P, _P, _P, _F, _P, _P, _SZ, _P], _I),
+    "medusa_packed_weight_bytes": ([_SP, _I], _SZ),
+    "medusa_pack_weight": ([_SP, _I, _P, _I, _P, _P], _I),
     "medusa_verify_forward": ([_SP, _P, _P, _P, _P, _F, _P, _P, _P, _P, _P, _P, _P, _F,
                                _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P], _I),
     "medusa_evaluate_posterior": ([_SP, _I, _F, _F, _F, _P, _P, _P, _P, _P, _P, _P, _P, _P,
@@ -167,6 +169,32 @@ def tree_attention(shape, q, k_tree, v_tree, k_cache, v_cache, kv_len, tree_mask
         ctypes.byref(shape), _ptr(q), _ptr(k_tree), _ptr(v_tree), _ptr(k_cache), _ptr(v_cache),
         _ptr(kv_len), _ptr(tree_mask), float(scale), _ptr(out), _ptr(workspace),
         workspace.numel() * workspace.element_size(), _stream(stream)))
+
+
+def packed_weight_bytes(shape: Shape, rows: int) -> int:
+    n = _lib.medusa_packed_weight_bytes(ctypes.byref(shape), int(rows))
+    if n == 0:
+        raise MedusaError(ERR_ARG, last_error())
+    return int(n)
+
+
+PACK_PLAIN = 0
+PACK_QKV = 1
+
+
+def pack_weight(shape, kind, W, rows, W_packed, *, stream=None):
+    """Pack a row-major [rows][d] weight into the verify GEMMs' tile order."""
+    _check(_lib.medusa_pack_weight(ctypes.byref(shape), int(kind), _ptr(W), int(rows),
+                                   _ptr(W_packed), _stream(stream)))
+
+
+def packed_copy(shape, kind, W, rows, *, stream=None):
+    """A new device buffer holding W packed (allocated with torch, same dtype)."""
+    import torch
+    n = packed_weight_bytes(shape, rows)
+    out = torch.empty(n // W.element_size(), dtype=W.dtype, device=W.device)
+    pack_weight(shape, kind, W, rows, out, stream=stream)
+    return out
 
 
 def verify_forward(shape, E, W_qkv, W_o, W_lm, rope_theta, tree_tokens, position_ids,

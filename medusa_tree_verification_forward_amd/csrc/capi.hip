@@ -67,6 +67,8 @@ constexpr int kMinW2Rows = 16;
 int w1_rows() { static int v = env_int("MEDUSA_W1_ROWS", 16, 4, 4096); return v; }
 int w2_rows() { static int v = env_int("MEDUSA_W2_ROWS", 128, kMinW2Rows, 65536); return v; }
 
+constexpr size_t kCounterBytes = 64 * 1024;   // workspace bytes reserved at offset 0 for counters
+
 int check_shape(const medusa_shape* s) {
   if (!s) return fail(MEDUSA_ERR_ARG, "shape: null pointer");
   if (s->dtype != MEDUSA_BF16 && s->dtype != MEDUSA_F32)
@@ -86,11 +88,14 @@ int check_shape(const medusa_shape* s) {
   if (s->d % 64 != 0) return fail(MEDUSA_ERR_UNSUPPORTED, "d=%d is not a multiple of 64", s->d);
   if (s->Dh != 64 && s->Dh != 128)
     return fail(MEDUSA_ERR_UNSUPPORTED, "Dh=%d is not 64 or 128", s->Dh);
+  if ((size_t)gemm_groups_max(3 * s->d) * gemm_passes_max(s->B * (s->N + 1)) >
+      kCounterBytes / sizeof(int))
+    return fail(MEDUSA_ERR_UNSUPPORTED, "d=%d with %d tree rows needs too many GEMM counters",
+                s->d, s->B * (s->N + 1));
   return MEDUSA_OK;
 }
 
 // ---- workspace layout ----------------------------------------------------------
-constexpr size_t kCounterBytes = 64 * 1024;   // reserved at offset 0 for counters
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
@@ -134,11 +139,12 @@ Layout layout_for(const medusa_shape* s) {
   L.q = take(B * T * d * es);
   L.o_elem = take(B * T * d * es);
   L.y_elem = take(B * T * d * es);
-  L.lm_part = take(B * T * lm_head_blocks(s->V) * 4 * 4);
+  L.lm_part = take(B * T * gemm_groups_max(s->V) * 4 * 4);
   {
     const bool f32 = s->dtype == MEDUSA_F32;
-    const size_t q_need = (size_t)gemm_splits(3 * s->d, s->d, f32) * B * T * 3 * d;
-    const size_t o_need = (size_t)gemm_splits(s->d, s->d, f32) * B * T * d;
+    // partials [groups][M][cols][KS]: groups * cols < N + 128
+    const size_t q_need = (size_t)gemm_splits(3 * s->d, s->d, f32) * B * T * (3 * d + 128);
+    const size_t o_need = (size_t)gemm_splits(s->d, s->d, f32) * B * T * (d + 128);
     L.gemm_part = take((q_need > o_need ? q_need : o_need) * 4);
   }
   L.pw = take(B * V * 4);
@@ -385,6 +391,36 @@ int medusa_tree_attention(const medusa_shape* shape, const void* q, const void* 
   return ok();
 }
 
+size_t medusa_packed_weight_bytes(const medusa_shape* shape, int rows) {
+  if (check_shape(shape) != MEDUSA_OK) return 0;
+  if (rows < 1) {
+    fail(MEDUSA_ERR_ARG, "rows must be positive");
+    return 0;
+  }
+  ok();
+  return packed_weight_bytes(rows, shape->d, shape->dtype == MEDUSA_F32);
+}
+
+int medusa_pack_weight(const medusa_shape* shape, int kind, const void* W, int rows,
+                       void* W_packed, void* stream) {
+  int rc = check_shape(shape);
+  if (rc) return rc;
+  if (rows < 1) return fail(MEDUSA_ERR_ARG, "rows must be positive");
+  if (kind != MEDUSA_PACK_PLAIN && kind != MEDUSA_PACK_QKV)
+    return fail(MEDUSA_ERR_ARG, "pack kind %d unknown", kind);
+  if (kind == MEDUSA_PACK_QKV && rows != 3 * shape->d)
+    return fail(MEDUSA_ERR_ARG, "MEDUSA_PACK_QKV needs rows = 3d = %d, got %d", 3 * shape->d,
+                rows);
+  REQUIRE_PTR(W);
+  REQUIRE_PTR(W_packed);
+  if (W == W_packed) return fail(MEDUSA_ERR_ARG, "W and W_packed must not overlap");
+  hipError_t e = launch_pack_weight(shape->dtype == MEDUSA_F32, W, rows, shape->d,
+                                    kind == MEDUSA_PACK_QKV ? shape->Dh : 0, W_packed,
+                                    static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "pack launch");
+  return ok();
+}
+
 int medusa_verify_forward(const medusa_shape* shape, const void* E, const void* W_qkv,
                           const void* W_o, const void* W_lm, float rope_theta,
                           const int32_t* tree_tokens, const int32_t* position_ids,
@@ -445,6 +481,7 @@ int medusa_verify_forward(const medusa_shape* shape, const void* E, const void* 
   g.k_out = k_tree_out;
   g.v_out = v_tree_out;
   g.part = at<float>(workspace, L.gemm_part);
+  g.counters = at<int>(workspace, L.counters);
   hipError_t e = launch_qkv(g, st);
   if (e != hipSuccess) return hip_fail(e, "qkv launch");
   // 2. tree attention, output rounded to the storage type

@@ -131,6 +131,15 @@ __device__ __forceinline__ void stage_barrier() {
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
 }
 
+// Workgroup barrier that publishes this wave's LDS writes (lgkmcnt 0) but
+// leaves its global loads in flight (no vmcnt wait, unlike __syncthreads).
+__device__ __forceinline__ void lds_barrier() {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(0xC07F);   // vmcnt 63, expcnt 7, lgkmcnt 0
+  __builtin_amdgcn_s_barrier();
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
 // ---- DPP wave reductions ----------------------------------------------------
 // DPP control codes (GFX9 encoding).
 constexpr int kDppQuadXor1 = 0xB1;   // quad_perm [1,0,3,2]

@@ -90,12 +90,23 @@ struct GemmParams {
   void* y_elem;                // [M][N] storage type
   // LM epilogue
   float inv_tau;
-  float* part;                 // LM: [M][blocks][4]; QKV/OPROJ: [KS][M][N] partials
+  float* part;                 // LM: [M][groups][4]; QKV/OPROJ: [groups][M][cols][KS]
   const int32_t* parent;       // [T]
   float* child_logit;          // [M]
   float* logits_out;           // [M][N] or null
+  int* counters;               // fused epilogue: one zeroed counter per (group, pass)
+  int group_cols;              // set by the launcher
+  int fused;                   // set by the launcher
 };
-int lm_head_blocks(int N);
+// Weights W[rows][K] of the node GEMMs are packed into MFMA tiles (see
+// node_gemm.hip) before use; pair_dh = Dh reorders the rows of each head
+// into rotation pairs (W_qkv), 0 keeps them in order.
+size_t packed_weight_bytes(int rows, int K, bool f32);
+hipError_t launch_pack_weight(bool f32, const void* W, int rows, int K, int pair_dh, void* out,
+                              hipStream_t st);
+int gemm_groups_max(int N);                // column groups of a node GEMM (upper bound)
+int gemm_passes_max(int M);                // row passes (upper bound)
+int lm_head_blocks(int N, int M);          // column groups of the LM head
 int gemm_splits(int N, int K, bool f32);   // K slices of the QKV / output projection GEMMs
 hipError_t launch_qkv(const GemmParams& p, hipStream_t st);
 hipError_t launch_oproj(const GemmParams& p, hipStream_t st);
@@ -103,7 +114,7 @@ hipError_t launch_lm_head(const GemmParams& p, float* row_stats, int* row_argmax
                           hipStream_t st);
 
 // ---- tree attention ---------------------------------------------------------------
-constexpr int kAttnChunk = 128;   // prefix keys per split
+constexpr int kAttnChunk = 256;   // prefix keys per split
 struct AttnArgs {
   bool f32;
   int B, T, H, Dh, Lmax;

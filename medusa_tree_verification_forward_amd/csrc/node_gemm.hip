@@ -2,33 +2,43 @@
 //   C[M][N] = A[M][K] * W[N][K]^T,  M = B*T tree rows (tens to a few hundred),
 //   N = 3d (QKV), d (output projection) or V (verification LM head).
 //
-// The weights stream from HBM once; A (a few hundred KB) stays in L2.
-// A workgroup of 8 waves owns 128 output columns (16 per wave), all M rows
-// (in passes of 16*MT rows) and one of KS slices of K. K advances in
-// k-blocks of 128 bytes per row. Both operands of a k-block -- the 128
-// weight rows and the 16*MT A rows -- are copied by direct global->LDS
-// loads (each lane names one 16-byte piece; a wave's 64 pieces land
-// lane-major) into a ring of S stages, so up to S-1 k-blocks are in flight
-// per workgroup without holding registers. One barrier per stage: every
-// wave waits for its own loads of the stage (vmcnt), then s_barrier, then
-// refills the slot freed by the previous stage. A lane then reads back
-// exactly the MFMA fragments it needs: for weights its own two pieces, for
-// A the pieces of each m-tile. Per 16-byte piece that is one
-// v_mfma_f32_16x16x32_bf16 per m-tile, or four v_mfma_f32_16x16x4_f32 for
-// fp32 storage (the k index inside a piece is permuted identically for
-// both operands, which does not change the sum).
+// The weights are read exactly once and dominate the traffic, so the kernel
+// is built around streaming them at full HBM rate:
+//  * W is pre-packed into MFMA operand tiles (launch_pack_weight): a tile is
+//    16 rows x 64 bytes of k, stored as 64 lane-ordered 16-byte pieces, so
+//    the B fragment of one v_mfma_f32_16x16x32_bf16 is a single 1 KB
+//    contiguous wave load, and a 16-row stripe of W is one contiguous run.
+//  * Each wave owns one 16-column stripe and streams its k-tiles through a
+//    ring of D registers (D loads in flight per wave).
+//  * A (the tree rows, a few hundred KB, L2-resident) is shared by the WV
+//    waves of a workgroup: it moves in chunks of CH k-tiles, loaded into
+//    registers one chunk ahead and written to one of two LDS buffers; one
+//    barrier per chunk publishes the next buffer.
+//  * fp32 storage uses v_mfma_f32_16x16x4_f32, four per 16-byte piece (the
+//    k order inside a piece is permuted identically for both operands,
+//    which leaves the dot products unchanged).
+//  * Rows beyond one pass of 16*MT go to further workgroups (grid z).
 //
-// With KS > 1 the workgroup writes fp32 partial tiles; an elementwise
-// epilogue kernel sums the KS partials in order and applies
+// QKV and the output projection split K over KS workgroups per column group
+// and write fp32 partials part[g][r][c][ks]; an epilogue sums the KS slices
+// of each output in slice order and applies
 //   QKV  : RoPE on q and k (pairs i, i+Dh/2; angle pos * theta^(-2i/Dh)),
 //          rounding to the storage type, scatter to [B][T][H][Dh];
 //   OPROJ: y = x + acc with x = E[token], written as fp32 and storage type.
-// The LM head runs with KS = 1 and reduces in-kernel: per row and 128-column
-// block (max, argmax, S, W) at temperature tau with S = sum e^{(l-m)/tau},
+// W_qkv is packed with the rows of every head reordered so that each
+// 16-column tile holds 8 whole rotation pairs (columns j and j+8 of the tile
+// are rows i and i+Dh/2 of the head, i = 8*(tile in head) + j).
+// The epilogue runs either in a kernel of its own, or (fused) in the last
+// of the KS workgroups of a group to finish, found with a device-scope
+// counter that it leaves at zero for the next launch.
+// The LM head runs with KS = 1 and reduces in-kernel: per row and column
+// group (max, argmax, S, W) at temperature tau with S = sum e^{(l-m)/tau},
 // W = sum e^{(l-m)/tau} (l-m)/tau; the logit of every tree node's token
 // under its parent's row; optional full logits. A merge kernel combines the
-// column blocks of a row.
+// column groups of a row.
 #include <stdlib.h>
+
+#include <type_traits>
 
 #include "common.h"
 #include "kernels.h"
@@ -37,8 +47,7 @@ namespace medusa {
 namespace {
 
 constexpr float kNegInf = -__builtin_huge_valf();
-constexpr int kGemmWaves = 8;
-constexpr int kGemmCols = 16 * kGemmWaves;   // output columns per workgroup
+constexpr int kMaxSplits = 16;
 
 // Merge of (max, S, W, argmax) records at temperature tau (see header).
 __device__ __forceinline__ void rec_merge(float& m, float& s, float& w, int& a, float m2,
@@ -58,205 +67,78 @@ __device__ __forceinline__ void rec_merge(float& m, float& s, float& w, int& a, 
   a = an;
 }
 
-template <class ET, int MT, int S, bool LM>
-__global__ __launch_bounds__(512) void node_gemm_kernel(GemmParams p) {
-  using St = typename ET::storage;
-  constexpr int PV = ET::kPerVec;   // elements per 16-byte piece
-  constexpr int KB = 8 * PV;        // k elements per k-block (128 bytes of a row)
-  constexpr int WV = kGemmWaves;
-  constexpr int NA = 2 * MT;        // A pieces per lane per k-block
-  constexpr int NAW = (NA + WV - 1) / WV;   // A load instructions per wave (max)
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int li = lane & 15, lq = lane >> 4;
-  const int g = blockIdx.x, ks = blockIdx.y, KS = gridDim.y;
-  const St* __restrict__ A = reinterpret_cast<const St*>(p.A);
-  const St* __restrict__ W = reinterpret_cast<const St*>(p.W);
-
-  const int n0 = g * kGemmCols;
-  const int col = n0 + 16 * wave + li;
-  const St* wrow = W + (size_t)min(col, p.N - 1) * p.K + PV * lq;
-  const int nkb = p.K / KB;
-  const int kb_lo = (int)((long)nkb * ks / KS), kb_hi = (int)((long)nkb * (ks + 1) / KS);
-  const int nloc = kb_hi - kb_lo;
-  const int na_w = wave < NA ? (NA - wave + WV - 1) / WV : 0;
-  const int ops = 2 + na_w;         // load instructions this wave issues per stage
-
-  __shared__ u32x4_t ringW[S][WV][2][64];
-  __shared__ u32x4_t ringA[S][MT][2][64];
-  __shared__ float stat[LM ? WV : 1][LM ? 16 * MT : 1][4];
-
-  for (int m0 = 0; m0 < p.M; m0 += 16 * MT) {
-    if (m0 > 0) __syncthreads();   // previous pass's readers are done
-    const St* arow[NAW];
+// One A fragment times one W fragment (16-byte pieces of both operands).
+template <class ET>
+__device__ __forceinline__ floatx4_t frag_mfma(const u32x4_t& a, const u32x4_t& b,
+                                               floatx4_t c) {
+  if constexpr (ET::kPerVec == 8) {
+    return mfma16x16x32_bf16(a, b, c);
+  } else {
 #pragma unroll
-    for (int j = 0; j < NAW; ++j) {
-      const int idx = min(wave + WV * j, NA - 1);
-      const int r = min(m0 + 16 * (idx >> 1) + li, p.M - 1);
-      const int src = p.a_rows ? min(max(p.a_rows[r], 0), p.a_nrows - 1) : r;
-      arow[j] = A + (size_t)src * p.lda + PV * lq + 4 * PV * (idx & 1);
-    }
-    auto issue = [&](int i) {
-      const int slot = i % S;
-      const size_t off = (size_t)(kb_lo + i) * KB;
-      dma16(wrow + off, &ringW[slot][wave][0][0]);
-      dma16(wrow + off + 4 * PV, &ringW[slot][wave][1][0]);
-#pragma unroll
-      for (int j = 0; j < NAW; ++j) {
-        const int idx = wave + WV * j;
-        if (idx < NA) dma16(arow[j] + off, &ringA[slot][idx >> 1][idx & 1][0]);
-      }
-    };
-    floatx4_t acc[MT];
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt) acc[mt] = floatx4_t{0.f, 0.f, 0.f, 0.f};
-
-    for (int i = 0; i < S - 1 && i < nloc; ++i) issue(i);
-    for (int i = 0; i < nloc; ++i) {
-      vmcnt_rt(min(S - 2, nloc - 1 - i) * ops);   // this wave's loads of stage i landed
-      stage_barrier();                            // ... and everyone else's
-      if (i + S - 1 < nloc) issue(i + S - 1);     // refill the slot stage i-1 used
-      const int slot = i % S;
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const u32x4_t b = ringW[slot][wave][h][lane];
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt) {
-          const u32x4_t a = ringA[slot][mt][h][lane];
-          if constexpr (PV == 8) {
-            acc[mt] = mfma16x16x32_bf16(a, b, acc[mt]);
-          } else {
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-              acc[mt] = mfma16x16x4_f32(__uint_as_float(a[j]), __uint_as_float(b[j]), acc[mt]);
-          }
-        }
-      }
-    }
-
-    if constexpr (!LM) {
-      // partial tile of slice ks: part[ks][r][n]
-      float* part = p.part + (size_t)ks * p.M * p.N;
-      if (col < p.N) {
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const int r = m0 + 16 * mt + 4 * lq + j;
-            if (r < p.M) part[(size_t)r * p.N + col] = acc[mt][j];
-          }
-      }
-    } else {
-      const bool cv = col < p.N;
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int rr = 16 * mt + 4 * lq + j;
-          const int r = m0 + rr;
-          // (max, lowest argmax) over this wave's 16 columns of the row
-          float bv = cv ? acc[mt][j] : kNegInf;
-          int bi = cv ? col : 0x7fffffff;
-#pragma unroll
-          for (int step = 0; step < 4; ++step) {
-            float ov;
-            int oi;
-            if (step == 0) { ov = dpp<kDppQuadXor1>(bv); oi = dppi<kDppQuadXor1>(bi); }
-            else if (step == 1) { ov = dpp<kDppQuadXor2>(bv); oi = dppi<kDppQuadXor2>(bi); }
-            else if (step == 2) { ov = dpp<kDppRowRor4>(bv); oi = dppi<kDppRowRor4>(bi); }
-            else { ov = dpp<kDppRowRor8>(bv); oi = dppi<kDppRowRor8>(bi); }
-            if (better(ov, oi, bv, bi)) { bv = ov; bi = oi; }
-          }
-          float sv = 0.f, wv = 0.f;
-          if (cv) {
-            const float z = (acc[mt][j] - bv) * p.inv_tau;
-            const float e = exp_e(z);
-            sv = e;
-            wv = e * z;
-          }
-          sv = row16_sum(sv);
-          wv = row16_sum(wv);
-          if (li == 0) {
-            stat[wave][rr][0] = bv;
-            stat[wave][rr][1] = sv;
-            stat[wave][rr][2] = wv;
-            stat[wave][rr][3] = __int_as_float(bi);
-          }
-          if (p.logits_out && cv && r < p.M) p.logits_out[(size_t)r * p.N + col] = acc[mt][j];
-        }
-      // logit of each tree node's token under its parent's row (this wave's columns)
-      const int rows_hi = min(p.M, m0 + 16 * MT);
-      const int c0 = n0 + 16 * wave;
-      const int bl = m0 / p.T, bh = (rows_hi - 1) / p.T;
-      const int nchild = (bh - bl + 1) * p.T;
-      for (int e0 = 0; e0 < nchild; e0 += 64) {
-        const int e = e0 + lane;
-        int r = -1, tok = -1, node = -1;
-        bool hit = false;
-        if (e < nchild) {
-          const int b = bl + e / p.T, cnode = e % p.T;
-          if (cnode >= 1) {
-            node = b * p.T + cnode;
-            tok = p.tokens[node];
-            r = b * p.T + min(max(p.parent[cnode], 0), p.T - 1);
-            hit = tok >= c0 && tok < c0 + 16 && r >= m0 && r < rows_hi;
-          }
-        }
-        uint64_t mask = __ballot(hit);
-        while (mask) {
-          const int src = __ffsll((unsigned long long)mask) - 1;
-          mask &= mask - 1;
-          const int hr = __builtin_amdgcn_readlane(r, src);
-          const int ht = __builtin_amdgcn_readlane(tok, src);
-          const int hn = __builtin_amdgcn_readlane(node, src);
-          const int rr = hr - m0;
-          const int want_li = ht - c0, want_mt = rr >> 4, want_lq = (rr & 15) >> 2,
-                    want_j = rr & 3;
-          float v = 0.f;
-#pragma unroll
-          for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-              if (mt == want_mt && j == want_j) v = acc[mt][j];
-          if (li == want_li && lq == want_lq) p.child_logit[hn] = v;
-        }
-      }
-      __syncthreads();
-      // one record per (row, column block): merge the 8 waves in order
-      for (int rr = threadIdx.x; rr < 16 * MT; rr += blockDim.x) {
-        const int r = m0 + rr;
-        if (r >= p.M) continue;
-        float m = kNegInf, sv = 0.f, wv = 0.f;
-        int a = 0x7fffffff;
-        for (int w = 0; w < WV; ++w)
-          rec_merge(m, sv, wv, a, stat[w][rr][0], stat[w][rr][1], stat[w][rr][2],
-                    __float_as_int(stat[w][rr][3]), p.inv_tau);
-        float* rec = p.part + ((size_t)r * gridDim.x + g) * 4;
-        rec[0] = m;
-        rec[1] = sv;
-        rec[2] = wv;
-        rec[3] = __int_as_float(a);
-      }
-    }
+    for (int j = 0; j < 4; ++j)
+      c = mfma16x16x4_f32(__uint_as_float(a[j]), __uint_as_float(b[j]), c);
+    return c;
   }
 }
 
-// QKV epilogue: sum the KS partials of (row r, column pair i, i+Dh/2) in
-// order, rotate q and k by the RoPE angle of the row's position (reduced
-// to one turn in double precision), round, scatter to [M][H][Dh].
-// grid = (M, 3H), block = Dh/2 threads.
+// Row of W held by packed row n: identity, or the rotation-pair order of
+// W_qkv (within each block of Dh rows, tile tt, lane column li: rows
+// 8 tt + li for li < 8, Dh/2 + 8 tt + li - 8 otherwise).
+__device__ __forceinline__ int packed_source_row(int n, int pair_dh) {
+  if (pair_dh == 0) return n;
+  const int blk = n / pair_dh, nl = n - blk * pair_dh;
+  const int tt = nl >> 4, li = nl & 15;
+  return blk * pair_dh + (li < 8 ? 8 * tt + li : (pair_dh >> 1) + 8 * tt + li - 8);
+}
+
+// Packing: piece q of the output is lane l = q % 64 of tile q / 64; tile
+// (nt, kt) = (tile / nkt, tile % nkt) holds packed rows 16 nt + l % 16, k
+// elements KT kt + PV (l / 16) .. + PV - 1 (KT = 4 PV). Rows >= rows are 0.
 template <class ET>
-__global__ void qkv_epilogue_kernel(GemmParams p, int KS) {
-  using S = typename ET::storage;
-  const int r = blockIdx.x, hp = blockIdx.y, i = threadIdx.x;
-  const int Dh = p.Dh, half = Dh / 2, H = p.H;
-  const int which = hp / H, h = hp - which * H;
-  const int c1 = hp * Dh + i, c2 = c1 + half;
-  float x1 = 0.f, x2 = 0.f;
-  for (int s = 0; s < KS; ++s) {
-    const float* part = p.part + ((size_t)s * p.M + r) * p.N;
-    x1 += part[c1];
-    x2 += part[c2];
+__global__ void pack_weight_kernel(const typename ET::storage* __restrict__ W, int rows, int K,
+                                   int pair_dh, u32x4_t* __restrict__ out, size_t pieces) {
+  constexpr int PV = ET::kPerVec, KT = 4 * PV;
+  const size_t q = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (q >= pieces) return;
+  const int nkt = K / KT;
+  const size_t tile = q >> 6;
+  const int l = (int)(q & 63);
+  const int nt = (int)(tile / nkt), kt = (int)(tile % nkt);
+  const int n = 16 * nt + (l & 15);
+  u32x4_t v = {0u, 0u, 0u, 0u};
+  if (n < rows) {
+    const int r = packed_source_row(n, pair_dh);
+    v = load16(W + (size_t)r * K + (size_t)KT * kt + PV * (l >> 4));
   }
+  out[q] = v;
+}
+
+// Sum, in slice order, of the KS partials of one output (KS contiguous floats).
+__device__ __forceinline__ float sum_slices(const float* p, int KS) {
+  float acc = 0.f;
+  if ((KS & 3) == 0) {
+    for (int s = 0; s < KS; s += 4) {
+      const floatx4_t v = *reinterpret_cast<const floatx4_t*>(p + s);
+      acc += v[0];
+      acc += v[1];
+      acc += v[2];
+      acc += v[3];
+    }
+  } else {
+    for (int s = 0; s < KS; ++s) acc += p[s];
+  }
+  return acc;
+}
+
+// QKV epilogue for one rotation pair (packed columns c1, c1 + 8) of row r.
+template <class ET>
+__device__ __forceinline__ void qkv_finish(const GemmParams& p, int r, int c1, float x1,
+                                           float x2) {
+  using St = typename ET::storage;
+  const int Dh = p.Dh, half = Dh >> 1;
+  const int blk = c1 / Dh, nl = c1 - blk * Dh;
+  const int i = 8 * (nl >> 4) + (nl & 7);
+  const int which = blk / p.H, h = blk - which * p.H;
   if (which < 2) {
     const double inv_freq = exp(-(2.0 * i / Dh) * p.log_theta);
     const double turns = (double)p.pos[r] * inv_freq * 0.15915494309189535;   // 1/(2 pi)
@@ -268,26 +150,288 @@ __global__ void qkv_epilogue_kernel(GemmParams p, int KS) {
     x1 = y1;
     x2 = y2;
   }
-  S* dst = reinterpret_cast<S*>(which == 0 ? p.q_out : (which == 1 ? p.k_out : p.v_out));
-  S* o = dst + ((size_t)r * H + h) * Dh + i;
+  St* dst = reinterpret_cast<St*>(which == 0 ? p.q_out : (which == 1 ? p.k_out : p.v_out));
+  St* o = dst + ((size_t)r * p.H + h) * Dh + i;
   o[0] = ET::from_float(x1);
   o[half] = ET::from_float(x2);
 }
 
-// Output-projection epilogue: y = E[token] + sum of partials, fp32 and
-// storage type. grid = (M, ceil(N/256)), block 256.
 template <class ET>
-__global__ void oproj_epilogue_kernel(GemmParams p, int KS) {
-  using S = typename ET::storage;
-  const int r = blockIdx.x, n = blockIdx.y * 256 + threadIdx.x;
-  if (n >= p.N) return;
-  float acc = 0.f;
-  for (int s = 0; s < KS; ++s) acc += p.part[((size_t)s * p.M + r) * p.N + n];
-  const S* x = reinterpret_cast<const S*>(p.E) +
-               (size_t)min(max(p.tokens[r], 0), p.a_nrows - 1) * p.N;
+__device__ __forceinline__ void oproj_finish(const GemmParams& p, int r, int n, float acc) {
+  using St = typename ET::storage;
+  const St* x = reinterpret_cast<const St*>(p.E) +
+                (size_t)min(max(p.tokens[r], 0), p.a_nrows - 1) * p.N;
   const float y = ET::load1(x + n) + acc;
   p.y_out[(size_t)r * p.N + n] = y;
-  reinterpret_cast<S*>(p.y_elem)[(size_t)r * p.N + n] = ET::from_float(y);
+  reinterpret_cast<St*>(p.y_elem)[(size_t)r * p.N + n] = ET::from_float(y);
+}
+
+// partials of output (r, packed column n): part[g][r][c][ks], g = n / GC
+__device__ __forceinline__ const float* partial_at(const GemmParams& p, int r, int n, int KS) {
+  const int g = n / p.group_cols, c = n - g * p.group_cols;
+  return p.part + (((size_t)g * p.M + r) * p.group_cols + c) * KS;
+}
+
+template <class ET, int WV, int MT, int CH, int D, int EPI>
+__global__ __launch_bounds__(64 * WV, (WV == 4 || MT <= 3) ? 4 : 2) void node_gemm_kernel(
+    GemmParams p) {
+  using St = typename ET::storage;
+  constexpr int PV = ET::kPerVec, KT = 4 * PV;   // k elements per tile
+  constexpr int GC = 16 * WV;                     // output columns per workgroup
+  static_assert((CH * MT) % WV == 0, "A fragments of a chunk must divide over the waves");
+  static_assert((2 * CH) % D == 0, "the weight ring must divide a pair of chunks");
+  constexpr int NAW = CH * MT / WV;               // A loads per wave per chunk
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int li = lane & 15, lq = lane >> 4;
+  const int g = blockIdx.x, ks = blockIdx.y, KS = gridDim.y;
+  const int m0 = blockIdx.z * 16 * MT;
+  const St* __restrict__ A = reinterpret_cast<const St*>(p.A);
+  const int nkt = p.K / KT;
+  const int kt_lo = (int)((long)nkt * ks / KS), kt_hi = (int)((long)nkt * (ks + 1) / KS);
+  const int nloc = kt_hi - kt_lo;
+  const int ntiles = (p.N + 15) >> 4;
+  const int n0 = g * GC;
+  const int col = n0 + 16 * wave + li;
+  const u32x4_t* __restrict__ wp = reinterpret_cast<const u32x4_t*>(p.W) +
+                                   ((size_t)min(g * WV + wave, ntiles - 1) * nkt + kt_lo) * 64 +
+                                   lane;
+
+  __shared__ u32x4_t sA0[CH][MT][64];
+  __shared__ u32x4_t sA1[CH][MT][64];
+  __shared__ float stat[EPI == EPI_LM ? WV : 1][EPI == EPI_LM ? 16 * MT : 1][4];
+  __shared__ int s_last;
+
+  // A fragment f = wave + WV i of a chunk is (k-tile f / MT, m-tile f % MT)
+  const St* asrc[NAW];
+#pragma unroll
+  for (int i = 0; i < NAW; ++i) {
+    const int mt = (wave + WV * i) % MT;
+    const int r = min(m0 + 16 * mt + li, p.M - 1);
+    const int src = p.a_rows ? min(max(p.a_rows[r], 0), p.a_nrows - 1) : r;
+    asrc[i] = A + (size_t)src * p.lda + (size_t)kt_lo * KT + PV * lq;
+  }
+  u32x4_t ra[NAW];   // A fragments of the next chunk, in flight
+  // Past the slice end the k-tile index is clamped (those values are never read).
+  auto load_a = [&](int c) {
+#pragma unroll
+    for (int i = 0; i < NAW; ++i) {
+      const int kt = min(c * CH + (wave + WV * i) / MT, nloc - 1);
+      ra[i] = load16(asrc[i] + (size_t)kt * KT);
+    }
+  };
+  auto store_a = [&](u32x4_t(&buf)[CH][MT][64]) {
+#pragma unroll
+    for (int i = 0; i < NAW; ++i) {
+      const int f = wave + WV * i;
+      buf[f / MT][f % MT][lane] = ra[i];
+    }
+  };
+  floatx4_t acc[MT];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) acc[mt] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+  u32x4_t wr[D];
+
+  const int nch = (nloc + CH - 1) / CH;
+  load_a(0);
+#pragma unroll
+  for (int j = 0; j < D; ++j) wr[j] = load16_stream(wp + (size_t)min(j, nloc - 1) * 64);
+  store_a(sA0);
+  load_a(1);
+  lds_barrier();
+
+  // Chunk c: CH k-tiles from the weight registers against the A fragments
+  // in `cur`; each consumed register is refilled D k-tiles ahead. Then the
+  // A fragments of chunk c+1 (loaded a chunk earlier) go to `nxt`, the loads
+  // of chunk c+2 start, and one barrier publishes `nxt`. A steady chunk has
+  // every step and every refill in range, so the loop keeps a fixed number
+  // of loads in flight; the last chunks check their bounds.
+  auto chunk = [&](int c, u32x4_t(&cur)[CH][MT][64], u32x4_t(&nxt)[CH][MT][64], auto steady,
+                   auto odd) {
+    constexpr bool S = decltype(steady)::value;
+    constexpr int R0 = decltype(odd)::value ? CH : 0;   // ring slot of the chunk's first step
+#pragma unroll
+    for (int j = 0; j < CH; ++j) {
+      const int s = c * CH + j;
+      if (S || s < nloc) {
+        const u32x4_t b = wr[(R0 + j) % D];
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) acc[mt] = frag_mfma<ET>(cur[j][mt][lane], b, acc[mt]);
+        if (S || s + D < nloc) wr[(R0 + j) % D] = load16_stream(wp + (size_t)(s + D) * 64);
+      }
+      // one k-tile at a time: hoisting later LDS reads only raises pressure
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    if (S || c + 1 < nch) {
+      store_a(nxt);
+      load_a(c + 2);
+      lds_barrier();
+    }
+  };
+  const std::integral_constant<bool, true> steady{};
+  const std::integral_constant<bool, false> guarded{};
+  const std::integral_constant<bool, false> even{};
+  const std::integral_constant<bool, true> odd{};
+  int c = 0;
+  for (; (c + 2) * CH + D <= nloc; c += 2) {
+    chunk(c, sA0, sA1, steady, even);
+    chunk(c + 1, sA1, sA0, steady, odd);
+  }
+  for (; c < nch; ++c) {
+    if (c & 1)
+      chunk(c, sA1, sA0, guarded, odd);
+    else
+      chunk(c, sA0, sA1, guarded, even);
+  }
+
+  if constexpr (EPI != EPI_LM) {
+    // partials of slice ks: part[g][r][c][ks]
+    float* part = p.part + ((size_t)g * p.M * GC + 16 * wave + li) * KS + ks;
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int r = m0 + 16 * mt + 4 * lq + j;
+        if (r < p.M) part[(size_t)r * GC * KS] = acc[mt][j];
+      }
+    if (!p.fused) return;
+    // The last of the KS workgroups of this (group, pass) finishes it.
+    __threadfence();   // release this workgroup's partials device-wide
+    __syncthreads();
+    int* counter = p.counters + g * gridDim.z + blockIdx.z;
+    if (threadIdx.x == 0) s_last = atomicAdd(counter, 1) == KS - 1;
+    __syncthreads();
+    if (!s_last) return;
+    __threadfence();   // acquire the other workgroups' partials
+    if (threadIdx.x == 0) *counter = 0;
+    const int rows_hi = min(p.M, m0 + 16 * MT);
+    if constexpr (EPI == EPI_QKV) {
+      // threads: 8 WV pairs x 8 row lanes
+      const int pi = threadIdx.x % (8 * WV), rl = threadIdx.x / (8 * WV);
+      const int c1 = n0 + 16 * (pi >> 3) + (pi & 7);
+      if (c1 >= p.N) return;
+      for (int r = m0 + rl; r < rows_hi; r += 8) {
+        const float x1 = sum_slices(partial_at(p, r, c1, KS), KS);
+        const float x2 = sum_slices(partial_at(p, r, c1 + 8, KS), KS);
+        qkv_finish<ET>(p, r, c1, x1, x2);
+      }
+    } else {
+      const int cl = threadIdx.x % GC, rl = threadIdx.x / GC;
+      const int n = n0 + cl;
+      if (n >= p.N) return;
+      for (int r = m0 + rl; r < rows_hi; r += 4)
+        oproj_finish<ET>(p, r, n, sum_slices(partial_at(p, r, n, KS), KS));
+    }
+  } else {
+    const bool cv = col < p.N;
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int rr = 16 * mt + 4 * lq + j;
+        const int r = m0 + rr;
+        // (max, lowest argmax) over this wave's 16 columns of the row
+        float bv = cv ? acc[mt][j] : kNegInf;
+        int bi = cv ? col : 0x7fffffff;
+#pragma unroll
+        for (int step = 0; step < 4; ++step) {
+          float ov;
+          int oi;
+          if (step == 0) { ov = dpp<kDppQuadXor1>(bv); oi = dppi<kDppQuadXor1>(bi); }
+          else if (step == 1) { ov = dpp<kDppQuadXor2>(bv); oi = dppi<kDppQuadXor2>(bi); }
+          else if (step == 2) { ov = dpp<kDppRowRor4>(bv); oi = dppi<kDppRowRor4>(bi); }
+          else { ov = dpp<kDppRowRor8>(bv); oi = dppi<kDppRowRor8>(bi); }
+          if (better(ov, oi, bv, bi)) { bv = ov; bi = oi; }
+        }
+        float sv = 0.f, wv = 0.f;
+        if (cv) {
+          const float z = (acc[mt][j] - bv) * p.inv_tau;
+          const float e = exp_e(z);
+          sv = e;
+          wv = e * z;
+        }
+        sv = row16_sum(sv);
+        wv = row16_sum(wv);
+        if (li == 0) {
+          stat[wave][rr][0] = bv;
+          stat[wave][rr][1] = sv;
+          stat[wave][rr][2] = wv;
+          stat[wave][rr][3] = __int_as_float(bi);
+        }
+        if (p.logits_out && cv && r < p.M) p.logits_out[(size_t)r * p.N + col] = acc[mt][j];
+      }
+    // logit of each tree node's token under its parent's row (this wave's columns)
+    const int rows_hi = min(p.M, m0 + 16 * MT);
+    const int c0 = n0 + 16 * wave;
+    const int bl = m0 / p.T, bh = (rows_hi - 1) / p.T;
+    const int nchild = (bh - bl + 1) * p.T;
+    for (int e0 = 0; e0 < nchild; e0 += 64) {
+      const int e = e0 + lane;
+      int r = -1, tok = -1, node = -1;
+      bool hit = false;
+      if (e < nchild) {
+        const int b = bl + e / p.T, cnode = e % p.T;
+        if (cnode >= 1) {
+          node = b * p.T + cnode;
+          tok = p.tokens[node];
+          r = b * p.T + min(max(p.parent[cnode], 0), p.T - 1);
+          hit = tok >= c0 && tok < c0 + 16 && r >= m0 && r < rows_hi;
+        }
+      }
+      uint64_t mask = __ballot(hit);
+      while (mask) {
+        const int src = __ffsll((unsigned long long)mask) - 1;
+        mask &= mask - 1;
+        const int hr = __builtin_amdgcn_readlane(r, src);
+        const int ht = __builtin_amdgcn_readlane(tok, src);
+        const int hn = __builtin_amdgcn_readlane(node, src);
+        const int rr = hr - m0;
+        const int want_li = ht - c0, want_mt = rr >> 4, want_lq = (rr & 15) >> 2,
+                  want_j = rr & 3;
+        float v = 0.f;
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            if (mt == want_mt && j == want_j) v = acc[mt][j];
+        if (li == want_li && lq == want_lq) p.child_logit[hn] = v;
+      }
+    }
+    __syncthreads();
+    // one record per (row, column group): merge the waves in order
+    for (int rr = threadIdx.x; rr < 16 * MT; rr += blockDim.x) {
+      const int r = m0 + rr;
+      if (r >= p.M) continue;
+      float m = kNegInf, sv = 0.f, wv = 0.f;
+      int a = 0x7fffffff;
+      for (int w = 0; w < WV; ++w)
+        rec_merge(m, sv, wv, a, stat[w][rr][0], stat[w][rr][1], stat[w][rr][2],
+                  __float_as_int(stat[w][rr][3]), p.inv_tau);
+      float* rec = p.part + ((size_t)r * gridDim.x + g) * 4;
+      rec[0] = m;
+      rec[1] = sv;
+      rec[2] = wv;
+      rec[3] = __int_as_float(a);
+    }
+  }
+}
+
+// Separate epilogues: one thread per (row, rotation pair) / (row, column).
+template <class ET>
+__global__ __launch_bounds__(256) void qkv_epilogue_kernel(GemmParams p, int KS) {
+  const int r = blockIdx.y;
+  const int P = blockIdx.x * 256 + threadIdx.x;   // pair index over the packed columns
+  const int c1 = 16 * (P >> 3) + (P & 7);
+  if (c1 >= p.N) return;
+  const float x1 = sum_slices(partial_at(p, r, c1, KS), KS);
+  const float x2 = sum_slices(partial_at(p, r, c1 + 8, KS), KS);
+  qkv_finish<ET>(p, r, c1, x1, x2);
+}
+
+template <class ET>
+__global__ __launch_bounds__(256) void oproj_epilogue_kernel(GemmParams p, int KS) {
+  const int r = blockIdx.y, n = blockIdx.x * 256 + threadIdx.x;
+  if (n >= p.N) return;
+  oproj_finish<ET>(p, r, n, sum_slices(partial_at(p, r, n, KS), KS));
 }
 
 __global__ __launch_bounds__(64) void row_stats_merge_kernel(const float* __restrict__ part,
@@ -315,73 +459,156 @@ __global__ __launch_bounds__(64) void row_stats_merge_kernel(const float* __rest
   }
 }
 
-template <class ET, bool LM>
-hipError_t launch_main(const GemmParams& p, int groups, int KS, hipStream_t st) {
-  const int mt_needed = (p.M + 15) / 16;
-  dim3 grid(groups, KS), block(64 * kGemmWaves);
-  // stages: as many as fit in LDS next to the A tiles
-  if (mt_needed <= 3)
-    hipLaunchKernelGGL((node_gemm_kernel<ET, 3, LM ? 6 : 7, LM>), grid, block, 0, st, p);
+// Tile configuration: waves per workgroup (= 16-column stripes), m-tiles
+// per pass, k-tiles per A chunk, weight loads in flight per wave.
+struct Config {
+  int wv, mt, ch, d;
+};
+
+// MEDUSA_GEMM_WAVES (4 or 8, default 4) picks the workgroup size of the
+// 48-row tile; taller tiles use 8 waves, 4-tile chunks and 4 loads in flight.
+int small_waves() {
+  static const int v = [] {
+    const char* s = getenv("MEDUSA_GEMM_WAVES");
+    return (s && atoi(s) == 8) ? 8 : 4;
+  }();
+  return v;
+}
+
+// MEDUSA_LM_DEPTH (8 or 16, default 8): weight loads in flight per wave of
+// the LM head's 48-row tile.
+int lm_depth() {
+  static const int v = [] {
+    const char* s = getenv("MEDUSA_LM_DEPTH");
+    return (s && atoi(s) == 16) ? 16 : 8;
+  }();
+  return v;
+}
+
+Config config_for(int M, int epi) {
+  if (M <= 48) {
+    if (epi == EPI_LM && lm_depth() == 16)
+      return small_waves() == 8 ? Config{8, 3, 8, 16} : Config{4, 3, 8, 16};
+    return small_waves() == 8 ? Config{8, 3, 8, 8} : Config{4, 3, 4, 8};
+  }
+  return Config{8, 12, 4, 4};
+}
+
+bool fused_epilogue() {
+  static const bool v = [] {
+    const char* s = getenv("MEDUSA_GEMM_FUSED_EPILOGUE");
+    return s && atoi(s) != 0;
+  }();
+  return v;
+}
+
+template <class ET, int EPI>
+hipError_t launch_main(const GemmParams& p, int KS, hipStream_t st) {
+  const Config c = config_for(p.M, EPI);
+  const int groups = (p.N + 16 * c.wv - 1) / (16 * c.wv);
+  const int passes = (p.M + 16 * c.mt - 1) / (16 * c.mt);
+  dim3 grid(groups, KS, passes), block(64 * c.wv);
+  if (c.mt == 3 && c.wv == 4 && c.d == 8)
+    hipLaunchKernelGGL((node_gemm_kernel<ET, 4, 3, 4, 8, EPI>), grid, block, 0, st, p);
+  else if (c.mt == 3 && c.wv == 8 && c.d == 8)
+    hipLaunchKernelGGL((node_gemm_kernel<ET, 8, 3, 8, 8, EPI>), grid, block, 0, st, p);
+  else if (EPI == EPI_LM && c.mt == 3 && c.wv == 4)
+    hipLaunchKernelGGL((node_gemm_kernel<ET, 4, 3, 8, 16, EPI>), grid, block, 0, st, p);
+  else if (EPI == EPI_LM && c.mt == 3)
+    hipLaunchKernelGGL((node_gemm_kernel<ET, 8, 3, 8, 16, EPI>), grid, block, 0, st, p);
   else
-    hipLaunchKernelGGL((node_gemm_kernel<ET, 9, 4, LM>), grid, block, 0, st, p);
+    hipLaunchKernelGGL((node_gemm_kernel<ET, 8, 12, 4, 4, EPI>), grid, block, 0, st, p);
+  return hipGetLastError();
+}
+
+template <int EPI>
+hipError_t launch_split(GemmParams p, hipStream_t st) {
+  const int KS = gemm_splits(p.N, p.K, p.f32);
+  p.group_cols = 16 * config_for(p.M, EPI).wv;
+  p.fused = fused_epilogue();
+  hipError_t e = p.f32 ? launch_main<F32, EPI>(p, KS, st) : launch_main<BF16, EPI>(p, KS, st);
+  if (e != hipSuccess || p.fused) return e;
+  if (EPI == EPI_QKV) {
+    dim3 grid((p.N / 2 + 255) / 256, p.M);
+    if (p.f32)
+      hipLaunchKernelGGL(qkv_epilogue_kernel<F32>, grid, dim3(256), 0, st, p, KS);
+    else
+      hipLaunchKernelGGL(qkv_epilogue_kernel<BF16>, grid, dim3(256), 0, st, p, KS);
+  } else {
+    dim3 grid((p.N + 255) / 256, p.M);
+    if (p.f32)
+      hipLaunchKernelGGL(oproj_epilogue_kernel<F32>, grid, dim3(256), 0, st, p, KS);
+    else
+      hipLaunchKernelGGL(oproj_epilogue_kernel<BF16>, grid, dim3(256), 0, st, p, KS);
+  }
   return hipGetLastError();
 }
 
 }  // namespace
 
-int lm_head_blocks(int N) { return (N + kGemmCols - 1) / kGemmCols; }
+int lm_head_blocks(int N, int M) {
+  const int gc = 16 * config_for(M, EPI_LM).wv;
+  return (N + gc - 1) / gc;
+}
+int gemm_groups_max(int N) { return (N + 63) / 64; }
+int gemm_passes_max(int M) { return (M + 47) / 48; }
 
-// Slices of K so that the grid has at least ~512 workgroups while every
-// wave keeps at least one k-block per slice.
+size_t packed_weight_bytes(int rows, int K, bool f32) {
+  return (size_t)((rows + 15) / 16) * 16 * K * (f32 ? 4 : 2);
+}
+
+hipError_t launch_pack_weight(bool f32, const void* W, int rows, int K, int pair_dh, void* out,
+                              hipStream_t st) {
+  const size_t pieces = packed_weight_bytes(rows, K, f32) / 16;
+  const int threads = 256;
+  const size_t blocks = (pieces + threads - 1) / threads;
+  if (f32)
+    hipLaunchKernelGGL(pack_weight_kernel<F32>, dim3((unsigned)blocks), dim3(threads), 0, st,
+                       static_cast<const float*>(W), rows, K, pair_dh,
+                       static_cast<u32x4_t*>(out), pieces);
+  else
+    hipLaunchKernelGGL(pack_weight_kernel<BF16>, dim3((unsigned)blocks), dim3(threads), 0, st,
+                       static_cast<const uint16_t*>(W), rows, K, pair_dh,
+                       static_cast<u32x4_t*>(out), pieces);
+  return hipGetLastError();
+}
+
+// Slices of K: the smallest power of two that gives the grid at least
+// MEDUSA_GEMM_MIN_WAVES waves (default 1024, 4 per compute unit) while
+// every wave keeps at least 8 k-tiles per slice.
 int gemm_splits(int N, int K, bool f32) {
-  static const int min_wgs = [] {
-    const char* s = getenv("MEDUSA_GEMM_MIN_WGS");
-    const int v = s && *s ? atoi(s) : 384;
-    return v < 1 ? 1 : (v > 4096 ? 4096 : v);
+  static const int forced = [] {
+    const char* s = getenv("MEDUSA_GEMM_SPLITS");
+    return s && *s ? atoi(s) : 0;
   }();
-  const int groups = (N + kGemmCols - 1) / kGemmCols;
-  const int nkb = K / (f32 ? 32 : 64);
+  static const int min_waves = [] {
+    const char* s = getenv("MEDUSA_GEMM_MIN_WAVES");
+    const int v = s && *s ? atoi(s) : 1024;
+    return v < 1 ? 1 : (v > 65536 ? 65536 : v);
+  }();
+  const int stripes = (N + 15) / 16;
+  const int nkt = K / (f32 ? 16 : 32);
   int ks = 1;
-  while (groups * ks < min_wgs && ks * 2 * 4 <= nkb && ks < 32) ks *= 2;
+  if (forced > 0) {
+    while (ks * 2 <= forced && nkt / (ks * 2) >= 8 && ks < kMaxSplits) ks *= 2;
+    return ks;
+  }
+  while (stripes * ks < min_waves && nkt / (ks * 2) >= 8 && ks < kMaxSplits) ks *= 2;
   return ks;
 }
 
-hipError_t launch_qkv(const GemmParams& p, hipStream_t st) {
-  const int KS = gemm_splits(p.N, p.K, p.f32);
-  const int groups = (p.N + kGemmCols - 1) / kGemmCols;
-  hipError_t e = p.f32 ? launch_main<F32, false>(p, groups, KS, st)
-                       : launch_main<BF16, false>(p, groups, KS, st);
-  if (e != hipSuccess) return e;
-  dim3 grid(p.M, 3 * p.H);
-  if (p.f32)
-    hipLaunchKernelGGL(qkv_epilogue_kernel<F32>, grid, dim3(p.Dh / 2), 0, st, p, KS);
-  else
-    hipLaunchKernelGGL(qkv_epilogue_kernel<BF16>, grid, dim3(p.Dh / 2), 0, st, p, KS);
-  return hipGetLastError();
-}
+hipError_t launch_qkv(const GemmParams& p, hipStream_t st) { return launch_split<EPI_QKV>(p, st); }
 
 hipError_t launch_oproj(const GemmParams& p, hipStream_t st) {
-  const int KS = gemm_splits(p.N, p.K, p.f32);
-  const int groups = (p.N + kGemmCols - 1) / kGemmCols;
-  hipError_t e = p.f32 ? launch_main<F32, false>(p, groups, KS, st)
-                       : launch_main<BF16, false>(p, groups, KS, st);
-  if (e != hipSuccess) return e;
-  dim3 grid(p.M, (p.N + 255) / 256);
-  if (p.f32)
-    hipLaunchKernelGGL(oproj_epilogue_kernel<F32>, grid, dim3(256), 0, st, p, KS);
-  else
-    hipLaunchKernelGGL(oproj_epilogue_kernel<BF16>, grid, dim3(256), 0, st, p, KS);
-  return hipGetLastError();
+  return launch_split<EPI_OPROJ>(p, st);
 }
 
 hipError_t launch_lm_head(const GemmParams& p, float* row_stats, int* row_argmax,
                           hipStream_t st) {
-  const int groups = lm_head_blocks(p.N);
-  hipError_t e = p.f32 ? launch_main<F32, true>(p, groups, 1, st)
-                       : launch_main<BF16, true>(p, groups, 1, st);
+  hipError_t e = p.f32 ? launch_main<F32, EPI_LM>(p, 1, st) : launch_main<BF16, EPI_LM>(p, 1, st);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(row_stats_merge_kernel, dim3(p.M), dim3(64), 0, st, p.part, groups,
-                     p.inv_tau, row_stats, row_argmax);
+  hipLaunchKernelGGL(row_stats_merge_kernel, dim3(p.M), dim3(64), 0, st, p.part,
+                     lm_head_blocks(p.N, p.M), p.inv_tau, row_stats, row_argmax);
   return hipGetLastError();
 }
 

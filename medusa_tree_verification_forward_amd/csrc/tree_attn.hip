@@ -28,9 +28,13 @@ namespace {
 
 constexpr float kNegInf = -__builtin_huge_valf();
 
-// SC keys are staged per round: all K rows (row-major, padded by 16 bytes)
-// and V transposed (padded) go to LDS with every global load of the round
-// in flight at once, then the waves compute from LDS.
+// SC keys are staged per round: K rows (row-major, padded by 16 bytes) and V
+// transposed (padded) go to LDS; the global loads of the next round are in
+// flight while the waves compute the current one from LDS.
+//
+// V^T is written with 32-bit LDS stores: the two lanes that hold the same
+// 8 dims of keys 2j and 2j+1 swap halves first (one cross-lane permute per
+// dword), so each lane owns (key 2j, key 2j+1) pairs of 4 dims.
 template <class ET, int DH, int QT, int SC>
 __global__ __launch_bounds__(256) void tree_attn_kernel(AttnArgs a) {
   using S = typename ET::storage;
@@ -42,6 +46,7 @@ __global__ __launch_bounds__(256) void tree_attn_kernel(AttnArgs a) {
   constexpr int PAD = 16 / sizeof(S); // 16 bytes of padding per LDS row
   constexpr int VEC_PER_KEY = DH / PV;
   constexpr int LOADS = SC * VEC_PER_KEY / 256;   // 16-byte loads per thread per tensor
+  static_assert(LOADS * 256 == SC * VEC_PER_KEY, "round must divide over the threads");
   const int s = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const int T = a.T, H = a.H;
   const int L = min(max(a.kv_len[b], 0), a.Lmax);
@@ -94,37 +99,49 @@ __global__ __launch_bounds__(256) void tree_attn_kernel(AttnArgs a) {
     l_run[u] = 0.f;
   }
 
+  // global loads of one round (keys past the range read a valid row; masked later)
+  u32x4_t kv[LOADS], vv[LOADS];
+  auto load_round = [&](int kb) {
+#pragma unroll
+    for (int i = 0; i < LOADS; ++i) {
+      const int c = threadIdx.x + 256 * i;
+      const int kk = c / VEC_PER_KEY, part = c - kk * VEC_PER_KEY;
+      const size_t off = (size_t)min(kb + kk, kend - 1) * krow + PV * part;
+      kv[i] = load16(k_src + off);
+      vv[i] = load16(v_src + off);
+    }
+  };
+  load_round(kbeg);
+
   for (int kb = kbeg; kb < kend; kb += SC) {
     if (kb > kbeg) __syncthreads();   // previous round's readers are done
-    // ---- stage K and V^T (keys past the range read a valid row; masked later) ----
-    {
-      u32x4_t kv[LOADS], vv[LOADS];
+    // ---- stage K and V^T ----
 #pragma unroll
-      for (int i = 0; i < LOADS; ++i) {
-        const int c = threadIdx.x + 256 * i;
-        const int kk = c / VEC_PER_KEY, part = c - kk * VEC_PER_KEY;
-        const size_t off = (size_t)min(kb + kk, kend - 1) * krow + PV * part;
-        kv[i] = load16(k_src + off);
-        vv[i] = load16(v_src + off);
-      }
+    for (int i = 0; i < LOADS; ++i) {
+      const int c = threadIdx.x + 256 * i;
+      const int kk = c / VEC_PER_KEY, part = c - kk * VEC_PER_KEY;
+      *reinterpret_cast<u32x4_t*>(&ks[kk][PV * part]) = kv[i];
+      if constexpr (BF) {
+        // partner lane holds the same dims of key kk ^ 1
+        const bool odd = kk & 1;
+        const uint32_t r0 = (uint32_t)__shfl_xor((int)(odd ? vv[i][0] : vv[i][2]), VEC_PER_KEY);
+        const uint32_t r1 = (uint32_t)__shfl_xor((int)(odd ? vv[i][1] : vv[i][3]), VEC_PER_KEY);
+        const uint32_t lo0 = odd ? r0 : vv[i][0], hi0 = odd ? vv[i][2] : r0;
+        const uint32_t lo1 = odd ? r1 : vv[i][1], hi1 = odd ? vv[i][3] : r1;
+        const int d0 = PV * part + (odd ? 4 : 0);
+        uint32_t* col = reinterpret_cast<uint32_t*>(&vt[d0][kk & ~1]);
+        constexpr int RW = (SC + PAD) / 2;   // row stride in dwords
+        col[0] = (lo0 & 0xffffu) | (hi0 << 16);
+        col[RW] = (lo0 >> 16) | (hi0 & 0xffff0000u);
+        col[2 * RW] = (lo1 & 0xffffu) | (hi1 << 16);
+        col[3 * RW] = (lo1 >> 16) | (hi1 & 0xffff0000u);
+      } else {
 #pragma unroll
-      for (int i = 0; i < LOADS; ++i) {
-        const int c = threadIdx.x + 256 * i;
-        const int kk = c / VEC_PER_KEY, part = c - kk * VEC_PER_KEY;
-        *reinterpret_cast<u32x4_t*>(&ks[kk][PV * part]) = kv[i];
-        if constexpr (BF) {
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            vt[PV * part + 2 * e][kk] = (S)(vv[i][e] & 0xffffu);
-            vt[PV * part + 2 * e + 1][kk] = (S)(vv[i][e] >> 16);
-          }
-        } else {
-#pragma unroll
-          for (int e = 0; e < 4; ++e) vt[PV * part + e][kk] = __uint_as_float(vv[i][e]);
-        }
+        for (int e = 0; e < 4; ++e) vt[PV * part + e][kk] = __uint_as_float(vv[i][e]);
       }
     }
     __syncthreads();
+    if (kb + SC < kend) load_round(kb + SC);   // next round in flight during compute
 
 #pragma unroll
     for (int u = 0; u < QT; ++u) {
@@ -243,10 +260,10 @@ __global__ __launch_bounds__(256) void tree_attn_kernel(AttnArgs a) {
 }
 
 // Combine the splits of every (b, query, h): fixed order, tree split first.
-// The (m, l) pairs of up to kMaxSplitsFast splits are loaded together, then
-// the O rows, so each thread waits for two rounds of loads, not one per
-// split.
-constexpr int kMaxSplitsFast = 48;
+// Splits are read in batches of kMergeBatch with every load of a batch
+// issued before any is used (indices past the last split are clamped to it
+// and given zero weight), so a thread waits once per batch.
+constexpr int kMergeBatch = 16;
 template <class ET>
 __global__ void attn_merge_kernel(AttnArgs a) {
   using S = typename ET::storage;
@@ -257,32 +274,27 @@ __global__ void attn_merge_kernel(AttnArgs a) {
   const int ns = 1 + (L + kAttnChunk - 1) / kAttnChunk;
   const size_t base = ((size_t)b * H + h) * a.NS * T + i;
   float M = kNegInf, l = 0.f, acc = 0.f;
-  for (int s0 = 0; s0 < ns; s0 += kMaxSplitsFast) {
-    const int n = min(kMaxSplitsFast, ns - s0);
-    float ms[kMaxSplitsFast], lsv[kMaxSplitsFast], os[kMaxSplitsFast];
+  for (int s0 = 0; s0 < ns; s0 += kMergeBatch) {
+    float ms[kMergeBatch], lsv[kMergeBatch], os[kMergeBatch];
 #pragma unroll
-    for (int j = 0; j < kMaxSplitsFast; ++j) {
-      if (j < n) {
-        const size_t r = base + (size_t)(s0 + j) * T;
-        ms[j] = a.part_ml[r * 2];
-        lsv[j] = a.part_ml[r * 2 + 1];
-        os[j] = a.part_o[r * DH + x];
-      }
+    for (int j = 0; j < kMergeBatch; ++j) {
+      const size_t r = base + (size_t)min(s0 + j, ns - 1) * T;
+      ms[j] = a.part_ml[r * 2];
+      lsv[j] = a.part_ml[r * 2 + 1];
+      os[j] = a.part_o[r * DH + x];
     }
     float Mn = M;
 #pragma unroll
-    for (int j = 0; j < kMaxSplitsFast; ++j)
-      if (j < n) Mn = fmaxf(Mn, ms[j]);
+    for (int j = 0; j < kMergeBatch; ++j) Mn = fmaxf(Mn, ms[j]);
     const float c = M == kNegInf ? 0.f : __builtin_amdgcn_exp2f(M - Mn);
     l *= c;
     acc *= c;
 #pragma unroll
-    for (int j = 0; j < kMaxSplitsFast; ++j) {
-      if (j < n && ms[j] != kNegInf) {
-        const float w = __builtin_amdgcn_exp2f(ms[j] - Mn);
-        l += w * lsv[j];
-        acc += w * os[j];
-      }
+    for (int j = 0; j < kMergeBatch; ++j) {
+      const bool live = s0 + j < ns && ms[j] != kNegInf;
+      const float w = live ? __builtin_amdgcn_exp2f(ms[j] - Mn) : 0.f;
+      l += w * lsv[j];
+      acc += w * os[j];
     }
     M = Mn;
   }

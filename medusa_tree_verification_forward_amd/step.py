@@ -60,6 +60,11 @@ class VerifyStep:
         dev = {k: to_device(v) for k, v in inputs.items()
                if k not in ("ranks",) and isinstance(v, np.ndarray)}
         self.inp = dev
+        # the verify GEMMs read their weights in MFMA tile order, packed once here
+        self.packed = {name: L.packed_copy(self.shape, kind, dev[name], rows)
+                       for name, kind, rows in (("W_qkv", L.PACK_QKV, 3 * d),
+                                                ("W_o", L.PACK_PLAIN, d),
+                                                ("W_lm", L.PACK_PLAIN, V))}
         self.kv_len0 = dev["kv_len"].clone()
         kv = np.asarray(inputs["kv_len"])
         self._uniform_kv = int(kv[0]) if np.all(kv == kv[0]) else None
@@ -113,7 +118,8 @@ class VerifyStep:
 
     def verify(self, stream=None):
         o, i = self.out, self.inp
-        L.verify_forward(self.shape, i["E"], i["W_qkv"], i["W_o"], i["W_lm"], self.theta,
+        w = self.packed
+        L.verify_forward(self.shape, i["E"], w["W_qkv"], w["W_o"], w["W_lm"], self.theta,
                          o["tree_tokens"], o["position_ids"], o["tree_mask"], o["parent"],
                          i["k_cache"], i["v_cache"], i["kv_len"], self.tau, o["k_tree"],
                          o["v_tree"], o["y"], o["row_stats"], o["row_argmax"], o["child_logit"],
