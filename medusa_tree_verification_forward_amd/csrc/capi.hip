@@ -61,11 +61,12 @@ int env_int(const char* name, int dflt, int lo, int hi) {
   return std::min(hi, std::max(lo, v));
 }
 
-// Tuning knobs (rows per workgroup of the head streams). Workspace sizes are
-// computed for the smallest allowed value, so any setting fits.
-constexpr int kMinW2Rows = 16;
-int w1_rows() { static int v = env_int("MEDUSA_W1_ROWS", 16, 4, 4096); return v; }
-int w2_rows() { static int v = env_int("MEDUSA_W2_ROWS", 128, kMinW2Rows, 65536); return v; }
+// Tuning knobs (rows per wave of the head streams; a workgroup has 4 waves).
+// Workspace sizes are computed for the smallest allowed value, so any
+// setting fits.
+constexpr int kMinW2Rows = 16;   // rows per workgroup at the smallest setting
+int w1_rows() { static int v = env_int("MEDUSA_W1_ROWS", 4, 1, 64); return v; }
+int w2_rows() { static int v = env_int("MEDUSA_W2_ROWS", 40, kMinW2Rows / 4, 64); return v; }
 
 constexpr size_t kCounterBytes = 64 * 1024;   // workspace bytes reserved at offset 0 for counters
 
@@ -125,7 +126,7 @@ Layout layout_for(const medusa_shape* s) {
   L.counters = take(kCounterBytes);
   const size_t B = s->B, K = s->K, d = s->d, S = s->s_max;
   const int Gmax = (s->V + kMinW2Rows - 1) / kMinW2Rows;
-  L.G = (s->V + w2_rows() - 1) / w2_rows();
+  L.G = (s->V + 4 * w2_rows() - 1) / (4 * w2_rows());
   L.z = take(B * K * d * 4);
   L.part_val = take(B * K * Gmax * S * 4);
   L.part_id = take(B * K * Gmax * S * 4);
@@ -286,8 +287,8 @@ int medusa_heads_forward(const medusa_shape* shape, const float* h, const void* 
   a.part_m = at<float>(workspace, L.part_m);
   a.part_s = at<float>(workspace, L.part_s);
   a.G = L.G;
-  a.w1_rows_per_wg = w1_rows();
-  a.w2_rows_per_wg = w2_rows();
+  a.w1_rows_per_wave = w1_rows();
+  a.w2_rows_per_wave = w2_rows();
   a.ev_before = g_ev_before;
   a.ev_after = g_ev_after;
   hipError_t e = launch_heads(a, static_cast<hipStream_t>(stream));

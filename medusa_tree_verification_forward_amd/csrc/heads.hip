@@ -2,14 +2,15 @@
 //   z_k = h + SiLU(W1_k h + b1_k),  l_k = W2_k z_k,  top-s of l_k,  lse of l_k.
 //
 // Both products are matrix-vector streams over bf16 (or fp32) weights, bound
-// by HBM bandwidth. A wavefront owns ROWS weight rows at a time; each lane
-// reads 16-byte vectors along the row (consecutive lanes, consecutive
-// vectors), multiplies them with the activation held in LDS, and the row sums
-// are finished with DPP reductions. The W2 pass never writes the V logits
-// unless asked: each wave keeps a running top-s list spread over lanes 0..s-1
-// (one entry per lane, best first) plus online softmax statistics, and a
-// workgroup leaves one partial record per (sequence, head, row block). A small
-// merge kernel reduces the records of one (sequence, head) in a fixed order.
+// by HBM bandwidth. A wavefront owns up to 64 consecutive weight rows and
+// streams them as 1 KB wave loads with a fixed number in flight (each lane
+// reads 16 bytes of a row, consecutive lanes consecutive bytes), multiplies
+// them with the activation held in LDS and finishes each row sum with a DPP
+// reduction; lane l keeps row l's result. The W2 pass never writes the V
+// logits unless asked: after its stream a wave takes the top-s of its rows
+// (lanes 0..s-1, best first) and their softmax statistics, and a workgroup
+// leaves one partial record per (sequence, head, row block). A small merge
+// kernel reduces the records of one (sequence, head) in a fixed order.
 #include "common.h"
 #include "kernels.h"
 
@@ -19,113 +20,182 @@ namespace {
 constexpr float kNegInf = -__builtin_huge_valf();
 constexpr int kNoId = 0x7fffffff;
 
-// Partial dot products of ROWS consecutive weight rows with NB activation
-// vectors (fp32 in LDS, row stride ldx). acc[b][r] holds this lane's share.
-// Rows past `nrows` read the last valid row and are ignored by the caller.
-template <class ET, int NB, int ROWS>
-__device__ __forceinline__ void dot_rows(const typename ET::storage* __restrict__ W,
-                                         size_t row0, int nrows, int d,
-                                         const float* __restrict__ xs, int ldx,
-                                         float (&acc)[NB][ROWS]) {
-  constexpr int PV = ET::kPerVec;
-  const int lane = threadIdx.x & 63;
-  const int nvec = d / PV;
-#pragma unroll
-  for (int b = 0; b < NB; ++b)
-#pragma unroll
-    for (int r = 0; r < ROWS; ++r) acc[b][r] = 0.f;
-  const typename ET::storage* rowp[ROWS];
-#pragma unroll
-  for (int r = 0; r < ROWS; ++r) rowp[r] = W + (row0 + (size_t)(r < nrows ? r : nrows - 1)) * d;
+constexpr int kHeadWaves = 4;   // waves per workgroup
+constexpr int kRing = 8;        // weight loads in flight per wave
 
-  int c = lane;
-  // two vectors per row in flight per iteration
-  for (; c + 64 < nvec; c += 128) {
-    u32x4_t w0[ROWS], w1[ROWS];
-#pragma unroll
-    for (int r = 0; r < ROWS; ++r) {
-      w0[r] = load16_stream(rowp[r] + (size_t)c * PV);
-      w1[r] = load16_stream(rowp[r] + (size_t)(c + 64) * PV);
-    }
-#pragma unroll
-    for (int b = 0; b < NB; ++b) {
-      float x0[PV], x1[PV];
-#pragma unroll
-      for (int e = 0; e < PV; ++e) {
-        x0[e] = xs[b * ldx + c * PV + e];
-        x1[e] = xs[b * ldx + (c + 64) * PV + e];
-      }
-#pragma unroll
-      for (int r = 0; r < ROWS; ++r) {
-        float f0[PV], f1[PV];
-        ET::widen(w0[r], f0);
-        ET::widen(w1[r], f1);
-        float a = acc[b][r];
-#pragma unroll
-        for (int e = 0; e < PV; ++e) a = fmaf(f0[e], x0[e], a);
-#pragma unroll
-        for (int e = 0; e < PV; ++e) a = fmaf(f1[e], x1[e], a);
-        acc[b][r] = a;
-      }
+// Weight-row stream of one wave: rows [rb, rb + nrows) of W ([*][d], row-major),
+// nrows <= 64. Step t is one 1 KB wave load: chunk sg of row r covers
+// elements [sg*CW, sg*CW + CW) of the row (CW = 64 PV, lane l takes PV of
+// them at sg*CW + PV*l); a row has SPR = ceil(d / CW) chunks. kRing loads
+// are in flight; refills past the end re-read the last chunk (never used),
+// so every step issues exactly one load and the pipeline depth is fixed.
+// The activation xs (fp32 in LDS, NB vectors of stride ldx, zero past d)
+// is read at the same positions; lanes past the end of a row read a valid
+// weight and a zero activation.
+template <class ET, int NB>
+struct RowStream {
+  using St = typename ET::storage;
+  static constexpr int PV = ET::kPerVec;
+  static constexpr int CW = 64 * PV;
+  const St* __restrict__ W;
+  int rb, nrows, d, SPR, lane;
+  int fr, fs;   // row / chunk of the next refill
+  u32x4_t wr[kRing];
+
+  __device__ __forceinline__ const St* chunk_ptr(int r, int sg) const {
+    return W + (size_t)(rb + r) * d + min(sg * CW + PV * lane, d - PV);
+  }
+  __device__ __forceinline__ void refill(int j) {
+    const bool past = fr >= nrows;
+    wr[j] = load16_stream(chunk_ptr(past ? nrows - 1 : fr, past ? SPR - 1 : fs));
+    if (++fs == SPR) {
+      fs = 0;
+      ++fr;
     }
   }
-  if (c < nvec) {
-    u32x4_t w0[ROWS];
+  // Issue the first kRing loads (a wave without rows reads row rb_ok, a
+  // valid row, and never consumes the results).
+  __device__ __forceinline__ void start(const St* W_, int rb_, int nrows_, int d_, int rb_ok) {
+    W = W_;
+    rb = nrows_ > 0 ? rb_ : rb_ok;
+    nrows = nrows_ > 0 ? nrows_ : 1;
+    d = d_;
+    SPR = (d + CW - 1) / CW;
+    lane = threadIdx.x & 63;
+    fr = 0;
+    fs = 0;
 #pragma unroll
-    for (int r = 0; r < ROWS; ++r) w0[r] = load16_stream(rowp[r] + (size_t)c * PV);
+    for (int j = 0; j < kRing; ++j) refill(j);
+  }
+  template <bool GUARD>
+  __device__ __forceinline__ void step(int t, int j, int total, const float* xs, int ldx,
+                                       float (&acc)[NB], float (&win)[NB], int& cr, int& cs) {
+    if (!GUARD || t < total) {
+      float wf[PV];
+      ET::widen(wr[j], wf);
+      const float* xp = xs + cs * CW + PV * lane;
 #pragma unroll
-    for (int b = 0; b < NB; ++b) {
-      float x0[PV];
+      for (int b = 0; b < NB; ++b) {
+        float a = acc[b];
 #pragma unroll
-      for (int e = 0; e < PV; ++e) x0[e] = xs[b * ldx + c * PV + e];
+        for (int e = 0; e < PV; e += 4) {
+          const floatx4_t xv = *reinterpret_cast<const floatx4_t*>(xp + b * ldx + e);
+          a = fmaf(wf[e], xv[0], a);
+          a = fmaf(wf[e + 1], xv[1], a);
+          a = fmaf(wf[e + 2], xv[2], a);
+          a = fmaf(wf[e + 3], xv[3], a);
+        }
+        acc[b] = a;
+      }
+      if (++cs == SPR) {
 #pragma unroll
-      for (int r = 0; r < ROWS; ++r) {
-        float f0[PV];
-        ET::widen(w0[r], f0);
-        float a = acc[b][r];
-#pragma unroll
-        for (int e = 0; e < PV; ++e) a = fmaf(f0[e], x0[e], a);
-        acc[b][r] = a;
+        for (int b = 0; b < NB; ++b) {
+          const float v = wave_sum(acc[b]);
+          win[b] = lane == cr ? v : win[b];
+          acc[b] = 0.f;
+        }
+        cs = 0;
+        ++cr;
       }
     }
+    if (!GUARD || t + kRing < total) refill(j);
   }
+  // Consume the stream; lane l of win[b] receives row rb + l's dot product
+  // with activation b (lanes >= nrows keep their old value). The steady
+  // loop has every step and refill in range, so it keeps exactly kRing
+  // loads in flight; the last two rounds check their bounds.
+  __device__ __forceinline__ void run(const float* xs, int ldx, float (&win)[NB]) {
+    const int total = nrows * SPR;
+    float acc[NB];
+#pragma unroll
+    for (int b = 0; b < NB; ++b) acc[b] = 0.f;
+    int cr = 0, cs = 0;   // row / chunk being consumed
+    int t0 = 0;
+    for (; t0 + 2 * kRing <= total; t0 += kRing) {
+#pragma unroll
+      for (int j = 0; j < kRing; ++j) step<false>(t0 + j, j, total, xs, ldx, acc, win, cr, cs);
+    }
+    for (; t0 < total; t0 += kRing) {
+#pragma unroll
+      for (int j = 0; j < kRing; ++j) step<true>(t0 + j, j, total, xs, ldx, acc, win, cr, cs);
+    }
+  }
+};
+
+// Stage NB activation vectors (src + b * src_stride, d floats each) into LDS
+// as xs[b][0 .. ldx), zero past d. The first round of activation loads is
+// issued before the weight stream starts, so it is not queued behind it.
+// Ends with a barrier that leaves the weight loads in flight.
+template <class ET, int NB>
+__device__ __forceinline__ void stage_and_start(RowStream<ET, NB>& rs, const float* __restrict__ src,
+                                                size_t src_stride, int nb, int d, float* xs,
+                                                int ldx, const typename ET::storage* W, int rb,
+                                                int nrows, int rb_ok) {
+  constexpr int XR = 8;   // float4 loads per thread per round
+  const int n4 = NB * ldx / 4;
+  auto load_round = [&](int base, floatx4_t (&v)[XR]) {
+#pragma unroll
+    for (int u = 0; u < XR; ++u) {
+      const int i4 = min(base + u * (int)blockDim.x + (int)threadIdx.x, n4 - 1);
+      const int b = (4 * i4) / ldx, j = 4 * i4 - b * ldx;
+      const int bb = min(b, nb - 1), jj = min(j, d - 4);
+      v[u] = *reinterpret_cast<const floatx4_t*>(src + bb * src_stride + jj);
+      if (b >= nb || j >= d) v[u] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+    }
+  };
+  auto store_round = [&](int base, const floatx4_t (&v)[XR]) {
+#pragma unroll
+    for (int u = 0; u < XR; ++u) {
+      const int i4 = base + u * (int)blockDim.x + (int)threadIdx.x;
+      if (i4 < n4) *reinterpret_cast<floatx4_t*>(xs + 4 * i4) = v[u];
+    }
+  };
+  floatx4_t v[XR];
+  load_round(0, v);
+  rs.start(W, rb, nrows, d, rb_ok);
+  store_round(0, v);
+  const int per_round = XR * (int)blockDim.x;
+  for (int base = per_round; base < n4; base += per_round) {
+    load_round(base, v);
+    store_round(base, v);
+  }
+  lds_barrier();
 }
 
 // ---------------------------------------------------------------------------
 // z[b][k][i] = h[b][i] + silu(sum_j W1[k][i][j] h[b][j] + b1[k][i])
-// grid.x: blocks of `rows_per_wg` rows over the K*d rows of all heads.
-template <class ET, int NB, int ROWS, int WAVES>
-__global__ __launch_bounds__(WAVES * 64) void heads_w1_kernel(
+// Rows are numbered k*d + i over all heads; wave w of workgroup g streams
+// rows [(g*4 + w) * rpw, ... + rpw).
+template <class ET, int NB>
+__global__ __launch_bounds__(kHeadWaves * 64) void heads_w1_kernel(
     const float* __restrict__ h, int B, int b0, int K, int d,
     const typename ET::storage* __restrict__ W1, const float* __restrict__ b1,
-    float* __restrict__ z, int rows_per_wg) {
-  extern __shared__ float xs[];   // [NB][d]
+    float* __restrict__ z, int rpw) {
+  extern __shared__ float xs[];   // [NB][ldx]
+  constexpr int CW = RowStream<ET, NB>::CW;
+  const int ldx = (d + CW - 1) / CW * CW;
   const int nb = min(NB, B - b0);
-  for (int i = threadIdx.x; i < NB * d; i += blockDim.x) {
-    const int b = i / d, j = i - b * d;
-    xs[i] = b < nb ? h[(size_t)(b0 + b) * d + j] : 0.f;
-  }
-  __syncthreads();
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int total = K * d;
-  const int rbeg = blockIdx.x * rows_per_wg;
-  const int rend = min(total, rbeg + rows_per_wg);
-  for (int r0 = rbeg + wave * ROWS; r0 < rend; r0 += WAVES * ROWS) {
-    const int nrows = min(ROWS, rend - r0);
-    float acc[NB][ROWS];
-    dot_rows<ET, NB, ROWS>(W1, (size_t)r0, nrows, d, xs, d, acc);
+  const int rb = (blockIdx.x * kHeadWaves + wave) * rpw;
+  const int nrows = max(0, min(rpw, total - rb));
+  RowStream<ET, NB> rs;
+  stage_and_start<ET, NB>(rs, h + (size_t)b0 * d, d, nb, d, xs, ldx, W1, rb, nrows, 0);
+  if (nrows == 0) return;
+  float win[NB];
+#pragma unroll
+  for (int b = 0; b < NB; ++b) win[b] = 0.f;
+  rs.run(xs, ldx, win);
+  if (lane < nrows) {
+    const int row = rb + lane;   // row = k*d + i
+    const int k = row / d, i = row - k * d;
+    const float bias = b1 ? b1[row] : 0.f;
 #pragma unroll
     for (int b = 0; b < NB; ++b) {
-#pragma unroll
-      for (int r = 0; r < ROWS; ++r) {
-        const float u = wave_sum(acc[b][r]);
-        if (lane == r && r < nrows && b < nb) {
-          const int row = r0 + r;          // row = k*d + i
-          const int k = row / d, i = row - k * d;
-          const float uu = u + (b1 ? b1[row] : 0.f);
-          const float sig = 1.f / (1.f + exp_e(-uu));
-          z[((size_t)(b0 + b) * K + k) * d + i] = xs[b * d + i] + uu * sig;
-        }
+      if (b < nb) {
+        const float u = win[b] + bias;
+        const float sig = 1.f / (1.f + exp_e(-u));
+        z[((size_t)(b0 + b) * K + k) * d + i] = xs[b * ldx + i] + u * sig;
       }
     }
   }
@@ -158,74 +228,88 @@ __device__ __forceinline__ void stats_merge(float& m, float& s, float m2, float 
   m = mn;
 }
 
+// Best (value desc, id asc) over the wave, returned to every lane.
+__device__ __forceinline__ void wave_best(float& bv, int& bi) {
+#pragma unroll
+  for (int step = 0; step < 4; ++step) {
+    float ov;
+    int oi;
+    if (step == 0) { ov = dpp<kDppQuadXor1>(bv); oi = dppi<kDppQuadXor1>(bi); }
+    else if (step == 1) { ov = dpp<kDppQuadXor2>(bv); oi = dppi<kDppQuadXor2>(bi); }
+    else if (step == 2) { ov = dpp<kDppRowRor4>(bv); oi = dppi<kDppRowRor4>(bi); }
+    else { ov = dpp<kDppRowRor8>(bv); oi = dppi<kDppRowRor8>(bi); }
+    if (better(ov, oi, bv, bi)) { bv = ov; bi = oi; }
+  }
+  float wv = readlane_f(bv, 0);
+  int wi = __builtin_amdgcn_readlane(bi, 0);
+#pragma unroll
+  for (int row = 16; row < 64; row += 16) {
+    const float ov = readlane_f(bv, row);
+    const int oi = __builtin_amdgcn_readlane(bi, row);
+    if (better(ov, oi, wv, wi)) {
+      wv = ov;
+      wi = oi;
+    }
+  }
+  bv = wv;
+  bi = wi;
+}
+
 // ---------------------------------------------------------------------------
-// l = W2_k z_k for the rows of one block; running top-S and (max, sum exp).
-// grid = (G, K): block g of head k covers rows [g*rows_per_wg, ...).
+// l = W2_k z_k for the rows of one block; top-S and (max, sum exp) of them.
+// grid = (G, K): wave w of block g of head k streams rows
+// [(g*4 + w) * rpw, ... + rpw) of head k.
 // Partial records: part_val/part_id [B][K][G][S], part_m/part_s [B][K][G].
-template <class ET, int NB, int ROWS, int WAVES>
-__global__ __launch_bounds__(WAVES * 64) void heads_w2_kernel(
+template <class ET, int NB>
+__global__ __launch_bounds__(kHeadWaves * 64) void heads_w2_kernel(
     const float* __restrict__ z, int B, int b0, int K, int V, int d,
-    const typename ET::storage* __restrict__ W2, int rows_per_wg, int S,
+    const typename ET::storage* __restrict__ W2, int rpw, int S,
     float* __restrict__ head_logits, float* __restrict__ part_val, int* __restrict__ part_id,
     float* __restrict__ part_m, float* __restrict__ part_s, int G) {
-  extern __shared__ float xs[];   // [NB][d], then per-wave list exchange
+  extern __shared__ float xs[];   // [NB][ldx], then per-wave list exchange
+  constexpr int CW = RowStream<ET, NB>::CW;
+  const int ldx = (d + CW - 1) / CW * CW;
   const int k = blockIdx.y, g = blockIdx.x;
   const int nb = min(NB, B - b0);
-  for (int i = threadIdx.x; i < NB * d; i += blockDim.x) {
-    const int b = i / d, j = i - b * d;
-    xs[i] = b < nb ? z[((size_t)(b0 + b) * K + k) * d + j] : 0.f;
-  }
-  __syncthreads();
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int rbeg = g * rows_per_wg;
-  const int rend = min(V, rbeg + rows_per_wg);
-  const typename ET::storage* Wk = W2 + (size_t)k * V * d;
+  const int rb = (g * kHeadWaves + wave) * rpw;
+  const int nrows = max(0, min(rpw, V - rb));
+  RowStream<ET, NB> rs;
+  stage_and_start<ET, NB>(rs, z + ((size_t)b0 * K + k) * d, (size_t)K * d, nb, d, xs, ldx,
+                          W2 + (size_t)k * V * d, rb, nrows, 0);
+  float win[NB];
+#pragma unroll
+  for (int b = 0; b < NB; ++b) win[b] = kNegInf;
+  if (nrows > 0) rs.run(xs, ldx, win);
 
   float tv[NB], m[NB], s[NB];
   int ti[NB];
+  const bool valid = lane < nrows;
 #pragma unroll
   for (int b = 0; b < NB; ++b) {
+    const float v = valid ? win[b] : kNegInf;
+    if (head_logits && b < nb && valid)
+      head_logits[((size_t)(b0 + b) * K + k) * V + rb + lane] = v;
+    // statistics of this wave's rows
+    const float mx = wave_max(v);
+    m[b] = mx;
+    s[b] = mx == kNegInf ? 0.f : wave_sum(valid ? exp_e(v - mx) : 0.f);
+    // top-S of this wave's rows, best first in lanes 0..S-1
+    float cv = v;
+    int ci = valid ? rb + lane : kNoId;
     tv[b] = kNegInf;
     ti[b] = kNoId;
-    m[b] = kNegInf;
-    s[b] = 0.f;
-  }
-  for (int r0 = rbeg + wave * ROWS; r0 < rend; r0 += WAVES * ROWS) {
-    const int nrows = min(ROWS, rend - r0);
-    float acc[NB][ROWS];
-    dot_rows<ET, NB, ROWS>(Wk, (size_t)r0, nrows, d, xs, d, acc);
-#pragma unroll
-    for (int b = 0; b < NB; ++b) {
-      float v[ROWS];
-#pragma unroll
-      for (int r = 0; r < ROWS; ++r) v[r] = wave_sum(acc[b][r]);
-      if (head_logits && b < nb && lane < nrows) {
-        float mine = v[0];
-#pragma unroll
-        for (int r = 1; r < ROWS; ++r)
-          if (lane == r) mine = v[r];
-        head_logits[((size_t)(b0 + b) * K + k) * V + r0 + lane] = mine;
+    for (int r = 0; r < S; ++r) {
+      float bv = cv;
+      int bi = ci;
+      wave_best(bv, bi);
+      if (lane == r) {
+        tv[b] = bv;
+        ti[b] = bi;
       }
-      // online statistics over the valid rows
-      float bm = v[0];
-#pragma unroll
-      for (int r = 1; r < ROWS; ++r)
-        if (r < nrows) bm = fmaxf(bm, v[r]);
-      float bs = 0.f;
-#pragma unroll
-      for (int r = 0; r < ROWS; ++r)
-        if (r < nrows) bs += exp_e(v[r] - bm);
-      stats_merge(m[b], s[b], bm, bs);
-      // top-S insertion, gated by the current S-th entry
-      float thv = readlane_f(tv[b], S - 1);
-      int thi = __builtin_amdgcn_readlane(ti[b], S - 1);
-#pragma unroll
-      for (int r = 0; r < ROWS; ++r) {
-        if (r < nrows && better(v[r], r0 + r, thv, thi)) {
-          list_insert(tv[b], ti[b], v[r], r0 + r, S);
-          thv = readlane_f(tv[b], S - 1);
-          thi = __builtin_amdgcn_readlane(ti[b], S - 1);
-        }
+      if (ci == bi) {
+        cv = kNegInf;
+        ci = kNoId;
       }
     }
   }
@@ -233,9 +317,9 @@ __global__ __launch_bounds__(WAVES * 64) void heads_w2_kernel(
   // longer needed)
   __syncthreads();
   float* lv = xs;                                        // [WAVES][NB][S]
-  int* li = reinterpret_cast<int*>(xs + WAVES * NB * MAXS_LDS);
-  float* lm = xs + 2 * WAVES * NB * MAXS_LDS;            // [WAVES][NB]
-  float* ls = lm + WAVES * NB;
+  int* li = reinterpret_cast<int*>(xs + kHeadWaves * NB * MAXS_LDS);
+  float* lm = xs + 2 * kHeadWaves * NB * MAXS_LDS;       // [WAVES][NB]
+  float* ls = lm + kHeadWaves * NB;
 #pragma unroll
   for (int b = 0; b < NB; ++b) {
     if (lane < S) {
@@ -251,7 +335,7 @@ __global__ __launch_bounds__(WAVES * 64) void heads_w2_kernel(
   if (wave != 0) return;
 #pragma unroll
   for (int b = 0; b < NB; ++b) {
-    for (int w = 1; w < WAVES; ++w) {
+    for (int w = 1; w < kHeadWaves; ++w) {
       for (int e = 0; e < S; ++e) {
         const float v = lv[(w * NB + b) * MAXS_LDS + e];
         const int id = li[(w * NB + b) * MAXS_LDS + e];
@@ -393,26 +477,25 @@ __global__ __launch_bounds__(64) void heads_merge_kernel(
 
 template <class ET, int NB>
 hipError_t launch_heads_nb(const HeadsArgs& a, int b0, hipStream_t st) {
-  constexpr int ROWS = NB <= 2 ? 4 : (NB == 4 ? 2 : 1);
-  constexpr int WAVES = NB <= 2 ? 4 : (NB == 4 ? 8 : 16);
-  const size_t lds_x = (size_t)NB * a.d * sizeof(float);
-  const int total1 = a.K * a.d;
-  const int g1 = (total1 + a.w1_rows_per_wg - 1) / a.w1_rows_per_wg;
-  hipLaunchKernelGGL((heads_w1_kernel<ET, NB, ROWS, WAVES>), dim3(g1), dim3(WAVES * 64), lds_x,
-                     st, a.h, a.B, b0, a.K, a.d,
-                     reinterpret_cast<const typename ET::storage*>(a.W1), a.b1, a.z,
-                     a.w1_rows_per_wg);
+  constexpr int CW = RowStream<ET, NB>::CW;
+  const int ldx = (a.d + CW - 1) / CW * CW;
+  const size_t lds_x = (size_t)NB * ldx * sizeof(float);
+  const int rows1 = kHeadWaves * a.w1_rows_per_wave;
+  const int g1 = (a.K * a.d + rows1 - 1) / rows1;
+  hipLaunchKernelGGL((heads_w1_kernel<ET, NB>), dim3(g1), dim3(kHeadWaves * 64), lds_x, st, a.h,
+                     a.B, b0, a.K, a.d, reinterpret_cast<const typename ET::storage*>(a.W1),
+                     a.b1, a.z, a.w1_rows_per_wave);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const size_t lds_list = (size_t)WAVES * NB * (2 * MAXS_LDS + 2) * sizeof(float);
+  const size_t lds_list = (size_t)kHeadWaves * NB * (2 * MAXS_LDS + 2) * sizeof(float);
   const size_t lds2 = lds_x > lds_list ? lds_x : lds_list;
   if (a.ev_before) {
     e = hipEventRecord(a.ev_before, st);
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL((heads_w2_kernel<ET, NB, ROWS, WAVES>), dim3(a.G, a.K), dim3(WAVES * 64),
-                     lds2, st, a.z, a.B, b0, a.K, a.V, a.d,
-                     reinterpret_cast<const typename ET::storage*>(a.W2), a.w2_rows_per_wg,
+  hipLaunchKernelGGL((heads_w2_kernel<ET, NB>), dim3(a.G, a.K), dim3(kHeadWaves * 64), lds2, st,
+                     a.z, a.B, b0, a.K, a.V, a.d,
+                     reinterpret_cast<const typename ET::storage*>(a.W2), a.w2_rows_per_wave,
                      a.S, a.head_logits, a.part_val, a.part_id, a.part_m, a.part_s, a.G);
   e = hipGetLastError();
   if (e != hipSuccess) return e;

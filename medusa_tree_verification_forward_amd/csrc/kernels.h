@@ -29,9 +29,9 @@ struct HeadsArgs {
   int* part_id;           // [B][K][G][S]
   float* part_m;          // [B][K][G]
   float* part_s;          // [B][K][G]
-  int G;                  // row blocks per head
-  int w1_rows_per_wg;
-  int w2_rows_per_wg;
+  int G;                  // row blocks per head (4 waves of w2_rows_per_wave rows)
+  int w1_rows_per_wave;   // 1..64
+  int w2_rows_per_wave;   // 4..64
   hipEvent_t ev_before;   // optional: recorded around the W2 kernel
   hipEvent_t ev_after;
 };
@@ -97,7 +97,9 @@ struct GemmParams {
   int* counters;               // fused epilogue: one zeroed counter per (group, pass)
   int group_cols;              // set by the launcher
   int fused;                   // set by the launcher
+  int kmajor;                  // set by the launcher: packed tile order
 };
+bool packed_kmajor();
 // Weights W[rows][K] of the node GEMMs are packed into MFMA tiles (see
 // node_gemm.hip) before use; pair_dh = Dh reorders the rows of each head
 // into rotation pairs (W_qkv), 0 keeps them in order.
@@ -110,8 +112,7 @@ int lm_head_blocks(int N, int M);          // column groups of the LM head
 int gemm_splits(int N, int K, bool f32);   // K slices of the QKV / output projection GEMMs
 hipError_t launch_qkv(const GemmParams& p, hipStream_t st);
 hipError_t launch_oproj(const GemmParams& p, hipStream_t st);
-hipError_t launch_lm_head(const GemmParams& p, float* row_stats, int* row_argmax,
-                          hipStream_t st);
+hipError_t launch_lm_head(GemmParams p, float* row_stats, int* row_argmax, hipStream_t st);
 
 // ---- tree attention ---------------------------------------------------------------
 constexpr int kAttnChunk = 256;   // prefix keys per split

@@ -36,6 +36,7 @@
 // W = sum e^{(l-m)/tau} (l-m)/tau; the logit of every tree node's token
 // under its parent's row; optional full logits. A merge kernel combines the
 // column groups of a row.
+#include <stdio.h>
 #include <stdlib.h>
 
 #include <type_traits>
@@ -96,14 +97,16 @@ __device__ __forceinline__ int packed_source_row(int n, int pair_dh) {
 // elements KT kt + PV (l / 16) .. + PV - 1 (KT = 4 PV). Rows >= rows are 0.
 template <class ET>
 __global__ void pack_weight_kernel(const typename ET::storage* __restrict__ W, int rows, int K,
-                                   int pair_dh, u32x4_t* __restrict__ out, size_t pieces) {
+                                   int pair_dh, int kmajor, u32x4_t* __restrict__ out,
+                                   size_t pieces) {
   constexpr int PV = ET::kPerVec, KT = 4 * PV;
   const size_t q = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (q >= pieces) return;
-  const int nkt = K / KT;
+  const int nkt = K / KT, ntiles = (rows + 15) / 16;
   const size_t tile = q >> 6;
   const int l = (int)(q & 63);
-  const int nt = (int)(tile / nkt), kt = (int)(tile % nkt);
+  const int nt = kmajor ? (int)(tile % ntiles) : (int)(tile / nkt);
+  const int kt = kmajor ? (int)(tile / ntiles) : (int)(tile % nkt);
   const int n = 16 * nt + (l & 15);
   u32x4_t v = {0u, 0u, 0u, 0u};
   if (n < rows) {
@@ -173,7 +176,7 @@ __device__ __forceinline__ const float* partial_at(const GemmParams& p, int r, i
 }
 
 template <class ET, int WV, int MT, int CH, int D, int EPI>
-__global__ __launch_bounds__(64 * WV, (WV == 4 || MT <= 3) ? 4 : 2) void node_gemm_kernel(
+__global__ __launch_bounds__(64 * WV, WV == 4 ? 4 : 2) void node_gemm_kernel(
     GemmParams p) {
   using St = typename ET::storage;
   constexpr int PV = ET::kPerVec, KT = 4 * PV;   // k elements per tile
@@ -192,9 +195,13 @@ __global__ __launch_bounds__(64 * WV, (WV == 4 || MT <= 3) ? 4 : 2) void node_ge
   const int ntiles = (p.N + 15) >> 4;
   const int n0 = g * GC;
   const int col = n0 + 16 * wave + li;
-  const u32x4_t* __restrict__ wp = reinterpret_cast<const u32x4_t*>(p.W) +
-                                   ((size_t)min(g * WV + wave, ntiles - 1) * nkt + kt_lo) * 64 +
-                                   lane;
+  // tile (nt, kt) sits at nt * nkt + kt (stripe-major) or kt * ntiles + nt
+  // (k-major); consecutive k-tiles of a stripe are `wstep` pieces apart
+  const int nt = min(g * WV + wave, ntiles - 1);
+  const size_t wstep = p.kmajor ? (size_t)ntiles * 64 : 64;
+  const u32x4_t* __restrict__ wp =
+      reinterpret_cast<const u32x4_t*>(p.W) +
+      (p.kmajor ? ((size_t)kt_lo * ntiles + nt) : ((size_t)nt * nkt + kt_lo)) * 64 + lane;
 
   __shared__ u32x4_t sA0[CH][MT][64];
   __shared__ u32x4_t sA1[CH][MT][64];
@@ -210,16 +217,17 @@ __global__ __launch_bounds__(64 * WV, (WV == 4 || MT <= 3) ? 4 : 2) void node_ge
     const int src = p.a_rows ? min(max(p.a_rows[r], 0), p.a_nrows - 1) : r;
     asrc[i] = A + (size_t)src * p.lda + (size_t)kt_lo * KT + PV * lq;
   }
-  u32x4_t ra[NAW];   // A fragments of the next chunk, in flight
+  // A fragments of chunks c+1 and c+2 are in flight in two register sets
+  u32x4_t ra0[NAW], ra1[NAW];
   // Past the slice end the k-tile index is clamped (those values are never read).
-  auto load_a = [&](int c) {
+  auto load_a = [&](int c, u32x4_t(&ra)[NAW]) {
 #pragma unroll
     for (int i = 0; i < NAW; ++i) {
       const int kt = min(c * CH + (wave + WV * i) / MT, nloc - 1);
       ra[i] = load16(asrc[i] + (size_t)kt * KT);
     }
   };
-  auto store_a = [&](u32x4_t(&buf)[CH][MT][64]) {
+  auto store_a = [&](u32x4_t(&buf)[CH][MT][64], const u32x4_t(&ra)[NAW]) {
 #pragma unroll
     for (int i = 0; i < NAW; ++i) {
       const int f = wave + WV * i;
@@ -232,21 +240,24 @@ __global__ __launch_bounds__(64 * WV, (WV == 4 || MT <= 3) ? 4 : 2) void node_ge
   u32x4_t wr[D];
 
   const int nch = (nloc + CH - 1) / CH;
-  load_a(0);
+  load_a(0, ra0);
+  load_a(1, ra1);
 #pragma unroll
-  for (int j = 0; j < D; ++j) wr[j] = load16_stream(wp + (size_t)min(j, nloc - 1) * 64);
-  store_a(sA0);
-  load_a(1);
+  for (int j = 0; j < D; ++j) wr[j] = load16_stream(wp + (size_t)min(j, nloc - 1) * wstep);
+  store_a(sA0, ra0);
+  load_a(2, ra0);
   lds_barrier();
 
   // Chunk c: CH k-tiles from the weight registers against the A fragments
   // in `cur`; each consumed register is refilled D k-tiles ahead. Then the
-  // A fragments of chunk c+1 (loaded a chunk earlier) go to `nxt`, the loads
-  // of chunk c+2 start, and one barrier publishes `nxt`. A steady chunk has
-  // every step and every refill in range, so the loop keeps a fixed number
-  // of loads in flight; the last chunks check their bounds.
-  auto chunk = [&](int c, u32x4_t(&cur)[CH][MT][64], u32x4_t(&nxt)[CH][MT][64], auto steady,
-                   auto odd) {
+  // A fragments of chunk c+1 (loaded two chunks earlier, in `ra`) go to
+  // `nxt`, the loads of chunk c+3 start in `ra`, and one barrier publishes
+  // `nxt`. Loading A two chunks ahead keeps its wait from draining the
+  // weight ring (D = 2 CH loads stay in flight across the barrier). A steady
+  // chunk has every step and every refill in range, so the loop keeps a fixed
+  // number of loads in flight; the last chunks check their bounds.
+  auto chunk = [&](int c, u32x4_t(&cur)[CH][MT][64], u32x4_t(&nxt)[CH][MT][64],
+                   u32x4_t(&ra)[NAW], auto steady, auto odd) {
     constexpr bool S = decltype(steady)::value;
     constexpr int R0 = decltype(odd)::value ? CH : 0;   // ring slot of the chunk's first step
 #pragma unroll
@@ -256,14 +267,14 @@ __global__ __launch_bounds__(64 * WV, (WV == 4 || MT <= 3) ? 4 : 2) void node_ge
         const u32x4_t b = wr[(R0 + j) % D];
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) acc[mt] = frag_mfma<ET>(cur[j][mt][lane], b, acc[mt]);
-        if (S || s + D < nloc) wr[(R0 + j) % D] = load16_stream(wp + (size_t)(s + D) * 64);
+        if (S || s + D < nloc) wr[(R0 + j) % D] = load16_stream(wp + (size_t)(s + D) * wstep);
       }
       // one k-tile at a time: hoisting later LDS reads only raises pressure
       __builtin_amdgcn_sched_barrier(0);
     }
     if (S || c + 1 < nch) {
-      store_a(nxt);
-      load_a(c + 2);
+      store_a(nxt, ra);
+      load_a(c + 3, ra);
       lds_barrier();
     }
   };
@@ -273,14 +284,14 @@ __global__ __launch_bounds__(64 * WV, (WV == 4 || MT <= 3) ? 4 : 2) void node_ge
   const std::integral_constant<bool, true> odd{};
   int c = 0;
   for (; (c + 2) * CH + D <= nloc; c += 2) {
-    chunk(c, sA0, sA1, steady, even);
-    chunk(c + 1, sA1, sA0, steady, odd);
+    chunk(c, sA0, sA1, ra1, steady, even);
+    chunk(c + 1, sA1, sA0, ra0, steady, odd);
   }
   for (; c < nch; ++c) {
     if (c & 1)
-      chunk(c, sA1, sA0, guarded, odd);
+      chunk(c, sA1, sA0, ra0, guarded, odd);
     else
-      chunk(c, sA0, sA1, guarded, even);
+      chunk(c, sA0, sA1, ra1, guarded, even);
   }
 
   if constexpr (EPI != EPI_LM) {
@@ -475,24 +486,43 @@ int small_waves() {
   return v;
 }
 
-// MEDUSA_LM_DEPTH (8 or 16, default 8): weight loads in flight per wave of
-// the LM head's 48-row tile.
-int lm_depth() {
-  static const int v = [] {
-    const char* s = getenv("MEDUSA_LM_DEPTH");
-    return (s && atoi(s) == 16) ? 16 : 8;
+// MEDUSA_LM_CFG ("wv,ch", default "8,8"): waves per workgroup and k-tiles per
+// A chunk of the LM head's 48-row tile (4,4: 8 weight loads in flight per
+// wave; 8,4: 8,8 chunks with 8 in flight; 8,8: 16 in flight).
+Config lm_config() {
+  static const Config v = [] {
+    const char* s = getenv("MEDUSA_LM_CFG");
+    int wv = 8, ch = 8;
+    if (s && *s) sscanf(s, "%d,%d", &wv, &ch);
+    if (wv == 4 && ch == 4) return Config{4, 3, 4, 8};
+    if (wv == 8 && ch == 4) return Config{8, 3, 8, 8};
+    return Config{8, 3, 8, 16};
   }();
   return v;
 }
 
 Config config_for(int M, int epi) {
   if (M <= 48) {
-    if (epi == EPI_LM && lm_depth() == 16)
-      return small_waves() == 8 ? Config{8, 3, 8, 16} : Config{4, 3, 8, 16};
+    if (epi == EPI_LM) return lm_config();
     return small_waves() == 8 ? Config{8, 3, 8, 8} : Config{4, 3, 4, 8};
   }
   return Config{8, 12, 4, 4};
 }
+
+}  // namespace
+
+// Packed tiles are ordered k-major: tile (nt, kt) at kt * ntiles + nt, so
+// the waves of a launch, which advance through k together, read adjacent
+// memory. MEDUSA_PACK_KMAJOR=0 selects stripe-major (nt * nkt + kt).
+bool packed_kmajor() {
+  static const bool v = [] {
+    const char* s = getenv("MEDUSA_PACK_KMAJOR");
+    return !(s && *s && atoi(s) == 0);
+  }();
+  return v;
+}
+
+namespace {
 
 bool fused_epilogue() {
   static const bool v = [] {
@@ -508,13 +538,11 @@ hipError_t launch_main(const GemmParams& p, int KS, hipStream_t st) {
   const int groups = (p.N + 16 * c.wv - 1) / (16 * c.wv);
   const int passes = (p.M + 16 * c.mt - 1) / (16 * c.mt);
   dim3 grid(groups, KS, passes), block(64 * c.wv);
-  if (c.mt == 3 && c.wv == 4 && c.d == 8)
+  if (c.mt == 3 && c.wv == 4)
     hipLaunchKernelGGL((node_gemm_kernel<ET, 4, 3, 4, 8, EPI>), grid, block, 0, st, p);
-  else if (c.mt == 3 && c.wv == 8 && c.d == 8)
+  else if (c.mt == 3 && c.d == 8)
     hipLaunchKernelGGL((node_gemm_kernel<ET, 8, 3, 8, 8, EPI>), grid, block, 0, st, p);
-  else if (EPI == EPI_LM && c.mt == 3 && c.wv == 4)
-    hipLaunchKernelGGL((node_gemm_kernel<ET, 4, 3, 8, 16, EPI>), grid, block, 0, st, p);
-  else if (EPI == EPI_LM && c.mt == 3)
+  else if (c.mt == 3)
     hipLaunchKernelGGL((node_gemm_kernel<ET, 8, 3, 8, 16, EPI>), grid, block, 0, st, p);
   else
     hipLaunchKernelGGL((node_gemm_kernel<ET, 8, 12, 4, 4, EPI>), grid, block, 0, st, p);
@@ -526,6 +554,7 @@ hipError_t launch_split(GemmParams p, hipStream_t st) {
   const int KS = gemm_splits(p.N, p.K, p.f32);
   p.group_cols = 16 * config_for(p.M, EPI).wv;
   p.fused = fused_epilogue();
+  p.kmajor = packed_kmajor();
   hipError_t e = p.f32 ? launch_main<F32, EPI>(p, KS, st) : launch_main<BF16, EPI>(p, KS, st);
   if (e != hipSuccess || p.fused) return e;
   if (EPI == EPI_QKV) {
@@ -564,11 +593,11 @@ hipError_t launch_pack_weight(bool f32, const void* W, int rows, int K, int pair
   const size_t blocks = (pieces + threads - 1) / threads;
   if (f32)
     hipLaunchKernelGGL(pack_weight_kernel<F32>, dim3((unsigned)blocks), dim3(threads), 0, st,
-                       static_cast<const float*>(W), rows, K, pair_dh,
+                       static_cast<const float*>(W), rows, K, pair_dh, (int)packed_kmajor(),
                        static_cast<u32x4_t*>(out), pieces);
   else
     hipLaunchKernelGGL(pack_weight_kernel<BF16>, dim3((unsigned)blocks), dim3(threads), 0, st,
-                       static_cast<const uint16_t*>(W), rows, K, pair_dh,
+                       static_cast<const uint16_t*>(W), rows, K, pair_dh, (int)packed_kmajor(),
                        static_cast<u32x4_t*>(out), pieces);
   return hipGetLastError();
 }
@@ -603,8 +632,8 @@ hipError_t launch_oproj(const GemmParams& p, hipStream_t st) {
   return launch_split<EPI_OPROJ>(p, st);
 }
 
-hipError_t launch_lm_head(const GemmParams& p, float* row_stats, int* row_argmax,
-                          hipStream_t st) {
+hipError_t launch_lm_head(GemmParams p, float* row_stats, int* row_argmax, hipStream_t st) {
+  p.kmajor = packed_kmajor();
   hipError_t e = p.f32 ? launch_main<F32, EPI_LM>(p, 1, st) : launch_main<BF16, EPI_LM>(p, 1, st);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(row_stats_merge_kernel, dim3(p.M), dim3(64), 0, st, p.part,
