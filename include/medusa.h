@@ -154,6 +154,9 @@ int medusa_heads_forward(const medusa_shape* shape, const float* h, const void* 
  *   retrieve     [P][K+1] int32 (out): node lists of root-to-leaf paths in
  *                lexicographic leaf order, -1 padded
  *   parent       [T] int32 (out, parent[0] = -1); depth [T] int32 (out)
+ * tree_mask, retrieve, parent and depth depend only on tree_ranks: each may
+ * be NULL to skip writing it (a decode loop writes them once per spec and
+ * passes NULL afterwards); tree_tokens and position_ids are always written.
  */
 int medusa_build_tree(const medusa_shape* shape, const int32_t* tree_ranks_host,
                       int draft_mode, const int32_t* root_tok, const int32_t* topk_ids,
@@ -184,9 +187,12 @@ int medusa_tree_attention(const medusa_shape* shape, const void* q, const void* 
  * operand tiles: tile (nt, kt) holds packed rows 16*nt .. 16*nt+15 and
  * columns c*kt .. c*kt+c-1 (c = 32 for bf16, 16 for fp32) of a row-major
  * [rows][d] matrix, stored as 64 consecutive 16-byte pieces, piece l =
- * packed row 16*nt + l%16, columns c*kt + (c/4)*(l/16) .. +c/4-1; tiles are
- * ordered nt-major, kt-minor, so 16 rows stream contiguously along d. Packed
- * rows past `rows` (up to the next multiple of 16) are zero.
+ * packed row 16*nt + l%16, columns c*kt + (c/4)*(l/16) .. +c/4-1. Tile
+ * (nt, kt) is stored at tile index kt*ntiles + nt (ntiles = ceil(rows/16)):
+ * k-major, so the 16-row stripes that a launch streams side by side sit
+ * next to each other. Packed rows past `rows` (up to the next multiple of 16)
+ * are zero. The packed buffer is only meaningful to this library: produce
+ * it with medusa_pack_weight in the process that uses it.
  * kind MEDUSA_PACK_PLAIN: packed row n is row n (W_o, W_lm).
  * kind MEDUSA_PACK_QKV (W_qkv, rows = 3d): within every block of Dh rows
  *   (one head of q, k or v) packed row 16*t + j is row 8*t + j for j < 8 and

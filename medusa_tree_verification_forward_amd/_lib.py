@@ -154,6 +154,7 @@ def heads_forward(shape, h, W1, W2, topk_ids, topk_logits, workspace, *, b1=None
 def build_tree(shape, tree_ranks: np.ndarray, root_tok, kv_len, tree_tokens, tree_mask,
                position_ids, retrieve, parent, depth, *, draft_mode=DRAFT_TOPK, topk_ids=None,
                head_logits=None, head_lse=None, u_draft=None, stream=None):
+    """tree_mask, retrieve, parent and depth may be None (not written)."""
     ranks = np.ascontiguousarray(tree_ranks, dtype=np.int32)
     rp = ranks.ctypes.data if ranks.size else None
     _check(_lib.medusa_build_tree(

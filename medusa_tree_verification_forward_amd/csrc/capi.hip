@@ -215,6 +215,7 @@ int make_plan(const medusa_shape* s, const int32_t* ranks, TreePlan* plan, int* 
     }
     plan->parent[n + 1] = (uint8_t)par;
     plan->last_rank[n + 1] = (uint8_t)tup[n].back();
+    plan->depth[n + 1] = (uint8_t)tup[n].size();
     has_child[par] = 1;
   }
   int P = 0;
@@ -302,6 +303,7 @@ int medusa_build_tree(const medusa_shape* shape, const int32_t* tree_ranks_host,
                       const float* u_draft_or_null, const int32_t* kv_len,
                       int32_t* tree_tokens, uint8_t* tree_mask, int32_t* position_ids,
                       int32_t* retrieve, int32_t* parent, int32_t* depth, void* stream) {
+  // tree_mask, retrieve, parent and depth are optional (see medusa.h)
   int rc = check_shape(shape);
   if (rc) return rc;
   if (draft_mode != MEDUSA_DRAFT_TOPK && draft_mode != MEDUSA_DRAFT_SAMPLE)
@@ -309,11 +311,11 @@ int medusa_build_tree(const medusa_shape* shape, const int32_t* tree_ranks_host,
   REQUIRE_PTR(root_tok);
   REQUIRE_PTR(kv_len);
   REQUIRE_PTR(tree_tokens);
-  REQUIRE_PTR(tree_mask);
   REQUIRE_PTR(position_ids);
-  REQUIRE_PTR(retrieve);
-  REQUIRE_PTR(parent);
-  REQUIRE_PTR(depth);
+  OPTIONAL_PTR(tree_mask);
+  OPTIONAL_PTR(retrieve);
+  OPTIONAL_PTR(parent);
+  OPTIONAL_PTR(depth);
   if (draft_mode == MEDUSA_DRAFT_TOPK) {
     REQUIRE_PTR(topk_ids);
   } else {

@@ -360,11 +360,16 @@ __global__ __launch_bounds__(kHeadWaves * 64) void heads_w2_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// Merge the G partial records of one (sequence, head): one wavefront.
-// grid = (K, B). Each lane keeps a private sorted list of its candidates in
-// registers (a candidate that does not beat the lane's S-th entry costs one
-// compare); then S selection rounds take the best lane head with a DPP
-// (value desc, id asc) reduction and pop it from its lane.
+// Merge the G partial records of one (sequence, head): one workgroup of
+// kMergeThreads. grid = (K, B). Every thread loads its share of the G*S
+// candidates at once (kMergeBatch per round) and keeps a private sorted
+// list in registers; each wave then takes its top S in S rounds of a
+// wave-wide (value desc, id asc) selection, and wave 0 selects the final S
+// from the waves' lists. The log-sum-exp combines the G (max, sum) records
+// with fixed-order reductions.
+constexpr int kMergeThreads = 256;
+constexpr int kMergeBatch = 4;
+
 template <int SMAX>
 __device__ __forceinline__ void reg_insert(float (&lv)[SMAX], int (&li)[SMAX], float v, int id,
                                            int S) {
@@ -382,71 +387,24 @@ __device__ __forceinline__ void reg_insert(float (&lv)[SMAX], int (&li)[SMAX], f
   }
 }
 
+// S rounds of selection over the lanes' sorted lists; lane r < S receives
+// the r-th best of the wave.
 template <int SMAX>
-__global__ __launch_bounds__(64) void heads_merge_kernel(
-    int K, int G, int S, const float* __restrict__ part_val, const int* __restrict__ part_id,
-    const float* __restrict__ part_m, const float* __restrict__ part_s,
-    int* __restrict__ topk_ids, float* __restrict__ topk_logits, float* __restrict__ lse) {
-  const int k = blockIdx.x, b = blockIdx.y;
-  const int lane = threadIdx.x;
-  const size_t rec0 = ((size_t)b * K + k) * G;
-  float lv[SMAX];
-  int li[SMAX];
-#pragma unroll
-  for (int j = 0; j < SMAX; ++j) {
-    lv[j] = kNegInf;
-    li[j] = kNoId;
-  }
-  const int ncand = G * S;
-  for (int c = lane; c < ncand; c += 64) {
-    const float v = part_val[rec0 * S + c];
-    const int id = part_id[rec0 * S + c];
-    // the S-th entry sits at a runtime index: select it with an unrolled scan
-    float tv = kNegInf;
-    int ti = kNoId;
-#pragma unroll
-    for (int j = 0; j < SMAX; ++j)
-      if (j == S - 1) {
-        tv = lv[j];
-        ti = li[j];
-      }
-    if (better(v, id, tv, ti)) reg_insert<SMAX>(lv, li, v, id, S);
-  }
-  float out_v = kNegInf;
-  int out_i = kNoId;
+__device__ __forceinline__ void wave_select(float (&lv)[SMAX], int (&li)[SMAX], int S,
+                                            float& out_v, int& out_i) {
+  const int lane = threadIdx.x & 63;
+  out_v = kNegInf;
+  out_i = kNoId;
   for (int r = 0; r < S; ++r) {
     float bv = lv[0];
     int bi = li[0];
-#pragma unroll
-    for (int step = 0; step < 4; ++step) {
-      float ov;
-      int oi;
-      if (step == 0) { ov = dpp<kDppQuadXor1>(bv); oi = dppi<kDppQuadXor1>(bi); }
-      else if (step == 1) { ov = dpp<kDppQuadXor2>(bv); oi = dppi<kDppQuadXor2>(bi); }
-      else if (step == 2) { ov = dpp<kDppRowRor4>(bv); oi = dppi<kDppRowRor4>(bi); }
-      else { ov = dpp<kDppRowRor8>(bv); oi = dppi<kDppRowRor8>(bi); }
-      if (better(ov, oi, bv, bi)) { bv = ov; bi = oi; }
-    }
-    // best of the four 16-lane rows (uniform)
-    float wv = readlane_f(bv, 0);
-    int wi = __builtin_amdgcn_readlane(bi, 0);
-#pragma unroll
-    for (int row = 16; row < 64; row += 16) {
-      const float ov = readlane_f(bv, row);
-      const int oi = __builtin_amdgcn_readlane(bi, row);
-      if (better(ov, oi, wv, wi)) {
-        wv = ov;
-        wi = oi;
-      }
-    }
-    bv = wv;
-    bi = wi;
+    wave_best(bv, bi);
     if (lane == r) {
       out_v = bv;
       out_i = bi;
     }
     // pop the winner from the lane that holds it (ids are unique)
-    if (li[0] == bi) {
+    if (li[0] == bi && bi != kNoId) {
 #pragma unroll
       for (int j = 0; j < SMAX - 1; ++j) {
         lv[j] = lv[j + 1];
@@ -456,22 +414,126 @@ __global__ __launch_bounds__(64) void heads_merge_kernel(
       li[SMAX - 1] = kNoId;
     }
   }
+}
+
+template <int SMAX>
+__global__ __launch_bounds__(kMergeThreads) void heads_merge_kernel(
+    int K, int G, int S, const float* __restrict__ part_val, const int* __restrict__ part_id,
+    const float* __restrict__ part_m, const float* __restrict__ part_s,
+    int* __restrict__ topk_ids, float* __restrict__ topk_logits, float* __restrict__ lse) {
+  constexpr int NW = kMergeThreads / 64;
+  const int k = blockIdx.x, b = blockIdx.y;
+  const int t = threadIdx.x, wave = t >> 6, lane = t & 63;
+  const size_t rec0 = ((size_t)b * K + k) * G;
+  __shared__ float sv[NW][MAXS_LDS];
+  __shared__ int si[NW][MAXS_LDS];
+  __shared__ float red[kMergeThreads];
+
+  // softmax records first, so their loads fly with the candidates'
+  float pm[kMergeBatch], ps[kMergeBatch];
+  const bool want_lse = lse != nullptr;
+#pragma unroll
+  for (int u = 0; u < kMergeBatch; ++u) {
+    const int g = min(t + kMergeThreads * u, G - 1);
+    pm[u] = want_lse ? part_m[rec0 + g] : kNegInf;
+    ps[u] = want_lse ? part_s[rec0 + g] : 0.f;
+  }
+
+  float lv[SMAX];
+  int li[SMAX];
+#pragma unroll
+  for (int j = 0; j < SMAX; ++j) {
+    lv[j] = kNegInf;
+    li[j] = kNoId;
+  }
+  const int ncand = G * S;
+  for (int base = 0; base < ncand; base += kMergeThreads * kMergeBatch) {
+    float v[kMergeBatch];
+    int id[kMergeBatch];
+#pragma unroll
+    for (int u = 0; u < kMergeBatch; ++u) {
+      const int c = base + t + kMergeThreads * u;
+      const int cc = min(c, ncand - 1);
+      v[u] = part_val[rec0 * S + cc];
+      id[u] = part_id[rec0 * S + cc];
+      if (c >= ncand) {
+        v[u] = kNegInf;
+        id[u] = kNoId;
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kMergeBatch; ++u) {
+      // the S-th entry sits at a runtime index: select it with an unrolled scan
+      float tv = kNegInf;
+      int ti = kNoId;
+#pragma unroll
+      for (int j = 0; j < SMAX; ++j)
+        if (j == S - 1) {
+          tv = lv[j];
+          ti = li[j];
+        }
+      if (better(v[u], id[u], tv, ti)) reg_insert<SMAX>(lv, li, v[u], id[u], S);
+    }
+  }
+  float wv;
+  int wi;
+  wave_select<SMAX>(lv, li, S, wv, wi);
+  if (lane < S) {
+    sv[wave][lane] = wv;
+    si[wave][lane] = wi;
+  }
+
+  // log-sum-exp of the G records: block max, then block sum, fixed order
+  float mx = kNegInf;
+  if (want_lse) {
+#pragma unroll
+    for (int u = 0; u < kMergeBatch; ++u)
+      if (t + kMergeThreads * u < G) mx = fmaxf(mx, pm[u]);
+    for (int g = t + kMergeThreads * kMergeBatch; g < G; g += kMergeThreads)
+      mx = fmaxf(mx, part_m[rec0 + g]);
+    red[t] = mx;
+  }
+  __syncthreads();
+  if (want_lse) {
+    float m_all = kNegInf;
+    for (int w = 0; w < NW; ++w) m_all = fmaxf(m_all, wave_max(red[w * 64 + lane]));
+    float ssum = 0.f;
+#pragma unroll
+    for (int u = 0; u < kMergeBatch; ++u)
+      if (t + kMergeThreads * u < G && pm[u] != kNegInf) ssum += ps[u] * exp_e(pm[u] - m_all);
+    for (int g = t + kMergeThreads * kMergeBatch; g < G; g += kMergeThreads) {
+      const float m2 = part_m[rec0 + g];
+      if (m2 != kNegInf) ssum += part_s[rec0 + g] * exp_e(m2 - m_all);
+    }
+    __syncthreads();
+    red[t] = ssum;
+    __syncthreads();
+    if (wave == 0) {
+      float tot = 0.f;
+      for (int w = 0; w < NW; ++w) tot += wave_sum(red[w * 64 + lane]);
+      if (lane == 0) lse[(size_t)b * K + k] = m_all + __logf(tot);
+    }
+  } else {
+    __syncthreads();
+  }
+  if (wave != 0) return;
+  // final selection over the waves' lists: lane l < NW*S holds one entry
+  float fv[SMAX];
+  int fi[SMAX];
+#pragma unroll
+  for (int j = 0; j < SMAX; ++j) {
+    fv[j] = kNegInf;
+    fi[j] = kNoId;
+  }
+  if (lane < NW * S) {
+    fv[0] = sv[lane / S][lane % S];
+    fi[0] = si[lane / S][lane % S];
+  }
+  wave_select<SMAX>(fv, fi, S, wv, wi);
   const size_t out = ((size_t)b * K + k) * S;
   if (lane < S) {
-    topk_ids[out + lane] = out_i;
-    topk_logits[out + lane] = out_v;
-  }
-  if (lse) {
-    float mm = kNegInf;
-    for (int g = lane; g < G; g += 64) mm = fmaxf(mm, part_m[rec0 + g]);
-    mm = wave_max(mm);
-    float ss = 0.f;
-    for (int g = lane; g < G; g += 64) {
-      const float pm = part_m[rec0 + g];
-      if (pm != kNegInf) ss += part_s[rec0 + g] * exp_e(pm - mm);
-    }
-    ss = wave_sum(ss);
-    if (lane == 0) lse[(size_t)b * K + k] = mm + __logf(ss);
+    topk_ids[out + lane] = wi;
+    topk_logits[out + lane] = wv;
   }
 }
 
@@ -519,7 +581,8 @@ hipError_t launch_heads_et(const HeadsArgs& a, hipStream_t st) {
     if (e != hipSuccess) return e;
   }
 #define MERGE_LAUNCH(SM)                                                                    \
-  hipLaunchKernelGGL(heads_merge_kernel<SM>, dim3(a.K, a.B), dim3(64), 0, st, a.K, a.G, a.S, \
+  hipLaunchKernelGGL(heads_merge_kernel<SM>, dim3(a.K, a.B), dim3(kMergeThreads), 0, st, a.K, \
+                     a.G, a.S, \
                      a.part_val, a.part_id, a.part_m, a.part_s, a.topk_ids, a.topk_logits,   \
                      a.lse)
   if (a.S <= 4)

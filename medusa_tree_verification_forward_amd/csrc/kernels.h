@@ -46,6 +46,7 @@ struct TreePlan {
   int K;
   uint8_t parent[MAXT];      // parent[0] unused
   uint8_t last_rank[MAXT];   // last_rank[0] unused
+  uint8_t depth[MAXT];       // depth[0] = 0
 };
 struct TreeArgs {
   TreePlan plan;
@@ -58,11 +59,11 @@ struct TreeArgs {
   const float* u_draft;          // [B][T] (sample mode)
   const int32_t* kv_len;         // [B]
   int32_t* tokens;               // [B][T]
-  uint8_t* mask;                 // [T][T]
+  uint8_t* mask;                 // [T][T] or null
   int32_t* position_ids;         // [B][T]
-  int32_t* retrieve;             // [P][K+1]
-  int32_t* parent;               // [T]
-  int32_t* depth;                // [T]
+  int32_t* retrieve;             // [P][K+1] or null
+  int32_t* parent;               // [T] or null
+  int32_t* depth;                // [T] or null
 };
 hipError_t launch_tree(const TreeArgs& a, hipStream_t st);
 

@@ -452,9 +452,20 @@ __global__ __launch_bounds__(64) void row_stats_merge_kernel(const float* __rest
   const int r = blockIdx.x, lane = threadIdx.x;
   float m = kNegInf, s = 0.f, w = 0.f;
   int a = 0x7fffffff;
-  for (int g = lane; g < G; g += 64) {
-    const float* rec = part + ((size_t)r * G + g) * 4;
-    rec_merge(m, s, w, a, rec[0], rec[1], rec[2], __float_as_int(rec[3]), inv_tau);
+  // all of a round's records are loaded before any is merged
+  constexpr int RB = 4;
+  for (int g0 = 0; g0 < G; g0 += 64 * RB) {
+    floatx4_t rec[RB];
+#pragma unroll
+    for (int u = 0; u < RB; ++u) {
+      const int g = min(g0 + lane + 64 * u, G - 1);
+      rec[u] = *reinterpret_cast<const floatx4_t*>(part + ((size_t)r * G + g) * 4);
+    }
+#pragma unroll
+    for (int u = 0; u < RB; ++u)
+      if (g0 + lane + 64 * u < G)
+        rec_merge(m, s, w, a, rec[u][0], rec[u][1], rec[u][2], __float_as_int(rec[u][3]),
+                  inv_tau);
   }
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) {

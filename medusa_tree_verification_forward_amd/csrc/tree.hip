@@ -2,13 +2,14 @@
 // ids, root-to-leaf paths and node tokens.
 //
 // The host has validated the rank-path spec and reduced it to (parent, own
-// rank) per node; one workgroup per sequence rebuilds the rest on the device
-// with one thread per node (T <= 256):
-//   depth      by walking parents,
+// rank, depth) per node. Per step, one thread per node writes
+//   tokens     = the root token, or head (depth-1)'s token of the node's rank,
+//   positions  = kv_len[b] + depth.
+// The topology, which only depends on the spec, is written when asked (once
+// per spec is enough), by one workgroup with one thread per node (T <= 256):
 //   mask[i][j] = 1 iff j is i or an ancestor of i,
-//   positions  = kv_len[b] + depth (one index per depth),
 //   paths      = the leaves in lexicographic rank-path order,
-//   tokens     = the root token, or head (depth-1)'s token of the node's rank.
+//   parent, depth.
 // In sampling mode a second kernel draws each node's token from its depth's
 // head softmax by inverse CDF.
 #include "common.h"
@@ -24,8 +25,24 @@ __device__ __forceinline__ bool lex_less(const uint8_t* a, int da, const uint8_t
   return da < db;
 }
 
-__global__ __launch_bounds__(256) void tree_kernel(TreeArgs a) {
+__global__ __launch_bounds__(256) void tree_nodes_kernel(TreeArgs a) {
   const int b = blockIdx.x;
+  const int n = threadIdx.x;
+  const int T = a.plan.T, K = a.plan.K;
+  if (n >= T) return;
+  const int d = a.plan.depth[n];
+  a.position_ids[(size_t)b * T + n] = a.kv_len[b] + d;
+  int tok;
+  if (n == 0)
+    tok = a.root_tok[b];
+  else if (a.sample)
+    return;   // drawn by tree_sample_kernel
+  else
+    tok = a.topk_ids[((size_t)b * K + (d - 1)) * a.S + a.plan.last_rank[n]];
+  a.tokens[(size_t)b * T + n] = tok;
+}
+
+__global__ __launch_bounds__(256) void tree_topology_kernel(TreeArgs a) {
   const int n = threadIdx.x;
   const int T = a.plan.T, K = a.plan.K;
   __shared__ uint8_t par[MAXT], lrank[MAXT], dep[MAXT], has_child[MAXT];
@@ -34,13 +51,12 @@ __global__ __launch_bounds__(256) void tree_kernel(TreeArgs a) {
   if (n < T) {
     par[n] = a.plan.parent[n];
     lrank[n] = a.plan.last_rank[n];
+    dep[n] = a.plan.depth[n];
     has_child[n] = 0;
   }
   __syncthreads();
   if (n < T) {
-    int d = 0;
-    for (int x = n; x != 0 && d < K; x = par[x]) ++d;
-    dep[n] = (uint8_t)d;
+    const int d = dep[n];
     int x = n;
     anc[n][d] = (uint8_t)n;
     for (int j = d - 1; j >= 0; --j) {
@@ -52,28 +68,17 @@ __global__ __launch_bounds__(256) void tree_kernel(TreeArgs a) {
   }
   __syncthreads();
   const int d = n < T ? dep[n] : 0;
-  if (n < T) {
-    int tok;
-    if (n == 0)
-      tok = a.root_tok[b];
-    else if (a.sample)
-      tok = -1;   // drawn by tree_sample_kernel
-    else
-      tok = a.topk_ids[((size_t)b * K + (d - 1)) * a.S + lrank[n]];
-    a.tokens[(size_t)b * T + n] = tok;
-    a.position_ids[(size_t)b * T + n] = a.kv_len[b] + d;
-  }
-  if (b != 0) return;   // the topology is shared by every sequence
   // mask[i][j] = j is i or an ancestor of i, written cooperatively
-  for (int e = n; e < T * T; e += blockDim.x) {
-    const int i = e / T, j = e - i * T;
-    a.mask[e] = (dep[j] <= dep[i] && anc[i][dep[j]] == j) ? 1 : 0;
-  }
+  if (a.mask)
+    for (int e = n; e < T * T; e += blockDim.x) {
+      const int i = e / T, j = e - i * T;
+      a.mask[e] = (dep[j] <= dep[i] && anc[i][dep[j]] == j) ? 1 : 0;
+    }
   if (n >= T) return;
-  a.parent[n] = n == 0 ? -1 : (int)par[n];
-  a.depth[n] = d;
+  if (a.parent) a.parent[n] = n == 0 ? -1 : (int)par[n];
+  if (a.depth) a.depth[n] = d;
   const bool leaf = T == 1 ? true : (n >= 1 && !has_child[n]);
-  if (!leaf) return;
+  if (!leaf || !a.retrieve) return;
   int p = 0;
   for (int m = 1; m < T; ++m)
     if (m != n && !has_child[m] && lex_less(tup[m], dep[m], tup[n], d)) ++p;
@@ -137,9 +142,7 @@ __global__ __launch_bounds__(1024) void tree_sample_kernel(TreeArgs a) {
   // nodes of this depth, one per thread
   int count = 0;
   for (int n = 1; n < T; ++n) {
-    int dd = 0;
-    for (int x = n; x != 0; x = a.plan.parent[x]) ++dd;
-    if (dd != kd + 1) continue;
+    if (a.plan.depth[n] != kd + 1) continue;
     if (count++ % 1024 != t) continue;
     const float target = a.u_draft[(size_t)b * T + n] * E[64];
     int tok = -1;
@@ -170,9 +173,15 @@ __global__ __launch_bounds__(1024) void tree_sample_kernel(TreeArgs a) {
 }  // namespace
 
 hipError_t launch_tree(const TreeArgs& a, hipStream_t st) {
-  hipLaunchKernelGGL(tree_kernel, dim3(a.B), dim3(256), 0, st, a);
+  hipLaunchKernelGGL(tree_nodes_kernel, dim3(a.B), dim3(256), 0, st, a);
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess || !a.sample) return e;
+  if (e != hipSuccess) return e;
+  if (a.mask || a.retrieve || a.parent || a.depth) {
+    hipLaunchKernelGGL(tree_topology_kernel, dim3(1), dim3(256), 0, st, a);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  if (!a.sample) return e;
   hipLaunchKernelGGL(tree_sample_kernel, dim3(a.plan.K, a.B), dim3(1024), 0, st, a);
   return hipGetLastError();
 }

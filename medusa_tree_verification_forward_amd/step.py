@@ -87,6 +87,9 @@ class VerifyStep:
             out_tokens=z((B, K + 1), i32), next_root=z((B,), i32), h_next=z((B, d), f),
         )
         self.ws = torch.zeros(L.workspace_bytes(self.shape), dtype=torch.uint8, device="cuda")
+        # the topology (mask, paths, parent, depth) depends only on the spec:
+        # written once here, then every step writes tokens and positions only
+        self.tree(topology=True)
 
     @staticmethod
     def _count_paths(ranks: np.ndarray) -> int:
@@ -106,11 +109,13 @@ class VerifyStep:
                         self.ws, head_lse=o["head_lse"], head_logits=o["head_logits"], z=o["z"],
                         stream=stream)
 
-    def tree(self, stream=None):
+    def tree(self, stream=None, topology: bool = False):
         o, i = self.out, self.inp
         sample = self.mode == "exact"
+        topo = (lambda t: t) if topology else (lambda t: None)  # noqa: E731
         L.build_tree(self.shape, self.ranks, i["root"], i["kv_len"], o["tree_tokens"],
-                     o["tree_mask"], o["position_ids"], o["retrieve"], o["parent"], o["depth"],
+                     topo(o["tree_mask"]), o["position_ids"], topo(o["retrieve"]),
+                     topo(o["parent"]), topo(o["depth"]),
                      draft_mode=L.DRAFT_SAMPLE if sample else L.DRAFT_TOPK,
                      topk_ids=o["topk_ids"], head_logits=o["head_logits"],
                      head_lse=o["head_lse"], u_draft=i.get("u_draft") if sample else None,

@@ -104,7 +104,9 @@ def test_null_and_misaligned_pointers_rejected():
     from workloads import cartesian_ranks
     ranks = cartesian_ranks((2, 2))
     shape = _shape(M, K=2, N=6, P=4, s_max=2)
-    assert _call_tree(M, shape, ranks, tree_mask=None) == M._lib.ERR_ARG
+    assert _call_tree(M, shape, ranks, tree_tokens=None) == M._lib.ERR_ARG
+    assert "tree_tokens" in M.last_error()
+    assert _call_tree(M, shape, ranks, tree_mask=FAKE + 2) == M._lib.ERR_ARG
     assert "tree_mask" in M.last_error()
     assert _call_tree(M, shape, ranks, retrieve=FAKE + 4) == M._lib.ERR_ARG
     assert "aligned" in M.last_error()

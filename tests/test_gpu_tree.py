@@ -142,3 +142,33 @@ def test_sampled_tree_tokens_follow_inverse_cdf():
                 assert near < 1e-5, (b, n, g[b, n], ref[n], near)
                 mismatches += 1
     assert mismatches <= 2
+
+
+@pytest.mark.gpu
+def test_topology_outputs_optional():
+    """Per-step calls pass NULL for the spec-only outputs: those buffers stay
+    untouched and tokens / positions match a full call's."""
+    import torch
+    import medusa_tree_verification_forward_amd as M
+    require_gpu()
+    s = (3, 2, 2, 1, 1)
+    rng = np.random.default_rng(7)
+    K, S, B, V = len(s), max(s), 2, 32000
+    spec = cartesian_ranks(s)
+    root = rng.integers(0, V, size=B).astype(np.int32)
+    topk = rng.integers(0, V, size=(B, K, S)).astype(np.int32)
+    kv_len = rng.integers(0, 4096, size=B).astype(np.int32)
+    topo, full = _build(spec, K, S, B, V, root, topk, kv_len)
+    N = spec.shape[0]
+    T = N + 1
+    shape = M.make_shape(B, 128, V, K, 1, 128, 8192, N, topo.P, S, "bf16")
+    tok = poisoned((B, T), torch.int32)
+    pos = poisoned((B, T), torch.int32)
+    mask = poisoned((T, T), torch.uint8)
+    before = host(mask).copy()
+    M.build_tree(shape, spec, dev(root), dev(kv_len), tok, None, pos, None, None, None,
+                 topk_ids=dev(topk))
+    torch.cuda.synchronize()
+    assert np.array_equal(host(tok), full["tok"])
+    assert np.array_equal(host(pos), full["pos"])
+    assert np.array_equal(host(mask), before)
