@@ -51,17 +51,79 @@ def w2_kernel_bytes(w):
 
 
 def cpu_baseline(w, inp):
-    """The oracle, as it stands, on one full step of the same workload."""
+    """The oracle, as it stands, timed on a bounded sample of the same step.
+
+    A whole oracle step at these shapes takes minutes (its five float64 head
+    passes dominate), so the sample is: the head stage for head 0 alone
+    (W1 and W2 of one head) plus everything after the heads for the full
+    step -- candidate tree, verifier forward, typical acceptance, posterior
+    and commit. The step time is estimated as K * head + rest.
+    """
     from threadpoolctl import threadpool_info
-    from oracle import step as OSTEP
+    from oracle import heads as OH, posterior as OP, tree as OT, verifier as OV
+    from oracle.numerics import widen
     threads = max([t.get("num_threads", 1) for t in threadpool_info()] + [1])
+    h = np.asarray(inp["h"], dtype=np.float64)
     t0 = time.perf_counter()
-    OSTEP.verify_step(inp, H=w.H, Dh=w.Dh, s_max=w.s_max, mode=w.mode, tau=w.tau, eps=w.eps,
-                      delta=w.delta, theta=w.rope_theta, bf16=True, want_margins=False)
-    dt = time.perf_counter() - t0
-    return {"value": 1.0 / dt, "unit": "steps/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"1 full {w.name} step (float64 NumPy, BLAS threads {threads}, "
-                      f"affinity cores {len(os.sched_getaffinity(0))}), {dt:.1f} s"}
+    _, hl = OH.heads_forward(h, inp["W1"][:1], inp["W2"][:1], inp.get("b1"))
+    t_head = time.perf_counter() - t0
+    # the rest of the step, with head 0's top-s pool standing in for every depth
+    ids, _, _ = OH.heads_topk(hl, w.s_max)
+    topk = np.repeat(ids, w.K, axis=1)
+    t1 = time.perf_counter()
+    topo = OT.topology(inp["ranks"], w.K)
+    for b in range(w.B):
+        L = int(inp["kv_len"][b])
+        tok = OT.draft_tokens_topk(topo, int(inp["root"][b]), topk[b])
+        pos = OT.position_ids(topo, L)
+        vf = OV.verifier_forward(inp["E"], inp["W_qkv"], inp["W_o"], inp["W_lm"], tok, pos,
+                                 topo.mask, inp["k_cache"][b], inp["v_cache"][b], L, w.H, w.Dh,
+                                 w.rope_theta, True)
+        p, ent, am = OV.row_distribution(vf["logits"], w.tau)
+        acc = OP.accept_typical(topo, tok, p, ent, w.eps, w.delta)
+        post = OP.posterior_deterministic(topo, tok, acc, am)
+        OP.commit(topo, post["last_node"], vf["k"], vf["v"], vf["y"], widen(inp["k_cache"][b]),
+                  widen(inp["v_cache"][b]), L)
+    t_rest = time.perf_counter() - t1
+    est = w.K * t_head + t_rest
+    return {"value": 1.0 / est, "unit": "steps/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{w.name}: head stage for 1 of {w.K} heads ({t_head:.1f} s) + tree, "
+                      f"verifier, typical acceptance, posterior and commit of the step "
+                      f"({t_rest:.1f} s); step estimated as {w.K} x head + rest = {est:.1f} s "
+                      f"(float64 NumPy, BLAS threads {threads}, affinity cores "
+                      f"{len(os.sched_getaffinity(0))})"}
+
+
+# HBM traffic of the dominant kernel from rocprofv3 FETCH_SIZE / WRITE_SIZE
+# counters, recorded in a committed profile summary together with a digest
+# of the kernel's sources; reported only while the sources still match.
+TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "heads_w2_vicuna7b_hbm_counters.md")
+W2_SOURCES = ["medusa_tree_verification_forward_amd/csrc/heads.hip",
+              "medusa_tree_verification_forward_amd/csrc/common.h",
+              "medusa_tree_verification_forward_amd/csrc/kernels.h"]
+
+
+def w2_source_digest():
+    import hashlib
+    h = hashlib.sha256()
+    for rel in W2_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def recorded_traffic():
+    """Bytes per launch from the counter summary, or None if absent or stale."""
+    import re
+    try:
+        text = open(TRAFFIC_SUMMARY).read()
+    except OSError:
+        return None
+    dig = re.search(r"source digest: `([0-9a-f]+)`", text)
+    val = re.search(r"HBM bytes per launch: `([0-9.e+]+)`", text)
+    if not dig or not val or dig.group(1) != w2_source_digest():
+        return None
+    return float(val.group(1))
 
 
 def main():
@@ -70,10 +132,15 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--print-digest", action="store_true",
+                    help="print the W2 kernel source digest (for the counter summary) and exit")
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="before the timed loop, run a plain device-to-device copy of this "
                          "many bytes 3 times (a known-size kernel for scaling HBM counters)")
     args = ap.parse_args()
+    if args.print_digest:
+        print(w2_source_digest())
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only: this build runs the verify step on a single "
               f"MI355X; --gpus {args.gpus} is not supported.", file=sys.stderr)
@@ -162,8 +229,10 @@ def main():
                           "frac": alg / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS},
         "roofline": {"kernel": "heads_w2 (vocabulary projection + fused top-s)",
                      "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
-                     "avg_us": w2_ms * 1e3, "bytes_per_launch": w2b},
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": recorded_traffic(),
+                     "avg_us": w2_ms * 1e3, "bytes_per_launch": w2b,
+                     "timing": "HIP events recorded on the launch stream around every W2 "
+                               "launch, over a second pass of the K timed steps"},
         "accept_len": [int(x) for x in res["accept_len"]],
     }
     if not args.no_cpu_baseline:
