@@ -67,6 +67,7 @@ int env_int(const char* name, int dflt, int lo, int hi) {
 constexpr int kMinW2Rows = 16;   // rows per workgroup at the smallest setting
 int w1_rows() { static int v = env_int("MEDUSA_W1_ROWS", 4, 1, 64); return v; }
 int w2_rows() { static int v = env_int("MEDUSA_W2_ROWS", 40, kMinW2Rows / 4, 64); return v; }
+int head_interleave() { static int v = env_int("MEDUSA_HEAD_INTERLEAVE", 1, 0, 1); return v; }
 
 constexpr size_t kCounterBytes = 64 * 1024;   // workspace bytes reserved at offset 0 for counters
 
@@ -140,7 +141,13 @@ Layout layout_for(const medusa_shape* s) {
   L.q = take(B * T * d * es);
   L.o_elem = take(B * T * d * es);
   L.y_elem = take(B * T * d * es);
-  L.lm_part = take(B * T * gemm_groups_max(s->V) * 4 * 4);
+  {
+    // LM records [M][groups][4], or split-K partial logits [KS][M][V + 128]
+    const size_t rec = B * T * gemm_groups_max(s->V) * 4;
+    const int lm_ks = lm_splits_for((int)(B * T));
+    const size_t split = lm_ks > 1 ? (size_t)lm_ks * B * T * (s->V + 128) : 0;
+    L.lm_part = take((rec > split ? rec : split) * 4);
+  }
   {
     const bool f32 = s->dtype == MEDUSA_F32;
     // partials [groups][M][cols][KS]: groups * cols < N + 128
@@ -290,6 +297,7 @@ int medusa_heads_forward(const medusa_shape* shape, const float* h, const void* 
   a.G = L.G;
   a.w1_rows_per_wave = w1_rows();
   a.w2_rows_per_wave = w2_rows();
+  a.interleave = head_interleave();
   a.ev_before = g_ev_before;
   a.ev_after = g_ev_after;
   hipError_t e = launch_heads(a, static_cast<hipStream_t>(stream));

@@ -140,6 +140,20 @@ __device__ __forceinline__ void lds_barrier() {
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
 }
 
+// Transposing LDS read (gfx950 ds_read_b64_tr_b16). Within each group of 16
+// lanes, let lane 4k + q pass the address of 4 consecutive 16-bit elements
+// of row R_k (elements c + 4q .. c + 4q + 3): lane i then receives element
+// c + i of rows R_0 .. R_3, in that order (as 2 dwords, row R_0 in the low
+// half of the first).
+typedef short short4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint2 lds_read_tr16(const void* p) {
+  const short4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) short4_t*)(p));
+  uint2 r;
+  __builtin_memcpy(&r, &v, 8);
+  return r;
+}
+
 // ---- DPP wave reductions ----------------------------------------------------
 // DPP control codes (GFX9 encoding).
 constexpr int kDppQuadXor1 = 0xB1;   // quad_perm [1,0,3,2]

@@ -38,12 +38,12 @@ struct RowStream {
   static constexpr int PV = ET::kPerVec;
   static constexpr int CW = 64 * PV;
   const St* __restrict__ W;
-  int rb, nrows, d, SPR, lane;
+  int rb, rstride, nrows, d, SPR, lane;
   int fr, fs;   // row / chunk of the next refill
   u32x4_t wr[kRing];
 
   __device__ __forceinline__ const St* chunk_ptr(int r, int sg) const {
-    return W + (size_t)(rb + r) * d + min(sg * CW + PV * lane, d - PV);
+    return W + (size_t)(rb + r * rstride) * d + min(sg * CW + PV * lane, d - PV);
   }
   __device__ __forceinline__ void refill(int j) {
     const bool past = fr >= nrows;
@@ -55,8 +55,10 @@ struct RowStream {
   }
   // Issue the first kRing loads (a wave without rows reads row rb_ok, a
   // valid row, and never consumes the results).
-  __device__ __forceinline__ void start(const St* W_, int rb_, int nrows_, int d_, int rb_ok) {
+  __device__ __forceinline__ void start(const St* W_, int rb_, int rstride_, int nrows_, int d_,
+                                        int rb_ok) {
     W = W_;
+    rstride = rstride_;
     rb = nrows_ > 0 ? rb_ : rb_ok;
     nrows = nrows_ > 0 ? nrows_ : 1;
     d = d_;
@@ -130,7 +132,7 @@ template <class ET, int NB>
 __device__ __forceinline__ void stage_and_start(RowStream<ET, NB>& rs, const float* __restrict__ src,
                                                 size_t src_stride, int nb, int d, float* xs,
                                                 int ldx, const typename ET::storage* W, int rb,
-                                                int nrows, int rb_ok) {
+                                                int rstride, int nrows, int rb_ok) {
   constexpr int XR = 8;   // float4 loads per thread per round
   const int n4 = NB * ldx / 4;
   auto load_round = [&](int base, floatx4_t (&v)[XR]) {
@@ -152,7 +154,7 @@ __device__ __forceinline__ void stage_and_start(RowStream<ET, NB>& rs, const flo
   };
   floatx4_t v[XR];
   load_round(0, v);
-  rs.start(W, rb, nrows, d, rb_ok);
+  rs.start(W, rb, rstride, nrows, d, rb_ok);
   store_round(0, v);
   const int per_round = XR * (int)blockDim.x;
   for (int base = per_round; base < n4; base += per_round) {
@@ -160,6 +162,23 @@ __device__ __forceinline__ void stage_and_start(RowStream<ET, NB>& rs, const flo
     store_round(base, v);
   }
   lds_barrier();
+}
+
+// Rows of wave wi out of nw waves streaming `total` rows, at most rpw each:
+// interleaved (rows wi, wi + nw, wi + 2 nw, ...), so the waves of a launch
+// advance through memory side by side, or in blocks of rpw consecutive rows
+// (MEDUSA_HEAD_INTERLEAVE=0).
+__device__ __forceinline__ void wave_rows(int wi, int nw, int rpw, int total, bool interleave,
+                                          int& rb, int& rstride, int& nrows) {
+  if (interleave) {
+    rb = wi;
+    rstride = nw;
+    nrows = wi < total ? min(rpw, (total - wi + nw - 1) / nw) : 0;
+  } else {
+    rb = wi * rpw;
+    rstride = 1;
+    nrows = max(0, min(rpw, total - rb));
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -170,24 +189,25 @@ template <class ET, int NB>
 __global__ __launch_bounds__(kHeadWaves * 64) void heads_w1_kernel(
     const float* __restrict__ h, int B, int b0, int K, int d,
     const typename ET::storage* __restrict__ W1, const float* __restrict__ b1,
-    float* __restrict__ z, int rpw) {
+    float* __restrict__ z, int rpw, int interleave) {
   extern __shared__ float xs[];   // [NB][ldx]
   constexpr int CW = RowStream<ET, NB>::CW;
   const int ldx = (d + CW - 1) / CW * CW;
   const int nb = min(NB, B - b0);
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int total = K * d;
-  const int rb = (blockIdx.x * kHeadWaves + wave) * rpw;
-  const int nrows = max(0, min(rpw, total - rb));
+  int rb, rstride, nrows;
+  wave_rows(blockIdx.x * kHeadWaves + wave, gridDim.x * kHeadWaves, rpw, total, interleave != 0,
+            rb, rstride, nrows);
   RowStream<ET, NB> rs;
-  stage_and_start<ET, NB>(rs, h + (size_t)b0 * d, d, nb, d, xs, ldx, W1, rb, nrows, 0);
+  stage_and_start<ET, NB>(rs, h + (size_t)b0 * d, d, nb, d, xs, ldx, W1, rb, rstride, nrows, 0);
   if (nrows == 0) return;
   float win[NB];
 #pragma unroll
   for (int b = 0; b < NB; ++b) win[b] = 0.f;
   rs.run(xs, ldx, win);
   if (lane < nrows) {
-    const int row = rb + lane;   // row = k*d + i
+    const int row = rb + lane * rstride;   // row = k*d + i
     const int k = row / d, i = row - k * d;
     const float bias = b1 ? b1[row] : 0.f;
 #pragma unroll
@@ -265,18 +285,19 @@ __global__ __launch_bounds__(kHeadWaves * 64) void heads_w2_kernel(
     const float* __restrict__ z, int B, int b0, int K, int V, int d,
     const typename ET::storage* __restrict__ W2, int rpw, int S,
     float* __restrict__ head_logits, float* __restrict__ part_val, int* __restrict__ part_id,
-    float* __restrict__ part_m, float* __restrict__ part_s, int G) {
+    float* __restrict__ part_m, float* __restrict__ part_s, int G, int interleave) {
   extern __shared__ float xs[];   // [NB][ldx], then per-wave list exchange
   constexpr int CW = RowStream<ET, NB>::CW;
   const int ldx = (d + CW - 1) / CW * CW;
   const int k = blockIdx.y, g = blockIdx.x;
   const int nb = min(NB, B - b0);
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int rb = (g * kHeadWaves + wave) * rpw;
-  const int nrows = max(0, min(rpw, V - rb));
+  int rb, rstride, nrows;
+  wave_rows(g * kHeadWaves + wave, gridDim.x * kHeadWaves, rpw, V, interleave != 0, rb, rstride,
+            nrows);
   RowStream<ET, NB> rs;
   stage_and_start<ET, NB>(rs, z + ((size_t)b0 * K + k) * d, (size_t)K * d, nb, d, xs, ldx,
-                          W2 + (size_t)k * V * d, rb, nrows, 0);
+                          W2 + (size_t)k * V * d, rb, rstride, nrows, 0);
   float win[NB];
 #pragma unroll
   for (int b = 0; b < NB; ++b) win[b] = kNegInf;
@@ -289,14 +310,14 @@ __global__ __launch_bounds__(kHeadWaves * 64) void heads_w2_kernel(
   for (int b = 0; b < NB; ++b) {
     const float v = valid ? win[b] : kNegInf;
     if (head_logits && b < nb && valid)
-      head_logits[((size_t)(b0 + b) * K + k) * V + rb + lane] = v;
+      head_logits[((size_t)(b0 + b) * K + k) * V + rb + lane * rstride] = v;
     // statistics of this wave's rows
     const float mx = wave_max(v);
     m[b] = mx;
     s[b] = mx == kNegInf ? 0.f : wave_sum(valid ? exp_e(v - mx) : 0.f);
     // top-S of this wave's rows, best first in lanes 0..S-1
     float cv = v;
-    int ci = valid ? rb + lane : kNoId;
+    int ci = valid ? rb + lane * rstride : kNoId;
     tv[b] = kNegInf;
     ti[b] = kNoId;
     for (int r = 0; r < S; ++r) {
@@ -546,7 +567,7 @@ hipError_t launch_heads_nb(const HeadsArgs& a, int b0, hipStream_t st) {
   const int g1 = (a.K * a.d + rows1 - 1) / rows1;
   hipLaunchKernelGGL((heads_w1_kernel<ET, NB>), dim3(g1), dim3(kHeadWaves * 64), lds_x, st, a.h,
                      a.B, b0, a.K, a.d, reinterpret_cast<const typename ET::storage*>(a.W1),
-                     a.b1, a.z, a.w1_rows_per_wave);
+                     a.b1, a.z, a.w1_rows_per_wave, a.interleave);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const size_t lds_list = (size_t)kHeadWaves * NB * (2 * MAXS_LDS + 2) * sizeof(float);
@@ -558,7 +579,8 @@ hipError_t launch_heads_nb(const HeadsArgs& a, int b0, hipStream_t st) {
   hipLaunchKernelGGL((heads_w2_kernel<ET, NB>), dim3(a.G, a.K), dim3(kHeadWaves * 64), lds2, st,
                      a.z, a.B, b0, a.K, a.V, a.d,
                      reinterpret_cast<const typename ET::storage*>(a.W2), a.w2_rows_per_wave,
-                     a.S, a.head_logits, a.part_val, a.part_id, a.part_m, a.part_s, a.G);
+                     a.S, a.head_logits, a.part_val, a.part_id, a.part_m, a.part_s, a.G,
+                     a.interleave);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (a.ev_after) e = hipEventRecord(a.ev_after, st);

@@ -32,6 +32,7 @@ struct HeadsArgs {
   int G;                  // row blocks per head (4 waves of w2_rows_per_wave rows)
   int w1_rows_per_wave;   // 1..64
   int w2_rows_per_wave;   // 4..64
+  int interleave;         // 1: wave w streams rows w, w + nw, ...; 0: blocks of rows
   hipEvent_t ev_before;   // optional: recorded around the W2 kernel
   hipEvent_t ev_after;
 };
@@ -68,7 +69,7 @@ struct TreeArgs {
 hipError_t launch_tree(const TreeArgs& a, hipStream_t st);
 
 // ---- node GEMMs (verify pass) ---------------------------------------------------
-enum { EPI_QKV = 0, EPI_OPROJ = 1, EPI_LM = 2 };
+enum { EPI_QKV = 0, EPI_OPROJ = 1, EPI_LM = 2, EPI_PART = 3 };
 struct GemmParams {
   bool f32;
   int M, N, K;                 // C[M][N] = A[M][K] * W[N][K]^T
@@ -110,6 +111,7 @@ hipError_t launch_pack_weight(bool f32, const void* W, int rows, int K, int pair
 int gemm_groups_max(int N);                // column groups of a node GEMM (upper bound)
 int gemm_passes_max(int M);                // row passes (upper bound)
 int lm_head_blocks(int N, int M);          // column groups of the LM head
+int lm_splits_for(int M);                  // K slices of the LM head (1: in-kernel statistics)
 int gemm_splits(int N, int K, bool f32);   // K slices of the QKV / output projection GEMMs
 hipError_t launch_qkv(const GemmParams& p, hipStream_t st);
 hipError_t launch_oproj(const GemmParams& p, hipStream_t st);

@@ -119,7 +119,11 @@ __global__ void pack_weight_kernel(const typename ET::storage* __restrict__ W, i
 // Sum, in slice order, of the KS partials of one output (KS contiguous floats).
 __device__ __forceinline__ float sum_slices(const float* p, int KS) {
   float acc = 0.f;
-  if ((KS & 3) == 0) {
+  if (KS == 2) {
+    const float2 v = *reinterpret_cast<const float2*>(p);
+    acc += v.x;
+    acc += v.y;
+  } else if ((KS & 3) == 0) {
     for (int s = 0; s < KS; s += 4) {
       const floatx4_t v = *reinterpret_cast<const floatx4_t*>(p + s);
       acc += v[0];
@@ -304,6 +308,7 @@ __global__ __launch_bounds__(64 * WV, WV == 4 ? 4 : 2) void node_gemm_kernel(
         const int r = m0 + 16 * mt + 4 * lq + j;
         if (r < p.M) part[(size_t)r * GC * KS] = acc[mt][j];
       }
+    if constexpr (EPI == EPI_PART) return;
     if (!p.fused) return;
     // The last of the KS workgroups of this (group, pass) finishes it.
     __threadfence();   // release this workgroup's partials device-wide
@@ -481,6 +486,68 @@ __global__ __launch_bounds__(64) void row_stats_merge_kernel(const float* __rest
   }
 }
 
+// LM-head statistics from split-K partials: one workgroup per row r.
+// l_n = sum of the KS slices of column n (slice order); every thread keeps
+// an online (max, lowest argmax, S, W) record of its columns at temperature
+// tau, the records are merged in a fixed order (lane butterfly, then waves
+// in order); optional full logits; the logit of each tree node whose
+// parent row is r at the node's token.
+constexpr int kStatThreads = 1024;
+__global__ __launch_bounds__(kStatThreads) void lm_stats_kernel(GemmParams p, int KS,
+                                                              float* __restrict__ row_stats,
+                                                              int* __restrict__ row_argmax) {
+  const int r = blockIdx.x, t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int V = p.N;
+  float m = kNegInf, s = 0.f, w = 0.f;
+  int a = 0x7fffffff;
+  constexpr int U = 8;   // columns per thread per round, loaded before any is used
+  for (int n0 = 0; n0 < V; n0 += kStatThreads * U) {
+    float lv[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      lv[u] = sum_slices(partial_at(p, r, min(n0 + t + kStatThreads * u, V - 1), KS), KS);
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int n = n0 + t + kStatThreads * u;
+      if (n < V) {
+        if (p.logits_out) p.logits_out[(size_t)r * V + n] = lv[u];
+        rec_merge(m, s, w, a, lv[u], 1.f, 0.f, n, p.inv_tau);
+      }
+    }
+  }
+  // child logits: node c (1 <= c < T) of this row's sequence whose parent is this row
+  const int T = p.T, b = r / T, rl = r - b * T;
+  if (t >= 1 && t < T && min(max(p.parent[t], 0), T - 1) == rl) {
+    const int node = b * T + t;
+    const int tok = min(max(p.tokens[node], 0), V - 1);
+    p.child_logit[node] = sum_slices(partial_at(p, r, tok, KS), KS);
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    const float m2 = __shfl_xor(m, off), s2 = __shfl_xor(s, off), w2 = __shfl_xor(w, off);
+    const int a2 = __shfl_xor(a, off);
+    rec_merge(m, s, w, a, m2, s2, w2, a2, p.inv_tau);
+  }
+  __shared__ float rec[kStatThreads / 64][4];
+  if (lane == 0) {
+    rec[wave][0] = m;
+    rec[wave][1] = s;
+    rec[wave][2] = w;
+    rec[wave][3] = __int_as_float(a);
+  }
+  __syncthreads();
+  if (t != 0) return;
+  m = kNegInf;
+  s = w = 0.f;
+  a = 0x7fffffff;
+  for (int i = 0; i < kStatThreads / 64; ++i)
+    rec_merge(m, s, w, a, rec[i][0], rec[i][1], rec[i][2], __float_as_int(rec[i][3]), p.inv_tau);
+  row_stats[(size_t)r * 3 + 0] = m;
+  row_stats[(size_t)r * 3 + 1] = s;
+  row_stats[(size_t)r * 3 + 2] = w;
+  row_argmax[r] = a;
+}
+
 // Tile configuration: waves per workgroup (= 16-column stripes), m-tiles
 // per pass, k-tiles per A chunk, weight loads in flight per wave.
 struct Config {
@@ -514,7 +581,7 @@ Config lm_config() {
 
 Config config_for(int M, int epi) {
   if (M <= 48) {
-    if (epi == EPI_LM) return lm_config();
+    if (epi == EPI_LM || epi == EPI_PART) return lm_config();
     return small_waves() == 8 ? Config{8, 3, 8, 8} : Config{4, 3, 4, 8};
   }
   return Config{8, 12, 4, 4};
@@ -643,8 +710,33 @@ hipError_t launch_oproj(const GemmParams& p, hipStream_t st) {
   return launch_split<EPI_OPROJ>(p, st);
 }
 
+// MEDUSA_LM_SPLITS (1, 2 or 4; default 1): K slices of the LM head for a
+// single 48-row pass. With 1, statistics are taken in the GEMM's epilogue;
+// with more, a per-row statistics kernel sums the slices (measured slower
+// for the 7B step: the partial-logit traffic and the row-per-workgroup
+// statistics cost more than the extra parallelism gains).
+int lm_splits_for(int M) {
+  static const int v = [] {
+    const char* s = getenv("MEDUSA_LM_SPLITS");
+    const int k = s && *s ? atoi(s) : 1;
+    return k >= 4 ? 4 : (k >= 2 ? 2 : 1);
+  }();
+  return M <= 48 ? v : 1;
+}
+
 hipError_t launch_lm_head(GemmParams p, float* row_stats, int* row_argmax, hipStream_t st) {
   p.kmajor = packed_kmajor();
+  const int KS = lm_splits_for(p.M);
+  if (KS > 1) {
+    p.group_cols = 16 * config_for(p.M, EPI_PART).wv;
+    p.fused = 0;
+    hipError_t e = p.f32 ? launch_main<F32, EPI_PART>(p, KS, st)
+                         : launch_main<BF16, EPI_PART>(p, KS, st);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(lm_stats_kernel, dim3(p.M), dim3(kStatThreads), 0, st, p, KS, row_stats,
+                       row_argmax);
+    return hipGetLastError();
+  }
   hipError_t e = p.f32 ? launch_main<F32, EPI_LM>(p, 1, st) : launch_main<BF16, EPI_LM>(p, 1, st);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(row_stats_merge_kernel, dim3(p.M), dim3(64), 0, st, p.part,

@@ -10,10 +10,11 @@
 //
 // Inside a workgroup everything is computed transposed, so that no lane
 // shuffles are needed between the two products:
-//   S^T = K Q^T     (A = K rows, loaded straight from HBM; B = Q rows),
+//   S^T = K Q^T     (A = K rows from LDS; B = Q rows, in registers),
 //   P^T = 2^(S^T * scale*log2e - m),
-//   O^T += V^T P^T  (A = V^T from LDS, where the workgroup stores the V
-//                    sub-chunk transposed; B = P^T straight from the S^T
+//   O^T += V^T P^T  (A = V^T: V rows sit row-major in LDS and gfx950's
+//                    transposing LDS read (ds_read_b64_tr_b16) returns each
+//                    lane 4 keys of one dh; B = P^T straight from the S^T
 //                    accumulators, since the MFMA result layout puts the 4
 //                    keys of a lane exactly where the next MFMA's B operand
 //                    expects its k slots, up to a permutation shared with A).
@@ -28,13 +29,9 @@ namespace {
 
 constexpr float kNegInf = -__builtin_huge_valf();
 
-// SC keys are staged per round: K rows (row-major, padded by 16 bytes) and V
-// transposed (padded) go to LDS; the global loads of the next round are in
-// flight while the waves compute the current one from LDS.
-//
-// V^T is written with 32-bit LDS stores: the two lanes that hold the same
-// 8 dims of keys 2j and 2j+1 swap halves first (one cross-lane permute per
-// dword), so each lane owns (key 2j, key 2j+1) pairs of 4 dims.
+// SC keys are staged per round: K and V rows go to LDS (row-major, padded)
+// with 16-byte stores; the global loads of the next round are in flight
+// while the waves compute the current one from LDS.
 template <class ET, int DH, int QT, int SC>
 __global__ __launch_bounds__(256) void tree_attn_kernel(AttnArgs a) {
   using S = typename ET::storage;
@@ -79,8 +76,11 @@ __global__ __launch_bounds__(256) void tree_attn_kernel(AttnArgs a) {
     krow = DH;
   }
 
+  // bf16: V row-major like K (row stride 288 / 160 bytes keeps the
+  // transposed reads conflict-free); fp32: V transposed.
+  constexpr int PADV = 32 / sizeof(S);
   __shared__ S ks[SC][DH + PAD];
-  __shared__ S vt[DH][SC + PAD];
+  __shared__ S vt[BF ? SC : DH][BF ? DH + PADV : SC + PAD];
 
   // Q fragments of my query tiles (B operand: lane = query, 16 B along Dh)
   u32x4_t qf[QT][DS];
@@ -122,19 +122,7 @@ __global__ __launch_bounds__(256) void tree_attn_kernel(AttnArgs a) {
       const int kk = c / VEC_PER_KEY, part = c - kk * VEC_PER_KEY;
       *reinterpret_cast<u32x4_t*>(&ks[kk][PV * part]) = kv[i];
       if constexpr (BF) {
-        // partner lane holds the same dims of key kk ^ 1
-        const bool odd = kk & 1;
-        const uint32_t r0 = (uint32_t)__shfl_xor((int)(odd ? vv[i][0] : vv[i][2]), VEC_PER_KEY);
-        const uint32_t r1 = (uint32_t)__shfl_xor((int)(odd ? vv[i][1] : vv[i][3]), VEC_PER_KEY);
-        const uint32_t lo0 = odd ? r0 : vv[i][0], hi0 = odd ? vv[i][2] : r0;
-        const uint32_t lo1 = odd ? r1 : vv[i][1], hi1 = odd ? vv[i][3] : r1;
-        const int d0 = PV * part + (odd ? 4 : 0);
-        uint32_t* col = reinterpret_cast<uint32_t*>(&vt[d0][kk & ~1]);
-        constexpr int RW = (SC + PAD) / 2;   // row stride in dwords
-        col[0] = (lo0 & 0xffffu) | (hi0 << 16);
-        col[RW] = (lo0 >> 16) | (hi0 & 0xffff0000u);
-        col[2 * RW] = (lo1 & 0xffffu) | (hi1 << 16);
-        col[3 * RW] = (lo1 >> 16) | (hi1 & 0xffff0000u);
+        *reinterpret_cast<u32x4_t*>(&vt[kk][PV * part]) = vv[i];
       } else {
 #pragma unroll
         for (int e = 0; e < 4; ++e) vt[PV * part + e][kk] = __uint_as_float(vv[i][e]);
@@ -211,12 +199,14 @@ __global__ __launch_bounds__(256) void tree_attn_kernel(AttnArgs a) {
           pf[1] = pack_bf16x2(st[2 * t][2], st[2 * t][3]);
           pf[2] = pack_bf16x2(st[2 * t + 1][0], st[2 * t + 1][1]);
           pf[3] = pack_bf16x2(st[2 * t + 1][2], st[2 * t + 1][3]);
+          // k slot j of this lane group is key 32t + 4lq + j (j < 4) or
+          // 32t + 16 + 4lq + j - 4: the S^T accumulator order
 #pragma unroll
           for (int dt = 0; dt < DT; ++dt) {
-            const S* vr = &vt[16 * dt + li][32 * t + 4 * lq];
-            const uint2 lo = *reinterpret_cast<const uint2*>(vr);
-            const uint2 hi = *reinterpret_cast<const uint2*>(vr + 16);
+            const S* v0 = &vt[32 * t + 4 * lq + (li >> 2)][16 * dt + 4 * (li & 3)];
             u32x4_t vf;
+            const uint2 lo = lds_read_tr16(v0);
+            const uint2 hi = lds_read_tr16(v0 + 16 * (DH + PADV));
             vf[0] = lo.x;
             vf[1] = lo.y;
             vf[2] = hi.x;
