@@ -1,9 +1,10 @@
 """Throughput of one Medusa verify step on one MI355X.
 
-A step is one pass of the whole hot path over one batch: heads (residual
-block + vocabulary projection with fused top-s) -> candidate tree -> verify
-forward (QKV + RoPE, split-KV tree attention, output projection, LM head
-with row statistics) -> posterior (typical acceptance) -> commit. The
+A step is one pass of the whole hot path over one batch, as one composite
+medusa_step call: heads (residual block + vocabulary projection with fused
+top-s) -> candidate tree -> verify forward (QKV + RoPE, split-KV tree
+attention, output projection, LM head with row statistics) -> posterior
+(typical acceptance) -> commit. The
 workload is the Vicuna-7B-shaped step (d 4096, V 32000, 5 heads, 45-node
 top-(3,2,2,1,1) tree, 2048-token prefix, typical acceptance eps 0.09,
 delta 0.3, tau 0.7) on seeded synthetic inputs resident in HBM.
@@ -132,6 +133,9 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--graph", action="store_true",
+                    help="time replays of one recorded step graph instead of eager launches "
+                         "(measured slower on this stack: per-node overhead)")
     ap.add_argument("--print-digest", action="store_true",
                     help="print the W2 kernel source digest (for the counter summary) and exit")
     ap.add_argument("--copy-bytes", type=int, default=0,
@@ -160,12 +164,25 @@ def main():
     L_total = int(np.sum(inp["kv_len"]))
 
     def step():
+        # stream=None: the calls go to torch's current stream (the capture
+        # stream while a graph is being recorded)
         st.reset_kv_len()
-        st.run(stream)
+        st.run_step()
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
+    graph = None
+    if args.graph:
+        # one step (prefix-length reset + medusa_step) recorded once and
+        # replayed
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            step()
+        for _ in range(3):
+            graph.replay()
+        torch.cuda.synchronize()
+    run_one = graph.replay if graph is not None else step
     if args.copy_bytes > 0:
         src = torch.empty(args.copy_bytes // 4, dtype=torch.float32, device="cuda").fill_(1.0)
         dst = torch.empty_like(src)
@@ -180,7 +197,7 @@ def main():
     torch.cuda.synchronize()
     t_start.record(stream)
     for _ in range(args.steps):
-        step()
+        run_one()
     t_stop.record(stream)
     torch.cuda.synchronize()
     ms_total = t_start.elapsed_time(t_stop)
@@ -220,6 +237,8 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic (seeded Gaussian weights and KV of Vicuna-7B shapes)",
+        "timing": ("replays of one recorded graph (prefix-length reset + medusa_step)"
+                   if graph is not None else "eager launches (prefix-length reset + medusa_step)"),
         "config": {"workload": w.name, "batch": w.B, "d": w.d, "V": w.V, "heads": w.K,
                    "tree": "top-(3,2,2,1,1)", "tree_nodes": T - 1, "prefix_kv": L_total,
                    "attn": f"{w.H}x{w.Dh}", "accept": f"typical eps={w.eps} delta={w.delta} "

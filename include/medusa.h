@@ -292,6 +292,78 @@ int medusa_commit(const medusa_shape* shape, const int32_t* last_node, const int
                   const void* k_tree, const void* v_tree, const float* y, void* k_cache,
                   void* v_cache, int32_t* kv_len, float* h_next, void* stream);
 
+/*
+ * One whole verify step ("Medusa Part I", introduction: heads propose, the
+ * tree is verified in one pass, the longest accepted prefix is committed;
+ * the parts as above), all launches on one stream with no host
+ * synchronisation, so a caller can capture it in a graph. It computes what
+ * medusa_heads_forward, medusa_build_tree (tokens and positions only),
+ * medusa_verify_forward, medusa_evaluate_posterior and medusa_commit compute
+ * in that order, with the same arguments and results, except that:
+ *  - tree_mask, parent and retrieve are inputs, written beforehand by one
+ *    medusa_build_tree call for the same tree_ranks;
+ *  - with MEDUSA_DRAFT_TOPK the head merge also writes tree_tokens and
+ *    position_ids, and in greedy / typical mode one workgroup per sequence
+ *    evaluates the posterior and commits.
+ * Pointers are device memory unless marked; _or_null members may be NULL
+ * where the corresponding call allows it. W_qkv, W_o and W_lm are packed
+ * (medusa_pack_weight). Errors as for the individual calls; validation of
+ * a later part can fail after earlier parts were launched.
+ */
+typedef struct {
+  /* heads */
+  const float* h;                  /* [B][d] */
+  const void* W1;                  /* [K][d][d] elem */
+  const float* b1_or_null;         /* [K][d] */
+  const void* W2;                  /* [K][V][d] elem */
+  /* tree */
+  const int32_t* tree_ranks_host; /* HOST [N][K], see medusa_build_tree */
+  int draft_mode;
+  const int32_t* root_tok;         /* [B] */
+  const float* u_draft_or_null;    /* [B][T] (MEDUSA_DRAFT_SAMPLE) */
+  const uint8_t* tree_mask;        /* [T][T] (input) */
+  const int32_t* parent;           /* [T] (input) */
+  const int32_t* retrieve;         /* [P][K+1] (input) */
+  /* verifier */
+  const void* E;                   /* [V][d] elem */
+  const void* W_qkv;               /* packed, MEDUSA_PACK_QKV */
+  const void* W_o;                 /* packed */
+  const void* W_lm;                /* packed */
+  float rope_theta;
+  void* k_cache;                   /* [B][H][Lmax][Dh] elem (in-out) */
+  void* v_cache;
+  int32_t* kv_len;                 /* [B] (in-out) */
+  /* posterior */
+  int mode;
+  float temperature, eps, delta;
+  const float* u_accept_or_null;   /* [B][T] (exact) */
+  const float* u_resample_or_null; /* [B][T] (exact) */
+  /* outputs */
+  int32_t* topk_ids;               /* [B][K][s_max] */
+  float* topk_logits;              /* [B][K][s_max] */
+  float* head_lse_or_null;         /* [B][K] */
+  float* head_logits_or_null;      /* [B][K][V] */
+  float* z_or_null;                /* [B][K][d] */
+  int32_t* tree_tokens;            /* [B][T] */
+  int32_t* position_ids;           /* [B][T] */
+  void* k_tree;                    /* [B][T][H][Dh] elem */
+  void* v_tree;
+  float* y;                        /* [B][T][d] */
+  float* row_stats;                /* [B][T][3] */
+  int32_t* row_argmax;             /* [B][T] */
+  float* child_logit;              /* [B][T] */
+  float* verify_logits_or_null;    /* [B][T][V] */
+  int32_t* accept_len;             /* [B] */
+  int32_t* best_path;              /* [B] */
+  int32_t* last_node;              /* [B] */
+  int32_t* out_tokens;             /* [B][K+1] */
+  int32_t* next_root;              /* [B] */
+  float* h_next;                   /* [B][d] */
+} medusa_step_args;
+
+int medusa_step(const medusa_shape* shape, const medusa_step_args* args, void* workspace,
+                size_t workspace_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

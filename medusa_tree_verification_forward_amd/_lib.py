@@ -56,6 +56,26 @@ if not os.path.exists(LIB_PATH):
 
 _lib = ctypes.CDLL(LIB_PATH)
 
+
+class StepArgs(ctypes.Structure):
+    """Mirror of medusa_step_args (include/medusa.h), member for member."""
+    _P, _I, _F = ctypes.c_void_p, ctypes.c_int32, ctypes.c_float
+    _fields_ = [
+        ("h", _P), ("W1", _P), ("b1_or_null", _P), ("W2", _P),
+        ("tree_ranks_host", _P), ("draft_mode", _I), ("root_tok", _P), ("u_draft_or_null", _P),
+        ("tree_mask", _P), ("parent", _P), ("retrieve", _P),
+        ("E", _P), ("W_qkv", _P), ("W_o", _P), ("W_lm", _P), ("rope_theta", _F),
+        ("k_cache", _P), ("v_cache", _P), ("kv_len", _P),
+        ("mode", _I), ("temperature", _F), ("eps", _F), ("delta", _F),
+        ("u_accept_or_null", _P), ("u_resample_or_null", _P),
+        ("topk_ids", _P), ("topk_logits", _P), ("head_lse_or_null", _P),
+        ("head_logits_or_null", _P), ("z_or_null", _P), ("tree_tokens", _P), ("position_ids", _P),
+        ("k_tree", _P), ("v_tree", _P), ("y", _P), ("row_stats", _P), ("row_argmax", _P),
+        ("child_logit", _P), ("verify_logits_or_null", _P), ("accept_len", _P),
+        ("best_path", _P), ("last_node", _P), ("out_tokens", _P), ("next_root", _P),
+        ("h_next", _P),
+    ]
+
 _P = ctypes.c_void_p
 _I = ctypes.c_int
 _F = ctypes.c_float
@@ -77,6 +97,7 @@ _SIGS = {
     "medusa_evaluate_posterior": ([_SP, _I, _F, _F, _F, _P, _P, _P, _P, _P, _P, _P, _P, _P,
                                    _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P], _I),
     "medusa_commit": ([_SP, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P], _I),
+    "medusa_step": ([_SP, ctypes.POINTER(StepArgs), _P, _SZ, _P], _I),
 }
 for _name, (_args, _res) in _SIGS.items():
     _fn = getattr(_lib, _name, None)
@@ -231,3 +252,10 @@ def commit(shape, last_node, parent, k_tree, v_tree, y, k_cache, v_cache, kv_len
     _check(_lib.medusa_commit(
         ctypes.byref(shape), _ptr(last_node), _ptr(parent), _ptr(k_tree), _ptr(v_tree), _ptr(y),
         _ptr(k_cache), _ptr(v_cache), _ptr(kv_len), _ptr(h_next), _stream(stream)))
+
+
+def step(shape, args: StepArgs, workspace, *, stream=None):
+    """The composite step (medusa_step); `args` holds every pointer, and its
+    tree_ranks_host member must point at host memory that outlives the call."""
+    _check(_lib.medusa_step(ctypes.byref(shape), ctypes.byref(args), _ptr(workspace),
+                            workspace.numel() * workspace.element_size(), _stream(stream)))

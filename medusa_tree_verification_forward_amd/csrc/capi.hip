@@ -69,6 +69,7 @@ int w1_rows() { static int v = env_int("MEDUSA_W1_ROWS", 4, 1, 64); return v; }
 int w2_rows() { static int v = env_int("MEDUSA_W2_ROWS", 40, kMinW2Rows / 4, 64); return v; }
 int head_interleave() { static int v = env_int("MEDUSA_HEAD_INTERLEAVE", 1, 0, 1); return v; }
 
+
 constexpr size_t kCounterBytes = 64 * 1024;   // workspace bytes reserved at offset 0 for counters
 
 int check_shape(const medusa_shape* s) {
@@ -255,11 +256,18 @@ size_t medusa_workspace_bytes(const medusa_shape* shape) {
   return layout_for(shape).total;
 }
 
-int medusa_heads_forward(const medusa_shape* shape, const float* h, const void* W1,
-                         const float* b1_or_null, const void* W2, int32_t* topk_ids,
-                         float* topk_logits, float* head_lse_or_null,
-                         float* head_logits_or_null, float* z_or_null, void* workspace,
-                         size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Heads, optionally writing the tree tokens and positions in the merge
+// (fuse_plan != null: top-s drafting inside the composite step).
+int heads_impl(const medusa_shape* shape, const float* h, const void* W1,
+               const float* b1_or_null, const void* W2, int32_t* topk_ids, float* topk_logits,
+               float* head_lse_or_null, float* head_logits_or_null, float* z_or_null,
+               void* workspace, size_t workspace_bytes, void* stream, const TreePlan* fuse_plan,
+               const int32_t* root_tok, const int32_t* kv_len, int32_t* tree_tokens,
+               int32_t* position_ids) {
   int rc = check_shape(shape);
   if (rc) return rc;
   REQUIRE_PTR(h);
@@ -300,9 +308,31 @@ int medusa_heads_forward(const medusa_shape* shape, const float* h, const void* 
   a.interleave = head_interleave();
   a.ev_before = g_ev_before;
   a.ev_after = g_ev_after;
+  if (fuse_plan) {
+    a.fuse_tree = true;
+    a.plan = *fuse_plan;
+    a.root_tok = root_tok;
+    a.kv_len = kv_len;
+    a.tree_tokens = tree_tokens;
+    a.position_ids = position_ids;
+  }
   hipError_t e = launch_heads(a, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "heads launch");
   return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+int medusa_heads_forward(const medusa_shape* shape, const float* h, const void* W1,
+                         const float* b1_or_null, const void* W2, int32_t* topk_ids,
+                         float* topk_logits, float* head_lse_or_null,
+                         float* head_logits_or_null, float* z_or_null, void* workspace,
+                         size_t workspace_bytes, void* stream) {
+  return heads_impl(shape, h, W1, b1_or_null, W2, topk_ids, topk_logits, head_lse_or_null,
+                    head_logits_or_null, z_or_null, workspace, workspace_bytes, stream, nullptr,
+                    nullptr, nullptr, nullptr, nullptr);
 }
 
 int medusa_build_tree(const medusa_shape* shape, const int32_t* tree_ranks_host,
@@ -432,15 +462,19 @@ int medusa_pack_weight(const medusa_shape* shape, int kind, const void* W, int r
   return ok();
 }
 
-int medusa_verify_forward(const medusa_shape* shape, const void* E, const void* W_qkv,
-                          const void* W_o, const void* W_lm, float rope_theta,
-                          const int32_t* tree_tokens, const int32_t* position_ids,
-                          const uint8_t* tree_mask, const int32_t* parent,
-                          const void* k_cache, const void* v_cache, const int32_t* kv_len,
-                          float temperature, void* k_tree_out, void* v_tree_out,
-                          float* y_out, float* row_stats, int32_t* row_argmax,
-                          float* child_logit, float* verify_logits_or_null,
-                          void* workspace, size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Verify forward (shared by medusa_verify_forward and medusa_step).
+int verify_impl(const medusa_shape* shape, const void* E, const void* W_qkv, const void* W_o,
+                const void* W_lm, float rope_theta, const int32_t* tree_tokens,
+                const int32_t* position_ids, const uint8_t* tree_mask, const int32_t* parent,
+                const void* k_cache, const void* v_cache, const int32_t* kv_len,
+                float temperature, void* k_tree_out, void* v_tree_out, float* y_out,
+                float* row_stats, int32_t* row_argmax, float* child_logit,
+                float* verify_logits_or_null, void* workspace, size_t workspace_bytes,
+                void* stream) {
   int rc = check_shape(shape);
   if (rc) return rc;
   REQUIRE_PTR(E);
@@ -546,6 +580,25 @@ int medusa_verify_forward(const medusa_shape* shape, const void* E, const void* 
   e = launch_lm_head(gl, row_stats, row_argmax, st);
   if (e != hipSuccess) return hip_fail(e, "lm head launch");
   return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+int medusa_verify_forward(const medusa_shape* shape, const void* E, const void* W_qkv,
+                          const void* W_o, const void* W_lm, float rope_theta,
+                          const int32_t* tree_tokens, const int32_t* position_ids,
+                          const uint8_t* tree_mask, const int32_t* parent,
+                          const void* k_cache, const void* v_cache, const int32_t* kv_len,
+                          float temperature, void* k_tree_out, void* v_tree_out,
+                          float* y_out, float* row_stats, int32_t* row_argmax,
+                          float* child_logit, float* verify_logits_or_null,
+                          void* workspace, size_t workspace_bytes, void* stream) {
+  return verify_impl(shape, E, W_qkv, W_o, W_lm, rope_theta, tree_tokens, position_ids,
+                     tree_mask, parent, k_cache, v_cache, kv_len, temperature, k_tree_out,
+                     v_tree_out, y_out, row_stats, row_argmax, child_logit,
+                     verify_logits_or_null, workspace, workspace_bytes, stream);
 }
 
 int medusa_evaluate_posterior(const medusa_shape* shape, int mode, float temperature,
@@ -656,6 +709,121 @@ int medusa_commit(const medusa_shape* shape, const int32_t* last_node, const int
   a.h_next = h_next;
   hipError_t e = launch_commit(a, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "commit launch");
+  return ok();
+}
+
+int medusa_step(const medusa_shape* shape, const medusa_step_args* x, void* workspace,
+                size_t workspace_bytes, void* stream) {
+  int rc = check_shape(shape);
+  if (rc) return rc;
+  if (!x) return fail(MEDUSA_ERR_ARG, "args: null pointer");
+  const int mode = x->mode;
+  if (mode != MEDUSA_GREEDY && mode != MEDUSA_TYPICAL && mode != MEDUSA_EXACT)
+    return fail(MEDUSA_ERR_ARG, "mode %d unknown", mode);
+  if (x->draft_mode != MEDUSA_DRAFT_TOPK && x->draft_mode != MEDUSA_DRAFT_SAMPLE)
+    return fail(MEDUSA_ERR_ARG, "draft_mode %d unknown", x->draft_mode);
+  // spec-only topology written once by medusa_build_tree, read here
+  REQUIRE_PTR(x->tree_mask);
+  REQUIRE_PTR(x->parent);
+  REQUIRE_PTR(x->retrieve);
+  REQUIRE_PTR(x->root_tok);
+  REQUIRE_PTR(x->kv_len);
+  REQUIRE_PTR(x->tree_tokens);
+  REQUIRE_PTR(x->position_ids);
+  TreePlan plan;
+  int P = 0;
+  rc = make_plan(shape, x->tree_ranks_host, &plan, &P);
+  if (rc) return rc;
+  if (P != shape->P)
+    return fail(MEDUSA_ERR_ARG, "tree has %d root-to-leaf paths, shape.P is %d", P, shape->P);
+  Layout L;
+  rc = check_workspace(shape, workspace, workspace_bytes, &L);
+  if (rc) return rc;
+  const bool fuse_tree = x->draft_mode == MEDUSA_DRAFT_TOPK;
+  // greedy / typical: the LM row records are merged by the fused posterior
+  const bool fuse_post = mode != MEDUSA_EXACT;
+  // 1. heads (+ tree tokens and positions)
+  rc = heads_impl(shape, x->h, x->W1, x->b1_or_null, x->W2, x->topk_ids, x->topk_logits,
+                  x->head_lse_or_null, x->head_logits_or_null, x->z_or_null, workspace,
+                  workspace_bytes, stream,
+                  fuse_tree ? &plan : nullptr, x->root_tok, x->kv_len, x->tree_tokens,
+                  x->position_ids);
+  if (rc) return rc;
+  // 2. tree tokens by sampling
+  if (!fuse_tree) {
+    rc = medusa_build_tree(shape, x->tree_ranks_host, x->draft_mode, x->root_tok, x->topk_ids,
+                           x->head_logits_or_null, x->head_lse_or_null, x->u_draft_or_null,
+                           x->kv_len, x->tree_tokens,
+                           nullptr, x->position_ids, nullptr, nullptr, nullptr, stream);
+    if (rc) return rc;
+  }
+  // 3. verify forward
+  rc = verify_impl(shape, x->E, x->W_qkv, x->W_o, x->W_lm, x->rope_theta, x->tree_tokens,
+                   x->position_ids, x->tree_mask, x->parent, x->k_cache, x->v_cache, x->kv_len,
+                   x->temperature, x->k_tree, x->v_tree, x->y, x->row_stats, x->row_argmax,
+                   x->child_logit, x->verify_logits_or_null, workspace, workspace_bytes, stream);
+  if (rc) return rc;
+  // 4. posterior and commit
+  if (!fuse_post) {
+    rc = medusa_evaluate_posterior(shape, mode, x->temperature, x->eps, x->delta, x->row_stats,
+                                   x->row_argmax, x->child_logit, x->verify_logits_or_null,
+                                   x->tree_tokens, x->parent, x->retrieve,
+                                   x->head_logits_or_null, x->head_lse_or_null,
+                                   x->u_accept_or_null, x->u_resample_or_null, x->accept_len,
+                                   x->best_path, x->last_node, x->out_tokens, x->next_root,
+                                   workspace, workspace_bytes, stream);
+    if (rc) return rc;
+    return medusa_commit(shape, x->last_node, x->parent, x->k_tree, x->v_tree, x->y,
+                         x->k_cache, x->v_cache, x->kv_len, x->h_next, stream);
+  }
+  REQUIRE_PTR(x->accept_len);
+  REQUIRE_PTR(x->best_path);
+  REQUIRE_PTR(x->last_node);
+  REQUIRE_PTR(x->out_tokens);
+  REQUIRE_PTR(x->next_root);
+  REQUIRE_PTR(x->h_next);
+  if (mode == MEDUSA_TYPICAL && (!(x->eps >= 0.f) || !(x->delta >= 0.f)))
+    return fail(MEDUSA_ERR_ARG, "eps, delta must be >= 0");
+  PostArgs a{};
+  a.mode = mode;
+  a.B = shape->B;
+  a.T = shape->N + 1;
+  a.K = shape->K;
+  a.P = shape->P;
+  a.V = shape->V;
+  a.inv_tau = 1.0f / x->temperature;
+  a.eps = x->eps;
+  a.delta = x->delta;
+  a.child_logit = x->child_logit;
+  a.tokens = x->tree_tokens;
+  a.parent = x->parent;
+  a.retrieve = x->retrieve;
+  a.accept_len = x->accept_len;
+  a.best_path = x->best_path;
+  a.last_node = x->last_node;
+  a.out_tokens = x->out_tokens;
+  a.next_root = x->next_root;
+  CommitArgs c{};
+  c.f32 = shape->dtype == MEDUSA_F32;
+  c.B = shape->B;
+  c.T = shape->N + 1;
+  c.K = shape->K;
+  c.H = shape->H;
+  c.Dh = shape->Dh;
+  c.d = shape->d;
+  c.Lmax = shape->Lmax;
+  c.parent = x->parent;
+  c.k_tree = x->k_tree;
+  c.v_tree = x->v_tree;
+  c.y = x->y;
+  c.k_cache = x->k_cache;
+  c.v_cache = x->v_cache;
+  c.kv_len = x->kv_len;
+  c.h_next = x->h_next;
+  a.row_stats = x->row_stats;
+  a.row_argmax = x->row_argmax;
+  hipError_t e = launch_posterior_commit(a, c, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "posterior launch");
   return ok();
 }
 

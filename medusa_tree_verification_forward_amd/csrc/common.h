@@ -210,6 +210,60 @@ __device__ __forceinline__ bool better(float va, int ia, float vb, int ib) {
   return va > vb || (va == vb && ia < ib);
 }
 
+// ---- row statistics of a logit row at temperature tau -----------------------
+// Record (m, S, W, a): max m, argmax a (lowest id on ties), S = sum
+// e^{(l-m)/tau}, W = sum e^{(l-m)/tau} (l-m)/tau over a set of columns.
+// Merge of two records (m = -inf marks an empty record).
+__device__ __forceinline__ void rec_merge(float& m, float& s, float& w, int& a, float m2,
+                                          float s2, float w2, int a2, float inv_tau) {
+  if (m2 == -__builtin_huge_valf()) return;
+  if (m == -__builtin_huge_valf()) {
+    m = m2; s = s2; w = w2; a = a2;
+    return;
+  }
+  const float mn = fmaxf(m, m2);
+  const float d1 = (m - mn) * inv_tau, d2 = (m2 - mn) * inv_tau;
+  const float c1 = __builtin_amdgcn_exp2f(d1 * 1.4426950408889634f);
+  const float c2 = __builtin_amdgcn_exp2f(d2 * 1.4426950408889634f);
+  const int an = (m > m2 || (m == m2 && a < a2)) ? a : a2;
+  w = c1 * (w + s * d1) + c2 * (w2 + s2 * d2);
+  s = c1 * s + c2 * s2;
+  m = mn;
+  a = an;
+}
+
+// One wave merges the G records part[r][0..G) (4 floats each, a as int bits)
+// in a fixed order: lane l takes records l, l+64, ... (all of a round loaded
+// before any is merged), then a lane butterfly. Every lane returns the result.
+__device__ __forceinline__ void merge_row_records(const float* __restrict__ part, int G, int r,
+                                                  float inv_tau, float& m, float& s, float& w,
+                                                  int& a) {
+  const int lane = threadIdx.x & 63;
+  m = -__builtin_huge_valf();
+  s = w = 0.f;
+  a = 0x7fffffff;
+  constexpr int RB = 4;
+  for (int g0 = 0; g0 < G; g0 += 64 * RB) {
+    floatx4_t rec[RB];
+#pragma unroll
+    for (int u = 0; u < RB; ++u) {
+      const int g = min(g0 + lane + 64 * u, G - 1);
+      rec[u] = *reinterpret_cast<const floatx4_t*>(part + ((size_t)r * G + g) * 4);
+    }
+#pragma unroll
+    for (int u = 0; u < RB; ++u)
+      if (g0 + lane + 64 * u < G)
+        rec_merge(m, s, w, a, rec[u][0], rec[u][1], rec[u][2], __float_as_int(rec[u][3]),
+                  inv_tau);
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    const float m2 = __shfl_xor(m, off), s2 = __shfl_xor(s, off), w2 = __shfl_xor(w, off);
+    const int a2 = __shfl_xor(a, off);
+    rec_merge(m, s, w, a, m2, s2, w2, a2, inv_tau);
+  }
+}
+
 // ---- MFMA ---------------------------------------------------------------------
 // v_mfma_f32_16x16x32_bf16: A 16x32, B 32x16, C 16x16 fp32.
 // Lane l holds A[l%16][8*(l/16) .. +7], B[8*(l/16) .. +7][l%16] and

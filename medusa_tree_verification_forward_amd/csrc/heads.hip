@@ -437,11 +437,22 @@ __device__ __forceinline__ void wave_select(float (&lv)[SMAX], int (&li)[SMAX], 
   }
 }
 
+// Tree tokens and positions written by the merge (composite step).
+struct MergeTree {
+  int on;
+  TreePlan plan;
+  const int32_t* root_tok;
+  const int32_t* kv_len;
+  int32_t* tokens;
+  int32_t* position_ids;
+};
+
 template <int SMAX>
 __global__ __launch_bounds__(kMergeThreads) void heads_merge_kernel(
     int K, int G, int S, const float* __restrict__ part_val, const int* __restrict__ part_id,
     const float* __restrict__ part_m, const float* __restrict__ part_s,
-    int* __restrict__ topk_ids, float* __restrict__ topk_logits, float* __restrict__ lse) {
+    int* __restrict__ topk_ids, float* __restrict__ topk_logits, float* __restrict__ lse,
+    MergeTree tr) {
   constexpr int NW = kMergeThreads / 64;
   const int k = blockIdx.x, b = blockIdx.y;
   const int t = threadIdx.x, wave = t >> 6, lane = t & 63;
@@ -556,6 +567,20 @@ __global__ __launch_bounds__(kMergeThreads) void heads_merge_kernel(
     topk_ids[out + lane] = wi;
     topk_logits[out + lane] = wv;
   }
+  if (!tr.on) return;
+  // nodes of depth k+1 take rank r's token of this head (held by lane r)
+  const int T = tr.plan.T;
+  for (int n0 = 0; n0 < T; n0 += 64) {
+    const int n = n0 + lane;
+    const bool mine = n < T && n >= 1 && tr.plan.depth[n] == k + 1;
+    const int r = n < T ? tr.plan.last_rank[n] : 0;
+    const int tok = __shfl(wi, min(r, S - 1));
+    if (mine) tr.tokens[(size_t)b * T + n] = tok;
+    if (k == 0 && n < T) {
+      tr.position_ids[(size_t)b * T + n] = tr.kv_len[b] + tr.plan.depth[n];
+      if (n == 0) tr.tokens[(size_t)b * T] = tr.root_tok[b];
+    }
+  }
 }
 
 template <class ET, int NB>
@@ -602,11 +627,19 @@ hipError_t launch_heads_et(const HeadsArgs& a, hipStream_t st) {
       e = launch_heads_nb<ET, 8>(a, b0, st);
     if (e != hipSuccess) return e;
   }
-#define MERGE_LAUNCH(SM)                                                                    \
+  MergeTree tr{};
+  tr.on = a.fuse_tree ? 1 : 0;
+  if (a.fuse_tree) {
+    tr.plan = a.plan;
+    tr.root_tok = a.root_tok;
+    tr.kv_len = a.kv_len;
+    tr.tokens = a.tree_tokens;
+    tr.position_ids = a.position_ids;
+  }
+#define MERGE_LAUNCH(SM)                                                                      \
   hipLaunchKernelGGL(heads_merge_kernel<SM>, dim3(a.K, a.B), dim3(kMergeThreads), 0, st, a.K, \
-                     a.G, a.S, \
-                     a.part_val, a.part_id, a.part_m, a.part_s, a.topk_ids, a.topk_logits,   \
-                     a.lse)
+                     a.G, a.S, a.part_val, a.part_id, a.part_m, a.part_s, a.topk_ids,          \
+                     a.topk_logits, a.lse, tr)
   if (a.S <= 4)
     MERGE_LAUNCH(4);
   else if (a.S <= 8)

@@ -12,6 +12,17 @@ constexpr int MAXS_LDS = 16;   // top-s list slots (>= MEDUSA_MAX_S)
 constexpr int MAXT = 256;      // tree rows
 constexpr int MAXK = 8;        // tree depth
 
+// ---- tree --------------------------------------------------------------------
+// The host-validated tree spec, passed to the kernel by value: for node n
+// (canonical order, node 0 = root) its parent index and the rank of its own
+// token inside its depth's pool.
+struct TreePlan {
+  int T;
+  int K;
+  uint8_t parent[MAXT];      // parent[0] unused
+  uint8_t last_rank[MAXT];   // last_rank[0] unused
+  uint8_t depth[MAXT];       // depth[0] = 0
+};
 // ---- heads -------------------------------------------------------------------
 struct HeadsArgs {
   bool f32;
@@ -35,20 +46,18 @@ struct HeadsArgs {
   int interleave;         // 1: wave w streams rows w, w + nw, ...; 0: blocks of rows
   hipEvent_t ev_before;   // optional: recorded around the W2 kernel
   hipEvent_t ev_after;
+  // optional (composite step, top-s drafting): the merge of head k also
+  // writes the tokens of the depth-(k+1) nodes; head 0 writes the root
+  // token and every position id
+  bool fuse_tree;
+  TreePlan plan;
+  const int32_t* root_tok;     // [B]
+  const int32_t* kv_len;       // [B]
+  int32_t* tree_tokens;        // [B][T]
+  int32_t* position_ids;       // [B][T]
 };
 hipError_t launch_heads(const HeadsArgs& a, hipStream_t st);
 
-// ---- tree --------------------------------------------------------------------
-// The host-validated tree spec, passed to the kernel by value: for node n
-// (canonical order, node 0 = root) its parent index and the rank of its own
-// token inside its depth's pool.
-struct TreePlan {
-  int T;
-  int K;
-  uint8_t parent[MAXT];      // parent[0] unused
-  uint8_t last_rank[MAXT];   // last_rank[0] unused
-  uint8_t depth[MAXT];       // depth[0] = 0
-};
 struct TreeArgs {
   TreePlan plan;
   int B, V, S, P;
@@ -178,5 +187,8 @@ struct CommitArgs {
   float* h_next;
 };
 hipError_t launch_commit(const CommitArgs& a, hipStream_t st);
+// Composite step (greedy / typical): posterior + commit in one workgroup per
+// sequence.
+hipError_t launch_posterior_commit(const PostArgs& a, const CommitArgs& c, hipStream_t st);
 
 }  // namespace medusa

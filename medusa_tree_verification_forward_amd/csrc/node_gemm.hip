@@ -50,23 +50,6 @@ namespace {
 constexpr float kNegInf = -__builtin_huge_valf();
 constexpr int kMaxSplits = 16;
 
-// Merge of (max, S, W, argmax) records at temperature tau (see header).
-__device__ __forceinline__ void rec_merge(float& m, float& s, float& w, int& a, float m2,
-                                          float s2, float w2, int a2, float inv_tau) {
-  if (m2 == kNegInf) return;
-  if (m == kNegInf) {
-    m = m2; s = s2; w = w2; a = a2;
-    return;
-  }
-  const float mn = fmaxf(m, m2);
-  const float d1 = (m - mn) * inv_tau, d2 = (m2 - mn) * inv_tau;
-  const float c1 = exp_e(d1), c2 = exp_e(d2);
-  const int an = better(m, a, m2, a2) ? a : a2;
-  w = c1 * (w + s * d1) + c2 * (w2 + s2 * d2);
-  s = c1 * s + c2 * s2;
-  m = mn;
-  a = an;
-}
 
 // One A fragment times one W fragment (16-byte pieces of both operands).
 template <class ET>
@@ -455,29 +438,9 @@ __global__ __launch_bounds__(64) void row_stats_merge_kernel(const float* __rest
                                                              float* __restrict__ row_stats,
                                                              int* __restrict__ row_argmax) {
   const int r = blockIdx.x, lane = threadIdx.x;
-  float m = kNegInf, s = 0.f, w = 0.f;
-  int a = 0x7fffffff;
-  // all of a round's records are loaded before any is merged
-  constexpr int RB = 4;
-  for (int g0 = 0; g0 < G; g0 += 64 * RB) {
-    floatx4_t rec[RB];
-#pragma unroll
-    for (int u = 0; u < RB; ++u) {
-      const int g = min(g0 + lane + 64 * u, G - 1);
-      rec[u] = *reinterpret_cast<const floatx4_t*>(part + ((size_t)r * G + g) * 4);
-    }
-#pragma unroll
-    for (int u = 0; u < RB; ++u)
-      if (g0 + lane + 64 * u < G)
-        rec_merge(m, s, w, a, rec[u][0], rec[u][1], rec[u][2], __float_as_int(rec[u][3]),
-                  inv_tau);
-  }
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) {
-    const float m2 = __shfl_xor(m, off), s2 = __shfl_xor(s, off), w2 = __shfl_xor(w, off);
-    const int a2 = __shfl_xor(a, off);
-    rec_merge(m, s, w, a, m2, s2, w2, a2, inv_tau);
-  }
+  float m, s, w;
+  int a;
+  merge_row_records(part, G, r, inv_tau, m, s, w, a);
   if (lane == 0) {
     row_stats[(size_t)r * 3 + 0] = m;
     row_stats[(size_t)r * 3 + 1] = s;

@@ -40,25 +40,33 @@ __device__ __forceinline__ int wave_max_i(int v) {
              max(__builtin_amdgcn_readlane(v, 32), __builtin_amdgcn_readlane(v, 48)));
 }
 
-__global__ __launch_bounds__(256) void posterior_kernel(PostArgs a) {
-  const int b = blockIdx.x, c = threadIdx.x;
+// Statistics of one verify row: max, S, W at temperature tau, argmax.
+struct RowStat {
+  float m, S, W;
+  int am;
+};
+
+// Greedy / typical posterior of sequence b over the whole workgroup
+// (blockDim.x >= T, a multiple of 64). stat(i) returns the statistics of
+// row i of the sequence. Thread 0 writes the outputs; every thread returns
+// the committed node.
+template <class StatFn>
+__device__ int posterior_det_block(const PostArgs& a, int b, StatFn stat) {
+  const int c = threadIdx.x;
   const int T = a.T;
   __shared__ uint8_t acc[MAXT];
-  __shared__ int wmax[4];
+  __shared__ int wmax[16];
+  __shared__ int s_best;
   const int* tok = a.tokens + (size_t)b * T;
   if (c < T) {
     bool ok = true;
     if (c > 0) {
-      const int v = parent_of(a.parent, c, T);
-      const size_t pr = (size_t)b * T + v;
+      const RowStat ps = stat(parent_of(a.parent, c, T));
       if (a.mode == 0) {
-        ok = tok[c] == a.row_argmax[pr];
+        ok = tok[c] == ps.am;
       } else {
-        const float m = a.row_stats[pr * 3 + 0];
-        const float S = a.row_stats[pr * 3 + 1];
-        const float W = a.row_stats[pr * 3 + 2];
-        const float p = exp_e((a.child_logit[(size_t)b * T + c] - m) * a.inv_tau) / S;
-        const float H = __logf(S) - W / S;
+        const float p = exp_e((a.child_logit[(size_t)b * T + c] - ps.m) * a.inv_tau) / ps.S;
+        const float H = __logf(ps.S) - ps.W / ps.S;
         const float thr = fminf(a.eps, a.delta * exp_e(-H));
         ok = p > thr;
       }
@@ -77,29 +85,44 @@ __global__ __launch_bounds__(256) void posterior_kernel(PostArgs a) {
     if (ok) key = (dep << 16) | (0xffff - c);
   }
   key = wave_max_i(key);
-  if ((threadIdx.x & 63) == 0) wmax[threadIdx.x >> 6] = key;
+  const int nw = blockDim.x >> 6;
+  if ((c & 63) == 0) wmax[c >> 6] = key;
   __syncthreads();
-  if (c != 0) return;
-  key = max(max(wmax[0], wmax[1]), max(wmax[2], wmax[3]));
-  const int best = 0xffff - (key & 0xffff);
-  const int depth = key >> 16;
-  a.accept_len[b] = depth;
-  a.last_node[b] = best;
-  int* out = a.out_tokens + (size_t)b * (a.K + 1);
-  for (int j = depth + 1; j <= a.K; ++j) out[j] = -1;
-  int x = best;
-  for (int j = depth; j >= 0; --j) {
-    out[j] = tok[x];
-    x = parent_of(a.parent, x, T);
-  }
-  a.next_root[b] = a.row_argmax[(size_t)b * T + best];
-  int bp = 0;
-  for (int p = 0; p < a.P; ++p)
-    if (a.retrieve[(size_t)p * (a.K + 1) + depth] == best) {
-      bp = p;
-      break;
+  if (c == 0) {
+    key = wmax[0];
+    for (int w = 1; w < nw; ++w) key = max(key, wmax[w]);
+    const int best = 0xffff - (key & 0xffff);
+    const int depth = key >> 16;
+    a.accept_len[b] = depth;
+    a.last_node[b] = best;
+    int* out = a.out_tokens + (size_t)b * (a.K + 1);
+    for (int j = depth + 1; j <= a.K; ++j) out[j] = -1;
+    int x = best;
+    for (int j = depth; j >= 0; --j) {
+      out[j] = tok[x];
+      x = parent_of(a.parent, x, T);
     }
-  a.best_path[b] = bp;
+    a.next_root[b] = stat(best).am;
+    int bp = 0;
+    for (int p = 0; p < a.P; ++p)
+      if (a.retrieve[(size_t)p * (a.K + 1) + depth] == best) {
+        bp = p;
+        break;
+      }
+    a.best_path[b] = bp;
+    s_best = best;
+  }
+  __syncthreads();
+  return s_best;
+}
+
+__global__ __launch_bounds__(256) void posterior_kernel(PostArgs a) {
+  const int b = blockIdx.x;
+  posterior_det_block(a, b, [&](int i) {
+    const size_t r = (size_t)b * a.T + i;
+    return RowStat{a.row_stats[r * 3 + 0], a.row_stats[r * 3 + 1], a.row_stats[r * 3 + 2],
+                   a.row_argmax[r]};
+  });
 }
 
 // ---- exact mode ----------------------------------------------------------------
@@ -300,16 +323,16 @@ __global__ __launch_bounds__(1024) void posterior_exact_kernel(PostArgs a) {
 // head's row Dh is contiguous in the cache), so each thread moves a few
 // vectors and the copy is bound by one round trip to memory, not by a chain
 // of dependent element copies.
+// Commit of sequence b's accepted path ending at node `last` over the whole
+// workgroup (see commit_kernel).
 template <class ET>
-__global__ __launch_bounds__(1024) void commit_kernel(CommitArgs a) {
-  using S = typename ET::storage;
+__device__ void commit_block(const CommitArgs& a, int b, int last_in) {
   constexpr int PV = ET::kPerVec;
-  const int b = blockIdx.x;
   const int T = a.T, H = a.H, Dh = a.Dh;
   __shared__ int path[MAXK + 1];
   __shared__ int sh_L, sh_depth;
   if (threadIdx.x == 0) {
-    const int last = min(max(a.last_node[b], 0), T - 1);
+    const int last = min(max(last_in, 0), T - 1);
     int d = 0;
     for (int x = last; x != 0 && d < a.K; x = parent_of(a.parent, x, T)) ++d;
     int x = last;
@@ -348,6 +371,24 @@ __global__ __launch_bounds__(1024) void commit_kernel(CommitArgs a) {
   if (threadIdx.x == 0) a.kv_len[b] = room ? L + d + 1 : -1;
 }
 
+template <class ET>
+__global__ __launch_bounds__(1024) void commit_kernel(CommitArgs a) {
+  commit_block<ET>(a, blockIdx.x, a.last_node[blockIdx.x]);
+}
+
+// Composite step, greedy / typical: one workgroup per sequence evaluates the
+// posterior from the merged row statistics and commits the accepted path.
+template <class ET>
+__global__ __launch_bounds__(1024) void posterior_commit_kernel(PostArgs a, CommitArgs c) {
+  const int b = blockIdx.x;
+  const int best = posterior_det_block(a, b, [&](int i) {
+    const size_t r = (size_t)b * a.T + i;
+    return RowStat{a.row_stats[r * 3 + 0], a.row_stats[r * 3 + 1], a.row_stats[r * 3 + 2],
+                   a.row_argmax[r]};
+  });
+  commit_block<ET>(c, b, best);
+}
+
 }  // namespace
 
 hipError_t launch_posterior(const PostArgs& a, hipStream_t st) {
@@ -355,6 +396,14 @@ hipError_t launch_posterior(const PostArgs& a, hipStream_t st) {
     hipLaunchKernelGGL(posterior_exact_kernel, dim3(a.B), dim3(1024), 0, st, a);
   else
     hipLaunchKernelGGL(posterior_kernel, dim3(a.B), dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_posterior_commit(const PostArgs& a, const CommitArgs& c, hipStream_t st) {
+  if (c.f32)
+    hipLaunchKernelGGL(posterior_commit_kernel<F32>, dim3(a.B), dim3(1024), 0, st, a, c);
+  else
+    hipLaunchKernelGGL(posterior_commit_kernel<BF16>, dim3(a.B), dim3(1024), 0, st, a, c);
   return hipGetLastError();
 }
 

@@ -156,6 +156,47 @@ class VerifyStep:
         else:
             self.inp["kv_len"].copy_(self.kv_len0)
 
+    def step_args(self):
+        """medusa_step arguments over this object's buffers (built once)."""
+        if getattr(self, "_args", None) is not None:
+            return self._args
+        o, i, w = self.out, self.inp, self.packed
+        p = L._ptr
+        exact = self.mode == "exact"
+        self._ranks_host = np.ascontiguousarray(self.ranks, dtype=np.int32)
+        a = L.StepArgs()
+        a.h, a.W1, a.W2 = p(i["h"]), p(i["W1"]), p(i["W2"])
+        a.b1_or_null = p(i.get("b1"))
+        a.tree_ranks_host = self._ranks_host.ctypes.data if self._ranks_host.size else None
+        a.draft_mode = L.DRAFT_SAMPLE if exact else L.DRAFT_TOPK
+        a.root_tok = p(i["root"])
+        a.u_draft_or_null = p(i.get("u_draft")) if exact else None
+        a.tree_mask, a.parent, a.retrieve = p(o["tree_mask"]), p(o["parent"]), p(o["retrieve"])
+        a.E, a.W_qkv, a.W_o, a.W_lm = p(i["E"]), p(w["W_qkv"]), p(w["W_o"]), p(w["W_lm"])
+        a.rope_theta = self.theta
+        a.k_cache, a.v_cache, a.kv_len = p(i["k_cache"]), p(i["v_cache"]), p(i["kv_len"])
+        a.mode = L.MODES[self.mode]
+        a.temperature, a.eps, a.delta = self.tau, self.eps, self.delta
+        a.u_accept_or_null = p(i.get("u_accept")) if exact else None
+        a.u_resample_or_null = p(i.get("u_resample")) if exact else None
+        a.topk_ids, a.topk_logits = p(o["topk_ids"]), p(o["topk_logits"])
+        a.head_lse_or_null, a.head_logits_or_null = p(o["head_lse"]), p(o["head_logits"])
+        a.z_or_null = p(o["z"])
+        a.tree_tokens, a.position_ids = p(o["tree_tokens"]), p(o["position_ids"])
+        a.k_tree, a.v_tree, a.y = p(o["k_tree"]), p(o["v_tree"]), p(o["y"])
+        a.row_stats, a.row_argmax = p(o["row_stats"]), p(o["row_argmax"])
+        a.child_logit, a.verify_logits_or_null = p(o["child_logit"]), p(o["verify_logits"])
+        a.accept_len, a.best_path, a.last_node = (p(o["accept_len"]), p(o["best_path"]),
+                                                  p(o["last_node"]))
+        a.out_tokens, a.next_root, a.h_next = (p(o["out_tokens"]), p(o["next_root"]),
+                                               p(o["h_next"]))
+        self._args = a
+        return a
+
+    def run_step(self, stream=None):
+        """The whole step as one composite call (medusa_step)."""
+        L.step(self.shape, self.step_args(), self.ws, stream=stream)
+
     def run(self, stream=None, commit: bool = True):
         """The whole step: heads, tree, verify forward, posterior, commit."""
         self.heads(stream)

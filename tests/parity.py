@@ -42,12 +42,16 @@ def oracle_for(w):
     return _ORACLE[w]
 
 
-def gpu_step(w, inp, want_logits=True):
+def gpu_step(w, inp, want_logits=True, composite=False):
+    """One step on the GPU: the five calls, or the composite medusa_step."""
     import torch
     from medusa_tree_verification_forward_amd.step import VerifyStep
     st = VerifyStep(inp, H=w.H, Dh=w.Dh, s_max=w.s_max, mode=w.mode, tau=w.tau, eps=w.eps,
                     delta=w.delta, theta=w.rope_theta, want_logits=want_logits)
-    st.run()
+    if composite:
+        st.run_step()
+    else:
+        st.run()
     torch.cuda.synchronize()
     res = st.results()
     from medusa_tree_verification_forward_amd.step import to_host

@@ -119,3 +119,28 @@ def test_heads_workspace_too_small():
     rc = lib.medusa_heads_forward(ctypes.byref(shape), FAKE, FAKE, None, FAKE, FAKE, FAKE, None,
                                   None, None, FAKE, 16, None)
     assert rc == M._lib.ERR_WORKSPACE
+
+
+def test_step_args_layout_matches_header(tmp_path):
+    """The binding's StepArgs mirrors medusa_step_args member for member."""
+    import shutil
+    import subprocess
+    M = _lib()
+    cc = shutil.which("gcc") or shutil.which("cc")
+    if cc is None:
+        pytest.skip("no C compiler")
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    names = [f for f, _ in M.StepArgs._fields_]
+    lines = ["#include <stdio.h>", "#include <stddef.h>", '#include "medusa.h"',
+             "int main(void) {", '  printf("%zu\\n", sizeof(medusa_step_args));']
+    lines += [f'  printf("%zu\\n", offsetof(medusa_step_args, {n}));' for n in names]
+    lines += ["  return 0;", "}"]
+    src = tmp_path / "layout.c"
+    src.write_text("\n".join(lines) + "\n")
+    exe = tmp_path / "layout"
+    subprocess.run([cc, "-I", os.path.join(root, "include"), str(src), "-o", str(exe)],
+                   check=True)
+    out = [int(x) for x in subprocess.run([str(exe)], capture_output=True, text=True,
+                                          check=True).stdout.split()]
+    assert out[0] == ctypes.sizeof(M.StepArgs)
+    assert out[1:] == [getattr(M.StepArgs, n).offset for n in names]
