@@ -143,7 +143,7 @@ Layout layout_for(const medusa_shape* s) {
   L.o_elem = take(B * T * d * es);
   L.y_elem = take(B * T * d * es);
   {
-    // LM records [M][groups][4], or split-K partial logits [KS][M][V + 128]
+    // LM records [M][groups][4], or split-K partial logits [groups][KS][M][cols]
     const size_t rec = B * T * gemm_groups_max(s->V) * 4;
     const int lm_ks = lm_splits_for((int)(B * T));
     const size_t split = lm_ks > 1 ? (size_t)lm_ks * B * T * (s->V + 128) : 0;
@@ -151,7 +151,7 @@ Layout layout_for(const medusa_shape* s) {
   }
   {
     const bool f32 = s->dtype == MEDUSA_F32;
-    // partials [groups][M][cols][KS]: groups * cols < N + 128
+    // partials [groups][KS][M][cols]: groups * cols < N + 128
     const size_t q_need = (size_t)gemm_splits(3 * s->d, s->d, f32) * B * T * (3 * d + 128);
     const size_t o_need = (size_t)gemm_splits(s->d, s->d, f32) * B * T * (d + 128);
     L.gemm_part = take((q_need > o_need ? q_need : o_need) * 4);

@@ -140,6 +140,50 @@ __device__ __forceinline__ void lds_barrier() {
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
 }
 
+// ---- hand-off between the workgroups of one launch -----------------------------
+// The L2 caches of the XCDs are not coherent with each other. Relaxed atomic
+// loads and stores at agent scope are: they compile to ordinary vector
+// loads and stores with the sc1 cache-policy bit (stores written through to
+// the coherent level, loads served from it), with no L2 write-back or
+// invalidate. Data that one workgroup hands to another in the same launch
+// goes through these, so the hand-off needs no device-wide fence (whose L2
+// write-back and invalidate would also evict the weight and activation lines
+// the other workgroups are still using).
+__device__ __forceinline__ void coherent_store(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void coherent_store(int* p, int v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float coherent_load(const float* p) {
+  return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ int coherent_load(const int* p) {
+  return __hip_atomic_load(const_cast<int*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Counts the calling workgroup in on `counter` and returns, in every thread,
+// whether it is the last of `n` workgroups to arrive; the last one resets the
+// counter to zero for the next launch. Every coherent_store of the workgroup
+// issued before the call is complete (each wave waits for its vector memory
+// operations, vmcnt 0) before the count moves, so the last workgroup's
+// coherent_loads afterwards see them all.
+__device__ __forceinline__ bool last_to_arrive(int* counter, int n) {
+  __shared__ int s_last;
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  vmcnt<0>();
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const int before =
+        __hip_atomic_fetch_add(counter, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    s_last = before == n - 1;
+    if (before == n - 1) coherent_store(counter, 0);
+  }
+  __syncthreads();
+  return s_last != 0;
+}
+
 // Transposing LDS read (gfx950 ds_read_b64_tr_b16). Within each group of 16
 // lanes, let lane 4k + q pass the address of 4 consecutive 16-bit elements
 // of row R_k (elements c + 4q .. c + 4q + 3): lane i then receives element

@@ -139,8 +139,8 @@ struct AttnArgs {
   const int32_t* kv_len;       // [B]
   const uint8_t* mask;         // [T][T]
   float scale;
-  int NS;                      // splits per (b, h): 1 tree split + prefix splits
-  float* part_o;               // [B][H][NS][T][Dh]
+  int NS;                      // prefix splits per (b, h) (kAttnChunk keys each)
+  float* part_o;               // [B][H][NS][Dh/16][T][16]
   float* part_ml;              // [B][H][NS][T][2]
   float* out;                  // [B][T][H][Dh] fp32 (or null)
   void* out_elem;              // [B][T][H][Dh] storage type (or null)

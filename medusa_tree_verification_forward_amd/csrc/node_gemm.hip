@@ -20,7 +20,7 @@
 //  * Rows beyond one pass of 16*MT go to further workgroups (grid z).
 //
 // QKV and the output projection split K over KS workgroups per column group
-// and write fp32 partials part[g][r][c][ks]; an epilogue sums the KS slices
+// and write fp32 partials part[g][ks][r][c]; an epilogue sums the KS slices
 // of each output in slice order and applies
 //   QKV  : RoPE on q and k (pairs i, i+Dh/2; angle pos * theta^(-2i/Dh)),
 //          rounding to the storage type, scatter to [B][T][H][Dh];
@@ -28,9 +28,10 @@
 // W_qkv is packed with the rows of every head reordered so that each
 // 16-column tile holds 8 whole rotation pairs (columns j and j+8 of the tile
 // are rows i and i+Dh/2 of the head, i = 8*(tile in head) + j).
-// The epilogue runs either in a kernel of its own, or (fused) in the last
-// of the KS workgroups of a group to finish, found with a device-scope
-// counter that it leaves at zero for the next launch.
+// The epilogue runs in the last of the KS workgroups of a group to finish
+// (found with a device-scope counter that it leaves at zero for the next
+// launch; the partials travel through agent-coherent stores and loads), or
+// in a kernel of its own.
 // The LM head runs with KS = 1 and reduces in-kernel: per row and column
 // group (max, argmax, S, W) at temperature tau with S = sum e^{(l-m)/tau},
 // W = sum e^{(l-m)/tau} (l-m)/tau; the logit of every tree node's token
@@ -99,31 +100,10 @@ __global__ void pack_weight_kernel(const typename ET::storage* __restrict__ W, i
   out[q] = v;
 }
 
-// Sum, in slice order, of the KS partials of one output (KS contiguous floats).
-__device__ __forceinline__ float sum_slices(const float* p, int KS) {
-  float acc = 0.f;
-  if (KS == 2) {
-    const float2 v = *reinterpret_cast<const float2*>(p);
-    acc += v.x;
-    acc += v.y;
-  } else if ((KS & 3) == 0) {
-    for (int s = 0; s < KS; s += 4) {
-      const floatx4_t v = *reinterpret_cast<const floatx4_t*>(p + s);
-      acc += v[0];
-      acc += v[1];
-      acc += v[2];
-      acc += v[3];
-    }
-  } else {
-    for (int s = 0; s < KS; ++s) acc += p[s];
-  }
-  return acc;
-}
-
 // QKV epilogue for one rotation pair (packed columns c1, c1 + 8) of row r.
 template <class ET>
-__device__ __forceinline__ void qkv_finish(const GemmParams& p, int r, int c1, float x1,
-                                           float x2) {
+__device__ __forceinline__ void qkv_finish(const GemmParams& p, int r, int c1, int pos,
+                                           float x1, float x2) {
   using St = typename ET::storage;
   const int Dh = p.Dh, half = Dh >> 1;
   const int blk = c1 / Dh, nl = c1 - blk * Dh;
@@ -131,7 +111,7 @@ __device__ __forceinline__ void qkv_finish(const GemmParams& p, int r, int c1, f
   const int which = blk / p.H, h = blk - which * p.H;
   if (which < 2) {
     const double inv_freq = exp(-(2.0 * i / Dh) * p.log_theta);
-    const double turns = (double)p.pos[r] * inv_freq * 0.15915494309189535;   // 1/(2 pi)
+    const double turns = (double)pos * inv_freq * 0.15915494309189535;   // 1/(2 pi)
     const float ang = (float)((turns - rint(turns)) * 6.283185307179586);
     float sn, cs;
     __sincosf(ang, &sn, &cs);
@@ -146,24 +126,50 @@ __device__ __forceinline__ void qkv_finish(const GemmParams& p, int r, int c1, f
   o[half] = ET::from_float(x2);
 }
 
+// y = x + acc, x = E[token of row r]: written as fp32 and storage type.
+template <class ET>
+__device__ __forceinline__ void oproj_store(const GemmParams& p, int r, int n, float y) {
+  using St = typename ET::storage;
+  p.y_out[(size_t)r * p.N + n] = y;
+  reinterpret_cast<St*>(p.y_elem)[(size_t)r * p.N + n] = ET::from_float(y);
+}
+
 template <class ET>
 __device__ __forceinline__ void oproj_finish(const GemmParams& p, int r, int n, float acc) {
   using St = typename ET::storage;
   const St* x = reinterpret_cast<const St*>(p.E) +
                 (size_t)min(max(p.tokens[r], 0), p.a_nrows - 1) * p.N;
-  const float y = ET::load1(x + n) + acc;
-  p.y_out[(size_t)r * p.N + n] = y;
-  reinterpret_cast<St*>(p.y_elem)[(size_t)r * p.N + n] = ET::from_float(y);
+  oproj_store<ET>(p, r, n, ET::load1(x + n) + acc);
 }
 
-// partials of output (r, packed column n): part[g][r][c][ks], g = n / GC
+// Partials are stored part[g][ks][r][c] (g = n / GC, c = n % GC): a
+// workgroup's slice is one contiguous [M][GC] block.
 __device__ __forceinline__ const float* partial_at(const GemmParams& p, int r, int n, int KS) {
   const int g = n / p.group_cols, c = n - g * p.group_cols;
-  return p.part + (((size_t)g * p.M + r) * p.group_cols + c) * KS;
+  return p.part + ((size_t)g * KS * p.M + r) * p.group_cols + c;
+}
+
+// Sum, in slice order, of the KS partials of output (r, n); loads of up to
+// four slices are issued before any is added.
+__device__ __forceinline__ float sum_partials(const GemmParams& p, int r, int n, int KS) {
+  const float* q = partial_at(p, r, n, KS);
+  const size_t stride = (size_t)p.M * p.group_cols;
+  float acc = 0.f;
+  int s = 0;
+  for (; s + 4 <= KS; s += 4) {
+    const float v0 = q[s * stride], v1 = q[(s + 1) * stride], v2 = q[(s + 2) * stride],
+                v3 = q[(s + 3) * stride];
+    acc += v0;
+    acc += v1;
+    acc += v2;
+    acc += v3;
+  }
+  for (; s < KS; ++s) acc += q[s * stride];
+  return acc;
 }
 
 template <class ET, int WV, int MT, int CH, int D, int EPI>
-__global__ __launch_bounds__(64 * WV, WV == 4 ? 4 : 2) void node_gemm_kernel(
+__global__ __launch_bounds__(64 * WV, (WV == 4 && D <= 8) ? 4 : 2) void node_gemm_kernel(
     GemmParams p) {
   using St = typename ET::storage;
   constexpr int PV = ET::kPerVec, KT = 4 * PV;   // k elements per tile
@@ -193,7 +199,6 @@ __global__ __launch_bounds__(64 * WV, WV == 4 ? 4 : 2) void node_gemm_kernel(
   __shared__ u32x4_t sA0[CH][MT][64];
   __shared__ u32x4_t sA1[CH][MT][64];
   __shared__ float stat[EPI == EPI_LM ? WV : 1][EPI == EPI_LM ? 16 * MT : 1][4];
-  __shared__ int s_last;
 
   // A fragment f = wave + WV i of a chunk is (k-tile f / MT, m-tile f % MT)
   const St* asrc[NAW];
@@ -282,43 +287,113 @@ __global__ __launch_bounds__(64 * WV, WV == 4 ? 4 : 2) void node_gemm_kernel(
   }
 
   if constexpr (EPI != EPI_LM) {
-    // partials of slice ks: part[g][r][c][ks]
-    float* part = p.part + ((size_t)g * p.M * GC + 16 * wave + li) * KS + ks;
+    // slice ks of the partials: part[g][ks][r][c]
+    float* part = p.part + (size_t)(g * KS + ks) * p.M * GC + 16 * wave + li;
+    const bool fused = EPI != EPI_PART && p.fused;
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int r = m0 + 16 * mt + 4 * lq + j;
-        if (r < p.M) part[(size_t)r * GC * KS] = acc[mt][j];
+        if (r < p.M) {
+          if (fused)
+            coherent_store(part + (size_t)r * GC, acc[mt][j]);
+          else
+            part[(size_t)r * GC] = acc[mt][j];
+        }
       }
-    if constexpr (EPI == EPI_PART) return;
-    if (!p.fused) return;
-    // The last of the KS workgroups of this (group, pass) finishes it.
-    __threadfence();   // release this workgroup's partials device-wide
-    __syncthreads();
-    int* counter = p.counters + g * gridDim.z + blockIdx.z;
-    if (threadIdx.x == 0) s_last = atomicAdd(counter, 1) == KS - 1;
-    __syncthreads();
-    if (!s_last) return;
-    __threadfence();   // acquire the other workgroups' partials
-    if (threadIdx.x == 0) *counter = 0;
-    const int rows_hi = min(p.M, m0 + 16 * MT);
+    if (!fused) return;
+    // The last of the KS workgroups of this (group, pass) finishes it: every
+    // thread loads all the slices of its outputs (and the row data they
+    // need) before it uses any, then sums them in slice order.
+    if (!last_to_arrive(p.counters + g * gridDim.z + blockIdx.z, KS)) return;
+    constexpr int NT = 64 * WV;
+    const size_t sstride = (size_t)p.M * GC;
+    const float* gpart = p.part + (size_t)g * KS * p.M * GC;
     if constexpr (EPI == EPI_QKV) {
-      // threads: 8 WV pairs x 8 row lanes
-      const int pi = threadIdx.x % (8 * WV), rl = threadIdx.x / (8 * WV);
-      const int c1 = n0 + 16 * (pi >> 3) + (pi & 7);
-      if (c1 >= p.N) return;
-      for (int r = m0 + rl; r < rows_hi; r += 8) {
-        const float x1 = sum_slices(partial_at(p, r, c1, KS), KS);
-        const float x2 = sum_slices(partial_at(p, r, c1 + 8, KS), KS);
-        qkv_finish<ET>(p, r, c1, x1, x2);
+      // thread: rotation pair pi of the group (packed columns c1, c1 + 8),
+      // rows m0 + rl + RL i, in batches of RB rows
+      constexpr int PG = 8 * WV, RL = NT / PG, RPT = 16 * MT / RL;
+      constexpr int RB = RPT < 6 ? RPT : 6;
+      static_assert(RPT % RB == 0, "row batches");
+      const int pi = threadIdx.x % PG, rl = threadIdx.x / PG;
+      const int cl = 16 * (pi >> 3) + (pi & 7), c1 = n0 + cl;
+#pragma unroll 1
+      for (int i0 = 0; i0 < RPT; i0 += RB) {
+        float x1[RB], x2[RB];
+        int pos[RB];
+#pragma unroll
+        for (int i = 0; i < RB; ++i) {
+          x1[i] = x2[i] = 0.f;
+          pos[i] = p.pos[min(m0 + rl + RL * (i0 + i), p.M - 1)];
+        }
+        for (int s0 = 0; s0 < KS; s0 += 2) {
+          float v1[2][RB], v2[2][RB];
+#pragma unroll
+          for (int u = 0; u < 2; ++u)
+#pragma unroll
+            for (int i = 0; i < RB; ++i) {
+              const int r = min(m0 + rl + RL * (i0 + i), p.M - 1);
+              const float* q = gpart + min(s0 + u, KS - 1) * sstride + (size_t)r * GC + cl;
+              v1[u][i] = coherent_load(q);
+              v2[u][i] = coherent_load(q + 8);
+            }
+#pragma unroll
+          for (int u = 0; u < 2; ++u)
+            if (s0 + u < KS)
+#pragma unroll
+              for (int i = 0; i < RB; ++i) {
+                x1[i] += v1[u][i];
+                x2[i] += v2[u][i];
+              }
+        }
+        if (c1 < p.N)
+#pragma unroll
+          for (int i = 0; i < RB; ++i) {
+            const int r = m0 + rl + RL * (i0 + i);
+            if (r < p.M) qkv_finish<ET>(p, r, c1, pos[i], x1[i], x2[i]);
+          }
       }
-    } else {
+    } else if constexpr (EPI == EPI_OPROJ) {
+      // thread: column cl of the group, rows m0 + rl + RL i, in batches of RB
+      constexpr int RL = NT / GC, RPT = 16 * MT / RL;
+      constexpr int RB = RPT < 12 ? RPT : 12;
+      static_assert(RPT % RB == 0, "row batches");
       const int cl = threadIdx.x % GC, rl = threadIdx.x / GC;
-      const int n = n0 + cl;
-      if (n >= p.N) return;
-      for (int r = m0 + rl; r < rows_hi; r += 4)
-        oproj_finish<ET>(p, r, n, sum_slices(partial_at(p, r, n, KS), KS));
+      const int n = min(n0 + cl, p.N - 1);
+#pragma unroll 1
+      for (int i0 = 0; i0 < RPT; i0 += RB) {
+        float x[RB], acc_s[RB];
+#pragma unroll
+        for (int i = 0; i < RB; ++i) {
+          const int r = min(m0 + rl + RL * (i0 + i), p.M - 1);
+          const int tok = min(max(p.tokens[r], 0), p.a_nrows - 1);
+          x[i] = ET::load1(reinterpret_cast<const St*>(p.E) + (size_t)tok * p.N + n);
+          acc_s[i] = 0.f;
+        }
+        for (int s0 = 0; s0 < KS; s0 += 4) {
+          float v[4][RB];
+#pragma unroll
+          for (int u = 0; u < 4; ++u)
+#pragma unroll
+            for (int i = 0; i < RB; ++i) {
+              const int r = min(m0 + rl + RL * (i0 + i), p.M - 1);
+              v[u][i] =
+                  coherent_load(gpart + min(s0 + u, KS - 1) * sstride + (size_t)r * GC + cl);
+            }
+#pragma unroll
+          for (int u = 0; u < 4; ++u)
+            if (s0 + u < KS)
+#pragma unroll
+              for (int i = 0; i < RB; ++i) acc_s[i] += v[u][i];
+        }
+        if (n0 + cl < p.N)
+#pragma unroll
+          for (int i = 0; i < RB; ++i) {
+            const int r = m0 + rl + RL * (i0 + i);
+            if (r < p.M) oproj_store<ET>(p, r, n, x[i] + acc_s[i]);
+          }
+      }
     }
   } else {
     const bool cv = col < p.N;
@@ -421,16 +496,16 @@ __global__ __launch_bounds__(256) void qkv_epilogue_kernel(GemmParams p, int KS)
   const int P = blockIdx.x * 256 + threadIdx.x;   // pair index over the packed columns
   const int c1 = 16 * (P >> 3) + (P & 7);
   if (c1 >= p.N) return;
-  const float x1 = sum_slices(partial_at(p, r, c1, KS), KS);
-  const float x2 = sum_slices(partial_at(p, r, c1 + 8, KS), KS);
-  qkv_finish<ET>(p, r, c1, x1, x2);
+  const float x1 = sum_partials(p, r, c1, KS);
+  const float x2 = sum_partials(p, r, c1 + 8, KS);
+  qkv_finish<ET>(p, r, c1, p.pos[r], x1, x2);
 }
 
 template <class ET>
 __global__ __launch_bounds__(256) void oproj_epilogue_kernel(GemmParams p, int KS) {
   const int r = blockIdx.y, n = blockIdx.x * 256 + threadIdx.x;
   if (n >= p.N) return;
-  oproj_finish<ET>(p, r, n, sum_slices(partial_at(p, r, n, KS), KS));
+  oproj_finish<ET>(p, r, n, sum_partials(p, r, n, KS));
 }
 
 __global__ __launch_bounds__(64) void row_stats_merge_kernel(const float* __restrict__ part,
@@ -468,7 +543,7 @@ __global__ __launch_bounds__(kStatThreads) void lm_stats_kernel(GemmParams p, in
     float lv[U];
 #pragma unroll
     for (int u = 0; u < U; ++u)
-      lv[u] = sum_slices(partial_at(p, r, min(n0 + t + kStatThreads * u, V - 1), KS), KS);
+      lv[u] = sum_partials(p, r, min(n0 + t + kStatThreads * u, V - 1), KS);
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int n = n0 + t + kStatThreads * u;
@@ -483,7 +558,7 @@ __global__ __launch_bounds__(kStatThreads) void lm_stats_kernel(GemmParams p, in
   if (t >= 1 && t < T && min(max(p.parent[t], 0), T - 1) == rl) {
     const int node = b * T + t;
     const int tok = min(max(p.tokens[node], 0), V - 1);
-    p.child_logit[node] = sum_slices(partial_at(p, r, tok, KS), KS);
+    p.child_logit[node] = sum_partials(p, r, tok, KS);
   }
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) {
@@ -517,12 +592,18 @@ struct Config {
   int wv, mt, ch, d;
 };
 
-// MEDUSA_GEMM_WAVES (4 or 8, default 4) picks the workgroup size of the
-// 48-row tile; taller tiles use 8 waves, 4-tile chunks and 4 loads in flight.
-int small_waves() {
-  static const int v = [] {
-    const char* s = getenv("MEDUSA_GEMM_WAVES");
-    return (s && atoi(s) == 8) ? 8 : 4;
+// MEDUSA_GEMM_CFG ("wv,ch,d", default "4,4,8") picks the 48-row tile of the
+// QKV and output projections: waves per workgroup, k-tiles per A chunk and
+// weight loads in flight per wave (4,4,8; 8,8,8; 8,8,16 or 4,8,16).
+Config small_config() {
+  static const Config v = [] {
+    const char* s = getenv("MEDUSA_GEMM_CFG");
+    int wv = 4, ch = 4, d = 8;
+    if (s && *s) sscanf(s, "%d,%d,%d", &wv, &ch, &d);
+    if (wv == 8 && ch == 8 && d == 16) return Config{8, 3, 8, 16};
+    if (wv == 8 && ch == 8 && d == 8) return Config{8, 3, 8, 8};
+    if (wv == 4 && ch == 8 && d == 16) return Config{4, 3, 8, 16};
+    return Config{4, 3, 4, 8};
   }();
   return v;
 }
@@ -545,7 +626,7 @@ Config lm_config() {
 Config config_for(int M, int epi) {
   if (M <= 48) {
     if (epi == EPI_LM || epi == EPI_PART) return lm_config();
-    return small_waves() == 8 ? Config{8, 3, 8, 8} : Config{4, 3, 4, 8};
+    return small_config();
   }
   return Config{8, 12, 4, 4};
 }
@@ -565,10 +646,13 @@ bool packed_kmajor() {
 
 namespace {
 
+// QKV and output-projection epilogues run in the last workgroup of each
+// column group (default), or with MEDUSA_GEMM_FUSED_EPILOGUE=0 in a kernel of
+// their own.
 bool fused_epilogue() {
   static const bool v = [] {
     const char* s = getenv("MEDUSA_GEMM_FUSED_EPILOGUE");
-    return s && atoi(s) != 0;
+    return !(s && *s && atoi(s) == 0);
   }();
   return v;
 }
@@ -579,7 +663,9 @@ hipError_t launch_main(const GemmParams& p, int KS, hipStream_t st) {
   const int groups = (p.N + 16 * c.wv - 1) / (16 * c.wv);
   const int passes = (p.M + 16 * c.mt - 1) / (16 * c.mt);
   dim3 grid(groups, KS, passes), block(64 * c.wv);
-  if (c.mt == 3 && c.wv == 4)
+  if (c.mt == 3 && c.wv == 4 && c.d == 16)
+    hipLaunchKernelGGL((node_gemm_kernel<ET, 4, 3, 8, 16, EPI>), grid, block, 0, st, p);
+  else if (c.mt == 3 && c.wv == 4)
     hipLaunchKernelGGL((node_gemm_kernel<ET, 4, 3, 4, 8, EPI>), grid, block, 0, st, p);
   else if (c.mt == 3 && c.d == 8)
     hipLaunchKernelGGL((node_gemm_kernel<ET, 8, 3, 8, 8, EPI>), grid, block, 0, st, p);

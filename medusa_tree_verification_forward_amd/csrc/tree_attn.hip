@@ -2,25 +2,31 @@
 // attention; "Medusa 深读", §6.1): every tree node attends to the whole
 // prefix KV cache and to its own ancestors (and itself) among the tree nodes.
 //
-// Split-KV (flash-decoding) layout: workgroup (s, h, b) handles one key
-// range -- split 0 is the tree block (T keys under the ancestor mask), split
-// s >= 1 covers prefix keys [(s-1)*C, s*C) -- for all T queries of (b, h),
-// and leaves an unnormalised partial (m, l, O) per query. A merge kernel
-// combines the splits in a fixed order.
+// Split-KV (flash-decoding) layout: workgroup (s, h, b) handles prefix keys
+// [s*C, (s+1)*C), C = kAttnChunk, for all T queries of (b, h), and leaves an
+// unnormalised partial (m, l, O) per query (m in log2 units of the scaled
+// score; O of a split stored [dh tile][query][16], so that a wave's 16x16
+// output tile is one contiguous 1 KB store). The merge kernel, one wave per (b, query, h), combines the splits
+// in order and then adds the query's tree keys -- the nodes the ancestor
+// mask allows, at most the tree depth plus one of them, so a few dot
+// products per query -- in increasing node order.
 //
-// Inside a workgroup everything is computed transposed, so that no lane
-// shuffles are needed between the two products:
-//   S^T = K Q^T     (A = K rows from LDS; B = Q rows, in registers),
-//   P^T = 2^(S^T * scale*log2e - m),
-//   O^T += V^T P^T  (A = V^T: V rows sit row-major in LDS and gfx950's
-//                    transposing LDS read (ds_read_b64_tr_b16) returns each
-//                    lane 4 keys of one dh; B = P^T straight from the S^T
-//                    accumulators, since the MFMA result layout puts the 4
-//                    keys of a lane exactly where the next MFMA's B operand
-//                    expects its k slots, up to a permutation shared with A).
-// In every accumulator a lane's column is one query, so the online-softmax
-// statistics (m, l, rescale factor) of a query live in that lane alone.
-// Waves split the query tiles (16 queries each).
+// bf16 prefix kernel (8 waves, 32 keys each; as many workgroups as fit the
+// device at once, each looping over chunks s, s + G, ... of its (b, h) with
+// the next chunk's K and V loads in flight while it computes the current):
+//   * S^T = K Q^T on MFMA: the K fragments (A operand, 16 keys x 32 dh) are
+//     16-byte pieces of cache rows, loaded straight into registers; each
+//     wave scores its own 32 keys against all query tiles.
+//   * Exact softmax over the chunk: per-query maxima and sums of the 8 waves
+//     meet in LDS (fixed order).
+//   * P (bf16) goes to LDS, V rows to LDS (row-major, padded); then the
+//     waves split O^T = V^T P^T by output dh tile: the A operand (16 dh x 32
+//     keys of V^T) comes from gfx950's transposing LDS read
+//     (ds_read_b64_tr_b16), the B operand (32 keys x 16 queries of P^T) is
+//     one 16-byte LDS read, P being stored in the key order the transposing
+//     read produces. No wave has to reduce another's O.
+// fp32 prefix kernel (4 waves, one query tile per wave, online softmax over
+// rounds of keys staged in LDS) for fp32 storage.
 #include "common.h"
 #include "kernels.h"
 
@@ -28,71 +34,255 @@ namespace medusa {
 namespace {
 
 constexpr float kNegInf = -__builtin_huge_valf();
+constexpr float kLog2e = 1.4426950408889634f;
 
-// SC keys are staged per round: K and V rows go to LDS (row-major, padded)
-// with 16-byte stores; the global loads of the next round are in flight
-// while the waves compute the current one from LDS.
-template <class ET, int DH, int QT, int SC>
-__global__ __launch_bounds__(256) void tree_attn_kernel(AttnArgs a) {
-  using S = typename ET::storage;
-  constexpr int PV = ET::kPerVec;
-  constexpr bool BF = PV == 8;
-  constexpr int DS = DH / (4 * PV);   // 16-byte steps along Dh per lane group
-  constexpr int DT = DH / 16;         // dh tiles of the output
-  constexpr int KT = SC / 16;         // key tiles per round
-  constexpr int PAD = 16 / sizeof(S); // 16 bytes of padding per LDS row
-  constexpr int VEC_PER_KEY = DH / PV;
+constexpr int kPfxWaves = 8;   // waves of the bf16 prefix kernel, 32 keys each
+static_assert(kPfxWaves * 32 == kAttnChunk, "one 32-key MFMA step per wave");
+
+template <int DH, int QG>
+__global__ __launch_bounds__(64 * kPfxWaves) void prefix_attn_bf16_kernel(AttnArgs a) {
+  using S = uint16_t;
+  static_assert(64 * kPfxWaves == 512, "Q staging assumes 512 threads");
+  constexpr int DS = DH / 32;             // 32-element k-steps of q.k
+  constexpr int DT = DH / 16;             // output dh tiles
+  constexpr int VP = DH / 8;              // 16-byte pieces per key row
+  constexpr int VL = 32 * VP / 64;        // V pieces per lane (32 keys per wave)
+  constexpr int VSTR = DH + 16;           // V row stride in LDS: 288 / 160 bytes keep the
+                                          // transposing reads conflict-free
+  constexpr int PSTR = kAttnChunk + 8;    // P row stride in LDS (528 bytes)
+  constexpr int QSTR = DH + 8;            // Q row stride in LDS (272 / 144 bytes)
+  constexpr int ITEMS = (QG * DT + kPfxWaves - 1) / kPfxWaves;   // (query tile, dh tile) per wave
+  constexpr int QPIECES = 16 * QG * VP;   // 16-byte pieces of a query group's Q rows
+  constexpr int QR = (QPIECES + 511) / 512;
+  const int h = blockIdx.y, b = blockIdx.z, G = gridDim.x;
+  const int T = a.T, H = a.H;
+  const int L = min(max(a.kv_len[b], 0), a.Lmax);
+  int s = blockIdx.x;   // chunks s, s + G, ... of (b, h)
+  if (s * kAttnChunk >= L) return;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int li = lane & 15, lq = lane >> 4;
+  const int MQ = (T + 15) / 16;
+  const bool one_group = MQ <= QG;   // Q stays in LDS for every chunk
+  const float sl2 = a.scale * kLog2e;
+
+  __shared__ S qs[16 * QG][QSTR];
+  __shared__ S vs[kAttnChunk][VSTR];
+  __shared__ S ps[16 * QG][PSTR];
+  __shared__ float red_m[kPfxWaves][16 * QG];
+  __shared__ float red_l[kPfxWaves][16 * QG];
+
+  const size_t head = ((size_t)b * H + h) * a.Lmax;
+  const S* __restrict__ kc = reinterpret_cast<const S*>(a.k_cache) + head * DH;
+  const S* __restrict__ vc = reinterpret_cast<const S*>(a.v_cache) + head * DH;
+  const S* __restrict__ qb = reinterpret_cast<const S*>(a.q);
+
+  // Q rows of query tiles g0 .. g0 + QG - 1, one 16-byte piece per thread and round
+  auto load_q = [&](int g0, u32x4_t(&qv)[QR]) {
+#pragma unroll
+    for (int r = 0; r < QR; ++r) {
+      const int p = min((int)threadIdx.x + 512 * r, QPIECES - 1), qr = p / VP, c = p - qr * VP;
+      const int qi = min(16 * g0 + qr, T - 1);
+      qv[r] = load16(qb + (((size_t)b * T + qi) * H + h) * DH + 8 * c);
+    }
+  };
+  // this wave's 32 keys of a chunk (rows past L are read clamped and masked later):
+  // K fragments (A operand), key 16 kt + li, dh 8 lq + 32 ds .. + 7; V rows, piece
+  // p = lane + 64 i at key p / VP, dh 8 (p % VP)
+  auto load_kv = [&](int chunk, u32x4_t(&kf)[2][DS], u32x4_t(&vv)[VL]) {
+    const int key0 = chunk * kAttnChunk + 32 * wave;
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int ds = 0; ds < DS; ++ds)
+        kf[kt][ds] = load16(kc + (size_t)min(key0 + 16 * kt + li, L - 1) * DH + 8 * lq + 32 * ds);
+#pragma unroll
+    for (int i = 0; i < VL; ++i) {
+      const int p = lane + 64 * i, kk = p / VP, c = p - kk * VP;
+      vv[i] = load16(vc + (size_t)min(key0 + kk, L - 1) * DH + 8 * c);
+    }
+  };
+
+  u32x4_t qv[QR];
+  load_q(0, qv);
+  u32x4_t kf[2][DS], vv[VL];
+  load_kv(s, kf, vv);
+  for (bool first = true;; first = false) {
+    const int key0 = s * kAttnChunk + 32 * wave;
+    const int sn = s + G;
+    const bool more = sn * kAttnChunk < L;
+#pragma unroll
+    for (int i = 0; i < VL; ++i) {
+      const int p = lane + 64 * i, kk = p / VP, c = p - kk * VP;
+      *reinterpret_cast<u32x4_t*>(&vs[32 * wave + kk][8 * c]) = vv[i];
+    }
+    u32x4_t kn[2][DS], vn[VL];
+    if (more) load_kv(sn, kn, vn);   // next chunk in flight during this one
+
+    const size_t base = ((size_t)b * H + h) * a.NS * T + (size_t)s * T;   // partial row of query 0
+    for (int g0 = 0; g0 < MQ; g0 += QG) {
+      if (first || !one_group) {
+        if (g0 > 0 || !first) load_q(g0, qv);
+#pragma unroll
+        for (int r = 0; r < QR; ++r) {
+          const int p = threadIdx.x + 512 * r, qr = p / VP, c = p - qr * VP;
+          if (p < QPIECES) *reinterpret_cast<u32x4_t*>(&qs[qr][8 * c]) = qv[r];
+        }
+        __syncthreads();   // Q rows of the group published
+      }
+      // ---- S^T: lane holds keys key0 + 16 kt + 4 lq + j of query 16 (g0 + u) + li ----
+      floatx4_t st[2][QG];
+#pragma unroll
+      for (int u = 0; u < QG; ++u) {
+        // Q fragments of tile u (B operand): query 16 (g0 + u) + li, dh 8 lq + 32 ds .. + 7
+        u32x4_t qf[DS];
+#pragma unroll
+        for (int ds = 0; ds < DS; ++ds)
+          qf[ds] = *reinterpret_cast<const u32x4_t*>(&qs[16 * u + li][8 * lq + 32 * ds]);
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt) {
+          st[kt][u] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int ds = 0; ds < DS; ++ds)
+            st[kt][u] = mfma16x16x32_bf16(kf[kt][ds], qf[ds], st[kt][u]);
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < QG; ++u) {
+        float mx = kNegInf;
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const bool ok = key0 + 16 * kt + 4 * lq + j < L;
+            const float v = ok ? st[kt][u][j] * sl2 : kNegInf;
+            st[kt][u][j] = v;
+            mx = fmaxf(mx, v);
+          }
+        mx = fmaxf(mx, __shfl_xor(mx, 16));
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        if (lq == 0) red_m[wave][16 * u + li] = mx;
+      }
+      __syncthreads();   // maxima (and the chunk's V rows) published
+      // ---- P = 2^(s - M) over the chunk; row sums; P to LDS in the transposed-read key order ----
+#pragma unroll
+      for (int u = 0; u < QG; ++u) {
+        float M = kNegInf;
+#pragma unroll
+        for (int w = 0; w < kPfxWaves; ++w) M = fmaxf(M, red_m[w][16 * u + li]);
+        float ls = 0.f;
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const float pv = M == kNegInf ? 0.f : __builtin_amdgcn_exp2f(st[kt][u][j] - M);
+            st[kt][u][j] = pv;
+            ls += pv;
+          }
+        ls += __shfl_xor(ls, 16);
+        ls += __shfl_xor(ls, 32);
+        if (lq == 0) red_l[wave][16 * u + li] = ls;
+        // key 32 wave + 16 kt + 4 lq + j sits at column 32 wave + 8 lq + 4 kt + j
+        u32x4_t pw;
+        pw[0] = pack_bf16x2(st[0][u][0], st[0][u][1]);
+        pw[1] = pack_bf16x2(st[0][u][2], st[0][u][3]);
+        pw[2] = pack_bf16x2(st[1][u][0], st[1][u][1]);
+        pw[3] = pack_bf16x2(st[1][u][2], st[1][u][3]);
+        *reinterpret_cast<u32x4_t*>(&ps[16 * u + li][32 * wave + 8 * lq]) = pw;
+      }
+      __syncthreads();   // P and the row sums are published
+      // ---- O^T += V^T P^T: item = wave + 8 it is (query tile item / DT, dh tile item % DT) ----
+#pragma unroll
+      for (int it = 0; it < ITEMS; ++it) {
+        const int item = wave + kPfxWaves * it;
+        const int u = item / DT, dt = item - u * DT;
+        if (item >= QG * DT || g0 + u >= MQ) continue;
+        floatx4_t o = floatx4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int t = 0; t < kAttnChunk / 32; ++t) {
+          // A: lane gets dh 16 dt + li of keys 32t + 4 lq + (0..3) and 32t + 16 + 4 lq + (0..3)
+          const S* v0 = &vs[32 * t + 4 * lq + (li >> 2)][16 * dt + 4 * (li & 3)];
+          const uint2 lo = lds_read_tr16(v0);
+          const uint2 hi = lds_read_tr16(v0 + 16 * VSTR);
+          u32x4_t vf;
+          vf[0] = lo.x;
+          vf[1] = lo.y;
+          vf[2] = hi.x;
+          vf[3] = hi.y;
+          const u32x4_t pf = *reinterpret_cast<const u32x4_t*>(&ps[16 * u + li][32 * t + 8 * lq]);
+          o = mfma16x16x32_bf16(vf, pf, o);
+        }
+        // lane holds O^T[dh 16 dt + 4 lq + j][query 16 (g0 + u) + li]
+        const int query = 16 * (g0 + u) + li;
+        if (query < T)
+          *reinterpret_cast<float4*>(a.part_o + base * DH + ((size_t)dt * T + query) * 16 +
+                                     4 * lq) = make_float4(o[0], o[1], o[2], o[3]);
+      }
+      if (wave == 0 && lane < 16 * QG) {
+        const int query = 16 * g0 + lane;
+        if (query < T) {
+          float M = kNegInf, l = 0.f;
+#pragma unroll
+          for (int w = 0; w < kPfxWaves; ++w) M = fmaxf(M, red_m[w][lane]);
+#pragma unroll
+          for (int w = 0; w < kPfxWaves; ++w) l += red_l[w][lane];
+          a.part_ml[(base + query) * 2 + 0] = M;
+          a.part_ml[(base + query) * 2 + 1] = l;
+        }
+      }
+    }
+    if (!more) break;
+    s = sn;
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int ds = 0; ds < DS; ++ds) kf[kt][ds] = kn[kt][ds];
+#pragma unroll
+    for (int i = 0; i < VL; ++i) vv[i] = vn[i];
+    __syncthreads();   // every wave is done with this chunk's V, P and row statistics
+  }
+}
+
+// fp32 prefix kernel: SC keys per round are staged in LDS (K row-major, V
+// transposed); the next round's global loads are in flight while the waves
+// compute the current one. Waves split the query tiles (16 queries each);
+// S^T = K Q^T and O^T += V^T P^T on v_mfma_f32_16x16x4_f32, online softmax.
+template <int DH, int QT, int SC>
+__global__ __launch_bounds__(256) void prefix_attn_f32_kernel(AttnArgs a) {
+  constexpr int DS = DH / 16;          // 16-byte steps along Dh per lane group
+  constexpr int DT = DH / 16;          // dh tiles of the output
+  constexpr int KT = SC / 16;          // key tiles per round
+  constexpr int PAD = 4;               // 16 bytes of padding per LDS row
+  constexpr int VEC_PER_KEY = DH / 4;
   constexpr int LOADS = SC * VEC_PER_KEY / 256;   // 16-byte loads per thread per tensor
   static_assert(LOADS * 256 == SC * VEC_PER_KEY, "round must divide over the threads");
   const int s = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const int T = a.T, H = a.H;
   const int L = min(max(a.kv_len[b], 0), a.Lmax);
-  const bool tree = s == 0;
-  int kbeg, kend;
-  if (tree) {
-    kbeg = 0;
-    kend = T;
-  } else {
-    kbeg = (s - 1) * kAttnChunk;
-    kend = min(L, s * kAttnChunk);
-    if (kbeg >= kend) return;
-  }
+  const int kbeg = s * kAttnChunk, kend = min(L, kbeg + kAttnChunk);
+  if (kbeg >= kend) return;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int li = lane & 15, lq = lane >> 4;
   const int MQ = (T + 15) / 16;
-  const float sl2 = a.scale * 1.4426950408889634f;
+  const float sl2 = a.scale * kLog2e;
 
-  const S* __restrict__ q = reinterpret_cast<const S*>(a.q);
-  const S* __restrict__ k_src;
-  const S* __restrict__ v_src;
-  size_t krow;   // elements between consecutive keys
-  if (tree) {
-    k_src = reinterpret_cast<const S*>(a.k_tree) + ((size_t)b * T * H + h) * DH;
-    v_src = reinterpret_cast<const S*>(a.v_tree) + ((size_t)b * T * H + h) * DH;
-    krow = (size_t)H * DH;
-  } else {
-    k_src = reinterpret_cast<const S*>(a.k_cache) + ((size_t)b * H + h) * a.Lmax * DH;
-    v_src = reinterpret_cast<const S*>(a.v_cache) + ((size_t)b * H + h) * a.Lmax * DH;
-    krow = DH;
-  }
+  const float* __restrict__ q = reinterpret_cast<const float*>(a.q);
+  const float* __restrict__ k_src =
+      reinterpret_cast<const float*>(a.k_cache) + ((size_t)b * H + h) * a.Lmax * DH;
+  const float* __restrict__ v_src =
+      reinterpret_cast<const float*>(a.v_cache) + ((size_t)b * H + h) * a.Lmax * DH;
 
-  // bf16: V row-major like K (row stride 288 / 160 bytes keeps the
-  // transposed reads conflict-free); fp32: V transposed.
-  constexpr int PADV = 32 / sizeof(S);
-  __shared__ S ks[SC][DH + PAD];
-  __shared__ S vt[BF ? SC : DH][BF ? DH + PADV : SC + PAD];
+  __shared__ float ks[SC][DH + PAD];
+  __shared__ float vt[DH][SC + PAD];
 
-  // Q fragments of my query tiles (B operand: lane = query, 16 B along Dh)
   u32x4_t qf[QT][DS];
   floatx4_t o[QT][DT];
   float m_run[QT], l_run[QT];
 #pragma unroll
   for (int u = 0; u < QT; ++u) {
-    const int qt = wave + 4 * u;
-    const int qi = min(16 * qt + li, T - 1);
-    const S* qp = q + (((size_t)b * T + qi) * H + h) * DH + PV * lq;
+    const int qi = min(16 * (wave + 4 * u) + li, T - 1);
+    const float* qp = q + (((size_t)b * T + qi) * H + h) * DH + 4 * lq;
 #pragma unroll
-    for (int ds = 0; ds < DS; ++ds) qf[u][ds] = load16(qp + 4 * PV * ds);
+    for (int ds = 0; ds < DS; ++ds) qf[u][ds] = load16(qp + 16 * ds);
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) o[u][dt] = floatx4_t{0.f, 0.f, 0.f, 0.f};
     m_run[u] = kNegInf;
@@ -106,7 +296,7 @@ __global__ __launch_bounds__(256) void tree_attn_kernel(AttnArgs a) {
     for (int i = 0; i < LOADS; ++i) {
       const int c = threadIdx.x + 256 * i;
       const int kk = c / VEC_PER_KEY, part = c - kk * VEC_PER_KEY;
-      const size_t off = (size_t)min(kb + kk, kend - 1) * krow + PV * part;
+      const size_t off = (size_t)min(kb + kk, kend - 1) * DH + 4 * part;
       kv[i] = load16(k_src + off);
       vv[i] = load16(v_src + off);
     }
@@ -115,18 +305,13 @@ __global__ __launch_bounds__(256) void tree_attn_kernel(AttnArgs a) {
 
   for (int kb = kbeg; kb < kend; kb += SC) {
     if (kb > kbeg) __syncthreads();   // previous round's readers are done
-    // ---- stage K and V^T ----
 #pragma unroll
     for (int i = 0; i < LOADS; ++i) {
       const int c = threadIdx.x + 256 * i;
       const int kk = c / VEC_PER_KEY, part = c - kk * VEC_PER_KEY;
-      *reinterpret_cast<u32x4_t*>(&ks[kk][PV * part]) = kv[i];
-      if constexpr (BF) {
-        *reinterpret_cast<u32x4_t*>(&vt[kk][PV * part]) = vv[i];
-      } else {
+      *reinterpret_cast<u32x4_t*>(&ks[kk][4 * part]) = kv[i];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) vt[PV * part + e][kk] = __uint_as_float(vv[i][e]);
-      }
+      for (int e = 0; e < 4; ++e) vt[4 * part + e][kk] = __uint_as_float(vv[i][e]);
     }
     __syncthreads();
     if (kb + SC < kend) load_round(kb + SC);   // next round in flight during compute
@@ -135,36 +320,26 @@ __global__ __launch_bounds__(256) void tree_attn_kernel(AttnArgs a) {
     for (int u = 0; u < QT; ++u) {
       const int qt = wave + 4 * u;
       if (qt >= MQ) break;
-      const int query = 16 * qt + li;
-      // ---- S^T = K Q^T over the round's key tiles ----
       floatx4_t st[KT];
 #pragma unroll
       for (int kt = 0; kt < KT; ++kt) {
         st[kt] = floatx4_t{0.f, 0.f, 0.f, 0.f};
-        const S* kp = &ks[16 * kt + li][PV * lq];
+        const float* kp = &ks[16 * kt + li][4 * lq];
 #pragma unroll
         for (int ds = 0; ds < DS; ++ds) {
-          const u32x4_t kf = *reinterpret_cast<const u32x4_t*>(kp + 4 * PV * ds);
-          if constexpr (BF) {
-            st[kt] = mfma16x16x32_bf16(kf, qf[u][ds], st[kt]);
-          } else {
+          const u32x4_t kf = *reinterpret_cast<const u32x4_t*>(kp + 16 * ds);
 #pragma unroll
-            for (int j = 0; j < 4; ++j)
-              st[kt] = mfma16x16x4_f32(__uint_as_float(kf[j]), __uint_as_float(qf[u][ds][j]),
-                                       st[kt]);
-          }
+          for (int j = 0; j < 4; ++j)
+            st[kt] = mfma16x16x4_f32(__uint_as_float(kf[j]), __uint_as_float(qf[u][ds][j]),
+                                     st[kt]);
         }
       }
-      // ---- scale, mask, online softmax (lane = query) ----
-      const uint8_t* mrow = a.mask + (size_t)min(query, T - 1) * T;
       float mx = kNegInf;
 #pragma unroll
       for (int kt = 0; kt < KT; ++kt)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const int key = kb + 16 * kt + 4 * lq + r;
-          bool ok = key < kend;
-          if (tree && ok && query < T) ok = mrow[key] != 0;
+          const bool ok = kb + 16 * kt + 4 * lq + r < kend;
           const float v = ok ? st[kt][r] * sl2 : kNegInf;
           st[kt][r] = v;
           mx = fmaxf(mx, v);
@@ -190,46 +365,19 @@ __global__ __launch_bounds__(256) void tree_attn_kernel(AttnArgs a) {
       for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
         for (int j = 0; j < 4; ++j) o[u][dt][j] *= alpha;
-      // ---- O^T += V^T P^T ----
-      if constexpr (BF) {
 #pragma unroll
-        for (int t = 0; t < KT / 2; ++t) {
-          u32x4_t pf;
-          pf[0] = pack_bf16x2(st[2 * t][0], st[2 * t][1]);
-          pf[1] = pack_bf16x2(st[2 * t][2], st[2 * t][3]);
-          pf[2] = pack_bf16x2(st[2 * t + 1][0], st[2 * t + 1][1]);
-          pf[3] = pack_bf16x2(st[2 * t + 1][2], st[2 * t + 1][3]);
-          // k slot j of this lane group is key 32t + 4lq + j (j < 4) or
-          // 32t + 16 + 4lq + j - 4: the S^T accumulator order
+      for (int kt = 0; kt < KT; ++kt)
 #pragma unroll
-          for (int dt = 0; dt < DT; ++dt) {
-            const S* v0 = &vt[32 * t + 4 * lq + (li >> 2)][16 * dt + 4 * (li & 3)];
-            u32x4_t vf;
-            const uint2 lo = lds_read_tr16(v0);
-            const uint2 hi = lds_read_tr16(v0 + 16 * (DH + PADV));
-            vf[0] = lo.x;
-            vf[1] = lo.y;
-            vf[2] = hi.x;
-            vf[3] = hi.y;
-            o[u][dt] = mfma16x16x32_bf16(vf, pf, o[u][dt]);
-          }
+        for (int dt = 0; dt < DT; ++dt) {
+          const float4 vr = *reinterpret_cast<const float4*>(&vt[16 * dt + li][16 * kt + 4 * lq]);
+          o[u][dt] = mfma16x16x4_f32(vr.x, st[kt][0], o[u][dt]);
+          o[u][dt] = mfma16x16x4_f32(vr.y, st[kt][1], o[u][dt]);
+          o[u][dt] = mfma16x16x4_f32(vr.z, st[kt][2], o[u][dt]);
+          o[u][dt] = mfma16x16x4_f32(vr.w, st[kt][3], o[u][dt]);
         }
-      } else {
-#pragma unroll
-        for (int kt = 0; kt < KT; ++kt)
-#pragma unroll
-          for (int dt = 0; dt < DT; ++dt) {
-            const float4 vr = *reinterpret_cast<const float4*>(&vt[16 * dt + li][16 * kt + 4 * lq]);
-            o[u][dt] = mfma16x16x4_f32(vr.x, st[kt][0], o[u][dt]);
-            o[u][dt] = mfma16x16x4_f32(vr.y, st[kt][1], o[u][dt]);
-            o[u][dt] = mfma16x16x4_f32(vr.z, st[kt][2], o[u][dt]);
-            o[u][dt] = mfma16x16x4_f32(vr.w, st[kt][3], o[u][dt]);
-          }
-      }
     }
   }
 
-  // ---- partial (m, l, O) per query ----
   const size_t base = (((size_t)b * H + h) * a.NS + s) * T;
 #pragma unroll
   for (int u = 0; u < QT; ++u) {
@@ -241,85 +389,182 @@ __global__ __launch_bounds__(256) void tree_attn_kernel(AttnArgs a) {
       a.part_ml[(base + query) * 2 + 0] = m_run[u];
       a.part_ml[(base + query) * 2 + 1] = l_run[u];
     }
-    float* op = a.part_o + (base + query) * DH;
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt)
-      *reinterpret_cast<float4*>(op + 16 * dt + 4 * lq) =
+      *reinterpret_cast<float4*>(a.part_o + base * DH + ((size_t)dt * T + query) * 16 + 4 * lq) =
           make_float4(o[u][dt][0], o[u][dt][1], o[u][dt][2], o[u][dt][3]);
   }
 }
 
-// Combine the splits of every (b, query, h): fixed order, tree split first.
-// Splits are read in batches of kMergeBatch with every load of a batch
-// issued before any is used (indices past the last split are clamped to it
-// and given zero weight), so a thread waits once per batch.
-constexpr int kMergeBatch = 16;
-template <class ET>
-__global__ void attn_merge_kernel(AttnArgs a) {
+// Merge, one wave per (b, query i, h), each lane holding DH / 64 consecutive
+// dh: the prefix splits in order (read in batches of kMergeBatch, every load
+// of a batch issued before any is used; indices past the last split are
+// clamped and given zero weight), then the tree keys j the mask allows for
+// i, in increasing j (key and value rows of up to kTreeBatch keys loaded
+// before use), all folded into one running (max, sum, weighted value).
+constexpr int kMergeBatch = 8;
+constexpr int kTreeBatch = 8;
+template <class ET, int DH>
+__global__ __launch_bounds__(64) void attn_merge_kernel(AttnArgs a) {
   using S = typename ET::storage;
-  const int i = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
-  const int x = threadIdx.x;   // one dh element per thread
-  const int T = a.T, H = a.H, DH = a.Dh;
+  constexpr int E = DH / 64;
+  const int i = blockIdx.x, h = blockIdx.y, b = blockIdx.z, lane = threadIdx.x;
+  const int T = a.T, H = a.H;
   const int L = min(max(a.kv_len[b], 0), a.Lmax);
-  const int ns = 1 + (L + kAttnChunk - 1) / kAttnChunk;
-  const size_t base = ((size_t)b * H + h) * a.NS * T + i;
-  float M = kNegInf, l = 0.f, acc = 0.f;
+  const int ns = (L + kAttnChunk - 1) / kAttnChunk;
+  const float sl2 = a.scale * kLog2e;
+  const size_t hs = ((size_t)b * H + h) * a.NS;   // split 0 of (b, h)
+  // dh E lane + e of query i inside a split's [DT][T][16] block
+  const size_t oin = ((size_t)(E * lane / 16) * T + i) * 16 + (E * lane) % 16;
+  const S* __restrict__ qp = reinterpret_cast<const S*>(a.q) + (((size_t)b * T + i) * H + h) * DH;
+  float qv[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) qv[e] = ET::load1(qp + E * lane + e);
+
+  float M = kNegInf, l = 0.f, acc[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) acc[e] = 0.f;
   for (int s0 = 0; s0 < ns; s0 += kMergeBatch) {
-    float ms[kMergeBatch], lsv[kMergeBatch], os[kMergeBatch];
+    float ms[kMergeBatch], lsv[kMergeBatch], os[kMergeBatch][E];
 #pragma unroll
     for (int j = 0; j < kMergeBatch; ++j) {
-      const size_t r = base + (size_t)min(s0 + j, ns - 1) * T;
-      ms[j] = a.part_ml[r * 2];
-      lsv[j] = a.part_ml[r * 2 + 1];
-      os[j] = a.part_o[r * DH + x];
+      const size_t sp = hs + min(s0 + j, ns - 1);
+      ms[j] = a.part_ml[(sp * T + i) * 2];
+      lsv[j] = a.part_ml[(sp * T + i) * 2 + 1];
+#pragma unroll
+      for (int e = 0; e < E; ++e) os[j][e] = a.part_o[sp * T * DH + oin + e];
     }
     float Mn = M;
 #pragma unroll
-    for (int j = 0; j < kMergeBatch; ++j) Mn = fmaxf(Mn, ms[j]);
+    for (int j = 0; j < kMergeBatch; ++j)
+      if (s0 + j < ns) Mn = fmaxf(Mn, ms[j]);
     const float c = M == kNegInf ? 0.f : __builtin_amdgcn_exp2f(M - Mn);
     l *= c;
-    acc *= c;
+#pragma unroll
+    for (int e = 0; e < E; ++e) acc[e] *= c;
 #pragma unroll
     for (int j = 0; j < kMergeBatch; ++j) {
       const bool live = s0 + j < ns && ms[j] != kNegInf;
       const float w = live ? __builtin_amdgcn_exp2f(ms[j] - Mn) : 0.f;
       l += w * lsv[j];
-      acc += w * os[j];
+#pragma unroll
+      for (int e = 0; e < E; ++e) acc[e] += w * os[j][e];
     }
     M = Mn;
   }
-  const float ov = acc / l;
-  const size_t out = (((size_t)b * T + i) * H + h) * DH + x;
-  if (a.out) a.out[out] = ov;
-  if (a.out_elem) reinterpret_cast<S*>(a.out_elem)[out] = ET::from_float(ov);
+
+  // the tree keys of query i
+  const uint8_t* __restrict__ mrow = a.mask + (size_t)i * T;
+  const S* __restrict__ ktr = reinterpret_cast<const S*>(a.k_tree) + ((size_t)b * T * H + h) * DH;
+  const S* __restrict__ vtr = reinterpret_cast<const S*>(a.v_tree) + ((size_t)b * T * H + h) * DH;
+  const size_t krow = (size_t)H * DH;
+  for (int j0 = 0; j0 < T; j0 += 64) {
+    uint64_t bits = __ballot(j0 + lane < T && mrow[j0 + lane] != 0);
+    while (bits) {
+      int js[kTreeBatch];
+      int nb = 0;
+#pragma unroll
+      for (int u = 0; u < kTreeBatch; ++u) {
+        js[u] = bits ? j0 + __ffsll((unsigned long long)bits) - 1 : js[0];
+        if (bits) {
+          bits &= bits - 1;
+          nb = u + 1;
+        }
+      }
+      float kx[kTreeBatch][E], vx[kTreeBatch][E];
+#pragma unroll
+      for (int u = 0; u < kTreeBatch; ++u)
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+          kx[u][e] = ET::load1(ktr + js[u] * krow + E * lane + e);
+          vx[u][e] = ET::load1(vtr + js[u] * krow + E * lane + e);
+        }
+      for (int u = 0; u < nb; ++u) {
+        float d = 0.f;
+#pragma unroll
+        for (int e = 0; e < E; ++e) d += qv[e] * kx[u][e];
+        const float sc = wave_sum(d) * sl2;
+        const float Mn = fmaxf(M, sc);
+        const float c = M == kNegInf ? 0.f : __builtin_amdgcn_exp2f(M - Mn);
+        const float w = __builtin_amdgcn_exp2f(sc - Mn);
+        l = l * c + w;
+#pragma unroll
+        for (int e = 0; e < E; ++e) acc[e] = acc[e] * c + w * vx[u][e];
+        M = Mn;
+      }
+    }
+  }
+
+  const float inv = 1.f / l;
+  const size_t out = (((size_t)b * T + i) * H + h) * DH + E * lane;
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const float ov = acc[e] * inv;
+    if (a.out) a.out[out + e] = ov;
+    if (a.out_elem) reinterpret_cast<S*>(a.out_elem)[out + e] = ET::from_float(ov);
+  }
 }
 
-template <class ET, int DH>
-hipError_t launch_dh(const AttnArgs& a, hipStream_t st) {
-  // fp32 with 128-wide heads stages 64 keys per round to keep LDS below 68 KB
-  constexpr int SC = (sizeof(typename ET::storage) == 4 && DH == 128) ? 64 : 128;
+// Compute units of the current device (cached per device).
+int device_cus() {
+  static int cus[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cus[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 1)
+      n = 256;
+    cus[dev] = n;
+  }
+  return cus[dev];
+}
+
+template <int DH>
+hipError_t launch_bf16(const AttnArgs& a, hipStream_t st) {
+  const int MQ = (a.T + 15) / 16;
+  // one workgroup per compute unit (its LDS use allows no second): chunks
+  // per (b, h) in flight = CUs / (B H), each workgroup looping over the rest
+  int G = device_cus() / (a.B * a.H);
+  G = G < 1 ? 1 : (G > a.NS ? a.NS : G);
+  dim3 grid(G, a.H, a.B), block(64 * kPfxWaves);
+  switch (MQ < 4 ? MQ : 4) {
+    case 1: hipLaunchKernelGGL((prefix_attn_bf16_kernel<DH, 1>), grid, block, 0, st, a); break;
+    case 2: hipLaunchKernelGGL((prefix_attn_bf16_kernel<DH, 2>), grid, block, 0, st, a); break;
+    case 3: hipLaunchKernelGGL((prefix_attn_bf16_kernel<DH, 3>), grid, block, 0, st, a); break;
+    default: hipLaunchKernelGGL((prefix_attn_bf16_kernel<DH, 4>), grid, block, 0, st, a); break;
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((attn_merge_kernel<BF16, DH>), dim3(a.T, a.H, a.B), dim3(64), 0, st, a);
+  return hipGetLastError();
+}
+
+template <int DH>
+hipError_t launch_f32(const AttnArgs& a, hipStream_t st) {
+  // 128-wide heads stage 64 keys per round to keep LDS below 68 KB
+  constexpr int SC = DH == 128 ? 64 : 128;
   const int MQ = (a.T + 15) / 16;
   const int QT = (MQ + 3) / 4;
   dim3 grid(a.NS, a.H, a.B), block(256);
   switch (QT) {
-    case 1: hipLaunchKernelGGL((tree_attn_kernel<ET, DH, 1, SC>), grid, block, 0, st, a); break;
-    case 2: hipLaunchKernelGGL((tree_attn_kernel<ET, DH, 2, SC>), grid, block, 0, st, a); break;
-    case 3: hipLaunchKernelGGL((tree_attn_kernel<ET, DH, 3, SC>), grid, block, 0, st, a); break;
-    default: hipLaunchKernelGGL((tree_attn_kernel<ET, DH, 4, SC>), grid, block, 0, st, a); break;
+    case 1: hipLaunchKernelGGL((prefix_attn_f32_kernel<DH, 1, SC>), grid, block, 0, st, a); break;
+    case 2: hipLaunchKernelGGL((prefix_attn_f32_kernel<DH, 2, SC>), grid, block, 0, st, a); break;
+    case 3: hipLaunchKernelGGL((prefix_attn_f32_kernel<DH, 3, SC>), grid, block, 0, st, a); break;
+    default: hipLaunchKernelGGL((prefix_attn_f32_kernel<DH, 4, SC>), grid, block, 0, st, a); break;
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(attn_merge_kernel<ET>, dim3(a.T, a.H, a.B), dim3(DH), 0, st, a);
+  hipLaunchKernelGGL((attn_merge_kernel<F32, DH>), dim3(a.T, a.H, a.B), dim3(64), 0, st, a);
   return hipGetLastError();
 }
 
 }  // namespace
 
-int attn_splits(int Lmax) { return 1 + (Lmax + kAttnChunk - 1) / kAttnChunk; }
+int attn_splits(int Lmax) { return Lmax > 0 ? (Lmax + kAttnChunk - 1) / kAttnChunk : 1; }
 
 hipError_t launch_tree_attention(const AttnArgs& a, hipStream_t st) {
-  if (a.f32) return a.Dh == 64 ? launch_dh<F32, 64>(a, st) : launch_dh<F32, 128>(a, st);
-  return a.Dh == 64 ? launch_dh<BF16, 64>(a, st) : launch_dh<BF16, 128>(a, st);
+  if (a.f32) return a.Dh == 64 ? launch_f32<64>(a, st) : launch_f32<128>(a, st);
+  return a.Dh == 64 ? launch_bf16<64>(a, st) : launch_bf16<128>(a, st);
 }
 
 }  // namespace medusa

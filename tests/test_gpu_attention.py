@@ -59,6 +59,10 @@ CASES = [
     ((2, 2), 2, 3, 64, [255, 257], "bf16"),               # Dh 64, around a chunk boundary
     ((16, 14), 1, 1, 128, [100], "bf16"),                  # 241 rows: 16 query tiles
     ((2, 2, 2), 2, 2, 128, [300, 5], "f32"),
+    # B H = 256: one chunk per (b, h) in flight on a 256-CU device, so each
+    # workgroup loops over its chunks with the next one prefetched
+    ((3, 2), 4, 64, 64, [1000, 513, 256, 3], "bf16"),
+    ((3, 2, 2), 2, 128, 128, [1100, 700], "bf16"),
 ]
 
 
