@@ -133,6 +133,9 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--reset-kv-len", action="store_true",
+                    help="advance kv_len in place and restore it with a fill kernel before "
+                         "every step (default: the advanced lengths go to a separate buffer)")
     ap.add_argument("--graph", action="store_true",
                     help="time replays of one recorded step graph instead of eager launches "
                          "(measured slower on this stack: per-node overhead)")
@@ -165,9 +168,15 @@ def main():
 
     def step():
         # stream=None: the calls go to torch's current stream (the capture
-        # stream while a graph is being recorded)
-        st.reset_kv_len()
-        st.run_step()
+        # stream while a graph is being recorded). By default the commit
+        # writes the advanced prefix lengths to a buffer of their own, so
+        # every step runs over the same prefix; --reset-kv-len instead
+        # advances kv_len in place and restores it before each step.
+        if args.reset_kv_len:
+            st.reset_kv_len()
+            st.run_step()
+        else:
+            st.run_step(keep_kv_len=True)
 
     for _ in range(args.warmup):
         step()
@@ -237,8 +246,10 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic (seeded Gaussian weights and KV of Vicuna-7B shapes)",
-        "timing": ("replays of one recorded graph (prefix-length reset + medusa_step)"
-                   if graph is not None else "eager launches (prefix-length reset + medusa_step)"),
+        "timing": (("replays of one recorded graph" if graph is not None else "eager launches")
+                   + (" (prefix-length reset + medusa_step)" if args.reset_kv_len else
+                      " (medusa_step; advanced prefix lengths written to a separate buffer, "
+                      "so every step runs over the same prefix)")),
         "config": {"workload": w.name, "batch": w.B, "d": w.d, "V": w.V, "heads": w.K,
                    "tree": "top-(3,2,2,1,1)", "tree_nodes": T - 1, "prefix_kv": L_total,
                    "attn": f"{w.H}x{w.Dh}", "accept": f"typical eps={w.eps} delta={w.delta} "

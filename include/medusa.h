@@ -332,7 +332,7 @@ typedef struct {
   float rope_theta;
   void* k_cache;                   /* [B][H][Lmax][Dh] elem (in-out) */
   void* v_cache;
-  int32_t* kv_len;                 /* [B] (in-out) */
+  int32_t* kv_len;                 /* [B] (in-out; only read when kv_len_out_or_null is set) */
   /* posterior */
   int mode;
   float temperature, eps, delta;
@@ -359,6 +359,12 @@ typedef struct {
   int32_t* out_tokens;             /* [B][K+1] */
   int32_t* next_root;              /* [B] */
   float* h_next;                   /* [B][d] */
+  /* [B] or NULL: where the commit writes the advanced prefix lengths (kv_len
+   * + a + 1, or -1). NULL advances kv_len in place, as medusa_commit does;
+   * a separate buffer leaves kv_len unchanged, so that the same step can be
+   * repeated over the same prefix (the appended cache rows are rewritten at
+   * the same positions) without restoring kv_len in between. */
+  int32_t* kv_len_out_or_null;
 } medusa_step_args;
 
 int medusa_step(const medusa_shape* shape, const medusa_step_args* args, void* workspace,

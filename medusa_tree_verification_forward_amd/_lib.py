@@ -73,7 +73,7 @@ class StepArgs(ctypes.Structure):
         ("k_tree", _P), ("v_tree", _P), ("y", _P), ("row_stats", _P), ("row_argmax", _P),
         ("child_logit", _P), ("verify_logits_or_null", _P), ("accept_len", _P),
         ("best_path", _P), ("last_node", _P), ("out_tokens", _P), ("next_root", _P),
-        ("h_next", _P),
+        ("h_next", _P), ("kv_len_out_or_null", _P),
     ]
 
 _P = ctypes.c_void_p

@@ -675,9 +675,13 @@ int medusa_evaluate_posterior(const medusa_shape* shape, int mode, float tempera
   return ok();
 }
 
-int medusa_commit(const medusa_shape* shape, const int32_t* last_node, const int32_t* parent,
-                  const void* k_tree, const void* v_tree, const float* y, void* k_cache,
-                  void* v_cache, int32_t* kv_len, float* h_next, void* stream) {
+}  // extern "C"
+
+namespace {
+int commit_impl(const medusa_shape* shape, const int32_t* last_node, const int32_t* parent,
+                const void* k_tree, const void* v_tree, const float* y, void* k_cache,
+                void* v_cache, int32_t* kv_len, int32_t* kv_len_out, float* h_next,
+                void* stream) {
   int rc = check_shape(shape);
   if (rc) return rc;
   REQUIRE_PTR(last_node);
@@ -706,10 +710,21 @@ int medusa_commit(const medusa_shape* shape, const int32_t* last_node, const int
   a.k_cache = k_cache;
   a.v_cache = v_cache;
   a.kv_len = kv_len;
+  a.kv_len_out = kv_len_out;
   a.h_next = h_next;
   hipError_t e = launch_commit(a, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "commit launch");
   return ok();
+}
+}  // namespace
+
+extern "C" {
+
+int medusa_commit(const medusa_shape* shape, const int32_t* last_node, const int32_t* parent,
+                  const void* k_tree, const void* v_tree, const float* y, void* k_cache,
+                  void* v_cache, int32_t* kv_len, float* h_next, void* stream) {
+  return commit_impl(shape, last_node, parent, k_tree, v_tree, y, k_cache, v_cache, kv_len,
+                     nullptr, h_next, stream);
 }
 
 int medusa_step(const medusa_shape* shape, const medusa_step_args* x, void* workspace,
@@ -773,8 +788,9 @@ int medusa_step(const medusa_shape* shape, const medusa_step_args* x, void* work
                                    x->best_path, x->last_node, x->out_tokens, x->next_root,
                                    workspace, workspace_bytes, stream);
     if (rc) return rc;
-    return medusa_commit(shape, x->last_node, x->parent, x->k_tree, x->v_tree, x->y,
-                         x->k_cache, x->v_cache, x->kv_len, x->h_next, stream);
+    return commit_impl(shape, x->last_node, x->parent, x->k_tree, x->v_tree, x->y,
+                       x->k_cache, x->v_cache, x->kv_len, x->kv_len_out_or_null, x->h_next,
+                       stream);
   }
   REQUIRE_PTR(x->accept_len);
   REQUIRE_PTR(x->best_path);
@@ -819,6 +835,7 @@ int medusa_step(const medusa_shape* shape, const medusa_step_args* x, void* work
   c.k_cache = x->k_cache;
   c.v_cache = x->v_cache;
   c.kv_len = x->kv_len;
+  c.kv_len_out = x->kv_len_out_or_null;
   c.h_next = x->h_next;
   a.row_stats = x->row_stats;
   a.row_argmax = x->row_argmax;

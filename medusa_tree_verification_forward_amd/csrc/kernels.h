@@ -184,6 +184,7 @@ struct CommitArgs {
   void* k_cache;
   void* v_cache;
   int32_t* kv_len;
+  int32_t* kv_len_out;         // advanced lengths go here; null: kv_len in place
   float* h_next;
 };
 hipError_t launch_commit(const CommitArgs& a, hipStream_t st);

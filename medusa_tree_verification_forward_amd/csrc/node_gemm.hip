@@ -28,7 +28,9 @@
 // W_qkv is packed with the rows of every head reordered so that each
 // 16-column tile holds 8 whole rotation pairs (columns j and j+8 of the tile
 // are rows i and i+Dh/2 of the head, i = 8*(tile in head) + j).
-// The epilogue runs in the last of the KS workgroups of a group to finish
+// With KS = 1 the epilogue runs on the accumulators themselves (the rotation
+// partner of a lane's column is in lane li ^ 8). Otherwise it runs in the last
+// of the KS workgroups of a group to finish
 // (found with a device-scope counter that it leaves at zero for the next
 // launch; the partials travel through agent-coherent stores and loads), or
 // in a kernel of its own.
@@ -286,6 +288,48 @@ __global__ __launch_bounds__(64 * WV, (WV == 4 && D <= 8) ? 4 : 2) void node_gem
       chunk(c, sA0, sA1, ra1, guarded, even);
   }
 
+  if constexpr (EPI == EPI_QKV || EPI == EPI_OPROJ) {
+    if (KS == 1) {
+      // One slice: finish straight from the accumulators (lane: column col,
+      // rows m0 + 16 mt + 4 lq + j), the row data loaded before any store.
+      int rv[MT][4];
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int r = min(m0 + 16 * mt + 4 * lq + j, p.M - 1);
+          rv[mt][j] = EPI == EPI_QKV ? p.pos[r] : min(max(p.tokens[r], 0), p.a_nrows - 1);
+        }
+      if constexpr (EPI == EPI_QKV) {
+        // the rotation partner of packed column col is col + 8, held by lane li + 8
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const float other = __shfl_xor(acc[mt][j], 8);
+            const int r = m0 + 16 * mt + 4 * lq + j;
+            if (li < 8 && r < p.M && col < p.N)
+              qkv_finish<ET>(p, r, col, rv[mt][j], acc[mt][j], other);
+          }
+      } else {
+        const int cc = min(col, p.N - 1);
+        float x[MT][4];
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            x[mt][j] = ET::load1(reinterpret_cast<const St*>(p.E) + (size_t)rv[mt][j] * p.N + cc);
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const int r = m0 + 16 * mt + 4 * lq + j;
+            if (r < p.M && col < p.N) oproj_store<ET>(p, r, col, x[mt][j] + acc[mt][j]);
+          }
+      }
+      return;
+    }
+  }
   if constexpr (EPI != EPI_LM) {
     // slice ks of the partials: part[g][ks][r][c]
     float* part = p.part + (size_t)(g * KS + ks) * p.M * GC + 16 * wave + li;
@@ -683,7 +727,7 @@ hipError_t launch_split(GemmParams p, hipStream_t st) {
   p.fused = fused_epilogue();
   p.kmajor = packed_kmajor();
   hipError_t e = p.f32 ? launch_main<F32, EPI>(p, KS, st) : launch_main<BF16, EPI>(p, KS, st);
-  if (e != hipSuccess || p.fused) return e;
+  if (e != hipSuccess || p.fused || KS == 1) return e;
   if (EPI == EPI_QKV) {
     dim3 grid((p.N / 2 + 255) / 256, p.M);
     if (p.f32)

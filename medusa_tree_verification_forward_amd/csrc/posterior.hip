@@ -368,7 +368,7 @@ __device__ void commit_block(const CommitArgs& a, int b, int last_in) {
   float4* hn = reinterpret_cast<float4*>(a.h_next + (size_t)b * a.d);
   for (int e = threadIdx.x; e < a.d / 4; e += blockDim.x) hn[e] = y[e];
   __syncthreads();
-  if (threadIdx.x == 0) a.kv_len[b] = room ? L + d + 1 : -1;
+  if (threadIdx.x == 0) (a.kv_len_out ? a.kv_len_out : a.kv_len)[b] = room ? L + d + 1 : -1;
 }
 
 template <class ET>

@@ -397,11 +397,13 @@ __global__ __launch_bounds__(256) void prefix_attn_f32_kernel(AttnArgs a) {
 }
 
 // Merge, one wave per (b, query i, h), each lane holding DH / 64 consecutive
-// dh: the prefix splits in order (read in batches of kMergeBatch, every load
-// of a batch issued before any is used; indices past the last split are
-// clamped and given zero weight), then the tree keys j the mask allows for
-// i, in increasing j (key and value rows of up to kTreeBatch keys loaded
-// before use), all folded into one running (max, sum, weighted value).
+// dh: the prefix splits in order, then the tree keys j the mask allows for
+// i, in increasing j, all folded into one running (max, sum, weighted
+// value). Loads go out in two waves of requests: the query row, the first
+// kMergeBatch splits and the first 64 mask bytes together, then the key and
+// value rows of the first kTreeBatch tree keys; further batches (long
+// prefixes, wide trees) follow the same pattern. Split indices past the last
+// are clamped and given zero weight.
 constexpr int kMergeBatch = 8;
 constexpr int kTreeBatch = 8;
 template <class ET, int DH>
@@ -417,23 +419,58 @@ __global__ __launch_bounds__(64) void attn_merge_kernel(AttnArgs a) {
   // dh E lane + e of query i inside a split's [DT][T][16] block
   const size_t oin = ((size_t)(E * lane / 16) * T + i) * 16 + (E * lane) % 16;
   const S* __restrict__ qp = reinterpret_cast<const S*>(a.q) + (((size_t)b * T + i) * H + h) * DH;
-  float qv[E];
-#pragma unroll
-  for (int e = 0; e < E; ++e) qv[e] = ET::load1(qp + E * lane + e);
+  const uint8_t* __restrict__ mrow = a.mask + (size_t)i * T;
+  const S* __restrict__ ktr = reinterpret_cast<const S*>(a.k_tree) + ((size_t)b * T * H + h) * DH;
+  const S* __restrict__ vtr = reinterpret_cast<const S*>(a.v_tree) + ((size_t)b * T * H + h) * DH;
+  const size_t krow = (size_t)H * DH;
 
-  float M = kNegInf, l = 0.f, acc[E];
-#pragma unroll
-  for (int e = 0; e < E; ++e) acc[e] = 0.f;
-  for (int s0 = 0; s0 < ns; s0 += kMergeBatch) {
-    float ms[kMergeBatch], lsv[kMergeBatch], os[kMergeBatch][E];
+  float ms[kMergeBatch], lsv[kMergeBatch], os[kMergeBatch][E];
+  auto load_splits = [&](int s0) {
 #pragma unroll
     for (int j = 0; j < kMergeBatch; ++j) {
-      const size_t sp = hs + min(s0 + j, ns - 1);
+      const size_t sp = hs + min(s0 + j, max(ns - 1, 0));
       ms[j] = a.part_ml[(sp * T + i) * 2];
       lsv[j] = a.part_ml[(sp * T + i) * 2 + 1];
 #pragma unroll
       for (int e = 0; e < E; ++e) os[j][e] = a.part_o[sp * T * DH + oin + e];
     }
+  };
+  int js[kTreeBatch];
+  float kx[kTreeBatch][E], vx[kTreeBatch][E];
+  // the next (up to) kTreeBatch keys of window j0 out of `bits`, rows loaded
+  auto take_tree = [&](int j0, uint64_t& bits) {
+    int nb = 0;
+#pragma unroll
+    for (int u = 0; u < kTreeBatch; ++u) {
+      js[u] = bits ? j0 + __ffsll((unsigned long long)bits) - 1 : js[0];
+      if (bits) {
+        bits &= bits - 1;
+        nb = u + 1;
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kTreeBatch; ++u)
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        kx[u][e] = ET::load1(ktr + js[u] * krow + E * lane + e);
+        vx[u][e] = ET::load1(vtr + js[u] * krow + E * lane + e);
+      }
+    return nb;
+  };
+
+  float qv[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) qv[e] = ET::load1(qp + E * lane + e);
+  const bool allow0 = lane < T && mrow[lane] != 0;
+  if (ns > 0) load_splits(0);
+  uint64_t bits = __ballot(allow0);
+  int nb = bits ? take_tree(0, bits) : 0;
+
+  float M = kNegInf, l = 0.f, acc[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) acc[e] = 0.f;
+  for (int s0 = 0; s0 < ns; s0 += kMergeBatch) {
+    if (s0 > 0) load_splits(s0);
     float Mn = M;
 #pragma unroll
     for (int j = 0; j < kMergeBatch; ++j)
@@ -454,45 +491,27 @@ __global__ __launch_bounds__(64) void attn_merge_kernel(AttnArgs a) {
   }
 
   // the tree keys of query i
-  const uint8_t* __restrict__ mrow = a.mask + (size_t)i * T;
-  const S* __restrict__ ktr = reinterpret_cast<const S*>(a.k_tree) + ((size_t)b * T * H + h) * DH;
-  const S* __restrict__ vtr = reinterpret_cast<const S*>(a.v_tree) + ((size_t)b * T * H + h) * DH;
-  const size_t krow = (size_t)H * DH;
-  for (int j0 = 0; j0 < T; j0 += 64) {
-    uint64_t bits = __ballot(j0 + lane < T && mrow[j0 + lane] != 0);
-    while (bits) {
-      int js[kTreeBatch];
-      int nb = 0;
+  for (int j0 = 0;;) {
+    for (int u = 0; u < nb; ++u) {
+      float d = 0.f;
 #pragma unroll
-      for (int u = 0; u < kTreeBatch; ++u) {
-        js[u] = bits ? j0 + __ffsll((unsigned long long)bits) - 1 : js[0];
-        if (bits) {
-          bits &= bits - 1;
-          nb = u + 1;
-        }
-      }
-      float kx[kTreeBatch][E], vx[kTreeBatch][E];
+      for (int e = 0; e < E; ++e) d += qv[e] * kx[u][e];
+      const float sc = wave_sum(d) * sl2;
+      const float Mn = fmaxf(M, sc);
+      const float c = M == kNegInf ? 0.f : __builtin_amdgcn_exp2f(M - Mn);
+      const float w = __builtin_amdgcn_exp2f(sc - Mn);
+      l = l * c + w;
 #pragma unroll
-      for (int u = 0; u < kTreeBatch; ++u)
-#pragma unroll
-        for (int e = 0; e < E; ++e) {
-          kx[u][e] = ET::load1(ktr + js[u] * krow + E * lane + e);
-          vx[u][e] = ET::load1(vtr + js[u] * krow + E * lane + e);
-        }
-      for (int u = 0; u < nb; ++u) {
-        float d = 0.f;
-#pragma unroll
-        for (int e = 0; e < E; ++e) d += qv[e] * kx[u][e];
-        const float sc = wave_sum(d) * sl2;
-        const float Mn = fmaxf(M, sc);
-        const float c = M == kNegInf ? 0.f : __builtin_amdgcn_exp2f(M - Mn);
-        const float w = __builtin_amdgcn_exp2f(sc - Mn);
-        l = l * c + w;
-#pragma unroll
-        for (int e = 0; e < E; ++e) acc[e] = acc[e] * c + w * vx[u][e];
-        M = Mn;
-      }
+      for (int e = 0; e < E; ++e) acc[e] = acc[e] * c + w * vx[u][e];
+      M = Mn;
     }
+    while (!bits) {
+      j0 += 64;
+      if (j0 >= T) break;
+      bits = __ballot(j0 + lane < T && mrow[j0 + lane] != 0);
+    }
+    if (!bits) break;
+    nb = take_tree(j0, bits);
   }
 
   const float inv = 1.f / l;

@@ -156,10 +156,14 @@ class VerifyStep:
         else:
             self.inp["kv_len"].copy_(self.kv_len0)
 
-    def step_args(self):
-        """medusa_step arguments over this object's buffers (built once)."""
-        if getattr(self, "_args", None) is not None:
-            return self._args
+    def step_args(self, keep_kv_len: bool = False):
+        """medusa_step arguments over this object's buffers (built once per
+        variant). keep_kv_len: the commit writes the advanced prefix lengths
+        to a buffer of their own (self.kv_len_next) and leaves kv_len as it
+        is, so that the step can be repeated over the same prefix."""
+        cached = getattr(self, "_args_keep" if keep_kv_len else "_args", None)
+        if cached is not None:
+            return cached
         o, i, w = self.out, self.inp, self.packed
         p = L._ptr
         exact = self.mode == "exact"
@@ -190,12 +194,19 @@ class VerifyStep:
                                                   p(o["last_node"]))
         a.out_tokens, a.next_root, a.h_next = (p(o["out_tokens"]), p(o["next_root"]),
                                                p(o["h_next"]))
-        self._args = a
+        if keep_kv_len:
+            import torch
+            self.kv_len_next = torch.empty_like(i["kv_len"])
+            a.kv_len_out_or_null = p(self.kv_len_next)
+            self._args_keep = a
+        else:
+            self._args = a
         return a
 
-    def run_step(self, stream=None):
-        """The whole step as one composite call (medusa_step)."""
-        L.step(self.shape, self.step_args(), self.ws, stream=stream)
+    def run_step(self, stream=None, keep_kv_len: bool = False):
+        """The whole step as one composite call (medusa_step); see step_args
+        for keep_kv_len."""
+        L.step(self.shape, self.step_args(keep_kv_len), self.ws, stream=stream)
 
     def run(self, stream=None, commit: bool = True):
         """The whole step: heads, tree, verify forward, posterior, commit."""

@@ -42,22 +42,30 @@ def oracle_for(w):
     return _ORACLE[w]
 
 
-def gpu_step(w, inp, want_logits=True, composite=False):
-    """One step on the GPU: the five calls, or the composite medusa_step."""
+def gpu_step(w, inp, want_logits=True, composite=False, keep_kv_len=False, repeat=1):
+    """One step on the GPU: the five calls, or the composite medusa_step.
+    keep_kv_len (composite only): the advanced prefix lengths go to a buffer
+    of their own and kv_len must come back unchanged (returned as
+    "kv_len_after"); repeat: the step runs that many times in a row (each
+    over the same prefix when keep_kv_len is set)."""
     import torch
-    from medusa_tree_verification_forward_amd.step import VerifyStep
+    from medusa_tree_verification_forward_amd.step import VerifyStep, to_host
     st = VerifyStep(inp, H=w.H, Dh=w.Dh, s_max=w.s_max, mode=w.mode, tau=w.tau, eps=w.eps,
                     delta=w.delta, theta=w.rope_theta, want_logits=want_logits)
-    if composite:
-        st.run_step()
-    else:
-        st.run()
+    for _ in range(repeat):
+        if composite:
+            st.run_step(keep_kv_len=keep_kv_len)
+        else:
+            st.run()
     torch.cuda.synchronize()
     res = st.results()
-    from medusa_tree_verification_forward_amd.step import to_host
     res["k_cache_next"] = to_host(st.inp["k_cache"])
     res["v_cache_next"] = to_host(st.inp["v_cache"])
-    res["kv_len_next"] = to_host(st.inp["kv_len"])
+    if keep_kv_len:
+        res["kv_len_next"] = to_host(st.kv_len_next)
+        res["kv_len_after"] = to_host(st.inp["kv_len"])
+    else:
+        res["kv_len_next"] = to_host(st.inp["kv_len"])
     return res
 
 

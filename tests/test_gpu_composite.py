@@ -30,6 +30,25 @@ def test_composite_matches_separate_calls(w):
         assert np.array_equal(a[k], b[k], equal_nan=True), k
 
 
+@pytest.mark.parametrize("w", CASES, ids=lambda w: f"{w.name}-d{w.d}-V{w.V}-B{w.B}-{w.mode}")
+def test_composite_separate_prefix_lengths(w):
+    """With kv_len_out_or_null set, kv_len is left unchanged, the advanced
+    lengths land in the separate buffer, and every other output equals the
+    in-place call's; a second step then runs over the same prefix and gives
+    the same outputs again."""
+    require_gpu()
+    inp = parity.inputs_for(w)
+    a = parity.gpu_step(w, inp, composite=True)
+    b = parity.gpu_step(w, inp, composite=True, keep_kv_len=True)
+    c = parity.gpu_step(w, inp, composite=True, keep_kv_len=True, repeat=2)
+    assert np.array_equal(b.pop("kv_len_after"), np.asarray(inp["kv_len"]))
+    assert np.array_equal(c.pop("kv_len_after"), np.asarray(inp["kv_len"]))
+    assert set(a) == set(b) == set(c)
+    for k in sorted(a):
+        assert np.array_equal(a[k], b[k], equal_nan=True), k
+        assert np.array_equal(a[k], c[k], equal_nan=True), k
+
+
 def test_composite_full_size_7b():
     """The throughput configuration, through the composite call, against the
     oracle."""
