@@ -755,7 +755,7 @@ int medusa_step(const medusa_shape* shape, const medusa_step_args* x, void* work
   rc = check_workspace(shape, workspace, workspace_bytes, &L);
   if (rc) return rc;
   const bool fuse_tree = x->draft_mode == MEDUSA_DRAFT_TOPK;
-  // greedy / typical: the LM row records are merged by the fused posterior
+  // greedy / typical: posterior and commit in one workgroup per sequence
   const bool fuse_post = mode != MEDUSA_EXACT;
   // 1. heads (+ tree tokens and positions)
   rc = heads_impl(shape, x->h, x->W1, x->b1_or_null, x->W2, x->topk_ids, x->topk_logits,

@@ -46,51 +46,59 @@ struct RowStat {
   int am;
 };
 
-// Greedy / typical posterior of sequence b over the whole workgroup
-// (blockDim.x >= T, a multiple of 64). stat(i) returns the statistics of
-// row i of the sequence. Thread 0 writes the outputs; every thread returns
-// the committed node.
-template <class StatFn>
-__device__ int posterior_det_block(const PostArgs& a, int b, StatFn stat) {
+// A sequence's tree in LDS: clamped parents, node tokens, row statistics,
+// acceptance flags and the decisions taken from them. Every walk along the
+// ancestor chain reads these, never global memory.
+struct TreeLds {
+  int parent[MAXT];
+  int tok[MAXT];
+  RowStat stat[MAXT];
+  uint8_t acc[MAXT];
+  int wmax[16];
+  int best, depth, bp, L;
+  int path[MAXK + 1];
+};
+
+// Greedy / typical posterior of sequence b over the workgroup (blockDim.x >=
+// T, a multiple of 64, at most 1024) from sh.parent, sh.tok, sh.stat and
+// thread c's child logit cl: thread 0 writes accept_len, last_node,
+// out_tokens and next_root; on return every thread sees sh.best, sh.depth.
+__device__ void posterior_det_lds(const PostArgs& a, int b, float cl, TreeLds& sh) {
   const int c = threadIdx.x;
   const int T = a.T;
-  __shared__ uint8_t acc[MAXT];
-  __shared__ int wmax[16];
-  __shared__ int s_best;
-  const int* tok = a.tokens + (size_t)b * T;
   if (c < T) {
     bool ok = true;
     if (c > 0) {
-      const RowStat ps = stat(parent_of(a.parent, c, T));
+      const RowStat ps = sh.stat[sh.parent[c]];
       if (a.mode == 0) {
-        ok = tok[c] == ps.am;
+        ok = sh.tok[c] == ps.am;
       } else {
-        const float p = exp_e((a.child_logit[(size_t)b * T + c] - ps.m) * a.inv_tau) / ps.S;
+        const float p = exp_e((cl - ps.m) * a.inv_tau) / ps.S;
         const float H = __logf(ps.S) - ps.W / ps.S;
         const float thr = fminf(a.eps, a.delta * exp_e(-H));
         ok = p > thr;
       }
     }
-    acc[c] = ok;
+    sh.acc[c] = ok;
   }
   __syncthreads();
   int key = -1;
   int dep = 0;
   if (c < T) {
     bool ok = true;
-    for (int x = c; x != 0 && dep < a.K; x = parent_of(a.parent, x, T)) {
-      ok = ok && acc[x];
+    for (int x = c; x != 0 && dep < a.K; x = sh.parent[x]) {
+      ok = ok && sh.acc[x];
       ++dep;
     }
     if (ok) key = (dep << 16) | (0xffff - c);
   }
   key = wave_max_i(key);
   const int nw = blockDim.x >> 6;
-  if ((c & 63) == 0) wmax[c >> 6] = key;
+  if ((c & 63) == 0) sh.wmax[c >> 6] = key;
   __syncthreads();
   if (c == 0) {
-    key = wmax[0];
-    for (int w = 1; w < nw; ++w) key = max(key, wmax[w]);
+    key = sh.wmax[0];
+    for (int w = 1; w < nw; ++w) key = max(key, sh.wmax[w]);
     const int best = 0xffff - (key & 0xffff);
     const int depth = key >> 16;
     a.accept_len[b] = depth;
@@ -99,30 +107,70 @@ __device__ int posterior_det_block(const PostArgs& a, int b, StatFn stat) {
     for (int j = depth + 1; j <= a.K; ++j) out[j] = -1;
     int x = best;
     for (int j = depth; j >= 0; --j) {
-      out[j] = tok[x];
-      x = parent_of(a.parent, x, T);
+      out[j] = sh.tok[x];
+      x = sh.parent[x];
     }
-    a.next_root[b] = stat(best).am;
-    int bp = 0;
-    for (int p = 0; p < a.P; ++p)
-      if (a.retrieve[(size_t)p * (a.K + 1) + depth] == best) {
-        bp = p;
-        break;
-      }
-    a.best_path[b] = bp;
-    s_best = best;
+    a.next_root[b] = sh.stat[best].am;
+    sh.best = best;
+    sh.depth = depth;
+    sh.bp = 0x7fffffff;
   }
   __syncthreads();
-  return s_best;
+}
+
+// Path rows of retrieve for thread c < P (entries 0..K), loaded up front.
+__device__ __forceinline__ void load_path_row(const PostArgs& a, int (&ret)[MAXK + 1]) {
+  const int c = threadIdx.x;
+#pragma unroll
+  for (int j = 0; j <= MAXK; ++j)
+    ret[j] = (c < a.P && j <= a.K) ? a.retrieve[(size_t)c * (a.K + 1) + j] : -1;
+}
+
+// best_path: the lowest path index whose node at the committed depth is the
+// committed node (0 if none; an LDS minimum over threads c < P).
+__device__ void best_path_lds(const PostArgs& a, int b, const int (&ret)[MAXK + 1],
+                              TreeLds& sh) {
+  const int c = threadIdx.x;
+  int r = -1;
+#pragma unroll
+  for (int j = 0; j <= MAXK; ++j)
+    if (j == sh.depth) r = ret[j];
+  if (c < a.P && r == sh.best) atomicMin(&sh.bp, c);
+  __syncthreads();
+  if (c == 0) a.best_path[b] = sh.bp < a.P ? sh.bp : 0;
+}
+
+// Tree data of sequence b into LDS (threads c < T), from values the caller
+// loaded into registers before (so that their loads fly with others).
+__device__ __forceinline__ void stage_tree(int T, int par, int tk, TreeLds& sh) {
+  const int c = threadIdx.x;
+  if (c < T) {
+    sh.parent[c] = min(max(par, 0), T - 1);
+    sh.tok[c] = tk;
+  }
 }
 
 __global__ __launch_bounds__(256) void posterior_kernel(PostArgs a) {
-  const int b = blockIdx.x;
-  posterior_det_block(a, b, [&](int i) {
-    const size_t r = (size_t)b * a.T + i;
-    return RowStat{a.row_stats[r * 3 + 0], a.row_stats[r * 3 + 1], a.row_stats[r * 3 + 2],
-                   a.row_argmax[r]};
-  });
+  const int b = blockIdx.x, c = threadIdx.x, T = a.T;
+  __shared__ TreeLds sh;
+  int par = 0, tk = 0;
+  float cl = 0.f;
+  RowStat st{0.f, 1.f, 0.f, 0};
+  if (c < T) {
+    const size_t r = (size_t)b * T + c;
+    par = a.parent[c];
+    tk = a.tokens[r];
+    cl = a.child_logit[r];
+    st = RowStat{a.row_stats[r * 3 + 0], a.row_stats[r * 3 + 1], a.row_stats[r * 3 + 2],
+                 a.row_argmax[r]};
+  }
+  int ret[MAXK + 1];
+  load_path_row(a, ret);
+  stage_tree(T, par, tk, sh);
+  if (c < T) sh.stat[c] = st;
+  __syncthreads();
+  posterior_det_lds(a, b, cl, sh);
+  best_path_lds(a, b, ret, sh);
 }
 
 // ---- exact mode ----------------------------------------------------------------
@@ -320,32 +368,33 @@ __global__ __launch_bounds__(1024) void posterior_exact_kernel(PostArgs a) {
 // ---- commit ----------------------------------------------------------------------
 // One 1024-thread workgroup per sequence; the path's K/V rows are copied as
 // 16-byte vectors (a node's row [H][Dh] is contiguous in the tree buffers, a
-// head's row Dh is contiguous in the cache), so each thread moves a few
-// vectors and the copy is bound by one round trip to memory, not by a chain
-// of dependent element copies.
-// Commit of sequence b's accepted path ending at node `last` over the whole
-// workgroup (see commit_kernel).
+// head's row Dh is contiguous in the cache), every thread loading all its
+// vectors (up to kCopyBatch per tensor) before it stores any, so the copy
+// costs one round trip to memory.
+constexpr int kCopyBatch = 4;
+
+// Commit of sequence b's accepted path ending at node `last`, prefix length
+// L, over the whole workgroup; sh.parent holds the tree.
 template <class ET>
-__device__ void commit_block(const CommitArgs& a, int b, int last_in) {
+__device__ void commit_lds(const CommitArgs& a, int b, int last_in, int L, TreeLds& sh) {
   constexpr int PV = ET::kPerVec;
   const int T = a.T, H = a.H, Dh = a.Dh;
-  __shared__ int path[MAXK + 1];
-  __shared__ int sh_L, sh_depth;
   if (threadIdx.x == 0) {
     const int last = min(max(last_in, 0), T - 1);
     int d = 0;
-    for (int x = last; x != 0 && d < a.K; x = parent_of(a.parent, x, T)) ++d;
+    for (int x = last; x != 0 && d < a.K; x = sh.parent[x]) ++d;
     int x = last;
     for (int j = d; j >= 0; --j) {
-      path[j] = x;
-      x = parent_of(a.parent, x, T);
+      sh.path[j] = x;
+      x = sh.parent[x];
     }
-    sh_depth = d;
-    sh_L = a.kv_len[b];
+    sh.depth = d;
   }
   __syncthreads();
-  const int L = sh_L, d = sh_depth;
+  const int d = sh.depth;
   const bool room = L >= 0 && L + d + 1 <= a.Lmax;
+  const float4* y = reinterpret_cast<const float4*>(a.y + ((size_t)b * T + sh.path[d]) * a.d);
+  float4* hn = reinterpret_cast<float4*>(a.h_next + (size_t)b * a.d);
   if (room) {
     const int vec_row = H * Dh / PV;          // 16-byte vectors per node row
     const int vec_head = Dh / PV;             // per head
@@ -354,18 +403,28 @@ __device__ void commit_block(const CommitArgs& a, int b, int last_in) {
     const u32x4_t* vt = reinterpret_cast<const u32x4_t*>(a.v_tree);
     u32x4_t* kc = reinterpret_cast<u32x4_t*>(a.k_cache);
     u32x4_t* vc = reinterpret_cast<u32x4_t*>(a.v_cache);
-    for (int e = threadIdx.x; e < total; e += blockDim.x) {
-      const int i = e / vec_row, rem = e - i * vec_row;
-      const int hh = rem / vec_head, x = rem - hh * vec_head;
-      const size_t src = ((size_t)b * T + path[i]) * vec_row + rem;
-      const size_t dst = (((size_t)b * H + hh) * a.Lmax + L + i) * vec_head + x;
-      const u32x4_t kv = kt[src], vv = vt[src];
-      kc[dst] = kv;
-      vc[dst] = vv;
+    for (int e0 = threadIdx.x; e0 < total; e0 += kCopyBatch * blockDim.x) {
+      u32x4_t kv[kCopyBatch], vv[kCopyBatch];
+#pragma unroll
+      for (int u = 0; u < kCopyBatch; ++u) {
+        const int e = min(e0 + u * (int)blockDim.x, total - 1);
+        const int i = e / vec_row, rem = e - i * vec_row;
+        const size_t src = ((size_t)b * T + sh.path[i]) * vec_row + rem;
+        kv[u] = kt[src];
+        vv[u] = vt[src];
+      }
+#pragma unroll
+      for (int u = 0; u < kCopyBatch; ++u) {
+        const int e = e0 + u * (int)blockDim.x;
+        if (e >= total) break;
+        const int i = e / vec_row, rem = e - i * vec_row;
+        const int hh = rem / vec_head, x = rem - hh * vec_head;
+        const size_t dst = (((size_t)b * H + hh) * a.Lmax + L + i) * vec_head + x;
+        kc[dst] = kv[u];
+        vc[dst] = vv[u];
+      }
     }
   }
-  const float4* y = reinterpret_cast<const float4*>(a.y + ((size_t)b * T + path[d]) * a.d);
-  float4* hn = reinterpret_cast<float4*>(a.h_next + (size_t)b * a.d);
   for (int e = threadIdx.x; e < a.d / 4; e += blockDim.x) hn[e] = y[e];
   __syncthreads();
   if (threadIdx.x == 0) (a.kv_len_out ? a.kv_len_out : a.kv_len)[b] = room ? L + d + 1 : -1;
@@ -373,20 +432,45 @@ __device__ void commit_block(const CommitArgs& a, int b, int last_in) {
 
 template <class ET>
 __global__ __launch_bounds__(1024) void commit_kernel(CommitArgs a) {
-  commit_block<ET>(a, blockIdx.x, a.last_node[blockIdx.x]);
+  const int b = blockIdx.x, c = threadIdx.x;
+  __shared__ TreeLds sh;
+  const int par = c < a.T ? a.parent[c] : 0;
+  if (c == 0) sh.L = a.kv_len[b];
+  const int last = a.last_node[b];
+  stage_tree(a.T, par, 0, sh);
+  __syncthreads();
+  commit_lds<ET>(a, b, last, sh.L, sh);
 }
 
 // Composite step, greedy / typical: one workgroup per sequence evaluates the
 // posterior from the merged row statistics and commits the accepted path.
+// All the loads the decision needs -- row statistics, child logits, tokens,
+// parents, path rows, the prefix length -- are issued before any is used.
 template <class ET>
 __global__ __launch_bounds__(1024) void posterior_commit_kernel(PostArgs a, CommitArgs c) {
-  const int b = blockIdx.x;
-  const int best = posterior_det_block(a, b, [&](int i) {
-    const size_t r = (size_t)b * a.T + i;
-    return RowStat{a.row_stats[r * 3 + 0], a.row_stats[r * 3 + 1], a.row_stats[r * 3 + 2],
-                   a.row_argmax[r]};
-  });
-  commit_block<ET>(c, b, best);
+  const int b = blockIdx.x, t = threadIdx.x, T = a.T;
+  __shared__ TreeLds sh;
+  int par = 0, tk = 0;
+  float cl = 0.f;
+  if (t < T) {
+    const size_t r = (size_t)b * T + t;
+    par = a.parent[t];
+    tk = a.tokens[r];
+    cl = a.child_logit[r];
+  }
+  int ret[MAXK + 1];
+  load_path_row(a, ret);
+  if (t == 0) sh.L = c.kv_len[b];
+  if (t < T) {
+    const size_t r = (size_t)b * T + t;
+    sh.stat[t] = RowStat{a.row_stats[r * 3 + 0], a.row_stats[r * 3 + 1],
+                         a.row_stats[r * 3 + 2], a.row_argmax[r]};
+  }
+  stage_tree(T, par, tk, sh);
+  __syncthreads();
+  posterior_det_lds(a, b, cl, sh);
+  best_path_lds(a, b, ret, sh);
+  commit_lds<ET>(c, b, sh.best, sh.L, sh);
 }
 
 }  // namespace
