@@ -65,7 +65,14 @@ int env_int(const char* name, int dflt, int lo, int hi) {
 // Workspace sizes are computed for the smallest allowed value, so any
 // setting fits.
 constexpr int kMinW2Rows = 16;   // rows per workgroup at the smallest setting
-int w1_rows() { static int v = env_int("MEDUSA_W1_ROWS", 4, 1, 64); return v; }
+// Rows per wave of the W1 stream: MEDUSA_W1_ROWS, else the fewest that let
+// all K d rows run as one wave of resident workgroups (4 per compute unit).
+int w1_rows(int rows) {
+  static const int forced = env_int("MEDUSA_W1_ROWS", 0, 0, 64);
+  if (forced > 0) return forced;
+  const int slots = 4 * 4 * device_cus();   // waves of the resident workgroups
+  return std::min(64, std::max(1, (rows + slots - 1) / slots));
+}
 int w2_rows() { static int v = env_int("MEDUSA_W2_ROWS", 40, kMinW2Rows / 4, 64); return v; }
 int head_interleave() { static int v = env_int("MEDUSA_HEAD_INTERLEAVE", 1, 0, 1); return v; }
 
@@ -303,7 +310,7 @@ int heads_impl(const medusa_shape* shape, const float* h, const void* W1,
   a.part_m = at<float>(workspace, L.part_m);
   a.part_s = at<float>(workspace, L.part_s);
   a.G = L.G;
-  a.w1_rows_per_wave = w1_rows();
+  a.w1_rows_per_wave = w1_rows(shape->K * shape->d);
   a.w2_rows_per_wave = w2_rows();
   a.interleave = head_interleave();
   a.ev_before = g_ev_before;

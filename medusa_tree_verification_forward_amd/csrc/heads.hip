@@ -13,12 +13,12 @@
 // kernel reduces the records of one (sequence, head) in a fixed order.
 #include "common.h"
 #include "kernels.h"
+#include "select.h"
 
 namespace medusa {
 namespace {
 
 constexpr float kNegInf = -__builtin_huge_valf();
-constexpr int kNoId = 0x7fffffff;
 
 constexpr int kHeadWaves = 4;   // waves per workgroup
 constexpr int kRing = 8;        // weight loads in flight per wave
@@ -248,33 +248,6 @@ __device__ __forceinline__ void stats_merge(float& m, float& s, float m2, float 
   m = mn;
 }
 
-// Best (value desc, id asc) over the wave, returned to every lane.
-__device__ __forceinline__ void wave_best(float& bv, int& bi) {
-#pragma unroll
-  for (int step = 0; step < 4; ++step) {
-    float ov;
-    int oi;
-    if (step == 0) { ov = dpp<kDppQuadXor1>(bv); oi = dppi<kDppQuadXor1>(bi); }
-    else if (step == 1) { ov = dpp<kDppQuadXor2>(bv); oi = dppi<kDppQuadXor2>(bi); }
-    else if (step == 2) { ov = dpp<kDppRowRor4>(bv); oi = dppi<kDppRowRor4>(bi); }
-    else { ov = dpp<kDppRowRor8>(bv); oi = dppi<kDppRowRor8>(bi); }
-    if (better(ov, oi, bv, bi)) { bv = ov; bi = oi; }
-  }
-  float wv = readlane_f(bv, 0);
-  int wi = __builtin_amdgcn_readlane(bi, 0);
-#pragma unroll
-  for (int row = 16; row < 64; row += 16) {
-    const float ov = readlane_f(bv, row);
-    const int oi = __builtin_amdgcn_readlane(bi, row);
-    if (better(ov, oi, wv, wi)) {
-      wv = ov;
-      wi = oi;
-    }
-  }
-  bv = wv;
-  bi = wi;
-}
-
 // ---------------------------------------------------------------------------
 // l = W2_k z_k for the rows of one block; top-S and (max, sum exp) of them.
 // grid = (G, K): wave w of block g of head k streams rows
@@ -386,56 +359,10 @@ __global__ __launch_bounds__(kHeadWaves * 64) void heads_w2_kernel(
 // candidates at once (kMergeBatch per round) and keeps a private sorted
 // list in registers; each wave then takes its top S in S rounds of a
 // wave-wide (value desc, id asc) selection, and wave 0 selects the final S
-// from the waves' lists. The log-sum-exp combines the G (max, sum) records
-// with fixed-order reductions.
+// from the waves' lists. Wave 0 also takes the log-sum-exp of the G (max,
+// sum) records (wave_lse, fixed order).
 constexpr int kMergeThreads = 256;
 constexpr int kMergeBatch = 4;
-
-template <int SMAX>
-__device__ __forceinline__ void reg_insert(float (&lv)[SMAX], int (&li)[SMAX], float v, int id,
-                                           int S) {
-#pragma unroll
-  for (int j = SMAX - 1; j >= 0; --j) {
-    if (j >= S) continue;
-    if (!better(v, id, lv[j], li[j])) continue;
-    if (j > 0 && better(v, id, lv[j - 1], li[j - 1])) {
-      lv[j] = lv[j - 1];
-      li[j] = li[j - 1];
-    } else {
-      lv[j] = v;
-      li[j] = id;
-    }
-  }
-}
-
-// S rounds of selection over the lanes' sorted lists; lane r < S receives
-// the r-th best of the wave.
-template <int SMAX>
-__device__ __forceinline__ void wave_select(float (&lv)[SMAX], int (&li)[SMAX], int S,
-                                            float& out_v, int& out_i) {
-  const int lane = threadIdx.x & 63;
-  out_v = kNegInf;
-  out_i = kNoId;
-  for (int r = 0; r < S; ++r) {
-    float bv = lv[0];
-    int bi = li[0];
-    wave_best(bv, bi);
-    if (lane == r) {
-      out_v = bv;
-      out_i = bi;
-    }
-    // pop the winner from the lane that holds it (ids are unique)
-    if (li[0] == bi && bi != kNoId) {
-#pragma unroll
-      for (int j = 0; j < SMAX - 1; ++j) {
-        lv[j] = lv[j + 1];
-        li[j] = li[j + 1];
-      }
-      lv[SMAX - 1] = kNegInf;
-      li[SMAX - 1] = kNoId;
-    }
-  }
-}
 
 // Tree tokens and positions written by the merge (composite step).
 struct MergeTree {
@@ -459,17 +386,6 @@ __global__ __launch_bounds__(kMergeThreads) void heads_merge_kernel(
   const size_t rec0 = ((size_t)b * K + k) * G;
   __shared__ float sv[NW][MAXS_LDS];
   __shared__ int si[NW][MAXS_LDS];
-  __shared__ float red[kMergeThreads];
-
-  // softmax records first, so their loads fly with the candidates'
-  float pm[kMergeBatch], ps[kMergeBatch];
-  const bool want_lse = lse != nullptr;
-#pragma unroll
-  for (int u = 0; u < kMergeBatch; ++u) {
-    const int g = min(t + kMergeThreads * u, G - 1);
-    pm[u] = want_lse ? part_m[rec0 + g] : kNegInf;
-    ps[u] = want_lse ? part_s[rec0 + g] : 0.f;
-  }
 
   float lv[SMAX];
   int li[SMAX];
@@ -515,39 +431,12 @@ __global__ __launch_bounds__(kMergeThreads) void heads_merge_kernel(
     si[wave][lane] = wi;
   }
 
-  // log-sum-exp of the G records: block max, then block sum, fixed order
-  float mx = kNegInf;
-  if (want_lse) {
-#pragma unroll
-    for (int u = 0; u < kMergeBatch; ++u)
-      if (t + kMergeThreads * u < G) mx = fmaxf(mx, pm[u]);
-    for (int g = t + kMergeThreads * kMergeBatch; g < G; g += kMergeThreads)
-      mx = fmaxf(mx, part_m[rec0 + g]);
-    red[t] = mx;
+  // log-sum-exp of the G (max, sum) records: wave 0, fixed order
+  if (lse != nullptr && wave == 0) {
+    const float v = wave_lse(part_m + rec0, part_s + rec0, G);
+    if (lane == 0) lse[(size_t)b * K + k] = v;
   }
   __syncthreads();
-  if (want_lse) {
-    float m_all = kNegInf;
-    for (int w = 0; w < NW; ++w) m_all = fmaxf(m_all, wave_max(red[w * 64 + lane]));
-    float ssum = 0.f;
-#pragma unroll
-    for (int u = 0; u < kMergeBatch; ++u)
-      if (t + kMergeThreads * u < G && pm[u] != kNegInf) ssum += ps[u] * exp_e(pm[u] - m_all);
-    for (int g = t + kMergeThreads * kMergeBatch; g < G; g += kMergeThreads) {
-      const float m2 = part_m[rec0 + g];
-      if (m2 != kNegInf) ssum += part_s[rec0 + g] * exp_e(m2 - m_all);
-    }
-    __syncthreads();
-    red[t] = ssum;
-    __syncthreads();
-    if (wave == 0) {
-      float tot = 0.f;
-      for (int w = 0; w < NW; ++w) tot += wave_sum(red[w * 64 + lane]);
-      if (lane == 0) lse[(size_t)b * K + k] = m_all + __logf(tot);
-    }
-  } else {
-    __syncthreads();
-  }
   if (wave != 0) return;
   // final selection over the waves' lists: lane l < NW*S holds one entry
   float fv[SMAX];

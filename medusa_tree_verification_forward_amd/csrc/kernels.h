@@ -146,6 +146,7 @@ struct AttnArgs {
   void* out_elem;              // [B][T][H][Dh] storage type (or null)
 };
 int attn_splits(int Lmax);
+int device_cus();   // compute units of the current device (cached per device)
 hipError_t launch_tree_attention(const AttnArgs& a, hipStream_t st);
 
 // ---- posterior and commit -------------------------------------------------------------

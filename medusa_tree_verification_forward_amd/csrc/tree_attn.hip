@@ -524,20 +524,6 @@ __global__ __launch_bounds__(64) void attn_merge_kernel(AttnArgs a) {
   }
 }
 
-// Compute units of the current device (cached per device).
-int device_cus() {
-  static int cus[64] = {0};
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (cus[dev] == 0) {
-    int n = 0;
-    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 1)
-      n = 256;
-    cus[dev] = n;
-  }
-  return cus[dev];
-}
-
 template <int DH>
 hipError_t launch_bf16(const AttnArgs& a, hipStream_t st) {
   const int MQ = (a.T + 15) / 16;
@@ -578,6 +564,20 @@ hipError_t launch_f32(const AttnArgs& a, hipStream_t st) {
 }
 
 }  // namespace
+
+// Compute units of the current device (cached per device).
+int device_cus() {
+  static int cus[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cus[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 1)
+      n = 256;
+    cus[dev] = n;
+  }
+  return cus[dev];
+}
 
 int attn_splits(int Lmax) { return Lmax > 0 ? (Lmax + kAttnChunk - 1) / kAttnChunk : 1; }
 
