@@ -149,19 +149,17 @@ Layout layout_for(const medusa_shape* s) {
   L.q = take(B * T * d * es);
   L.o_elem = take(B * T * d * es);
   L.y_elem = take(B * T * d * es);
-  {
-    // LM records [M][groups][4], or split-K partial logits [groups][KS][M][cols]
-    const size_t rec = B * T * gemm_groups_max(s->V) * 4;
-    const int lm_ks = lm_splits_for((int)(B * T));
-    const size_t split = lm_ks > 1 ? (size_t)lm_ks * B * T * (s->V + 128) : 0;
-    L.lm_part = take((rec > split ? rec : split) * 4);
-  }
+  // LM records [M][groups][4]
+  L.lm_part = take(B * T * gemm_groups_max(s->V) * 4 * 4);
   {
     const bool f32 = s->dtype == MEDUSA_F32;
-    // partials [groups][KS][M][cols]: groups * cols < N + 128
+    // QKV / O-proj partials [groups][KS][M][cols] (groups * cols < N + 128),
+    // or the LM head's slices [groups][KS][48][cols] when its K is split
     const size_t q_need = (size_t)gemm_splits(3 * s->d, s->d, f32) * B * T * (3 * d + 128);
     const size_t o_need = (size_t)gemm_splits(s->d, s->d, f32) * B * T * (d + 128);
-    L.gemm_part = take((q_need > o_need ? q_need : o_need) * 4);
+    const int lm_ks = lm_splits_for((int)(B * T));
+    const size_t lm_need = lm_ks > 1 ? (size_t)lm_ks * 48 * (s->V + 128) : 0;
+    L.gemm_part = take(std::max(q_need, std::max(o_need, lm_need)) * 4);
   }
   L.pw = take(B * V * 4);
   L.total = off;
@@ -582,6 +580,7 @@ int verify_impl(const medusa_shape* shape, const void* E, const void* W_qkv, con
   gl.parent = parent;
   gl.inv_tau = 1.0f / temperature;
   gl.part = at<float>(workspace, L.lm_part);
+  gl.lm_slices = at<float>(workspace, L.gemm_part);
   gl.child_logit = child_logit;
   gl.logits_out = verify_logits_or_null;
   e = launch_lm_head(gl, row_stats, row_argmax, st);

@@ -78,7 +78,7 @@ struct TreeArgs {
 hipError_t launch_tree(const TreeArgs& a, hipStream_t st);
 
 // ---- node GEMMs (verify pass) ---------------------------------------------------
-enum { EPI_QKV = 0, EPI_OPROJ = 1, EPI_LM = 2, EPI_PART = 3 };
+enum { EPI_QKV = 0, EPI_OPROJ = 1, EPI_LM = 2 };
 struct GemmParams {
   bool f32;
   int M, N, K;                 // C[M][N] = A[M][K] * W[N][K]^T
@@ -109,6 +109,7 @@ struct GemmParams {
   int group_cols;              // set by the launcher
   int fused;                   // set by the launcher
   int kmajor;                  // set by the launcher: packed tile order
+  float* lm_slices;            // LM head split over K: [groups][KS][48][cols] fp32
 };
 bool packed_kmajor();
 // Weights W[rows][K] of the node GEMMs are packed into MFMA tiles (see
@@ -120,7 +121,7 @@ hipError_t launch_pack_weight(bool f32, const void* W, int rows, int K, int pair
 int gemm_groups_max(int N);                // column groups of a node GEMM (upper bound)
 int gemm_passes_max(int M);                // row passes (upper bound)
 int lm_head_blocks(int N, int M);          // column groups of the LM head
-int lm_splits_for(int M);                  // K slices of the LM head (1: in-kernel statistics)
+int lm_splits_for(int M);                  // K slices of the LM head
 int gemm_splits(int N, int K, bool f32);   // K slices of the QKV / output projection GEMMs
 hipError_t launch_qkv(const GemmParams& p, hipStream_t st);
 hipError_t launch_oproj(const GemmParams& p, hipStream_t st);

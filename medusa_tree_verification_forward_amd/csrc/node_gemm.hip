@@ -34,8 +34,9 @@
 // (found with a device-scope counter that it leaves at zero for the next
 // launch; the partials travel through agent-coherent stores and loads), or
 // in a kernel of its own.
-// The LM head runs with KS = 1 and reduces in-kernel: per row and column
-// group (max, argmax, S, W) at temperature tau with S = sum e^{(l-m)/tau},
+// The LM head reduces in-kernel (after the split-K hand-off when K is split):
+// per row and column group (max, argmax, S, W) at temperature tau with
+// S = sum e^{(l-m)/tau},
 // W = sum e^{(l-m)/tau} (l-m)/tau; the logit of every tree node's token
 // under its parent's row; optional full logits. A merge kernel combines the
 // column groups of a row.
@@ -333,7 +334,7 @@ __global__ __launch_bounds__(64 * WV, (WV == 4 && D <= 8) ? 4 : 2) void node_gem
   if constexpr (EPI != EPI_LM) {
     // slice ks of the partials: part[g][ks][r][c]
     float* part = p.part + (size_t)(g * KS + ks) * p.M * GC + 16 * wave + li;
-    const bool fused = EPI != EPI_PART && p.fused;
+    const bool fused = p.fused;
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
@@ -440,6 +441,42 @@ __global__ __launch_bounds__(64 * WV, (WV == 4 && D <= 8) ? 4 : 2) void node_gem
       }
     }
   } else {
+    if (KS > 1) {
+      // Slices of the logit tile: the last of the KS workgroups of this
+      // (group, pass) sums them in slice order (partials handed over through
+      // agent-coherent stores and loads) and goes on to the statistics.
+      constexpr int TILE = 16 * MT * GC;
+      float* sl = p.lm_slices + ((size_t)g * gridDim.z + blockIdx.z) * KS * TILE;
+      const int ci = 16 * wave + li;
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          coherent_store(sl + (size_t)ks * TILE + (16 * mt + 4 * lq + j) * GC + ci, acc[mt][j]);
+      if (!last_to_arrive(p.counters + g * gridDim.z + blockIdx.z, KS)) return;
+      float tot[MT][4];
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) tot[mt][j] = 0.f;
+      for (int s0 = 0; s0 < KS; ++s0) {
+        float v[MT][4];
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            v[mt][j] = s0 == ks ? acc[mt][j]
+                                : coherent_load(sl + (size_t)s0 * TILE + (16 * mt + 4 * lq + j) * GC + ci);
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) tot[mt][j] += v[mt][j];
+      }
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[mt][j] = tot[mt][j];
+    }
     const bool cv = col < p.N;
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
@@ -568,68 +605,6 @@ __global__ __launch_bounds__(64) void row_stats_merge_kernel(const float* __rest
   }
 }
 
-// LM-head statistics from split-K partials: one workgroup per row r.
-// l_n = sum of the KS slices of column n (slice order); every thread keeps
-// an online (max, lowest argmax, S, W) record of its columns at temperature
-// tau, the records are merged in a fixed order (lane butterfly, then waves
-// in order); optional full logits; the logit of each tree node whose
-// parent row is r at the node's token.
-constexpr int kStatThreads = 1024;
-__global__ __launch_bounds__(kStatThreads) void lm_stats_kernel(GemmParams p, int KS,
-                                                              float* __restrict__ row_stats,
-                                                              int* __restrict__ row_argmax) {
-  const int r = blockIdx.x, t = threadIdx.x, lane = t & 63, wave = t >> 6;
-  const int V = p.N;
-  float m = kNegInf, s = 0.f, w = 0.f;
-  int a = 0x7fffffff;
-  constexpr int U = 8;   // columns per thread per round, loaded before any is used
-  for (int n0 = 0; n0 < V; n0 += kStatThreads * U) {
-    float lv[U];
-#pragma unroll
-    for (int u = 0; u < U; ++u)
-      lv[u] = sum_partials(p, r, min(n0 + t + kStatThreads * u, V - 1), KS);
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int n = n0 + t + kStatThreads * u;
-      if (n < V) {
-        if (p.logits_out) p.logits_out[(size_t)r * V + n] = lv[u];
-        rec_merge(m, s, w, a, lv[u], 1.f, 0.f, n, p.inv_tau);
-      }
-    }
-  }
-  // child logits: node c (1 <= c < T) of this row's sequence whose parent is this row
-  const int T = p.T, b = r / T, rl = r - b * T;
-  if (t >= 1 && t < T && min(max(p.parent[t], 0), T - 1) == rl) {
-    const int node = b * T + t;
-    const int tok = min(max(p.tokens[node], 0), V - 1);
-    p.child_logit[node] = sum_partials(p, r, tok, KS);
-  }
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) {
-    const float m2 = __shfl_xor(m, off), s2 = __shfl_xor(s, off), w2 = __shfl_xor(w, off);
-    const int a2 = __shfl_xor(a, off);
-    rec_merge(m, s, w, a, m2, s2, w2, a2, p.inv_tau);
-  }
-  __shared__ float rec[kStatThreads / 64][4];
-  if (lane == 0) {
-    rec[wave][0] = m;
-    rec[wave][1] = s;
-    rec[wave][2] = w;
-    rec[wave][3] = __int_as_float(a);
-  }
-  __syncthreads();
-  if (t != 0) return;
-  m = kNegInf;
-  s = w = 0.f;
-  a = 0x7fffffff;
-  for (int i = 0; i < kStatThreads / 64; ++i)
-    rec_merge(m, s, w, a, rec[i][0], rec[i][1], rec[i][2], __float_as_int(rec[i][3]), p.inv_tau);
-  row_stats[(size_t)r * 3 + 0] = m;
-  row_stats[(size_t)r * 3 + 1] = s;
-  row_stats[(size_t)r * 3 + 2] = w;
-  row_argmax[r] = a;
-}
-
 // Tile configuration: waves per workgroup (= 16-column stripes), m-tiles
 // per pass, k-tiles per A chunk, weight loads in flight per wave.
 struct Config {
@@ -655,21 +630,25 @@ Config small_config() {
 // MEDUSA_LM_CFG ("wv,ch", default "8,8"): waves per workgroup and k-tiles per
 // A chunk of the LM head's 48-row tile (4,4: 8 weight loads in flight per
 // wave; 8,4: 8,8 chunks with 8 in flight; 8,8: 16 in flight).
-Config lm_config() {
-  static const Config v = [] {
+Config lm_config(int KS) {
+  static const Config forced = [] {
     const char* s = getenv("MEDUSA_LM_CFG");
-    int wv = 8, ch = 8;
+    int wv = 0, ch = 0;
     if (s && *s) sscanf(s, "%d,%d", &wv, &ch);
     if (wv == 4 && ch == 4) return Config{4, 3, 4, 8};
     if (wv == 8 && ch == 4) return Config{8, 3, 8, 8};
-    return Config{8, 3, 8, 16};
+    if (wv == 8 && ch == 8) return Config{8, 3, 8, 16};
+    return Config{0, 0, 0, 0};
   }();
-  return v;
+  if (forced.wv) return forced;
+  // unsplit: one 8-wave workgroup per compute unit, 16 loads in flight per
+  // wave; split: 4-wave workgroups, four per compute unit
+  return KS > 1 ? Config{4, 3, 4, 8} : Config{8, 3, 8, 16};
 }
 
 Config config_for(int M, int epi) {
   if (M <= 48) {
-    if (epi == EPI_LM || epi == EPI_PART) return lm_config();
+    if (epi == EPI_LM) return lm_config(lm_splits_for(M));
     return small_config();
   }
   return Config{8, 12, 4, 4};
@@ -804,10 +783,9 @@ hipError_t launch_oproj(const GemmParams& p, hipStream_t st) {
 }
 
 // MEDUSA_LM_SPLITS (1, 2 or 4; default 1): K slices of the LM head for a
-// single 48-row pass. With 1, statistics are taken in the GEMM's epilogue;
-// with more, a per-row statistics kernel sums the slices (measured slower
-// for the 7B step: the partial-logit traffic and the row-per-workgroup
-// statistics cost more than the extra parallelism gains).
+// single 48-row pass. With more than one, the last workgroup of each column
+// group sums the slices' logit tiles (handed over without fences) before the
+// in-kernel statistics.
 int lm_splits_for(int M) {
   static const int v = [] {
     const char* s = getenv("MEDUSA_LM_SPLITS");
@@ -819,18 +797,9 @@ int lm_splits_for(int M) {
 
 hipError_t launch_lm_head(GemmParams p, float* row_stats, int* row_argmax, hipStream_t st) {
   p.kmajor = packed_kmajor();
+  p.group_cols = 16 * config_for(p.M, EPI_LM).wv;
   const int KS = lm_splits_for(p.M);
-  if (KS > 1) {
-    p.group_cols = 16 * config_for(p.M, EPI_PART).wv;
-    p.fused = 0;
-    hipError_t e = p.f32 ? launch_main<F32, EPI_PART>(p, KS, st)
-                         : launch_main<BF16, EPI_PART>(p, KS, st);
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(lm_stats_kernel, dim3(p.M), dim3(kStatThreads), 0, st, p, KS, row_stats,
-                       row_argmax);
-    return hipGetLastError();
-  }
-  hipError_t e = p.f32 ? launch_main<F32, EPI_LM>(p, 1, st) : launch_main<BF16, EPI_LM>(p, 1, st);
+  hipError_t e = p.f32 ? launch_main<F32, EPI_LM>(p, KS, st) : launch_main<BF16, EPI_LM>(p, KS, st);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(row_stats_merge_kernel, dim3(p.M), dim3(64), 0, st, p.part,
                      lm_head_blocks(p.N, p.M), p.inv_tau, row_stats, row_argmax);
