@@ -149,8 +149,8 @@ Layout layout_for(const medusa_shape* s) {
   L.q = take(B * T * d * es);
   L.o_elem = take(B * T * d * es);
   L.y_elem = take(B * T * d * es);
-  // LM records [M][groups][4]
-  L.lm_part = take(B * T * gemm_groups_max(s->V) * 4 * 4);
+  // LM records [M][stripes][4]
+  L.lm_part = take(B * T * (size_t)lm_record_slots(s->V) * 4 * 4);
   {
     const bool f32 = s->dtype == MEDUSA_F32;
     // QKV / O-proj partials [groups][KS][M][cols] (groups * cols < N + 128),

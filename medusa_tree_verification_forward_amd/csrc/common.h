@@ -276,38 +276,6 @@ __device__ __forceinline__ void rec_merge(float& m, float& s, float& w, int& a, 
   a = an;
 }
 
-// One wave merges the G records part[r][0..G) (4 floats each, a as int bits)
-// in a fixed order: lane l takes records l, l+64, ... (all of a round loaded
-// before any is merged), then a lane butterfly. Every lane returns the result.
-__device__ __forceinline__ void merge_row_records(const float* __restrict__ part, int G, int r,
-                                                  float inv_tau, float& m, float& s, float& w,
-                                                  int& a) {
-  const int lane = threadIdx.x & 63;
-  m = -__builtin_huge_valf();
-  s = w = 0.f;
-  a = 0x7fffffff;
-  constexpr int RB = 4;
-  for (int g0 = 0; g0 < G; g0 += 64 * RB) {
-    floatx4_t rec[RB];
-#pragma unroll
-    for (int u = 0; u < RB; ++u) {
-      const int g = min(g0 + lane + 64 * u, G - 1);
-      rec[u] = *reinterpret_cast<const floatx4_t*>(part + ((size_t)r * G + g) * 4);
-    }
-#pragma unroll
-    for (int u = 0; u < RB; ++u)
-      if (g0 + lane + 64 * u < G)
-        rec_merge(m, s, w, a, rec[u][0], rec[u][1], rec[u][2], __float_as_int(rec[u][3]),
-                  inv_tau);
-  }
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) {
-    const float m2 = __shfl_xor(m, off), s2 = __shfl_xor(s, off), w2 = __shfl_xor(w, off);
-    const int a2 = __shfl_xor(a, off);
-    rec_merge(m, s, w, a, m2, s2, w2, a2, inv_tau);
-  }
-}
-
 // ---- MFMA ---------------------------------------------------------------------
 // v_mfma_f32_16x16x32_bf16: A 16x32, B 32x16, C 16x16 fp32.
 // Lane l holds A[l%16][8*(l/16) .. +7], B[8*(l/16) .. +7][l%16] and

@@ -35,11 +35,11 @@
 // launch; the partials travel through agent-coherent stores and loads), or
 // in a kernel of its own.
 // The LM head reduces in-kernel (after the split-K hand-off when K is split):
-// per row and column group (max, argmax, S, W) at temperature tau with
-// S = sum e^{(l-m)/tau},
-// W = sum e^{(l-m)/tau} (l-m)/tau; the logit of every tree node's token
-// under its parent's row; optional full logits. A merge kernel combines the
-// column groups of a row.
+// per row and 16-column stripe (max, argmax, S, W) at temperature tau with
+// S = sum e^{(l-m)/tau}, W = sum e^{(l-m)/tau} (l-m)/tau, one record per
+// (row, stripe) written by the wave that owns the stripe; the logit of every
+// tree node's token under its parent's row; optional full logits. A merge
+// kernel combines the stripes of a row in order.
 #include <stdio.h>
 #include <stdlib.h>
 
@@ -201,7 +201,6 @@ __global__ __launch_bounds__(64 * WV, (WV == 4 && D <= 8) ? 4 : 2) void node_gem
 
   __shared__ u32x4_t sA0[CH][MT][64];
   __shared__ u32x4_t sA1[CH][MT][64];
-  __shared__ float stat[EPI == EPI_LM ? WV : 1][EPI == EPI_LM ? 16 * MT : 1][4];
 
   // A fragment f = wave + WV i of a chunk is (k-tile f / MT, m-tile f % MT)
   const St* asrc[NAW];
@@ -506,11 +505,12 @@ __global__ __launch_bounds__(64 * WV, (WV == 4 && D <= 8) ? 4 : 2) void node_gem
         }
         sv = row16_sum(sv);
         wv = row16_sum(wv);
-        if (li == 0) {
-          stat[wave][rr][0] = bv;
-          stat[wave][rr][1] = sv;
-          stat[wave][rr][2] = wv;
-          stat[wave][rr][3] = __int_as_float(bi);
+        // one record per (row, 16-column stripe): rows 4 lq + j of the wave
+        // are held by lanes li == 0
+        if (li == 0 && r < p.M) {
+          const int stripes = gridDim.x * WV;
+          *reinterpret_cast<float4*>(p.part + ((size_t)r * stripes + g * WV + wave) * 4) =
+              make_float4(bv, sv, wv, __int_as_float(bi));
         }
         if (p.logits_out && cv && r < p.M) p.logits_out[(size_t)r * p.N + col] = acc[mt][j];
       }
@@ -551,22 +551,6 @@ __global__ __launch_bounds__(64 * WV, (WV == 4 && D <= 8) ? 4 : 2) void node_gem
         if (li == want_li && lq == want_lq) p.child_logit[hn] = v;
       }
     }
-    __syncthreads();
-    // one record per (row, column group): merge the waves in order
-    for (int rr = threadIdx.x; rr < 16 * MT; rr += blockDim.x) {
-      const int r = m0 + rr;
-      if (r >= p.M) continue;
-      float m = kNegInf, sv = 0.f, wv = 0.f;
-      int a = 0x7fffffff;
-      for (int w = 0; w < WV; ++w)
-        rec_merge(m, sv, wv, a, stat[w][rr][0], stat[w][rr][1], stat[w][rr][2],
-                  __float_as_int(stat[w][rr][3]), p.inv_tau);
-      float* rec = p.part + ((size_t)r * gridDim.x + g) * 4;
-      rec[0] = m;
-      rec[1] = sv;
-      rec[2] = wv;
-      rec[3] = __int_as_float(a);
-    }
   }
 }
 
@@ -589,20 +573,49 @@ __global__ __launch_bounds__(256) void oproj_epilogue_kernel(GemmParams p, int K
   oproj_finish<ET>(p, r, n, sum_partials(p, r, n, KS));
 }
 
-__global__ __launch_bounds__(64) void row_stats_merge_kernel(const float* __restrict__ part,
-                                                             int G, float inv_tau,
-                                                             float* __restrict__ row_stats,
-                                                             int* __restrict__ row_argmax) {
-  const int r = blockIdx.x, lane = threadIdx.x;
-  float m, s, w;
-  int a;
-  merge_row_records(part, G, r, inv_tau, m, s, w, a);
-  if (lane == 0) {
-    row_stats[(size_t)r * 3 + 0] = m;
-    row_stats[(size_t)r * 3 + 1] = s;
-    row_stats[(size_t)r * 3 + 2] = w;
-    row_argmax[r] = a;
+// Row statistics from the G records of row r: 256 threads, thread t takes
+// records t + 256 u in u order (every load of a round issued before any is
+// used), then a lane butterfly and the four waves in order.
+constexpr int kRowMergeThreads = 256;
+__global__ __launch_bounds__(kRowMergeThreads) void row_stats_merge_kernel(
+    const float* __restrict__ part, int G, float inv_tau, float* __restrict__ row_stats,
+    int* __restrict__ row_argmax) {
+  constexpr int RB = 8;
+  const int r = blockIdx.x, t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  float m = kNegInf, s = 0.f, w = 0.f;
+  int a = 0x7fffffff;
+  for (int g0 = 0; g0 < G; g0 += kRowMergeThreads * RB) {
+    floatx4_t rec[RB];
+#pragma unroll
+    for (int u = 0; u < RB; ++u) {
+      const int g = min(g0 + t + kRowMergeThreads * u, G - 1);
+      rec[u] = *reinterpret_cast<const floatx4_t*>(part + ((size_t)r * G + g) * 4);
+    }
+#pragma unroll
+    for (int u = 0; u < RB; ++u)
+      if (g0 + t + kRowMergeThreads * u < G)
+        rec_merge(m, s, w, a, rec[u][0], rec[u][1], rec[u][2], __float_as_int(rec[u][3]),
+                  inv_tau);
   }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    const float m2 = __shfl_xor(m, off), s2 = __shfl_xor(s, off), w2 = __shfl_xor(w, off);
+    const int a2 = __shfl_xor(a, off);
+    rec_merge(m, s, w, a, m2, s2, w2, a2, inv_tau);
+  }
+  __shared__ floatx4_t wr[kRowMergeThreads / 64];
+  if (lane == 0) wr[wave] = floatx4_t{m, s, w, __int_as_float(a)};
+  __syncthreads();
+  if (t != 0) return;
+  m = kNegInf;
+  s = w = 0.f;
+  a = 0x7fffffff;
+  for (int i = 0; i < kRowMergeThreads / 64; ++i)
+    rec_merge(m, s, w, a, wr[i][0], wr[i][1], wr[i][2], __float_as_int(wr[i][3]), inv_tau);
+  row_stats[(size_t)r * 3 + 0] = m;
+  row_stats[(size_t)r * 3 + 1] = s;
+  row_stats[(size_t)r * 3 + 2] = w;
+  row_argmax[r] = a;
 }
 
 // Tile configuration: waves per workgroup (= 16-column stripes), m-tiles
@@ -726,9 +739,10 @@ hipError_t launch_split(GemmParams p, hipStream_t st) {
 }  // namespace
 
 int lm_head_blocks(int N, int M) {
-  const int gc = 16 * config_for(M, EPI_LM).wv;
-  return (N + gc - 1) / gc;
+  const Config c = config_for(M, EPI_LM);
+  return (N + 16 * c.wv - 1) / (16 * c.wv) * c.wv;
 }
+int lm_record_slots(int N) { return (N + 15) / 16 + 8; }
 int gemm_groups_max(int N) { return (N + 63) / 64; }
 int gemm_passes_max(int M) { return (M + 47) / 48; }
 
@@ -801,7 +815,7 @@ hipError_t launch_lm_head(GemmParams p, float* row_stats, int* row_argmax, hipSt
   const int KS = lm_splits_for(p.M);
   hipError_t e = p.f32 ? launch_main<F32, EPI_LM>(p, KS, st) : launch_main<BF16, EPI_LM>(p, KS, st);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(row_stats_merge_kernel, dim3(p.M), dim3(64), 0, st, p.part,
+  hipLaunchKernelGGL(row_stats_merge_kernel, dim3(p.M), dim3(kRowMergeThreads), 0, st, p.part,
                      lm_head_blocks(p.N, p.M), p.inv_tau, row_stats, row_argmax);
   return hipGetLastError();
 }
