@@ -106,14 +106,13 @@ __global__ void pack_weight_kernel(const typename ET::storage* __restrict__ W, i
 // QKV epilogue for one rotation pair (packed columns c1, c1 + 8) of row r.
 template <class ET>
 __device__ __forceinline__ void qkv_finish(const GemmParams& p, int r, int c1, int pos,
-                                           float x1, float x2) {
+                                           double inv_freq, float x1, float x2) {
   using St = typename ET::storage;
   const int Dh = p.Dh, half = Dh >> 1;
   const int blk = c1 / Dh, nl = c1 - blk * Dh;
   const int i = 8 * (nl >> 4) + (nl & 7);
   const int which = blk / p.H, h = blk - which * p.H;
   if (which < 2) {
-    const double inv_freq = exp(-(2.0 * i / Dh) * p.log_theta);
     const double turns = (double)pos * inv_freq * 0.15915494309189535;   // 1/(2 pi)
     const float ang = (float)((turns - rint(turns)) * 6.283185307179586);
     float sn, cs;
@@ -127,6 +126,14 @@ __device__ __forceinline__ void qkv_finish(const GemmParams& p, int r, int c1, i
   St* o = dst + ((size_t)r * p.H + h) * Dh + i;
   o[0] = ET::from_float(x1);
   o[half] = ET::from_float(x2);
+}
+
+// theta^(-2i/Dh) of the rotation pair whose first packed column is c1
+// (fp64; the same for every row, so computed once per column).
+__device__ __forceinline__ double rope_inv_freq(const GemmParams& p, int c1) {
+  const int nl = c1 % p.Dh;
+  const int i = 8 * (nl >> 4) + (nl & 7);
+  return exp(-(2.0 * i / p.Dh) * p.log_theta);
 }
 
 // y = x + acc, x = E[token of row r]: written as fp32 and storage type.
@@ -302,6 +309,7 @@ __global__ __launch_bounds__(64 * WV, (WV == 4 && D <= 8) ? 4 : 2) void node_gem
         }
       if constexpr (EPI == EPI_QKV) {
         // the rotation partner of packed column col is col + 8, held by lane li + 8
+        const double inv_freq = rope_inv_freq(p, min(col, p.N - 1));
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
@@ -309,7 +317,7 @@ __global__ __launch_bounds__(64 * WV, (WV == 4 && D <= 8) ? 4 : 2) void node_gem
             const float other = __shfl_xor(acc[mt][j], 8);
             const int r = m0 + 16 * mt + 4 * lq + j;
             if (li < 8 && r < p.M && col < p.N)
-              qkv_finish<ET>(p, r, col, rv[mt][j], acc[mt][j], other);
+              qkv_finish<ET>(p, r, col, rv[mt][j], inv_freq, acc[mt][j], other);
           }
       } else {
         const int cc = min(col, p.N - 1);
@@ -348,9 +356,11 @@ __global__ __launch_bounds__(64 * WV, (WV == 4 && D <= 8) ? 4 : 2) void node_gem
       }
     if (!fused) return;
     // The last of the KS workgroups of this (group, pass) finishes it: every
-    // thread loads all the slices of its outputs (and the row data they
-    // need) before it uses any, then sums them in slice order.
-    if (!last_to_arrive(p.counters + g * gridDim.z + blockIdx.z, KS)) return;
+    // thread loads all the slices of its outputs before it uses any, then
+    // sums them in slice order. The row data of a thread's first batch of
+    // rows (positions, residual rows) is loaded before the hand-off, so its
+    // latency overlaps the count; workgroups that turn out not to be last
+    // drop it.
     constexpr int NT = 64 * WV;
     const size_t sstride = (size_t)p.M * GC;
     const float* gpart = p.part + (size_t)g * KS * p.M * GC;
@@ -362,15 +372,20 @@ __global__ __launch_bounds__(64 * WV, (WV == 4 && D <= 8) ? 4 : 2) void node_gem
       static_assert(RPT % RB == 0, "row batches");
       const int pi = threadIdx.x % PG, rl = threadIdx.x / PG;
       const int cl = 16 * (pi >> 3) + (pi & 7), c1 = n0 + cl;
+      int pos[RB];
+      auto load_pos = [&](int i0) {
+#pragma unroll
+        for (int i = 0; i < RB; ++i) pos[i] = p.pos[min(m0 + rl + RL * (i0 + i), p.M - 1)];
+      };
+      load_pos(0);
+      const double inv_freq = rope_inv_freq(p, min(c1, p.N - 1));
+      if (!last_to_arrive(p.counters + g * gridDim.z + blockIdx.z, KS)) return;
 #pragma unroll 1
       for (int i0 = 0; i0 < RPT; i0 += RB) {
+        if (i0 > 0) load_pos(i0);
         float x1[RB], x2[RB];
-        int pos[RB];
 #pragma unroll
-        for (int i = 0; i < RB; ++i) {
-          x1[i] = x2[i] = 0.f;
-          pos[i] = p.pos[min(m0 + rl + RL * (i0 + i), p.M - 1)];
-        }
+        for (int i = 0; i < RB; ++i) x1[i] = x2[i] = 0.f;
         for (int s0 = 0; s0 < KS; s0 += 2) {
           float v1[2][RB], v2[2][RB];
 #pragma unroll
@@ -395,7 +410,7 @@ __global__ __launch_bounds__(64 * WV, (WV == 4 && D <= 8) ? 4 : 2) void node_gem
 #pragma unroll
           for (int i = 0; i < RB; ++i) {
             const int r = m0 + rl + RL * (i0 + i);
-            if (r < p.M) qkv_finish<ET>(p, r, c1, pos[i], x1[i], x2[i]);
+            if (r < p.M) qkv_finish<ET>(p, r, c1, pos[i], inv_freq, x1[i], x2[i]);
           }
       }
     } else if constexpr (EPI == EPI_OPROJ) {
@@ -405,16 +420,24 @@ __global__ __launch_bounds__(64 * WV, (WV == 4 && D <= 8) ? 4 : 2) void node_gem
       static_assert(RPT % RB == 0, "row batches");
       const int cl = threadIdx.x % GC, rl = threadIdx.x / GC;
       const int n = min(n0 + cl, p.N - 1);
+      float x[RB];
+      auto load_x = [&](int i0) {
+        int tok[RB];
+#pragma unroll
+        for (int i = 0; i < RB; ++i)
+          tok[i] = min(max(p.tokens[min(m0 + rl + RL * (i0 + i), p.M - 1)], 0), p.a_nrows - 1);
+#pragma unroll
+        for (int i = 0; i < RB; ++i)
+          x[i] = ET::load1(reinterpret_cast<const St*>(p.E) + (size_t)tok[i] * p.N + n);
+      };
+      load_x(0);
+      if (!last_to_arrive(p.counters + g * gridDim.z + blockIdx.z, KS)) return;
 #pragma unroll 1
       for (int i0 = 0; i0 < RPT; i0 += RB) {
-        float x[RB], acc_s[RB];
+        if (i0 > 0) load_x(i0);
+        float acc_s[RB];
 #pragma unroll
-        for (int i = 0; i < RB; ++i) {
-          const int r = min(m0 + rl + RL * (i0 + i), p.M - 1);
-          const int tok = min(max(p.tokens[r], 0), p.a_nrows - 1);
-          x[i] = ET::load1(reinterpret_cast<const St*>(p.E) + (size_t)tok * p.N + n);
-          acc_s[i] = 0.f;
-        }
+        for (int i = 0; i < RB; ++i) acc_s[i] = 0.f;
         for (int s0 = 0; s0 < KS; s0 += 4) {
           float v[4][RB];
 #pragma unroll
@@ -563,7 +586,7 @@ __global__ __launch_bounds__(256) void qkv_epilogue_kernel(GemmParams p, int KS)
   if (c1 >= p.N) return;
   const float x1 = sum_partials(p, r, c1, KS);
   const float x2 = sum_partials(p, r, c1 + 8, KS);
-  qkv_finish<ET>(p, r, c1, p.pos[r], x1, x2);
+  qkv_finish<ET>(p, r, c1, p.pos[r], rope_inv_freq(p, c1), x1, x2);
 }
 
 template <class ET>
