@@ -387,6 +387,12 @@ __global__ __launch_bounds__(kMergeThreads) void heads_merge_kernel(
   __shared__ float sv[NW][MAXS_LDS];
   __shared__ int si[NW][MAXS_LDS];
 
+  // wave 0's log-sum-exp records, loaded with the candidates when they fit
+  // in registers
+  const bool lse_early = lse != nullptr && wave == 0 && G <= 64 * kLseRegs;
+  float lm[kLseRegs], ls[kLseRegs];
+  if (lse_early) lse_load(part_m + rec0, part_s + rec0, G, lm, ls);
+
   float lv[SMAX];
   int li[SMAX];
 #pragma unroll
@@ -433,7 +439,7 @@ __global__ __launch_bounds__(kMergeThreads) void heads_merge_kernel(
 
   // log-sum-exp of the G (max, sum) records: wave 0, fixed order
   if (lse != nullptr && wave == 0) {
-    const float v = wave_lse(part_m + rec0, part_s + rec0, G);
+    const float v = lse_early ? lse_of(lm, ls, G) : wave_lse(part_m + rec0, part_s + rec0, G);
     if (lane == 0) lse[(size_t)b * K + k] = v;
   }
   __syncthreads();

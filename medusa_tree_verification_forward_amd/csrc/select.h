@@ -123,8 +123,39 @@ __device__ __forceinline__ void wave_topk(const float* __restrict__ val,
 // log sum_g s_g e^{m_g} of G partial records (m_g, s_g) in one wave
 // (natural log), returned to every lane: lane l takes records l + 64 u in
 // u order, then a fixed-order wave maximum and sum.
+constexpr int kLseRegs = 4;   // records per lane held in registers (G <= 256)
+__device__ __forceinline__ void lse_load(const float* __restrict__ pm,
+                                         const float* __restrict__ ps, int G,
+                                         float (&m)[kLseRegs], float (&sv)[kLseRegs]) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int u = 0; u < kLseRegs; ++u) {
+    const int g = min(lane + 64 * u, G - 1);
+    m[u] = pm[g];
+    sv[u] = ps[g];
+  }
+}
+__device__ __forceinline__ float lse_of(const float (&m)[kLseRegs], const float (&sv)[kLseRegs],
+                                        int G) {
+  const int lane = threadIdx.x & 63;
+  float mx = -__builtin_huge_valf();
+#pragma unroll
+  for (int u = 0; u < kLseRegs; ++u)
+    if (lane + 64 * u < G) mx = fmaxf(mx, m[u]);
+  mx = wave_max(mx);
+  float s = 0.f;
+#pragma unroll
+  for (int u = 0; u < kLseRegs; ++u)
+    if (lane + 64 * u < G && m[u] != -__builtin_huge_valf()) s += sv[u] * exp_e(m[u] - mx);
+  return mx + __logf(wave_sum(s));
+}
 __device__ __forceinline__ float wave_lse(const float* __restrict__ pm,
                                           const float* __restrict__ ps, int G) {
+  if (G <= 64 * kLseRegs) {
+    float m[kLseRegs], sv[kLseRegs];
+    lse_load(pm, ps, G, m, sv);
+    return lse_of(m, sv, G);
+  }
   constexpr int kBatch = 4;
   const int lane = threadIdx.x & 63;
   float mx = -__builtin_huge_valf();
