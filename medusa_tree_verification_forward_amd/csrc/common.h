@@ -140,6 +140,16 @@ __device__ __forceinline__ void lds_barrier() {
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
 }
 
+// Makes this wave's LDS writes visible to its own other lanes: the LDS
+// queue of one wave completes in order, so waiting for its writes and
+// keeping the compiler from moving accesses across is enough.
+__device__ __forceinline__ void wave_lds_sync() {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt 0
+  __builtin_amdgcn_wave_barrier();
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
 // ---- hand-off between the workgroups of one launch -----------------------------
 // The L2 caches of the XCDs are not coherent with each other. Relaxed atomic
 // loads and stores at agent scope are: they compile to ordinary vector

@@ -108,10 +108,10 @@ struct GemmParams {
   int* counters;               // fused epilogue: one zeroed counter per (group, pass)
   int group_cols;              // set by the launcher
   int fused;                   // set by the launcher
-  int kmajor;                  // set by the launcher: packed tile order
+  int kg_shift;                // set by the launcher: log2 of the k-tiles per packed run
   float* lm_slices;            // LM head split over K: [groups][KS][48][cols] fp32
 };
-bool packed_kmajor();
+int packed_kg_shift();
 // Weights W[rows][K] of the node GEMMs are packed into MFMA tiles (see
 // node_gemm.hip) before use; pair_dh = Dh reorders the rows of each head
 // into rotation pairs (W_qkv), 0 keeps them in order.
@@ -123,7 +123,7 @@ int gemm_passes_max(int M);                // row passes (upper bound)
 int lm_head_blocks(int N, int M);          // row records of the LM head (16-column stripes)
 int lm_record_slots(int N);                // upper bound of lm_head_blocks over the configs
 int lm_splits_for(int M);                  // K slices of the LM head
-int gemm_splits(int N, int K, bool f32);   // K slices of the QKV / output projection GEMMs
+int gemm_splits(int epi, int N, int K, bool f32);   // K slices of the QKV / output projection
 hipError_t launch_qkv(const GemmParams& p, hipStream_t st);
 hipError_t launch_oproj(const GemmParams& p, hipStream_t st);
 hipError_t launch_lm_head(GemmParams p, float* row_stats, int* row_argmax, hipStream_t st);

@@ -79,12 +79,23 @@ __device__ __forceinline__ int packed_source_row(int n, int pair_dh) {
   return blk * pair_dh + (li < 8 ? 8 * tt + li : (pair_dh >> 1) + 8 * tt + li - 8);
 }
 
+// Tile order: k-tiles are grouped in runs of 2^sh; group G (k-tiles
+// k0 = G 2^sh .. k0 + gs - 1, gs = 2^sh except for a short last group) of
+// every stripe follows the whole group G - 1, stripe after stripe, and the
+// gs tiles of one stripe in a group are adjacent. sh = 0 is k-major order,
+// 2^sh >= nkt stripe-major.
+__device__ __forceinline__ size_t packed_tile(int nt, int kt, int nkt, int ntiles, int sh) {
+  const int k0 = (kt >> sh) << sh;
+  const int gs = min(1 << sh, nkt - k0);
+  return (size_t)k0 * ntiles + (size_t)nt * gs + (kt - k0);
+}
+
 // Packing: piece q of the output is lane l = q % 64 of tile q / 64; tile
-// (nt, kt) = (tile / nkt, tile % nkt) holds packed rows 16 nt + l % 16, k
-// elements KT kt + PV (l / 16) .. + PV - 1 (KT = 4 PV). Rows >= rows are 0.
+// (nt, kt) (order above) holds packed rows 16 nt + l % 16, k elements
+// KT kt + PV (l / 16) .. + PV - 1 (KT = 4 PV). Rows >= rows are 0.
 template <class ET>
 __global__ void pack_weight_kernel(const typename ET::storage* __restrict__ W, int rows, int K,
-                                   int pair_dh, int kmajor, u32x4_t* __restrict__ out,
+                                   int pair_dh, int sh, u32x4_t* __restrict__ out,
                                    size_t pieces) {
   constexpr int PV = ET::kPerVec, KT = 4 * PV;
   const size_t q = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -92,8 +103,11 @@ __global__ void pack_weight_kernel(const typename ET::storage* __restrict__ W, i
   const int nkt = K / KT, ntiles = (rows + 15) / 16;
   const size_t tile = q >> 6;
   const int l = (int)(q & 63);
-  const int nt = kmajor ? (int)(tile % ntiles) : (int)(tile / nkt);
-  const int kt = kmajor ? (int)(tile / ntiles) : (int)(tile % nkt);
+  const size_t full = (size_t)ntiles << sh;   // tiles of a whole group
+  const int k0 = (int)(tile / full) << sh;
+  const int gs = min(1 << sh, nkt - k0);
+  const int rem = (int)(tile - (size_t)k0 * ntiles);
+  const int nt = rem / gs, kt = k0 + rem % gs;
   const int n = 16 * nt + (l & 15);
   u32x4_t v = {0u, 0u, 0u, 0u};
   if (n < rows) {
@@ -179,7 +193,7 @@ __device__ __forceinline__ float sum_partials(const GemmParams& p, int r, int n,
 }
 
 template <class ET, int WV, int MT, int CH, int D, int EPI>
-__global__ __launch_bounds__(64 * WV, (WV == 4 && D <= 8) ? 4 : 2) void node_gemm_kernel(
+__global__ __launch_bounds__(64 * WV, (WV == 4 && D <= 8) ? 4 : (WV <= 3 ? 1 : 2)) void node_gemm_kernel(
     GemmParams p) {
   using St = typename ET::storage;
   constexpr int PV = ET::kPerVec, KT = 4 * PV;   // k elements per tile
@@ -198,16 +212,34 @@ __global__ __launch_bounds__(64 * WV, (WV == 4 && D <= 8) ? 4 : 2) void node_gem
   const int ntiles = (p.N + 15) >> 4;
   const int n0 = g * GC;
   const int col = n0 + 16 * wave + li;
-  // tile (nt, kt) sits at nt * nkt + kt (stripe-major) or kt * ntiles + nt
-  // (k-major); consecutive k-tiles of a stripe are `wstep` pieces apart
-  const int nt = min(g * WV + wave, ntiles - 1);
-  const size_t wstep = p.kmajor ? (size_t)ntiles * 64 : 64;
-  const u32x4_t* __restrict__ wp =
-      reinterpret_cast<const u32x4_t*>(p.W) +
-      (p.kmajor ? ((size_t)kt_lo * ntiles + nt) : ((size_t)nt * nkt + kt_lo)) * 64 + lane;
+  // this wave's stripe (wave-uniform) and its k-tile s of the slice
+  const int nt = min(g * WV + __builtin_amdgcn_readfirstlane(wave), ntiles - 1);
+  const u32x4_t* __restrict__ W4 = reinterpret_cast<const u32x4_t*>(p.W) + lane;
+  auto wtile = [&](int s) { return W4 + packed_tile(nt, kt_lo + s, nkt, ntiles, p.kg_shift) * 64; };
 
   __shared__ u32x4_t sA0[CH][MT][64];
   __shared__ u32x4_t sA1[CH][MT][64];
+
+  // LM head: node e of the pass's sequences (row of its parent, its token),
+  // node = -1 for roots and past the end
+  const int rows_hi = min(p.M, m0 + 16 * MT);
+  const int bl = m0 / max(p.T, 1), bh = (rows_hi - 1) / max(p.T, 1);
+  const int nchild = EPI == EPI_LM ? (bh - bl + 1) * p.T : 0;
+  auto child_of = [&](int e, int& r, int& tok, int& node) {
+    r = -1;
+    tok = -1;
+    node = -1;
+    if (e < nchild) {
+      const int b = bl + e / p.T, cnode = e % p.T;
+      if (cnode >= 1) {
+        node = b * p.T + cnode;
+        tok = p.tokens[node];
+        r = b * p.T + min(max(p.parent[cnode], 0), p.T - 1);
+      }
+    }
+  };
+  int ch_r = -1, ch_tok = -1, ch_node = -1;
+  if constexpr (EPI == EPI_LM) child_of(lane, ch_r, ch_tok, ch_node);
 
   // A fragment f = wave + WV i of a chunk is (k-tile f / MT, m-tile f % MT)
   const St* asrc[NAW];
@@ -240,11 +272,44 @@ __global__ __launch_bounds__(64 * WV, (WV == 4 && D <= 8) ? 4 : 2) void node_gem
   for (int mt = 0; mt < MT; ++mt) acc[mt] = floatx4_t{0.f, 0.f, 0.f, 0.f};
   u32x4_t wr[D];
 
+  // Row data of the one-slice QKV / output-projection epilogue: positions
+  // (and the column's RoPE frequency) or residual values of the lane's rows
+  // m0 + 16 mt + 4 lq + j. Configurations with at most three waves run one
+  // workgroup per compute unit and hold them through the stream.
+  constexpr bool kEarlyRows = (EPI == EPI_QKV || EPI == EPI_OPROJ) && WV <= 3;
+  int rv[MT][4];
+  float x[MT][4];
+  double inv_freq = 0.0;
+  auto load_rows = [&]() {
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int r = min(m0 + 16 * mt + 4 * lq + j, p.M - 1);
+        rv[mt][j] = EPI == EPI_QKV ? p.pos[r] : min(max(p.tokens[r], 0), p.a_nrows - 1);
+      }
+    if constexpr (EPI == EPI_QKV) inv_freq = rope_inv_freq(p, min(col, p.N - 1));
+  };
+  auto load_residual = [&]() {
+    const int cc = min(col, p.N - 1);
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        x[mt][j] = ET::load1(reinterpret_cast<const St*>(p.E) + (size_t)rv[mt][j] * p.N + cc);
+  };
+  if constexpr (kEarlyRows) {
+    if (KS == 1) {
+      load_rows();
+      if constexpr (EPI == EPI_OPROJ) load_residual();
+    }
+  }
+
   const int nch = (nloc + CH - 1) / CH;
   load_a(0, ra0);
   load_a(1, ra1);
 #pragma unroll
-  for (int j = 0; j < D; ++j) wr[j] = load16_stream(wp + (size_t)min(j, nloc - 1) * wstep);
+  for (int j = 0; j < D; ++j) wr[j] = load16_stream(wtile(min(j, nloc - 1)));
   store_a(sA0, ra0);
   load_a(2, ra0);
   lds_barrier();
@@ -268,7 +333,7 @@ __global__ __launch_bounds__(64 * WV, (WV == 4 && D <= 8) ? 4 : 2) void node_gem
         const u32x4_t b = wr[(R0 + j) % D];
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) acc[mt] = frag_mfma<ET>(cur[j][mt][lane], b, acc[mt]);
-        if (S || s + D < nloc) wr[(R0 + j) % D] = load16_stream(wp + (size_t)(s + D) * wstep);
+        if (S || s + D < nloc) wr[(R0 + j) % D] = load16_stream(wtile(s + D));
       }
       // one k-tile at a time: hoisting later LDS reads only raises pressure
       __builtin_amdgcn_sched_barrier(0);
@@ -298,18 +363,11 @@ __global__ __launch_bounds__(64 * WV, (WV == 4 && D <= 8) ? 4 : 2) void node_gem
   if constexpr (EPI == EPI_QKV || EPI == EPI_OPROJ) {
     if (KS == 1) {
       // One slice: finish straight from the accumulators (lane: column col,
-      // rows m0 + 16 mt + 4 lq + j), the row data loaded before any store.
-      int rv[MT][4];
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int r = min(m0 + 16 * mt + 4 * lq + j, p.M - 1);
-          rv[mt][j] = EPI == EPI_QKV ? p.pos[r] : min(max(p.tokens[r], 0), p.a_nrows - 1);
-        }
+      // rows m0 + 16 mt + 4 lq + j), the row data loaded before any store
+      // (before the stream, where the configuration has the registers).
+      if constexpr (!kEarlyRows) load_rows();
       if constexpr (EPI == EPI_QKV) {
         // the rotation partner of packed column col is col + 8, held by lane li + 8
-        const double inv_freq = rope_inv_freq(p, min(col, p.N - 1));
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
@@ -320,13 +378,7 @@ __global__ __launch_bounds__(64 * WV, (WV == 4 && D <= 8) ? 4 : 2) void node_gem
               qkv_finish<ET>(p, r, col, rv[mt][j], inv_freq, acc[mt][j], other);
           }
       } else {
-        const int cc = min(col, p.N - 1);
-        float x[MT][4];
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-          for (int j = 0; j < 4; ++j)
-            x[mt][j] = ET::load1(reinterpret_cast<const St*>(p.E) + (size_t)rv[mt][j] * p.N + cc);
+        if constexpr (!kEarlyRows) load_residual();
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
@@ -499,81 +551,76 @@ __global__ __launch_bounds__(64 * WV, (WV == 4 && D <= 8) ? 4 : 2) void node_gem
 #pragma unroll
         for (int j = 0; j < 4; ++j) acc[mt][j] = tot[mt][j];
     }
-    const bool cv = col < p.N;
+    // The wave's logit tile goes through LDS, 48 rows (MG m-tiles) at a time,
+    // so that lane r owns row r of the group: per row and 16-column stripe
+    // (max, lowest argmax, S, W) scanned over the columns in order, one
+    // record per row; then the tree nodes whose parent row is in the group.
+    constexpr int MG = MT < 3 ? MT : 3;
+    static_assert(MT % MG == 0, "row groups");
+    constexpr int LTS = 20;   // row stride (floats) of the tile: 16-byte rows
+    __shared__ float lt[WV][16 * MG][LTS];
+    const int c0 = n0 + 16 * wave;
+    const int nv = min(16, p.N - c0);   // valid columns of the stripe
+    const int stripes = gridDim.x * WV;
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
+    for (int mq = 0; mq < MT; mq += MG) {
+      if (mq > 0) wave_lds_sync();   // the previous group's reads are done
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int rr = 16 * mt + 4 * lq + j;
-        const int r = m0 + rr;
-        // (max, lowest argmax) over this wave's 16 columns of the row
-        float bv = cv ? acc[mt][j] : kNegInf;
-        int bi = cv ? col : 0x7fffffff;
+      for (int mt = 0; mt < MG; ++mt)
 #pragma unroll
-        for (int step = 0; step < 4; ++step) {
-          float ov;
-          int oi;
-          if (step == 0) { ov = dpp<kDppQuadXor1>(bv); oi = dppi<kDppQuadXor1>(bi); }
-          else if (step == 1) { ov = dpp<kDppQuadXor2>(bv); oi = dppi<kDppQuadXor2>(bi); }
-          else if (step == 2) { ov = dpp<kDppRowRor4>(bv); oi = dppi<kDppRowRor4>(bi); }
-          else { ov = dpp<kDppRowRor8>(bv); oi = dppi<kDppRowRor8>(bi); }
-          if (better(ov, oi, bv, bi)) { bv = ov; bi = oi; }
+        for (int j = 0; j < 4; ++j) lt[wave][16 * mt + 4 * lq + j][li] = acc[mq + mt][j];
+      wave_lds_sync();
+      const int g0 = m0 + 16 * mq;   // first row of the group
+      if (lane < 16 * MG) {
+        const int r = g0 + lane;
+        float v[16];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const float4 x = *reinterpret_cast<const float4*>(&lt[wave][lane][4 * q]);
+          v[4 * q] = x.x;
+          v[4 * q + 1] = x.y;
+          v[4 * q + 2] = x.z;
+          v[4 * q + 3] = x.w;
         }
+        float bv = kNegInf;
+        int bi = 0x7fffffff;
+#pragma unroll
+        for (int c = 0; c < 16; ++c)
+          if (c < nv && v[c] > bv) {
+            bv = v[c];
+            bi = c0 + c;
+          }
         float sv = 0.f, wv = 0.f;
-        if (cv) {
-          const float z = (acc[mt][j] - bv) * p.inv_tau;
-          const float e = exp_e(z);
-          sv = e;
-          wv = e * z;
-        }
-        sv = row16_sum(sv);
-        wv = row16_sum(wv);
-        // one record per (row, 16-column stripe): rows 4 lq + j of the wave
-        // are held by lanes li == 0
-        if (li == 0 && r < p.M) {
-          const int stripes = gridDim.x * WV;
+#pragma unroll
+        for (int c = 0; c < 16; ++c)
+          if (c < nv) {
+            const float z = (v[c] - bv) * p.inv_tau;
+            const float e = exp_e(z);
+            sv += e;
+            wv += e * z;
+          }
+        if (r < p.M)
           *reinterpret_cast<float4*>(p.part + ((size_t)r * stripes + g * WV + wave) * 4) =
               make_float4(bv, sv, wv, __int_as_float(bi));
-        }
-        if (p.logits_out && cv && r < p.M) p.logits_out[(size_t)r * p.N + col] = acc[mt][j];
       }
-    // logit of each tree node's token under its parent's row (this wave's columns)
-    const int rows_hi = min(p.M, m0 + 16 * MT);
-    const int c0 = n0 + 16 * wave;
-    const int bl = m0 / p.T, bh = (rows_hi - 1) / p.T;
-    const int nchild = (bh - bl + 1) * p.T;
-    for (int e0 = 0; e0 < nchild; e0 += 64) {
-      const int e = e0 + lane;
-      int r = -1, tok = -1, node = -1;
-      bool hit = false;
-      if (e < nchild) {
-        const int b = bl + e / p.T, cnode = e % p.T;
-        if (cnode >= 1) {
-          node = b * p.T + cnode;
-          tok = p.tokens[node];
-          r = b * p.T + min(max(p.parent[cnode], 0), p.T - 1);
-          hit = tok >= c0 && tok < c0 + 16 && r >= m0 && r < rows_hi;
-        }
-      }
-      uint64_t mask = __ballot(hit);
-      while (mask) {
-        const int src = __ffsll((unsigned long long)mask) - 1;
-        mask &= mask - 1;
-        const int hr = __builtin_amdgcn_readlane(r, src);
-        const int ht = __builtin_amdgcn_readlane(tok, src);
-        const int hn = __builtin_amdgcn_readlane(node, src);
-        const int rr = hr - m0;
-        const int want_li = ht - c0, want_mt = rr >> 4, want_lq = (rr & 15) >> 2,
-                  want_j = rr & 3;
-        float v = 0.f;
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-          for (int j = 0; j < 4; ++j)
-            if (mt == want_mt && j == want_j) v = acc[mt][j];
-        if (li == want_li && lq == want_lq) p.child_logit[hn] = v;
+      // logit of each tree node's token under its parent's row (this wave's
+      // columns); the first 64 nodes' (row, token) were loaded before the stream
+      const int g1 = min(rows_hi, g0 + 16 * MG);
+      for (int e0 = 0; e0 < nchild; e0 += 64) {
+        int r = ch_r, tok = ch_tok, node = ch_node;
+        if (e0 > 0) child_of(e0 + lane, r, tok, node);
+        if (node >= 0 && tok >= c0 && tok < c0 + 16 && r >= g0 && r < g1)
+          p.child_logit[node] = lt[wave][r - g0][tok - c0];
       }
     }
+    if (p.logits_out && col < p.N)
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int r = m0 + 16 * mt + 4 * lq + j;
+          if (r < p.M) p.logits_out[(size_t)r * p.N + col] = acc[mt][j];
+        }
   }
 }
 
@@ -647,20 +694,37 @@ struct Config {
   int wv, mt, ch, d;
 };
 
-// MEDUSA_GEMM_CFG ("wv,ch,d", default "4,4,8") picks the 48-row tile of the
-// QKV and output projections: waves per workgroup, k-tiles per A chunk and
-// weight loads in flight per wave (4,4,8; 8,8,8; 8,8,16 or 4,8,16).
-Config small_config() {
-  static const Config v = [] {
-    const char* s = getenv("MEDUSA_GEMM_CFG");
-    int wv = 4, ch = 4, d = 8;
-    if (s && *s) sscanf(s, "%d,%d,%d", &wv, &ch, &d);
-    if (wv == 8 && ch == 8 && d == 16) return Config{8, 3, 8, 16};
-    if (wv == 8 && ch == 8 && d == 8) return Config{8, 3, 8, 8};
-    if (wv == 4 && ch == 8 && d == 16) return Config{4, 3, 8, 16};
-    return Config{4, 3, 4, 8};
-  }();
-  return v;
+// The 48-row tile of the QKV and output projections: waves per workgroup,
+// k-tiles per A chunk, weight loads in flight per wave and K slices (0:
+// automatic). MEDUSA_QKV_CFG / MEDUSA_OPROJ_CFG ("wv,ch,d,ks"; one of the
+// (wv, ch, d) sets launch_main instantiates) fix it; otherwise, with 2 to 4
+// sixteen-column stripes per compute unit, one workgroup of 3 or 4 waves per
+// compute unit streams the whole K (no hand-off between workgroups), and
+// with fewer stripes 4-wave workgroups split K.
+struct SmallConfig {
+  Config c;
+  int ks;
+};
+SmallConfig parse_small(const char* env) {
+  const char* s = getenv(env);
+  if (!(s && *s)) return SmallConfig{{0, 0, 0, 0}, 0};
+  int wv = 0, ch = 0, d = 0, ks = 0;
+  if (sscanf(s, "%d,%d,%d,%d", &wv, &ch, &d, &ks) < 3) return SmallConfig{{0, 0, 0, 0}, 0};
+  const Config known[] = {{4, 3, 4, 8}, {4, 3, 8, 16}, {8, 3, 8, 8}, {8, 3, 8, 16},
+                          {3, 3, 8, 16}, {2, 3, 8, 16}};
+  for (const Config& k : known)
+    if (k.wv == wv && k.ch == ch && k.d == d) return SmallConfig{k, ks < 0 ? 0 : ks};
+  return SmallConfig{{0, 0, 0, 0}, 0};
+}
+SmallConfig small_config(int epi, int N) {
+  static const SmallConfig q = parse_small("MEDUSA_QKV_CFG");
+  static const SmallConfig o = parse_small("MEDUSA_OPROJ_CFG");
+  const SmallConfig& f = epi == EPI_QKV ? q : o;
+  if (f.c.wv) return f;
+  const int stripes = (N + 15) / 16, cus = device_cus();
+  if (stripes > 2 * cus && stripes <= 3 * cus) return SmallConfig{{3, 3, 8, 16}, 1};
+  if (stripes > 3 * cus && stripes <= 4 * cus) return SmallConfig{{4, 3, 8, 16}, 1};
+  return SmallConfig{{4, 3, 4, 8}, 0};
 }
 
 // MEDUSA_LM_CFG ("wv,ch", default "8,8"): waves per workgroup and k-tiles per
@@ -682,23 +746,29 @@ Config lm_config(int KS) {
   return KS > 1 ? Config{4, 3, 4, 8} : Config{8, 3, 8, 16};
 }
 
-Config config_for(int M, int epi) {
+Config config_for(int M, int N, int epi) {
   if (M <= 48) {
     if (epi == EPI_LM) return lm_config(lm_splits_for(M));
-    return small_config();
+    return small_config(epi, N).c;
   }
   return Config{8, 12, 4, 4};
 }
 
 }  // namespace
 
-// Packed tiles are ordered k-major: tile (nt, kt) at kt * ntiles + nt, so
-// the waves of a launch, which advance through k together, read adjacent
-// memory. MEDUSA_PACK_KMAJOR=0 selects stripe-major (nt * nkt + kt).
-bool packed_kmajor() {
-  static const bool v = [] {
-    const char* s = getenv("MEDUSA_PACK_KMAJOR");
-    return !(s && *s && atoi(s) == 0);
+// Packed tiles come in runs of 2^sh k-tiles per stripe, the runs of all
+// stripes for one range of k adjacent (packed_tile), so the waves of a launch,
+// which advance through k together, read nearby memory while each reads a
+// short contiguous run. MEDUSA_PACK_KGROUP (a power of two, default 1:
+// k-major) sets the run length; one at least the k-tile count is
+// stripe-major.
+int packed_kg_shift() {
+  static const int v = [] {
+    const char* s = getenv("MEDUSA_PACK_KGROUP");
+    const int g = s && *s ? atoi(s) : 1;
+    int sh = 0;
+    while (sh < 16 && (2 << sh) <= g) ++sh;
+    return sh;
   }();
   return v;
 }
@@ -718,11 +788,15 @@ bool fused_epilogue() {
 
 template <class ET, int EPI>
 hipError_t launch_main(const GemmParams& p, int KS, hipStream_t st) {
-  const Config c = config_for(p.M, EPI);
+  const Config c = config_for(p.M, p.N, EPI);
   const int groups = (p.N + 16 * c.wv - 1) / (16 * c.wv);
   const int passes = (p.M + 16 * c.mt - 1) / (16 * c.mt);
   dim3 grid(groups, KS, passes), block(64 * c.wv);
-  if (c.mt == 3 && c.wv == 4 && c.d == 16)
+  if (c.mt == 3 && c.wv == 3)
+    hipLaunchKernelGGL((node_gemm_kernel<ET, 3, 3, 8, 16, EPI>), grid, block, 0, st, p);
+  else if (c.mt == 3 && c.wv == 2)
+    hipLaunchKernelGGL((node_gemm_kernel<ET, 2, 3, 8, 16, EPI>), grid, block, 0, st, p);
+  else if (c.mt == 3 && c.wv == 4 && c.d == 16)
     hipLaunchKernelGGL((node_gemm_kernel<ET, 4, 3, 8, 16, EPI>), grid, block, 0, st, p);
   else if (c.mt == 3 && c.wv == 4)
     hipLaunchKernelGGL((node_gemm_kernel<ET, 4, 3, 4, 8, EPI>), grid, block, 0, st, p);
@@ -737,10 +811,10 @@ hipError_t launch_main(const GemmParams& p, int KS, hipStream_t st) {
 
 template <int EPI>
 hipError_t launch_split(GemmParams p, hipStream_t st) {
-  const int KS = gemm_splits(p.N, p.K, p.f32);
-  p.group_cols = 16 * config_for(p.M, EPI).wv;
+  const int KS = gemm_splits(EPI, p.N, p.K, p.f32);
+  p.group_cols = 16 * config_for(p.M, p.N, EPI).wv;
   p.fused = fused_epilogue();
-  p.kmajor = packed_kmajor();
+  p.kg_shift = packed_kg_shift();
   hipError_t e = p.f32 ? launch_main<F32, EPI>(p, KS, st) : launch_main<BF16, EPI>(p, KS, st);
   if (e != hipSuccess || p.fused || KS == 1) return e;
   if (EPI == EPI_QKV) {
@@ -762,11 +836,11 @@ hipError_t launch_split(GemmParams p, hipStream_t st) {
 }  // namespace
 
 int lm_head_blocks(int N, int M) {
-  const Config c = config_for(M, EPI_LM);
+  const Config c = config_for(M, N, EPI_LM);
   return (N + 16 * c.wv - 1) / (16 * c.wv) * c.wv;
 }
 int lm_record_slots(int N) { return (N + 15) / 16 + 8; }
-int gemm_groups_max(int N) { return (N + 63) / 64; }
+int gemm_groups_max(int N) { return (N + 15) / 16; }
 int gemm_passes_max(int M) { return (M + 47) / 48; }
 
 size_t packed_weight_bytes(int rows, int K, bool f32) {
@@ -780,28 +854,26 @@ hipError_t launch_pack_weight(bool f32, const void* W, int rows, int K, int pair
   const size_t blocks = (pieces + threads - 1) / threads;
   if (f32)
     hipLaunchKernelGGL(pack_weight_kernel<F32>, dim3((unsigned)blocks), dim3(threads), 0, st,
-                       static_cast<const float*>(W), rows, K, pair_dh, (int)packed_kmajor(),
+                       static_cast<const float*>(W), rows, K, pair_dh, packed_kg_shift(),
                        static_cast<u32x4_t*>(out), pieces);
   else
     hipLaunchKernelGGL(pack_weight_kernel<BF16>, dim3((unsigned)blocks), dim3(threads), 0, st,
-                       static_cast<const uint16_t*>(W), rows, K, pair_dh, (int)packed_kmajor(),
+                       static_cast<const uint16_t*>(W), rows, K, pair_dh, packed_kg_shift(),
                        static_cast<u32x4_t*>(out), pieces);
   return hipGetLastError();
 }
 
-// Slices of K: the smallest power of two that gives the grid at least
-// MEDUSA_GEMM_MIN_WAVES waves (default 1024, 4 per compute unit) while
-// every wave keeps at least 8 k-tiles per slice.
-int gemm_splits(int N, int K, bool f32) {
-  static const int forced = [] {
-    const char* s = getenv("MEDUSA_GEMM_SPLITS");
-    return s && *s ? atoi(s) : 0;
-  }();
+// Slices of K: the count the tile configuration fixes, else the smallest
+// power of two that gives the grid at least MEDUSA_GEMM_MIN_WAVES waves
+// (default 1024, 4 per compute unit); either way every wave keeps at least
+// 8 k-tiles per slice.
+int gemm_splits(int epi, int N, int K, bool f32) {
   static const int min_waves = [] {
     const char* s = getenv("MEDUSA_GEMM_MIN_WAVES");
     const int v = s && *s ? atoi(s) : 1024;
     return v < 1 ? 1 : (v > 65536 ? 65536 : v);
   }();
+  const int forced = small_config(epi, N).ks;
   const int stripes = (N + 15) / 16;
   const int nkt = K / (f32 ? 16 : 32);
   int ks = 1;
@@ -833,8 +905,8 @@ int lm_splits_for(int M) {
 }
 
 hipError_t launch_lm_head(GemmParams p, float* row_stats, int* row_argmax, hipStream_t st) {
-  p.kmajor = packed_kmajor();
-  p.group_cols = 16 * config_for(p.M, EPI_LM).wv;
+  p.kg_shift = packed_kg_shift();
+  p.group_cols = 16 * config_for(p.M, p.N, EPI_LM).wv;
   const int KS = lm_splits_for(p.M);
   hipError_t e = p.f32 ? launch_main<F32, EPI_LM>(p, KS, st) : launch_main<BF16, EPI_LM>(p, KS, st);
   if (e != hipSuccess) return e;
