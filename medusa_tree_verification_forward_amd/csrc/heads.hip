@@ -11,6 +11,8 @@
 // (lanes 0..s-1, best first) and their softmax statistics, and a workgroup
 // leaves one partial record per (sequence, head, row block). A small merge
 // kernel reduces the records of one (sequence, head) in a fixed order.
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 #include "select.h"
@@ -32,11 +34,22 @@ constexpr int kRing = 8;        // weight loads in flight per wave
 // The activation xs (fp32 in LDS, NB vectors of stride ldx, zero past d)
 // is read at the same positions; lanes past the end of a row read a valid
 // weight and a zero activation.
+//
+// bf16 weights with one or two activation vectors take the dot products on
+// the matrix cores: lane l gives its 8 weights as its B fragment and the 8
+// activations they multiply as its A fragment of a v_mfma_f32_16x16x32_bf16,
+// so the diagonal entry (n, n) of the product is the sum of the dot products
+// of lanes n, n + 16, n + 32, n + 48, and the trace over a row's chunks is
+// the row's dot product. The activation enters as two bf16 parts, x = hi +
+// lo (hi = bf16(x), lo = bf16(x - hi), together within 2^-17 |x|), one
+// product each; the vector ALUs then only keep the stream going.
 template <class ET, int NB>
 struct RowStream {
   using St = typename ET::storage;
   static constexpr int PV = ET::kPerVec;
   static constexpr int CW = 64 * PV;
+  static constexpr bool kMfma = std::is_same<ET, BF16>::value && NB <= 2;
+  using Acc = typename std::conditional<kMfma, floatx4_t, float>::type;
   const St* __restrict__ W;
   int rb, rstride, nrows, d, SPR, lane;
   int fr, fs;   // row / chunk of the next refill
@@ -69,9 +82,42 @@ struct RowStream {
 #pragma unroll
     for (int j = 0; j < kRing; ++j) refill(j);
   }
+  // Row value from the accumulated product: the sum of its diagonal, whose
+  // entry (n, n) sits in lane 20 q + j (n = 4 q + j) as element j.
+  __device__ __forceinline__ static float trace(const floatx4_t& c) {
+    const int l = threadIdx.x & 63, dj = (l & 15) - 4 * (l >> 4);
+    float v = 0.f;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) v = dj == j ? c[j] : v;
+    return wave_sum(v);
+  }
   template <bool GUARD>
   __device__ __forceinline__ void step(int t, int j, int total, const float* xs, int ldx,
-                                       float (&acc)[NB], float (&win)[NB], int& cr, int& cs) {
+                                       Acc (&acc)[NB], float (&win)[NB], int& cr, int& cs) {
+    if constexpr (kMfma) {
+      if (!GUARD || t < total) {
+        // activation parts: hi plane [NB][ldx] then lo plane, bf16
+        const uint16_t* xh = reinterpret_cast<const uint16_t*>(xs) + cs * CW + PV * lane;
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+          const u32x4_t ah = *reinterpret_cast<const u32x4_t*>(xh + b * ldx);
+          const u32x4_t al = *reinterpret_cast<const u32x4_t*>(xh + (NB + b) * ldx);
+          acc[b] = mfma16x16x32_bf16(ah, wr[j], acc[b]);
+          acc[b] = mfma16x16x32_bf16(al, wr[j], acc[b]);
+        }
+        if (++cs == SPR) {
+#pragma unroll
+          for (int b = 0; b < NB; ++b) {
+            const float v = trace(acc[b]);
+            win[b] = lane == cr ? v : win[b];
+            acc[b] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+          }
+          cs = 0;
+          ++cr;
+        }
+      }
+      if (!GUARD || t + kRing < total) refill(j);
+    } else {
     if (!GUARD || t < total) {
       float wf[PV];
       ET::widen(wr[j], wf);
@@ -101,6 +147,7 @@ struct RowStream {
       }
     }
     if (!GUARD || t + kRing < total) refill(j);
+    }
   }
   // Consume the stream; lane l of win[b] receives row rb + l's dot product
   // with activation b (lanes >= nrows keep their old value). The steady
@@ -108,9 +155,9 @@ struct RowStream {
   // loads in flight; the last two rounds check their bounds.
   __device__ __forceinline__ void run(const float* xs, int ldx, float (&win)[NB]) {
     const int total = nrows * SPR;
-    float acc[NB];
+    Acc acc[NB];
 #pragma unroll
-    for (int b = 0; b < NB; ++b) acc[b] = 0.f;
+    for (int b = 0; b < NB; ++b) acc[b] = Acc{};
     int cr = 0, cs = 0;   // row / chunk being consumed
     int t0 = 0;
     for (; t0 + 2 * kRing <= total; t0 += kRing) {
@@ -124,12 +171,95 @@ struct RowStream {
   }
 };
 
+// Row stream for rows of exactly SPR chunks (d a multiple of CW): the ring
+// holds one row, so chunk s of the next row refills slot s as soon as chunk
+// s of the current row is consumed; addresses advance by one add per row and
+// the row's dot product is reduced once, after its last chunk. Same contract
+// as RowStream (lane l of win[b] receives the wave's row l).
+template <class ET, int NB, int SPR>
+struct RowStreamRows {
+  using St = typename ET::storage;
+  static constexpr int PV = ET::kPerVec;
+  static constexpr int CW = 64 * PV;
+  static constexpr bool kMfma = RowStream<ET, NB>::kMfma;
+  using Acc = typename RowStream<ET, NB>::Acc;
+  const St* __restrict__ p;   // this lane's piece of the row being consumed
+  size_t rstep;               // elements from one of the wave's rows to the next
+  int nrows;
+  u32x4_t wr[SPR];
+
+  __device__ __forceinline__ void start(const St* W, int rb, int rstride, int nrows_, int d,
+                                        int /*rb_ok*/) {
+    nrows = nrows_;
+    p = W + (size_t)rb * d + PV * (threadIdx.x & 63);
+    rstep = (size_t)rstride * d;
+    if (nrows > 0) {
+#pragma unroll
+      for (int s = 0; s < SPR; ++s) wr[s] = load16_stream(p + s * CW);
+    }
+  }
+  template <bool REFILL>
+  __device__ __forceinline__ void row(int i, const float* xs, int ldx, float (&win)[NB]) {
+    const int lane = threadIdx.x & 63;
+    const St* pn = p + rstep;
+    Acc acc[NB];
+#pragma unroll
+    for (int b = 0; b < NB; ++b) acc[b] = Acc{};
+#pragma unroll
+    for (int s = 0; s < SPR; ++s) {
+      if constexpr (kMfma) {
+        const uint16_t* xh = reinterpret_cast<const uint16_t*>(xs) + s * CW + PV * lane;
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+          const u32x4_t ah = *reinterpret_cast<const u32x4_t*>(xh + b * ldx);
+          const u32x4_t al = *reinterpret_cast<const u32x4_t*>(xh + (NB + b) * ldx);
+          acc[b] = mfma16x16x32_bf16(ah, wr[s], acc[b]);
+          acc[b] = mfma16x16x32_bf16(al, wr[s], acc[b]);
+        }
+      } else {
+        float wf[PV];
+        ET::widen(wr[s], wf);
+        const float* xp = xs + s * CW + PV * lane;
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+          float a = acc[b];
+#pragma unroll
+          for (int e = 0; e < PV; e += 4) {
+            const floatx4_t xv = *reinterpret_cast<const floatx4_t*>(xp + b * ldx + e);
+            a = fmaf(wf[e], xv[0], a);
+            a = fmaf(wf[e + 1], xv[1], a);
+            a = fmaf(wf[e + 2], xv[2], a);
+            a = fmaf(wf[e + 3], xv[3], a);
+          }
+          acc[b] = a;
+        }
+      }
+      if (REFILL) wr[s] = load16_stream(pn + s * CW);
+    }
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+      float v;
+      if constexpr (kMfma)
+        v = RowStream<ET, NB>::trace(acc[b]);
+      else
+        v = wave_sum(acc[b]);
+      win[b] = lane == i ? v : win[b];
+    }
+    p = pn;
+  }
+  __device__ __forceinline__ void run(const float* xs, int ldx, float (&win)[NB]) {
+    int i = 0;
+    for (; i + 1 < nrows; ++i) row<true>(i, xs, ldx, win);
+    if (i < nrows) row<false>(i, xs, ldx, win);
+  }
+};
+
 // Stage NB activation vectors (src + b * src_stride, d floats each) into LDS
 // as xs[b][0 .. ldx), zero past d. The first round of activation loads is
 // issued before the weight stream starts, so it is not queued behind it.
 // Ends with a barrier that leaves the weight loads in flight.
-template <class ET, int NB>
-__device__ __forceinline__ void stage_and_start(RowStream<ET, NB>& rs, const float* __restrict__ src,
+template <class ET, int NB, class Stream>
+__device__ __forceinline__ void stage_and_start(Stream& rs, const float* __restrict__ src,
                                                 size_t src_stride, int nb, int d, float* xs,
                                                 int ldx, const typename ET::storage* W, int rb,
                                                 int rstride, int nrows, int rb_ok) {
@@ -149,7 +279,22 @@ __device__ __forceinline__ void stage_and_start(RowStream<ET, NB>& rs, const flo
 #pragma unroll
     for (int u = 0; u < XR; ++u) {
       const int i4 = base + u * (int)blockDim.x + (int)threadIdx.x;
-      if (i4 < n4) *reinterpret_cast<floatx4_t*>(xs + 4 * i4) = v[u];
+      if (i4 >= n4) continue;
+      if constexpr (Stream::kMfma) {
+        // bf16 parts: hi = bf16(x), lo = bf16(x - hi)
+        uint32_t hb[4], lb[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          hb[e] = f32_to_bf16_bits(v[u][e]);
+          lb[e] = f32_to_bf16_bits(v[u][e] - __uint_as_float(hb[e] << 16));
+        }
+        uint16_t* xh = reinterpret_cast<uint16_t*>(xs);
+        *reinterpret_cast<uint2*>(xh + 4 * i4) = make_uint2(hb[0] | (hb[1] << 16), hb[2] | (hb[3] << 16));
+        *reinterpret_cast<uint2*>(xh + NB * ldx + 4 * i4) =
+            make_uint2(lb[0] | (lb[1] << 16), lb[2] | (lb[3] << 16));
+      } else {
+        *reinterpret_cast<floatx4_t*>(xs + 4 * i4) = v[u];
+      }
     }
   };
   floatx4_t v[XR];
@@ -185,8 +330,12 @@ __device__ __forceinline__ void wave_rows(int wi, int nw, int rpw, int total, bo
 // z[b][k][i] = h[b][i] + silu(sum_j W1[k][i][j] h[b][j] + b1[k][i])
 // Rows are numbered k*d + i over all heads; wave w of workgroup g streams
 // rows [(g*4 + w) * rpw, ... + rpw).
-template <class ET, int NB>
-__global__ __launch_bounds__(kHeadWaves * 64) void heads_w1_kernel(
+template <class ET, int NB, int SPR>
+using HeadStream =
+    typename std::conditional<SPR == 0, RowStream<ET, NB>, RowStreamRows<ET, NB, SPR>>::type;
+
+template <class ET, int NB, int SPR>
+__global__ __launch_bounds__(kHeadWaves * 64, 4) void heads_w1_kernel(
     const float* __restrict__ h, int B, int b0, int K, int d,
     const typename ET::storage* __restrict__ W1, const float* __restrict__ b1,
     float* __restrict__ z, int rpw, int interleave) {
@@ -199,7 +348,15 @@ __global__ __launch_bounds__(kHeadWaves * 64) void heads_w1_kernel(
   int rb, rstride, nrows;
   wave_rows(blockIdx.x * kHeadWaves + wave, gridDim.x * kHeadWaves, rpw, total, interleave != 0,
             rb, rstride, nrows);
-  RowStream<ET, NB> rs;
+  // the residual h of the lane's row, read before the stream
+  float hres[NB];
+  {
+    const int row = min(rb + min(lane, max(nrows - 1, 0)) * rstride, total - 1);
+    const int i = row - (row / d) * d;
+#pragma unroll
+    for (int b = 0; b < NB; ++b) hres[b] = h[(size_t)(b0 + min(b, nb - 1)) * d + i];
+  }
+  HeadStream<ET, NB, SPR> rs;
   stage_and_start<ET, NB>(rs, h + (size_t)b0 * d, d, nb, d, xs, ldx, W1, rb, rstride, nrows, 0);
   if (nrows == 0) return;
   float win[NB];
@@ -215,7 +372,7 @@ __global__ __launch_bounds__(kHeadWaves * 64) void heads_w1_kernel(
       if (b < nb) {
         const float u = win[b] + bias;
         const float sig = 1.f / (1.f + exp_e(-u));
-        z[((size_t)(b0 + b) * K + k) * d + i] = xs[b * ldx + i] + u * sig;
+        z[((size_t)(b0 + b) * K + k) * d + i] = hres[b] + u * sig;
       }
     }
   }
@@ -253,8 +410,8 @@ __device__ __forceinline__ void stats_merge(float& m, float& s, float m2, float 
 // grid = (G, K): wave w of block g of head k streams rows
 // [(g*4 + w) * rpw, ... + rpw) of head k.
 // Partial records: part_val/part_id [B][K][G][S], part_m/part_s [B][K][G].
-template <class ET, int NB>
-__global__ __launch_bounds__(kHeadWaves * 64) void heads_w2_kernel(
+template <class ET, int NB, int SPR>
+__global__ __launch_bounds__(kHeadWaves * 64, 4) void heads_w2_kernel(
     const float* __restrict__ z, int B, int b0, int K, int V, int d,
     const typename ET::storage* __restrict__ W2, int rpw, int S,
     float* __restrict__ head_logits, float* __restrict__ part_val, int* __restrict__ part_id,
@@ -268,7 +425,7 @@ __global__ __launch_bounds__(kHeadWaves * 64) void heads_w2_kernel(
   int rb, rstride, nrows;
   wave_rows(g * kHeadWaves + wave, gridDim.x * kHeadWaves, rpw, V, interleave != 0, rb, rstride,
             nrows);
-  RowStream<ET, NB> rs;
+  HeadStream<ET, NB, SPR> rs;
   stage_and_start<ET, NB>(rs, z + ((size_t)b0 * K + k) * d, (size_t)K * d, nb, d, xs, ldx,
                           W2 + (size_t)k * V * d, rb, rstride, nrows, 0);
   float win[NB];
@@ -478,14 +635,14 @@ __global__ __launch_bounds__(kMergeThreads) void heads_merge_kernel(
   }
 }
 
-template <class ET, int NB>
-hipError_t launch_heads_nb(const HeadsArgs& a, int b0, hipStream_t st) {
+template <class ET, int NB, int SPR>
+hipError_t launch_heads_spr(const HeadsArgs& a, int b0, hipStream_t st) {
   constexpr int CW = RowStream<ET, NB>::CW;
   const int ldx = (a.d + CW - 1) / CW * CW;
   const size_t lds_x = (size_t)NB * ldx * sizeof(float);
   const int rows1 = kHeadWaves * a.w1_rows_per_wave;
   const int g1 = (a.K * a.d + rows1 - 1) / rows1;
-  hipLaunchKernelGGL((heads_w1_kernel<ET, NB>), dim3(g1), dim3(kHeadWaves * 64), lds_x, st, a.h,
+  hipLaunchKernelGGL((heads_w1_kernel<ET, NB, SPR>), dim3(g1), dim3(kHeadWaves * 64), lds_x, st, a.h,
                      a.B, b0, a.K, a.d, reinterpret_cast<const typename ET::storage*>(a.W1),
                      a.b1, a.z, a.w1_rows_per_wave, a.interleave);
   hipError_t e = hipGetLastError();
@@ -496,7 +653,7 @@ hipError_t launch_heads_nb(const HeadsArgs& a, int b0, hipStream_t st) {
     e = hipEventRecord(a.ev_before, st);
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL((heads_w2_kernel<ET, NB>), dim3(a.G, a.K), dim3(kHeadWaves * 64), lds2, st,
+  hipLaunchKernelGGL((heads_w2_kernel<ET, NB, SPR>), dim3(a.G, a.K), dim3(kHeadWaves * 64), lds2, st,
                      a.z, a.B, b0, a.K, a.V, a.d,
                      reinterpret_cast<const typename ET::storage*>(a.W2), a.w2_rows_per_wave,
                      a.S, a.head_logits, a.part_val, a.part_id, a.part_m, a.part_s, a.G,
@@ -505,6 +662,31 @@ hipError_t launch_heads_nb(const HeadsArgs& a, int b0, hipStream_t st) {
   if (e != hipSuccess) return e;
   if (a.ev_after) e = hipEventRecord(a.ev_after, st);
   return e;
+}
+
+// MEDUSA_HEAD_ROW_STREAM=0 keeps the generic stream for every d.
+bool head_row_stream() {
+  static const bool v = [] {
+    const char* s = getenv("MEDUSA_HEAD_ROW_STREAM");
+    return !(s && *s && atoi(s) == 0);
+  }();
+  return v;
+}
+
+// Whole-row streams for bf16 rows of 8, 10 or 16 chunks (d = 4096, 5120,
+// 8192) and one or two activation vectors; the generic stream otherwise.
+template <class ET, int NB>
+hipError_t launch_heads_nb(const HeadsArgs& a, int b0, hipStream_t st) {
+  constexpr int CW = RowStream<ET, NB>::CW;
+  if (std::is_same<ET, BF16>::value && NB <= 2 && head_row_stream() && a.d % CW == 0) {
+    switch (a.d / CW) {
+      case 8: return launch_heads_spr<ET, NB, (NB <= 2 ? 8 : 0)>(a, b0, st);
+      case 10: return launch_heads_spr<ET, NB, (NB <= 2 ? 10 : 0)>(a, b0, st);
+      case 16: return launch_heads_spr<ET, NB, (NB <= 2 ? 16 : 0)>(a, b0, st);
+      default: break;
+    }
+  }
+  return launch_heads_spr<ET, NB, 0>(a, b0, st);
 }
 
 template <class ET>
