@@ -73,7 +73,15 @@ int w1_rows(int rows) {
   const int slots = 4 * 4 * device_cus();   // waves of the resident workgroups
   return std::min(64, std::max(1, (rows + slots - 1) / slots));
 }
-int w2_rows() { static int v = env_int("MEDUSA_W2_ROWS", 40, kMinW2Rows / 4, 64); return v; }
+// W2 grid: rows per wave (MEDUSA_W2_ROWS, default 56) and the workgroups per
+// head that cover the V rows with them. 56 was measured fastest for the 7B heads
+// (715 workgroups; 40, 48, 54, 58, 60 and 64 rows, and grids filling exactly
+// 3 or 4 workgroups per compute unit, were 0.6-15 us slower).
+void w2_grid(int V, int& G, int& rpw) {
+  static const int rows = env_int("MEDUSA_W2_ROWS", 56, kMinW2Rows / 4, 64);
+  rpw = rows;
+  G = (V + 4 * rpw - 1) / (4 * rpw);
+}
 int head_interleave() { static int v = env_int("MEDUSA_HEAD_INTERLEAVE", 1, 0, 1); return v; }
 
 
@@ -135,7 +143,10 @@ Layout layout_for(const medusa_shape* s) {
   L.counters = take(kCounterBytes);
   const size_t B = s->B, K = s->K, d = s->d, S = s->s_max;
   const int Gmax = (s->V + kMinW2Rows - 1) / kMinW2Rows;
-  L.G = (s->V + 4 * w2_rows() - 1) / (4 * w2_rows());
+  {
+    int rpw;
+    w2_grid(s->V, L.G, rpw);
+  }
   L.z = take(B * K * d * 4);
   L.part_val = take(B * K * Gmax * S * 4);
   L.part_id = take(B * K * Gmax * S * 4);
@@ -309,7 +320,10 @@ int heads_impl(const medusa_shape* shape, const float* h, const void* W1,
   a.part_s = at<float>(workspace, L.part_s);
   a.G = L.G;
   a.w1_rows_per_wave = w1_rows(shape->K * shape->d);
-  a.w2_rows_per_wave = w2_rows();
+  {
+    int G;
+    w2_grid(shape->V, G, a.w2_rows_per_wave);
+  }
   a.interleave = head_interleave();
   a.ev_before = g_ev_before;
   a.ev_after = g_ev_after;
