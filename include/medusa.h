@@ -136,6 +136,35 @@ int medusa_heads_forward(const medusa_shape* shape, const float* h, const void* 
                          size_t workspace_bytes, void* stream);
 
 /*
+ * Calibrated sparse tree ("Medusa 深读", §6.2): from per-head rank
+ * probabilities, choose the `budget` tree nodes (rank paths) that maximise
+ * the expected accepted depth under the approximation that heads are
+ * independent. A rank path (r_1 .. r_k) weighs w = prod_j a[j][r_j]; the
+ * frontier starts with the depth-1 paths; `budget` times the frontier path
+ * of largest weight (ties: the lexicographically smaller path, a prefix
+ * first) joins the tree and its S children join the frontier. The expected
+ * accepted depth is the sum of the chosen weights (tail-sum identity). Host
+ * code only: no device memory, no stream, no GPU needed.
+ *
+ *   K, S                heads (1..MEDUSA_MAX_K) and ranks per head (1..MEDUSA_MAX_S)
+ *   a_host              HOST [K][S] float64, a[k][i] = P(head k+1's true token
+ *                       has 0-based rank i); finite and >= 0
+ *   budget              nodes to choose, 0..MEDUSA_MAX_T-1 (fewer when the full
+ *                       tree of sum_k S^k paths is smaller)
+ *   tree_ranks_host     HOST [budget][K] int32 (out): the chosen paths in
+ *                       canonical order (depth, then lexicographic), -1
+ *                       padded, ready for medusa_build_tree / medusa_step
+ *   weights_host_or_null     HOST [budget] float64 (out): w of each row
+ *   pick_order_host_or_null  HOST [budget] int32 (out): row of the i-th pick
+ *   n_nodes_host        HOST int32 (out): number of rows written
+ * Returns MEDUSA_ERR_ARG for null pointers, negative sizes or a table entry
+ * that is negative, infinite or NaN; MEDUSA_ERR_UNSUPPORTED beyond the limits.
+ */
+int medusa_sparse_tree(int K, int S, const double* a_host, int budget, int32_t* tree_ranks_host,
+                       double* weights_host_or_null, int32_t* pick_order_host_or_null,
+                       int32_t* n_nodes_host);
+
+/*
  * Candidate tree ("Medusa 深读", §6.1; node-count equation): node 0 is the
  * root (the base LM head's token); node n >= 1 has rank path tree_ranks[n-1].
  *

@@ -98,6 +98,7 @@ _SIGS = {
                                    _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P], _I),
     "medusa_commit": ([_SP, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P], _I),
     "medusa_step": ([_SP, ctypes.POINTER(StepArgs), _P, _SZ, _P], _I),
+    "medusa_sparse_tree": ([_I, _I, _P, _I, _P, _P, _P, _P], _I),
 }
 for _name, (_args, _res) in _SIGS.items():
     _fn = getattr(_lib, _name, None)
@@ -183,6 +184,25 @@ def build_tree(shape, tree_ranks: np.ndarray, root_tok, kv_len, tree_tokens, tre
         _ptr(head_logits), _ptr(head_lse), _ptr(u_draft), _ptr(kv_len), _ptr(tree_tokens),
         _ptr(tree_mask), _ptr(position_ids), _ptr(retrieve), _ptr(parent), _ptr(depth),
         _stream(stream)))
+
+
+def sparse_tree(a, budget: int):
+    """medusa_sparse_tree: (tree_ranks [N][K] int32 canonical, weights [N] float64,
+    pick_order [N] int32) for the rank-probability table a [K][S]."""
+    a = np.ascontiguousarray(a, dtype=np.float64)
+    if a.ndim != 2:
+        raise ValueError("a must be [K][S]")
+    K, S = a.shape
+    cap = max(int(budget), 1)
+    ranks = np.full((cap, max(K, 1)), -1, dtype=np.int32)
+    weights = np.zeros(cap, dtype=np.float64)
+    order = np.zeros(cap, dtype=np.int32)
+    n = ctypes.c_int32(0)
+    _check(_lib.medusa_sparse_tree(int(K), int(S), a.ctypes.data if a.size else None, int(budget),
+                                   ranks.ctypes.data, weights.ctypes.data, order.ctypes.data,
+                                   ctypes.addressof(n)))
+    N = n.value
+    return ranks[:N].copy(), weights[:N].copy(), order[:N].copy()
 
 
 def tree_attention(shape, q, k_tree, v_tree, k_cache, v_cache, kv_len, tree_mask, scale, out,

@@ -865,3 +865,99 @@ int medusa_step(const medusa_shape* shape, const medusa_step_args* x, void* work
 }
 
 }  // extern "C"
+
+// ---- calibrated sparse tree (host) -------------------------------------------------
+namespace {
+
+// A rank path and its weight prod_j a[j][r_j]; the weight of a child is its
+// parent's times one more factor, the product taken in path order.
+struct TreePath {
+  double w;
+  int len;
+  int8_t r[MEDUSA_MAX_K];
+};
+
+// Lexicographic order of rank paths (a proper prefix comes first).
+bool path_less(const TreePath& x, const TreePath& y) {
+  const int n = std::min(x.len, y.len);
+  for (int i = 0; i < n; ++i)
+    if (x.r[i] != y.r[i]) return x.r[i] < y.r[i];
+  return x.len < y.len;
+}
+
+// x is picked before y: larger weight, then the lexicographically smaller path.
+bool picked_before(const TreePath& x, const TreePath& y) {
+  if (x.w != y.w) return x.w > y.w;
+  return path_less(x, y);
+}
+
+}  // namespace
+
+extern "C" {
+
+int medusa_sparse_tree(int K, int S, const double* a_host, int budget, int32_t* tree_ranks_host,
+                       double* weights_host_or_null, int32_t* pick_order_host_or_null,
+                       int32_t* n_nodes_host) {
+  if (!a_host || !tree_ranks_host || !n_nodes_host)
+    return fail(MEDUSA_ERR_ARG, "sparse tree: null pointer");
+  if (K < 1 || S < 1 || budget < 0)
+    return fail(MEDUSA_ERR_ARG, "sparse tree: K=%d, S=%d, budget=%d", K, S, budget);
+  if (K > MEDUSA_MAX_K || S > MEDUSA_MAX_S || budget > MEDUSA_MAX_T - 1)
+    return fail(MEDUSA_ERR_UNSUPPORTED, "sparse tree: K=%d > %d, S=%d > %d or budget=%d > %d", K,
+                MEDUSA_MAX_K, S, MEDUSA_MAX_S, budget, MEDUSA_MAX_T - 1);
+  for (int i = 0; i < K * S; ++i)
+    if (!(a_host[i] >= 0.0) || !std::isfinite(a_host[i]))
+      return fail(MEDUSA_ERR_ARG, "sparse tree: a[%d][%d] = %g is not a finite probability",
+                  i / S, i % S, a_host[i]);
+  // frontier: a heap whose top is the path picked next
+  auto heap_less = [](const TreePath& x, const TreePath& y) { return picked_before(y, x); };
+  std::vector<TreePath> frontier;
+  frontier.reserve((size_t)S * (budget + 1));
+  for (int r = 0; r < S; ++r) {
+    TreePath t{};
+    t.w = 1.0 * a_host[r];
+    t.len = 1;
+    t.r[0] = (int8_t)r;
+    frontier.push_back(t);
+  }
+  std::make_heap(frontier.begin(), frontier.end(), heap_less);
+  std::vector<TreePath> picks;
+  picks.reserve(budget);
+  while ((int)picks.size() < budget && !frontier.empty()) {
+    std::pop_heap(frontier.begin(), frontier.end(), heap_less);
+    const TreePath best = frontier.back();
+    frontier.pop_back();
+    picks.push_back(best);
+    if (best.len < K) {
+      for (int r = 0; r < S; ++r) {
+        TreePath c = best;
+        c.w = best.w * a_host[best.len * S + r];
+        c.r[c.len++] = (int8_t)r;
+        frontier.push_back(c);
+        std::push_heap(frontier.begin(), frontier.end(), heap_less);
+      }
+    }
+  }
+  // canonical order: depth, then lexicographic
+  const int N = (int)picks.size();
+  std::vector<int> idx(N);
+  for (int i = 0; i < N; ++i) idx[i] = i;
+  std::sort(idx.begin(), idx.end(), [&](int x, int y) {
+    if (picks[x].len != picks[y].len) return picks[x].len < picks[y].len;
+    return path_less(picks[x], picks[y]);
+  });
+  std::vector<int> canon_of(N);
+  for (int c = 0; c < N; ++c) {
+    const TreePath& t = picks[idx[c]];
+    canon_of[idx[c]] = c;
+    for (int j = 0; j < K; ++j) tree_ranks_host[(size_t)c * K + j] = j < t.len ? t.r[j] : -1;
+    if (weights_host_or_null) weights_host_or_null[c] = t.w;
+  }
+  if (pick_order_host_or_null)
+    for (int i = 0; i < N; ++i) pick_order_host_or_null[i] = canon_of[i];
+  *n_nodes_host = N;
+  return ok();
+}
+
+}  // extern "C"
+

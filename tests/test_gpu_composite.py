@@ -61,3 +61,30 @@ def test_composite_full_size_7b():
     parity.compare_step(w, inp, g, o, report)
     assert report.get("ambiguous", 0) <= 2, report
     parity.gpu_posterior_consistent(w, g, o["topo"])
+
+
+def test_composite_calibrated_sparse_tree():
+    """A tree chosen by the native builder (medusa_sparse_tree) from a synthetic
+    calibration table — 40 nodes, mixed-depth leaves — through the composite
+    call, against the oracle step over the same spec."""
+    require_gpu()
+    from oracle import step as OSTEP
+    import medusa_tree_verification_forward_amd._lib as L
+    w = scaled(WORKLOADS["vicuna7b_typical"], d=512, H=4, V=3001, L=300, L_range=(300, 300))
+    K, S = w.K, w.s_max
+    a = np.array([[0.62 * 0.35 ** i * 0.9 ** k for i in range(S)] for k in range(K)])
+    ranks, _, _ = L.sparse_tree(a, 40)
+    assert len(ranks) == 40 and len({int((r >= 0).sum()) for r in ranks}) > 2
+    inp = dict(parity.inputs_for(w))
+    inp["ranks"] = ranks
+    rng = np.random.default_rng(41)
+    T = len(ranks) + 1
+    for name in [k for k in inp if k.startswith("u_")]:
+        inp[name] = rng.random((w.B, T), dtype=np.float32)
+    o = OSTEP.verify_step(inp, H=w.H, Dh=w.Dh, s_max=w.s_max, mode=w.mode, tau=w.tau,
+                          eps=w.eps, delta=w.delta, theta=w.rope_theta, bf16=(w.dtype == "bf16"))
+    g = parity.gpu_step(w, inp, composite=True)
+    report = {}
+    parity.compare_step(w, inp, g, o, report)
+    assert report.get("ambiguous", 0) <= 2, report
+    parity.gpu_posterior_consistent(w, g, o["topo"])
