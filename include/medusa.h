@@ -399,6 +399,38 @@ typedef struct {
 int medusa_step(const medusa_shape* shape, const medusa_step_args* args, void* workspace,
                 size_t workspace_bytes, void* stream);
 
+/*
+ * Decoding loop ("Medusa 深读", generate loop; "Medusa: Faster LLM text
+ * generation", decoding with heads and tree attention): n_steps composite
+ * steps back to back on one stream, each step's accepted prefix becoming the
+ * next step's context with no host round trip, so the loop (or any number of
+ * its steps) can be captured in one graph.
+ *
+ *   args             as for medusa_step, with the loop state in-out:
+ *                    h [B][d] and root_tok [B] (the hidden state of the last
+ *                    accepted token and the base model's next token) are read
+ *                    by the first step and hold the state after the last one
+ *                    on return; h_next and next_root are the loop's second
+ *                    state buffer (overwritten); kv_len and the KV cache
+ *                    advance in place (kv_len_out_or_null must be NULL);
+ *                    out_tokens and accept_len are not used; the exact-mode
+ *                    uniforms, when given, are [n_steps][B][T] (step i reads
+ *                    row block i)
+ *   n_steps          steps to run, >= 0
+ *   out_tokens_steps int32 (out): step i's committed tokens (root, then the
+ *                    accepted nodes), -1 padded, as a [B][K+1] block at
+ *                    element i * MEDUSA_ALIGN4(B * (K+1))
+ *   accept_len_steps int32 (out): step i's accepted depths a (the step
+ *                    commits a + 1 tokens) as [B] at element i * MEDUSA_ALIGN4(B)
+ *                    (the per-step blocks keep the 16-byte alignment)
+ * The caller sizes the cache for kv_len + n_steps * (K + 1) rows. Errors as
+ * for medusa_step; on an error some steps may already be launched.
+ */
+#define MEDUSA_ALIGN4(n) (((n) + 3) & ~3)
+int medusa_generate(const medusa_shape* shape, const medusa_step_args* args, int n_steps,
+                    int32_t* out_tokens_steps, int32_t* accept_len_steps, void* workspace,
+                    size_t workspace_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -99,6 +99,7 @@ _SIGS = {
     "medusa_commit": ([_SP, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P], _I),
     "medusa_step": ([_SP, ctypes.POINTER(StepArgs), _P, _SZ, _P], _I),
     "medusa_sparse_tree": ([_I, _I, _P, _I, _P, _P, _P, _P], _I),
+    "medusa_generate": ([_SP, ctypes.POINTER(StepArgs), _I, _P, _P, _P, _SZ, _P], _I),
 }
 for _name, (_args, _res) in _SIGS.items():
     _fn = getattr(_lib, _name, None)
@@ -184,6 +185,14 @@ def build_tree(shape, tree_ranks: np.ndarray, root_tok, kv_len, tree_tokens, tre
         _ptr(head_logits), _ptr(head_lse), _ptr(u_draft), _ptr(kv_len), _ptr(tree_tokens),
         _ptr(tree_mask), _ptr(position_ids), _ptr(retrieve), _ptr(parent), _ptr(depth),
         _stream(stream)))
+
+
+def generate(shape, args: StepArgs, n_steps: int, out_tokens_steps, accept_len_steps, workspace,
+             *, stream=None):
+    """medusa_generate: n_steps composite steps with the state kept on the device."""
+    _check(_lib.medusa_generate(ctypes.byref(shape), ctypes.byref(args), int(n_steps),
+                                _ptr(out_tokens_steps), _ptr(accept_len_steps), _ptr(workspace),
+                                workspace.numel() * workspace.element_size(), _stream(stream)))
 
 
 def sparse_tree(a, budget: int):

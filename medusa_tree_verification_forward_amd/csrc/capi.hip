@@ -961,3 +961,53 @@ int medusa_sparse_tree(int K, int S, const double* a_host, int budget, int32_t* 
 
 }  // extern "C"
 
+// ---- decode loop -------------------------------------------------------------------
+extern "C" {
+
+int medusa_generate(const medusa_shape* shape, const medusa_step_args* args, int n_steps,
+                    int32_t* out_tokens_steps, int32_t* accept_len_steps, void* workspace,
+                    size_t workspace_bytes, void* stream) {
+  int rc = check_shape(shape);
+  if (rc) return rc;
+  if (!args || !out_tokens_steps || !accept_len_steps)
+    return fail(MEDUSA_ERR_ARG, "generate: null pointer");
+  if (n_steps < 0) return fail(MEDUSA_ERR_ARG, "generate: n_steps=%d", n_steps);
+  if (args->kv_len_out_or_null)
+    return fail(MEDUSA_ERR_ARG, "generate: the loop advances kv_len in place (kv_len_out_or_null must be NULL)");
+  REQUIRE_PTR(args->h);
+  REQUIRE_PTR(args->h_next);
+  REQUIRE_PTR(args->root_tok);
+  REQUIRE_PTR(args->next_root);
+  const size_t B = shape->B, T = shape->N + 1, K1 = shape->K + 1;
+  // the state alternates between (h, root_tok) and (h_next, next_root)
+  float* hs[2] = {const_cast<float*>(args->h), args->h_next};
+  int32_t* roots[2] = {const_cast<int32_t*>(args->root_tok), args->next_root};
+  medusa_step_args x = *args;
+  for (int i = 0; i < n_steps; ++i) {
+    const int cur = i & 1;
+    x.h = hs[cur];
+    x.root_tok = roots[cur];
+    x.h_next = hs[cur ^ 1];
+    x.next_root = roots[cur ^ 1];
+    x.out_tokens = out_tokens_steps + (size_t)i * MEDUSA_ALIGN4(B * K1);
+    x.accept_len = accept_len_steps + (size_t)i * MEDUSA_ALIGN4(B);
+    if (args->u_draft_or_null) x.u_draft_or_null = args->u_draft_or_null + (size_t)i * B * T;
+    if (args->u_accept_or_null) x.u_accept_or_null = args->u_accept_or_null + (size_t)i * B * T;
+    if (args->u_resample_or_null)
+      x.u_resample_or_null = args->u_resample_or_null + (size_t)i * B * T;
+    rc = medusa_step(shape, &x, workspace, workspace_bytes, stream);
+    if (rc) return rc;
+  }
+  if (n_steps & 1) {
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    hipError_t e = hipMemcpyAsync(hs[0], hs[1], B * shape->d * sizeof(float),
+                                  hipMemcpyDeviceToDevice, st);
+    if (e == hipSuccess)
+      e = hipMemcpyAsync(roots[0], roots[1], B * sizeof(int32_t), hipMemcpyDeviceToDevice, st);
+    if (e != hipSuccess) return hip_fail(e, "generate: state copy");
+  }
+  return ok();
+}
+
+}  // extern "C"
+

@@ -208,6 +208,29 @@ class VerifyStep:
         for keep_kv_len."""
         L.step(self.shape, self.step_args(keep_kv_len), self.ws, stream=stream)
 
+    def generate(self, n_steps: int, stream=None, uniforms=None):
+        """medusa_generate: n_steps steps with the state kept on the device.
+        Returns (out_tokens [n][B][K+1], accept_len [n][B]) device tensors;
+        afterwards inp["h"], inp["root"], inp["kv_len"] and the caches hold the
+        advanced state. Exact mode takes uniforms = {u_draft, u_accept,
+        u_resample}, each [n][B][T] on the device."""
+        import torch
+        a = L.StepArgs.from_buffer_copy(self.step_args(False))
+        if self.mode == "exact":
+            if uniforms is None:
+                raise ValueError("exact mode needs per-step uniforms")
+            a.u_draft_or_null = L._ptr(uniforms["u_draft"])
+            a.u_accept_or_null = L._ptr(uniforms["u_accept"])
+            a.u_resample_or_null = L._ptr(uniforms["u_resample"])
+        B, K = self.shape.B, self.shape.K
+        ot, al = (B * (K + 1) + 3) & ~3, (B + 3) & ~3   # 16-byte aligned step blocks
+        n = max(n_steps, 1)
+        toks = torch.full((n, ot), -1, dtype=torch.int32, device="cuda")
+        acc = torch.zeros((n, al), dtype=torch.int32, device="cuda")
+        L.generate(self.shape, a, n_steps, toks, acc, self.ws, stream=stream)
+        return (toks[:n_steps, :B * (K + 1)].reshape(n_steps, B, K + 1),
+                acc[:n_steps, :B])
+
     def run(self, stream=None, commit: bool = True):
         """The whole step: heads, tree, verify forward, posterior, commit."""
         self.heads(stream)

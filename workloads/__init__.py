@@ -285,3 +285,71 @@ def make_inputs(w: Workload, with_weights: bool = True,
     for name in ("u_draft", "u_accept", "u_resample"):
         out[name] = _rng(w, name).random((B, T), dtype=np.float32)
     return out
+
+
+# --------------------------------------------------------------------------
+# Planted agreement between the heads and the verifier (decoding loop)
+# --------------------------------------------------------------------------
+
+def planted_inputs(a: np.ndarray, ranks: np.ndarray, *, V: int = 512, H: int = 4,
+                   Dh: int = 128, L: int = 64, n_steps: int = 32, B: int = 1,
+                   seed: int = 2024) -> Dict[str, np.ndarray]:
+    """Inputs under which the heads agree with the verifier at planted ranks.
+
+    Random weights give the heads no agreement with the verifier, so the
+    acceptance of a decoding loop says nothing. Here the "language" is a fixed
+    permutation pi of a vocabulary of V tokens with one-hot embeddings
+    (d = V): E[t] = e_t and W_lm[pi(t)] = 8 e_t, so the verifier's next token
+    after t is pi(t) by a wide margin (the attention and output projection
+    add ~1% noise to the one-hot state); W1 = 0, so z_k = h. For each head k
+    (1-based) and token t the true continuation pi^(k+1)(t) is placed at a
+    rank drawn from the row a[k-1] (0-based ranks; beyond the head's pool
+    with probability 1 - sum a[k-1]), decoys filling the other ranks, so the
+    rank of the true token at depth k is distributed as a[k-1]. The state
+    starts at h = e_t0, root = pi(t0). Returns the step inputs plus "pi" and
+    "true_rank" [K][V] (the planted rank, S meaning beyond the pool).
+    """
+    a = np.asarray(a, dtype=np.float64)
+    K, S = a.shape
+    d = V
+    rng = np.random.default_rng([seed, V, K, S])
+    pi = rng.permutation(V).astype(np.int64)
+    pipow = [np.arange(V)]
+    for _ in range(K + 1):
+        pipow.append(pi[pipow[-1]])
+    out: Dict[str, np.ndarray] = {"ranks": np.ascontiguousarray(ranks, dtype=np.int32)}
+    E = np.eye(V, d, dtype=np.float32)
+    W_lm = np.zeros((V, d), dtype=np.float32)
+    W_lm[pi, np.arange(V)] = 8.0
+    W2 = np.zeros((K, V, d), dtype=np.float32)
+    true_rank = np.full((K, V), S, dtype=np.int32)
+    p_ranks = np.concatenate([a, 1.0 - a.sum(axis=1, keepdims=True).clip(0, 1)], axis=1)
+    p_ranks /= p_ranks.sum(axis=1, keepdims=True)
+    for k in range(K):
+        for t in range(V):
+            target = int(pipow[k + 2][t])
+            r = int(rng.choice(S + 1, p=p_ranks[k]))
+            true_rank[k, t] = r
+            decoys = rng.choice(np.delete(np.arange(V), target), size=S, replace=False)
+            slots = list(decoys)
+            if r < S:
+                slots[r] = target
+            for i, v in enumerate(slots):
+                W2[k, v, t] = 8.0 * (1.0 - 0.0625 * i)
+            if r >= S:
+                W2[k, target, t] = 8.0 * (1.0 - 0.0625 * (S + 1))
+    W_qkv = rng.standard_normal((3 * d, d), dtype=np.float32) / np.sqrt(d)
+    W_o = rng.standard_normal((d, d), dtype=np.float32) * (0.01 / np.sqrt(d))
+    Lmax = L + n_steps * (K + 1) + 8
+    kc = rng.standard_normal((B, H, Lmax, Dh), dtype=np.float32)
+    vc = rng.standard_normal((B, H, Lmax, Dh), dtype=np.float32)
+    t0 = rng.integers(0, V, size=B)
+    h = np.zeros((B, d), dtype=np.float32)
+    h[np.arange(B), t0] = 1.0
+    out.update(
+        h=h, W1=f32_to_bf16_bits(np.zeros((K, d, d), dtype=np.float32)), W2=f32_to_bf16_bits(W2),
+        E=f32_to_bf16_bits(E), W_qkv=f32_to_bf16_bits(W_qkv), W_o=f32_to_bf16_bits(W_o),
+        W_lm=f32_to_bf16_bits(W_lm), k_cache=f32_to_bf16_bits(kc), v_cache=f32_to_bf16_bits(vc),
+        kv_len=np.full(B, L, dtype=np.int32), root=pi[t0].astype(np.int32),
+        pi=pi.astype(np.int32), true_rank=true_rank)
+    return out
