@@ -15,6 +15,12 @@ own stream inside the timed region) and the CPU oracle timed on a bounded
 sample of the same workload.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+
+With --decode it prints a different line instead: the decoding loop
+(medusa_generate) on planted agreement — accepted tokens per step A for a
+Cartesian and a calibrated sparse tree against the tail-sum prediction —
+and the step-cost ratio r of the 7B step to a plain one-token step made of
+the same kernels.
 """
 
 from __future__ import annotations
@@ -148,6 +154,99 @@ def recorded_traffic():
     return float(val.group(1))
 
 
+# Synthetic calibration table for the decoding report: P(rank i) of head k's
+# true continuation (top-1 decaying with depth, as the heads' accuracy does).
+DECODE_A = np.array([[0.60, 0.15, 0.06], [0.45, 0.13, 0.06], [0.35, 0.12, 0.05],
+                     [0.28, 0.10, 0.05], [0.22, 0.09, 0.04]])
+
+
+def decode_report(steps):
+    """The decoding loop on planted agreement and the step-cost ratio."""
+    import torch
+    import medusa_tree_verification_forward_amd._lib as L
+    from medusa_tree_verification_forward_amd.step import VerifyStep, to_host
+    from workloads import WORKLOADS, cartesian_ranks, make_inputs, planted_inputs
+
+    a = DECODE_A
+    K, S = a.shape
+    sparse, sparse_w, _ = L.sparse_tree(a, 45)
+    trees = {"cartesian (3,2,2,1,1), 45 nodes": cartesian_ranks((3, 2, 2, 1, 1)),
+             "calibrated sparse, 45 nodes": sparse}
+    out = {}
+    for name, spec in trees.items():
+        paths = [tuple(int(x) for x in row if x >= 0) for row in spec]
+        predicted = 1.0 + sum(float(np.prod([a[j, r] for j, r in enumerate(p)])) for p in paths)
+        B, V = 8, 4096
+        full = planted_inputs(a, spec, V=V, H=32, Dh=128, n_steps=steps, B=B, L=64)
+        inp = {k: v for k, v in full.items() if k not in ("pi", "true_rank")}
+        t_first = np.argmax(inp["h"], axis=1)
+        st = VerifyStep(inp, H=32, Dh=128, s_max=S, mode="typical", tau=0.7, eps=0.09,
+                        delta=0.3, theta=10000.0)
+        toks, acc = st.generate(steps)
+        torch.cuda.synchronize()
+        toks, acc = to_host(toks), to_host(acc)
+        # depth the planted ranks allow for the token each step starts from
+        pset, rank = set(paths), full["true_rank"]
+        closed = np.zeros_like(acc)
+        for b in range(B):
+            t = int(t_first[b])
+            for i in range(steps):
+                dep = 0
+                while dep < K and tuple(int(rank[j, t]) for j in range(dep + 1)) in pset:
+                    dep += 1
+                closed[i, b] = dep
+                t = int(toks[i, b, acc[i, b]])
+        out[name] = {"nodes": len(paths), "A_measured": float(np.mean(acc + 1)),
+                     "A_tail_sum_prediction": predicted,
+                     "A_closed_form_on_visited_tokens": float(np.mean(closed + 1)),
+                     "steps": steps, "sequences": B,
+                     "distinct_start_tokens": int(len({int(x) for x in toks[:, :, 0].ravel()}))}
+    # step cost: the 7B composite step against a plain one-token step
+    w = WORKLOADS[WORKLOAD]
+    inp = make_inputs(w)
+    st = VerifyStep(inp, H=w.H, Dh=w.Dh, s_max=w.s_max, mode=w.mode, tau=w.tau, eps=w.eps,
+                    delta=w.delta, theta=w.rope_theta)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    for _ in range(20):
+        st.run_step(keep_kv_len=True)
+    e0.record()
+    for _ in range(100):
+        st.run_step(keep_kv_len=True)
+    e1.record()
+    torch.cuda.synchronize()
+    t_medusa = e0.elapsed_time(e1) / 100 * 1e3
+    plain_inp = dict(inp)
+    plain_inp["ranks"] = np.zeros((0, K), dtype=np.int32)
+    del st
+    pl = VerifyStep(plain_inp, H=w.H, Dh=w.Dh, s_max=w.s_max, mode=w.mode, tau=w.tau,
+                    eps=w.eps, delta=w.delta, theta=w.rope_theta)
+
+    def plain():   # root-only tree: draft nothing, verify the root, commit one token
+        pl.tree()
+        pl.verify()
+        pl.posterior()
+        pl.commit()
+    for _ in range(10):
+        plain()
+    pl.reset_kv_len()   # the cache has room for ~60 one-token commits past the prefix
+    e0.record()
+    for _ in range(40):
+        plain()
+    e1.record()
+    torch.cuda.synchronize()
+    t_plain = e0.elapsed_time(e1) / 40 * 1e3
+    r = t_medusa / t_plain
+    print(json.dumps({
+        "metric": "decoding loop: accepted tokens per step A (planted agreement) and A/r",
+        "trees": out, "t_medusa_step_us": t_medusa, "t_plain_step_us": t_plain, "r": r,
+        "A_over_r": {k: v["A_measured"] / r for k, v in out.items()},
+        "data": "synthetic: planted agreement (permutation language, one-hot embeddings, "
+                "V=d=4096, head ranks drawn from a synthetic calibration table); step times "
+                "at the 7B shapes with seeded random weights",
+        "note": "the verifier is one transformer layer plus the LM head, so r here weighs "
+                "the heads against one layer, not against a whole base model"}))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -165,7 +264,12 @@ def main():
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="before the timed loop, run a plain device-to-device copy of this "
                          "many bytes 3 times (a known-size kernel for scaling HBM counters)")
+    ap.add_argument("--decode", action="store_true",
+                    help="print the decoding-loop report (A, A/r) instead of the step line")
     args = ap.parse_args()
+    if args.decode:
+        decode_report(max(args.steps, 8))
+        return
     if args.print_digest:
         print(w2_source_digest())
         return

@@ -300,8 +300,9 @@ def planted_inputs(a: np.ndarray, ranks: np.ndarray, *, V: int = 512, H: int = 4
     acceptance of a decoding loop says nothing. Here the "language" is a fixed
     permutation pi of a vocabulary of V tokens with one-hot embeddings
     (d = V): E[t] = e_t and W_lm[pi(t)] = 8 e_t, so the verifier's next token
-    after t is pi(t) by a wide margin (the attention and output projection
-    add ~1% noise to the one-hot state); W1 = 0, so z_k = h. For each head k
+    after t is pi(t) by a wide margin (the attention and output projection,
+    random bf16 weights of magnitude ~1/sqrt(d) and ~1% of that, add little
+    to the one-hot state); W1 = 0, so z_k = h. For each head k
     (1-based) and token t the true continuation pi^(k+1)(t) is placed at a
     rank drawn from the row a[k-1] (0-based ranks; beyond the head's pool
     with probability 1 - sum a[k-1]), decoys filling the other ranks, so the
@@ -318,38 +319,54 @@ def planted_inputs(a: np.ndarray, ranks: np.ndarray, *, V: int = 512, H: int = 4
     for _ in range(K + 1):
         pipow.append(pi[pipow[-1]])
     out: Dict[str, np.ndarray] = {"ranks": np.ascontiguousarray(ranks, dtype=np.int32)}
-    E = np.eye(V, d, dtype=np.float32)
-    W_lm = np.zeros((V, d), dtype=np.float32)
-    W_lm[pi, np.arange(V)] = 8.0
-    W2 = np.zeros((K, V, d), dtype=np.float32)
+    one, eight = 0x3F80, 0x4100                       # bf16 bit patterns of 1.0 and 8.0
+    E = np.zeros((V, d), dtype=np.uint16)
+    E[np.arange(V), np.arange(V)] = one
+    W_lm = np.zeros((V, d), dtype=np.uint16)
+    W_lm[pi, np.arange(V)] = eight
+    W2 = np.zeros((K, V, d), dtype=np.uint16)
     true_rank = np.full((K, V), S, dtype=np.int32)
     p_ranks = np.concatenate([a, 1.0 - a.sum(axis=1, keepdims=True).clip(0, 1)], axis=1)
     p_ranks /= p_ranks.sum(axis=1, keepdims=True)
+    level = f32_to_bf16_bits(8.0 * (1.0 - 0.0625 * np.arange(S + 2, dtype=np.float32)))
+    ks, vs, ts, ls = [], [], [], []
     for k in range(K):
         for t in range(V):
             target = int(pipow[k + 2][t])
             r = int(rng.choice(S + 1, p=p_ranks[k]))
             true_rank[k, t] = r
-            decoys = rng.choice(np.delete(np.arange(V), target), size=S, replace=False)
-            slots = list(decoys)
+            cand = rng.choice(V, size=S + 1, replace=False)
+            slots = [int(x) for x in cand if x != target][:S]
             if r < S:
                 slots[r] = target
+            else:
+                slots.append(target)          # just below the pool
             for i, v in enumerate(slots):
-                W2[k, v, t] = 8.0 * (1.0 - 0.0625 * i)
-            if r >= S:
-                W2[k, target, t] = 8.0 * (1.0 - 0.0625 * (S + 1))
-    W_qkv = rng.standard_normal((3 * d, d), dtype=np.float32) / np.sqrt(d)
-    W_o = rng.standard_normal((d, d), dtype=np.float32) * (0.01 / np.sqrt(d))
+                ks.append(k)
+                vs.append(v)
+                ts.append(t)
+                ls.append(level[i if i < S else S + 1])
+    W2[np.array(ks), np.array(vs), np.array(ts)] = np.array(ls, dtype=np.uint16)
+    def random_bf16(shape, exponent):
+        # random sign and mantissa at a fixed binary exponent: |x| in [2^e, 2^(e+1))
+        n = int(np.prod(shape))
+        bits = np.frombuffer(rng.bytes(2 * n), dtype=np.uint16).reshape(shape)
+        return (bits & np.uint16(0x807F)) | np.uint16((127 + exponent) << 7)
+    e_qkv = int(np.floor(np.log2(1.0 / np.sqrt(d)))) - 1   # |w| ~ 1/sqrt(d)
+    W_qkv = random_bf16((3 * d, d), e_qkv)
+    W_o = random_bf16((d, d), e_qkv - 7)                   # ~1% of the residual
     Lmax = L + n_steps * (K + 1) + 8
-    kc = rng.standard_normal((B, H, Lmax, Dh), dtype=np.float32)
-    vc = rng.standard_normal((B, H, Lmax, Dh), dtype=np.float32)
+    # the prefix rows are random; the rows the loop commits are written by it
+    kc = np.zeros((B, H, Lmax, Dh), dtype=np.uint16)
+    vc = np.zeros((B, H, Lmax, Dh), dtype=np.uint16)
+    kc[:, :, :L] = f32_to_bf16_bits(rng.standard_normal((B, H, L, Dh), dtype=np.float32))
+    vc[:, :, :L] = f32_to_bf16_bits(rng.standard_normal((B, H, L, Dh), dtype=np.float32))
     t0 = rng.integers(0, V, size=B)
     h = np.zeros((B, d), dtype=np.float32)
     h[np.arange(B), t0] = 1.0
     out.update(
-        h=h, W1=f32_to_bf16_bits(np.zeros((K, d, d), dtype=np.float32)), W2=f32_to_bf16_bits(W2),
-        E=f32_to_bf16_bits(E), W_qkv=f32_to_bf16_bits(W_qkv), W_o=f32_to_bf16_bits(W_o),
-        W_lm=f32_to_bf16_bits(W_lm), k_cache=f32_to_bf16_bits(kc), v_cache=f32_to_bf16_bits(vc),
-        kv_len=np.full(B, L, dtype=np.int32), root=pi[t0].astype(np.int32),
-        pi=pi.astype(np.int32), true_rank=true_rank)
+        h=h, W1=np.zeros((K, d, d), dtype=np.uint16), W2=W2, E=E,
+        W_qkv=W_qkv, W_o=W_o, W_lm=W_lm,
+        k_cache=kc, v_cache=vc, kv_len=np.full(B, L, dtype=np.int32),
+        root=pi[t0].astype(np.int32), pi=pi.astype(np.int32), true_rank=true_rank)
     return out
