@@ -15,6 +15,12 @@ own stream inside the timed region) and the CPU oracle timed on a bounded
 sample of the same workload.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+                    [--workload NAME]
+
+--workload times another bf16 workload with the same line (13B shapes with a
+136-node tree and a 4k prefix; eight 7B sequences with ragged prefixes and
+greedy acceptance; 7B shapes with exact p/q acceptance); the CPU baseline is
+taken on the 7B workload only.
 
 With --decode it prints a different line instead: the decoding loop
 (medusa_generate) on planted agreement — accepted tokens per step A for a
@@ -48,13 +54,36 @@ def algorithmic_bytes(w, T, L_total):
     kv = wb * 2 * H * Dh * L_total
     emb = wb * d * B * T
     act = 4 * d * B
-    return weights + kv + emb + act
+    logits = 2 * 4 * K * V * B if w.mode == "exact" else 0   # head logits written, then read
+    return weights + kv + emb + act + logits
 
 
 def w2_kernel_bytes(w):
     """Algorithmic bytes of one vocabulary-projection launch: the K*V*d bf16
-    weights plus the K fp32 input vectors per sequence."""
-    return 2 * w.K * w.V * w.d + 4 * w.B * w.K * w.d
+    weights plus the K fp32 input vectors per sequence, and in exact mode the
+    fp32 head logits it writes for drafting."""
+    extra = 4 * w.B * w.K * w.V if w.mode == "exact" else 0
+    return 2 * w.K * w.V * w.d + 4 * w.B * w.K * w.d + extra
+
+
+MFMA_BF16_PEAK_FLOPS = 2.5e15   # MI355X dense bf16 matrix peak
+
+
+def combined_roofline_us(w, T, L_total):
+    """Sum over the step's stages of max(bytes / HBM peak, flops / bf16 MFMA
+    peak): the floor when the node GEMMs reach the ridge (many tree rows)."""
+    d, V, K, B, H, Dh = w.d, w.V, w.K, w.B, w.H, w.Dh
+    M = B * T
+    logits = 2 * 4 * K * V * B if w.mode == "exact" else 0
+    stages = [  # (bytes, flops)
+        (2 * K * d * d, 2 * B * K * d * d),                  # W1
+        (2 * K * V * d + logits, 2 * B * K * V * d),         # W2
+        (2 * 3 * d * d + 2 * d * M, 2 * M * 3 * d * d),      # QKV (+ E rows)
+        (2 * 2 * H * Dh * L_total, 4 * H * Dh * T * L_total),  # prefix attention
+        (2 * d * d, 2 * M * d * d),                          # output projection
+        (2 * V * d, 2 * M * V * d),                          # LM head
+    ]
+    return sum(max(b / (HBM_PEAK_GBS * 1e9), f / MFMA_BF16_PEAK_FLOPS) for b, f in stages) * 1e6
 
 
 def _oracle_rest(w, inp, topk):
@@ -264,6 +293,10 @@ def main():
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="before the timed loop, run a plain device-to-device copy of this "
                          "many bytes 3 times (a known-size kernel for scaling HBM counters)")
+    ap.add_argument("--workload", default=WORKLOAD,
+                    choices=["vicuna7b_typical", "vicuna13b_typical", "vicuna7b_batch8_ragged",
+                             "vicuna7b_exact"],
+                    help="workload to time (default: the 7B typical-acceptance step)")
     ap.add_argument("--decode", action="store_true",
                     help="print the decoding-loop report (A, A/r) instead of the step line")
     args = ap.parse_args()
@@ -283,7 +316,7 @@ def main():
     from medusa_tree_verification_forward_amd.step import VerifyStep
     from workloads import WORKLOADS, make_inputs
 
-    w = WORKLOADS[WORKLOAD]
+    w = WORKLOADS[args.workload]
     inp = make_inputs(w)
     st = VerifyStep(inp, H=w.H, Dh=w.Dh, s_max=w.s_max, mode=w.mode, tau=w.tau, eps=w.eps,
                     delta=w.delta, theta=w.rope_theta)
@@ -357,9 +390,13 @@ def main():
     w2b = w2_kernel_bytes(w)
     achieved = w2b / (w2_ms * 1e-3) / 1e9
     res = st.results()
+    comb_us = combined_roofline_us(w, T, L_total)
+    accept = {"typical": f"typical eps={w.eps} delta={w.delta} tau={w.tau}",
+              "greedy": "greedy", "exact": f"exact p/q rejection, tau={w.tau}"}[w.mode]
+    metric = ("Medusa verify-steps/sec at 7B shapes (K=5, 45-node tree, 2k KV); % HBM roofline"
+              if w.name == WORKLOAD else f"Medusa verify-steps/sec, {w.name}; % HBM roofline")
     line = {
-        "metric": "Medusa verify-steps/sec at 7B shapes (K=5, 45-node tree, 2k KV); "
-                  "% HBM roofline",
+        "metric": metric,
         "value": 1000.0 / ms_step,
         "unit": "steps/s",
         "n_gpus": 1,
@@ -370,27 +407,29 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16",
-        "data": "synthetic (seeded Gaussian weights and KV of Vicuna-7B shapes)",
+        "data": f"synthetic (seeded Gaussian weights and KV, {w.name} shapes)",
         "timing": (("replays of one recorded graph" if graph is not None else "eager launches")
                    + (" (prefix-length reset + medusa_step)" if args.reset_kv_len else
                       " (medusa_step; advanced prefix lengths written to a separate buffer, "
                       "so every step runs over the same prefix)")),
         "config": {"workload": w.name, "batch": w.B, "d": w.d, "V": w.V, "heads": w.K,
-                   "tree": "top-(3,2,2,1,1)", "tree_nodes": T - 1, "prefix_kv": L_total,
-                   "attn": f"{w.H}x{w.Dh}", "accept": f"typical eps={w.eps} delta={w.delta} "
-                                                    f"tau={w.tau}"},
+                   "tree": f"top-{w.s}".replace(" ", ""), "tree_nodes": T - 1,
+                   "prefix_kv": L_total, "attn": f"{w.H}x{w.Dh}", "accept": accept},
         "step_roofline": {"bound": "hbm", "algorithmic_bytes": alg,
                           "achieved_GBs": alg / (ms_step * 1e-3) / 1e9, "peak": HBM_PEAK_GBS,
-                          "frac": alg / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS},
+                          "frac": alg / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                          "combined_floor_us": comb_us,
+                          "combined_frac": comb_us / (ms_step * 1e3)},
         "roofline": {"kernel": "heads_w2 (vocabulary projection + fused top-s)",
                      "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": recorded_traffic(),
+                     "frac": achieved / HBM_PEAK_GBS,
+                     "traffic": recorded_traffic() if w.name == WORKLOAD else None,
                      "avg_us": w2_ms * 1e3, "bytes_per_launch": w2b,
                      "timing": "HIP events recorded on the launch stream around every W2 "
                                "launch, over a second pass of the K timed steps"},
         "accept_len": [int(x) for x in res["accept_len"]],
     }
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and w.name == WORKLOAD:
         line["cpu_baseline"] = cpu_baseline(w, inp)
     print(json.dumps(line), flush=True)
 
