@@ -120,7 +120,7 @@ size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 struct Layout {
   size_t counters = 0;
   // heads
-  size_t z = 0, part_val = 0, part_id = 0, part_m = 0, part_s = 0;
+  size_t z = 0, part_val = 0, part_id = 0, part_m = 0, part_s = 0, afrag = 0;
   int G = 0;
   // attention
   size_t att_o = 0, att_ml = 0;
@@ -152,6 +152,7 @@ Layout layout_for(const medusa_shape* s) {
   L.part_id = take(B * K * Gmax * S * 4);
   L.part_m = take(B * K * Gmax * 4);
   L.part_s = take(B * K * Gmax * 4);
+  L.afrag = take((K + 1) * 32 * d);
   const size_t T = s->N + 1, H = s->H, Dh = s->Dh, V = s->V;
   const size_t es = s->dtype == MEDUSA_F32 ? 4 : 2;
   L.NS = attn_splits(s->Lmax);
@@ -318,6 +319,7 @@ int heads_impl(const medusa_shape* shape, const float* h, const void* W1,
   a.part_id = at<int>(workspace, L.part_id);
   a.part_m = at<float>(workspace, L.part_m);
   a.part_s = at<float>(workspace, L.part_s);
+  a.afrag = at<char>(workspace, L.afrag);
   a.G = L.G;
   a.w1_rows_per_wave = w1_rows(shape->K * shape->d);
   {

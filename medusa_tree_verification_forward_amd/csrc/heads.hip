@@ -405,34 +405,17 @@ __device__ __forceinline__ void stats_merge(float& m, float& s, float m2, float 
   m = mn;
 }
 
-// ---------------------------------------------------------------------------
-// l = W2_k z_k for the rows of one block; top-S and (max, sum exp) of them.
-// grid = (G, K): wave w of block g of head k streams rows
-// [(g*4 + w) * rpw, ... + rpw) of head k.
-// Partial records: part_val/part_id [B][K][G][S], part_m/part_s [B][K][G].
-template <class ET, int NB, int SPR>
-__global__ __launch_bounds__(kHeadWaves * 64, 4) void heads_w2_kernel(
-    const float* __restrict__ z, int B, int b0, int K, int V, int d,
-    const typename ET::storage* __restrict__ W2, int rpw, int S,
-    float* __restrict__ head_logits, float* __restrict__ part_val, int* __restrict__ part_id,
-    float* __restrict__ part_m, float* __restrict__ part_s, int G, int interleave) {
-  extern __shared__ float xs[];   // [NB][ldx], then per-wave list exchange
-  constexpr int CW = RowStream<ET, NB>::CW;
-  const int ldx = (d + CW - 1) / CW * CW;
-  const int k = blockIdx.y, g = blockIdx.x;
-  const int nb = min(NB, B - b0);
+// Per-wave top-S and softmax statistics of the rows in win (lane l: row
+// rb + l rstride, valid below nrows), merged over the workgroup's waves
+// through LDS (xs, at least kHeadWaves NB (2 MAXS_LDS + 2) floats; the
+// caller's last use of it must be done) into one partial record per vector.
+template <int NB>
+__device__ __forceinline__ void w2_finish(const float (&win)[NB], int nb, int b0, int K, int k,
+                                          int V, int G, int g, int rb, int rstride, int nrows,
+                                          int S, float* xs, float* __restrict__ head_logits,
+                                          float* __restrict__ part_val, int* __restrict__ part_id,
+                                          float* __restrict__ part_m, float* __restrict__ part_s) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  int rb, rstride, nrows;
-  wave_rows(g * kHeadWaves + wave, gridDim.x * kHeadWaves, rpw, V, interleave != 0, rb, rstride,
-            nrows);
-  HeadStream<ET, NB, SPR> rs;
-  stage_and_start<ET, NB>(rs, z + ((size_t)b0 * K + k) * d, (size_t)K * d, nb, d, xs, ldx,
-                          W2 + (size_t)k * V * d, rb, rstride, nrows, 0);
-  float win[NB];
-#pragma unroll
-  for (int b = 0; b < NB; ++b) win[b] = kNegInf;
-  if (nrows > 0) rs.run(xs, ldx, win);
-
   float tv[NB], m[NB], s[NB];
   int ti[NB];
   const bool valid = lane < nrows;
@@ -508,6 +491,218 @@ __global__ __launch_bounds__(kHeadWaves * 64, 4) void heads_w2_kernel(
       }
     }
   }
+}
+
+// ---------------------------------------------------------------------------
+// l = W2_k z_k for the rows of one block; top-S and (max, sum exp) of them.
+// grid = (G, K): wave w of block g of head k streams rows
+// [(g*4 + w) * rpw, ... + rpw) of head k.
+// Partial records: part_val/part_id [B][K][G][S], part_m/part_s [B][K][G].
+template <class ET, int NB, int SPR>
+__global__ __launch_bounds__(kHeadWaves * 64, 4) void heads_w2_kernel(
+    const float* __restrict__ z, int B, int b0, int K, int V, int d,
+    const typename ET::storage* __restrict__ W2, int rpw, int S,
+    float* __restrict__ head_logits, float* __restrict__ part_val, int* __restrict__ part_id,
+    float* __restrict__ part_m, float* __restrict__ part_s, int G, int interleave) {
+  extern __shared__ float xs[];   // [NB][ldx], then per-wave list exchange
+  constexpr int CW = RowStream<ET, NB>::CW;
+  const int ldx = (d + CW - 1) / CW * CW;
+  const int k = blockIdx.y, g = blockIdx.x;
+  const int nb = min(NB, B - b0);
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  int rb, rstride, nrows;
+  wave_rows(g * kHeadWaves + wave, gridDim.x * kHeadWaves, rpw, V, interleave != 0, rb, rstride,
+            nrows);
+  HeadStream<ET, NB, SPR> rs;
+  stage_and_start<ET, NB>(rs, z + ((size_t)b0 * K + k) * d, (size_t)K * d, nb, d, xs, ldx,
+                          W2 + (size_t)k * V * d, rb, rstride, nrows, 0);
+  float win[NB];
+#pragma unroll
+  for (int b = 0; b < NB; ++b) win[b] = kNegInf;
+  if (nrows > 0) rs.run(xs, ldx, win);
+
+  w2_finish<NB>(win, nb, b0, K, k, V, G, g, rb, rstride, nrows, S, xs, head_logits, part_val,
+                part_id, part_m, part_s);
+}
+
+// ---------------------------------------------------------------------------
+// Batched head streams: 3 to 8 activation vectors over bf16 weights.
+//
+// With several vectors the weights are multiplied in the plain MFMA product
+// layout. Weight tile (rows r_0..r_15, column block t) is 16 rows by 32
+// columns: lane (j, q) = (l % 16, l / 16) takes the 16 bytes of row r_j at
+// column 32 t + 8 q as its B fragment (64 contiguous bytes of each row). The
+// A fragment of column block t holds the same columns for 16 operand rows,
+// row 2 s + p being part p (bf16 hi, lo as above) of vector s, so one
+// v_mfma_f32_16x16x32_bf16 per 1 KB tile accumulates the partial sums of
+// every vector for 16 weight rows. Entry (i, j) of the product sits in lane
+// j + 16 (i / 4) as element i % 4: lane (j, q) holds vectors 2 q (elements
+// 0 + 1) and 2 q + 1 (elements 2 + 3) of row r_j. The A fragments of a
+// vector set (32 d bytes) are built once and read from global memory, where
+// they stay in L2, so the LDS holds nothing per vector and several
+// workgroups share a compute unit.
+constexpr int kTileVecs = 8;   // vectors per batched pass
+
+__device__ __forceinline__ uint32_t bf16_part_bits(float x, int p) {
+  const uint32_t hi = f32_to_bf16_bits(x);
+  return p ? f32_to_bf16_bits(x - __uint_as_float(hi << 16)) : hi;
+}
+
+// A fragments of nb <= 8 fp32 vectors (src + s * stride, d values each; zero
+// rows for s >= nb): frag[64 t + l] is part l % 2 of vector (l % 16) / 2 at
+// columns 32 t + 8 (l / 16) .. + 7. One thread per fragment.
+__global__ __launch_bounds__(256) void act_frag_kernel(const float* __restrict__ src,
+                                                       size_t stride, int nb, int d,
+                                                       u32x4_t* __restrict__ frag) {
+  const int idx = blockIdx.x * 256 + threadIdx.x;
+  if (idx >= (d / 32) * 64) return;
+  const int t = idx >> 6, l = idx & 63, i = l & 15, v = i >> 1;
+  u32x4_t out = {0u, 0u, 0u, 0u};
+  if (v < nb) {
+    const float* p = src + (size_t)v * stride + 32 * t + 8 * (l >> 4);
+    const floatx4_t x0 = *reinterpret_cast<const floatx4_t*>(p);
+    const floatx4_t x1 = *reinterpret_cast<const floatx4_t*>(p + 4);
+    const int part = i & 1;
+    out[0] = bf16_part_bits(x0[0], part) | (bf16_part_bits(x0[1], part) << 16);
+    out[1] = bf16_part_bits(x0[2], part) | (bf16_part_bits(x0[3], part) << 16);
+    out[2] = bf16_part_bits(x1[0], part) | (bf16_part_bits(x1[1], part) << 16);
+    out[3] = bf16_part_bits(x1[2], part) | (bf16_part_bits(x1[3], part) << 16);
+  }
+  frag[idx] = out;
+}
+
+// NG tile rows of one wave over nt column blocks, DS blocks (NG DS tiles and
+// DS A fragments) in flight: wp[g] points at the lane's 8 weights of the
+// first block in group g, ap at its A fragment of the first block. Requires
+// nt a positive multiple of DS. The weight loads are plain (cached) loads: a
+// tile reads half of each 128-byte line and the next block the other half,
+// and with the non-temporal hint the line was often gone by then (37% more
+// HBM traffic).
+template <int NG, int DS>
+__device__ __forceinline__ void tile_stream(const uint16_t* const (&wp)[NG],
+                                            const u32x4_t* __restrict__ ap, int nt,
+                                            floatx4_t (&acc)[NG]) {
+  u32x4_t wr[DS][NG], ar[DS];
+#pragma unroll
+  for (int j = 0; j < DS; ++j) {
+#pragma unroll
+    for (int g = 0; g < NG; ++g) wr[j][g] = load16(wp[g] + 32 * j);
+    ar[j] = load16(ap + 64 * j);
+  }
+#pragma unroll
+  for (int g = 0; g < NG; ++g) acc[g] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+  int t = 0;
+  for (; t + DS < nt; t += DS) {
+#pragma unroll
+    for (int j = 0; j < DS; ++j) {
+      const int tn = t + DS + j;
+#pragma unroll
+      for (int g = 0; g < NG; ++g) {
+        acc[g] = mfma16x16x32_bf16(ar[j], wr[j][g], acc[g]);
+        wr[j][g] = load16(wp[g] + 32 * tn);
+      }
+      ar[j] = load16(ap + 64 * tn);
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < DS; ++j)
+#pragma unroll
+    for (int g = 0; g < NG; ++g) acc[g] = mfma16x16x32_bf16(ar[j], wr[j][g], acc[g]);
+}
+
+// W1 over 3..8 vectors: z[b][k][i] as heads_w1_kernel computes it, plus the
+// A fragments of z for the W2 pass (zfrag[k], layout as act_frag_kernel's).
+// A workgroup takes 16 (4 / KS) consecutive rows of the K d rows: wave w
+// streams rows 16 (w / KS) .. + 15 over column blocks of part w % KS of d,
+// and the KS partial tiles are summed through LDS in part order.
+template <int KS, int DS>
+__global__ __launch_bounds__(kHeadWaves * 64, 4) void heads_w1_tile_kernel(
+    const float* __restrict__ h, int B, int b0, int K, int d, const uint16_t* __restrict__ W1,
+    const float* __restrict__ b1, const u32x4_t* __restrict__ hfrag, float* __restrict__ z,
+    uint16_t* __restrict__ zfrag) {
+  constexpr int RS = kHeadWaves / KS;   // row sets of 16 per workgroup
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int j = lane & 15, q = lane >> 4;
+  const int set = wave / KS, part = wave % KS;
+  const int nb = min(kTileVecs, B - b0);
+  const int total = K * d;
+  const int row = min((blockIdx.x * RS + set) * 16 + j, total - 1);
+  const int k = row / d, i = row - k * d;
+  const int nblk = d / 32, per = nblk / KS;
+  // residuals h[b0 + 2 q + e][i] and the bias, read before the stream
+  float hres[2];
+#pragma unroll
+  for (int e = 0; e < 2; ++e) hres[e] = h[(size_t)(b0 + min(2 * q + e, nb - 1)) * d + i];
+  const float bias = b1 ? b1[row] : 0.f;
+  const uint16_t* wp[1] = {W1 + (size_t)row * d + 32 * per * part + 8 * q};
+  floatx4_t acc[1];
+  tile_stream<1, DS>(wp, hfrag + (size_t)per * part * 64 + lane, per, acc);
+  if constexpr (KS > 1) {
+    __shared__ floatx4_t red[RS][KS - 1][64];
+    if (part > 0) red[set][part - 1][lane] = acc[0];
+    __syncthreads();
+    if (part > 0) return;
+#pragma unroll
+    for (int u = 0; u < KS - 1; ++u) acc[0] += red[set][u][lane];
+  }
+  if ((blockIdx.x * RS + set) * 16 + j >= total) return;
+#pragma unroll
+  for (int e = 0; e < 2; ++e) {
+    const int v = 2 * q + e;
+    float zv = 0.f;
+    if (v < nb) {
+      const float u = acc[0][2 * e] + acc[0][2 * e + 1] + bias;
+      zv = hres[e] + u * (1.f / (1.f + exp_e(-u)));
+      z[((size_t)(b0 + v) * K + k) * d + i] = zv;
+    }
+    // operand rows 2 v (hi) and 2 v + 1 (lo) of column i in head k's fragments
+    uint16_t* f = zfrag + ((((size_t)k * nblk + (i >> 5)) * 64 + 16 * ((i & 31) >> 3) + 2 * v) * 8 +
+                           (i & 7));
+    f[0] = (uint16_t)bf16_part_bits(zv, 0);
+    f[8] = (uint16_t)bf16_part_bits(zv, 1);
+  }
+}
+
+// W2 over 3..8 vectors: the records of heads_w2_kernel. Wave w of block g of
+// head k streams 16 NG consecutive rows as NG tile rows over all of d (the
+// rows of a wave stay within a few pages; rows interleaved over the waves
+// spread every wave over the whole head); the values are moved to lane = row
+// (lane 16 g + j takes row j of tile row g) for the shared top-S epilogue.
+template <int NG, int DS>
+__global__ __launch_bounds__(kHeadWaves * 64, 4) void heads_w2_tile_kernel(
+    int B, int b0, int K, int V, int d, const uint16_t* __restrict__ W2,
+    const u32x4_t* __restrict__ zfrag, int S, float* __restrict__ head_logits,
+    float* __restrict__ part_val, int* __restrict__ part_id, float* __restrict__ part_m,
+    float* __restrict__ part_s, int G) {
+  __shared__ float xs[kHeadWaves * kTileVecs * (2 * MAXS_LDS + 2)];
+  const int k = blockIdx.y, g = blockIdx.x;
+  const int nb = min(kTileVecs, B - b0);
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int j = lane & 15, q = lane >> 4;
+  int rb, rstride, nrows;
+  wave_rows(g * kHeadWaves + wave, gridDim.x * kHeadWaves, 16 * NG, V, false, rb, rstride, nrows);
+  float win[kTileVecs];
+#pragma unroll
+  for (int b = 0; b < kTileVecs; ++b) win[b] = kNegInf;
+  if (nrows > 0) {
+    const uint16_t* wp[NG];
+#pragma unroll
+    for (int tg = 0; tg < NG; ++tg)
+      wp[tg] = W2 + ((size_t)k * V + rb + (size_t)min(16 * tg + j, nrows - 1) * rstride) * d + 8 * q;
+    floatx4_t acc[NG];
+    tile_stream<NG, DS>(wp, zfrag + (size_t)k * (d / 32) * 64 + lane, d / 32, acc);
+#pragma unroll
+    for (int tg = 0; tg < NG; ++tg) {
+      const float v0 = acc[tg][0] + acc[tg][1], v1 = acc[tg][2] + acc[tg][3];
+#pragma unroll
+      for (int b = 0; b < kTileVecs; ++b) {
+        const float x = __shfl(b & 1 ? v1 : v0, j + 16 * (b >> 1));
+        if (q == tg) win[b] = x;
+      }
+    }
+  }
+  w2_finish<kTileVecs>(win, nb, b0, K, k, V, G, g, rb, rstride, nrows, S, xs, head_logits,
+                       part_val, part_id, part_m, part_s);
 }
 
 // ---------------------------------------------------------------------------
@@ -689,12 +884,94 @@ hipError_t launch_heads_nb(const HeadsArgs& a, int b0, hipStream_t st) {
   return launch_heads_spr<ET, NB, 0>(a, b0, st);
 }
 
+// Batched passes (3 or more vectors, bf16): W1 split over KS waves with DS
+// column blocks in flight, W2 in tile rows of NG with DS in flight.
+// MEDUSA_HEAD_TILE=0 keeps the per-row streams; MEDUSA_W1_TILE_KS (1, 2, 4)
+// and MEDUSA_W2_TILE_NG (3, 4) choose the shapes where d allows (default
+// 4 and 3: 48 rows a wave measured 4% faster than 64 at batch 8).
+bool head_tile() {
+  static const bool v = [] {
+    const char* s = getenv("MEDUSA_HEAD_TILE");
+    return !(s && *s && atoi(s) == 0);
+  }();
+  return v;
+}
+int env_choice(const char* name, int dflt) {
+  const char* s = getenv(name);
+  return s && *s ? atoi(s) : dflt;
+}
+int w2_tile_ng() {
+  static const int v = env_choice("MEDUSA_W2_TILE_NG", 3) == 4 ? 4 : 3;
+  return v;
+}
+// rows per W2 workgroup of the batched pass
+int w2_tile_rows() { return kHeadWaves * 16 * w2_tile_ng(); }
+
+hipError_t launch_heads_tile(const HeadsArgs& a, int b0, int G, hipStream_t st) {
+  const int nb = std::min(kTileVecs, a.B - b0);
+  const int d = a.d, nblk = d / 32;
+  u32x4_t* hfrag = reinterpret_cast<u32x4_t*>(a.afrag);
+  u32x4_t* zfrag = hfrag + (size_t)nblk * 64;
+  hipLaunchKernelGGL(act_frag_kernel, dim3((nblk * 64 + 255) / 256), dim3(256), 0, st,
+                     a.h + (size_t)b0 * d, (size_t)d, nb, d, hfrag);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const uint16_t* W1 = reinterpret_cast<const uint16_t*>(a.W1);
+  uint16_t* zf16 = reinterpret_cast<uint16_t*>(zfrag);
+  const int ks_env = env_choice("MEDUSA_W1_TILE_KS", 4);
+  const int total = a.K * d;
+#define W1_TILE(KS, DS)                                                                        \
+  hipLaunchKernelGGL((heads_w1_tile_kernel<KS, DS>),                                           \
+                     dim3((total + 16 * (kHeadWaves / KS) - 1) / (16 * (kHeadWaves / KS))),    \
+                     dim3(kHeadWaves * 64), 0, st, a.h, a.B, b0, a.K, d, W1, a.b1, hfrag, a.z, \
+                     zf16)
+  if (ks_env >= 4 && nblk % 32 == 0)
+    W1_TILE(4, 8);
+  else if (ks_env >= 2 && nblk % 16 == 0)
+    W1_TILE(2, 8);
+  else if (nblk % 8 == 0)
+    W1_TILE(1, 8);
+  else
+    W1_TILE(1, 2);
+#undef W1_TILE
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  if (a.ev_before) {
+    e = hipEventRecord(a.ev_before, st);
+    if (e != hipSuccess) return e;
+  }
+  const uint16_t* W2 = reinterpret_cast<const uint16_t*>(a.W2);
+#define W2_TILE(NG, DS)                                                                       \
+  hipLaunchKernelGGL((heads_w2_tile_kernel<NG, DS>), dim3(G, a.K), dim3(kHeadWaves * 64), 0, st, \
+                     a.B, b0, a.K, a.V, d, W2, zfrag, a.S, a.head_logits, a.part_val,          \
+                     a.part_id, a.part_m, a.part_s, G)
+  if (w2_tile_ng() == 3 && nblk % 4 == 0)
+    W2_TILE(3, 4);
+  else if (w2_tile_ng() == 3)
+    W2_TILE(3, 2);
+  else if (nblk % 4 == 0)
+    W2_TILE(4, 4);
+  else
+    W2_TILE(4, 2);
+#undef W2_TILE
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  if (a.ev_after) e = hipEventRecord(a.ev_after, st);
+  return e;
+}
+
 template <class ET>
 hipError_t launch_heads_et(const HeadsArgs& a, hipStream_t st) {
+  // Three or more bf16 vectors go through the batched passes, all of them
+  // (the merge reads every sequence's records with one row-block count).
+  const bool tile = std::is_same<ET, BF16>::value && a.B >= 3 && head_tile() && a.afrag;
+  const int G = tile ? (a.V + w2_tile_rows() - 1) / w2_tile_rows() : a.G;
   for (int b0 = 0; b0 < a.B; b0 += 8) {
     const int nb = a.B - b0;
     hipError_t e;
-    if (nb == 1)
+    if (tile)
+      e = launch_heads_tile(a, b0, G, st);
+    else if (nb == 1)
       e = launch_heads_nb<ET, 1>(a, b0, st);
     else if (nb == 2)
       e = launch_heads_nb<ET, 2>(a, b0, st);
@@ -715,7 +992,7 @@ hipError_t launch_heads_et(const HeadsArgs& a, hipStream_t st) {
   }
 #define MERGE_LAUNCH(SM)                                                                      \
   hipLaunchKernelGGL(heads_merge_kernel<SM>, dim3(a.K, a.B), dim3(kMergeThreads), 0, st, a.K, \
-                     a.G, a.S, a.part_val, a.part_id, a.part_m, a.part_s, a.topk_ids,          \
+                     G, a.S, a.part_val, a.part_id, a.part_m, a.part_s, a.topk_ids,            \
                      a.topk_logits, a.lse, tr)
   if (a.S <= 4)
     MERGE_LAUNCH(4);

@@ -40,6 +40,7 @@ struct HeadsArgs {
   int* part_id;           // [B][K][G][S]
   float* part_m;          // [B][K][G]
   float* part_s;          // [B][K][G]
+  void* afrag;            // (K + 1) * 32 * d bytes: MFMA A fragments of the batched passes
   int G;                  // row blocks per head (4 waves of w2_rows_per_wave rows)
   int w1_rows_per_wave;   // 1..64
   int w2_rows_per_wave;   // 4..64

@@ -69,8 +69,13 @@ SMALL = [
     scaled(WORKLOADS["vicuna7b_typical"], d=512, V=2999, H=4, Dh=128),
     # batch of 3 (ragged batch tile), fp32
     scaled(WORKLOADS["tiny_fp32"], B=3, V=777),
-    # batch of 8 bf16
+    # batches of 3 or more bf16 vectors (the batched MFMA passes): 8 at d=256,
+    # 3 at d=512, 11 (passes of 8 and 3) at d=1024, 5 at d=320 (odd column
+    # block count)
     scaled(WORKLOADS["vicuna7b_batch8_ragged"], d=256, V=1500, H=2, Dh=128),
+    scaled(WORKLOADS["vicuna7b_batch8_ragged"], B=3, d=512, V=2999, H=4, Dh=128),
+    scaled(WORKLOADS["vicuna7b_batch8_ragged"], B=11, d=1024, V=1000, H=8, Dh=128),
+    scaled(WORKLOADS["vicuna7b_batch8_ragged"], B=5, d=320, V=777, H=5, Dh=64),
     # wide pools (s_max = 16)
     scaled(WORKLOADS["tiny_fp32"], s=(16, 2), K=2, V=4000),
 ]
@@ -138,3 +143,23 @@ def test_heads_full_size_7b():
         rows = rng.integers(0, w.V, size=64)
         for r in rows:
             assert abs(g["logits"][0, k, r] - float(W2k[r] @ z[0, k])) < 1e-4
+
+
+def test_heads_full_size_batch8():
+    # Eight 7B-shaped sequences: the batched passes at the launch configuration
+    # of the batch-8 workload; W1 in full, W2 on sampled rows of every head.
+    w = WORKLOADS["vicuna7b_batch8_ragged"]
+    inp = make_inputs(w, only=("W1", "W2"))
+    g = _run_heads(w, inp)
+    _check_topk_on_own_logits(g)
+    z = np.empty((w.B, w.K, w.d))
+    for k in range(w.K):
+        z[:, k] = OH.residual_block(inp["W1"][k], inp["h"].astype(np.float64))
+    assert_close(g["z"], z, 1e-5, "z")
+    rng = np.random.default_rng(1)
+    for k in range(w.K):
+        rows = np.sort(rng.choice(w.V, size=256, replace=False))
+        ref = ON.widen(inp["W2"][k][rows]) @ z[:, k].T          # [rows][B]
+        assert_close(g["logits"][:, k, rows], ref.T, 1e-5, f"head {k} sampled logits")
+        for b in range(w.B):
+            assert abs(g["lse"][b, k] - OH.log_sum_exp(g["logits"][b, k].astype(np.float64))) < 1e-4
