@@ -1,0 +1,164 @@
+// Inverse-CDF draws over V non-negative weights in one 1024-thread
+// workgroup: a drafted token from a head softmax ("Medusa 深读", sampling
+// the candidates in the exact acceptance setting) and the next root from the
+// target or residual distribution ("Medusa Part I", Part 2, the rejection
+// rule's resampling step).
+//
+// The CDF is a fixed sum that is monotone by construction. Chunks of CS
+// consecutive tokens (CS a multiple of 8, at most kCdfChunks chunks) are each
+// summed in token order by one lane; groups of 64 consecutive chunks carry
+// the running sum F of their chunks, taken in order; group totals are
+// combined in order into E. For token x in chunk c of group g,
+//   C(x) = E[g] + (F[c] + (w_first(c) + ... + w_x)),
+// and every step adds a non-negative weight to the value before it, so C
+// never decreases. The last chunk of a group ends at exactly E[g + 1], and
+// chunk c ends at exactly E[g] + F[c + 1]. A draw with uniform u is the
+// smallest x with C(x) > u * C(V - 1), clamped to the last token with a
+// positive weight (reached only when rounding puts u * C(V - 1) at the top).
+#pragma once
+
+#include "common.h"
+
+namespace medusa {
+
+constexpr int kCdfThreads = 1024;
+constexpr int kCdfChunks = 2048;
+constexpr int kCdfGroups = kCdfChunks / 64;
+
+struct CdfLds {
+  float cs[kCdfChunks];      // chunk sums
+  float F[kCdfChunks];       // running sum of the group's chunks before chunk c
+  float E[kCdfGroups + 1];   // running sum of the groups before group g; E[ng] = total
+  int ng, nch, csz, last_nz;
+};
+
+// Tokens per chunk: 8, doubled until the chunks fit (16 for a 32000 vocabulary).
+__host__ __device__ inline int cdf_chunk_size(int V) {
+  int cs = 8;
+  while ((V + cs - 1) / cs > kCdfChunks) cs *= 2;
+  return cs;
+}
+
+// Weights of tokens x0 .. x0 + N - 1 (zero past V). The weights are read at
+// clamped indices without a condition, so all N loads are in flight before
+// the first is used; tokens past V are zeroed afterwards.
+template <int N, class Wf>
+__device__ __forceinline__ void cdf_weights(const Wf& w, int x0, int V, float (&wv)[N]) {
+#pragma unroll
+  for (int i = 0; i < N; ++i) wv[i] = w(max(min(x0 + i, V - 1), 0));
+#pragma unroll
+  for (int i = 0; i < N; ++i) wv[i] = x0 + i < V ? wv[i] : 0.f;
+}
+
+// Sequential sum of chunk c's weights in token order, its last positive
+// token in *last; N tokens loaded at a time.
+template <int N, class Wf>
+__device__ __forceinline__ float cdf_chunk_sum(const Wf& w, int c, int csz, int V, int* last) {
+  float s = 0.f;
+  for (int i0 = 0; i0 < csz; i0 += N) {
+    float wv[N];
+    cdf_weights<N>(w, c * csz + i0, V, wv);
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      s += wv[i];
+      if (wv[i] > 0.f) *last = c * csz + i0 + i;
+    }
+  }
+  return s;
+}
+
+// Build the CDF of w(0 .. V-1) into sh. Every thread of the workgroup calls
+// it; ends with a barrier.
+template <class Wf>
+__device__ void cdf_build(const Wf& w, int V, CdfLds& sh) {
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int csz = cdf_chunk_size(V);
+  const int nch = (V + csz - 1) / csz;
+  const int ng = (nch + 63) / 64;
+  if (t == 0) sh.last_nz = -1;
+  __syncthreads();
+  int my_last = -1;
+  // wave w sums the rows of 64 chunks w, w + 16, ...; lane l chunk 64 r + l
+  for (int c0 = 64 * wave; c0 < nch; c0 += 64 * (kCdfThreads / 64)) {
+    const int c = c0 + lane;
+    const float s = csz == 8 ? cdf_chunk_sum<8>(w, c, csz, V, &my_last)
+                             : cdf_chunk_sum<16>(w, c, csz, V, &my_last);
+    if (c < nch) sh.cs[c] = s;   // chunks past nch hold only tokens >= V
+  }
+  {
+    // token indices are exact in float (V < 2^24)
+    const int wl = (int)wave_max((float)my_last);
+    if (lane == 0) atomicMax(&sh.last_nz, wl);   // LDS atomic, one per wave
+  }
+  __syncthreads();
+  if (t < ng) {
+    float f = 0.f;
+    const int end = min(64 * t + 64, nch);
+#pragma unroll 8
+    for (int c = 64 * t; c < end; ++c) {
+      sh.F[c] = f;
+      f = f + sh.cs[c];
+    }
+    sh.E[t + 1] = f;   // the group's total, until the pass below
+  }
+  __syncthreads();
+  if (t == 0) {
+    float e = 0.f;
+    for (int g = 0; g < ng; ++g) {
+      const float gt = sh.E[g + 1];
+      sh.E[g] = e;
+      e = e + gt;
+    }
+    sh.E[ng] = e;
+    sh.ng = ng;
+    sh.nch = nch;
+    sh.csz = csz;
+  }
+  __syncthreads();
+}
+
+// One draw with uniform u from a built CDF (any single thread).
+template <class Wf>
+__device__ int cdf_draw(const Wf& w, int V, float u, const CdfLds& sh) {
+  const int ng = sh.ng, nch = sh.nch, csz = sh.csz;
+  const float target = u * sh.E[ng];
+  int x = -1;
+  // first group ending above the target
+  int lo = 0, hi = ng;
+  while (lo < hi) {
+    const int mid = (lo + hi) >> 1;
+    if (sh.E[mid + 1] > target)
+      hi = mid;
+    else
+      lo = mid + 1;
+  }
+  if (lo < ng) {
+    const int g = lo;
+    const float eg = sh.E[g];
+    // first chunk of the group ending above the target (its last chunk does)
+    int a = 64 * g, bnd = min(64 * g + 64, nch) - 1;
+    while (a < bnd) {
+      const int mid = (a + bnd) >> 1;
+      if (eg + (sh.F[mid] + sh.cs[mid]) > target)
+        bnd = mid;
+      else
+        a = mid + 1;
+    }
+    const int c = a;
+    const float fc = sh.F[c];
+    float local = 0.f;
+    for (int i0 = 0; i0 < csz && x < 0; i0 += 8) {
+      float wv[8];
+      cdf_weights<8>(w, c * csz + i0, V, wv);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        local += wv[i];
+        if (x < 0 && eg + (fc + local) > target) x = c * csz + i0 + i;
+      }
+    }
+  }
+  if (x < 0 || x > sh.last_nz) x = sh.last_nz < 0 ? V - 1 : sh.last_nz;
+  return x;
+}
+
+}  // namespace medusa

@@ -17,6 +17,7 @@
 // (depth, -index) maximum is found with DPP wave reductions.
 // Exact: one 1024-thread workgroup per sequence walks the tree; each p/q
 // step is a block-wide pass over the vocabulary.
+#include "cdf.h"
 #include "common.h"
 #include "kernels.h"
 
@@ -196,85 +197,14 @@ __device__ float block_max(float v, float* red) {
   return s;
 }
 
-// Inverse-CDF draw from the non-negative weights w[0..V): the same fixed
-// two-level sum as the tree sampler (chunk per thread, 64 groups of 16
-// chunks, groups combined in order); smallest x with C(x) > u * C(V-1),
-// clamped to the last positive weight.
-__device__ int block_inverse_cdf(const float* w, int V, float u, float* cs, float* F, float* E,
-                                 int* last_nz) {
-  const int t = threadIdx.x;
-  const int csz = (V + 1023) / 1024;
-  float s = 0.f;
-  int my_last = -1;
-  for (int i = 0; i < csz; ++i) {
-    const int v = t * csz + i;
-    if (v < V) {
-      s += w[v];
-      if (w[v] > 0.f) my_last = v;
-    }
-  }
-  __syncthreads();
-  cs[t] = s;
-  if (t == 0) *last_nz = -1;
-  __syncthreads();
-  atomicMax(last_nz, my_last);
-  if (t < 64) {
-    float f = 0.f;
-    for (int j = 0; j < 16; ++j) {
-      F[t * 16 + j] = f;
-      f = f + cs[t * 16 + j];
-    }
-    E[t + 1] = f;
-  }
-  __syncthreads();
-  if (t == 0) {
-    float e = 0.f;
-    for (int g = 0; g < 64; ++g) {
-      const float gt = E[g + 1];
-      E[g] = e;
-      e = e + gt;
-    }
-    E[64] = e;
-  }
-  __syncthreads();
-  // thread t tests whether the draw falls in its chunk
-  const float target = u * E[64];
-  const int g = t >> 4;
-  const float eg = E[g];
-  const float lo = eg + F[t];
-  const float hi = eg + (F[t] + cs[t]);
-  __shared__ int found;
-  if (t == 0) found = 0x7fffffff;
-  __syncthreads();
-  if (!(lo > target) && hi > target) {
-    float local = 0.f;
-    int x = -1;
-    for (int i = 0; i < csz; ++i) {
-      const int v = t * csz + i;
-      if (v >= V) break;
-      local += w[v];
-      if (eg + (F[t] + local) > target) {
-        x = v;
-        break;
-      }
-    }
-    if (x < 0) x = min(V - 1, t * csz + csz - 1);
-    atomicMin(&found, x);
-  }
-  __syncthreads();
-  int x = found;
-  if (x == 0x7fffffff || x > *last_nz) x = *last_nz < 0 ? V - 1 : *last_nz;
-  __syncthreads();
-  return x;
-}
-
+// Exact mode for any vocabulary: the target distribution lives in the
+// workspace row pw and every pass is a block-wide loop over it.
 __global__ __launch_bounds__(1024) void posterior_exact_kernel(PostArgs a) {
   const int b = blockIdx.x, t = threadIdx.x;
   const int T = a.T, V = a.V, K = a.K;
   __shared__ float red[16];
-  __shared__ float cs[1024], F[1024], E[65];
-  __shared__ int last_nz;
-  __shared__ int sh_taken;
+  __shared__ CdfLds cdf;
+  __shared__ int sh_taken, sh_next;
   float* pw = a.pw + (size_t)b * V;   // current target distribution p
   const int* tok = a.tokens + (size_t)b * T;
   const float* ur = a.u_resample + (size_t)b * T;
@@ -337,7 +267,11 @@ __global__ __launch_bounds__(1024) void posterior_exact_kernel(PostArgs a) {
       }
     }
     if (taken < 0) {
-      next = block_inverse_cdf(pw, V, ur[v], cs, F, E, &last_nz);
+      const auto w = [&](int x) { return pw[x]; };
+      cdf_build(w, V, cdf);
+      if (t == 0) sh_next = cdf_draw(w, V, ur[v], cdf);
+      __syncthreads();
+      next = sh_next;
       break;
     }
     v = taken;
@@ -363,6 +297,139 @@ __global__ __launch_bounds__(1024) void posterior_exact_kernel(PostArgs a) {
       break;
     }
   a.best_path[b] = bp;
+}
+
+// Exact mode for V <= kExactLdsV: the target distribution lives in LDS as
+// unnormalised weights p[x] with one scale factor, p(x) = p[x] * scale, which
+// is the product posterior_exact_kernel stores, so every value and decision
+// is the same while the normalising passes disappear. Each pass over the
+// vocabulary reads its logits from clamped indices, all of a thread's loads
+// (32 for V = 32768) in flight before the first is used; the tree, tokens and
+// uniforms are staged in LDS.
+constexpr int kExactLdsV = 32768;
+
+__global__ __launch_bounds__(1024) void posterior_exact_lds_kernel(PostArgs a) {
+  const int b = blockIdx.x, t = threadIdx.x;
+  const int T = a.T, V = a.V, K = a.K;
+  constexpr int kStride = 1024, kBatch = kExactLdsV / 1024;
+  __shared__ float p[kExactLdsV];
+  __shared__ float red[16];
+  __shared__ CdfLds cdf;
+  __shared__ int s_par[MAXT], s_tok[MAXT];
+  __shared__ float s_ua[MAXT];
+  __shared__ int s_next, s_bp;
+  if (t < T) {
+    s_par[t] = a.parent[t];
+    s_tok[t] = a.tokens[(size_t)b * T + t];
+    s_ua[t] = a.u_accept[(size_t)b * T + t];
+  }
+  if (t == 0) s_bp = 0x7fffffff;
+  __syncthreads();
+  const auto par = [&](int x) { return min(max(s_par[x], 0), T - 1); };
+  // f(x, value of row[x]) for this thread's tokens x = t + 1024 i, in x order
+  const auto stream = [&](const float* row, auto&& f) {
+    for (int x0 = t; x0 < V; x0 += kStride * kBatch) {
+      float lv[kBatch];
+#pragma unroll
+      for (int i = 0; i < kBatch; ++i) lv[i] = row[min(x0 + kStride * i, V - 1)];
+#pragma unroll
+      for (int i = 0; i < kBatch; ++i)
+        if (x0 + kStride * i < V) f(x0 + kStride * i, lv[i]);
+    }
+  };
+  float scale = 1.f;
+  const auto load_p = [&](int v) {
+    float mx = kNegInf;
+    stream(a.verify_logits + ((size_t)b * T + v) * V, [&](int x, float l) {
+      const float z = l * a.inv_tau;
+      p[x] = z;
+      mx = fmaxf(mx, z);
+    });
+    mx = block_max(mx, red);
+    float s = 0.f;
+#pragma unroll 8
+    for (int x = t; x < V; x += kStride) {
+      const float e = exp_e(p[x] - mx);
+      p[x] = e;
+      s += e;
+    }
+    s = block_sum(s, red);   // ends with a barrier: p is complete
+    scale = 1.f / s;
+  };
+
+  int v = 0;
+  int next = -1;
+  load_p(0);
+  while (true) {
+    int dv = 0;
+    for (int x = v; x != 0 && dv < K; x = par(x)) ++dv;
+    int taken = -1;
+    if (dv < K) {
+      const float* hl = a.head_logits + ((size_t)b * K + dv) * V;
+      const float lse = a.head_lse[(size_t)b * K + dv];
+      for (int c = v + 1; c < T; ++c) {
+        if (s_par[c] != v) continue;
+        const int x = min(max(s_tok[c], 0), V - 1);
+        // every thread takes the same decision from the same values
+        if (s_ua[c] * exp_e(hl[x] - lse) < p[x] * scale) {
+          taken = c;
+          break;
+        }
+        // residual p <- norm(max(0, p - q)); kept when all zero
+        float s = 0.f;
+        stream(hl, [&](int y, float l) { s += fmaxf(p[y] * scale - exp_e(l - lse), 0.f); });
+        s = block_sum(s, red);
+        if (s > 0.f) {
+          stream(hl, [&](int y, float l) { p[y] = fmaxf(p[y] * scale - exp_e(l - lse), 0.f); });
+          scale = 1.f / s;
+        }
+        __syncthreads();
+      }
+    }
+    if (taken < 0) {
+      const auto w = [&](int x) { return p[x] * scale; };
+      cdf_build(w, V, cdf);
+      if (t == 0) s_next = cdf_draw(w, V, a.u_resample[(size_t)b * T + v], cdf);
+      __syncthreads();
+      next = s_next;
+      break;
+    }
+    v = taken;
+    load_p(v);
+  }
+  int depth = 0;
+  for (int x = v; x != 0 && depth < K; x = par(x)) ++depth;
+  // best path: the lowest path index whose node at this depth is v
+  if (t < a.P && a.retrieve[(size_t)t * (K + 1) + depth] == v) atomicMin(&s_bp, t);
+  __syncthreads();
+  if (t != 0) return;
+  a.accept_len[b] = depth;
+  a.last_node[b] = v;
+  int* out = a.out_tokens + (size_t)b * (K + 1);
+  for (int j = depth + 1; j <= K; ++j) out[j] = -1;
+  int x = v;
+  for (int j = depth; j >= 0; --j) {
+    out[j] = s_tok[x];
+    x = par(x);
+  }
+  a.next_root[b] = next;
+  a.best_path[b] = s_bp == 0x7fffffff ? 0 : s_bp;
+}
+
+// The LDS kernel needs more LDS than older parts give one workgroup; it runs
+// where the device's per-workgroup limit holds it.
+bool exact_lds_fits() {
+  static const bool v = [] {
+    int dev = 0, lim = 0;
+    hipFuncAttributes fa{};
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&lim, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess ||
+        hipFuncGetAttributes(&fa, reinterpret_cast<const void*>(posterior_exact_lds_kernel)) !=
+            hipSuccess)
+      return false;
+    return fa.sharedSizeBytes <= (size_t)lim;
+  }();
+  return v;
 }
 
 // ---- commit ----------------------------------------------------------------------
@@ -476,7 +543,9 @@ __global__ __launch_bounds__(1024) void posterior_commit_kernel(PostArgs a, Comm
 }  // namespace
 
 hipError_t launch_posterior(const PostArgs& a, hipStream_t st) {
-  if (a.mode == 2)
+  if (a.mode == 2 && a.V <= kExactLdsV && exact_lds_fits())
+    hipLaunchKernelGGL(posterior_exact_lds_kernel, dim3(a.B), dim3(1024), 0, st, a);
+  else if (a.mode == 2)
     hipLaunchKernelGGL(posterior_exact_kernel, dim3(a.B), dim3(1024), 0, st, a);
   else
     hipLaunchKernelGGL(posterior_kernel, dim3(a.B), dim3(256), 0, st, a);

@@ -12,6 +12,7 @@
 //   parent, depth.
 // In sampling mode a second kernel draws each node's token from its depth's
 // head softmax by inverse CDF.
+#include "cdf.h"
 #include "common.h"
 #include "kernels.h"
 
@@ -87,87 +88,23 @@ __global__ __launch_bounds__(256) void tree_topology_kernel(TreeArgs a) {
   for (int j = d + 1; j <= K; ++j) r[j] = -1;
 }
 
-// Inverse-CDF draws for sampling mode. One 1024-thread block per
-// (depth k, sequence b); weights w_v = exp(l_v - lse) of head k.
-// The CDF is a fixed two-level sum: thread t sums chunk t sequentially (cs),
-// 64 groups of 16 chunks are combined sequentially (F inside a group, E
-// across groups), so C(x) = E_g + (F_j + local(x)) is monotone and every
-// search below evaluates exactly that function. A node draws the smallest
-// x with C(x) > u * C(V-1), clamped to the last token of nonzero weight.
-__global__ __launch_bounds__(1024) void tree_sample_kernel(TreeArgs a) {
+// Inverse-CDF draws for sampling mode. One 1024-thread workgroup per
+// (depth k, sequence b) builds the CDF of head k's softmax weights
+// w_v = exp(l_v - lse) (cdf.h); thread n then draws node n's token with the
+// node's uniform if node n has depth k + 1 (T <= 256 threads).
+__global__ __launch_bounds__(kCdfThreads) void tree_sample_kernel(TreeArgs a) {
   const int kd = blockIdx.x;     // 0-based head = depth - 1
   const int b = blockIdx.y;
   const int t = threadIdx.x;
   const int T = a.plan.T, K = a.plan.K, V = a.V;
   const float* l = a.head_logits + ((size_t)b * K + kd) * V;
   const float lse = a.head_lse[(size_t)b * K + kd];
-  const int csz = (V + 1023) / 1024;
-  __shared__ float cs[1024];
-  __shared__ float F[1024];
-  __shared__ float E[65];
-  __shared__ int last_nz;
-  float s = 0.f;
-  int my_last = -1;
-  for (int i = 0; i < csz; ++i) {
-    const int v = t * csz + i;
-    if (v < V) {
-      const float w = exp_e(l[v] - lse);
-      s += w;
-      if (w > 0.f) my_last = v;
-    }
-  }
-  cs[t] = s;
-  if (t == 0) last_nz = -1;
-  __syncthreads();
-  atomicMax(&last_nz, my_last);
-  if (t < 64) {
-    float f = 0.f;
-    for (int j = 0; j < 16; ++j) {
-      F[t * 16 + j] = f;
-      f = f + cs[t * 16 + j];
-    }
-    E[t + 1] = f;                         // temporarily the group total
-  }
-  __syncthreads();
-  if (t == 0) {
-    float e = 0.f;
-    for (int g = 0; g < 64; ++g) {
-      const float gt = E[g + 1];
-      E[g] = e;
-      e = e + gt;
-    }
-    E[64] = e;
-  }
-  __syncthreads();
-  // nodes of this depth, one per thread
-  int count = 0;
-  for (int n = 1; n < T; ++n) {
-    if (a.plan.depth[n] != kd + 1) continue;
-    if (count++ % 1024 != t) continue;
-    const float target = a.u_draft[(size_t)b * T + n] * E[64];
-    int tok = -1;
-    for (int g = 0; g < 64 && tok < 0; ++g) {
-      const float eg = E[g];
-      const float gend = eg + (F[g * 16 + 15] + cs[g * 16 + 15]);
-      if (!(gend > target)) continue;
-      for (int j = g * 16; j < g * 16 + 16 && tok < 0; ++j) {
-        if (!(eg + (F[j] + cs[j]) > target)) continue;
-        float local = 0.f;
-        for (int i = 0; i < csz; ++i) {
-          const int v = j * csz + i;
-          if (v >= V) break;
-          local += exp_e(l[v] - lse);
-          if (eg + (F[j] + local) > target) {
-            tok = v;
-            break;
-          }
-        }
-        if (tok < 0) tok = min(V - 1, j * csz + csz - 1);
-      }
-    }
-    if (tok < 0 || tok > last_nz) tok = last_nz < 0 ? V - 1 : last_nz;
-    a.tokens[(size_t)b * T + n] = tok;
-  }
+  __shared__ CdfLds sh;
+  const auto w = [&](int x) { return exp_e(l[x] - lse); };
+  const bool mine = t >= 1 && t < T && a.plan.depth[min(t, MAXT - 1)] == kd + 1;
+  const float u = mine ? a.u_draft[(size_t)b * T + t] : 0.f;
+  cdf_build(w, V, sh);
+  if (mine) a.tokens[(size_t)b * T + t] = cdf_draw(w, V, u, sh);
 }
 
 }  // namespace
@@ -182,7 +119,7 @@ hipError_t launch_tree(const TreeArgs& a, hipStream_t st) {
     if (e != hipSuccess) return e;
   }
   if (!a.sample) return e;
-  hipLaunchKernelGGL(tree_sample_kernel, dim3(a.plan.K, a.B), dim3(1024), 0, st, a);
+  hipLaunchKernelGGL(tree_sample_kernel, dim3(a.plan.K, a.B), dim3(kCdfThreads), 0, st, a);
   return hipGetLastError();
 }
 
