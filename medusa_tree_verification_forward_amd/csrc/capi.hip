@@ -167,8 +167,9 @@ Layout layout_for(const medusa_shape* s) {
     const bool f32 = s->dtype == MEDUSA_F32;
     // QKV / O-proj partials [groups][KS][M][cols] (groups * cols < N + 128),
     // or the LM head's slices [groups][KS][48][cols] when its K is split
-    const size_t q_need = (size_t)gemm_splits(EPI_QKV, 3 * s->d, s->d, f32) * B * T * (3 * d + 128);
-    const size_t o_need = (size_t)gemm_splits(EPI_OPROJ, s->d, s->d, f32) * B * T * (d + 128);
+    const int M = (int)(B * T);
+    const size_t q_need = (size_t)gemm_splits(EPI_QKV, 3 * s->d, s->d, f32, M) * B * T * (3 * d + 128);
+    const size_t o_need = (size_t)gemm_splits(EPI_OPROJ, s->d, s->d, f32, M) * B * T * (d + 128);
     const int lm_ks = lm_splits_for((int)(B * T));
     const size_t lm_need = lm_ks > 1 ? (size_t)lm_ks * 48 * (s->V + 128) : 0;
     L.gemm_part = take(std::max(q_need, std::max(o_need, lm_need)) * 4);

@@ -124,7 +124,7 @@ int gemm_passes_max(int M);                // row passes (upper bound)
 int lm_head_blocks(int N, int M);          // row records of the LM head (16-column stripes)
 int lm_record_slots(int N);                // upper bound of lm_head_blocks over the configs
 int lm_splits_for(int M);                  // K slices of the LM head
-int gemm_splits(int epi, int N, int K, bool f32);   // K slices of the QKV / output projection
+int gemm_splits(int epi, int N, int K, bool f32, int M);   // K slices of the QKV / output projection of M rows
 hipError_t launch_qkv(const GemmParams& p, hipStream_t st);
 hipError_t launch_oproj(const GemmParams& p, hipStream_t st);
 hipError_t launch_lm_head(GemmParams p, float* row_stats, int* row_argmax, hipStream_t st);

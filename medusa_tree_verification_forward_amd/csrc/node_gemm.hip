@@ -751,7 +751,14 @@ Config config_for(int M, int N, int epi) {
     if (epi == EPI_LM) return lm_config(lm_splits_for(M));
     return small_config(epi, N).c;
   }
-  return Config{8, 12, 4, 4};
+  // more rows: 8-wave workgroups of 12 m-tiles (A chunks of 48 KB, double
+  // buffered) with MEDUSA_BIG_GEMM_D (4 or 8, default 4: 8 spills registers
+  // and measured no faster) weight loads in flight per wave
+  static const int d = [] {
+    const char* s = getenv("MEDUSA_BIG_GEMM_D");
+    return s && *s && atoi(s) == 8 ? 8 : 4;
+  }();
+  return Config{8, 12, 4, d};
 }
 
 }  // namespace
@@ -804,14 +811,16 @@ hipError_t launch_main(const GemmParams& p, int KS, hipStream_t st) {
     hipLaunchKernelGGL((node_gemm_kernel<ET, 8, 3, 8, 8, EPI>), grid, block, 0, st, p);
   else if (c.mt == 3)
     hipLaunchKernelGGL((node_gemm_kernel<ET, 8, 3, 8, 16, EPI>), grid, block, 0, st, p);
-  else
+  else if (c.d == 4)
     hipLaunchKernelGGL((node_gemm_kernel<ET, 8, 12, 4, 4, EPI>), grid, block, 0, st, p);
+  else
+    hipLaunchKernelGGL((node_gemm_kernel<ET, 8, 12, 4, 8, EPI>), grid, block, 0, st, p);
   return hipGetLastError();
 }
 
 template <int EPI>
 hipError_t launch_split(GemmParams p, hipStream_t st) {
-  const int KS = gemm_splits(EPI, p.N, p.K, p.f32);
+  const int KS = gemm_splits(EPI, p.N, p.K, p.f32, p.M);
   p.group_cols = 16 * config_for(p.M, p.N, EPI).wv;
   p.fused = fused_epilogue();
   p.kg_shift = packed_kg_shift();
@@ -867,16 +876,24 @@ hipError_t launch_pack_weight(bool f32, const void* W, int rows, int K, int pair
 // power of two that gives the grid at least MEDUSA_GEMM_MIN_WAVES waves
 // (default 1024, 4 per compute unit); either way every wave keeps at least
 // 8 k-tiles per slice.
-int gemm_splits(int epi, int N, int K, bool f32) {
+int gemm_splits(int epi, int N, int K, bool f32, int M) {
   static const int min_waves = [] {
     const char* s = getenv("MEDUSA_GEMM_MIN_WAVES");
     const int v = s && *s ? atoi(s) : 1024;
     return v < 1 ? 1 : (v > 65536 ? 65536 : v);
   }();
-  const int forced = small_config(epi, N).ks;
-  const int stripes = (N + 15) / 16;
   const int nkt = K / (f32 ? 16 : 32);
   int ks = 1;
+  if (M > 48) {
+    // workgroups of the 12-m-tile configuration take most of a compute
+    // unit's LDS: split K while the grid still fits one workgroup per unit
+    const Config c = config_for(M, N, epi);
+    const int wgs = (N + 16 * c.wv - 1) / (16 * c.wv) * ((M + 16 * c.mt - 1) / (16 * c.mt));
+    while (wgs * ks * 2 <= device_cus() && nkt / (ks * 2) >= 8 && ks < kMaxSplits) ks *= 2;
+    return ks;
+  }
+  const int forced = small_config(epi, N).ks;
+  const int stripes = (N + 15) / 16;
   if (forced > 0) {
     while (ks * 2 <= forced && nkt / (ks * 2) >= 8 && ks < kMaxSplits) ks *= 2;
     return ks;
