@@ -887,8 +887,10 @@ hipError_t launch_heads_nb(const HeadsArgs& a, int b0, hipStream_t st) {
 // Batched passes (3 or more vectors, bf16): W1 split over KS waves with DS
 // column blocks in flight, W2 in tile rows of NG with DS in flight.
 // MEDUSA_HEAD_TILE=0 keeps the per-row streams; MEDUSA_W1_TILE_KS (1, 2, 4)
-// and MEDUSA_W2_TILE_NG (3, 4) choose the shapes where d allows (default
-// 4 and 3: 48 rows a wave measured 4% faster than 64 at batch 8).
+// and MEDUSA_W2_TILE ("ng,ds") choose the shapes where d allows (default
+// 4 and 2,4: 32 rows a wave with 8 tiles in flight; at batch 8 the step took
+// 746 us against 755-779 for 16-64 rows and 4-16 tiles in flight; fragment-
+// shaped reads lose DRAM locality as more of them are outstanding).
 bool head_tile() {
   static const bool v = [] {
     const char* s = getenv("MEDUSA_HEAD_TILE");
@@ -900,10 +902,24 @@ int env_choice(const char* name, int dflt) {
   const char* s = getenv(name);
   return s && *s ? atoi(s) : dflt;
 }
-int w2_tile_ng() {
-  static const int v = env_choice("MEDUSA_W2_TILE_NG", 3) == 4 ? 4 : 3;
+// MEDUSA_W2_TILE ("ng,ds": tile rows per wave and column blocks in flight,
+// one of the instantiated pairs below)
+struct TileShape {
+  int ng, ds;
+};
+TileShape w2_tile_shape() {
+  static const TileShape v = [] {
+    const char* s = getenv("MEDUSA_W2_TILE");
+    int ng = 0, ds = 0;
+    if (s && *s) sscanf(s, "%d,%d", &ng, &ds);
+    const TileShape known[] = {{1, 8}, {2, 2}, {2, 4}, {2, 8}, {3, 2}, {3, 4}, {4, 2}, {4, 4}};
+    for (const TileShape& k : known)
+      if (k.ng == ng && k.ds == ds) return k;
+    return TileShape{2, 4};
+  }();
   return v;
 }
+int w2_tile_ng() { return w2_tile_shape().ng; }
 // rows per W2 workgroup of the batched pass
 int w2_tile_rows() { return kHeadWaves * 16 * w2_tile_ng(); }
 
@@ -945,14 +961,26 @@ hipError_t launch_heads_tile(const HeadsArgs& a, int b0, int G, hipStream_t st) 
   hipLaunchKernelGGL((heads_w2_tile_kernel<NG, DS>), dim3(G, a.K), dim3(kHeadWaves * 64), 0, st, \
                      a.B, b0, a.K, a.V, d, W2, zfrag, a.S, a.head_logits, a.part_val,          \
                      a.part_id, a.part_m, a.part_s, G)
-  if (w2_tile_ng() == 3 && nblk % 4 == 0)
-    W2_TILE(3, 4);
-  else if (w2_tile_ng() == 3)
-    W2_TILE(3, 2);
-  else if (nblk % 4 == 0)
+  const TileShape ts = w2_tile_shape();
+  const int ds = nblk % ts.ds == 0 ? ts.ds : 2;   // d is a multiple of 64: nblk even
+  if (ts.ng == 1 && ds == 8)
+    W2_TILE(1, 8);
+  else if (ts.ng == 1)
+    W2_TILE(1, 2);
+  else if (ts.ng == 2 && ds == 8)
+    W2_TILE(2, 8);
+  else if (ts.ng == 2 && ds == 4)
+    W2_TILE(2, 4);
+  else if (ts.ng == 2)
+    W2_TILE(2, 2);
+  else if (ts.ng == 4 && ds == 4)
     W2_TILE(4, 4);
-  else
+  else if (ts.ng == 4)
     W2_TILE(4, 2);
+  else if (ds == 4)
+    W2_TILE(3, 4);
+  else
+    W2_TILE(3, 2);
 #undef W2_TILE
   e = hipGetLastError();
   if (e != hipSuccess) return e;
