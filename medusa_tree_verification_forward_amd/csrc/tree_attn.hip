@@ -39,7 +39,11 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr int kPfxWaves = 8;   // waves of the bf16 prefix kernel, 32 keys each
 static_assert(kPfxWaves * 32 == kAttnChunk, "one 32-key MFMA step per wave");
 
-template <int DH, int QG>
+// QG query tiles are processed per pass over a chunk. With QH > QG the Q
+// rows of all (at most QH) query tiles are held in LDS for the whole kernel,
+// loaded once; with QH == QG a query group's rows are reloaded for every
+// chunk when the tree has more than QG tiles.
+template <int DH, int QG, int QH>
 __global__ __launch_bounds__(64 * kPfxWaves) void prefix_attn_bf16_kernel(AttnArgs a) {
   using S = uint16_t;
   static_assert(64 * kPfxWaves == 512, "Q staging assumes 512 threads");
@@ -62,10 +66,11 @@ __global__ __launch_bounds__(64 * kPfxWaves) void prefix_attn_bf16_kernel(AttnAr
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int li = lane & 15, lq = lane >> 4;
   const int MQ = (T + 15) / 16;
-  const bool one_group = MQ <= QG;   // Q stays in LDS for every chunk
+  constexpr bool kHold = QH > QG;
+  const bool one_group = kHold || MQ <= QG;   // Q stays in LDS for every chunk
   const float sl2 = a.scale * kLog2e;
 
-  __shared__ S qs[16 * QG][QSTR];
+  __shared__ S qs[16 * QH][QSTR];
   __shared__ S vs[kAttnChunk][VSTR];
   __shared__ S ps[16 * QG][PSTR];
   __shared__ float red_m[kPfxWaves][16 * QG];
@@ -103,7 +108,19 @@ __global__ __launch_bounds__(64 * kPfxWaves) void prefix_attn_bf16_kernel(AttnAr
   };
 
   u32x4_t qv[QR];
-  load_q(0, qv);
+  if constexpr (kHold) {
+    // every query tile's rows, once (rows past T read clamped, never used)
+    constexpr int QPA = 16 * QH * VP, QRA = (QPA + 511) / 512;
+#pragma unroll
+    for (int r = 0; r < QRA; ++r) {
+      const int p = threadIdx.x + 512 * r;
+      const int pc = min(p, QPA - 1), qr = pc / VP, c = pc - qr * VP;
+      const u32x4_t v = load16(qb + (((size_t)b * T + min(qr, T - 1)) * H + h) * DH + 8 * c);
+      if (p < QPA) *reinterpret_cast<u32x4_t*>(&qs[qr][8 * c]) = v;
+    }
+  } else {
+    load_q(0, qv);
+  }
   u32x4_t kf[2][DS], vv[VL];
   load_kv(s, kf, vv);
   for (bool first = true;; first = false) {
@@ -120,7 +137,9 @@ __global__ __launch_bounds__(64 * kPfxWaves) void prefix_attn_bf16_kernel(AttnAr
 
     const size_t base = ((size_t)b * H + h) * a.NS * T + (size_t)s * T;   // partial row of query 0
     for (int g0 = 0; g0 < MQ; g0 += QG) {
-      if (first || !one_group) {
+      if (kHold) {
+        if (first && g0 == 0) __syncthreads();   // the held Q rows are published
+      } else if (first || !one_group) {
         if (g0 > 0 || !first) load_q(g0, qv);
 #pragma unroll
         for (int r = 0; r < QR; ++r) {
@@ -134,10 +153,13 @@ __global__ __launch_bounds__(64 * kPfxWaves) void prefix_attn_bf16_kernel(AttnAr
 #pragma unroll
       for (int u = 0; u < QG; ++u) {
         // Q fragments of tile u (B operand): query 16 (g0 + u) + li, dh 8 lq + 32 ds .. + 7
+        // (held rows: tile g0 + u, clamped into the held tiles; tiles past
+        // the tree compute values that are never stored)
+        const int qrow = kHold ? 16 * min(g0 + u, QH - 1) + li : 16 * u + li;
         u32x4_t qf[DS];
 #pragma unroll
         for (int ds = 0; ds < DS; ++ds)
-          qf[ds] = *reinterpret_cast<const u32x4_t*>(&qs[16 * u + li][8 * lq + 32 * ds]);
+          qf[ds] = *reinterpret_cast<const u32x4_t*>(&qs[qrow][8 * lq + 32 * ds]);
 #pragma unroll
         for (int kt = 0; kt < 2; ++kt) {
           st[kt][u] = floatx4_t{0.f, 0.f, 0.f, 0.f};
@@ -524,20 +546,48 @@ __global__ __launch_bounds__(64) void attn_merge_kernel(AttnArgs a) {
   }
 }
 
+constexpr int kHeldTiles = 9;   // query tiles whose Q rows the bf16 kernel can hold
+
+// MEDUSA_ATTN_HOLD_Q=0 reloads each query group per chunk for trees of 5-9
+// query tiles (the shape below 65 queries); held rows need the device to
+// give a workgroup the kernel's LDS.
+template <int DH>
+bool attn_hold_q_for() {
+  static const bool v = [] {
+    const char* s = getenv("MEDUSA_ATTN_HOLD_Q");
+    if (s && *s && atoi(s) == 0) return false;
+    int dev = 0, lim = 0;
+    hipFuncAttributes fa{};
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&lim, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess ||
+        hipFuncGetAttributes(&fa, reinterpret_cast<const void*>(
+                                      prefix_attn_bf16_kernel<DH, 4, kHeldTiles>)) != hipSuccess)
+      return false;
+    return fa.sharedSizeBytes <= (size_t)lim;
+  }();
+  return v;
+}
+
 template <int DH>
 hipError_t launch_bf16(const AttnArgs& a, hipStream_t st) {
+  const auto attn_hold_q = [] { return attn_hold_q_for<DH>(); };
   const int MQ = (a.T + 15) / 16;
   // one workgroup per compute unit (its LDS use allows no second): chunks
   // per (b, h) in flight = CUs / (B H), each workgroup looping over the rest
   int G = device_cus() / (a.B * a.H);
   G = G < 1 ? 1 : (G > a.NS ? a.NS : G);
   dim3 grid(G, a.H, a.B), block(64 * kPfxWaves);
-  switch (MQ < 4 ? MQ : 4) {
-    case 1: hipLaunchKernelGGL((prefix_attn_bf16_kernel<DH, 1>), grid, block, 0, st, a); break;
-    case 2: hipLaunchKernelGGL((prefix_attn_bf16_kernel<DH, 2>), grid, block, 0, st, a); break;
-    case 3: hipLaunchKernelGGL((prefix_attn_bf16_kernel<DH, 3>), grid, block, 0, st, a); break;
-    default: hipLaunchKernelGGL((prefix_attn_bf16_kernel<DH, 4>), grid, block, 0, st, a); break;
-  }
+  // 5 to 9 query tiles: all Q rows held in LDS (151 KB with the V and P
+  // buffers for 128-wide heads), so no query group is reloaded per chunk
+  if (MQ > 4 && MQ <= kHeldTiles && attn_hold_q())
+    hipLaunchKernelGGL((prefix_attn_bf16_kernel<DH, 4, kHeldTiles>), grid, block, 0, st, a);
+  else
+    switch (MQ < 4 ? MQ : 4) {
+      case 1: hipLaunchKernelGGL((prefix_attn_bf16_kernel<DH, 1, 1>), grid, block, 0, st, a); break;
+      case 2: hipLaunchKernelGGL((prefix_attn_bf16_kernel<DH, 2, 2>), grid, block, 0, st, a); break;
+      case 3: hipLaunchKernelGGL((prefix_attn_bf16_kernel<DH, 3, 3>), grid, block, 0, st, a); break;
+      default: hipLaunchKernelGGL((prefix_attn_bf16_kernel<DH, 4, 4>), grid, block, 0, st, a); break;
+    }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((attn_merge_kernel<BF16, DH>), dim3(a.T, a.H, a.B), dim3(64), 0, st, a);
