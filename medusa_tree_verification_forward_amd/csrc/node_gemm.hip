@@ -192,6 +192,35 @@ __device__ __forceinline__ float sum_partials(const GemmParams& p, int r, int n,
   return acc;
 }
 
+// Workgroup coordinates: column group g, K slice ks, row pass pz. With one
+// row pass they are the block indices. With several, the passes of one
+// (group, slice) get linear ids 8 apart: linear id mod 8 picks the XCD, so
+// they run on the same XCD at about the same time and stream the same
+// weight tiles through its L2 instead of each from HBM.
+__device__ __forceinline__ void wg_coords(int& g, int& ks, int& pz) {
+  const int P = gridDim.z;
+  if (P == 1) {
+    g = blockIdx.x;
+    ks = blockIdx.y;
+    pz = 0;
+    return;
+  }
+  const int units = gridDim.x * gridDim.y;
+  const int lin = blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z);
+  const int full = units & ~7;
+  int u;
+  if (lin < full * P) {
+    u = 8 * (lin / (8 * P)) + (lin & 7);
+    pz = (lin >> 3) % P;
+  } else {
+    const int rest = units - full, l2 = lin - full * P;
+    u = full + l2 % rest;
+    pz = l2 / rest;
+  }
+  g = u % gridDim.x;
+  ks = u / gridDim.x;
+}
+
 template <class ET, int WV, int MT, int CH, int D, int EPI>
 __global__ __launch_bounds__(64 * WV, (WV == 4 && D <= 8) ? 4 : (WV <= 3 ? 1 : 2)) void node_gemm_kernel(
     GemmParams p) {
@@ -203,8 +232,10 @@ __global__ __launch_bounds__(64 * WV, (WV == 4 && D <= 8) ? 4 : (WV <= 3 ? 1 : 2
   constexpr int NAW = CH * MT / WV;               // A loads per wave per chunk
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int li = lane & 15, lq = lane >> 4;
-  const int g = blockIdx.x, ks = blockIdx.y, KS = gridDim.y;
-  const int m0 = blockIdx.z * 16 * MT;
+  int g, ks, pz;
+  wg_coords(g, ks, pz);
+  const int KS = gridDim.y;
+  const int m0 = pz * 16 * MT;
   const St* __restrict__ A = reinterpret_cast<const St*>(p.A);
   const int nkt = p.K / KT;
   const int kt_lo = (int)((long)nkt * ks / KS), kt_hi = (int)((long)nkt * (ks + 1) / KS);
@@ -431,7 +462,7 @@ __global__ __launch_bounds__(64 * WV, (WV == 4 && D <= 8) ? 4 : (WV <= 3 ? 1 : 2
       };
       load_pos(0);
       const double inv_freq = rope_inv_freq(p, min(c1, p.N - 1));
-      if (!last_to_arrive(p.counters + g * gridDim.z + blockIdx.z, KS)) return;
+      if (!last_to_arrive(p.counters + g * gridDim.z + pz, KS)) return;
 #pragma unroll 1
       for (int i0 = 0; i0 < RPT; i0 += RB) {
         if (i0 > 0) load_pos(i0);
@@ -483,7 +514,7 @@ __global__ __launch_bounds__(64 * WV, (WV == 4 && D <= 8) ? 4 : (WV <= 3 ? 1 : 2
           x[i] = ET::load1(reinterpret_cast<const St*>(p.E) + (size_t)tok[i] * p.N + n);
       };
       load_x(0);
-      if (!last_to_arrive(p.counters + g * gridDim.z + blockIdx.z, KS)) return;
+      if (!last_to_arrive(p.counters + g * gridDim.z + pz, KS)) return;
 #pragma unroll 1
       for (int i0 = 0; i0 < RPT; i0 += RB) {
         if (i0 > 0) load_x(i0);
@@ -520,14 +551,14 @@ __global__ __launch_bounds__(64 * WV, (WV == 4 && D <= 8) ? 4 : (WV <= 3 ? 1 : 2
       // (group, pass) sums them in slice order (partials handed over through
       // agent-coherent stores and loads) and goes on to the statistics.
       constexpr int TILE = 16 * MT * GC;
-      float* sl = p.lm_slices + ((size_t)g * gridDim.z + blockIdx.z) * KS * TILE;
+      float* sl = p.lm_slices + ((size_t)g * gridDim.z + pz) * KS * TILE;
       const int ci = 16 * wave + li;
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
         for (int j = 0; j < 4; ++j)
           coherent_store(sl + (size_t)ks * TILE + (16 * mt + 4 * lq + j) * GC + ci, acc[mt][j]);
-      if (!last_to_arrive(p.counters + g * gridDim.z + blockIdx.z, KS)) return;
+      if (!last_to_arrive(p.counters + g * gridDim.z + pz, KS)) return;
       float tot[MT][4];
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt)
