@@ -304,6 +304,69 @@ def test_exact_rule_agrees_with_oracle_per_trial():
     assert agree / total > 0.995, agree / total
 
 
+def test_exact_rule_agrees_with_oracle_large_vocab():
+    # V = 40000: the posterior past the vocabulary it holds in LDS (the
+    # global-memory walk) and the sampler's 32-token CDF chunks. Verify rows
+    # are the drafting head's logits plus noise, so children are accepted
+    # and rejected (residual resampling) in a mix; per trial the kernel must
+    # agree with the float64 rule except within rounding of a boundary.
+    import torch
+    import medusa_tree_verification_forward_amd as M
+    require_gpu()
+    K, V, B = 5, 40000, 16
+    rng = np.random.default_rng(11)
+    s = (3, 2, 2, 1, 1)
+    spec = cartesian_ranks(s)
+    topo = OT.topology(spec, K)
+    T = topo.T
+    head_logits = (rng.standard_normal((K, V)) * 1.5).astype(np.float32)
+    lse = scipy.special.logsumexp(head_logits.astype(np.float64), axis=-1).astype(np.float32)
+    q = scipy.special.softmax(head_logits.astype(np.float64), axis=-1)
+    shape = M.make_shape(B, 128, V, K, 1, 128, 4096, T - 1, topo.P, 3, "bf16")
+    ws = workspace(M.workspace_bytes(shape))
+    hl = dev(np.ascontiguousarray(np.broadcast_to(head_logits, (B, K, V))))
+    hlse = dev(np.ascontiguousarray(np.broadcast_to(lse, (B, K))))
+    i32 = torch.int32
+    tok = poisoned((B, T), i32)
+    mask = poisoned((T, T), torch.uint8)
+    pos = poisoned((B, T), i32)
+    ret = poisoned((topo.P, K + 1), i32)
+    par = poisoned((T,), i32)
+    dep = poisoned((T,), i32)
+    o = _outs(torch, B, K)
+    agree = total = accepted = 0
+    for it in range(4):
+        u = rng.random((3, B, T), dtype=np.float32)
+        M.build_tree(shape, spec, dev(np.zeros(B, np.int32)), dev(np.zeros(B, np.int32)), tok,
+                     mask, pos, ret, par, dep, draft_mode=M.DRAFT_SAMPLE, head_logits=hl,
+                     head_lse=hlse, u_draft=dev(u[0]))
+        t = host(tok)
+        # node n's verify row: the logits of the head that drafts its children
+        vl = np.empty((B, T, V), np.float32)
+        for n in range(T):
+            k = min(topo.depth[n], K - 1)
+            vl[:, n] = head_logits[k] + (rng.standard_normal((B, V)) * 0.6).astype(np.float32)
+        M.evaluate_posterior(shape, "exact", 1.0, 0.0, 0.0, None, None, None, tok, par, ret,
+                             o["accept_len"], o["best_path"], o["last_node"], o["out_tokens"],
+                             o["next_root"], ws, verify_logits=dev(vl), head_logits=hl,
+                             head_lse=hlse, u_accept=dev(u[1]), u_resample=dev(u[2]))
+        torch.cuda.synchronize()
+        alen, out, nxt = host(o["accept_len"]), host(o["out_tokens"]), host(o["next_root"])
+        for b in range(B):
+            # the drafted tokens themselves: an inverse-CDF draw per node
+            ref_t = OT.draft_tokens_sampled(topo, 0, head_logits.astype(np.float64), u[0, b])
+            assert np.mean(ref_t[1:] == t[b, 1:]) > 0.95
+            p_rows = scipy.special.softmax(vl[b].astype(np.float64), axis=-1)
+            ref = OP.posterior_exact(topo, t[b], p_rows, q, u[1, b], u[2, b])
+            same = (ref["accept_len"] == alen[b] and ref["next_root"] == nxt[b]
+                    and np.array_equal(ref["out_tokens"], out[b]))
+            agree += same
+            total += 1
+            accepted += int(alen[b]) > 0
+    assert total - agree <= 1, (agree, total)
+    assert 0 < accepted < total          # both outcomes occur
+
+
 def test_commit_capacity_guard():
     import torch
     import medusa_tree_verification_forward_amd as M

@@ -98,7 +98,8 @@ def test_root_only_tree():
     _check(topo, g, root, topk, kv_len)
 
 
-def test_sampled_tree_tokens_follow_inverse_cdf():
+@pytest.mark.parametrize("V", [32000, 70000])
+def test_sampled_tree_tokens_follow_inverse_cdf(V):
     # Sampling mode: each node draws from its depth's head softmax by inverse
     # CDF with its own uniform. Fed the same fp32 logits, the oracle's float64
     # CDF can only disagree where u * total falls within rounding of a CDF
@@ -108,7 +109,7 @@ def test_sampled_tree_tokens_follow_inverse_cdf():
     require_gpu()
     rng = np.random.default_rng(3)
     s = (3, 2, 2, 1, 1)
-    K, S, B, V = 5, 3, 2, 32000
+    K, S, B = 5, 3, 2
     spec = cartesian_ranks(s)
     topo = OT.topology(spec, K)
     T = topo.T
