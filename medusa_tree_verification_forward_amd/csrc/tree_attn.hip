@@ -574,7 +574,20 @@ hipError_t launch_bf16(const AttnArgs& a, hipStream_t st) {
   const int MQ = (a.T + 15) / 16;
   // one workgroup per compute unit (its LDS use allows no second): chunks
   // per (b, h) in flight = CUs / (B H), each workgroup looping over the rest
-  int G = device_cus() / (a.B * a.H);
+  // With several sequences and at most one workgroup per (sequence, head),
+  // one workgroup would loop over every chunk of its sequence and ragged
+  // prefixes would leave compute units idle while the longest finish: then
+  // 4x as many workgroups are launched, so that those of short prefixes
+  // finish early and free their units (MEDUSA_ATTN_GRID overrides the
+  // factor; 1-16).
+  static const int forced = [] {
+    const char* s = getenv("MEDUSA_ATTN_GRID");
+    const int v = s && *s ? atoi(s) : 0;
+    return v < 0 ? 0 : (v > 16 ? 16 : v);
+  }();
+  const int cus = device_cus();
+  const int over = forced ? forced : (a.B > 1 && cus <= a.B * a.H ? 4 : 1);
+  int G = over * cus / (a.B * a.H);
   G = G < 1 ? 1 : (G > a.NS ? a.NS : G);
   dim3 grid(G, a.H, a.B), block(64 * kPfxWaves);
   // 5 to 9 query tiles: all Q rows held in LDS (151 KB with the V and P
