@@ -65,13 +65,12 @@ int env_int(const char* name, int dflt, int lo, int hi) {
 // Workspace sizes are computed for the smallest allowed value, so any
 // setting fits.
 constexpr int kMinW2Rows = 16;   // rows per workgroup at the smallest setting
-// Rows per wave of the W1 stream: MEDUSA_W1_ROWS, else the fewest that let
-// all K d rows run as one wave of resident workgroups (4 per compute unit).
-int w1_rows(int rows) {
-  static const int forced = env_int("MEDUSA_W1_ROWS", 0, 0, 64);
-  if (forced > 0) return forced;
-  const int slots = 4 * 4 * device_cus();   // waves of the resident workgroups
-  return std::min(64, std::max(1, (rows + slots - 1) / slots));
+// Rows per wave of the W1 stream: MEDUSA_W1_ROWS, else 0 (the launcher takes
+// the fewest that let all K d rows run as one wave of four resident
+// workgroups per compute unit).
+int w1_rows() {
+  static const int v = env_int("MEDUSA_W1_ROWS", 0, 0, 64);
+  return v;
 }
 // W2 grid: rows per wave (MEDUSA_W2_ROWS, default 56) and the workgroups per
 // head that cover the V rows with them. 56 was measured fastest for the 7B heads
@@ -322,7 +321,7 @@ int heads_impl(const medusa_shape* shape, const float* h, const void* W1,
   a.part_s = at<float>(workspace, L.part_s);
   a.afrag = at<char>(workspace, L.afrag);
   a.G = L.G;
-  a.w1_rows_per_wave = w1_rows(shape->K * shape->d);
+  a.w1_rows_per_wave = w1_rows();
   {
     int G;
     w2_grid(shape->V, G, a.w2_rows_per_wave);

@@ -334,8 +334,18 @@ template <class ET, int NB, int SPR>
 using HeadStream =
     typename std::conditional<SPR == 0, RowStream<ET, NB>, RowStreamRows<ET, NB, SPR>>::type;
 
+// Resident workgroups per compute unit the head kernels are compiled for:
+// four (128 registers) where the stream fits them, fewer where a whole-row
+// ring of 10 or 16 chunks, or two activation vectors, needs more registers —
+// at four those spilled (two vectors at d = 4096: a 770 us step at batch 2
+// against 420; one vector at d = 5120: 597 against 556 us).
+template <int NB, int SPR>
+constexpr int head_min_blocks() {
+  return (SPR == 0 || (NB == 1 && SPR <= 8)) ? 4 : ((NB == 1 && SPR <= 10) ? 3 : 2);
+}
+
 template <class ET, int NB, int SPR>
-__global__ __launch_bounds__(kHeadWaves * 64, 4) void heads_w1_kernel(
+__global__ __launch_bounds__(kHeadWaves * 64, (head_min_blocks<NB, SPR>())) void heads_w1_kernel(
     const float* __restrict__ h, int B, int b0, int K, int d,
     const typename ET::storage* __restrict__ W1, const float* __restrict__ b1,
     float* __restrict__ z, int rpw, int interleave) {
@@ -499,7 +509,7 @@ __device__ __forceinline__ void w2_finish(const float (&win)[NB], int nb, int b0
 // [(g*4 + w) * rpw, ... + rpw) of head k.
 // Partial records: part_val/part_id [B][K][G][S], part_m/part_s [B][K][G].
 template <class ET, int NB, int SPR>
-__global__ __launch_bounds__(kHeadWaves * 64, 4) void heads_w2_kernel(
+__global__ __launch_bounds__(kHeadWaves * 64, (head_min_blocks<NB, SPR>())) void heads_w2_kernel(
     const float* __restrict__ z, int B, int b0, int K, int V, int d,
     const typename ET::storage* __restrict__ W2, int rpw, int S,
     float* __restrict__ head_logits, float* __restrict__ part_val, int* __restrict__ part_id,
@@ -835,11 +845,20 @@ hipError_t launch_heads_spr(const HeadsArgs& a, int b0, hipStream_t st) {
   constexpr int CW = RowStream<ET, NB>::CW;
   const int ldx = (a.d + CW - 1) / CW * CW;
   const size_t lds_x = (size_t)NB * ldx * sizeof(float);
-  const int rows1 = kHeadWaves * a.w1_rows_per_wave;
+  // rows per wave: as given, or the fewest that let all K d rows run as one
+  // wave of four workgroups per compute unit (also where the kernel fits
+  // fewer: the larger grid measured as fast or faster, 417-421 against
+  // 423 us a step at batch 2)
+  int rpw1 = a.w1_rows_per_wave;
+  if (rpw1 <= 0) {
+    const int slots = kHeadWaves * 4 * device_cus();
+    rpw1 = std::min(64, std::max(1, (a.K * a.d + slots - 1) / slots));
+  }
+  const int rows1 = kHeadWaves * rpw1;
   const int g1 = (a.K * a.d + rows1 - 1) / rows1;
   hipLaunchKernelGGL((heads_w1_kernel<ET, NB, SPR>), dim3(g1), dim3(kHeadWaves * 64), lds_x, st, a.h,
                      a.B, b0, a.K, a.d, reinterpret_cast<const typename ET::storage*>(a.W1),
-                     a.b1, a.z, a.w1_rows_per_wave, a.interleave);
+                     a.b1, a.z, rpw1, a.interleave);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const size_t lds_list = (size_t)kHeadWaves * NB * (2 * MAXS_LDS + 2) * sizeof(float);
@@ -877,7 +896,7 @@ hipError_t launch_heads_nb(const HeadsArgs& a, int b0, hipStream_t st) {
     switch (a.d / CW) {
       case 8: return launch_heads_spr<ET, NB, (NB <= 2 ? 8 : 0)>(a, b0, st);
       case 10: return launch_heads_spr<ET, NB, (NB <= 2 ? 10 : 0)>(a, b0, st);
-      case 16: return launch_heads_spr<ET, NB, (NB <= 2 ? 16 : 0)>(a, b0, st);
+      case 16: return launch_heads_spr<ET, NB, (NB == 1 ? 16 : 0)>(a, b0, st);   // two spill
       default: break;
     }
   }

@@ -42,7 +42,7 @@ struct HeadsArgs {
   float* part_s;          // [B][K][G]
   void* afrag;            // (K + 1) * 32 * d bytes: MFMA A fragments of the batched passes
   int G;                  // row blocks per head (4 waves of w2_rows_per_wave rows)
-  int w1_rows_per_wave;   // 1..64
+  int w1_rows_per_wave;   // 1..64, or 0: the fewest that fit one wave of resident workgroups
   int w2_rows_per_wave;   // 4..64
   int interleave;         // 1: wave w streams rows w, w + nw, ...; 0: blocks of rows
   hipEvent_t ev_before;   // optional: recorded around the W2 kernel
