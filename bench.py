@@ -307,8 +307,8 @@ def main():
         print(w2_source_digest())
         return
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only: this build runs the verify step on a single "
-              f"MI355X; --gpus {args.gpus} is not supported.", file=sys.stderr)
+        print(f"bench.py measures one GPU only: the verify step runs on a single MI355X; "
+              f"--gpus {args.gpus} is not supported.", file=sys.stderr)
         sys.exit(2)
 
     import torch

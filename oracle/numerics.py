@@ -30,7 +30,7 @@ def round_bf16(x: np.ndarray) -> np.ndarray:
     0.5 <= |f| < 1 (``frexp``), keep 8 significant bits of f by rounding
     f * 2**8 to the nearest integer with ties to even (``rint``), and scale
     back. Zeros stay zero. Values below the bf16 normal range do not occur in
-    this build's data and are not treated specially.
+    the seeded workloads' data and are not treated specially.
     """
     x = np.asarray(x, dtype=np.float64)
     f, e = np.frexp(x)
