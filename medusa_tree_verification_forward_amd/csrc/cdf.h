@@ -67,9 +67,62 @@ __device__ __forceinline__ float cdf_chunk_sum(const Wf& w, int c, int csz, int 
   return s;
 }
 
-// Build the CDF of w(0 .. V-1) into sh. Every thread of the workgroup calls
-// it; ends with a barrier.
+// Weights e^(l_x - lse) of a logit row l (16-byte aligned, V a multiple of
+// 4): w(x) for one token, w4(x) for tokens x .. x + 3 (x a multiple of 4) in
+// one 16-byte load, zero past V.
+struct ExpRow {
+  const float* l;
+  float lse;
+  int V;
+  __device__ __forceinline__ float operator()(int x) const { return exp_e(l[x] - lse); }
+  __device__ __forceinline__ floatx4_t w4(int x) const {
+    const floatx4_t v = *reinterpret_cast<const floatx4_t*>(l + min(x, V - 4));
+    floatx4_t r;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) r[i] = x + i < V ? exp_e(v[i] - lse) : 0.f;
+    return r;
+  }
+};
+
+// Weights p[x] * scale of a row in LDS or memory (16-byte aligned, V a
+// multiple of 4): w(x) for one token, w4(x) for four, zero past V.
+struct ScaledRow {
+  const float* p;
+  float scale;
+  int V;
+  __device__ __forceinline__ float operator()(int x) const { return p[x] * scale; }
+  __device__ __forceinline__ floatx4_t w4(int x) const {
+    const floatx4_t v = *reinterpret_cast<const floatx4_t*>(p + min(x, V - 4));
+    floatx4_t r;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) r[i] = x + i < V ? v[i] * scale : 0.f;
+    return r;
+  }
+};
+
+// Chunk c's sequential sum with the weights read four at a time (Wf::w4).
 template <class Wf>
+__device__ __forceinline__ float cdf_chunk_sum_v4(const Wf& w, int c, int csz, int* last) {
+  float s = 0.f;
+  for (int i0 = 0; i0 < csz; i0 += 16) {
+    floatx4_t q[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) q[u] = w.w4(c * csz + i0 + 4 * u);
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        s += q[u][i];
+        if (q[u][i] > 0.f) *last = c * csz + i0 + 4 * u + i;
+      }
+  }
+  return s;
+}
+
+// Build the CDF of w(0 .. V-1) into sh. Every thread of the workgroup calls
+// it; ends with a barrier. kVec4: chunks of 16 or more tokens read through
+// Wf::w4 (16-byte loads) when V is a multiple of 4; the sums are the same.
+template <bool kVec4 = false, class Wf>
 __device__ void cdf_build(const Wf& w, int V, CdfLds& sh) {
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   const int csz = cdf_chunk_size(V);
@@ -81,8 +134,15 @@ __device__ void cdf_build(const Wf& w, int V, CdfLds& sh) {
   // wave w sums the rows of 64 chunks w, w + 16, ...; lane l chunk 64 r + l
   for (int c0 = 64 * wave; c0 < nch; c0 += 64 * (kCdfThreads / 64)) {
     const int c = c0 + lane;
-    const float s = csz == 8 ? cdf_chunk_sum<8>(w, c, csz, V, &my_last)
-                             : cdf_chunk_sum<16>(w, c, csz, V, &my_last);
+    float s;
+    if constexpr (kVec4) {
+      s = csz >= 16 && (V & 3) == 0 ? cdf_chunk_sum_v4(w, c, csz, &my_last)
+          : csz == 8               ? cdf_chunk_sum<8>(w, c, csz, V, &my_last)
+                                   : cdf_chunk_sum<16>(w, c, csz, V, &my_last);
+    } else {
+      s = csz == 8 ? cdf_chunk_sum<8>(w, c, csz, V, &my_last)
+                   : cdf_chunk_sum<16>(w, c, csz, V, &my_last);
+    }
     if (c < nch) sh.cs[c] = s;   // chunks past nch hold only tokens >= V
   }
   {

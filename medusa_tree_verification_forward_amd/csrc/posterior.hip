@@ -267,8 +267,8 @@ __global__ __launch_bounds__(1024) void posterior_exact_kernel(PostArgs a) {
       }
     }
     if (taken < 0) {
-      const auto w = [&](int x) { return pw[x]; };
-      cdf_build(w, V, cdf);
+      const ScaledRow w{pw, 1.f, V};   // x 1 is exact
+      cdf_build<true>(w, V, cdf);
       if (t == 0) sh_next = cdf_draw(w, V, ur[v], cdf);
       __syncthreads();
       next = sh_next;
@@ -387,8 +387,8 @@ __global__ __launch_bounds__(1024) void posterior_exact_lds_kernel(PostArgs a) {
       }
     }
     if (taken < 0) {
-      const auto w = [&](int x) { return p[x] * scale; };
-      cdf_build(w, V, cdf);
+      const ScaledRow w{p, scale, V};
+      cdf_build<true>(w, V, cdf);
       if (t == 0) s_next = cdf_draw(w, V, a.u_resample[(size_t)b * T + v], cdf);
       __syncthreads();
       next = s_next;

@@ -100,10 +100,10 @@ __global__ __launch_bounds__(kCdfThreads) void tree_sample_kernel(TreeArgs a) {
   const float* l = a.head_logits + ((size_t)b * K + kd) * V;
   const float lse = a.head_lse[(size_t)b * K + kd];
   __shared__ CdfLds sh;
-  const auto w = [&](int x) { return exp_e(l[x] - lse); };
+  const ExpRow w{l, lse, V};
   const bool mine = t >= 1 && t < T && a.plan.depth[min(t, MAXT - 1)] == kd + 1;
   const float u = mine ? a.u_draft[(size_t)b * T + t] : 0.f;
-  cdf_build(w, V, sh);
+  cdf_build<true>(w, V, sh);
   if (mine) a.tokens[(size_t)b * T + t] = cdf_draw(w, V, u, sh);
 }
 

@@ -98,7 +98,7 @@ def test_root_only_tree():
     _check(topo, g, root, topk, kv_len)
 
 
-@pytest.mark.parametrize("V", [32000, 70000])
+@pytest.mark.parametrize("V", [32000, 32001, 70000])
 def test_sampled_tree_tokens_follow_inverse_cdf(V):
     # Sampling mode: each node draws from its depth's head softmax by inverse
     # CDF with its own uniform. Fed the same fp32 logits, the oracle's float64
