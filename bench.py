@@ -380,10 +380,10 @@ def main():
         b.record(stream)
     torch.cuda.synchronize()
     for i in range(args.steps):
-        M.set_profile_events(evs[i][0], evs[i][1])
-        step()
+        if args.reset_kv_len:
+            st.reset_kv_len()
+        st.run_step(keep_kv_len=not args.reset_kv_len, w2_events=evs[i])
     torch.cuda.synchronize()
-    M.set_profile_events(None, None)
     w2_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
 
     alg = algorithmic_bytes(w, T, L_total)

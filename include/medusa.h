@@ -93,17 +93,6 @@ const char* medusa_last_error(void);
 const char* medusa_version(void);
 
 /*
- * Benchmark hook. When both handles are non-NULL hipEvent_t values, every
- * later medusa_heads_forward call records `before` and `after` on its own
- * stream immediately around its vocabulary-projection kernel (l_k = W2_k z_k
- * with the fused top-s, the step's dominant HBM stream), so a caller can
- * time that kernel alone. NULL, NULL turns the hook off. Process-wide, not
- * thread-safe; meant for single-threaded benchmark drivers. Returns
- * MEDUSA_OK.
- */
-int medusa_set_profile_events(void* before, void* after);
-
-/*
  * Workspace bytes that one call sequence of this shape needs (the largest
  * need of any call below, plus a counter block). Zero-fill a new workspace
  * once before its first use; every call leaves its counters at zero again,
@@ -336,8 +325,8 @@ int medusa_commit(const medusa_shape* shape, const int32_t* last_node, const int
  *    evaluates the posterior and commits.
  * Pointers are device memory unless marked; _or_null members may be NULL
  * where the corresponding call allows it. W_qkv, W_o and W_lm are packed
- * (medusa_pack_weight). Errors as for the individual calls; validation of
- * a later part can fail after earlier parts were launched.
+ * (medusa_pack_weight). Every part is validated before the first launch;
+ * errors as for the individual calls (on an error nothing is launched).
  */
 typedef struct {
   /* heads */
@@ -400,6 +389,17 @@ int medusa_step(const medusa_shape* shape, const medusa_step_args* args, void* w
                 size_t workspace_bytes, void* stream);
 
 /*
+ * medusa_step for timing tools: the same step, which also records the two
+ * hipEvent_t handles ev_w2_start and ev_w2_end (both non-NULL, created by the
+ * caller) on `stream` immediately before and after the vocabulary-projection
+ * kernel (l_k = W2_k z_k with the fused top-s, "Medusa 深读", §3.1: the
+ * step's dominant HBM stream), so that kernel can be timed alone inside a
+ * running step loop. Keeps no state; results and errors as for medusa_step.
+ */
+int medusa_step_timed(const medusa_shape* shape, const medusa_step_args* args, void* workspace,
+                      size_t workspace_bytes, void* stream, void* ev_w2_start, void* ev_w2_end);
+
+/*
  * Decoding loop ("Medusa 深读", generate loop; "Medusa: Faster LLM text
  * generation", decoding with heads and tree attention): n_steps composite
  * steps back to back on one stream, each step's accepted prefix becoming the
@@ -414,8 +414,9 @@ int medusa_step(const medusa_shape* shape, const medusa_step_args* args, void* w
  *                    state buffer (overwritten); kv_len and the KV cache
  *                    advance in place (kv_len_out_or_null must be NULL);
  *                    out_tokens and accept_len are not used; the exact-mode
- *                    uniforms, when given, are [n_steps][B][T] (step i reads
- *                    row block i)
+ *                    uniforms, when given, hold one [B][T] block per step,
+ *                    step i's at element i * MEDUSA_ALIGN4(B * T) (so every
+ *                    block keeps the 16-byte alignment of the first)
  *   n_steps          steps to run, >= 0
  *   out_tokens_steps int32 (out): step i's committed tokens (root, then the
  *                    accepted nodes), -1 padded, as a [B][K+1] block at
@@ -423,8 +424,9 @@ int medusa_step(const medusa_shape* shape, const medusa_step_args* args, void* w
  *   accept_len_steps int32 (out): step i's accepted depths a (the step
  *                    commits a + 1 tokens) as [B] at element i * MEDUSA_ALIGN4(B)
  *                    (the per-step blocks keep the 16-byte alignment)
- * The caller sizes the cache for kv_len + n_steps * (K + 1) rows. Errors as
- * for medusa_step; on an error some steps may already be launched.
+ * The caller sizes the cache for kv_len + n_steps * (K + 1) rows. Every
+ * step's arguments are validated before the first launch; errors as for
+ * medusa_step (on an error nothing is launched).
  */
 #define MEDUSA_ALIGN4(n) (((n) + 3) & ~3)
 int medusa_generate(const medusa_shape* shape, const medusa_step_args* args, int n_steps,

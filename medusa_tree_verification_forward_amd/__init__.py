@@ -9,5 +9,5 @@ from ._lib import (  # noqa: F401
     BF16, DRAFT_SAMPLE, DRAFT_TOPK, EXACT, F32, GREEDY, LIB_PATH, MODES, PACK_PLAIN, PACK_QKV,
     TYPICAL, MedusaError,
     Shape, StepArgs, build_tree, commit, evaluate_posterior, exported_symbols, heads_forward, last_error,
-    make_shape, pack_weight, packed_copy, packed_weight_bytes, set_profile_events,
-    step, tree_attention, verify_forward, version, workspace_bytes)
+    make_shape, pack_weight, packed_copy, packed_weight_bytes,
+    step, step_timed, tree_attention, verify_forward, version, workspace_bytes)

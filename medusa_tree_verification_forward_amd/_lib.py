@@ -86,7 +86,6 @@ _SIGS = {
     "medusa_last_error": ([], ctypes.c_char_p),
     "medusa_version": ([], ctypes.c_char_p),
     "medusa_workspace_bytes": ([_SP], _SZ),
-    "medusa_set_profile_events": ([_P, _P], _I),
     "medusa_heads_forward": ([_SP, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P], _I),
     "medusa_build_tree": ([_SP, _P, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P], _I),
     "medusa_tree_attention": ([_SP, _P, _P, _P, _P, _P, _P, _P, _F, _P, _P, _SZ, _P], _I),
@@ -98,6 +97,7 @@ _SIGS = {
                                    _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P], _I),
     "medusa_commit": ([_SP, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P], _I),
     "medusa_step": ([_SP, ctypes.POINTER(StepArgs), _P, _SZ, _P], _I),
+    "medusa_step_timed": ([_SP, ctypes.POINTER(StepArgs), _P, _SZ, _P, _P, _P], _I),
     "medusa_sparse_tree": ([_I, _I, _P, _I, _P, _P, _P, _P], _I),
     "medusa_generate": ([_SP, ctypes.POINTER(StepArgs), _I, _P, _P, _P, _SZ, _P], _I),
 }
@@ -149,14 +149,6 @@ def make_shape(B, d, V, K, H, Dh, Lmax, N, P, s_max, dtype) -> Shape:
                  dtype if isinstance(dtype, int) else (F32 if dtype == "f32" else BF16))
 
 
-def set_profile_events(before=None, after=None):
-    """Record `before`/`after` (torch.cuda.Event or raw handles) around the
-    vocabulary-projection kernel of later heads calls; None, None disables."""
-    def h(e):
-        if e is None:
-            return None
-        return e if isinstance(e, int) else e.cuda_event
-    _check(_lib.medusa_set_profile_events(h(before), h(after)))
 
 
 def workspace_bytes(shape: Shape) -> int:
@@ -288,3 +280,14 @@ def step(shape, args: StepArgs, workspace, *, stream=None):
     tree_ranks_host member must point at host memory that outlives the call."""
     _check(_lib.medusa_step(ctypes.byref(shape), ctypes.byref(args), _ptr(workspace),
                             workspace.numel() * workspace.element_size(), _stream(stream)))
+
+
+def step_timed(shape, args: StepArgs, workspace, ev_w2_start, ev_w2_end, *, stream=None):
+    """medusa_step_timed: the composite step, recording the two events
+    (torch.cuda.Event, created by a first record, or raw handles) on the
+    stream around the vocabulary-projection kernel."""
+    def h(e):
+        return e if isinstance(e, int) else e.cuda_event
+    _check(_lib.medusa_step_timed(ctypes.byref(shape), ctypes.byref(args), _ptr(workspace),
+                                  workspace.numel() * workspace.element_size(), _stream(stream),
+                                  h(ev_w2_start), h(ev_w2_end)))

@@ -21,7 +21,6 @@ using namespace medusa;
 namespace {
 
 thread_local std::string g_err;
-hipEvent_t g_ev_before = nullptr, g_ev_after = nullptr;   // benchmark hook
 
 int fail(int code, const char* fmt, ...) {
   char buf[512];
@@ -258,16 +257,6 @@ const char* medusa_last_error(void) { return g_err.c_str(); }
 
 const char* medusa_version(void) { return "medusa-mi355x 0.1 (gfx950)"; }
 
-int medusa_set_profile_events(void* before, void* after) {
-  if (before && after) {
-    g_ev_before = static_cast<hipEvent_t>(before);
-    g_ev_after = static_cast<hipEvent_t>(after);
-  } else {
-    g_ev_before = g_ev_after = nullptr;
-  }
-  return ok();
-}
-
 size_t medusa_workspace_bytes(const medusa_shape* shape) {
   if (check_shape(shape) != MEDUSA_OK) return 0;
   return layout_for(shape).total;
@@ -284,7 +273,8 @@ int heads_impl(const medusa_shape* shape, const float* h, const void* W1,
                float* head_lse_or_null, float* head_logits_or_null, float* z_or_null,
                void* workspace, size_t workspace_bytes, void* stream, const TreePlan* fuse_plan,
                const int32_t* root_tok, const int32_t* kv_len, int32_t* tree_tokens,
-               int32_t* position_ids) {
+               int32_t* position_ids, bool dry, hipEvent_t ev_w2_start = nullptr,
+               hipEvent_t ev_w2_end = nullptr) {
   int rc = check_shape(shape);
   if (rc) return rc;
   REQUIRE_PTR(h);
@@ -299,6 +289,7 @@ int heads_impl(const medusa_shape* shape, const float* h, const void* W1,
   Layout L;
   rc = check_workspace(shape, workspace, workspace_bytes, &L);
   if (rc) return rc;
+  if (dry) return MEDUSA_OK;
   HeadsArgs a{};
   a.f32 = shape->dtype == MEDUSA_F32;
   a.B = shape->B;
@@ -327,8 +318,8 @@ int heads_impl(const medusa_shape* shape, const float* h, const void* W1,
     w2_grid(shape->V, G, a.w2_rows_per_wave);
   }
   a.interleave = head_interleave();
-  a.ev_before = g_ev_before;
-  a.ev_after = g_ev_after;
+  a.ev_before = ev_w2_start;
+  a.ev_after = ev_w2_end;
   if (fuse_plan) {
     a.fuse_tree = true;
     a.plan = *fuse_plan;
@@ -353,15 +344,18 @@ int medusa_heads_forward(const medusa_shape* shape, const float* h, const void* 
                          size_t workspace_bytes, void* stream) {
   return heads_impl(shape, h, W1, b1_or_null, W2, topk_ids, topk_logits, head_lse_or_null,
                     head_logits_or_null, z_or_null, workspace, workspace_bytes, stream, nullptr,
-                    nullptr, nullptr, nullptr, nullptr);
+                    nullptr, nullptr, nullptr, nullptr, false);
 }
 
-int medusa_build_tree(const medusa_shape* shape, const int32_t* tree_ranks_host,
-                      int draft_mode, const int32_t* root_tok, const int32_t* topk_ids,
-                      const float* head_logits_or_null, const float* head_lse_or_null,
-                      const float* u_draft_or_null, const int32_t* kv_len,
-                      int32_t* tree_tokens, uint8_t* tree_mask, int32_t* position_ids,
-                      int32_t* retrieve, int32_t* parent, int32_t* depth, void* stream) {
+}  // extern "C"
+
+namespace {
+
+int tree_impl(const medusa_shape* shape, const int32_t* tree_ranks_host, int draft_mode,
+              const int32_t* root_tok, const int32_t* topk_ids, const float* head_logits_or_null,
+              const float* head_lse_or_null, const float* u_draft_or_null, const int32_t* kv_len,
+              int32_t* tree_tokens, uint8_t* tree_mask, int32_t* position_ids, int32_t* retrieve,
+              int32_t* parent, int32_t* depth, void* stream, bool dry) {
   // tree_mask, retrieve, parent and depth are optional (see medusa.h)
   int rc = check_shape(shape);
   if (rc) return rc;
@@ -388,6 +382,7 @@ int medusa_build_tree(const medusa_shape* shape, const int32_t* tree_ranks_host,
   if (rc) return rc;
   if (P != shape->P)
     return fail(MEDUSA_ERR_ARG, "tree has %d root-to-leaf paths, shape.P is %d", P, shape->P);
+  if (dry) return MEDUSA_OK;
   a.B = shape->B;
   a.V = shape->V;
   a.S = shape->s_max;
@@ -408,6 +403,21 @@ int medusa_build_tree(const medusa_shape* shape, const int32_t* tree_ranks_host,
   hipError_t e = launch_tree(a, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "tree launch");
   return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+int medusa_build_tree(const medusa_shape* shape, const int32_t* tree_ranks_host,
+                      int draft_mode, const int32_t* root_tok, const int32_t* topk_ids,
+                      const float* head_logits_or_null, const float* head_lse_or_null,
+                      const float* u_draft_or_null, const int32_t* kv_len,
+                      int32_t* tree_tokens, uint8_t* tree_mask, int32_t* position_ids,
+                      int32_t* retrieve, int32_t* parent, int32_t* depth, void* stream) {
+  return tree_impl(shape, tree_ranks_host, draft_mode, root_tok, topk_ids, head_logits_or_null,
+                   head_lse_or_null, u_draft_or_null, kv_len, tree_tokens, tree_mask,
+                   position_ids, retrieve, parent, depth, stream, false);
 }
 
 int medusa_tree_attention(const medusa_shape* shape, const void* q, const void* k_tree,
@@ -495,7 +505,7 @@ int verify_impl(const medusa_shape* shape, const void* E, const void* W_qkv, con
                 float temperature, void* k_tree_out, void* v_tree_out, float* y_out,
                 float* row_stats, int32_t* row_argmax, float* child_logit,
                 float* verify_logits_or_null, void* workspace, size_t workspace_bytes,
-                void* stream) {
+                void* stream, bool dry) {
   int rc = check_shape(shape);
   if (rc) return rc;
   REQUIRE_PTR(E);
@@ -523,6 +533,7 @@ int verify_impl(const medusa_shape* shape, const void* E, const void* W_qkv, con
   Layout L;
   rc = check_workspace(shape, workspace, workspace_bytes, &L);
   if (rc) return rc;
+  if (dry) return MEDUSA_OK;
   hipStream_t st = static_cast<hipStream_t>(stream);
   const bool f32 = shape->dtype == MEDUSA_F32;
   const int T = shape->N + 1, M = shape->B * T, d = shape->d;
@@ -620,20 +631,22 @@ int medusa_verify_forward(const medusa_shape* shape, const void* E, const void* 
   return verify_impl(shape, E, W_qkv, W_o, W_lm, rope_theta, tree_tokens, position_ids,
                      tree_mask, parent, k_cache, v_cache, kv_len, temperature, k_tree_out,
                      v_tree_out, y_out, row_stats, row_argmax, child_logit,
-                     verify_logits_or_null, workspace, workspace_bytes, stream);
+                     verify_logits_or_null, workspace, workspace_bytes, stream, false);
 }
 
-int medusa_evaluate_posterior(const medusa_shape* shape, int mode, float temperature,
-                              float eps, float delta, const float* row_stats,
-                              const int32_t* row_argmax, const float* child_logit,
-                              const float* verify_logits_or_null,
-                              const int32_t* tree_tokens, const int32_t* parent,
-                              const int32_t* retrieve, const float* head_logits_or_null,
-                              const float* head_lse_or_null, const float* u_accept_or_null,
-                              const float* u_resample_or_null, int32_t* accept_len,
-                              int32_t* best_path, int32_t* last_node, int32_t* out_tokens,
-                              int32_t* next_root, void* workspace, size_t workspace_bytes,
-                              void* stream) {
+}  // extern "C"
+
+namespace {
+
+int posterior_impl(const medusa_shape* shape, int mode, float temperature, float eps,
+                   float delta, const float* row_stats, const int32_t* row_argmax,
+                   const float* child_logit, const float* verify_logits_or_null,
+                   const int32_t* tree_tokens, const int32_t* parent, const int32_t* retrieve,
+                   const float* head_logits_or_null, const float* head_lse_or_null,
+                   const float* u_accept_or_null, const float* u_resample_or_null,
+                   int32_t* accept_len, int32_t* best_path, int32_t* last_node,
+                   int32_t* out_tokens, int32_t* next_root, void* workspace,
+                   size_t workspace_bytes, void* stream, bool dry) {
   int rc = check_shape(shape);
   if (rc) return rc;
   if (mode != MEDUSA_GREEDY && mode != MEDUSA_TYPICAL && mode != MEDUSA_EXACT)
@@ -665,6 +678,7 @@ int medusa_evaluate_posterior(const medusa_shape* shape, int mode, float tempera
   Layout L;
   rc = check_workspace(shape, workspace, workspace_bytes, &L);
   if (rc) return rc;
+  if (dry) return MEDUSA_OK;
   PostArgs a{};
   a.mode = mode;
   a.B = shape->B;
@@ -697,13 +711,35 @@ int medusa_evaluate_posterior(const medusa_shape* shape, int mode, float tempera
   return ok();
 }
 
+}  // namespace
+
+extern "C" {
+
+int medusa_evaluate_posterior(const medusa_shape* shape, int mode, float temperature,
+                              float eps, float delta, const float* row_stats,
+                              const int32_t* row_argmax, const float* child_logit,
+                              const float* verify_logits_or_null,
+                              const int32_t* tree_tokens, const int32_t* parent,
+                              const int32_t* retrieve, const float* head_logits_or_null,
+                              const float* head_lse_or_null, const float* u_accept_or_null,
+                              const float* u_resample_or_null, int32_t* accept_len,
+                              int32_t* best_path, int32_t* last_node, int32_t* out_tokens,
+                              int32_t* next_root, void* workspace, size_t workspace_bytes,
+                              void* stream) {
+  return posterior_impl(shape, mode, temperature, eps, delta, row_stats, row_argmax, child_logit,
+                        verify_logits_or_null, tree_tokens, parent, retrieve,
+                        head_logits_or_null, head_lse_or_null, u_accept_or_null,
+                        u_resample_or_null, accept_len, best_path, last_node, out_tokens,
+                        next_root, workspace, workspace_bytes, stream, false);
+}
+
 }  // extern "C"
 
 namespace {
 int commit_impl(const medusa_shape* shape, const int32_t* last_node, const int32_t* parent,
                 const void* k_tree, const void* v_tree, const float* y, void* k_cache,
                 void* v_cache, int32_t* kv_len, int32_t* kv_len_out, float* h_next,
-                void* stream) {
+                void* stream, bool dry) {
   int rc = check_shape(shape);
   if (rc) return rc;
   REQUIRE_PTR(last_node);
@@ -715,6 +751,8 @@ int commit_impl(const medusa_shape* shape, const int32_t* last_node, const int32
   REQUIRE_PTR(v_cache);
   REQUIRE_PTR(kv_len);
   REQUIRE_PTR(h_next);
+  OPTIONAL_PTR(kv_len_out);
+  if (dry) return MEDUSA_OK;
   CommitArgs a{};
   a.f32 = shape->dtype == MEDUSA_F32;
   a.B = shape->B;
@@ -746,11 +784,19 @@ int medusa_commit(const medusa_shape* shape, const int32_t* last_node, const int
                   const void* k_tree, const void* v_tree, const float* y, void* k_cache,
                   void* v_cache, int32_t* kv_len, float* h_next, void* stream) {
   return commit_impl(shape, last_node, parent, k_tree, v_tree, y, k_cache, v_cache, kv_len,
-                     nullptr, h_next, stream);
+                     nullptr, h_next, stream, false);
 }
 
-int medusa_step(const medusa_shape* shape, const medusa_step_args* x, void* workspace,
-                size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// The composite step. With dry set it runs every check of every stage and
+// launches nothing, so that a caller can validate a whole step (or a whole
+// loop of steps) before its first launch.
+int step_impl(const medusa_shape* shape, const medusa_step_args* x, void* workspace,
+              size_t workspace_bytes, void* stream, bool dry, hipEvent_t ev_w2_start = nullptr,
+              hipEvent_t ev_w2_end = nullptr) {
   int rc = check_shape(shape);
   if (rc) return rc;
   if (!x) return fail(MEDUSA_ERR_ARG, "args: null pointer");
@@ -779,49 +825,53 @@ int medusa_step(const medusa_shape* shape, const medusa_step_args* x, void* work
   const bool fuse_tree = x->draft_mode == MEDUSA_DRAFT_TOPK;
   // greedy / typical: posterior and commit in one workgroup per sequence
   const bool fuse_post = mode != MEDUSA_EXACT;
+  if (fuse_post) {
+    REQUIRE_PTR(x->accept_len);
+    REQUIRE_PTR(x->best_path);
+    REQUIRE_PTR(x->last_node);
+    REQUIRE_PTR(x->out_tokens);
+    REQUIRE_PTR(x->next_root);
+    REQUIRE_PTR(x->h_next);
+    OPTIONAL_PTR(x->kv_len_out_or_null);
+    if (mode == MEDUSA_TYPICAL && (!(x->eps >= 0.f) || !(x->delta >= 0.f)))
+      return fail(MEDUSA_ERR_ARG, "eps, delta must be >= 0");
+  }
   // 1. heads (+ tree tokens and positions)
   rc = heads_impl(shape, x->h, x->W1, x->b1_or_null, x->W2, x->topk_ids, x->topk_logits,
                   x->head_lse_or_null, x->head_logits_or_null, x->z_or_null, workspace,
                   workspace_bytes, stream,
                   fuse_tree ? &plan : nullptr, x->root_tok, x->kv_len, x->tree_tokens,
-                  x->position_ids);
+                  x->position_ids, dry, ev_w2_start, ev_w2_end);
   if (rc) return rc;
   // 2. tree tokens by sampling
   if (!fuse_tree) {
-    rc = medusa_build_tree(shape, x->tree_ranks_host, x->draft_mode, x->root_tok, x->topk_ids,
-                           x->head_logits_or_null, x->head_lse_or_null, x->u_draft_or_null,
-                           x->kv_len, x->tree_tokens,
-                           nullptr, x->position_ids, nullptr, nullptr, nullptr, stream);
+    rc = tree_impl(shape, x->tree_ranks_host, x->draft_mode, x->root_tok, x->topk_ids,
+                   x->head_logits_or_null, x->head_lse_or_null, x->u_draft_or_null, x->kv_len,
+                   x->tree_tokens, nullptr, x->position_ids, nullptr, nullptr, nullptr, stream,
+                   dry);
     if (rc) return rc;
   }
   // 3. verify forward
   rc = verify_impl(shape, x->E, x->W_qkv, x->W_o, x->W_lm, x->rope_theta, x->tree_tokens,
                    x->position_ids, x->tree_mask, x->parent, x->k_cache, x->v_cache, x->kv_len,
                    x->temperature, x->k_tree, x->v_tree, x->y, x->row_stats, x->row_argmax,
-                   x->child_logit, x->verify_logits_or_null, workspace, workspace_bytes, stream);
+                   x->child_logit, x->verify_logits_or_null, workspace, workspace_bytes, stream,
+                   dry);
   if (rc) return rc;
   // 4. posterior and commit
   if (!fuse_post) {
-    rc = medusa_evaluate_posterior(shape, mode, x->temperature, x->eps, x->delta, x->row_stats,
-                                   x->row_argmax, x->child_logit, x->verify_logits_or_null,
-                                   x->tree_tokens, x->parent, x->retrieve,
-                                   x->head_logits_or_null, x->head_lse_or_null,
-                                   x->u_accept_or_null, x->u_resample_or_null, x->accept_len,
-                                   x->best_path, x->last_node, x->out_tokens, x->next_root,
-                                   workspace, workspace_bytes, stream);
+    rc = posterior_impl(shape, mode, x->temperature, x->eps, x->delta, x->row_stats,
+                        x->row_argmax, x->child_logit, x->verify_logits_or_null, x->tree_tokens,
+                        x->parent, x->retrieve, x->head_logits_or_null, x->head_lse_or_null,
+                        x->u_accept_or_null, x->u_resample_or_null, x->accept_len, x->best_path,
+                        x->last_node, x->out_tokens, x->next_root, workspace, workspace_bytes,
+                        stream, dry);
     if (rc) return rc;
     return commit_impl(shape, x->last_node, x->parent, x->k_tree, x->v_tree, x->y,
                        x->k_cache, x->v_cache, x->kv_len, x->kv_len_out_or_null, x->h_next,
-                       stream);
+                       stream, dry);
   }
-  REQUIRE_PTR(x->accept_len);
-  REQUIRE_PTR(x->best_path);
-  REQUIRE_PTR(x->last_node);
-  REQUIRE_PTR(x->out_tokens);
-  REQUIRE_PTR(x->next_root);
-  REQUIRE_PTR(x->h_next);
-  if (mode == MEDUSA_TYPICAL && (!(x->eps >= 0.f) || !(x->delta >= 0.f)))
-    return fail(MEDUSA_ERR_ARG, "eps, delta must be >= 0");
+  if (dry) return MEDUSA_OK;
   PostArgs a{};
   a.mode = mode;
   a.B = shape->B;
@@ -864,6 +914,26 @@ int medusa_step(const medusa_shape* shape, const medusa_step_args* x, void* work
   hipError_t e = launch_posterior_commit(a, c, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "posterior launch");
   return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+int medusa_step(const medusa_shape* shape, const medusa_step_args* x, void* workspace,
+                size_t workspace_bytes, void* stream) {
+  const int rc = step_impl(shape, x, workspace, workspace_bytes, stream, true);
+  if (rc) return rc;
+  return step_impl(shape, x, workspace, workspace_bytes, stream, false);
+}
+
+int medusa_step_timed(const medusa_shape* shape, const medusa_step_args* x, void* workspace,
+                      size_t workspace_bytes, void* stream, void* ev_w2_start, void* ev_w2_end) {
+  if (!ev_w2_start || !ev_w2_end) return fail(MEDUSA_ERR_ARG, "step_timed: null event");
+  const int rc = step_impl(shape, x, workspace, workspace_bytes, stream, true);
+  if (rc) return rc;
+  return step_impl(shape, x, workspace, workspace_bytes, stream, false,
+                   static_cast<hipEvent_t>(ev_w2_start), static_cast<hipEvent_t>(ev_w2_end));
 }
 
 }  // extern "C"
@@ -971,8 +1041,9 @@ int medusa_generate(const medusa_shape* shape, const medusa_step_args* args, int
                     size_t workspace_bytes, void* stream) {
   int rc = check_shape(shape);
   if (rc) return rc;
-  if (!args || !out_tokens_steps || !accept_len_steps)
-    return fail(MEDUSA_ERR_ARG, "generate: null pointer");
+  if (!args) return fail(MEDUSA_ERR_ARG, "generate: args: null pointer");
+  REQUIRE_PTR(out_tokens_steps);
+  REQUIRE_PTR(accept_len_steps);
   if (n_steps < 0) return fail(MEDUSA_ERR_ARG, "generate: n_steps=%d", n_steps);
   if (args->kv_len_out_or_null)
     return fail(MEDUSA_ERR_ARG, "generate: the loop advances kv_len in place (kv_len_out_or_null must be NULL)");
@@ -984,8 +1055,8 @@ int medusa_generate(const medusa_shape* shape, const medusa_step_args* args, int
   // the state alternates between (h, root_tok) and (h_next, next_root)
   float* hs[2] = {const_cast<float*>(args->h), args->h_next};
   int32_t* roots[2] = {const_cast<int32_t*>(args->root_tok), args->next_root};
-  medusa_step_args x = *args;
-  for (int i = 0; i < n_steps; ++i) {
+  const auto step_args = [&](int i) {
+    medusa_step_args x = *args;
     const int cur = i & 1;
     x.h = hs[cur];
     x.root_tok = roots[cur];
@@ -993,11 +1064,22 @@ int medusa_generate(const medusa_shape* shape, const medusa_step_args* args, int
     x.next_root = roots[cur ^ 1];
     x.out_tokens = out_tokens_steps + (size_t)i * MEDUSA_ALIGN4(B * K1);
     x.accept_len = accept_len_steps + (size_t)i * MEDUSA_ALIGN4(B);
-    if (args->u_draft_or_null) x.u_draft_or_null = args->u_draft_or_null + (size_t)i * B * T;
-    if (args->u_accept_or_null) x.u_accept_or_null = args->u_accept_or_null + (size_t)i * B * T;
-    if (args->u_resample_or_null)
-      x.u_resample_or_null = args->u_resample_or_null + (size_t)i * B * T;
-    rc = medusa_step(shape, &x, workspace, workspace_bytes, stream);
+    // per-step uniform blocks keep the 16-byte alignment of the first
+    const size_t ustep = (size_t)i * MEDUSA_ALIGN4(B * T);
+    if (args->u_draft_or_null) x.u_draft_or_null = args->u_draft_or_null + ustep;
+    if (args->u_accept_or_null) x.u_accept_or_null = args->u_accept_or_null + ustep;
+    if (args->u_resample_or_null) x.u_resample_or_null = args->u_resample_or_null + ustep;
+    return x;
+  };
+  // every step is validated before the first launch
+  for (int i = 0; i < n_steps; ++i) {
+    const medusa_step_args x = step_args(i);
+    rc = step_impl(shape, &x, workspace, workspace_bytes, stream, true);
+    if (rc) return rc;
+  }
+  for (int i = 0; i < n_steps; ++i) {
+    const medusa_step_args x = step_args(i);
+    rc = step_impl(shape, &x, workspace, workspace_bytes, stream, false);
     if (rc) return rc;
   }
   if (n_steps & 1) {

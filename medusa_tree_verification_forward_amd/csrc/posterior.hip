@@ -394,6 +394,9 @@ __global__ __launch_bounds__(1024) void posterior_exact_lds_kernel(PostArgs a) {
       next = s_next;
       break;
     }
+    // Every wave has read p[x] for the decision above before any wave
+    // overwrites p with the accepted child's row.
+    __syncthreads();
     v = taken;
     load_p(v);
   }

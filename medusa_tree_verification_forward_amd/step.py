@@ -203,26 +203,43 @@ class VerifyStep:
             self._args = a
         return a
 
-    def run_step(self, stream=None, keep_kv_len: bool = False):
+    def run_step(self, stream=None, keep_kv_len: bool = False, w2_events=None):
         """The whole step as one composite call (medusa_step); see step_args
-        for keep_kv_len."""
-        L.step(self.shape, self.step_args(keep_kv_len), self.ws, stream=stream)
+        for keep_kv_len. w2_events = (start, end): medusa_step_timed records
+        them around the vocabulary-projection kernel."""
+        if w2_events is None:
+            L.step(self.shape, self.step_args(keep_kv_len), self.ws, stream=stream)
+        else:
+            L.step_timed(self.shape, self.step_args(keep_kv_len), self.ws, w2_events[0],
+                         w2_events[1], stream=stream)
 
     def generate(self, n_steps: int, stream=None, uniforms=None):
         """medusa_generate: n_steps steps with the state kept on the device.
         Returns (out_tokens [n][B][K+1], accept_len [n][B]) device tensors;
         afterwards inp["h"], inp["root"], inp["kv_len"] and the caches hold the
         advanced state. Exact mode takes uniforms = {u_draft, u_accept,
-        u_resample}, each [n][B][T] on the device."""
+        u_resample}, each a float32 [n][B][T] tensor on the device."""
         import torch
         a = L.StepArgs.from_buffer_copy(self.step_args(False))
+        B, K, T = self.shape.B, self.shape.K, self.T
         if self.mode == "exact":
             if uniforms is None:
                 raise ValueError("exact mode needs per-step uniforms")
-            a.u_draft_or_null = L._ptr(uniforms["u_draft"])
-            a.u_accept_or_null = L._ptr(uniforms["u_accept"])
-            a.u_resample_or_null = L._ptr(uniforms["u_resample"])
-        B, K = self.shape.B, self.shape.K
+            # the library reads step i's [B][T] block at element
+            # i * MEDUSA_ALIGN4(B*T): copy into blocks of that stride (kept
+            # alive on self until the next call)
+            bt = (B * T + 3) & ~3
+            self._u_blocks = {}
+            for name in ("u_draft", "u_accept", "u_resample"):
+                u = uniforms[name]
+                if tuple(u.shape) != (n_steps, B, T):
+                    raise ValueError(f"{name}: shape {tuple(u.shape)}, want {(n_steps, B, T)}")
+                blk = torch.zeros((max(n_steps, 1), bt), dtype=torch.float32, device=u.device)
+                blk[:n_steps, :B * T] = u.reshape(n_steps, B * T)
+                self._u_blocks[name] = blk
+            a.u_draft_or_null = L._ptr(self._u_blocks["u_draft"])
+            a.u_accept_or_null = L._ptr(self._u_blocks["u_accept"])
+            a.u_resample_or_null = L._ptr(self._u_blocks["u_resample"])
         ot, al = (B * (K + 1) + 3) & ~3, (B + 3) & ~3   # 16-byte aligned step blocks
         n = max(n_steps, 1)
         toks = torch.full((n, ot), -1, dtype=torch.int32, device="cuda")

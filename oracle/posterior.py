@@ -44,7 +44,7 @@ from typing import Dict, Optional
 
 import numpy as np
 
-from .tree import Topology, inverse_cdf
+from .tree import Topology, inverse_cdf, inverse_cdf_margin
 
 
 def typical_accepts(p_tok: float, entropy: float, eps: float, delta: float) -> bool:
@@ -122,38 +122,55 @@ def posterior_deterministic(topo: Topology, tokens: np.ndarray, acc: np.ndarray,
     return _result(topo, tokens, best, int(argmax[best]))
 
 
+def _log_gap(a: float, b: float) -> float:
+    """|log a - log b| for the test a < b; inf when exactly one side is 0
+    (the decision cannot flip), 0 when both are."""
+    if a > 0 and b > 0:
+        return float(abs(np.log(a) - np.log(b)))
+    return 0.0 if a == b else float(np.inf)
+
+
 def posterior_exact(topo: Topology, tokens: np.ndarray, p_rows: np.ndarray,
                     q_heads: np.ndarray, u_accept: np.ndarray,
-                    u_resample: np.ndarray) -> Dict:
+                    u_resample: np.ndarray, with_margins: bool = False) -> Dict:
     """Recursive p/q rejection over the tree (reading above).
 
     p_rows [T, V]: target distribution at every node; q_heads [K, V]: the
     drafting distribution of each depth (head k drafts depth k+1, 0-based
-    index k); u_accept, u_resample [T].
+    index k); u_accept, u_resample [T]. with_margins adds "accept_margin"
+    (the smallest |log(u q(x)) - log p(x)| over the acceptance tests taken,
+    inf if none) and "draw_margin" (``inverse_cdf_margin`` of the final
+    draw): how far the walk's decisions are from flipping.
     """
     v = 0
     p = np.array(p_rows[0], dtype=np.float64)
+    acc_margin = np.inf
     while True:
         kids = topo.children(v)
         if not kids:
-            nxt = inverse_cdf(p, float(u_resample[v]))
             break
         q = q_heads[topo.depth[v]]
         taken = None
         for c in kids:
             x = int(tokens[c])
-            if float(u_accept[c]) * q[x] < p[x]:
+            uq = float(u_accept[c]) * q[x]
+            acc_margin = min(acc_margin, _log_gap(uq, p[x]))
+            if uq < p[x]:
                 taken = c
                 break
             r = np.maximum(p - q, 0.0)
             if r.sum() > 0:
                 p = r / r.sum()
         if taken is None:
-            nxt = inverse_cdf(p, float(u_resample[v]))
             break
         v = taken
         p = np.array(p_rows[v], dtype=np.float64)
-    return _result(topo, tokens, v, nxt)
+    nxt = inverse_cdf(p, float(u_resample[v]))
+    out = _result(topo, tokens, v, nxt)
+    if with_margins:
+        out["accept_margin"] = float(acc_margin)
+        out["draw_margin"] = inverse_cdf_margin(p, float(u_resample[v]))
+    return out
 
 
 def commit(topo: Topology, last_node: int, k_tree: np.ndarray, v_tree: np.ndarray,

@@ -22,13 +22,16 @@ from .numerics import widen
 
 def verify_step(inp: Dict[str, np.ndarray], *, H: int, Dh: int, s_max: int, mode: str,
                 tau: float, eps: float, delta: float, theta: float, bf16: bool,
-                want_margins: bool = True) -> Dict:
+                want_margins: bool = True,
+                tokens_override: Optional[np.ndarray] = None) -> Dict:
     """Run one step for every sequence of a batch.
 
     ``inp`` holds h [B,d], W1, W2, E, W_qkv, W_o, W_lm, k_cache, v_cache
     [B,H,Lmax,Dh], kv_len [B], root [B], ranks [N,K] and (exact mode)
     u_draft, u_accept, u_resample [B,T]. Returns a dict of per-stage
-    results, batched along the first axis.
+    results, batched along the first axis. tokens_override [B,T], when
+    given, replaces the drafted tree tokens (every later stage then runs on
+    those tokens), so a run can be repeated on another drafter's tokens.
     """
     h = np.asarray(inp["h"], dtype=np.float64)
     B = h.shape[0]
@@ -43,7 +46,8 @@ def verify_step(inp: Dict[str, np.ndarray], *, H: int, Dh: int, s_max: int, mode
     keys = ["tokens", "positions", "q", "k", "v", "o", "y", "logits", "p_entropy",
             "argmax", "acc", "accept_len", "last_node", "best_path", "out_tokens",
             "next_root", "kv_len_next", "h_next", "k_cache_next", "v_cache_next",
-            "row_max", "topk_margin", "decision_margin", "argmax_margin"]
+            "row_max", "topk_margin", "decision_margin", "argmax_margin",
+            "draft_margin", "accept_margin", "draw_margin"]
     per = {k_: [] for k_ in keys}
     for b in range(B):
         L = int(inp["kv_len"][b])
@@ -51,6 +55,8 @@ def verify_step(inp: Dict[str, np.ndarray], *, H: int, Dh: int, s_max: int, mode
             tok = T_.draft_tokens_sampled(topo, int(inp["root"][b]), hl[b], inp["u_draft"][b])
         else:
             tok = T_.draft_tokens_topk(topo, int(inp["root"][b]), topk_ids[b])
+        if tokens_override is not None:
+            tok = np.asarray(tokens_override[b], dtype=np.int32).copy()
         pos = T_.position_ids(topo, L)
         vf = V_.verifier_forward(inp["E"], inp["W_qkv"], inp["W_o"], inp["W_lm"], tok, pos,
                                  topo.mask, inp["k_cache"][b], inp["v_cache"][b], L, H, Dh,
@@ -67,7 +73,7 @@ def verify_step(inp: Dict[str, np.ndarray], *, H: int, Dh: int, s_max: int, mode
             qh = np.stack([T_.softmax(hl[b, k]) for k in range(K)])
             acc = np.zeros(T, dtype=bool)
             post = P_.posterior_exact(topo, tok, p, qh, inp["u_accept"][b],
-                                      inp["u_resample"][b])
+                                      inp["u_resample"][b], with_margins=want_margins)
         else:
             raise ValueError(mode)
         kc, vc, Lnext, hnext = P_.commit(topo, post["last_node"], vf["k"], vf["v"], vf["y"],
@@ -91,6 +97,10 @@ def verify_step(inp: Dict[str, np.ndarray], *, H: int, Dh: int, s_max: int, mode
             per["decision_margin"].append(
                 P_.decision_margins(topo, tok, logits, tau, mode, eps, delta, p, ent))
             per["argmax_margin"].append(P_.argmax_margin(logits[post["last_node"]]))
+            if mode == "exact":
+                per["draft_margin"].append(T_.draft_margins(topo, hl[b], inp["u_draft"][b]))
+                per["accept_margin"].append(post["accept_margin"])
+                per["draw_margin"].append(post["draw_margin"])
     for k_, v_ in per.items():
         if v_:
             res[k_] = np.stack([np.asarray(x) for x in v_])

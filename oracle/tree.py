@@ -199,6 +199,26 @@ def inverse_cdf(weights: np.ndarray, u: float) -> int:
     return min(x, last)
 
 
+def inverse_cdf_margin(weights: np.ndarray, u: float) -> float:
+    """Distance of an inverse-CDF draw from its flip points.
+
+    With C and the drawn token x as in ``inverse_cdf``, the draw point
+    u * C(last) lies in x's step [C(x-1), C(x)); the margin is its distance
+    to the nearer edge of that step as a fraction of C(last). A draw
+    computed from weights (or a CDF) with relative errors below the margin
+    picks the same token; a margin of 0 means the point sits on an edge.
+    """
+    w = np.asarray(weights, dtype=np.float64)
+    C = np.cumsum(w)
+    total = C[-1]
+    if not total > 0:
+        return 0.0
+    x = inverse_cdf(w, u)
+    point = u * total
+    lo = C[x - 1] if x > 0 else 0.0
+    return float(max(0.0, min(point - lo, C[x] - point)) / total)
+
+
 def softmax(logits: np.ndarray, tau: float = 1.0) -> np.ndarray:
     z = np.asarray(logits, dtype=np.float64) / tau
     e = np.exp(z - z.max())
@@ -218,3 +238,13 @@ def draft_tokens_sampled(topo: Topology, root: int, head_logits: np.ndarray,
     for n in range(1, topo.T):
         tok[n] = inverse_cdf(q[topo.depth[n] - 1], float(u_draft[n]))
     return tok
+
+
+def draft_margins(topo: Topology, head_logits: np.ndarray, u_draft: np.ndarray) -> np.ndarray:
+    """inverse_cdf_margin of every node's draw in ``draft_tokens_sampled``
+    ([T]; the root, which draws nothing, gets inf)."""
+    q = [softmax(head_logits[k]) for k in range(head_logits.shape[0])]
+    m = np.full(topo.T, np.inf)
+    for n in range(1, topo.T):
+        m[n] = inverse_cdf_margin(q[topo.depth[n] - 1], float(u_draft[n]))
+    return m

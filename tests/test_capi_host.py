@@ -144,3 +144,81 @@ def test_step_args_layout_matches_header(tmp_path):
                                           check=True).stdout.split()]
     assert out[0] == ctypes.sizeof(M.StepArgs)
     assert out[1:] == [getattr(M.StepArgs, n).offset for n in names]
+
+
+def _step_args(M, ranks, exact=True):
+    """medusa_step_args with every device pointer a fake aligned address."""
+    a = M.StepArgs()
+    for name, _ in M.StepArgs._fields_:
+        if name not in ("draft_mode", "mode", "rope_theta", "temperature", "eps", "delta",
+                        "tree_ranks_host", "b1_or_null", "kv_len_out_or_null"):
+            setattr(a, name, FAKE)
+    a.tree_ranks_host = ranks.ctypes.data
+    a.draft_mode = M.DRAFT_SAMPLE if exact else M.DRAFT_TOPK
+    a.mode = M.EXACT if exact else M.TYPICAL
+    a.rope_theta, a.temperature, a.eps, a.delta = 10000.0, 1.0, 0.09, 0.3
+    return a
+
+
+def test_step_validates_every_part_before_launching():
+    # A bad pointer of a late part (the verifier's embedding, the posterior's
+    # uniforms) is reported as an argument error. On a machine without a GPU
+    # a launch would fail with MEDUSA_ERR_HIP, so ERR_ARG shows that the
+    # earlier parts (heads, tree) were not launched either.
+    M = _lib()
+    from workloads import cartesian_ranks
+    ranks = cartesian_ranks((3, 2, 2, 1, 1))
+    shape = _shape(M)
+    nbytes = M.workspace_bytes(shape)
+    lib = M._lib._lib
+    for field, exact in (("E", False), ("W_lm", True), ("u_accept_or_null", True),
+                         ("h_next", False), ("h_next", True)):
+        a = _step_args(M, ranks, exact)
+        setattr(a, field, None)
+        rc = lib.medusa_step(ctypes.byref(shape), ctypes.byref(a), FAKE, nbytes, None)
+        assert rc == M._lib.ERR_ARG, (field, rc, M.last_error())
+        assert field.split("_or_null")[0] in M.last_error(), (field, M.last_error())
+
+
+def test_generate_validates_every_step_before_launching():
+    # Exact mode at B=1, T=46: a step's uniform block is 46 floats, not a
+    # multiple of 4, so the library advances by MEDUSA_ALIGN4(B*T) = 48 per
+    # step. A misaligned base pointer is rejected before anything launches,
+    # and so is a null pointer that only a later stage reads.
+    M = _lib()
+    from workloads import cartesian_ranks
+    ranks = cartesian_ranks((3, 2, 2, 1, 1))
+    shape = _shape(M)
+    nbytes = M.workspace_bytes(shape)
+    lib = M._lib._lib
+    for field, value in (("u_resample_or_null", FAKE + 4), ("u_draft_or_null", FAKE + 8),
+                         ("y", None), ("k_tree", FAKE + 2)):
+        a = _step_args(M, ranks, exact=True)
+        setattr(a, field, value)
+        rc = lib.medusa_generate(ctypes.byref(shape), ctypes.byref(a), 5, FAKE, FAKE, FAKE,
+                                 nbytes, None)
+        assert rc == M._lib.ERR_ARG, (field, rc, M.last_error())
+        assert field.split("_or_null")[0] in M.last_error(), (field, M.last_error())
+    # the per-step output blocks must be aligned too
+    a = _step_args(M, ranks, exact=True)
+    rc = lib.medusa_generate(ctypes.byref(shape), ctypes.byref(a), 5, FAKE + 4, FAKE, FAKE,
+                             nbytes, None)
+    assert rc == M._lib.ERR_ARG and "out_tokens_steps" in M.last_error()
+    # the loop advances kv_len in place
+    a = _step_args(M, ranks, exact=True)
+    a.kv_len_out_or_null = FAKE
+    rc = lib.medusa_generate(ctypes.byref(shape), ctypes.byref(a), 5, FAKE, FAKE, FAKE,
+                             nbytes, None)
+    assert rc == M._lib.ERR_ARG and "kv_len_out_or_null" in M.last_error()
+
+
+def test_step_timed_needs_both_events():
+    M = _lib()
+    from workloads import cartesian_ranks
+    ranks = cartesian_ranks((3, 2, 2, 1, 1))
+    shape = _shape(M)
+    a = _step_args(M, ranks, exact=False)
+    lib = M._lib._lib
+    rc = lib.medusa_step_timed(ctypes.byref(shape), ctypes.byref(a), FAKE,
+                               M.workspace_bytes(shape), None, FAKE, None)
+    assert rc == M._lib.ERR_ARG and "event" in M.last_error()

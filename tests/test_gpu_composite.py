@@ -59,8 +59,9 @@ def test_composite_full_size_7b():
     g = parity.gpu_step(w, inp, composite=True)
     report = {}
     parity.compare_step(w, inp, g, o, report)
-    assert report.get("ambiguous", 0) <= 2, report
-    parity.gpu_posterior_consistent(w, g, o["topo"])
+    assert report["ambiguous"] <= 2, report
+    assert report["decisions_checked"] == w.B, report
+    assert parity.gpu_posterior_consistent(w, g, o["topo"], inp) == w.B
 
 
 def test_composite_calibrated_sparse_tree():
@@ -86,5 +87,6 @@ def test_composite_calibrated_sparse_tree():
     g = parity.gpu_step(w, inp, composite=True)
     report = {}
     parity.compare_step(w, inp, g, o, report)
-    assert report.get("ambiguous", 0) <= 2, report
-    parity.gpu_posterior_consistent(w, g, o["topo"])
+    assert report["ambiguous"] <= 2, report
+    assert report["decisions_checked"] == w.B, report
+    assert parity.gpu_posterior_consistent(w, g, o["topo"], inp) == w.B

@@ -72,3 +72,81 @@ def test_generate_in_two_calls():
     assert np.array_equal(to_host(a1), np.concatenate([to_host(aa), to_host(ab)]))
     for k in ("h", "root", "kv_len", "k_cache", "v_cache"):
         assert np.array_equal(to_host(one.inp[k]), to_host(two.inp[k])), k
+
+
+def _exact_loop_inputs(n, B, seed):
+    inp = _inputs(n, B=B, seed=seed)
+    rng = np.random.default_rng(seed + 1)
+    T = SPEC.shape[0] + 1
+    for name in ("u_draft", "u_accept", "u_resample"):
+        inp[name + "_steps"] = rng.random((n, B, T), dtype=np.float32)
+        inp[name] = inp[name + "_steps"][0].copy()
+    return inp
+
+
+U_NAMES = ("u_draft", "u_accept", "u_resample")
+
+
+def test_generate_exact_mode_equals_single_steps():
+    # Exact p/q rejection in the decoding loop, 6 steps on the 45-node tree
+    # at B = 1 (a step's [B][T] uniform block is 46 floats, so the library's
+    # per-step stride MEDUSA_ALIGN4(B*T) = 48 differs from B*T): the loop must
+    # reproduce, bit for bit, the same steps issued one composite call at a
+    # time with the state handed on by the caller.
+    require_gpu()
+    import torch
+    from medusa_tree_verification_forward_amd.step import to_host, to_device
+    n = 6
+    for B in (1, 3):
+        inp = _exact_loop_inputs(n, B, seed=77 + B)
+        loop = _step(inp, "exact")
+        toks, acc = loop.generate(n, uniforms={k: to_device(inp[k + "_steps"])
+                                               for k in U_NAMES})
+        one = _step(inp, "exact")
+        s_toks, s_acc = [], []
+        for i in range(n):
+            for k in U_NAMES:
+                one.inp[k].copy_(to_device(inp[k + "_steps"][i]))
+            one.run_step()
+            one.inp["h"].copy_(one.out["h_next"])
+            one.inp["root"].copy_(one.out["next_root"])
+            s_toks.append(one.out["out_tokens"].clone())
+            s_acc.append(one.out["accept_len"].clone())
+        torch.cuda.synchronize()
+        assert np.array_equal(to_host(toks), np.stack([to_host(t) for t in s_toks])), B
+        assert np.array_equal(to_host(acc), np.stack([to_host(a) for a in s_acc])), B
+        for k in ("h", "root", "kv_len", "k_cache", "v_cache"):
+            assert np.array_equal(to_host(loop.inp[k]), to_host(one.inp[k])), (B, k)
+        assert to_host(acc).sum() > 0
+
+
+def test_generate_exact_mode_matches_oracle_loop():
+    # The same loop against the oracle's: every step of every sequence must
+    # be the oracle loop's until the first step with a sampling decision
+    # within float error of its flip point (a draft draw within float32
+    # rounding of a CDF edge, an acceptance test within 1e-3 of log p/q, the
+    # final draw within 1e-4 of an edge); later steps of that sequence
+    # depend on it and are not compared.
+    require_gpu()
+    import torch
+    from medusa_tree_verification_forward_amd.step import to_host, to_device
+    n, B = 6, 3
+    inp = _exact_loop_inputs(n, B, seed=77)
+    st = _step(inp, "exact")
+    toks, acc = st.generate(n, uniforms={k: to_device(inp[k + "_steps"]) for k in U_NAMES})
+    torch.cuda.synchronize()
+    o = OG.generate(inp, n, exact_margins=True, mode="exact", bf16=True, **STEP)
+    gt, ga = to_host(toks), to_host(acc)
+    near = ((o["draft_margin"] < 2e-6) | (o["accept_margin"] < 1e-3)
+            | (o["draw_margin"] < 1e-4))
+    compared = 0
+    for b in range(B):
+        for i in range(n):
+            if near[i, b]:
+                break
+            assert ga[i, b] == o["accept_len"][i, b], (i, b)
+            assert np.array_equal(gt[i, b], o["out_tokens"][i, b]), (i, b)
+            compared += 1
+    print("compared steps", compared, "of", n * B)
+    assert compared >= n, (compared, o["draft_margin"], o["accept_margin"], o["draw_margin"])
+    assert o["accept_len"].sum() > 0 and (o["accept_len"] == 0).any()

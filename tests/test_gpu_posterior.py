@@ -367,6 +367,76 @@ def test_exact_rule_agrees_with_oracle_large_vocab():
     assert 0 < accepted < total          # both outcomes occur
 
 
+def test_exact_lds_kernel_agrees_with_oracle_per_trial_v32000():
+    # V = 32000, the 7B vocabulary: the posterior keeps the target in LDS and
+    # reads its CDF in 16-token chunks. 1024 trials (64 sequences x 16
+    # calls); drafting on the GPU, the oracle's rule on the GPU's drafted
+    # tokens with the same float32 logits and uniforms. Verify rows are the
+    # drafting head's logits plus noise drawn from a bank, so children are
+    # accepted and rejected (residual resampling) in a mix. A trial may
+    # disagree only where the oracle's walk lies within float32 rounding of
+    # a flip point, and at most once.
+    import torch
+    import medusa_tree_verification_forward_amd as M
+    require_gpu()
+    K, V, B, calls = 5, 32000, 64, 16
+    rng = np.random.default_rng(32000)
+    spec = cartesian_ranks((3, 2, 2, 1, 1))
+    topo = OT.topology(spec, K)
+    T = topo.T
+    head_logits = (rng.standard_normal((K, V)) * 1.5).astype(np.float32)
+    lse = scipy.special.logsumexp(head_logits.astype(np.float64), axis=-1).astype(np.float32)
+    q = scipy.special.softmax(head_logits.astype(np.float64), axis=-1)
+    bank = (rng.standard_normal((64, V)) * 0.6).astype(np.float32)
+    node_head = np.minimum(topo.depth, K - 1)
+    shape = M.make_shape(B, 128, V, K, 1, 128, 4096, T - 1, topo.P, 3, "bf16")
+    ws = workspace(M.workspace_bytes(shape))
+    hl = dev(np.ascontiguousarray(np.broadcast_to(head_logits, (B, K, V))))
+    hlse = dev(np.ascontiguousarray(np.broadcast_to(lse, (B, K))))
+    i32 = torch.int32
+    tok = poisoned((B, T), i32)
+    mask = poisoned((T, T), torch.uint8)
+    pos = poisoned((B, T), i32)
+    ret = poisoned((topo.P, K + 1), i32)
+    par = poisoned((T,), i32)
+    dep = poisoned((T,), i32)
+    o = _outs(torch, B, K)
+    disagree, total, lens = [], 0, set()
+    for it in range(calls):
+        u = rng.random((3, B, T), dtype=np.float32)
+        M.build_tree(shape, spec, dev(np.zeros(B, np.int32)), dev(np.zeros(B, np.int32)), tok,
+                     mask, pos, ret, par, dep, draft_mode=M.DRAFT_SAMPLE, head_logits=hl,
+                     head_lse=hlse, u_draft=dev(u[0]))
+        t = host(tok)
+        idx = rng.integers(0, bank.shape[0], size=(B, T))
+        vl = head_logits[node_head][None, :, :] + bank[idx]
+        M.evaluate_posterior(shape, "exact", 1.0, 0.0, 0.0, None, None, None, tok, par, ret,
+                             o["accept_len"], o["best_path"], o["last_node"], o["out_tokens"],
+                             o["next_root"], ws, verify_logits=dev(vl), head_logits=hl,
+                             head_lse=hlse, u_accept=dev(u[1]), u_resample=dev(u[2]))
+        torch.cuda.synchronize()
+        g = {k: host(v) for k, v in o.items()}
+        for b in range(B):
+            ref_t = OT.draft_tokens_sampled(topo, 0, head_logits.astype(np.float64), u[0, b])
+            dm = OT.draft_margins(topo, head_logits.astype(np.float64), u[0, b])
+            bad = np.nonzero(ref_t[1:] != t[b, 1:])[0] + 1
+            assert np.all(dm[bad] < 2e-6), (it, b, bad, dm[bad])
+            p_rows = scipy.special.softmax(vl[b].astype(np.float64), axis=-1)
+            ref = OP.posterior_exact(topo, t[b], p_rows, q, u[1, b], u[2, b], with_margins=True)
+            total += 1
+            lens.add(int(ref["accept_len"]))
+            same = (all(g[k][b] == ref[k] for k in ("accept_len", "last_node", "best_path",
+                                                     "next_root"))
+                    and np.array_equal(ref["out_tokens"], g["out_tokens"][b]))
+            if not same:
+                disagree.append((it, b, ref["accept_margin"], ref["draw_margin"]))
+    assert total == B * calls
+    assert len(disagree) <= 1, disagree
+    for _, _, am, dm in disagree:
+        assert am < 1e-5 or dm < 2e-6, disagree
+    assert len(lens) >= 3, lens          # accepted depths 0, 1, 2, ... all occur
+
+
 def test_commit_capacity_guard():
     import torch
     import medusa_tree_verification_forward_amd as M

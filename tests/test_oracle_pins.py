@@ -676,3 +676,137 @@ def test_sparse_tree_cover_is_tail_sum():
             d += 1
         depth_sum += d
     assert depth_sum / n == pytest.approx(OS.expected_cover(a, picks), abs=0.02)
+
+
+# ---------------------------------------------------------------- q/k/v block order
+
+@pytest.mark.parametrize("blk", [0, 1, 2])
+def test_qkv_single_entry_block_and_head(blk):
+    # W_qkv rows are [q | k | v], each block d rows in head-major order
+    # (row h*Dh + i is head h, lane i). A single nonzero weight in block blk
+    # at (blk*d + h*Dh + i, j), fed the one-hot row e_j at position 0 (where
+    # the rotation is the identity), must show up in that block's tensor at
+    # [h, i] alone; the other two tensors stay zero.
+    H, Dh = 3, 8
+    d = H * Dh
+    h_, i_, j_ = 2, 5, 7
+    W = np.zeros((3 * d, d))
+    W[blk * d + h_ * Dh + i_, j_] = 1.5
+    x = np.zeros((1, d))
+    x[0, j_] = 1.0
+    q, k, v = OV.qkv_project(x, W, np.array([0]), H, Dh, 10000.0, bf16=False)
+    outs = [q, k, v]
+    for b, t in enumerate(outs):
+        want = np.zeros((1, H, Dh))
+        if b == blk:
+            want[0, h_, i_] = 1.5
+        assert np.array_equal(t, want), (blk, b)
+
+
+@pytest.mark.parametrize("blk", [0, 1, 2])
+def test_qkv_single_entry_rotation_stays_in_pair(blk):
+    # At a nonzero position q and k rotate pairs (i, i + Dh/2) of one head and
+    # v does not rotate: the single weight's output stays in its own head and
+    # in lanes {i, partner} of its own block (v: lane i alone, unchanged),
+    # and the pair's norm is kept.
+    H, Dh = 2, 8
+    d = H * Dh
+    h_, i_, j_ = 1, 6, 3
+    partner = i_ - Dh // 2
+    W = np.zeros((3 * d, d))
+    W[blk * d + h_ * Dh + i_, j_] = 2.0
+    x = np.zeros((1, d))
+    x[0, j_] = 1.0
+    outs = OV.qkv_project(x, W, np.array([37]), H, Dh, 10000.0, bf16=False)
+    for b, t in enumerate(outs):
+        if b != blk:
+            assert not np.any(t), (blk, b)
+            continue
+        nz = set(zip(*np.nonzero(t[0])))
+        if blk == 2:
+            assert nz == {(h_, i_)} and t[0, h_, i_] == 2.0
+        else:
+            assert nz <= {(h_, i_), (h_, partner)} and len(nz) == 2
+            assert np.isclose(np.hypot(t[0, h_, i_], t[0, h_, partner]), 2.0, rtol=1e-14)
+
+
+# ---------------------------------------------------------------- margin helpers
+
+def test_topk_margin_closed_forms():
+    row = np.array([5.0, 3.0, 3.5, 1.0, -2.0])
+    # sorted 5, 3.5, 3, 1, -2: top-1 needs the gap 5-3.5, top-2 also 3.5-3
+    assert OH.topk_margin(row, 1) == 1.5
+    assert OH.topk_margin(row, 2) == 0.5
+    assert OH.topk_margin(row, 3) == 0.5
+    assert OH.topk_margin(np.array([2.0, 2.0, 1.0]), 1) == 0.0
+    assert OH.topk_margin(np.array([4.0, 1.0, 0.0]), 2) == 1.0
+
+
+def test_argmax_margin_closed_forms():
+    assert OP.argmax_margin(np.array([1.0, 4.0, 2.0])) == 2.0
+    assert OP.argmax_margin(np.array([3.0, -1.0, 3.0])) == 0.0
+    assert OP.argmax_margin(np.array([-5.0, -2.5])) == 2.5
+
+
+def test_decision_margins_closed_forms():
+    topo = OT.topology(np.array([[0], [1]], dtype=np.int32), 1)
+    logits = np.array([[1.0, 4.0, 2.0], [0, 0, 0], [0, 0, 0]])
+    tokens = np.array([9, 0, 1])
+    m = OP.decision_margins(topo, tokens, logits, 1.0, "greedy", 0.09, 0.3)
+    assert m[0] == np.inf
+    assert m[1] == 3.0          # token 0 (logit 1) against the best other, 4
+    assert m[2] == 2.0          # token 1 (logit 4) against the best other, 2
+    # typical, uniform p over 4 tokens: H = ln 4, threshold min(0.09, 0.3/4)
+    p = np.full((3, 4), 0.25)
+    Hh = np.full(3, np.log(4.0))
+    m = OP.decision_margins(topo, tokens, np.zeros((3, 4)), 1.0, "typical", 0.09, 0.3, p, Hh)
+    assert np.isclose(m[1], np.log(0.25 / 0.075), rtol=1e-14)
+    assert np.isclose(m[2], np.log(0.25 / 0.075), rtol=1e-14)
+    # a one-hot row: threshold min(eps, delta) = 0.09; the hot token's margin
+    # is log(1/0.09)
+    p1 = np.zeros((3, 4))
+    p1[0, 1] = 1.0
+    H1 = np.zeros(3)
+    m = OP.decision_margins(topo, np.array([0, 1, 1]), np.zeros((3, 4)), 1.0, "typical",
+                            0.09, 0.3, p1, H1)
+    assert np.isclose(m[1], np.log(1 / 0.09), rtol=1e-14)
+
+
+def test_inverse_cdf_margin_closed_forms():
+    w = np.ones(4)                      # C = 1, 2, 3, 4 of 4
+    assert OT.inverse_cdf(w, 0.3) == 1
+    assert np.isclose(OT.inverse_cdf_margin(w, 0.3), 0.05, rtol=1e-12)
+    assert np.isclose(OT.inverse_cdf_margin(w, 0.9), 0.1, rtol=1e-12)
+    assert OT.inverse_cdf_margin(w, 0.0) == 0.0          # on the first edge
+    w = np.array([0.0, 2.0, 0.0, 2.0])  # C = 0, 2, 2, 4: u = 0.5 sits on an edge
+    assert OT.inverse_cdf(w, 0.5) == 3
+    assert OT.inverse_cdf_margin(w, 0.5) == 0.0
+    assert np.isclose(OT.inverse_cdf_margin(w, 0.625), 0.125, rtol=1e-12)
+    # unnormalised weights: the margin is a fraction of the total
+    assert np.isclose(OT.inverse_cdf_margin(10 * np.ones(4), 0.3), 0.05, rtol=1e-12)
+
+
+def test_exact_posterior_margins_closed_form():
+    # root -> one child (a leaf). p_root = (0.5, 0.5), q = (0.8, 0.2); the
+    # child's token 0 with u = 0.5: u q = 0.4 < 0.5, accepted with log margin
+    # log(0.5/0.4). The leaf's target (0.25, 0.75) is drawn with u = 0.1:
+    # point 0.1 in token 0's step [0, 0.25), margin 0.1.
+    topo = OT.topology(np.array([[0]], dtype=np.int32), 1)
+    p_rows = np.array([[0.5, 0.5], [0.25, 0.75]])
+    q = np.array([[0.8, 0.2]])
+    r = OP.posterior_exact(topo, np.array([1, 0]), p_rows, q, np.array([0.0, 0.5]),
+                           np.array([0.0, 0.1]), with_margins=True)
+    assert r["accept_len"] == 1 and r["next_root"] == 0
+    assert np.isclose(r["accept_margin"], np.log(0.5 / 0.4), rtol=1e-14)
+    assert np.isclose(r["draw_margin"], 0.1, rtol=1e-12)
+    # rejected (u = 0.7: 0.56 > 0.5): residual (0.5-0.8)+, (0.5-0.2)+ = (0, 0.3)
+    # -> (0, 1); the draw with u = 0.2 takes token 1 at margin 0.2
+    r = OP.posterior_exact(topo, np.array([1, 0]), p_rows, q, np.array([0.0, 0.7]),
+                           np.array([0.2, 0.0]), with_margins=True)
+    assert r["accept_len"] == 0 and r["next_root"] == 1
+    assert np.isclose(r["accept_margin"], np.log(0.56 / 0.5), rtol=1e-14)
+    assert np.isclose(r["draw_margin"], 0.2, rtol=1e-12)
+    # margins do not change the decisions
+    r0 = OP.posterior_exact(topo, np.array([1, 0]), p_rows, q, np.array([0.0, 0.7]),
+                            np.array([0.2, 0.0]))
+    assert all(np.array_equal(r0[k], r[k]) for k in r0)
