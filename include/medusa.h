@@ -400,6 +400,23 @@ int medusa_step_timed(const medusa_shape* shape, const medusa_step_args* args, v
                       size_t workspace_bytes, void* stream, void* ev_w2_start, void* ev_w2_end);
 
 /*
+ * medusa_step for callers that cannot allocate device memory (code under
+ * graph capture, serving loops or harnesses that forbid hipMalloc): the same
+ * step with the same results, its workspace taken from a device array the
+ * library owns, MEDUSA_STATIC_WORKSPACE_BYTES bytes on every GPU it runs on,
+ * held until the process ends. The array of the calling thread's current
+ * device is used; its address is looked up once per device. The call
+ * allocates nothing; it clears the array's counter block with one small
+ * kernel on `stream` before the step. Every call on one GPU shares that
+ * GPU's array, so calls that overlap on one GPU (other streams, other
+ * threads) race: serialise them. A shape whose medusa_workspace_bytes()
+ * exceeds the array returns MEDUSA_ERR_WORKSPACE before anything runs;
+ * other errors as for medusa_step.
+ */
+#define MEDUSA_STATIC_WORKSPACE_BYTES (64u << 20)
+int medusa_step_static(const medusa_shape* shape, const medusa_step_args* args, void* stream);
+
+/*
  * Decoding loop ("Medusa 深读", generate loop; "Medusa: Faster LLM text
  * generation", decoding with heads and tree attention): n_steps composite
  * steps back to back on one stream, each step's accepted prefix becoming the

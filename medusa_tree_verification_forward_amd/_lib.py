@@ -98,6 +98,7 @@ _SIGS = {
     "medusa_commit": ([_SP, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P], _I),
     "medusa_step": ([_SP, ctypes.POINTER(StepArgs), _P, _SZ, _P], _I),
     "medusa_step_timed": ([_SP, ctypes.POINTER(StepArgs), _P, _SZ, _P, _P, _P], _I),
+    "medusa_step_static": ([_SP, ctypes.POINTER(StepArgs), _P], _I),
     "medusa_sparse_tree": ([_I, _I, _P, _I, _P, _P, _P, _P], _I),
     "medusa_generate": ([_SP, ctypes.POINTER(StepArgs), _I, _P, _P, _P, _SZ, _P], _I),
 }
@@ -291,3 +292,12 @@ def step_timed(shape, args: StepArgs, workspace, ev_w2_start, ev_w2_end, *, stre
     _check(_lib.medusa_step_timed(ctypes.byref(shape), ctypes.byref(args), _ptr(workspace),
                                   workspace.numel() * workspace.element_size(), _stream(stream),
                                   h(ev_w2_start), h(ev_w2_end)))
+
+
+STATIC_WORKSPACE_BYTES = 64 << 20   # MEDUSA_STATIC_WORKSPACE_BYTES
+
+
+def step_static(shape, args: StepArgs, *, stream=None):
+    """medusa_step_static: the composite step on the library's own per-GPU
+    workspace (no workspace argument, nothing allocated)."""
+    _check(_lib.medusa_step_static(ctypes.byref(shape), ctypes.byref(args), _stream(stream)))

@@ -9,6 +9,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -1095,3 +1096,72 @@ int medusa_generate(const medusa_shape* shape, const medusa_step_args* args, int
 
 }  // extern "C"
 
+
+// ---- step without a caller workspace -------------------------------------------
+// The workspace lives in a file-scope device array, one copy per GPU, whose
+// address each device reports once through hipGetSymbolAddress; host code
+// uses that address only (the array's own name is a host-side stand-in).
+namespace {
+
+__device__ __align__(256) unsigned char scratch[MEDUSA_STATIC_WORKSPACE_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch[kMaxDevices] = {};
+
+// Zeroes n 16-byte words (the counter block every call needs at zero).
+__global__ __launch_bounds__(256) void zero_words_kernel(uint4* p, int n) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i < n) p[i] = make_uint4(0u, 0u, 0u, 0u);
+}
+
+int scratch_for_current_device(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "step_static: hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(MEDUSA_ERR_UNSUPPORTED, "step_static: device %d >= %d", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_fail(e, "step_static: hipGetSymbolAddress(scratch)");
+    if (!p || (reinterpret_cast<uintptr_t>(p) & 255u) != 0)
+      return fail(MEDUSA_ERR_HIP, "step_static: scratch address %p is not 256-byte aligned", p);
+    g_scratch[dev] = p;
+  }
+  *out = g_scratch[dev];
+  return MEDUSA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int medusa_step_static(const medusa_shape* shape, const medusa_step_args* x, void* stream) {
+  int rc = check_shape(shape);
+  if (rc) return rc;
+  const size_t need = layout_for(shape).total;
+  if (need > (size_t)MEDUSA_STATIC_WORKSPACE_BYTES)
+    return fail(MEDUSA_ERR_WORKSPACE,
+                "step_static: this shape needs %zu workspace bytes, more than the %zu of the "
+                "library's static workspace (use medusa_step with a caller workspace)",
+                need, (size_t)MEDUSA_STATIC_WORKSPACE_BYTES);
+  void* ws = nullptr;
+  rc = scratch_for_current_device(&ws);
+  if (rc) return rc;
+  rc = step_impl(shape, x, ws, need, stream, true);
+  if (rc) return rc;
+  // the counters start at zero (the previous call left them so unless it
+  // was cut short); a fill kernel rather than a memset, so that the call
+  // can be captured in a graph
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const int words = (int)(kCounterBytes / 16);
+  hipLaunchKernelGGL(zero_words_kernel, dim3((words + 255) / 256), dim3(256), 0, st,
+                     static_cast<uint4*>(ws), words);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return hip_fail(e, "step_static: counter clear launch");
+  return step_impl(shape, x, ws, need, stream, false);
+}
+
+}  // extern "C"

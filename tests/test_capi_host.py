@@ -222,3 +222,16 @@ def test_step_timed_needs_both_events():
     rc = lib.medusa_step_timed(ctypes.byref(shape), ctypes.byref(a), FAKE,
                                M.workspace_bytes(shape), None, FAKE, None)
     assert rc == M._lib.ERR_ARG and "event" in M.last_error()
+
+
+def test_step_static_rejects_shapes_beyond_its_workspace():
+    # The 13B step (136-node tree, 4k prefix) needs more workspace than the
+    # library's static array holds: refused before any device call.
+    M = _lib()
+    from workloads import cartesian_ranks
+    ranks = cartesian_ranks((4, 3, 2, 2, 1))
+    shape = _shape(M, d=5120, H=40, Lmax=4160, N=136, P=48, s_max=4)
+    assert M.workspace_bytes(shape) > M.STATIC_WORKSPACE_BYTES
+    a = _step_args(M, ranks, exact=False)
+    rc = M._lib._lib.medusa_step_static(ctypes.byref(shape), ctypes.byref(a), None)
+    assert rc == M._lib.ERR_WORKSPACE and "static workspace" in M.last_error()
