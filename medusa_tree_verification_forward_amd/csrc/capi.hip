@@ -127,7 +127,7 @@ struct Layout {
   // verify
   size_t q = 0, o_elem = 0, y_elem = 0, lm_part = 0, gemm_part = 0;
   // posterior (exact)
-  size_t pw = 0;
+  size_t pw = 0, exact_dec = 0;
   size_t total = 0;
 };
 
@@ -174,6 +174,7 @@ Layout layout_for(const medusa_shape* s) {
     L.gemm_part = take(std::max(q_need, std::max(o_need, lm_need)) * 4);
   }
   L.pw = take(B * V * 4);
+  L.exact_dec = take(B * T * 2 * 4);
   L.total = off;
   return L;
 }
@@ -702,6 +703,7 @@ int posterior_impl(const medusa_shape* shape, int mode, float temperature, float
   a.u_accept = u_accept_or_null;
   a.u_resample = u_resample_or_null;
   a.pw = at<float>(workspace, L.pw);
+  a.exact_dec = at<int32_t>(workspace, L.exact_dec);
   a.accept_len = accept_len;
   a.best_path = best_path;
   a.last_node = last_node;

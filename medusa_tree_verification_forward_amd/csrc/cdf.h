@@ -119,32 +119,13 @@ __device__ __forceinline__ float cdf_chunk_sum_v4(const Wf& w, int c, int csz, i
   return s;
 }
 
-// Build the CDF of w(0 .. V-1) into sh. Every thread of the workgroup calls
-// it; ends with a barrier. kVec4: chunks of 16 or more tokens read through
-// Wf::w4 (16-byte loads) when V is a multiple of 4; the sums are the same.
-template <bool kVec4 = false, class Wf>
-__device__ void cdf_build(const Wf& w, int V, CdfLds& sh) {
-  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
-  const int csz = cdf_chunk_size(V);
-  const int nch = (V + csz - 1) / csz;
+// The rest of a build once sh.cs holds the chunk sums (written by every
+// thread before the call, which every thread makes): the last token with a
+// positive weight (the maximum of the threads' my_last), the groups'
+// running sums F and the group totals E. Ends with a barrier.
+__device__ inline void cdf_prefix(int my_last, int nch, int csz, CdfLds& sh) {
+  const int t = threadIdx.x, lane = t & 63;
   const int ng = (nch + 63) / 64;
-  if (t == 0) sh.last_nz = -1;
-  __syncthreads();
-  int my_last = -1;
-  // wave w sums the rows of 64 chunks w, w + 16, ...; lane l chunk 64 r + l
-  for (int c0 = 64 * wave; c0 < nch; c0 += 64 * (kCdfThreads / 64)) {
-    const int c = c0 + lane;
-    float s;
-    if constexpr (kVec4) {
-      s = csz >= 16 && (V & 3) == 0 ? cdf_chunk_sum_v4(w, c, csz, &my_last)
-          : csz == 8               ? cdf_chunk_sum<8>(w, c, csz, V, &my_last)
-                                   : cdf_chunk_sum<16>(w, c, csz, V, &my_last);
-    } else {
-      s = csz == 8 ? cdf_chunk_sum<8>(w, c, csz, V, &my_last)
-                   : cdf_chunk_sum<16>(w, c, csz, V, &my_last);
-    }
-    if (c < nch) sh.cs[c] = s;   // chunks past nch hold only tokens >= V
-  }
   {
     // token indices are exact in float (V < 2^24)
     const int wl = (int)wave_max((float)my_last);
@@ -177,13 +158,42 @@ __device__ void cdf_build(const Wf& w, int V, CdfLds& sh) {
   __syncthreads();
 }
 
-// One draw with uniform u from a built CDF (any single thread).
-template <class Wf>
-__device__ int cdf_draw(const Wf& w, int V, float u, const CdfLds& sh) {
-  const int ng = sh.ng, nch = sh.nch, csz = sh.csz;
-  const float target = u * sh.E[ng];
-  int x = -1;
-  // first group ending above the target
+// Build the CDF of w(0 .. V-1) into sh. Every thread of the workgroup calls
+// it; ends with a barrier. kVec4: chunks of 16 or more tokens read through
+// Wf::w4 (16-byte loads) when V is a multiple of 4; the sums are the same.
+template <bool kVec4 = false, class Wf>
+__device__ void cdf_build(const Wf& w, int V, CdfLds& sh) {
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int csz = cdf_chunk_size(V);
+  const int nch = (V + csz - 1) / csz;
+  if (t == 0) sh.last_nz = -1;
+  __syncthreads();
+  int my_last = -1;
+  // wave w sums the rows of 64 chunks w, w + 16, ...; lane l chunk 64 r + l
+  for (int c0 = 64 * wave; c0 < nch; c0 += 64 * (kCdfThreads / 64)) {
+    const int c = c0 + lane;
+    float s;
+    if constexpr (kVec4) {
+      s = csz >= 16 && (V & 3) == 0 ? cdf_chunk_sum_v4(w, c, csz, &my_last)
+          : csz == 8               ? cdf_chunk_sum<8>(w, c, csz, V, &my_last)
+                                   : cdf_chunk_sum<16>(w, c, csz, V, &my_last);
+    } else {
+      s = csz == 8 ? cdf_chunk_sum<8>(w, c, csz, V, &my_last)
+                   : cdf_chunk_sum<16>(w, c, csz, V, &my_last);
+    }
+    if (c < nch) sh.cs[c] = s;   // chunks past nch hold only tokens >= V
+  }
+  cdf_prefix(my_last, nch, csz, sh);
+}
+
+// The chunk in which a draw with uniform u lands: the first group, then the
+// first chunk of it, whose end lies above target = u * total; returns the
+// chunk (-1 when no group does, only for a target at the top) and the CDF
+// before its first token, E[g] + F[c], as eg and fc.
+__device__ inline int cdf_locate(float u, const CdfLds& sh, float& target, float& eg,
+                                 float& fc) {
+  const int ng = sh.ng, nch = sh.nch;
+  target = u * sh.E[ng];
   int lo = 0, hi = ng;
   while (lo < hi) {
     const int mid = (lo + hi) >> 1;
@@ -192,20 +202,30 @@ __device__ int cdf_draw(const Wf& w, int V, float u, const CdfLds& sh) {
     else
       lo = mid + 1;
   }
-  if (lo < ng) {
-    const int g = lo;
-    const float eg = sh.E[g];
-    // first chunk of the group ending above the target (its last chunk does)
-    int a = 64 * g, bnd = min(64 * g + 64, nch) - 1;
-    while (a < bnd) {
-      const int mid = (a + bnd) >> 1;
-      if (eg + (sh.F[mid] + sh.cs[mid]) > target)
-        bnd = mid;
-      else
-        a = mid + 1;
-    }
-    const int c = a;
-    const float fc = sh.F[c];
+  if (lo >= ng) return -1;
+  const int g = lo;
+  eg = sh.E[g];
+  // first chunk of the group ending above the target (its last chunk does)
+  int a = 64 * g, bnd = min(64 * g + 64, nch) - 1;
+  while (a < bnd) {
+    const int mid = (a + bnd) >> 1;
+    if (eg + (sh.F[mid] + sh.cs[mid]) > target)
+      bnd = mid;
+    else
+      a = mid + 1;
+  }
+  fc = sh.F[a];
+  return a;
+}
+
+// One draw with uniform u from a built CDF (any single thread).
+template <class Wf>
+__device__ int cdf_draw(const Wf& w, int V, float u, const CdfLds& sh) {
+  const int csz = sh.csz;
+  float target, eg, fc;
+  const int c = cdf_locate(u, sh, target, eg, fc);
+  int x = -1;
+  if (c >= 0) {
     float local = 0.f;
     for (int i0 = 0; i0 < csz && x < 0; i0 += 8) {
       float wv[8];

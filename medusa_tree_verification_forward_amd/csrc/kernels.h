@@ -168,7 +168,8 @@ struct PostArgs {
   const float* head_lse;       // [B][K] (exact)
   const float* u_accept;       // [B][T] (exact)
   const float* u_resample;     // [B][T] (exact)
-  float* pw;                   // [B][V] workspace (exact)
+  float* pw;                   // [B][V] workspace (exact, large vocabularies)
+  int32_t* exact_dec;          // [B][T][2] workspace (exact): first accepted child, draw
   int32_t* accept_len;
   int32_t* best_path;
   int32_t* last_node;

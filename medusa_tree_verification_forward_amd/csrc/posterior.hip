@@ -15,8 +15,12 @@
 // Greedy/typical: one workgroup per sequence, one thread per node; the
 // accepted-prefix flags are ANDed along each node's ancestor chain and the
 // (depth, -index) maximum is found with DPP wave reductions.
-// Exact: one 1024-thread workgroup per sequence walks the tree; each p/q
-// step is a block-wide pass over the vocabulary.
+// Exact: every node's p/q steps in a workgroup of its own (vocabularies up
+// to 32768, held in LDS), then a walk over the nodes' decisions; larger
+// vocabularies: one 1024-thread workgroup per sequence walks the tree, each
+// p/q step a block-wide pass over the vocabulary in global memory.
+#include <type_traits>
+
 #include "cdf.h"
 #include "common.h"
 #include "kernels.h"
@@ -299,113 +303,219 @@ __global__ __launch_bounds__(1024) void posterior_exact_kernel(PostArgs a) {
   a.best_path[b] = bp;
 }
 
-// Exact mode for V <= kExactLdsV: the target distribution lives in LDS as
-// unnormalised weights p[x] with one scale factor, p(x) = p[x] * scale, which
-// is the product posterior_exact_kernel stores, so every value and decision
-// is the same while the normalising passes disappear. Each pass over the
-// vocabulary reads its logits from clamped indices, all of a thread's loads
-// (32 for V = 32768) in flight before the first is used; the tree, tokens and
-// uniforms are staged in LDS.
+// Exact mode for V <= kExactLdsV, node-parallel. The walk's work at a node v
+// depends only on v's own verify row and its depth's drafting distribution:
+// p_v, the acceptance tests of v's children in order with the residual
+// update after each rejection, and -- when no child is accepted, or v has
+// none -- the draw from the final residual. So one workgroup per (node,
+// sequence) does exactly that for every node at once (exact_node_kernel,
+// writing (first accepted child or -1, draw) per node), and a small kernel
+// follows the accepted children from the root (exact_walk_kernel). Nodes the
+// walk never reaches cost only idle compute units.
+//
+// In a node's workgroup thread t holds the 32 consecutive tokens 32t ..
+// 32t + 31 in registers: the target as unnormalised weights p_i with one
+// scale factor (p(x) = p_i * scale) and the drafting distribution q_i =
+// e^(head logit - lse). Memory is read once, the verify row and the head
+// row; every later pass -- the residual's sum, its update (kept when the
+// residual is all zero), the CDF's chunk sums (chunks of 8 or 16 consecutive
+// tokens, inside one thread) -- runs on registers. An acceptance test reads
+// p(x) and q(x) from the thread that holds x, through LDS.
 constexpr int kExactLdsV = 32768;
+constexpr int kExactPer = kExactLdsV / 1024;   // tokens per thread
 
-__global__ __launch_bounds__(1024) void posterior_exact_lds_kernel(PostArgs a) {
-  const int b = blockIdx.x, t = threadIdx.x;
+// Row values of tokens 32t .. 32t + 31 (clamped indices, so every load is in
+// flight before the first is used; values past V are never used).
+__device__ __forceinline__ void load_row32(const float* __restrict__ row, int V,
+                                           float (&out)[kExactPer]) {
+  const int x0 = kExactPer * threadIdx.x;
+  if ((V & 3) == 0) {
+#pragma unroll
+    for (int j = 0; j < kExactPer / 4; ++j) {
+      const floatx4_t v =
+          *reinterpret_cast<const floatx4_t*>(row + max(min(x0 + 4 * j, V - 4), 0));
+#pragma unroll
+      for (int i = 0; i < 4; ++i) out[4 * j + i] = v[i];
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < kExactPer; ++i) out[i] = row[min(x0 + i, V - 1)];
+  }
+}
+
+// Register i of an array, for a runtime i the same in the whole wave
+// (selects, no indexed register access).
+__device__ __forceinline__ float pick32(const float (&r)[kExactPer], int i) {
+  float v = 0.f;
+#pragma unroll
+  for (int j = 0; j < kExactPer; ++j) v = j == i ? r[j] : v;
+  return v;
+}
+
+__global__ __launch_bounds__(1024) void exact_node_kernel(PostArgs a) {
+  const int v = blockIdx.x, b = blockIdx.y, t = threadIdx.x;
   const int T = a.T, V = a.V, K = a.K;
-  constexpr int kStride = 1024, kBatch = kExactLdsV / 1024;
-  __shared__ float p[kExactLdsV];
+  const int x0 = kExactPer * t;
   __shared__ float red[16];
   __shared__ CdfLds cdf;
   __shared__ int s_par[MAXT], s_tok[MAXT];
   __shared__ float s_ua[MAXT];
-  __shared__ int s_next, s_bp;
+  __shared__ float s_pq[2];
+  __shared__ int s_next;
+  float p[kExactPer], q[kExactPer];
+  load_row32(a.verify_logits + ((size_t)b * T + v) * V, V, p);
   if (t < T) {
     s_par[t] = a.parent[t];
     s_tok[t] = a.tokens[(size_t)b * T + t];
     s_ua[t] = a.u_accept[(size_t)b * T + t];
   }
-  if (t == 0) s_bp = 0x7fffffff;
+  if (t == 0) cdf.last_nz = -1;
   __syncthreads();
-  const auto par = [&](int x) { return min(max(s_par[x], 0), T - 1); };
-  // f(x, value of row[x]) for this thread's tokens x = t + 1024 i, in x order
-  const auto stream = [&](const float* row, auto&& f) {
-    for (int x0 = t; x0 < V; x0 += kStride * kBatch) {
-      float lv[kBatch];
+  int dv = 0;
+  for (int x = v; x != 0 && dv < K; x = min(max(s_par[x], 0), T - 1)) ++dv;
+  const bool kids = dv < K;
+  const float* hl = a.head_logits + ((size_t)b * K + min(dv, K - 1)) * V;
+  if (kids) load_row32(hl, V, q);   // in flight during the softmax below
+  // p = softmax(l_v / tau): unnormalised weights and their scale
+  float mx = kNegInf;
 #pragma unroll
-      for (int i = 0; i < kBatch; ++i) lv[i] = row[min(x0 + kStride * i, V - 1)];
+  for (int i = 0; i < kExactPer; ++i) {
+    p[i] = p[i] * a.inv_tau;
+    if (x0 + i < V) mx = fmaxf(mx, p[i]);
+  }
+  mx = block_max(mx, red);
+  float s = 0.f;
 #pragma unroll
-      for (int i = 0; i < kBatch; ++i)
-        if (x0 + kStride * i < V) f(x0 + kStride * i, lv[i]);
-    }
-  };
-  float scale = 1.f;
-  const auto load_p = [&](int v) {
-    float mx = kNegInf;
-    stream(a.verify_logits + ((size_t)b * T + v) * V, [&](int x, float l) {
-      const float z = l * a.inv_tau;
-      p[x] = z;
-      mx = fmaxf(mx, z);
-    });
-    mx = block_max(mx, red);
-    float s = 0.f;
-#pragma unroll 8
-    for (int x = t; x < V; x += kStride) {
-      const float e = exp_e(p[x] - mx);
-      p[x] = e;
-      s += e;
-    }
-    s = block_sum(s, red);   // ends with a barrier: p is complete
-    scale = 1.f / s;
-  };
+  for (int i = 0; i < kExactPer; ++i) {
+    p[i] = x0 + i < V ? exp_e(p[i] - mx) : 0.f;
+    s += p[i];
+  }
+  s = block_sum(s, red);
+  float scale = 1.f / s;
 
-  int v = 0;
-  int next = -1;
-  load_p(0);
-  while (true) {
-    int dv = 0;
-    for (int x = v; x != 0 && dv < K; x = par(x)) ++dv;
-    int taken = -1;
-    if (dv < K) {
-      const float* hl = a.head_logits + ((size_t)b * K + dv) * V;
-      const float lse = a.head_lse[(size_t)b * K + dv];
-      for (int c = v + 1; c < T; ++c) {
-        if (s_par[c] != v) continue;
-        const int x = min(max(s_tok[c], 0), V - 1);
-        // every thread takes the same decision from the same values
-        if (s_ua[c] * exp_e(hl[x] - lse) < p[x] * scale) {
-          taken = c;
-          break;
-        }
-        // residual p <- norm(max(0, p - q)); kept when all zero
-        float s = 0.f;
-        stream(hl, [&](int y, float l) { s += fmaxf(p[y] * scale - exp_e(l - lse), 0.f); });
-        s = block_sum(s, red);
-        if (s > 0.f) {
-          stream(hl, [&](int y, float l) { p[y] = fmaxf(p[y] * scale - exp_e(l - lse), 0.f); });
-          scale = 1.f / s;
-        }
-        __syncthreads();
+  int taken = -1;
+  if (kids) {
+    const float lse = a.head_lse[(size_t)b * K + dv];
+#pragma unroll
+    for (int i = 0; i < kExactPer; ++i) q[i] = x0 + i < V ? exp_e(q[i] - lse) : 0.f;
+    for (int c = v + 1; c < T; ++c) {
+      if (s_par[c] != v) continue;
+      const int x = min(max(s_tok[c], 0), V - 1);
+      if (t == x / kExactPer) {
+        s_pq[0] = pick32(p, x % kExactPer) * scale;
+        s_pq[1] = pick32(q, x % kExactPer);
+      }
+      __syncthreads();
+      // every thread takes the same decision from the same values
+      if (s_ua[c] * s_pq[1] < s_pq[0]) {
+        taken = c;
+        break;
+      }
+      // residual p <- norm(max(0, p - q)); kept when all zero
+      float rs = 0.f;
+#pragma unroll
+      for (int i = 0; i < kExactPer; ++i) rs += fmaxf(p[i] * scale - q[i], 0.f);
+      rs = block_sum(rs, red);   // also orders this child's s_pq reads before the next write
+      if (rs > 0.f) {
+#pragma unroll
+        for (int i = 0; i < kExactPer; ++i) p[i] = fmaxf(p[i] * scale - q[i], 0.f);
+        scale = 1.f / rs;
       }
     }
-    if (taken < 0) {
-      const ScaledRow w{p, scale, V};
-      cdf_build<true>(w, V, cdf);
-      if (t == 0) s_next = cdf_draw(w, V, a.u_resample[(size_t)b * T + v], cdf);
-      __syncthreads();
-      next = s_next;
-      break;
-    }
-    // Every wave has read p[x] for the decision above before any wave
-    // overwrites p with the accepted child's row.
-    __syncthreads();
-    v = taken;
-    load_p(v);
   }
+  if (taken < 0) {
+    // the CDF of p * scale: this thread's chunks, each summed in token order
+    const int csz = cdf_chunk_size(V);
+    const int nch = (V + csz - 1) / csz;
+    int my_last = -1;
+    float w[kExactPer];
+#pragma unroll
+    for (int i = 0; i < kExactPer; ++i) {
+      w[i] = p[i] * scale;
+      if (w[i] > 0.f) my_last = x0 + i;
+    }
+    // (csz is 8 or 16: both shapes unrolled, so every register index is fixed)
+    const auto chunk_sums = [&](auto csz_c) {
+      constexpr int CS = decltype(csz_c)::value;
+#pragma unroll
+      for (int c0 = 0; c0 < kExactPer; c0 += CS) {
+        float cs = 0.f;
+#pragma unroll
+        for (int i = 0; i < CS; ++i) cs += w[c0 + i];
+        const int c = (x0 + c0) / CS;
+        if (c < nch) cdf.cs[c] = cs;
+      }
+    };
+    if (csz == 8)
+      chunk_sums(std::integral_constant<int, 8>{});
+    else
+      chunk_sums(std::integral_constant<int, 16>{});
+    cdf_prefix(my_last, nch, csz, cdf);
+    float target, eg, fc;
+    const int c = cdf_locate(a.u_resample[(size_t)b * T + v], cdf, target, eg, fc);
+    if (t == 0) s_next = -1;
+    __syncthreads();
+    if (c >= 0 && t == c * csz / kExactPer) {
+      const int i0 = c * csz - x0;
+      float local = 0.f;
+      int x = -1;
+#pragma unroll
+      for (int i = 0; i < 16; ++i)
+        if (i < csz) {
+          local += pick32(w, i0 + i);
+          if (x < 0 && eg + (fc + local) > target) x = c * csz + i;
+        }
+      s_next = x;
+    }
+    __syncthreads();
+  }
+  if (t == 0) {
+    int next = -1;
+    if (taken < 0) {
+      next = s_next;
+      if (next < 0 || next > cdf.last_nz) next = cdf.last_nz < 0 ? V - 1 : cdf.last_nz;
+    }
+    *reinterpret_cast<int2*>(a.exact_dec + ((size_t)b * T + v) * 2) = make_int2(taken, next);
+  }
+}
+
+// The walk over the nodes' decisions, one wave per sequence: from the root
+// along the accepted children; the next root is the draw of the node where
+// it stops.
+__global__ __launch_bounds__(64) void exact_walk_kernel(PostArgs a) {
+  const int b = blockIdx.x, lane = threadIdx.x;
+  const int T = a.T, K = a.K;
+  __shared__ int s_par[MAXT], s_tok[MAXT], s_taken[MAXT], s_draw[MAXT];
+  __shared__ int s_v;
+  for (int x = lane; x < T; x += 64) {
+    const int2 dec = *reinterpret_cast<const int2*>(a.exact_dec + ((size_t)b * T + x) * 2);
+    s_par[x] = min(max(a.parent[x], 0), T - 1);
+    s_tok[x] = a.tokens[(size_t)b * T + x];
+    s_taken[x] = dec.x;
+    s_draw[x] = dec.y;
+  }
+  __syncthreads();
+  const auto par = [&](int x) { return s_par[x]; };
+  if (lane == 0) {
+    int v = 0;
+    // a taken child is a later node, so the walk ends within T steps
+    for (int i = 0; i < T; ++i) {
+      const int c = s_taken[v];
+      if (c <= v || c >= T) break;
+      v = c;
+    }
+    s_v = v;
+  }
+  __syncthreads();
+  const int v = s_v;
   int depth = 0;
   for (int x = v; x != 0 && depth < K; x = par(x)) ++depth;
   // best path: the lowest path index whose node at this depth is v
-  if (t < a.P && a.retrieve[(size_t)t * (K + 1) + depth] == v) atomicMin(&s_bp, t);
-  __syncthreads();
-  if (t != 0) return;
+  int bp = 0x7fffffff;
+  for (int q = lane; q < a.P; q += 64)
+    if (a.retrieve[(size_t)q * (K + 1) + depth] == v) bp = min(bp, q);
+  bp = -wave_max_i(-bp);
+  if (lane != 0) return;
   a.accept_len[b] = depth;
   a.last_node[b] = v;
   int* out = a.out_tokens + (size_t)b * (K + 1);
@@ -415,8 +525,8 @@ __global__ __launch_bounds__(1024) void posterior_exact_lds_kernel(PostArgs a) {
     out[j] = s_tok[x];
     x = par(x);
   }
-  a.next_root[b] = next;
-  a.best_path[b] = s_bp == 0x7fffffff ? 0 : s_bp;
+  a.next_root[b] = s_draw[v];
+  a.best_path[b] = bp == 0x7fffffff ? 0 : bp;
 }
 
 // The LDS kernel needs more LDS than older parts give one workgroup; it runs
@@ -427,7 +537,7 @@ bool exact_lds_fits() {
     hipFuncAttributes fa{};
     if (hipGetDevice(&dev) != hipSuccess ||
         hipDeviceGetAttribute(&lim, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess ||
-        hipFuncGetAttributes(&fa, reinterpret_cast<const void*>(posterior_exact_lds_kernel)) !=
+        hipFuncGetAttributes(&fa, reinterpret_cast<const void*>(exact_node_kernel)) !=
             hipSuccess)
       return false;
     return fa.sharedSizeBytes <= (size_t)lim;
@@ -546,8 +656,12 @@ __global__ __launch_bounds__(1024) void posterior_commit_kernel(PostArgs a, Comm
 }  // namespace
 
 hipError_t launch_posterior(const PostArgs& a, hipStream_t st) {
-  if (a.mode == 2 && a.V <= kExactLdsV && exact_lds_fits())
-    hipLaunchKernelGGL(posterior_exact_lds_kernel, dim3(a.B), dim3(1024), 0, st, a);
+  if (a.mode == 2 && a.V <= kExactLdsV && exact_lds_fits()) {
+    hipLaunchKernelGGL(exact_node_kernel, dim3(a.T, a.B), dim3(1024), 0, st, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(exact_walk_kernel, dim3(a.B), dim3(64), 0, st, a);
+  }
   else if (a.mode == 2)
     hipLaunchKernelGGL(posterior_exact_kernel, dim3(a.B), dim3(1024), 0, st, a);
   else
