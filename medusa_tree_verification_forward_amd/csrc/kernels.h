@@ -143,6 +143,7 @@ struct AttnArgs {
   const uint8_t* mask;         // [T][T]
   float scale;
   int NS;                      // prefix splits per (b, h) (kAttnChunk keys each)
+  int NP;                      // partials per (b, h) the merge reads (set by the launcher)
   float* part_o;               // [B][H][NS][Dh/16][T][16]
   float* part_ml;              // [B][H][NS][T][2]
   float* out;                  // [B][T][H][Dh] fp32 (or null)

@@ -43,7 +43,11 @@ static_assert(kPfxWaves * 32 == kAttnChunk, "one 32-key MFMA step per wave");
 // rows of all (at most QH) query tiles are held in LDS for the whole kernel,
 // loaded once; with QH == QG a query group's rows are reloaded for every
 // chunk when the tree has more than QG tiles.
-template <int DH, int QG, int QH>
+// ACC: the workgroup folds its chunks into one running partial (for trees of
+// several query groups, or workgroups that loop over more than two chunks);
+// otherwise every chunk leaves its own partial at its chunk index (one query
+// group only).
+template <int DH, int QG, int QH, bool ACC>
 __global__ __launch_bounds__(64 * kPfxWaves) void prefix_attn_bf16_kernel(AttnArgs a) {
   using S = uint16_t;
   static_assert(64 * kPfxWaves == 512, "Q staging assumes 512 threads");
@@ -121,6 +125,25 @@ __global__ __launch_bounds__(64 * kPfxWaves) void prefix_attn_bf16_kernel(AttnAr
   } else {
     load_q(0, qv);
   }
+  // Running (max, sum, output) of every query over this workgroup's chunks
+  // (online softmax: a chunk's own exact softmax is folded in with the
+  // rescaling 2^(M_old - M_new)); one partial per workgroup at the end.
+  // Output tiles of group gi live in orun[gi] (the group loop is unrolled).
+  constexpr int NGR = !ACC ? 1 : kHold ? (QH + QG - 1) / QG : (QG < 4 ? 1 : (MAXT / 16) / QG);
+  constexpr int NRQ = 16 * QG * NGR;   // query rows with running statistics
+  __shared__ float run_m[NRQ], run_l[NRQ];
+  floatx4_t orun[NGR][ITEMS];
+#pragma unroll
+  for (int gi = 0; gi < NGR; ++gi)
+#pragma unroll
+    for (int it = 0; it < ITEMS; ++it) orun[gi][it] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+  if (ACC)
+    for (int i = threadIdx.x; i < NRQ; i += 64 * kPfxWaves) {
+      run_m[i] = kNegInf;
+      run_l[i] = 0.f;
+    }
+  // (published by the first barrier below)
+
   u32x4_t kf[2][DS], vv[VL];
   load_kv(s, kf, vv);
   for (bool first = true;; first = false) {
@@ -135,8 +158,10 @@ __global__ __launch_bounds__(64 * kPfxWaves) void prefix_attn_bf16_kernel(AttnAr
     u32x4_t kn[2][DS], vn[VL];
     if (more) load_kv(sn, kn, vn);   // next chunk in flight during this one
 
-    const size_t base = ((size_t)b * H + h) * a.NS * T + (size_t)s * T;   // partial row of query 0
-    for (int g0 = 0; g0 < MQ; g0 += QG) {
+#pragma unroll
+    for (int gi = 0; gi < NGR; ++gi) {
+      const int g0 = gi * QG;
+      if (g0 >= MQ) continue;   // uniform over the workgroup
       if (kHold) {
         if (first && g0 == 0) __syncthreads();   // the held Q rows are published
       } else if (first || !one_group) {
@@ -212,6 +237,21 @@ __global__ __launch_bounds__(64 * kPfxWaves) void prefix_attn_bf16_kernel(AttnAr
         *reinterpret_cast<u32x4_t*>(&ps[16 * u + li][32 * wave + 8 * lq]) = pw;
       }
       __syncthreads();   // P and the row sums are published
+      // chunk statistics of query row 16 g0 + rl of the group, and the
+      // rescaling factors of the running and the chunk's values
+      const auto fold = [&](int rl, float& Mn, float& ca, float& cb, float& lc) {
+        float Mc = kNegInf;
+        lc = 0.f;
+#pragma unroll
+        for (int w = 0; w < kPfxWaves; ++w) {
+          Mc = fmaxf(Mc, red_m[w][rl]);
+          lc += red_l[w][rl];
+        }
+        const float Mr = run_m[16 * g0 + rl];
+        Mn = fmaxf(Mr, Mc);
+        ca = Mr == kNegInf ? 0.f : __builtin_amdgcn_exp2f(Mr - Mn);
+        cb = Mc == kNegInf ? 0.f : __builtin_amdgcn_exp2f(Mc - Mn);
+      };
       // ---- O^T += V^T P^T: item = wave + 8 it is (query tile item / DT, dh tile item % DT) ----
 #pragma unroll
       for (int it = 0; it < ITEMS; ++it) {
@@ -234,22 +274,51 @@ __global__ __launch_bounds__(64 * kPfxWaves) void prefix_attn_bf16_kernel(AttnAr
           o = mfma16x16x32_bf16(vf, pf, o);
         }
         // lane holds O^T[dh 16 dt + 4 lq + j][query 16 (g0 + u) + li]
-        const int query = 16 * (g0 + u) + li;
-        if (query < T)
-          *reinterpret_cast<float4*>(a.part_o + base * DH + ((size_t)dt * T + query) * 16 +
-                                     4 * lq) = make_float4(o[0], o[1], o[2], o[3]);
-      }
-      if (wave == 0 && lane < 16 * QG) {
-        const int query = 16 * g0 + lane;
-        if (query < T) {
-          float M = kNegInf, l = 0.f;
+        if constexpr (ACC) {
+          float Mn, ca, cb, lc;
+          fold(16 * u + li, Mn, ca, cb, lc);
 #pragma unroll
-          for (int w = 0; w < kPfxWaves; ++w) M = fmaxf(M, red_m[w][lane]);
-#pragma unroll
-          for (int w = 0; w < kPfxWaves; ++w) l += red_l[w][lane];
-          a.part_ml[(base + query) * 2 + 0] = M;
-          a.part_ml[(base + query) * 2 + 1] = l;
+          for (int j = 0; j < 4; ++j) orun[gi][it][j] = orun[gi][it][j] * ca + o[j] * cb;
+        } else {
+          const int query = 16 * (g0 + u) + li;
+          const size_t base = ((size_t)b * H + h) * a.NS * T + (size_t)s * T;
+          if (query < T)
+            *reinterpret_cast<float4*>(a.part_o + base * DH + ((size_t)dt * T + query) * 16 +
+                                       4 * lq) = make_float4(o[0], o[1], o[2], o[3]);
         }
+      }
+      if constexpr (!ACC) {
+        // this chunk's statistics (one group: the next writes of red_m and
+        // red_l come after the barrier that ends the chunk)
+        if (wave == 0 && lane < 16 * QG) {
+          const int query = 16 * g0 + lane;
+          if (query < T) {
+            float M = kNegInf, l = 0.f;
+#pragma unroll
+            for (int w = 0; w < kPfxWaves; ++w) M = fmaxf(M, red_m[w][lane]);
+#pragma unroll
+            for (int w = 0; w < kPfxWaves; ++w) l += red_l[w][lane];
+            const size_t base = ((size_t)b * H + h) * a.NS * T + (size_t)s * T;
+            a.part_ml[(base + query) * 2 + 0] = M;
+            a.part_ml[(base + query) * 2 + 1] = l;
+          }
+        }
+        continue;
+      }
+      // the group's running statistics: every read above happens before the
+      // barrier, wave 0 writes after it (so the next group's writes of red_m
+      // and these reads do not overlap)
+      float nm = kNegInf, nl = 0.f;
+      if (wave == 0 && lane < 16 * QG) {
+        float Mn, ca, cb, lc;
+        fold(lane, Mn, ca, cb, lc);
+        nm = Mn;
+        nl = run_l[16 * g0 + lane] * ca + lc * cb;
+      }
+      __syncthreads();
+      if (wave == 0 && lane < 16 * QG) {
+        run_m[16 * g0 + lane] = nm;
+        run_l[16 * g0 + lane] = nl;
       }
     }
     if (!more) break;
@@ -261,6 +330,28 @@ __global__ __launch_bounds__(64 * kPfxWaves) void prefix_attn_bf16_kernel(AttnAr
 #pragma unroll
     for (int i = 0; i < VL; ++i) vv[i] = vn[i];
     __syncthreads();   // every wave is done with this chunk's V, P and row statistics
+  }
+  if constexpr (!ACC) return;
+  // this workgroup's partial: slot blockIdx.x of (b, h)
+  __syncthreads();   // the last running statistics are published
+  const size_t base = ((size_t)b * H + h) * a.NS * T + (size_t)blockIdx.x * T;
+#pragma unroll
+  for (int gi = 0; gi < NGR; ++gi) {
+    const int g0 = gi * QG;
+    if (g0 >= MQ) continue;
+#pragma unroll
+    for (int it = 0; it < ITEMS; ++it) {
+      const int item = wave + kPfxWaves * it;
+      const int u = item / DT, dt = item - u * DT;
+      const int query = 16 * (g0 + u) + li;
+      if (item >= QG * DT || g0 + u >= MQ || query >= T) continue;
+      *reinterpret_cast<float4*>(a.part_o + base * DH + ((size_t)dt * T + query) * 16 + 4 * lq) =
+          make_float4(orun[gi][it][0], orun[gi][it][1], orun[gi][it][2], orun[gi][it][3]);
+    }
+  }
+  for (int query = threadIdx.x; query < min(T, NRQ); query += 64 * kPfxWaves) {
+    a.part_ml[(base + query) * 2 + 0] = run_m[query];
+    a.part_ml[(base + query) * 2 + 1] = run_l[query];
   }
 }
 
@@ -435,7 +526,8 @@ __global__ __launch_bounds__(64) void attn_merge_kernel(AttnArgs a) {
   const int i = blockIdx.x, h = blockIdx.y, b = blockIdx.z, lane = threadIdx.x;
   const int T = a.T, H = a.H;
   const int L = min(max(a.kv_len[b], 0), a.Lmax);
-  const int ns = (L + kAttnChunk - 1) / kAttnChunk;
+  // partials: one per prefix workgroup that had a chunk
+  const int ns = min(a.NP, (L + kAttnChunk - 1) / kAttnChunk);
   const float sl2 = a.scale * kLog2e;
   const size_t hs = ((size_t)b * H + h) * a.NS;   // split 0 of (b, h)
   // dh E lane + e of query i inside a split's [DT][T][16] block
@@ -561,7 +653,7 @@ bool attn_hold_q_for() {
     if (hipGetDevice(&dev) != hipSuccess ||
         hipDeviceGetAttribute(&lim, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess ||
         hipFuncGetAttributes(&fa, reinterpret_cast<const void*>(
-                                      prefix_attn_bf16_kernel<DH, 4, kHeldTiles>)) != hipSuccess)
+                                      prefix_attn_bf16_kernel<DH, 4, kHeldTiles, true>)) != hipSuccess)
       return false;
     return fa.sharedSizeBytes <= (size_t)lim;
   }();
@@ -590,20 +682,35 @@ hipError_t launch_bf16(const AttnArgs& a, hipStream_t st) {
   int G = over * cus / (a.B * a.H);
   G = G < 1 ? 1 : (G > a.NS ? a.NS : G);
   dim3 grid(G, a.H, a.B), block(64 * kPfxWaves);
+  AttnArgs m = a;
+  // A workgroup that loops over more than two chunks, or a tree of more
+  // than one query group, folds its chunks into one partial; otherwise each
+  // chunk leaves its own.
+  const bool acc = MQ > 4 || a.NS > 2 * G;
+  m.NP = acc ? G : a.NS;
   // 5 to 9 query tiles: all Q rows held in LDS (151 KB with the V and P
   // buffers for 128-wide heads), so no query group is reloaded per chunk
   if (MQ > 4 && MQ <= kHeldTiles && attn_hold_q())
-    hipLaunchKernelGGL((prefix_attn_bf16_kernel<DH, 4, kHeldTiles>), grid, block, 0, st, a);
+    hipLaunchKernelGGL((prefix_attn_bf16_kernel<DH, 4, kHeldTiles, true>), grid, block, 0, st, a);
+  else if (MQ > 4)
+    hipLaunchKernelGGL((prefix_attn_bf16_kernel<DH, 4, 4, true>), grid, block, 0, st, a);
+  else if (acc)
+    switch (MQ) {
+      case 1: hipLaunchKernelGGL((prefix_attn_bf16_kernel<DH, 1, 1, true>), grid, block, 0, st, a); break;
+      case 2: hipLaunchKernelGGL((prefix_attn_bf16_kernel<DH, 2, 2, true>), grid, block, 0, st, a); break;
+      case 3: hipLaunchKernelGGL((prefix_attn_bf16_kernel<DH, 3, 3, true>), grid, block, 0, st, a); break;
+      default: hipLaunchKernelGGL((prefix_attn_bf16_kernel<DH, 4, 4, true>), grid, block, 0, st, a); break;
+    }
   else
-    switch (MQ < 4 ? MQ : 4) {
-      case 1: hipLaunchKernelGGL((prefix_attn_bf16_kernel<DH, 1, 1>), grid, block, 0, st, a); break;
-      case 2: hipLaunchKernelGGL((prefix_attn_bf16_kernel<DH, 2, 2>), grid, block, 0, st, a); break;
-      case 3: hipLaunchKernelGGL((prefix_attn_bf16_kernel<DH, 3, 3>), grid, block, 0, st, a); break;
-      default: hipLaunchKernelGGL((prefix_attn_bf16_kernel<DH, 4, 4>), grid, block, 0, st, a); break;
+    switch (MQ) {
+      case 1: hipLaunchKernelGGL((prefix_attn_bf16_kernel<DH, 1, 1, false>), grid, block, 0, st, a); break;
+      case 2: hipLaunchKernelGGL((prefix_attn_bf16_kernel<DH, 2, 2, false>), grid, block, 0, st, a); break;
+      case 3: hipLaunchKernelGGL((prefix_attn_bf16_kernel<DH, 3, 3, false>), grid, block, 0, st, a); break;
+      default: hipLaunchKernelGGL((prefix_attn_bf16_kernel<DH, 4, 4, false>), grid, block, 0, st, a); break;
     }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((attn_merge_kernel<BF16, DH>), dim3(a.T, a.H, a.B), dim3(64), 0, st, a);
+  hipLaunchKernelGGL((attn_merge_kernel<BF16, DH>), dim3(a.T, a.H, a.B), dim3(64), 0, st, m);
   return hipGetLastError();
 }
 
@@ -622,7 +729,9 @@ hipError_t launch_f32(const AttnArgs& a, hipStream_t st) {
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((attn_merge_kernel<F32, DH>), dim3(a.T, a.H, a.B), dim3(64), 0, st, a);
+  AttnArgs m = a;
+  m.NP = a.NS;   // one partial per chunk
+  hipLaunchKernelGGL((attn_merge_kernel<F32, DH>), dim3(a.T, a.H, a.B), dim3(64), 0, st, m);
   return hipGetLastError();
 }
 
