@@ -15,12 +15,14 @@ own stream inside the timed region) and the CPU oracle timed on a bounded
 sample of the same workload.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
-                    [--workload NAME]
+                    [--workload NAME] [--headline-only]
 
---workload times another bf16 workload with the same line (13B shapes with a
-136-node tree and a 4k prefix; eight 7B sequences with ragged prefixes and
-greedy acceptance; 7B shapes with exact p/q acceptance); the CPU baseline is
-taken on the 7B workload only.
+By default the line also carries other_workloads: the same whole-step
+timing (K/4 steps, at least 20) of the 13B shapes with a 136-node tree and a
+4k prefix, of eight 7B sequences with ragged prefixes and greedy acceptance,
+and of the 7B shapes with exact p/q acceptance, each with its HBM and
+combined (HBM + MFMA) roofline fraction. --workload times one of them alone
+with the full line; the CPU baseline is taken on the 7B workload only.
 
 With --decode it prints a different line instead: the decoding loop
 (medusa_generate) on planted agreement — accepted tokens per step A for a
@@ -276,6 +278,94 @@ def decode_report(steps):
                 "the heads against one layer, not against a whole base model"}))
 
 
+def time_step(w, steps, warmup, reset_kv_len=False, graph=False, copy_bytes=0):
+    """Time `steps` whole steps of workload w (inputs resident in HBM), then
+    the dominant kernel in a second pass of the same steps. Returns a dict
+    with the step object and the timings."""
+    import torch
+    from medusa_tree_verification_forward_amd.step import VerifyStep
+    from workloads import make_inputs
+
+    inp = make_inputs(w)
+    st = VerifyStep(inp, H=w.H, Dh=w.Dh, s_max=w.s_max, mode=w.mode, tau=w.tau, eps=w.eps,
+                    delta=w.delta, theta=w.rope_theta)
+    stream = torch.cuda.current_stream()
+
+    def step():
+        # stream=None: the calls go to torch's current stream (the capture
+        # stream while a graph is being recorded). By default the commit
+        # writes the advanced prefix lengths to a buffer of their own, so
+        # every step runs over the same prefix; reset_kv_len instead
+        # advances kv_len in place and restores it before each step.
+        if reset_kv_len:
+            st.reset_kv_len()
+            st.run_step()
+        else:
+            st.run_step(keep_kv_len=True)
+
+    # W untimed warm-up steps, continued until the GPU has been busy for at
+    # least MIN_WARM_S: a 5-step warm-up left the first timed steps ~2-4%
+    # slower than steady state (clocks and caches still settling), which a
+    # serving loop never sees. The timed region below is unaffected.
+    n, t0 = 0, time.perf_counter()
+    while n < warmup or time.perf_counter() - t0 < MIN_WARM_S:
+        step()
+        n += 1
+        if n % 8 == 0:
+            torch.cuda.synchronize()   # the wall clock follows the GPU
+    torch.cuda.synchronize()
+    g = None
+    if graph:
+        # one step (prefix-length reset + medusa_step) recorded once and replayed
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            step()
+        for _ in range(3):
+            g.replay()
+        torch.cuda.synchronize()
+    run_one = g.replay if g is not None else step
+    if copy_bytes > 0:
+        src = torch.empty(copy_bytes // 4, dtype=torch.float32, device="cuda").fill_(1.0)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    # whole steps, bracketed by synchronisation
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_stop = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record(stream)
+    for _ in range(steps):
+        run_one()
+    t_stop.record(stream)
+    torch.cuda.synchronize()
+    ms_step = t_start.elapsed_time(t_stop) / steps
+
+    # dominant kernel: the same steps again, with HIP events recorded on the
+    # kernel's stream right around the vocabulary projection of every step
+    # (kept out of the whole-step loop: each event record costs a few us)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(steps)]
+    for a, b in evs:       # create the underlying events before handing them over
+        a.record(stream)
+        b.record(stream)
+    torch.cuda.synchronize()
+    for i in range(steps):
+        if reset_kv_len:
+            st.reset_kv_len()
+        st.run_step(keep_kv_len=not reset_kv_len, w2_events=evs[i])
+    torch.cuda.synchronize()
+    w2_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+    return dict(inp=inp, st=st, T=st.T, L_total=int(np.sum(inp["kv_len"])), ms_step=ms_step,
+                w2_ms=w2_ms, graph=g is not None)
+
+
+OTHER_WORKLOADS = ["vicuna13b_typical", "vicuna7b_batch8_ragged", "vicuna7b_exact"]
+MIN_WARM_S = 0.3   # untimed steps before the timed ones, at least this long (and W of them)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -293,10 +383,12 @@ def main():
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="before the timed loop, run a plain device-to-device copy of this "
                          "many bytes 3 times (a known-size kernel for scaling HBM counters)")
-    ap.add_argument("--workload", default=WORKLOAD,
-                    choices=["vicuna7b_typical", "vicuna13b_typical", "vicuna7b_batch8_ragged",
-                             "vicuna7b_exact"],
-                    help="workload to time (default: the 7B typical-acceptance step)")
+    ap.add_argument("--workload", default=None,
+                    choices=["vicuna7b_typical"] + OTHER_WORKLOADS,
+                    help="time this workload alone (default: the 7B typical-acceptance step, "
+                         "followed by the other workloads under other_workloads)")
+    ap.add_argument("--headline-only", action="store_true",
+                    help="time the 7B step alone (no other_workloads)")
     ap.add_argument("--decode", action="store_true",
                     help="print the decoding-loop report (A, A/r) instead of the step line")
     args = ap.parse_args()
@@ -312,84 +404,16 @@ def main():
         sys.exit(2)
 
     import torch
-    import medusa_tree_verification_forward_amd as M
-    from medusa_tree_verification_forward_amd.step import VerifyStep
-    from workloads import WORKLOADS, make_inputs
+    from workloads import WORKLOADS
 
-    w = WORKLOADS[args.workload]
-    inp = make_inputs(w)
-    st = VerifyStep(inp, H=w.H, Dh=w.Dh, s_max=w.s_max, mode=w.mode, tau=w.tau, eps=w.eps,
-                    delta=w.delta, theta=w.rope_theta)
-    stream = torch.cuda.current_stream()
-    T = st.T
-    L_total = int(np.sum(inp["kv_len"]))
-
-    def step():
-        # stream=None: the calls go to torch's current stream (the capture
-        # stream while a graph is being recorded). By default the commit
-        # writes the advanced prefix lengths to a buffer of their own, so
-        # every step runs over the same prefix; --reset-kv-len instead
-        # advances kv_len in place and restores it before each step.
-        if args.reset_kv_len:
-            st.reset_kv_len()
-            st.run_step()
-        else:
-            st.run_step(keep_kv_len=True)
-
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    graph = None
-    if args.graph:
-        # one step (prefix-length reset + medusa_step) recorded once and
-        # replayed
-        graph = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(graph):
-            step()
-        for _ in range(3):
-            graph.replay()
-        torch.cuda.synchronize()
-    run_one = graph.replay if graph is not None else step
-    if args.copy_bytes > 0:
-        src = torch.empty(args.copy_bytes // 4, dtype=torch.float32, device="cuda").fill_(1.0)
-        dst = torch.empty_like(src)
-        for _ in range(3):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        del src, dst
-
-    # headline: K whole steps, bracketed by synchronisation
-    t_start = torch.cuda.Event(enable_timing=True)
-    t_stop = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t_start.record(stream)
-    for _ in range(args.steps):
-        run_one()
-    t_stop.record(stream)
-    torch.cuda.synchronize()
-    ms_total = t_start.elapsed_time(t_stop)
-    ms_step = ms_total / args.steps
-
-    # dominant kernel: the same K steps again, with HIP events recorded on the
-    # kernel's stream right around the vocabulary projection of every step
-    # (kept out of the headline loop: each event record costs a few us)
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(args.steps)]
-    for a, b in evs:       # create the underlying events before handing them over
-        a.record(stream)
-        b.record(stream)
-    torch.cuda.synchronize()
-    for i in range(args.steps):
-        if args.reset_kv_len:
-            st.reset_kv_len()
-        st.run_step(keep_kv_len=not args.reset_kv_len, w2_events=evs[i])
-    torch.cuda.synchronize()
-    w2_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
-
+    name = args.workload or WORKLOAD
+    w = WORKLOADS[name]
+    r = time_step(w, args.steps, args.warmup, args.reset_kv_len, args.graph, args.copy_bytes)
+    ms_step, T, L_total = r["ms_step"], r["T"], r["L_total"]
     alg = algorithmic_bytes(w, T, L_total)
     w2b = w2_kernel_bytes(w)
-    achieved = w2b / (w2_ms * 1e-3) / 1e9
-    res = st.results()
+    achieved = w2b / (r["w2_ms"] * 1e-3) / 1e9
+    res = r["st"].results()
     comb_us = combined_roofline_us(w, T, L_total)
     accept = {"typical": f"typical eps={w.eps} delta={w.delta} tau={w.tau}",
               "greedy": "greedy", "exact": f"exact p/q rejection, tau={w.tau}"}[w.mode]
@@ -408,10 +432,12 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": f"synthetic (seeded Gaussian weights and KV, {w.name} shapes)",
-        "timing": (("replays of one recorded graph" if graph is not None else "eager launches")
+        "timing": (("replays of one recorded graph" if r["graph"] else "eager launches")
                    + (" (prefix-length reset + medusa_step)" if args.reset_kv_len else
                       " (medusa_step; advanced prefix lengths written to a separate buffer, "
-                      "so every step runs over the same prefix)")),
+                      "so every step runs over the same prefix)")
+                   + f"; untimed warm-up: the W steps, continued to at least {MIN_WARM_S} s "
+                     "of GPU work"),
         "config": {"workload": w.name, "batch": w.B, "d": w.d, "V": w.V, "heads": w.K,
                    "tree": f"top-{w.s}".replace(" ", ""), "tree_nodes": T - 1,
                    "prefix_kv": L_total, "attn": f"{w.H}x{w.Dh}", "accept": accept},
@@ -424,13 +450,38 @@ def main():
                      "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS,
                      "traffic": recorded_traffic() if w.name == WORKLOAD else None,
-                     "avg_us": w2_ms * 1e3, "bytes_per_launch": w2b,
+                     "avg_us": r["w2_ms"] * 1e3, "bytes_per_launch": w2b,
                      "timing": "HIP events recorded on the launch stream around every W2 "
                                "launch, over a second pass of the K timed steps"},
         "accept_len": [int(x) for x in res["accept_len"]],
     }
+    cpu = None
     if not args.no_cpu_baseline and w.name == WORKLOAD:
-        line["cpu_baseline"] = cpu_baseline(w, inp)
+        cpu = cpu_baseline(w, r["inp"])
+    del r, res
+    torch.cuda.empty_cache()
+    if args.workload is None and not args.headline_only:
+        # the other workloads, same step and timing (fewer steps), no CPU baseline
+        others = []
+        for oname in OTHER_WORKLOADS:
+            ow = WORKLOADS[oname]
+            n = max(20, args.steps // 4)
+            o = time_step(ow, n, max(5, args.warmup // 4))
+            oalg = algorithmic_bytes(ow, o["T"], o["L_total"])
+            ocomb = combined_roofline_us(ow, o["T"], o["L_total"])
+            others.append({
+                "workload": oname, "value": 1000.0 / o["ms_step"], "unit": "steps/s",
+                "ms_per_step": o["ms_step"], "steps": n, "batch": ow.B, "tree_nodes": o["T"] - 1,
+                "prefix_kv": o["L_total"], "accept": ow.mode,
+                "algorithmic_bytes": oalg,
+                "hbm_frac": oalg / (o["ms_step"] * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                "combined_floor_us": ocomb, "combined_frac": ocomb / (o["ms_step"] * 1e3),
+                "w2_avg_us": o["w2_ms"] * 1e3})
+            del o
+            torch.cuda.empty_cache()
+        line["other_workloads"] = others
+    if cpu is not None:
+        line["cpu_baseline"] = cpu
     print(json.dumps(line), flush=True)
 
 

@@ -54,34 +54,18 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
     if ((p) && !aligned16(p)) return fail(MEDUSA_ERR_ARG, "%s: not 16-byte aligned", #p); \
   } while (0)
 
-int env_int(const char* name, int dflt, int lo, int hi) {
-  const char* s = getenv(name);
-  if (!s || !*s) return dflt;
-  int v = atoi(s);
-  return std::min(hi, std::max(lo, v));
-}
-
-// Tuning knobs (rows per wave of the head streams; a workgroup has 4 waves).
-// Workspace sizes are computed for the smallest allowed value, so any
-// setting fits.
-constexpr int kMinW2Rows = 16;   // rows per workgroup at the smallest setting
-// Rows per wave of the W1 stream: MEDUSA_W1_ROWS, else 0 (the launcher takes
-// the fewest that let all K d rows run as one wave of four resident
-// workgroups per compute unit).
-int w1_rows() {
-  static const int v = env_int("MEDUSA_W1_ROWS", 0, 0, 64);
-  return v;
-}
-// W2 grid: rows per wave (MEDUSA_W2_ROWS, default 56) and the workgroups per
-// head that cover the V rows with them. 56 was measured fastest for the 7B heads
-// (715 workgroups; 40, 48, 54, 58, 60 and 64 rows, and grids filling exactly
-// 3 or 4 workgroups per compute unit, were 0.6-15 us slower).
+// Rows per wave of the head streams (a workgroup has 4 waves). W1: the
+// fewest that let all K d rows run as one wave of resident workgroups (0:
+// the launcher computes it). W2: 56 rows a wave and the workgroups per head
+// that cover the V rows with them -- measured fastest for the 7B heads (715
+// workgroups; 40, 48, 54, 58, 60 and 64 rows, and grids filling exactly 3 or
+// 4 workgroups per compute unit, were 0.6-15 us slower).
+constexpr int kW1Rows = 0;
+constexpr int kW2Rows = 56;
 void w2_grid(int V, int& G, int& rpw) {
-  static const int rows = env_int("MEDUSA_W2_ROWS", 56, kMinW2Rows / 4, 64);
-  rpw = rows;
+  rpw = kW2Rows;
   G = (V + 4 * rpw - 1) / (4 * rpw);
 }
-int head_interleave() { static int v = env_int("MEDUSA_HEAD_INTERLEAVE", 1, 0, 1); return v; }
 
 
 constexpr size_t kCounterBytes = 64 * 1024;   // workspace bytes reserved at offset 0 for counters
@@ -141,7 +125,7 @@ Layout layout_for(const medusa_shape* s) {
   };
   L.counters = take(kCounterBytes);
   const size_t B = s->B, K = s->K, d = s->d, S = s->s_max;
-  const int Gmax = (s->V + kMinW2Rows - 1) / kMinW2Rows;
+  const int Gmax = heads_row_blocks_max(s->V, kW2Rows);
   {
     int rpw;
     w2_grid(s->V, L.G, rpw);
@@ -164,14 +148,11 @@ Layout layout_for(const medusa_shape* s) {
   L.lm_part = take(B * T * (size_t)lm_record_slots(s->V) * 4 * 4);
   {
     const bool f32 = s->dtype == MEDUSA_F32;
-    // QKV / O-proj partials [groups][KS][M][cols] (groups * cols < N + 128),
-    // or the LM head's slices [groups][KS][48][cols] when its K is split
+    // QKV / O-proj partials [groups][KS][M][cols] (groups * cols < N + 128)
     const int M = (int)(B * T);
     const size_t q_need = (size_t)gemm_splits(EPI_QKV, 3 * s->d, s->d, f32, M) * B * T * (3 * d + 128);
     const size_t o_need = (size_t)gemm_splits(EPI_OPROJ, s->d, s->d, f32, M) * B * T * (d + 128);
-    const int lm_ks = lm_splits_for((int)(B * T));
-    const size_t lm_need = lm_ks > 1 ? (size_t)lm_ks * 48 * (s->V + 128) : 0;
-    L.gemm_part = take(std::max(q_need, std::max(o_need, lm_need)) * 4);
+    L.gemm_part = take(std::max(q_need, o_need) * 4);
   }
   L.pw = take(B * V * 4);
   L.exact_dec = take(B * T * 2 * 4);
@@ -314,12 +295,11 @@ int heads_impl(const medusa_shape* shape, const float* h, const void* W1,
   a.part_s = at<float>(workspace, L.part_s);
   a.afrag = at<char>(workspace, L.afrag);
   a.G = L.G;
-  a.w1_rows_per_wave = w1_rows();
+  a.w1_rows_per_wave = kW1Rows;
   {
     int G;
     w2_grid(shape->V, G, a.w2_rows_per_wave);
   }
-  a.interleave = head_interleave();
   a.ev_before = ev_w2_start;
   a.ev_after = ev_w2_end;
   if (fuse_plan) {
@@ -609,7 +589,6 @@ int verify_impl(const medusa_shape* shape, const void* E, const void* W_qkv, con
   gl.parent = parent;
   gl.inv_tau = 1.0f / temperature;
   gl.part = at<float>(workspace, L.lm_part);
-  gl.lm_slices = at<float>(workspace, L.gemm_part);
   gl.child_logit = child_logit;
   gl.logits_out = verify_logits_or_null;
   e = launch_lm_head(gl, row_stats, row_argmax, st);

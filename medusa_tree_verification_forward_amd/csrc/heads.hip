@@ -11,6 +11,7 @@
 // (lanes 0..s-1, best first) and their softmax statistics, and a workgroup
 // leaves one partial record per (sequence, head, row block). A small merge
 // kernel reduces the records of one (sequence, head) in a fixed order.
+#include <algorithm>
 #include <type_traits>
 
 #include "common.h"
@@ -309,21 +310,15 @@ __device__ __forceinline__ void stage_and_start(Stream& rs, const float* __restr
   lds_barrier();
 }
 
-// Rows of wave wi out of nw waves streaming `total` rows, at most rpw each:
+// Rows of wave wi out of nw waves streaming `total` rows, at most rpw each,
 // interleaved (rows wi, wi + nw, wi + 2 nw, ...), so the waves of a launch
-// advance through memory side by side, or in blocks of rpw consecutive rows
-// (MEDUSA_HEAD_INTERLEAVE=0).
-__device__ __forceinline__ void wave_rows(int wi, int nw, int rpw, int total, bool interleave,
-                                          int& rb, int& rstride, int& nrows) {
-  if (interleave) {
-    rb = wi;
-    rstride = nw;
-    nrows = wi < total ? min(rpw, (total - wi + nw - 1) / nw) : 0;
-  } else {
-    rb = wi * rpw;
-    rstride = 1;
-    nrows = max(0, min(rpw, total - rb));
-  }
+// advance through memory side by side (blocks of consecutive rows a wave
+// measured slower).
+__device__ __forceinline__ void wave_rows(int wi, int nw, int rpw, int total, int& rb,
+                                          int& rstride, int& nrows) {
+  rb = wi;
+  rstride = nw;
+  nrows = wi < total ? min(rpw, (total - wi + nw - 1) / nw) : 0;
 }
 
 // ---------------------------------------------------------------------------
@@ -348,7 +343,7 @@ template <class ET, int NB, int SPR>
 __global__ __launch_bounds__(kHeadWaves * 64, (head_min_blocks<NB, SPR>())) void heads_w1_kernel(
     const float* __restrict__ h, int B, int b0, int K, int d,
     const typename ET::storage* __restrict__ W1, const float* __restrict__ b1,
-    float* __restrict__ z, int rpw, int interleave) {
+    float* __restrict__ z, int rpw) {
   extern __shared__ float xs[];   // [NB][ldx]
   constexpr int CW = RowStream<ET, NB>::CW;
   const int ldx = (d + CW - 1) / CW * CW;
@@ -356,7 +351,7 @@ __global__ __launch_bounds__(kHeadWaves * 64, (head_min_blocks<NB, SPR>())) void
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int total = K * d;
   int rb, rstride, nrows;
-  wave_rows(blockIdx.x * kHeadWaves + wave, gridDim.x * kHeadWaves, rpw, total, interleave != 0,
+  wave_rows(blockIdx.x * kHeadWaves + wave, gridDim.x * kHeadWaves, rpw, total,
             rb, rstride, nrows);
   // the residual h of the lane's row, read before the stream
   float hres[NB];
@@ -513,7 +508,7 @@ __global__ __launch_bounds__(kHeadWaves * 64, (head_min_blocks<NB, SPR>())) void
     const float* __restrict__ z, int B, int b0, int K, int V, int d,
     const typename ET::storage* __restrict__ W2, int rpw, int S,
     float* __restrict__ head_logits, float* __restrict__ part_val, int* __restrict__ part_id,
-    float* __restrict__ part_m, float* __restrict__ part_s, int G, int interleave) {
+    float* __restrict__ part_m, float* __restrict__ part_s, int G) {
   extern __shared__ float xs[];   // [NB][ldx], then per-wave list exchange
   constexpr int CW = RowStream<ET, NB>::CW;
   const int ldx = (d + CW - 1) / CW * CW;
@@ -521,7 +516,7 @@ __global__ __launch_bounds__(kHeadWaves * 64, (head_min_blocks<NB, SPR>())) void
   const int nb = min(NB, B - b0);
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   int rb, rstride, nrows;
-  wave_rows(g * kHeadWaves + wave, gridDim.x * kHeadWaves, rpw, V, interleave != 0, rb, rstride,
+  wave_rows(g * kHeadWaves + wave, gridDim.x * kHeadWaves, rpw, V, rb, rstride,
             nrows);
   HeadStream<ET, NB, SPR> rs;
   stage_and_start<ET, NB>(rs, z + ((size_t)b0 * K + k) * d, (size_t)K * d, nb, d, xs, ldx,
@@ -689,8 +684,9 @@ __global__ __launch_bounds__(kHeadWaves * 64, 4) void heads_w2_tile_kernel(
   const int nb = min(kTileVecs, B - b0);
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int j = lane & 15, q = lane >> 4;
-  int rb, rstride, nrows;
-  wave_rows(g * kHeadWaves + wave, gridDim.x * kHeadWaves, 16 * NG, V, false, rb, rstride, nrows);
+  // a wave's 16 NG rows are consecutive (interleaved rows measured slower here)
+  const int rstride = 1, rb = (g * kHeadWaves + wave) * 16 * NG;
+  const int nrows = max(0, min(16 * NG, V - rb));
   float win[kTileVecs];
 #pragma unroll
   for (int b = 0; b < kTileVecs; ++b) win[b] = kNegInf;
@@ -858,7 +854,7 @@ hipError_t launch_heads_spr(const HeadsArgs& a, int b0, hipStream_t st) {
   const int g1 = (a.K * a.d + rows1 - 1) / rows1;
   hipLaunchKernelGGL((heads_w1_kernel<ET, NB, SPR>), dim3(g1), dim3(kHeadWaves * 64), lds_x, st, a.h,
                      a.B, b0, a.K, a.d, reinterpret_cast<const typename ET::storage*>(a.W1),
-                     a.b1, a.z, rpw1, a.interleave);
+                     a.b1, a.z, rpw1);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const size_t lds_list = (size_t)kHeadWaves * NB * (2 * MAXS_LDS + 2) * sizeof(float);
@@ -870,21 +866,11 @@ hipError_t launch_heads_spr(const HeadsArgs& a, int b0, hipStream_t st) {
   hipLaunchKernelGGL((heads_w2_kernel<ET, NB, SPR>), dim3(a.G, a.K), dim3(kHeadWaves * 64), lds2, st,
                      a.z, a.B, b0, a.K, a.V, a.d,
                      reinterpret_cast<const typename ET::storage*>(a.W2), a.w2_rows_per_wave,
-                     a.S, a.head_logits, a.part_val, a.part_id, a.part_m, a.part_s, a.G,
-                     a.interleave);
+                     a.S, a.head_logits, a.part_val, a.part_id, a.part_m, a.part_s, a.G);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (a.ev_after) e = hipEventRecord(a.ev_after, st);
   return e;
-}
-
-// MEDUSA_HEAD_ROW_STREAM=0 keeps the generic stream for every d.
-bool head_row_stream() {
-  static const bool v = [] {
-    const char* s = getenv("MEDUSA_HEAD_ROW_STREAM");
-    return !(s && *s && atoi(s) == 0);
-  }();
-  return v;
 }
 
 // Whole-row streams for bf16 rows of 8, 10 or 16 chunks (d = 4096, 5120,
@@ -892,7 +878,7 @@ bool head_row_stream() {
 template <class ET, int NB>
 hipError_t launch_heads_nb(const HeadsArgs& a, int b0, hipStream_t st) {
   constexpr int CW = RowStream<ET, NB>::CW;
-  if (std::is_same<ET, BF16>::value && NB <= 2 && head_row_stream() && a.d % CW == 0) {
+  if (std::is_same<ET, BF16>::value && NB <= 2 && a.d % CW == 0) {
     switch (a.d / CW) {
       case 8: return launch_heads_spr<ET, NB, (NB <= 2 ? 8 : 0)>(a, b0, st);
       case 10: return launch_heads_spr<ET, NB, (NB <= 2 ? 10 : 0)>(a, b0, st);
@@ -903,44 +889,15 @@ hipError_t launch_heads_nb(const HeadsArgs& a, int b0, hipStream_t st) {
   return launch_heads_spr<ET, NB, 0>(a, b0, st);
 }
 
-// Batched passes (3 or more vectors, bf16): W1 split over KS waves with DS
-// column blocks in flight, W2 in tile rows of NG with DS in flight.
-// MEDUSA_HEAD_TILE=0 keeps the per-row streams; MEDUSA_W1_TILE_KS (1, 2, 4)
-// and MEDUSA_W2_TILE ("ng,ds") choose the shapes where d allows (default
-// 4 and 2,4: 32 rows a wave with 8 tiles in flight; at batch 8 the step took
-// 746 us against 755-779 for 16-64 rows and 4-16 tiles in flight; fragment-
-// shaped reads lose DRAM locality as more of them are outstanding).
-bool head_tile() {
-  static const bool v = [] {
-    const char* s = getenv("MEDUSA_HEAD_TILE");
-    return !(s && *s && atoi(s) == 0);
-  }();
-  return v;
-}
-int env_choice(const char* name, int dflt) {
-  const char* s = getenv(name);
-  return s && *s ? atoi(s) : dflt;
-}
-// MEDUSA_W2_TILE ("ng,ds": tile rows per wave and column blocks in flight,
-// one of the instantiated pairs below)
-struct TileShape {
-  int ng, ds;
-};
-TileShape w2_tile_shape() {
-  static const TileShape v = [] {
-    const char* s = getenv("MEDUSA_W2_TILE");
-    int ng = 0, ds = 0;
-    if (s && *s) sscanf(s, "%d,%d", &ng, &ds);
-    const TileShape known[] = {{1, 8}, {2, 2}, {2, 4}, {2, 8}, {3, 2}, {3, 4}, {4, 2}, {4, 4}};
-    for (const TileShape& k : known)
-      if (k.ng == ng && k.ds == ds) return k;
-    return TileShape{2, 4};
-  }();
-  return v;
-}
-int w2_tile_ng() { return w2_tile_shape().ng; }
+// Batched passes (3 or more vectors, bf16): W1 split over 4 waves (fewer
+// where d does not allow) with 8 column blocks in flight, W2 in tile rows of
+// two (32 rows a wave) with 4 column blocks in flight (2 where d does not
+// allow). At batch 8 the step took 746 us with these against 755-779 for
+// 16-64 rows a wave and 4-16 tiles in flight: fragment-shaped reads lose
+// DRAM locality as more of them are outstanding.
+constexpr int kW2TileNg = 2;
 // rows per W2 workgroup of the batched pass
-int w2_tile_rows() { return kHeadWaves * 16 * w2_tile_ng(); }
+int w2_tile_rows() { return kHeadWaves * 16 * kW2TileNg; }
 
 hipError_t launch_heads_tile(const HeadsArgs& a, int b0, int G, hipStream_t st) {
   const int nb = std::min(kTileVecs, a.B - b0);
@@ -953,16 +910,15 @@ hipError_t launch_heads_tile(const HeadsArgs& a, int b0, int G, hipStream_t st) 
   if (e != hipSuccess) return e;
   const uint16_t* W1 = reinterpret_cast<const uint16_t*>(a.W1);
   uint16_t* zf16 = reinterpret_cast<uint16_t*>(zfrag);
-  const int ks_env = env_choice("MEDUSA_W1_TILE_KS", 4);
   const int total = a.K * d;
 #define W1_TILE(KS, DS)                                                                        \
   hipLaunchKernelGGL((heads_w1_tile_kernel<KS, DS>),                                           \
                      dim3((total + 16 * (kHeadWaves / KS) - 1) / (16 * (kHeadWaves / KS))),    \
                      dim3(kHeadWaves * 64), 0, st, a.h, a.B, b0, a.K, d, W1, a.b1, hfrag, a.z, \
                      zf16)
-  if (ks_env >= 4 && nblk % 32 == 0)
+  if (nblk % 32 == 0)
     W1_TILE(4, 8);
-  else if (ks_env >= 2 && nblk % 16 == 0)
+  else if (nblk % 16 == 0)
     W1_TILE(2, 8);
   else if (nblk % 8 == 0)
     W1_TILE(1, 8);
@@ -980,26 +936,11 @@ hipError_t launch_heads_tile(const HeadsArgs& a, int b0, int G, hipStream_t st) 
   hipLaunchKernelGGL((heads_w2_tile_kernel<NG, DS>), dim3(G, a.K), dim3(kHeadWaves * 64), 0, st, \
                      a.B, b0, a.K, a.V, d, W2, zfrag, a.S, a.head_logits, a.part_val,          \
                      a.part_id, a.part_m, a.part_s, G)
-  const TileShape ts = w2_tile_shape();
-  const int ds = nblk % ts.ds == 0 ? ts.ds : 2;   // d is a multiple of 64: nblk even
-  if (ts.ng == 1 && ds == 8)
-    W2_TILE(1, 8);
-  else if (ts.ng == 1)
-    W2_TILE(1, 2);
-  else if (ts.ng == 2 && ds == 8)
-    W2_TILE(2, 8);
-  else if (ts.ng == 2 && ds == 4)
-    W2_TILE(2, 4);
-  else if (ts.ng == 2)
-    W2_TILE(2, 2);
-  else if (ts.ng == 4 && ds == 4)
-    W2_TILE(4, 4);
-  else if (ts.ng == 4)
-    W2_TILE(4, 2);
-  else if (ds == 4)
-    W2_TILE(3, 4);
+  // d is a multiple of 64: nblk is even
+  if (nblk % 4 == 0)
+    W2_TILE(kW2TileNg, 4);
   else
-    W2_TILE(3, 2);
+    W2_TILE(kW2TileNg, 2);
 #undef W2_TILE
   e = hipGetLastError();
   if (e != hipSuccess) return e;
@@ -1011,7 +952,7 @@ template <class ET>
 hipError_t launch_heads_et(const HeadsArgs& a, hipStream_t st) {
   // Three or more bf16 vectors go through the batched passes, all of them
   // (the merge reads every sequence's records with one row-block count).
-  const bool tile = std::is_same<ET, BF16>::value && a.B >= 3 && head_tile() && a.afrag;
+  const bool tile = std::is_same<ET, BF16>::value && a.B >= 3 && a.afrag;
   const int G = tile ? (a.V + w2_tile_rows() - 1) / w2_tile_rows() : a.G;
   for (int b0 = 0; b0 < a.B; b0 += 8) {
     const int nb = a.B - b0;
@@ -1052,6 +993,12 @@ hipError_t launch_heads_et(const HeadsArgs& a, hipStream_t st) {
 }
 
 }  // namespace
+
+int heads_row_blocks_max(int V, int rows_per_wave) {
+  const int per_row = (V + 4 * rows_per_wave - 1) / (4 * rows_per_wave);
+  const int batched = (V + w2_tile_rows() - 1) / w2_tile_rows();
+  return std::max(per_row, batched);
+}
 
 hipError_t launch_heads(const HeadsArgs& a, hipStream_t st) {
   return a.f32 ? launch_heads_et<F32>(a, st) : launch_heads_et<BF16>(a, st);

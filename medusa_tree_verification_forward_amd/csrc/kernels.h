@@ -44,7 +44,6 @@ struct HeadsArgs {
   int G;                  // row blocks per head (4 waves of w2_rows_per_wave rows)
   int w1_rows_per_wave;   // 1..64, or 0: the fewest that fit one wave of resident workgroups
   int w2_rows_per_wave;   // 4..64
-  int interleave;         // 1: wave w streams rows w, w + nw, ...; 0: blocks of rows
   hipEvent_t ev_before;   // optional: recorded around the W2 kernel
   hipEvent_t ev_after;
   // optional (composite step, top-s drafting): the merge of head k also
@@ -58,6 +57,10 @@ struct HeadsArgs {
   int32_t* position_ids;       // [B][T]
 };
 hipError_t launch_heads(const HeadsArgs& a, hipStream_t st);
+// Row blocks a head's partial records can need: the per-row streams'
+// workgroups of 4 waves x rows_per_wave rows, or the batched passes' (3 or
+// more sequences) smaller ones, whichever gives more.
+int heads_row_blocks_max(int V, int rows_per_wave);
 
 struct TreeArgs {
   TreePlan plan;
@@ -106,13 +109,9 @@ struct GemmParams {
   const int32_t* parent;       // [T]
   float* child_logit;          // [M]
   float* logits_out;           // [M][N] or null
-  int* counters;               // fused epilogue: one zeroed counter per (group, pass)
+  int* counters;               // split-K hand-off: one zeroed counter per (group, pass)
   int group_cols;              // set by the launcher
-  int fused;                   // set by the launcher
-  int kg_shift;                // set by the launcher: log2 of the k-tiles per packed run
-  float* lm_slices;            // LM head split over K: [groups][KS][48][cols] fp32
 };
-int packed_kg_shift();
 // Weights W[rows][K] of the node GEMMs are packed into MFMA tiles (see
 // node_gemm.hip) before use; pair_dh = Dh reorders the rows of each head
 // into rotation pairs (W_qkv), 0 keeps them in order.
@@ -123,7 +122,6 @@ int gemm_groups_max(int N);                // column groups of a node GEMM (uppe
 int gemm_passes_max(int M);                // row passes (upper bound)
 int lm_head_blocks(int N, int M);          // row records of the LM head (16-column stripes)
 int lm_record_slots(int N);                // upper bound of lm_head_blocks over the configs
-int lm_splits_for(int M);                  // K slices of the LM head
 int gemm_splits(int epi, int N, int K, bool f32, int M);   // K slices of the QKV / output projection of M rows
 hipError_t launch_qkv(const GemmParams& p, hipStream_t st);
 hipError_t launch_oproj(const GemmParams& p, hipStream_t st);

@@ -30,11 +30,10 @@
 // are rows i and i+Dh/2 of the head, i = 8*(tile in head) + j).
 // With KS = 1 the epilogue runs on the accumulators themselves (the rotation
 // partner of a lane's column is in lane li ^ 8). Otherwise it runs in the last
-// of the KS workgroups of a group to finish
-// (found with a device-scope counter that it leaves at zero for the next
-// launch; the partials travel through agent-coherent stores and loads), or
-// in a kernel of its own.
-// The LM head reduces in-kernel (after the split-K hand-off when K is split):
+// of the KS workgroups of a group to finish (found with a device-scope
+// counter that it leaves at zero for the next launch; the partials travel
+// through agent-coherent stores and loads, no fence).
+// The LM head (never split over K) reduces in-kernel:
 // per row and 16-column stripe (max, argmax, S, W) at temperature tau with
 // S = sum e^{(l-m)/tau}, W = sum e^{(l-m)/tau} (l-m)/tau, one record per
 // (row, stripe) written by the wave that owns the stripe; the logit of every
@@ -79,15 +78,12 @@ __device__ __forceinline__ int packed_source_row(int n, int pair_dh) {
   return blk * pair_dh + (li < 8 ? 8 * tt + li : (pair_dh >> 1) + 8 * tt + li - 8);
 }
 
-// Tile order: k-tiles are grouped in runs of 2^sh; group G (k-tiles
-// k0 = G 2^sh .. k0 + gs - 1, gs = 2^sh except for a short last group) of
-// every stripe follows the whole group G - 1, stripe after stripe, and the
-// gs tiles of one stripe in a group are adjacent. sh = 0 is k-major order,
-// 2^sh >= nkt stripe-major.
-__device__ __forceinline__ size_t packed_tile(int nt, int kt, int nkt, int ntiles, int sh) {
-  const int k0 = (kt >> sh) << sh;
-  const int gs = min(1 << sh, nkt - k0);
-  return (size_t)k0 * ntiles + (size_t)nt * gs + (kt - k0);
+// Tile order: k-major -- tile (nt, kt) at kt * ntiles + nt, so the stripes
+// that the waves of a launch stream side by side are adjacent in memory
+// (stripe-major order, and runs of 2-16 k-tiles a stripe, measured no
+// faster).
+__device__ __forceinline__ size_t packed_tile(int nt, int kt, int ntiles) {
+  return (size_t)kt * ntiles + nt;
 }
 
 // Packing: piece q of the output is lane l = q % 64 of tile q / 64; tile
@@ -95,19 +91,14 @@ __device__ __forceinline__ size_t packed_tile(int nt, int kt, int nkt, int ntile
 // KT kt + PV (l / 16) .. + PV - 1 (KT = 4 PV). Rows >= rows are 0.
 template <class ET>
 __global__ void pack_weight_kernel(const typename ET::storage* __restrict__ W, int rows, int K,
-                                   int pair_dh, int sh, u32x4_t* __restrict__ out,
-                                   size_t pieces) {
+                                   int pair_dh, u32x4_t* __restrict__ out, size_t pieces) {
   constexpr int PV = ET::kPerVec, KT = 4 * PV;
   const size_t q = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (q >= pieces) return;
-  const int nkt = K / KT, ntiles = (rows + 15) / 16;
+  const int ntiles = (rows + 15) / 16;
   const size_t tile = q >> 6;
   const int l = (int)(q & 63);
-  const size_t full = (size_t)ntiles << sh;   // tiles of a whole group
-  const int k0 = (int)(tile / full) << sh;
-  const int gs = min(1 << sh, nkt - k0);
-  const int rem = (int)(tile - (size_t)k0 * ntiles);
-  const int nt = rem / gs, kt = k0 + rem % gs;
+  const int kt = (int)(tile / ntiles), nt = (int)(tile - (size_t)kt * ntiles);
   const int n = 16 * nt + (l & 15);
   u32x4_t v = {0u, 0u, 0u, 0u};
   if (n < rows) {
@@ -156,40 +147,6 @@ __device__ __forceinline__ void oproj_store(const GemmParams& p, int r, int n, f
   using St = typename ET::storage;
   p.y_out[(size_t)r * p.N + n] = y;
   reinterpret_cast<St*>(p.y_elem)[(size_t)r * p.N + n] = ET::from_float(y);
-}
-
-template <class ET>
-__device__ __forceinline__ void oproj_finish(const GemmParams& p, int r, int n, float acc) {
-  using St = typename ET::storage;
-  const St* x = reinterpret_cast<const St*>(p.E) +
-                (size_t)min(max(p.tokens[r], 0), p.a_nrows - 1) * p.N;
-  oproj_store<ET>(p, r, n, ET::load1(x + n) + acc);
-}
-
-// Partials are stored part[g][ks][r][c] (g = n / GC, c = n % GC): a
-// workgroup's slice is one contiguous [M][GC] block.
-__device__ __forceinline__ const float* partial_at(const GemmParams& p, int r, int n, int KS) {
-  const int g = n / p.group_cols, c = n - g * p.group_cols;
-  return p.part + ((size_t)g * KS * p.M + r) * p.group_cols + c;
-}
-
-// Sum, in slice order, of the KS partials of output (r, n); loads of up to
-// four slices are issued before any is added.
-__device__ __forceinline__ float sum_partials(const GemmParams& p, int r, int n, int KS) {
-  const float* q = partial_at(p, r, n, KS);
-  const size_t stride = (size_t)p.M * p.group_cols;
-  float acc = 0.f;
-  int s = 0;
-  for (; s + 4 <= KS; s += 4) {
-    const float v0 = q[s * stride], v1 = q[(s + 1) * stride], v2 = q[(s + 2) * stride],
-                v3 = q[(s + 3) * stride];
-    acc += v0;
-    acc += v1;
-    acc += v2;
-    acc += v3;
-  }
-  for (; s < KS; ++s) acc += q[s * stride];
-  return acc;
 }
 
 // Workgroup coordinates: column group g, K slice ks, row pass pz. With one
@@ -246,7 +203,7 @@ __global__ __launch_bounds__(64 * WV, (WV == 4 && D <= 8) ? 4 : (WV <= 3 ? 1 : 2
   // this wave's stripe (wave-uniform) and its k-tile s of the slice
   const int nt = min(g * WV + __builtin_amdgcn_readfirstlane(wave), ntiles - 1);
   const u32x4_t* __restrict__ W4 = reinterpret_cast<const u32x4_t*>(p.W) + lane;
-  auto wtile = [&](int s) { return W4 + packed_tile(nt, kt_lo + s, nkt, ntiles, p.kg_shift) * 64; };
+  auto wtile = [&](int s) { return W4 + packed_tile(nt, kt_lo + s, ntiles) * 64; };
 
   __shared__ u32x4_t sA0[CH][MT][64];
   __shared__ u32x4_t sA1[CH][MT][64];
@@ -422,22 +379,16 @@ __global__ __launch_bounds__(64 * WV, (WV == 4 && D <= 8) ? 4 : (WV <= 3 ? 1 : 2
     }
   }
   if constexpr (EPI != EPI_LM) {
-    // slice ks of the partials: part[g][ks][r][c]
+    // slice ks of the partials: part[g][ks][r][c] (a workgroup's slice is one
+    // contiguous [M][GC] block)
     float* part = p.part + (size_t)(g * KS + ks) * p.M * GC + 16 * wave + li;
-    const bool fused = p.fused;
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int r = m0 + 16 * mt + 4 * lq + j;
-        if (r < p.M) {
-          if (fused)
-            coherent_store(part + (size_t)r * GC, acc[mt][j]);
-          else
-            part[(size_t)r * GC] = acc[mt][j];
-        }
+        if (r < p.M) coherent_store(part + (size_t)r * GC, acc[mt][j]);
       }
-    if (!fused) return;
     // The last of the KS workgroups of this (group, pass) finishes it: every
     // thread loads all the slices of its outputs before it uses any, then
     // sums them in slice order. The row data of a thread's first batch of
@@ -546,42 +497,6 @@ __global__ __launch_bounds__(64 * WV, (WV == 4 && D <= 8) ? 4 : (WV <= 3 ? 1 : 2
       }
     }
   } else {
-    if (KS > 1) {
-      // Slices of the logit tile: the last of the KS workgroups of this
-      // (group, pass) sums them in slice order (partials handed over through
-      // agent-coherent stores and loads) and goes on to the statistics.
-      constexpr int TILE = 16 * MT * GC;
-      float* sl = p.lm_slices + ((size_t)g * gridDim.z + pz) * KS * TILE;
-      const int ci = 16 * wave + li;
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          coherent_store(sl + (size_t)ks * TILE + (16 * mt + 4 * lq + j) * GC + ci, acc[mt][j]);
-      if (!last_to_arrive(p.counters + g * gridDim.z + pz, KS)) return;
-      float tot[MT][4];
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) tot[mt][j] = 0.f;
-      for (int s0 = 0; s0 < KS; ++s0) {
-        float v[MT][4];
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-          for (int j = 0; j < 4; ++j)
-            v[mt][j] = s0 == ks ? acc[mt][j]
-                                : coherent_load(sl + (size_t)s0 * TILE + (16 * mt + 4 * lq + j) * GC + ci);
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-          for (int j = 0; j < 4; ++j) tot[mt][j] += v[mt][j];
-      }
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acc[mt][j] = tot[mt][j];
-    }
     // The wave's logit tile goes through LDS, 48 rows (MG m-tiles) at a time,
     // so that lane r owns row r of the group: per row and 16-column stripe
     // (max, lowest argmax, S, W) scanned over the columns in order, one
@@ -655,25 +570,6 @@ __global__ __launch_bounds__(64 * WV, (WV == 4 && D <= 8) ? 4 : (WV <= 3 ? 1 : 2
   }
 }
 
-// Separate epilogues: one thread per (row, rotation pair) / (row, column).
-template <class ET>
-__global__ __launch_bounds__(256) void qkv_epilogue_kernel(GemmParams p, int KS) {
-  const int r = blockIdx.y;
-  const int P = blockIdx.x * 256 + threadIdx.x;   // pair index over the packed columns
-  const int c1 = 16 * (P >> 3) + (P & 7);
-  if (c1 >= p.N) return;
-  const float x1 = sum_partials(p, r, c1, KS);
-  const float x2 = sum_partials(p, r, c1 + 8, KS);
-  qkv_finish<ET>(p, r, c1, p.pos[r], rope_inv_freq(p, c1), x1, x2);
-}
-
-template <class ET>
-__global__ __launch_bounds__(256) void oproj_epilogue_kernel(GemmParams p, int KS) {
-  const int r = blockIdx.y, n = blockIdx.x * 256 + threadIdx.x;
-  if (n >= p.N) return;
-  oproj_finish<ET>(p, r, n, sum_partials(p, r, n, KS));
-}
-
 // Row statistics from the G records of row r: 256 threads, thread t takes
 // records t + 256 u in u order (every load of a round issued before any is
 // used), then a lane butterfly and the four waves in order.
@@ -725,103 +621,35 @@ struct Config {
   int wv, mt, ch, d;
 };
 
-// The 48-row tile of the QKV and output projections: waves per workgroup,
-// k-tiles per A chunk, weight loads in flight per wave and K slices (0:
-// automatic). MEDUSA_QKV_CFG / MEDUSA_OPROJ_CFG ("wv,ch,d,ks"; one of the
-// (wv, ch, d) sets launch_main instantiates) fix it; otherwise, with 2 to 4
-// sixteen-column stripes per compute unit, one workgroup of 3 or 4 waves per
-// compute unit streams the whole K (no hand-off between workgroups), and
-// with fewer stripes 4-wave workgroups split K.
+// The 48-row tile of the QKV and output projections, and its K slices (0:
+// as many as gemm_splits gives). With 2 to 4 sixteen-column stripes per
+// compute unit one workgroup of 3 or 4 waves per compute unit streams the
+// whole K (no hand-off between workgroups: the 7B QKV, 768 stripes); with
+// fewer stripes 4-wave workgroups split K (the 7B output projection, 256
+// stripes, 4 slices).
 struct SmallConfig {
   Config c;
   int ks;
 };
-SmallConfig parse_small(const char* env) {
-  const char* s = getenv(env);
-  if (!(s && *s)) return SmallConfig{{0, 0, 0, 0}, 0};
-  int wv = 0, ch = 0, d = 0, ks = 0;
-  if (sscanf(s, "%d,%d,%d,%d", &wv, &ch, &d, &ks) < 3) return SmallConfig{{0, 0, 0, 0}, 0};
-  const Config known[] = {{4, 3, 4, 8}, {4, 3, 8, 16}, {8, 3, 8, 8}, {8, 3, 8, 16},
-                          {3, 3, 8, 16}, {2, 3, 8, 16}};
-  for (const Config& k : known)
-    if (k.wv == wv && k.ch == ch && k.d == d) return SmallConfig{k, ks < 0 ? 0 : ks};
-  return SmallConfig{{0, 0, 0, 0}, 0};
-}
-SmallConfig small_config(int epi, int N) {
-  static const SmallConfig q = parse_small("MEDUSA_QKV_CFG");
-  static const SmallConfig o = parse_small("MEDUSA_OPROJ_CFG");
-  const SmallConfig& f = epi == EPI_QKV ? q : o;
-  if (f.c.wv) return f;
+SmallConfig small_config(int N) {
   const int stripes = (N + 15) / 16, cus = device_cus();
   if (stripes > 2 * cus && stripes <= 3 * cus) return SmallConfig{{3, 3, 8, 16}, 1};
   if (stripes > 3 * cus && stripes <= 4 * cus) return SmallConfig{{4, 3, 8, 16}, 1};
   return SmallConfig{{4, 3, 4, 8}, 0};
 }
 
-// MEDUSA_LM_CFG ("wv,ch", default "8,8"): waves per workgroup and k-tiles per
-// A chunk of the LM head's 48-row tile (4,4: 8 weight loads in flight per
-// wave; 8,4: 8,8 chunks with 8 in flight; 8,8: 16 in flight).
-Config lm_config(int KS) {
-  static const Config forced = [] {
-    const char* s = getenv("MEDUSA_LM_CFG");
-    int wv = 0, ch = 0;
-    if (s && *s) sscanf(s, "%d,%d", &wv, &ch);
-    if (wv == 4 && ch == 4) return Config{4, 3, 4, 8};
-    if (wv == 8 && ch == 4) return Config{8, 3, 8, 8};
-    if (wv == 8 && ch == 8) return Config{8, 3, 8, 16};
-    return Config{0, 0, 0, 0};
-  }();
-  if (forced.wv) return forced;
-  // unsplit: one 8-wave workgroup per compute unit, 16 loads in flight per
-  // wave; split: 4-wave workgroups, four per compute unit
-  return KS > 1 ? Config{4, 3, 4, 8} : Config{8, 3, 8, 16};
-}
-
 Config config_for(int M, int N, int epi) {
   if (M <= 48) {
-    if (epi == EPI_LM) return lm_config(lm_splits_for(M));
-    return small_config(epi, N).c;
+    // LM head: one 8-wave workgroup per compute unit, 16 weight loads in
+    // flight per wave, no K split (split variants measured slower: the
+    // 4-wave workgroups they need read the tree rows from L2 twice as often)
+    if (epi == EPI_LM) return Config{8, 3, 8, 16};
+    return small_config(N).c;
   }
   // more rows: 8-wave workgroups of 12 m-tiles (A chunks of 48 KB, double
-  // buffered) with MEDUSA_BIG_GEMM_D (4 or 8, default 4: 8 spills registers
-  // and measured no faster) weight loads in flight per wave
-  static const int d = [] {
-    const char* s = getenv("MEDUSA_BIG_GEMM_D");
-    return s && *s && atoi(s) == 8 ? 8 : 4;
-  }();
-  return Config{8, 12, 4, d};
-}
-
-}  // namespace
-
-// Packed tiles come in runs of 2^sh k-tiles per stripe, the runs of all
-// stripes for one range of k adjacent (packed_tile), so the waves of a launch,
-// which advance through k together, read nearby memory while each reads a
-// short contiguous run. MEDUSA_PACK_KGROUP (a power of two, default 1:
-// k-major) sets the run length; one at least the k-tile count is
-// stripe-major.
-int packed_kg_shift() {
-  static const int v = [] {
-    const char* s = getenv("MEDUSA_PACK_KGROUP");
-    const int g = s && *s ? atoi(s) : 1;
-    int sh = 0;
-    while (sh < 16 && (2 << sh) <= g) ++sh;
-    return sh;
-  }();
-  return v;
-}
-
-namespace {
-
-// QKV and output-projection epilogues run in the last workgroup of each
-// column group (default), or with MEDUSA_GEMM_FUSED_EPILOGUE=0 in a kernel of
-// their own.
-bool fused_epilogue() {
-  static const bool v = [] {
-    const char* s = getenv("MEDUSA_GEMM_FUSED_EPILOGUE");
-    return !(s && *s && atoi(s) == 0);
-  }();
-  return v;
+  // buffered) with 4 weight loads in flight per wave (8 spills registers
+  // and measured no faster)
+  return Config{8, 12, 4, 4};
 }
 
 template <class ET, int EPI>
@@ -832,20 +660,14 @@ hipError_t launch_main(const GemmParams& p, int KS, hipStream_t st) {
   dim3 grid(groups, KS, passes), block(64 * c.wv);
   if (c.mt == 3 && c.wv == 3)
     hipLaunchKernelGGL((node_gemm_kernel<ET, 3, 3, 8, 16, EPI>), grid, block, 0, st, p);
-  else if (c.mt == 3 && c.wv == 2)
-    hipLaunchKernelGGL((node_gemm_kernel<ET, 2, 3, 8, 16, EPI>), grid, block, 0, st, p);
   else if (c.mt == 3 && c.wv == 4 && c.d == 16)
     hipLaunchKernelGGL((node_gemm_kernel<ET, 4, 3, 8, 16, EPI>), grid, block, 0, st, p);
   else if (c.mt == 3 && c.wv == 4)
     hipLaunchKernelGGL((node_gemm_kernel<ET, 4, 3, 4, 8, EPI>), grid, block, 0, st, p);
-  else if (c.mt == 3 && c.d == 8)
-    hipLaunchKernelGGL((node_gemm_kernel<ET, 8, 3, 8, 8, EPI>), grid, block, 0, st, p);
   else if (c.mt == 3)
     hipLaunchKernelGGL((node_gemm_kernel<ET, 8, 3, 8, 16, EPI>), grid, block, 0, st, p);
-  else if (c.d == 4)
-    hipLaunchKernelGGL((node_gemm_kernel<ET, 8, 12, 4, 4, EPI>), grid, block, 0, st, p);
   else
-    hipLaunchKernelGGL((node_gemm_kernel<ET, 8, 12, 4, 8, EPI>), grid, block, 0, st, p);
+    hipLaunchKernelGGL((node_gemm_kernel<ET, 8, 12, 4, 4, EPI>), grid, block, 0, st, p);
   return hipGetLastError();
 }
 
@@ -853,24 +675,7 @@ template <int EPI>
 hipError_t launch_split(GemmParams p, hipStream_t st) {
   const int KS = gemm_splits(EPI, p.N, p.K, p.f32, p.M);
   p.group_cols = 16 * config_for(p.M, p.N, EPI).wv;
-  p.fused = fused_epilogue();
-  p.kg_shift = packed_kg_shift();
-  hipError_t e = p.f32 ? launch_main<F32, EPI>(p, KS, st) : launch_main<BF16, EPI>(p, KS, st);
-  if (e != hipSuccess || p.fused || KS == 1) return e;
-  if (EPI == EPI_QKV) {
-    dim3 grid((p.N / 2 + 255) / 256, p.M);
-    if (p.f32)
-      hipLaunchKernelGGL(qkv_epilogue_kernel<F32>, grid, dim3(256), 0, st, p, KS);
-    else
-      hipLaunchKernelGGL(qkv_epilogue_kernel<BF16>, grid, dim3(256), 0, st, p, KS);
-  } else {
-    dim3 grid((p.N + 255) / 256, p.M);
-    if (p.f32)
-      hipLaunchKernelGGL(oproj_epilogue_kernel<F32>, grid, dim3(256), 0, st, p, KS);
-    else
-      hipLaunchKernelGGL(oproj_epilogue_kernel<BF16>, grid, dim3(256), 0, st, p, KS);
-  }
-  return hipGetLastError();
+  return p.f32 ? launch_main<F32, EPI>(p, KS, st) : launch_main<BF16, EPI>(p, KS, st);
 }
 
 }  // namespace
@@ -894,25 +699,20 @@ hipError_t launch_pack_weight(bool f32, const void* W, int rows, int K, int pair
   const size_t blocks = (pieces + threads - 1) / threads;
   if (f32)
     hipLaunchKernelGGL(pack_weight_kernel<F32>, dim3((unsigned)blocks), dim3(threads), 0, st,
-                       static_cast<const float*>(W), rows, K, pair_dh, packed_kg_shift(),
+                       static_cast<const float*>(W), rows, K, pair_dh,
                        static_cast<u32x4_t*>(out), pieces);
   else
     hipLaunchKernelGGL(pack_weight_kernel<BF16>, dim3((unsigned)blocks), dim3(threads), 0, st,
-                       static_cast<const uint16_t*>(W), rows, K, pair_dh, packed_kg_shift(),
+                       static_cast<const uint16_t*>(W), rows, K, pair_dh,
                        static_cast<u32x4_t*>(out), pieces);
   return hipGetLastError();
 }
 
 // Slices of K: the count the tile configuration fixes, else the smallest
-// power of two that gives the grid at least MEDUSA_GEMM_MIN_WAVES waves
-// (default 1024, 4 per compute unit); either way every wave keeps at least
-// 8 k-tiles per slice.
+// power of two that gives the grid at least kGemmMinWaves waves (4 per
+// compute unit); either way every wave keeps at least 8 k-tiles per slice.
+constexpr int kGemmMinWaves = 1024;
 int gemm_splits(int epi, int N, int K, bool f32, int M) {
-  static const int min_waves = [] {
-    const char* s = getenv("MEDUSA_GEMM_MIN_WAVES");
-    const int v = s && *s ? atoi(s) : 1024;
-    return v < 1 ? 1 : (v > 65536 ? 65536 : v);
-  }();
   const int nkt = K / (f32 ? 16 : 32);
   int ks = 1;
   if (M > 48) {
@@ -923,13 +723,13 @@ int gemm_splits(int epi, int N, int K, bool f32, int M) {
     while (wgs * ks * 2 <= device_cus() && nkt / (ks * 2) >= 8 && ks < kMaxSplits) ks *= 2;
     return ks;
   }
-  const int forced = small_config(epi, N).ks;
+  const int forced = small_config(N).ks;
   const int stripes = (N + 15) / 16;
   if (forced > 0) {
     while (ks * 2 <= forced && nkt / (ks * 2) >= 8 && ks < kMaxSplits) ks *= 2;
     return ks;
   }
-  while (stripes * ks < min_waves && nkt / (ks * 2) >= 8 && ks < kMaxSplits) ks *= 2;
+  while (stripes * ks < kGemmMinWaves && nkt / (ks * 2) >= 8 && ks < kMaxSplits) ks *= 2;
   return ks;
 }
 
@@ -939,24 +739,9 @@ hipError_t launch_oproj(const GemmParams& p, hipStream_t st) {
   return launch_split<EPI_OPROJ>(p, st);
 }
 
-// MEDUSA_LM_SPLITS (1, 2 or 4; default 1): K slices of the LM head for a
-// single 48-row pass. With more than one, the last workgroup of each column
-// group sums the slices' logit tiles (handed over without fences) before the
-// in-kernel statistics.
-int lm_splits_for(int M) {
-  static const int v = [] {
-    const char* s = getenv("MEDUSA_LM_SPLITS");
-    const int k = s && *s ? atoi(s) : 1;
-    return k >= 4 ? 4 : (k >= 2 ? 2 : 1);
-  }();
-  return M <= 48 ? v : 1;
-}
-
 hipError_t launch_lm_head(GemmParams p, float* row_stats, int* row_argmax, hipStream_t st) {
-  p.kg_shift = packed_kg_shift();
   p.group_cols = 16 * config_for(p.M, p.N, EPI_LM).wv;
-  const int KS = lm_splits_for(p.M);
-  hipError_t e = p.f32 ? launch_main<F32, EPI_LM>(p, KS, st) : launch_main<BF16, EPI_LM>(p, KS, st);
+  hipError_t e = p.f32 ? launch_main<F32, EPI_LM>(p, 1, st) : launch_main<BF16, EPI_LM>(p, 1, st);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(row_stats_merge_kernel, dim3(p.M), dim3(kRowMergeThreads), 0, st, p.part,
                      lm_head_blocks(p.N, p.M), p.inv_tau, row_stats, row_argmax);

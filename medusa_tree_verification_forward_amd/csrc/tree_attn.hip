@@ -640,14 +640,12 @@ __global__ __launch_bounds__(64) void attn_merge_kernel(AttnArgs a) {
 
 constexpr int kHeldTiles = 9;   // query tiles whose Q rows the bf16 kernel can hold
 
-// MEDUSA_ATTN_HOLD_Q=0 reloads each query group per chunk for trees of 5-9
-// query tiles (the shape below 65 queries); held rows need the device to
-// give a workgroup the kernel's LDS.
+// Trees of 5-9 query tiles hold every query row in LDS when the device gives
+// a workgroup the kernel's LDS (151 KB for 128-wide heads); else each query
+// group's rows are reloaded per chunk.
 template <int DH>
 bool attn_hold_q_for() {
   static const bool v = [] {
-    const char* s = getenv("MEDUSA_ATTN_HOLD_Q");
-    if (s && *s && atoi(s) == 0) return false;
     int dev = 0, lim = 0;
     hipFuncAttributes fa{};
     if (hipGetDevice(&dev) != hipSuccess ||
@@ -665,20 +663,15 @@ hipError_t launch_bf16(const AttnArgs& a, hipStream_t st) {
   const auto attn_hold_q = [] { return attn_hold_q_for<DH>(); };
   const int MQ = (a.T + 15) / 16;
   // one workgroup per compute unit (its LDS use allows no second): chunks
-  // per (b, h) in flight = CUs / (B H), each workgroup looping over the rest
+  // per (b, h) in flight = CUs / (B H), each workgroup looping over the rest.
   // With several sequences and at most one workgroup per (sequence, head),
   // one workgroup would loop over every chunk of its sequence and ragged
   // prefixes would leave compute units idle while the longest finish: then
   // 4x as many workgroups are launched, so that those of short prefixes
-  // finish early and free their units (MEDUSA_ATTN_GRID overrides the
-  // factor; 1-16).
-  static const int forced = [] {
-    const char* s = getenv("MEDUSA_ATTN_GRID");
-    const int v = s && *s ? atoi(s) : 0;
-    return v < 0 ? 0 : (v > 16 ? 16 : v);
-  }();
+  // finish early and free their units (a second round of workgroups
+  // measured 2-4x slower for one sequence).
   const int cus = device_cus();
-  const int over = forced ? forced : (a.B > 1 && cus <= a.B * a.H ? 4 : 1);
+  const int over = a.B > 1 && cus <= a.B * a.H ? 4 : 1;
   int G = over * cus / (a.B * a.H);
   G = G < 1 ? 1 : (G > a.NS ? a.NS : G);
   dim3 grid(G, a.H, a.B), block(64 * kPfxWaves);
