@@ -150,3 +150,54 @@ def test_generate_exact_mode_matches_oracle_loop():
     print("compared steps", compared, "of", n * B)
     assert compared >= n, (compared, o["draft_margin"], o["accept_margin"], o["draw_margin"])
     assert o["accept_len"].sum() > 0 and (o["accept_len"] == 0).any()
+
+
+def test_generate_graph_replay():
+    # The decoding loop (5 steps, so the final state copy runs too) recorded
+    # in one HIP graph and replayed three times, the loop state restored by
+    # eager copies between replays: every replay must equal the eager loop
+    # bit for bit -- tokens, accepted depths, h, root, kv_len and both caches
+    # -- and the oracle's loop.
+    require_gpu()
+    import torch
+    from medusa_tree_verification_forward_amd.step import to_host
+    n, B = 5, 3
+    inp = _inputs(n, B=B, seed=99)
+    st = _step(inp, "greedy")
+    keys = ("h", "root", "kv_len", "k_cache", "v_cache")
+    start = {k: st.inp[k].clone() for k in keys}
+
+    def restore():
+        for k in keys:
+            st.inp[k].copy_(start[k])
+
+    def snapshot(toks, acc):
+        out = {"toks": to_host(toks), "acc": to_host(acc)}
+        out.update({k: to_host(st.inp[k]) for k in keys})
+        return out
+
+    toks, acc = st.generate(n)
+    torch.cuda.synchronize()
+    ref = snapshot(toks, acc)
+    o = OG.generate(inp, n, mode="greedy", bf16=True, **STEP)
+    assert np.array_equal(ref["acc"], o["accept_len"])
+    assert np.array_equal(ref["toks"], o["out_tokens"])
+    assert o["accept_len"].sum() > 0
+
+    restore()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        gtoks, gacc = st.generate(n)
+    for rep in range(3):
+        restore()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        got = snapshot(gtoks, gacc)
+        for k in ref:
+            assert np.array_equal(ref[k], got[k]), (rep, k)
+        # eager work between the replays
+        restore()
+        st.generate(1)
+        torch.cuda.synchronize()
