@@ -278,7 +278,8 @@ def decode_report(steps):
                 "the heads against one layer, not against a whole base model"}))
 
 
-def time_step(w, steps, warmup, reset_kv_len=False, graph=False, copy_bytes=0):
+def time_step(w, steps, warmup, reset_kv_len=False, graph=False, copy_bytes=0,
+              min_warm_s=None):
     """Time `steps` whole steps of workload w (inputs resident in HBM), then
     the dominant kernel in a second pass of the same steps. Returns a dict
     with the step object and the timings."""
@@ -307,8 +308,9 @@ def time_step(w, steps, warmup, reset_kv_len=False, graph=False, copy_bytes=0):
     # least MIN_WARM_S: a 5-step warm-up left the first timed steps ~2-4%
     # slower than steady state (clocks and caches still settling), which a
     # serving loop never sees. The timed region below is unaffected.
+    min_warm_s = MIN_WARM_S if min_warm_s is None else min_warm_s
     n, t0 = 0, time.perf_counter()
-    while n < warmup or time.perf_counter() - t0 < MIN_WARM_S:
+    while n < warmup or time.perf_counter() - t0 < min_warm_s:
         step()
         n += 1
         if n % 8 == 0:
@@ -389,6 +391,9 @@ def main():
                          "followed by the other workloads under other_workloads)")
     ap.add_argument("--headline-only", action="store_true",
                     help="time the 7B step alone (no other_workloads)")
+    ap.add_argument("--min-warm", type=float, default=MIN_WARM_S,
+                    help="continue the untimed warm-up until this many seconds of GPU work "
+                         "(0: exactly W steps, for profiling runs that count launches)")
     ap.add_argument("--decode", action="store_true",
                     help="print the decoding-loop report (A, A/r) instead of the step line")
     args = ap.parse_args()
@@ -408,7 +413,8 @@ def main():
 
     name = args.workload or WORKLOAD
     w = WORKLOADS[name]
-    r = time_step(w, args.steps, args.warmup, args.reset_kv_len, args.graph, args.copy_bytes)
+    r = time_step(w, args.steps, args.warmup, args.reset_kv_len, args.graph, args.copy_bytes,
+                  args.min_warm)
     ms_step, T, L_total = r["ms_step"], r["T"], r["L_total"]
     alg = algorithmic_bytes(w, T, L_total)
     w2b = w2_kernel_bytes(w)
@@ -436,7 +442,7 @@ def main():
                    + (" (prefix-length reset + medusa_step)" if args.reset_kv_len else
                       " (medusa_step; advanced prefix lengths written to a separate buffer, "
                       "so every step runs over the same prefix)")
-                   + f"; untimed warm-up: the W steps, continued to at least {MIN_WARM_S} s "
+                   + f"; untimed warm-up: the W steps, continued to at least {args.min_warm} s "
                      "of GPU work"),
         "config": {"workload": w.name, "batch": w.B, "d": w.d, "V": w.V, "heads": w.K,
                    "tree": f"top-{w.s}".replace(" ", ""), "tree_nodes": T - 1,
@@ -466,7 +472,7 @@ def main():
         for oname in OTHER_WORKLOADS:
             ow = WORKLOADS[oname]
             n = max(20, args.steps // 4)
-            o = time_step(ow, n, max(5, args.warmup // 4))
+            o = time_step(ow, n, max(5, args.warmup // 4), min_warm_s=args.min_warm)
             oalg = algorithmic_bytes(ow, o["T"], o["L_total"])
             ocomb = combined_roofline_us(ow, o["T"], o["L_total"])
             others.append({

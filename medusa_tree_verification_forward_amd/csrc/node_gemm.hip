@@ -504,7 +504,19 @@ __global__ __launch_bounds__(64 * WV, (WV == 4 && D <= 8) ? 4 : (WV <= 3 ? 1 : 2
     constexpr int MG = MT < 3 ? MT : 3;
     static_assert(MT % MG == 0, "row groups");
     constexpr int LTS = 20;   // row stride (floats) of the tile: 16-byte rows
-    __shared__ float lt[WV][16 * MG][LTS];
+    // the tiles take the A buffers' LDS when they fit there (every wave is
+    // past its last chunk after the barrier), else LDS of their own
+    constexpr int kLtFloats = WV * 16 * MG * LTS;
+    constexpr bool kLtInA = kLtFloats * 4 <= (int)sizeof(sA0);
+    __shared__ float lt_own[kLtInA ? 1 : kLtFloats];
+    float* lt_base = lt_own;
+    if constexpr (kLtInA) {
+      __syncthreads();
+      lt_base = reinterpret_cast<float*>(&sA0[0][0][0]);
+    }
+    const auto lt = [&](int r, int c) -> float& {
+      return lt_base[(wave * 16 * MG + r) * LTS + c];
+    };
     const int c0 = n0 + 16 * wave;
     const int nv = min(16, p.N - c0);   // valid columns of the stripe
     const int stripes = gridDim.x * WV;
@@ -514,7 +526,7 @@ __global__ __launch_bounds__(64 * WV, (WV == 4 && D <= 8) ? 4 : (WV <= 3 ? 1 : 2
 #pragma unroll
       for (int mt = 0; mt < MG; ++mt)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) lt[wave][16 * mt + 4 * lq + j][li] = acc[mq + mt][j];
+        for (int j = 0; j < 4; ++j) lt(16 * mt + 4 * lq + j, li) = acc[mq + mt][j];
       wave_lds_sync();
       const int g0 = m0 + 16 * mq;   // first row of the group
       if (lane < 16 * MG) {
@@ -522,7 +534,7 @@ __global__ __launch_bounds__(64 * WV, (WV == 4 && D <= 8) ? 4 : (WV <= 3 ? 1 : 2
         float v[16];
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          const float4 x = *reinterpret_cast<const float4*>(&lt[wave][lane][4 * q]);
+          const float4 x = *reinterpret_cast<const float4*>(&lt(lane, 4 * q));
           v[4 * q] = x.x;
           v[4 * q + 1] = x.y;
           v[4 * q + 2] = x.z;
@@ -556,7 +568,7 @@ __global__ __launch_bounds__(64 * WV, (WV == 4 && D <= 8) ? 4 : (WV <= 3 ? 1 : 2
         int r = ch_r, tok = ch_tok, node = ch_node;
         if (e0 > 0) child_of(e0 + lane, r, tok, node);
         if (node >= 0 && tok >= c0 && tok < c0 + 16 && r >= g0 && r < g1)
-          p.child_logit[node] = lt[wave][r - g0][tok - c0];
+          p.child_logit[node] = lt(r - g0, tok - c0);
       }
     }
     if (p.logits_out && col < p.N)
