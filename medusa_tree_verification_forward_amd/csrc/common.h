@@ -52,6 +52,9 @@ struct BF16 {
   __device__ __forceinline__ static float load1(const storage* p) {
     return __uint_as_float(((uint32_t)*p) << 16);
   }
+  // the bits of one element, widened to 32 (converted later by from_raw)
+  __device__ __forceinline__ static uint32_t load_raw(const storage* p) { return *p; }
+  __device__ __forceinline__ static float from_raw(uint32_t r) { return __uint_as_float(r << 16); }
   __device__ __forceinline__ static storage from_float(float f) {
     return (storage)f32_to_bf16_bits(f);
   }
@@ -66,9 +69,20 @@ struct F32 {
     for (int i = 0; i < 4; ++i) out[i] = __uint_as_float(v[i]);
   }
   __device__ __forceinline__ static float load1(const storage* p) { return *p; }
+  __device__ __forceinline__ static uint32_t load_raw(const storage* p) { return __float_as_uint(*p); }
+  __device__ __forceinline__ static float from_raw(uint32_t r) { return __uint_as_float(r); }
   __device__ __forceinline__ static storage from_float(float f) { return f; }
   __device__ __forceinline__ static float round(float f) { return f; }
 };
+
+// An empty asm that claims to change v: arithmetic on a prefetched value
+// placed after it cannot be hoisted up to the load (where it would wait for
+// the data before later loads are issued); the wait for the load lands here.
+template <class T>
+__device__ __forceinline__ T opaque(T v) {
+  asm volatile("" : "+v"(v));
+  return v;
+}
 
 // 16-byte global load that bypasses nothing special (plain vector load).
 __device__ __forceinline__ u32x4_t load16(const void* p) {

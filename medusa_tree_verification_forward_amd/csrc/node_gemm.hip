@@ -108,38 +108,54 @@ __global__ void pack_weight_kernel(const typename ET::storage* __restrict__ W, i
   out[q] = v;
 }
 
-// QKV epilogue for one rotation pair (packed columns c1, c1 + 8) of row r.
+// QKV epilogue of packed column c1 (a rotation pair: columns c1 and c1 + 8
+// of the tile are elements i and i + Dh/2 of head h of q, k or v). What
+// depends on the column alone is computed once per lane: the destination of
+// row 0, the RoPE frequency theta^(-2i/Dh) in fp64, and whether to rotate
+// (q and k). The three output addresses go through opaque(): a
+// lane-dependent choice among kernel arguments would otherwise become a load
+// from the argument segment at every use; the chosen one is used as a global
+// (address space 1) pointer.
 template <class ET>
-__device__ __forceinline__ void qkv_finish(const GemmParams& p, int r, int c1, int pos,
-                                           double inv_freq, float x1, float x2) {
+struct QkvColumn {
   using St = typename ET::storage;
-  const int Dh = p.Dh, half = Dh >> 1;
-  const int blk = c1 / Dh, nl = c1 - blk * Dh;
-  const int i = 8 * (nl >> 4) + (nl & 7);
-  const int which = blk / p.H, h = blk - which * p.H;
-  if (which < 2) {
-    const double turns = (double)pos * inv_freq * 0.15915494309189535;   // 1/(2 pi)
-    const float ang = (float)((turns - rint(turns)) * 6.283185307179586);
-    float sn, cs;
-    __sincosf(ang, &sn, &cs);
-    const float y1 = x1 * cs - x2 * sn;
-    const float y2 = x2 * cs + x1 * sn;
-    x1 = y1;
-    x2 = y2;
+  typedef __attribute__((address_space(1))) St GSt;
+  GSt* o;         // element (row 0, i) of the destination
+  int rstride;    // elements per row: H * Dh
+  int half;       // Dh / 2
+  bool rope;
+  double inv_freq;
+  __device__ __forceinline__ QkvColumn(const GemmParams& p, int c1) {
+    const int Dh = p.Dh;
+    const int blk = c1 / Dh, nl = c1 - blk * Dh;
+    const int i = 8 * (nl >> 4) + (nl & 7);
+    const int which = blk / p.H, h = blk - which * p.H;
+    const uint64_t q = opaque((uint64_t)(uintptr_t)p.q_out);
+    const uint64_t k = opaque((uint64_t)(uintptr_t)p.k_out);
+    const uint64_t v = opaque((uint64_t)(uintptr_t)p.v_out);
+    o = (GSt*)(which == 0 ? q : (which == 1 ? k : v)) + (size_t)h * Dh + i;
+    rstride = p.H * Dh;
+    half = Dh >> 1;
+    rope = which < 2;
+    inv_freq = exp(-(2.0 * i / Dh) * p.log_theta);
   }
-  St* dst = reinterpret_cast<St*>(which == 0 ? p.q_out : (which == 1 ? p.k_out : p.v_out));
-  St* o = dst + ((size_t)r * p.H + h) * Dh + i;
-  o[0] = ET::from_float(x1);
-  o[half] = ET::from_float(x2);
-}
-
-// theta^(-2i/Dh) of the rotation pair whose first packed column is c1
-// (fp64; the same for every row, so computed once per column).
-__device__ __forceinline__ double rope_inv_freq(const GemmParams& p, int c1) {
-  const int nl = c1 % p.Dh;
-  const int i = 8 * (nl >> 4) + (nl & 7);
-  return exp(-(2.0 * i / p.Dh) * p.log_theta);
-}
+  // row r at position pos: rotate (x1, x2) by pos * inv_freq, round, store
+  __device__ __forceinline__ void store(int r, int pos, float x1, float x2) const {
+    if (rope) {
+      const double turns = (double)pos * inv_freq * 0.15915494309189535;   // 1/(2 pi)
+      const float ang = (float)((turns - rint(turns)) * 6.283185307179586);
+      float sn, cs;
+      __sincosf(ang, &sn, &cs);
+      const float y1 = x1 * cs - x2 * sn;
+      const float y2 = x2 * cs + x1 * sn;
+      x1 = y1;
+      x2 = y2;
+    }
+    GSt* const d = o + (size_t)r * rstride;
+    d[0] = ET::from_float(x1);
+    d[half] = ET::from_float(x2);
+  }
+};
 
 // y = x + acc, x = E[token of row r]: written as fp32 and storage type.
 template <class ET>
@@ -178,8 +194,62 @@ __device__ __forceinline__ void wg_coords(int& g, int& ks, int& pz) {
   ks = u / gridDim.x;
 }
 
+// Row data and outputs of the one-slice QKV / output-projection epilogue:
+// lane (li, lq) holds column col and rows m0 + 16 mt + 4 lq + j of the
+// accumulators. QKV: the rows' positions; output projection: the rows'
+// residual elements E[token], raw bits. Loads
+// are issued by load() and used only in finish() (opaque() keeps the
+// arithmetic on them there, so that a load issued early does not stall).
+template <class ET, int MT, int EPI>
+struct SliceRows {
+  int rv[MT][4];
+  uint32_t xr[MT][4];
+  __device__ __forceinline__ void load(const GemmParams& p, int m0, int lq, int col) {
+    using St = typename ET::storage;
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int r = min(m0 + 16 * mt + 4 * lq + j, p.M - 1);
+        rv[mt][j] = EPI == EPI_QKV ? p.pos[r] : min(max(p.tokens[r], 0), p.a_nrows - 1);
+      }
+    if constexpr (EPI != EPI_QKV) {
+      const int cc = min(col, p.N - 1);
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          xr[mt][j] = ET::load_raw(reinterpret_cast<const St*>(p.E) + (size_t)rv[mt][j] * p.N + cc);
+    }
+  }
+  __device__ __forceinline__ void finish(const GemmParams& p, const floatx4_t (&acc)[MT], int m0,
+                                         int li, int lq, int col) const {
+    if constexpr (EPI == EPI_QKV) {
+      // the rotation partner of packed column col is col + 8, held by lane li + 8
+      const QkvColumn<ET> cq(p, min(col, p.N - 1));
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const float other = __shfl_xor(acc[mt][j], 8);
+          const int r = m0 + 16 * mt + 4 * lq + j;
+          if (li < 8 && r < p.M && col < p.N) cq.store(r, opaque(rv[mt][j]), acc[mt][j], other);
+        }
+    } else {
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int r = m0 + 16 * mt + 4 * lq + j;
+          if (r < p.M && col < p.N)
+            oproj_store<ET>(p, r, col, ET::from_raw(opaque(xr[mt][j])) + acc[mt][j]);
+        }
+    }
+  }
+};
+
 template <class ET, int WV, int MT, int CH, int D, int EPI>
-__global__ __launch_bounds__(64 * WV, (WV == 4 && D <= 8) ? 4 : (WV <= 3 ? 1 : 2)) void node_gemm_kernel(
+__global__ __launch_bounds__(64 * WV, WV <= 3 ? 1 : 2) void node_gemm_kernel(
     GemmParams p) {
   using St = typename ET::storage;
   constexpr int PV = ET::kPerVec, KT = 4 * PV;   // k elements per tile
@@ -208,35 +278,49 @@ __global__ __launch_bounds__(64 * WV, (WV == 4 && D <= 8) ? 4 : (WV <= 3 ? 1 : 2
   __shared__ u32x4_t sA0[CH][MT][64];
   __shared__ u32x4_t sA1[CH][MT][64];
 
-  // LM head: node e of the pass's sequences (row of its parent, its token),
-  // node = -1 for roots and past the end
+  // LM head: node e of the pass's sequences (-1 for roots and past the end),
+  // its token and the row of its parent. The token and parent loads are in
+  // range for every e; what is computed from them is computed where used.
   const int rows_hi = min(p.M, m0 + 16 * MT);
   const int bl = m0 / max(p.T, 1), bh = (rows_hi - 1) / max(p.T, 1);
   const int nchild = EPI == EPI_LM ? (bh - bl + 1) * p.T : 0;
-  auto child_of = [&](int e, int& r, int& tok, int& node) {
-    r = -1;
-    tok = -1;
-    node = -1;
-    if (e < nchild) {
-      const int b = bl + e / p.T, cnode = e % p.T;
-      if (cnode >= 1) {
-        node = b * p.T + cnode;
-        tok = p.tokens[node];
-        r = b * p.T + min(max(p.parent[cnode], 0), p.T - 1);
-      }
-    }
+  auto child_node = [&](int e) {
+    const int cnode = e % p.T;
+    return e < nchild && cnode >= 1 ? (bl + e / p.T) * p.T + cnode : -1;
   };
-  int ch_r = -1, ch_tok = -1, ch_node = -1;
-  if constexpr (EPI == EPI_LM) child_of(lane, ch_r, ch_tok, ch_node);
+  auto child_raw = [&](int node, int& tok_raw, int& par_raw) {
+    const int nd = max(node, 0);   // node < M = B T for every e < nchild
+    tok_raw = p.tokens[nd];
+    par_raw = p.parent[nd % p.T];
+  };
+  // the first 64 nodes' loads go out before the stream (not with twelve
+  // m-tiles, whose registers are taken)
+  constexpr bool kEarlyChild = EPI == EPI_LM && MT <= 3;
+  int ch_node = -1, ch_tok_raw = 0, ch_par_raw = 0;
+  if constexpr (kEarlyChild) {
+    ch_node = child_node(lane);
+    child_raw(ch_node, ch_tok_raw, ch_par_raw);
+  }
 
-  // A fragment f = wave + WV i of a chunk is (k-tile f / MT, m-tile f % MT)
+  // A fragment f = wave + WV i of a chunk is (k-tile f / MT, m-tile f % MT).
+  // Gathered rows: every index load is issued before any is used (a load
+  // and its clamp per fragment would put one memory latency per fragment in
+  // front of the weight stream).
   const St* asrc[NAW];
+  {
+    int src[NAW];
 #pragma unroll
-  for (int i = 0; i < NAW; ++i) {
-    const int mt = (wave + WV * i) % MT;
-    const int r = min(m0 + 16 * mt + li, p.M - 1);
-    const int src = p.a_rows ? min(max(p.a_rows[r], 0), p.a_nrows - 1) : r;
-    asrc[i] = A + (size_t)src * p.lda + (size_t)kt_lo * KT + PV * lq;
+    for (int i = 0; i < NAW; ++i) src[i] = min(m0 + 16 * ((wave + WV * i) % MT) + li, p.M - 1);
+    if (p.a_rows) {
+      int raw[NAW];
+#pragma unroll
+      for (int i = 0; i < NAW; ++i) raw[i] = p.a_rows[src[i]];
+#pragma unroll
+      for (int i = 0; i < NAW; ++i) src[i] = min(max(raw[i], 0), p.a_nrows - 1);
+    }
+#pragma unroll
+    for (int i = 0; i < NAW; ++i)
+      asrc[i] = A + (size_t)src[i] * p.lda + (size_t)kt_lo * KT + PV * lq;
   }
   // A fragments of chunks c+1 and c+2 are in flight in two register sets
   u32x4_t ra0[NAW], ra1[NAW];
@@ -260,44 +344,20 @@ __global__ __launch_bounds__(64 * WV, (WV == 4 && D <= 8) ? 4 : (WV <= 3 ? 1 : 2
   for (int mt = 0; mt < MT; ++mt) acc[mt] = floatx4_t{0.f, 0.f, 0.f, 0.f};
   u32x4_t wr[D];
 
-  // Row data of the one-slice QKV / output-projection epilogue: positions
-  // (and the column's RoPE frequency) or residual values of the lane's rows
-  // m0 + 16 mt + 4 lq + j. Configurations with at most three waves run one
-  // workgroup per compute unit and hold them through the stream.
+  // Row data of the one-slice epilogue. Configurations with at most three
+  // waves run one workgroup per compute unit and hold it through the stream.
   constexpr bool kEarlyRows = (EPI == EPI_QKV || EPI == EPI_OPROJ) && WV <= 3;
-  int rv[MT][4];
-  float x[MT][4];
-  double inv_freq = 0.0;
-  auto load_rows = [&]() {
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int r = min(m0 + 16 * mt + 4 * lq + j, p.M - 1);
-        rv[mt][j] = EPI == EPI_QKV ? p.pos[r] : min(max(p.tokens[r], 0), p.a_nrows - 1);
-      }
-    if constexpr (EPI == EPI_QKV) inv_freq = rope_inv_freq(p, min(col, p.N - 1));
-  };
-  auto load_residual = [&]() {
-    const int cc = min(col, p.N - 1);
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        x[mt][j] = ET::load1(reinterpret_cast<const St*>(p.E) + (size_t)rv[mt][j] * p.N + cc);
-  };
-  if constexpr (kEarlyRows) {
-    if (KS == 1) {
-      load_rows();
-      if constexpr (EPI == EPI_OPROJ) load_residual();
-    }
-  }
+  SliceRows<ET, MT, EPI> rows;
 
   const int nch = (nloc + CH - 1) / CH;
   load_a(0, ra0);
   load_a(1, ra1);
 #pragma unroll
   for (int j = 0; j < D; ++j) wr[j] = load16_stream(wtile(min(j, nloc - 1)));
+  // row data held through the stream: loaded once the stream is under way
+  if constexpr (kEarlyRows) {
+    if (KS == 1) rows.load(p, m0, lq, col);
+  }
   store_a(sA0, ra0);
   load_a(2, ra0);
   lds_barrier();
@@ -350,31 +410,9 @@ __global__ __launch_bounds__(64 * WV, (WV == 4 && D <= 8) ? 4 : (WV <= 3 ? 1 : 2
 
   if constexpr (EPI == EPI_QKV || EPI == EPI_OPROJ) {
     if (KS == 1) {
-      // One slice: finish straight from the accumulators (lane: column col,
-      // rows m0 + 16 mt + 4 lq + j), the row data loaded before any store
-      // (before the stream, where the configuration has the registers).
-      if constexpr (!kEarlyRows) load_rows();
-      if constexpr (EPI == EPI_QKV) {
-        // the rotation partner of packed column col is col + 8, held by lane li + 8
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const float other = __shfl_xor(acc[mt][j], 8);
-            const int r = m0 + 16 * mt + 4 * lq + j;
-            if (li < 8 && r < p.M && col < p.N)
-              qkv_finish<ET>(p, r, col, rv[mt][j], inv_freq, acc[mt][j], other);
-          }
-      } else {
-        if constexpr (!kEarlyRows) load_residual();
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const int r = m0 + 16 * mt + 4 * lq + j;
-            if (r < p.M && col < p.N) oproj_store<ET>(p, r, col, x[mt][j] + acc[mt][j]);
-          }
-      }
+      // One slice: finish straight from the accumulators.
+      if constexpr (!kEarlyRows) rows.load(p, m0, lq, col);
+      rows.finish(p, acc, m0, li, lq, col);
       return;
     }
   }
@@ -412,7 +450,7 @@ __global__ __launch_bounds__(64 * WV, (WV == 4 && D <= 8) ? 4 : (WV <= 3 ? 1 : 2
         for (int i = 0; i < RB; ++i) pos[i] = p.pos[min(m0 + rl + RL * (i0 + i), p.M - 1)];
       };
       load_pos(0);
-      const double inv_freq = rope_inv_freq(p, min(c1, p.N - 1));
+      const QkvColumn<ET> cq(p, min(c1, p.N - 1));
       if (!last_to_arrive(p.counters + g * gridDim.z + pz, KS)) return;
 #pragma unroll 1
       for (int i0 = 0; i0 < RPT; i0 += RB) {
@@ -444,7 +482,7 @@ __global__ __launch_bounds__(64 * WV, (WV == 4 && D <= 8) ? 4 : (WV <= 3 ? 1 : 2
 #pragma unroll
           for (int i = 0; i < RB; ++i) {
             const int r = m0 + rl + RL * (i0 + i);
-            if (r < p.M) qkv_finish<ET>(p, r, c1, pos[i], inv_freq, x1[i], x2[i]);
+            if (r < p.M) cq.store(r, pos[i], x1[i], x2[i]);
           }
       }
     } else if constexpr (EPI == EPI_OPROJ) {
@@ -562,11 +600,15 @@ __global__ __launch_bounds__(64 * WV, (WV == 4 && D <= 8) ? 4 : (WV <= 3 ? 1 : 2
               make_float4(bv, sv, wv, __int_as_float(bi));
       }
       // logit of each tree node's token under its parent's row (this wave's
-      // columns); the first 64 nodes' (row, token) were loaded before the stream
+      // columns), 64 nodes at a time
       const int g1 = min(rows_hi, g0 + 16 * MG);
       for (int e0 = 0; e0 < nchild; e0 += 64) {
-        int r = ch_r, tok = ch_tok, node = ch_node;
-        if (e0 > 0) child_of(e0 + lane, r, tok, node);
+        int node = ch_node, tok = opaque(ch_tok_raw), par = opaque(ch_par_raw);
+        if (!kEarlyChild || e0 > 0) {
+          node = child_node(e0 + lane);
+          child_raw(node, tok, par);
+        }
+        const int r = (max(node, 0) / p.T) * p.T + min(max(par, 0), p.T - 1);
         if (node >= 0 && tok >= c0 && tok < c0 + 16 && r >= g0 && r < g1)
           p.child_logit[node] = lt(r - g0, tok - c0);
       }

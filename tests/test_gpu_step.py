@@ -24,6 +24,10 @@ SMALL = [
     # 13B-style wide tree (136 nodes, 9 query tiles), Dh 128
     scaled(WORKLOADS["vicuna13b_typical"], d=256, H=2, V=1999, L=520, L_range=(520, 520),
            entropy_target=None),
+    # mid-size widths (fp32 d 2560, bf16 d 3072): 160 and 192 output-projection
+    # stripes, K split over workgroups with the default tile
+    scaled(WORKLOADS["tiny_fp32"], d=2560, H=20, Dh=128, V=1000, L=200, L_range=(200, 200)),
+    scaled(WORKLOADS["vicuna7b_typical"], d=3072, H=24, V=2000, L=300, L_range=(300, 300)),
 ]
 
 FULL = ["vicuna7b_typical", "vicuna13b_typical", "vicuna7b_batch8_ragged"]
