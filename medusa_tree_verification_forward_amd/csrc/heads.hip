@@ -750,6 +750,19 @@ __global__ __launch_bounds__(kMergeThreads) void heads_merge_kernel(
   const bool lse_early = lse != nullptr && wave == 0 && G <= 64 * kLseRegs;
   float lm[kLseRegs], ls[kLseRegs];
   if (lse_early) lse_load(part_m + rec0, part_s + rec0, G, lm, ls);
+  // wave 0's tree data (plan rows lane + 64 i, all inside the plan's arrays;
+  // the plan is a kernel argument), loaded now and used at the end
+  constexpr int NQ = MAXT / 64;
+  int pdep[NQ], prank[NQ], pkv = 0, proot = 0;
+  if (tr.on && wave == 0) {
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) {
+      pdep[q] = tr.plan.depth[lane + 64 * q];
+      prank[q] = tr.plan.last_rank[lane + 64 * q];
+    }
+    pkv = tr.kv_len[b];
+    proot = tr.root_tok[b];
+  }
 
   float lv[SMAX];
   int li[SMAX];
@@ -823,15 +836,17 @@ __global__ __launch_bounds__(kMergeThreads) void heads_merge_kernel(
   if (!tr.on) return;
   // nodes of depth k+1 take rank r's token of this head (held by lane r)
   const int T = tr.plan.T;
-  for (int n0 = 0; n0 < T; n0 += 64) {
-    const int n = n0 + lane;
-    const bool mine = n < T && n >= 1 && tr.plan.depth[n] == k + 1;
-    const int r = n < T ? tr.plan.last_rank[n] : 0;
-    const int tok = __shfl(wi, min(r, S - 1));
+#pragma unroll
+  for (int q = 0; q < NQ; ++q) {
+    const int n = 64 * q + lane;
+    if (64 * q >= T) break;
+    const int dep = opaque(pdep[q]), rk = opaque(prank[q]);
+    const bool mine = n < T && n >= 1 && dep == k + 1;
+    const int tok = __shfl(wi, min(n < T ? rk : 0, S - 1));
     if (mine) tr.tokens[(size_t)b * T + n] = tok;
     if (k == 0 && n < T) {
-      tr.position_ids[(size_t)b * T + n] = tr.kv_len[b] + tr.plan.depth[n];
-      if (n == 0) tr.tokens[(size_t)b * T] = tr.root_tok[b];
+      tr.position_ids[(size_t)b * T + n] = opaque(pkv) + dep;
+      if (n == 0) tr.tokens[(size_t)b * T] = opaque(proot);
     }
   }
 }

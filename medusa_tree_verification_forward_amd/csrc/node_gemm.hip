@@ -139,13 +139,17 @@ struct QkvColumn {
     rope = which < 2;
     inv_freq = exp(-(2.0 * i / Dh) * p.log_theta);
   }
-  // row r at position pos: rotate (x1, x2) by pos * inv_freq, round, store
+  // cos and sin of the rotation at position pos
+  __device__ __forceinline__ void angle(int pos, float& cs, float& sn) const {
+    const double turns = (double)pos * inv_freq * 0.15915494309189535;   // 1/(2 pi)
+    const float ang = (float)((turns - rint(turns)) * 6.283185307179586);
+    __sincosf(ang, &sn, &cs);
+  }
+  // row r at position pos: rotate (x1, x2), round, store both elements
   __device__ __forceinline__ void store(int r, int pos, float x1, float x2) const {
     if (rope) {
-      const double turns = (double)pos * inv_freq * 0.15915494309189535;   // 1/(2 pi)
-      const float ang = (float)((turns - rint(turns)) * 6.283185307179586);
-      float sn, cs;
-      __sincosf(ang, &sn, &cs);
+      float cs, sn;
+      angle(pos, cs, sn);
       const float y1 = x1 * cs - x2 * sn;
       const float y2 = x2 * cs + x1 * sn;
       x1 = y1;
@@ -154,6 +158,19 @@ struct QkvColumn {
     GSt* const d = o + (size_t)r * rstride;
     d[0] = ET::from_float(x1);
     d[half] = ET::from_float(x2);
+  }
+  // One element of the pair: the first (second = false: x1 own, x2 the
+  // partner's) or the second (x2 own, x1 the partner's); the same rounding
+  // as store().
+  __device__ __forceinline__ void store_one(int r, int pos, float own, float partner,
+                                            bool second) const {
+    float y = own;
+    if (rope) {
+      float cs, sn;
+      angle(pos, cs, sn);
+      y = second ? own * cs + partner * sn : own * cs - partner * sn;
+    }
+    o[(size_t)r * rstride + (second ? half : 0)] = ET::from_float(y);
   }
 };
 
@@ -225,15 +242,18 @@ struct SliceRows {
   __device__ __forceinline__ void finish(const GemmParams& p, const floatx4_t (&acc)[MT], int m0,
                                          int li, int lq, int col) const {
     if constexpr (EPI == EPI_QKV) {
-      // the rotation partner of packed column col is col + 8, held by lane li + 8
+      // lanes li and li ^ 8 hold the two elements of a rotation pair: each
+      // rotates and stores its own (the pair's column constants are the same
+      // for both)
       const QkvColumn<ET> cq(p, min(col, p.N - 1));
+      const bool second = li >= 8;
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const float other = __shfl_xor(acc[mt][j], 8);
           const int r = m0 + 16 * mt + 4 * lq + j;
-          if (li < 8 && r < p.M && col < p.N) cq.store(r, opaque(rv[mt][j]), acc[mt][j], other);
+          if (r < p.M && col < p.N) cq.store_one(r, opaque(rv[mt][j]), acc[mt][j], other, second);
         }
     } else {
 #pragma unroll
