@@ -120,7 +120,7 @@ hipError_t launch_pack_weight(bool f32, const void* W, int rows, int K, int pair
                               hipStream_t st);
 int gemm_groups_max(int N);                // column groups of a node GEMM (upper bound)
 int gemm_passes_max(int M);                // row passes (upper bound)
-int lm_head_blocks(int N, int M);          // row records of the LM head (16-column stripes)
+int lm_head_blocks(int N, int M, bool f32);   // row records of the LM head (per stripe or workgroup)
 int lm_record_slots(int N);                // upper bound of lm_head_blocks over the configs
 int gemm_splits(int epi, int N, int K, bool f32, int M);   // K slices of the QKV / output projection of M rows
 hipError_t launch_qkv(const GemmParams& p, hipStream_t st);

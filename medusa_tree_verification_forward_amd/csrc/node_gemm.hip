@@ -43,6 +43,7 @@
 #include <stdlib.h>
 
 #include <type_traits>
+#include <utility>
 
 #include "common.h"
 #include "kernels.h"
@@ -644,6 +645,276 @@ __global__ __launch_bounds__(64 * WV, WV <= 3 ? 1 : 2) void node_gemm_kernel(
   }
 }
 
+// f(integral_constant<int, J>) for J = 0, 1, ... in order, unrolled
+template <class F, int... J>
+__device__ __forceinline__ void unroll_seq(F&& f, std::integer_sequence<int, J...>) {
+  (f(std::integral_constant<int, J>{}), ...);
+}
+
+// ---------------------------------------------------------------------------
+// QKV projection and LM head of more than 48 tree rows (13B trees, batches),
+// bf16. The WV waves of a workgroup split the rows -- wave w takes rows
+// m0 + 48 w .. + 48 (MW = 3 m-tiles) -- and share the weight tiles of the
+// workgroup's NS stripes: each k-tile's NS tiles are loaded once per
+// workgroup (wave w loads tiles w, w + WV, ...), written to one of two LDS
+// slots and read by every wave after one barrier per k-tile. Each wave
+// loads its own A fragments (its rows are nobody else's) straight from
+// global memory. Per k-tile a wave does MW x NS MFMAs: a B fragment read
+// from LDS feeds MW products and an A fragment NS.
+// Weights and A fragments are both loaded D k-tiles ahead: vector loads
+// complete in issue order, so waiting for an A fragment also waits for
+// every weight load issued before it, and the weight prefetch is only as
+// deep as the A prefetch. The LDS holds four k-tiles of weights: a step
+// publishes k-tile s + 2 and reads k-tile s + 1's B fragments into
+// registers before it multiplies k-tile s, so the one barrier per step
+// separates writes from reads two steps later and the LDS latency hides
+// behind the MFMAs instead of sitting between the barrier and them.
+//
+// LM epilogue: per m-tile the wave's 16 x 16 NS logit tile goes through LDS;
+// lane (r, part) = (lane % 16, lane / 16) scans row r's columns
+// part 4 NS .. + 4 NS in order, the four parts are merged in a fixed order
+// (rec_merge is commutative), and one record per (row, workgroup) is
+// written: the row-statistics merge reads ceil(stripes / NS) records a row.
+template <int WV, int NS, int EPI>
+__global__ __launch_bounds__(64 * WV, 1) void node_gemm_rows_kernel(GemmParams p) {
+  using ET = BF16;
+  using St = typename ET::storage;
+  static_assert(EPI == EPI_QKV || EPI == EPI_LM, "QKV projection or LM head");
+  constexpr int PV = ET::kPerVec, KT = 4 * PV;
+  constexpr int MW = 3;                    // m-tiles a wave
+  constexpr int NPW = (NS + WV - 1) / WV;  // weight tiles a wave loads per k-tile
+  constexpr int D = WV == 4 ? (NS <= 4 ? 12 : 8) : (NS <= 4 ? 8 : 4);   // k-tiles in flight
+  static_assert(D % 4 == 0, "ring depth (a multiple of the 4 LDS slots)");
+  constexpr int DW = D, DA = D;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int li = lane & 15, lq = lane >> 4;
+  int g, ks, pz;
+  wg_coords(g, ks, pz);
+  const int m0 = pz * 16 * MW * WV;
+  const int mw = m0 + 16 * MW * wave;      // the wave's first row
+  const bool rows_live = mw < p.M;         // wave-uniform
+  const int nkt = p.K / KT, ntiles = (p.N + 15) >> 4;
+  const int n0 = g * 16 * NS;
+
+  // A rows of the wave (gathered rows: every index load before any use)
+  const St* arow[MW];
+  {
+    int src[MW];
+#pragma unroll
+    for (int mt = 0; mt < MW; ++mt) src[mt] = min(mw + 16 * mt + li, p.M - 1);
+    if (p.a_rows) {
+      int raw[MW];
+#pragma unroll
+      for (int mt = 0; mt < MW; ++mt) raw[mt] = p.a_rows[src[mt]];
+#pragma unroll
+      for (int mt = 0; mt < MW; ++mt) src[mt] = min(max(raw[mt], 0), p.a_nrows - 1);
+    }
+#pragma unroll
+    for (int mt = 0; mt < MW; ++mt)
+      arow[mt] = reinterpret_cast<const St*>(p.A) + (size_t)src[mt] * p.lda + PV * lq;
+  }
+  // the wave's weight tiles: t = wave + WV u of the group (loads of t >= NS
+  // are clamped and never published); tile (nt, kt) is at kt * ntiles + nt
+  const u32x4_t* wbase[NPW];
+#pragma unroll
+  for (int u = 0; u < NPW; ++u) {
+    const int t = min(wave + WV * u, NS - 1);
+    wbase[u] = reinterpret_cast<const u32x4_t*>(p.W) + (size_t)min(g * NS + t, ntiles - 1) * 64 +
+               lane;
+  }
+  const size_t kstride = (size_t)ntiles * 64;
+  // k-tiles past the end are clamped: every step issues the same loads, and
+  // what they bring past the end is never used
+  auto load_w = [&](int kt, u32x4_t(&w)[NPW]) {
+    const size_t off = (size_t)min(kt, nkt - 1) * kstride;
+#pragma unroll
+    for (int u = 0; u < NPW; ++u) w[u] = load16_stream(wbase[u] + off);
+  };
+  auto load_a = [&](int kt, u32x4_t(&a)[MW]) {
+    const size_t off = (size_t)min(kt, nkt - 1) * KT;
+#pragma unroll
+    for (int mt = 0; mt < MW; ++mt) a[mt] = load16(arow[mt] + off);
+  };
+  __shared__ u32x4_t sW[4][NS][64];
+  auto publish = [&](int slot, const u32x4_t(&w)[NPW]) {
+#pragma unroll
+    for (int u = 0; u < NPW; ++u)
+      if (wave + WV * u < NS) sW[slot][wave + WV * u][lane] = w[u];
+  };
+
+  floatx4_t acc[MW][NS];
+#pragma unroll
+  for (int mt = 0; mt < MW; ++mt)
+#pragma unroll
+    for (int nt = 0; nt < NS; ++nt) acc[mt][nt] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+  u32x4_t wq[DW][NPW], aq[DA][MW];
+#pragma unroll
+  for (int j = 0; j < DW; ++j) load_w(j, wq[j]);
+#pragma unroll
+  for (int j = 0; j < DA; ++j) load_a(j, aq[j]);
+  // k-tiles 0 and 1 into slots 0 and 1, their registers refilled with
+  // k-tiles D and D + 1; then k-tile 0's B fragments
+  publish(0, wq[0]);
+  load_w(DW, wq[0]);
+  publish(1, wq[1]);
+  load_w(DW + 1, wq[1]);
+  lds_barrier();
+  u32x4_t b[NS];
+#pragma unroll
+  for (int nt = 0; nt < NS; ++nt) b[nt] = sW[0][nt][lane];
+
+  // Step s (j = s mod D): publish k-tile s + 2 (loaded D steps earlier) to
+  // slot (s + 2) & 3, last read two barriers ago, and refill its registers
+  // with k-tile s + 2 + D; read k-tile s + 1's B fragments (slot (s + 1) & 3,
+  // published before the last barrier); multiply k-tile s with the
+  // fragments read in the previous step (A from aq[s mod D]); refill aq
+  // with k-tile s + D; one barrier.
+  auto step = [&](int s, auto jc) {
+    constexpr int j = decltype(jc)::value;
+    publish((j + 2) & 3, wq[(j + 2) % DW]);
+    load_w(s + 2 + DW, wq[(j + 2) % DW]);
+    u32x4_t bn[NS];
+#pragma unroll
+    for (int nt = 0; nt < NS; ++nt) bn[nt] = sW[(j + 1) & 3][nt][lane];
+    if (rows_live) {
+#pragma unroll
+      for (int mt = 0; mt < MW; ++mt)
+#pragma unroll
+        for (int nt = 0; nt < NS; ++nt)
+          acc[mt][nt] = mfma16x16x32_bf16(aq[j % DA][mt], b[nt], acc[mt][nt]);
+    }
+#pragma unroll
+    for (int nt = 0; nt < NS; ++nt) b[nt] = bn[nt];
+    load_a(s + DA, aq[j % DA]);
+    lds_barrier();
+  };
+  int s0 = 0;
+  for (; s0 + DW <= nkt; s0 += DW)
+    unroll_seq([&](auto jc) { step(s0 + decltype(jc)::value, jc); },
+               std::make_integer_sequence<int, DW>{});
+  if (s0 < nkt)
+    unroll_seq(
+        [&](auto jc) {
+          if (s0 + decltype(jc)::value < nkt) step(s0 + decltype(jc)::value, jc);
+        },
+        std::make_integer_sequence<int, DW>{});
+
+  if constexpr (EPI == EPI_QKV) {
+    // lanes li and li ^ 8 hold the two elements of a rotation pair; each
+    // rotates and stores its own
+    int pos[MW][4];
+#pragma unroll
+    for (int mt = 0; mt < MW; ++mt)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) pos[mt][j] = p.pos[min(mw + 16 * mt + 4 * lq + j, p.M - 1)];
+    const bool second = li >= 8;
+#pragma unroll
+    for (int nt = 0; nt < NS; ++nt) {
+      const int col = n0 + 16 * nt + li;
+      const QkvColumn<ET> cq(p, min(col, p.N - 1));
+#pragma unroll
+      for (int mt = 0; mt < MW; ++mt)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const float other = __shfl_xor(acc[mt][nt][j], 8);
+          const int r = mw + 16 * mt + 4 * lq + j;
+          if (r < p.M && col < p.N) cq.store_one(r, pos[mt][j], acc[mt][nt][j], other, second);
+        }
+    }
+  } else {
+    if (p.logits_out)
+#pragma unroll
+      for (int mt = 0; mt < MW; ++mt)
+#pragma unroll
+        for (int nt = 0; nt < NS; ++nt)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const int r = mw + 16 * mt + 4 * lq + j, col = n0 + 16 * nt + li;
+            if (r < p.M && col < p.N) p.logits_out[(size_t)r * p.N + col] = acc[mt][nt][j];
+          }
+    if (!rows_live) return;
+    // tree nodes of the pass's sequences (-1 for roots and past the end)
+    const int rows_hi = min(p.M, m0 + 16 * MW * WV);
+    const int bl = m0 / max(p.T, 1), bh = (rows_hi - 1) / max(p.T, 1);
+    const int nchild = (bh - bl + 1) * p.T;
+    constexpr int LW = 16 * NS + 4;        // row stride (floats) of the tile
+    __shared__ float lt_s[WV][16][LW];
+    float(*lt)[LW] = lt_s[wave];
+    const int r = lane & 15, part = lane >> 4;
+    constexpr int PC = 4 * NS;              // columns a lane scans
+    const int G = gridDim.x;
+    // the pass's tree nodes (lane's node e0 + lane of each batch of 64): node,
+    // token and parent row, loaded once for all the wave's m-tiles
+    constexpr int kChildBatches = 8;        // 512 nodes; more are loaded per m-tile
+    int cnode[kChildBatches], ctok[kChildBatches], cpr[kChildBatches];
+    auto child_load = [&](int e, int& node, int& tok, int& pr) {
+      const int cn = e % p.T;
+      node = e < nchild && cn >= 1 ? (bl + e / p.T) * p.T + cn : -1;
+      const int nd = max(node, 0);
+      tok = p.tokens[nd];
+      pr = (nd / p.T) * p.T + min(max(p.parent[nd % p.T], 0), p.T - 1);
+    };
+#pragma unroll
+    for (int q = 0; q < kChildBatches; ++q)
+      if (64 * q < nchild) child_load(64 * q + lane, cnode[q], ctok[q], cpr[q]);
+#pragma unroll
+    for (int mt = 0; mt < MW; ++mt) {
+      if (mt > 0) wave_lds_sync();         // the previous tile's reads are done
+#pragma unroll
+      for (int nt = 0; nt < NS; ++nt)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) lt[4 * lq + j][16 * nt + li] = acc[mt][nt][j];
+      wave_lds_sync();
+      const int g0 = mw + 16 * mt;          // first row of the tile
+      const int c0 = n0 + part * PC;
+      float bv = kNegInf;
+      int bi = 0x7fffffff;
+#pragma unroll
+      for (int c = 0; c < PC; ++c) {
+        const float v = lt[r][part * PC + c];
+        if (c0 + c < p.N && v > bv) {
+          bv = v;
+          bi = c0 + c;
+        }
+      }
+      float sv = 0.f, wv = 0.f;
+#pragma unroll
+      for (int c = 0; c < PC; ++c)
+        if (c0 + c < p.N) {
+          const float z = (lt[r][part * PC + c] - bv) * p.inv_tau;
+          const float e = exp_e(z);
+          sv += e;
+          wv += e * z;
+        }
+      // parts (0, 1) and (2, 3), then the two pairs
+#pragma unroll
+      for (int off = 16; off <= 32; off <<= 1) {
+        const float m2 = __shfl_xor(bv, off), s2 = __shfl_xor(sv, off), w2 = __shfl_xor(wv, off);
+        const int a2 = __shfl_xor(bi, off);
+        rec_merge(bv, sv, wv, bi, m2, s2, w2, a2, p.inv_tau);
+      }
+      if (part == 0 && g0 + r < p.M)
+        *reinterpret_cast<float4*>(p.part + ((size_t)(g0 + r) * G + g) * 4) =
+            make_float4(bv, sv, wv, __int_as_float(bi));
+      // logit of each tree node's token under its parent's row, where both
+      // fall in this tile
+      const int g1 = min(p.M, g0 + 16);
+      auto child_store = [&](int node, int tok, int pr) {
+        if (node >= 0 && tok >= n0 && tok < n0 + 16 * NS && tok < p.N && pr >= g0 && pr < g1)
+          p.child_logit[node] = lt[pr - g0][tok - n0];
+      };
+#pragma unroll
+      for (int q = 0; q < kChildBatches; ++q)
+        if (64 * q < nchild) child_store(cnode[q], ctok[q], cpr[q]);
+      for (int e0 = 64 * kChildBatches; e0 < nchild; e0 += 64) {
+        int node, tok, pr;
+        child_load(e0 + lane, node, tok, pr);
+        child_store(node, tok, pr);
+      }
+    }
+  }
+}
+
 // Row statistics from the G records of row r: 256 threads, thread t takes
 // records t + 256 u in u order (every load of a round issued before any is
 // used), then a lane butterfly and the four waves in order.
@@ -745,8 +1016,51 @@ hipError_t launch_main(const GemmParams& p, int KS, hipStream_t st) {
   return hipGetLastError();
 }
 
+// Shape of the row-split kernel (bf16 QKV projection or LM head of more than
+// 48 rows): WV waves of 48 rows -- 4 (one pass of 192 rows) up to 192 rows,
+// else 8 (passes of 384) -- and NS stripes a workgroup -- the fewest of 3,
+// 4, 8 whose column groups fit one workgroup per compute unit, else 8.
+struct RowsCfg {
+  int wv, ns;
+};
+bool rows_config(int M, int N, int epi, bool f32, RowsCfg& c) {
+  if (f32 || M <= 48 || (epi != EPI_QKV && epi != EPI_LM)) return false;
+  c.wv = M <= 192 ? 4 : 8;
+  const int stripes = (N + 15) / 16, cus = device_cus();
+  c.ns = 8;
+  for (int ns : {3, 4, 8})
+    if ((stripes + ns - 1) / ns <= cus) {
+      c.ns = ns;
+      break;
+    }
+  return true;
+}
+
+template <int EPI>
+hipError_t launch_rows(const GemmParams& p, const RowsCfg& c, hipStream_t st) {
+  const dim3 grid((p.N + 16 * c.ns - 1) / (16 * c.ns), 1, (p.M + 48 * c.wv - 1) / (48 * c.wv));
+  const dim3 block(64 * c.wv);
+#define ROWS_CASE(WV_, NS_)                                                                    \
+  if (c.wv == WV_ && c.ns == NS_) {                                                            \
+    hipLaunchKernelGGL((node_gemm_rows_kernel<WV_, NS_, EPI>), grid, block, 0, st, p);         \
+    return hipGetLastError();                                                                  \
+  }
+  ROWS_CASE(4, 3)
+  ROWS_CASE(4, 4)
+  ROWS_CASE(4, 8)
+  ROWS_CASE(8, 3)
+  ROWS_CASE(8, 4)
+  ROWS_CASE(8, 8)
+#undef ROWS_CASE
+  return hipErrorInvalidValue;
+}
+
 template <int EPI>
 hipError_t launch_split(GemmParams p, hipStream_t st) {
+  if constexpr (EPI == EPI_QKV) {
+    RowsCfg rc;
+    if (rows_config(p.M, p.N, EPI, p.f32, rc)) return launch_rows<EPI>(p, rc, st);
+  }
   const int KS = gemm_splits(EPI, p.N, p.K, p.f32, p.M);
   p.group_cols = 16 * config_for(p.M, p.N, EPI).wv;
   return p.f32 ? launch_main<F32, EPI>(p, KS, st) : launch_main<BF16, EPI>(p, KS, st);
@@ -754,7 +1068,11 @@ hipError_t launch_split(GemmParams p, hipStream_t st) {
 
 }  // namespace
 
-int lm_head_blocks(int N, int M) {
+// Records per row the LM head writes: one per (row, 16-column stripe), or
+// with the row-split kernel one per (row, workgroup).
+int lm_head_blocks(int N, int M, bool f32) {
+  RowsCfg rc;
+  if (rows_config(M, N, EPI_LM, f32, rc)) return (N + 16 * rc.ns - 1) / (16 * rc.ns);
   const Config c = config_for(M, N, EPI_LM);
   return (N + 16 * c.wv - 1) / (16 * c.wv) * c.wv;
 }
@@ -815,10 +1133,15 @@ hipError_t launch_oproj(const GemmParams& p, hipStream_t st) {
 
 hipError_t launch_lm_head(GemmParams p, float* row_stats, int* row_argmax, hipStream_t st) {
   p.group_cols = 16 * config_for(p.M, p.N, EPI_LM).wv;
-  hipError_t e = p.f32 ? launch_main<F32, EPI_LM>(p, 1, st) : launch_main<BF16, EPI_LM>(p, 1, st);
+  RowsCfg rc;
+  hipError_t e;
+  if (rows_config(p.M, p.N, EPI_LM, p.f32, rc))
+    e = launch_rows<EPI_LM>(p, rc, st);
+  else
+    e = p.f32 ? launch_main<F32, EPI_LM>(p, 1, st) : launch_main<BF16, EPI_LM>(p, 1, st);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(row_stats_merge_kernel, dim3(p.M), dim3(kRowMergeThreads), 0, st, p.part,
-                     lm_head_blocks(p.N, p.M), p.inv_tau, row_stats, row_argmax);
+                     lm_head_blocks(p.N, p.M, p.f32), p.inv_tau, row_stats, row_argmax);
   return hipGetLastError();
 }
 
