@@ -73,7 +73,7 @@ class StepArgs(ctypes.Structure):
         ("k_tree", _P), ("v_tree", _P), ("y", _P), ("row_stats", _P), ("row_argmax", _P),
         ("child_logit", _P), ("verify_logits_or_null", _P), ("accept_len", _P),
         ("best_path", _P), ("last_node", _P), ("out_tokens", _P), ("next_root", _P),
-        ("h_next", _P), ("kv_len_out_or_null", _P),
+        ("h_next", _P), ("kv_len_out_or_null", _P), ("W2_packed_or_null", _P),
     ]
 
 _P = ctypes.c_void_p
@@ -86,7 +86,7 @@ _SIGS = {
     "medusa_last_error": ([], ctypes.c_char_p),
     "medusa_version": ([], ctypes.c_char_p),
     "medusa_workspace_bytes": ([_SP], _SZ),
-    "medusa_heads_forward": ([_SP, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P], _I),
+    "medusa_heads_forward": ([_SP, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P], _I),
     "medusa_build_tree": ([_SP, _P, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P], _I),
     "medusa_tree_attention": ([_SP, _P, _P, _P, _P, _P, _P, _P, _F, _P, _P, _SZ, _P], _I),
     "medusa_packed_weight_bytes": ([_SP, _I], _SZ),
@@ -160,9 +160,10 @@ def workspace_bytes(shape: Shape) -> int:
 
 
 def heads_forward(shape, h, W1, W2, topk_ids, topk_logits, workspace, *, b1=None,
-                  head_lse=None, head_logits=None, z=None, stream=None):
+                  head_lse=None, head_logits=None, z=None, W2_packed=None, stream=None):
     _check(_lib.medusa_heads_forward(
-        ctypes.byref(shape), _ptr(h), _ptr(W1), _ptr(b1), _ptr(W2), _ptr(topk_ids),
+        ctypes.byref(shape), _ptr(h), _ptr(W1), _ptr(b1), _ptr(W2), _ptr(W2_packed),
+        _ptr(topk_ids),
         _ptr(topk_logits), _ptr(head_lse), _ptr(head_logits), _ptr(z), _ptr(workspace),
         workspace.numel() * workspace.element_size(), _stream(stream)))
 
@@ -238,6 +239,18 @@ def packed_copy(shape, kind, W, rows, *, stream=None):
     n = packed_weight_bytes(shape, rows)
     out = torch.empty(n // W.element_size(), dtype=W.dtype, device=W.device)
     pack_weight(shape, kind, W, rows, out, stream=stream)
+    return out
+
+
+def packed_heads_w2(shape, W2, *, stream=None):
+    """W2 [K][V][d] packed per head (medusa_heads_forward's W2_packed_or_null):
+    each head's [V][d] block packed plain (rows = V), heads one after another."""
+    import torch
+    K, V = W2.shape[0], W2.shape[1]
+    per = packed_weight_bytes(shape, V) // W2.element_size()
+    out = torch.empty(K * per, dtype=W2.dtype, device=W2.device)
+    for k in range(K):
+        pack_weight(shape, PACK_PLAIN, W2[k], V, out[k * per:(k + 1) * per], stream=stream)
     return out
 
 

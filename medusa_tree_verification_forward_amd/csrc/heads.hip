@@ -583,15 +583,17 @@ __global__ __launch_bounds__(256) void act_frag_kernel(const float* __restrict__
 // tile reads half of each 128-byte line and the next block the other half,
 // and with the non-temporal hint the line was often gone by then (37% more
 // HBM traffic).
+// `step`: elements from one column block of a lane's row piece to the next
+// (32 in a row-major W, ntiles * 512 in a packed one).
 template <int NG, int DS>
-__device__ __forceinline__ void tile_stream(const uint16_t* const (&wp)[NG],
+__device__ __forceinline__ void tile_stream(const uint16_t* const (&wp)[NG], size_t step,
                                             const u32x4_t* __restrict__ ap, int nt,
                                             floatx4_t (&acc)[NG]) {
   u32x4_t wr[DS][NG], ar[DS];
 #pragma unroll
   for (int j = 0; j < DS; ++j) {
 #pragma unroll
-    for (int g = 0; g < NG; ++g) wr[j][g] = load16(wp[g] + 32 * j);
+    for (int g = 0; g < NG; ++g) wr[j][g] = load16(wp[g] + step * j);
     ar[j] = load16(ap + 64 * j);
   }
 #pragma unroll
@@ -604,7 +606,7 @@ __device__ __forceinline__ void tile_stream(const uint16_t* const (&wp)[NG],
 #pragma unroll
       for (int g = 0; g < NG; ++g) {
         acc[g] = mfma16x16x32_bf16(ar[j], wr[j][g], acc[g]);
-        wr[j][g] = load16(wp[g] + 32 * tn);
+        wr[j][g] = load16(wp[g] + step * tn);
       }
       ar[j] = load16(ap + 64 * tn);
     }
@@ -641,7 +643,7 @@ __global__ __launch_bounds__(kHeadWaves * 64, 4) void heads_w1_tile_kernel(
   const float bias = b1 ? b1[row] : 0.f;
   const uint16_t* wp[1] = {W1 + (size_t)row * d + 32 * per * part + 8 * q};
   floatx4_t acc[1];
-  tile_stream<1, DS>(wp, hfrag + (size_t)per * part * 64 + lane, per, acc);
+  tile_stream<1, DS>(wp, 32, hfrag + (size_t)per * part * 64 + lane, per, acc);
   if constexpr (KS > 1) {
     __shared__ floatx4_t red[RS][KS - 1][64];
     if (part > 0) red[set][part - 1][lane] = acc[0];
@@ -676,7 +678,8 @@ __global__ __launch_bounds__(kHeadWaves * 64, 4) void heads_w1_tile_kernel(
 template <int NG, int DS>
 __global__ __launch_bounds__(kHeadWaves * 64, 4) void heads_w2_tile_kernel(
     int B, int b0, int K, int V, int d, const uint16_t* __restrict__ W2,
-    const u32x4_t* __restrict__ zfrag, int S, float* __restrict__ head_logits,
+    const uint16_t* __restrict__ W2p, const u32x4_t* __restrict__ zfrag, int S,
+    float* __restrict__ head_logits,
     float* __restrict__ part_val, int* __restrict__ part_id, float* __restrict__ part_m,
     float* __restrict__ part_s, int G) {
   __shared__ float xs[kHeadWaves * kTileVecs * (2 * MAXS_LDS + 2)];
@@ -692,11 +695,25 @@ __global__ __launch_bounds__(kHeadWaves * 64, 4) void heads_w2_tile_kernel(
   for (int b = 0; b < kTileVecs; ++b) win[b] = kNegInf;
   if (nrows > 0) {
     const uint16_t* wp[NG];
+    size_t step = 32;
+    if (W2p) {
+      // packed tiles (16 rows x 32 columns, 64 lane pieces, k-major within
+      // each head): lane (j, q)'s piece of tile (row block, column block t)
+      // is row j, columns 32 t + 8 q .. + 7 -- the same fragment
+      const int ntiles = (V + 15) / 16;
+      step = (size_t)ntiles * 512;
+      const uint16_t* head = W2p + (size_t)k * ntiles * 16 * d;
 #pragma unroll
-    for (int tg = 0; tg < NG; ++tg)
-      wp[tg] = W2 + ((size_t)k * V + rb + (size_t)min(16 * tg + j, nrows - 1) * rstride) * d + 8 * q;
+      for (int tg = 0; tg < NG; ++tg)
+        wp[tg] = head + ((size_t)min(rb / 16 + tg, ntiles - 1) * 64 + lane) * 8;
+    } else {
+#pragma unroll
+      for (int tg = 0; tg < NG; ++tg)
+        wp[tg] = W2 + ((size_t)k * V + rb + (size_t)min(16 * tg + j, nrows - 1) * rstride) * d +
+                 8 * q;
+    }
     floatx4_t acc[NG];
-    tile_stream<NG, DS>(wp, zfrag + (size_t)k * (d / 32) * 64 + lane, d / 32, acc);
+    tile_stream<NG, DS>(wp, step, zfrag + (size_t)k * (d / 32) * 64 + lane, d / 32, acc);
 #pragma unroll
     for (int tg = 0; tg < NG; ++tg) {
       const float v0 = acc[tg][0] + acc[tg][1], v1 = acc[tg][2] + acc[tg][3];
@@ -907,9 +924,11 @@ hipError_t launch_heads_nb(const HeadsArgs& a, int b0, hipStream_t st) {
 // Batched passes (3 or more vectors, bf16): W1 split over 4 waves (fewer
 // where d does not allow) with 8 column blocks in flight, W2 in tile rows of
 // two (32 rows a wave) with 4 column blocks in flight (2 where d does not
-// allow). At batch 8 the step took 746 us with these against 755-779 for
-// 16-64 rows a wave and 4-16 tiles in flight: fragment-shaped reads lose
-// DRAM locality as more of them are outstanding.
+// allow). From a row-major W2 the batch-8 step took 746 us with these
+// against 755-779 for 16-64 rows a wave and 4-16 tiles in flight:
+// fragment-shaped reads lose DRAM locality as more of them are outstanding.
+// From packed tiles the W2 pass takes 237 us against 286 (row-major); 3
+// tile rows a wave (835 workgroups) took 254, 4 spill registers (305).
 constexpr int kW2TileNg = 2;
 // rows per W2 workgroup of the batched pass
 int w2_tile_rows() { return kHeadWaves * 16 * kW2TileNg; }
@@ -947,9 +966,10 @@ hipError_t launch_heads_tile(const HeadsArgs& a, int b0, int G, hipStream_t st) 
     if (e != hipSuccess) return e;
   }
   const uint16_t* W2 = reinterpret_cast<const uint16_t*>(a.W2);
+  const uint16_t* W2p = reinterpret_cast<const uint16_t*>(a.W2_packed);
 #define W2_TILE(NG, DS)                                                                       \
   hipLaunchKernelGGL((heads_w2_tile_kernel<NG, DS>), dim3(G, a.K), dim3(kHeadWaves * 64), 0, st, \
-                     a.B, b0, a.K, a.V, d, W2, zfrag, a.S, a.head_logits, a.part_val,          \
+                     a.B, b0, a.K, a.V, d, W2, W2p, zfrag, a.S, a.head_logits, a.part_val,     \
                      a.part_id, a.part_m, a.part_s, G)
   // d is a multiple of 64: nblk is even
   if (nblk % 4 == 0)

@@ -31,6 +31,7 @@ struct HeadsArgs {
   const void* W1;
   const float* b1;        // may be null
   const void* W2;
+  const void* W2_packed;  // or null: each head's W2_k packed (plain, rows = V), heads in order
   float* z;               // [B][K][d]
   float* head_logits;     // [B][K][V] or null
   int* topk_ids;          // [B][K][S]

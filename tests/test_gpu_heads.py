@@ -12,7 +12,7 @@ from gpu_helpers import assert_close, dev, host, poisoned, require_gpu, workspac
 pytestmark = pytest.mark.gpu
 
 
-def _run_heads(w, inp, with_logits=True):
+def _run_heads(w, inp, with_logits=True, packed=False):
     import torch
     import medusa_tree_verification_forward_amd as M
     require_gpu()
@@ -25,8 +25,10 @@ def _run_heads(w, inp, with_logits=True):
     lse = poisoned((B, K), torch.float32)
     logits = poisoned((B, K, w.V), torch.float32) if with_logits else None
     z = poisoned((B, K, w.d), torch.float32)
-    M.heads_forward(shape, dev(inp["h"]), dev(inp["W1"]), dev(inp["W2"]), ids, vals, ws,
-                    head_lse=lse, head_logits=logits, z=z)
+    W2 = dev(inp["W2"])
+    W2p = M.packed_heads_w2(shape, W2) if packed else None
+    M.heads_forward(shape, dev(inp["h"]), dev(inp["W1"]), W2, ids, vals, ws,
+                    head_lse=lse, head_logits=logits, z=z, W2_packed=W2p)
     torch.cuda.synchronize()
     out = dict(ids=host(ids), vals=host(vals), lse=host(lse), z=host(z))
     if with_logits:
@@ -87,6 +89,20 @@ def test_heads_small_shapes(w):
     g = _run_heads(w, inp)
     _check_topk_on_own_logits(g)
     _check_against_oracle(w, inp, g)
+
+
+BATCHED = [w for w in SMALL if w.dtype == "bf16" and w.B >= 3]
+
+
+@pytest.mark.parametrize("w", BATCHED, ids=lambda w: f"{w.name}-d{w.d}-V{w.V}-B{w.B}")
+def test_heads_packed_w2_equals_row_major(w):
+    # The batched passes read W2 in packed tiles when given them: the same
+    # fragments in the same order, so every output is bit-identical.
+    inp = make_inputs(w, only=("W1", "W2"))
+    g = _run_heads(w, inp)
+    gp = _run_heads(w, inp, packed=True)
+    for key in g:
+        assert np.array_equal(g[key], gp[key]), key
 
 
 def test_heads_bias_and_identity_init():
@@ -152,6 +168,10 @@ def test_heads_full_size_batch8():
     inp = make_inputs(w, only=("W1", "W2"))
     g = _run_heads(w, inp)
     _check_topk_on_own_logits(g)
+    # the packed-W2 pass (as the step runs it) gives the same bits
+    gp = _run_heads(w, inp, packed=True)
+    for key in g:
+        assert np.array_equal(g[key], gp[key]), key
     z = np.empty((w.B, w.K, w.d))
     for k in range(w.K):
         z[:, k] = OH.residual_block(inp["W1"][k], inp["h"].astype(np.float64))
