@@ -111,6 +111,10 @@ size_t medusa_workspace_bytes(const medusa_shape* shape);
  *
  *   h            [B][d] fp32
  *   W1           [K][d][d] elem;   b1_or_null [K][d] fp32 (NULL = no bias)
+ *   W1_packed_or_null  W1 viewed as one [K d][d] matrix, packed by
+ *                medusa_pack_weight (MEDUSA_PACK_PLAIN, rows = K d); NULL =
+ *                none. Read instead of W1 by batches of 3 to 8 sequences in
+ *                bf16; ignored otherwise.
  *   W2           [K][V][d] elem
  *   W2_packed_or_null  the K heads' W2_k each packed by medusa_pack_weight
  *                (MEDUSA_PACK_PLAIN, rows = V), head k at byte
@@ -125,8 +129,8 @@ size_t medusa_workspace_bytes(const medusa_shape* shape);
  *   z            [B][K][d] fp32        (out, may be NULL)
  */
 int medusa_heads_forward(const medusa_shape* shape, const float* h, const void* W1,
-                         const float* b1_or_null, const void* W2,
-                         const void* W2_packed_or_null, int32_t* topk_ids,
+                         const void* W1_packed_or_null, const float* b1_or_null,
+                         const void* W2, const void* W2_packed_or_null, int32_t* topk_ids,
                          float* topk_logits, float* head_lse_or_null,
                          float* head_logits_or_null, float* z_or_null, void* workspace,
                          size_t workspace_bytes, void* stream);
@@ -390,8 +394,10 @@ typedef struct {
    * repeated over the same prefix (the appended cache rows are rewritten at
    * the same positions) without restoring kv_len in between. */
   int32_t* kv_len_out_or_null;
-  /* heads: W2 packed per head, as medusa_heads_forward's W2_packed_or_null */
+  /* heads: packed copies, as medusa_heads_forward's W2_packed_or_null and
+   * W1_packed_or_null */
   const void* W2_packed_or_null;
+  const void* W1_packed_or_null;
 } medusa_step_args;
 
 int medusa_step(const medusa_shape* shape, const medusa_step_args* args, void* workspace,

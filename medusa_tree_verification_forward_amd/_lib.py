@@ -74,6 +74,7 @@ class StepArgs(ctypes.Structure):
         ("child_logit", _P), ("verify_logits_or_null", _P), ("accept_len", _P),
         ("best_path", _P), ("last_node", _P), ("out_tokens", _P), ("next_root", _P),
         ("h_next", _P), ("kv_len_out_or_null", _P), ("W2_packed_or_null", _P),
+        ("W1_packed_or_null", _P),
     ]
 
 _P = ctypes.c_void_p
@@ -86,7 +87,8 @@ _SIGS = {
     "medusa_last_error": ([], ctypes.c_char_p),
     "medusa_version": ([], ctypes.c_char_p),
     "medusa_workspace_bytes": ([_SP], _SZ),
-    "medusa_heads_forward": ([_SP, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P], _I),
+    "medusa_heads_forward": ([_SP, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P],
+                             _I),
     "medusa_build_tree": ([_SP, _P, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P], _I),
     "medusa_tree_attention": ([_SP, _P, _P, _P, _P, _P, _P, _P, _F, _P, _P, _SZ, _P], _I),
     "medusa_packed_weight_bytes": ([_SP, _I], _SZ),
@@ -160,9 +162,11 @@ def workspace_bytes(shape: Shape) -> int:
 
 
 def heads_forward(shape, h, W1, W2, topk_ids, topk_logits, workspace, *, b1=None,
-                  head_lse=None, head_logits=None, z=None, W2_packed=None, stream=None):
+                  head_lse=None, head_logits=None, z=None, W1_packed=None, W2_packed=None,
+                  stream=None):
     _check(_lib.medusa_heads_forward(
-        ctypes.byref(shape), _ptr(h), _ptr(W1), _ptr(b1), _ptr(W2), _ptr(W2_packed),
+        ctypes.byref(shape), _ptr(h), _ptr(W1), _ptr(W1_packed), _ptr(b1), _ptr(W2),
+        _ptr(W2_packed),
         _ptr(topk_ids),
         _ptr(topk_logits), _ptr(head_lse), _ptr(head_logits), _ptr(z), _ptr(workspace),
         workspace.numel() * workspace.element_size(), _stream(stream)))
@@ -240,6 +244,13 @@ def packed_copy(shape, kind, W, rows, *, stream=None):
     out = torch.empty(n // W.element_size(), dtype=W.dtype, device=W.device)
     pack_weight(shape, kind, W, rows, out, stream=stream)
     return out
+
+
+def packed_heads_w1(shape, W1, *, stream=None):
+    """W1 [K][d][d] packed as one [K d][d] matrix (medusa_heads_forward's
+    W1_packed_or_null)."""
+    K, d = W1.shape[0], W1.shape[1]
+    return packed_copy(shape, PACK_PLAIN, W1.reshape(K * d, d), K * d, stream=stream)
 
 
 def packed_heads_w2(shape, W2, *, stream=None):

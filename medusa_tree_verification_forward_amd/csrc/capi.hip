@@ -252,7 +252,8 @@ namespace {
 // Heads, optionally writing the tree tokens and positions in the merge
 // (fuse_plan != null: top-s drafting inside the composite step).
 int heads_impl(const medusa_shape* shape, const float* h, const void* W1,
-               const float* b1_or_null, const void* W2, const void* W2_packed_or_null,
+               const void* W1_packed_or_null, const float* b1_or_null, const void* W2,
+               const void* W2_packed_or_null,
                int32_t* topk_ids, float* topk_logits,
                float* head_lse_or_null, float* head_logits_or_null, float* z_or_null,
                void* workspace, size_t workspace_bytes, void* stream, const TreePlan* fuse_plan,
@@ -267,6 +268,7 @@ int heads_impl(const medusa_shape* shape, const float* h, const void* W1,
   REQUIRE_PTR(topk_ids);
   REQUIRE_PTR(topk_logits);
   OPTIONAL_PTR(b1_or_null);
+  OPTIONAL_PTR(W1_packed_or_null);
   OPTIONAL_PTR(W2_packed_or_null);
   OPTIONAL_PTR(head_lse_or_null);
   OPTIONAL_PTR(head_logits_or_null);
@@ -284,6 +286,7 @@ int heads_impl(const medusa_shape* shape, const float* h, const void* W1,
   a.S = shape->s_max;
   a.h = h;
   a.W1 = W1;
+  a.W1_packed = W1_packed_or_null;
   a.b1 = b1_or_null;
   a.W2 = W2;
   a.W2_packed = W2_packed_or_null;
@@ -323,12 +326,13 @@ int heads_impl(const medusa_shape* shape, const float* h, const void* W1,
 extern "C" {
 
 int medusa_heads_forward(const medusa_shape* shape, const float* h, const void* W1,
-                         const float* b1_or_null, const void* W2,
-                         const void* W2_packed_or_null, int32_t* topk_ids,
+                         const void* W1_packed_or_null, const float* b1_or_null,
+                         const void* W2, const void* W2_packed_or_null, int32_t* topk_ids,
                          float* topk_logits, float* head_lse_or_null,
                          float* head_logits_or_null, float* z_or_null, void* workspace,
                          size_t workspace_bytes, void* stream) {
-  return heads_impl(shape, h, W1, b1_or_null, W2, W2_packed_or_null, topk_ids, topk_logits,
+  return heads_impl(shape, h, W1, W1_packed_or_null, b1_or_null, W2, W2_packed_or_null,
+                    topk_ids, topk_logits,
                     head_lse_or_null,
                     head_logits_or_null, z_or_null, workspace, workspace_bytes, stream, nullptr,
                     nullptr, nullptr, nullptr, nullptr, false);
@@ -824,7 +828,8 @@ int step_impl(const medusa_shape* shape, const medusa_step_args* x, void* worksp
       return fail(MEDUSA_ERR_ARG, "eps, delta must be >= 0");
   }
   // 1. heads (+ tree tokens and positions)
-  rc = heads_impl(shape, x->h, x->W1, x->b1_or_null, x->W2, x->W2_packed_or_null, x->topk_ids,
+  rc = heads_impl(shape, x->h, x->W1, x->W1_packed_or_null, x->b1_or_null, x->W2,
+                  x->W2_packed_or_null, x->topk_ids,
                   x->topk_logits,
                   x->head_lse_or_null, x->head_logits_or_null, x->z_or_null, workspace,
                   workspace_bytes, stream,

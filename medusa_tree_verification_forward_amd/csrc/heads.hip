@@ -625,7 +625,8 @@ __device__ __forceinline__ void tile_stream(const uint16_t* const (&wp)[NG], siz
 template <int KS, int DS>
 __global__ __launch_bounds__(kHeadWaves * 64, 4) void heads_w1_tile_kernel(
     const float* __restrict__ h, int B, int b0, int K, int d, const uint16_t* __restrict__ W1,
-    const float* __restrict__ b1, const u32x4_t* __restrict__ hfrag, float* __restrict__ z,
+    const uint16_t* __restrict__ W1p, const float* __restrict__ b1,
+    const u32x4_t* __restrict__ hfrag, float* __restrict__ z,
     uint16_t* __restrict__ zfrag) {
   constexpr int RS = kHeadWaves / KS;   // row sets of 16 per workgroup
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -641,9 +642,20 @@ __global__ __launch_bounds__(kHeadWaves * 64, 4) void heads_w1_tile_kernel(
 #pragma unroll
   for (int e = 0; e < 2; ++e) hres[e] = h[(size_t)(b0 + min(2 * q + e, nb - 1)) * d + i];
   const float bias = b1 ? b1[row] : 0.f;
-  const uint16_t* wp[1] = {W1 + (size_t)row * d + 32 * per * part + 8 * q};
+  // row-major W1, or W1 packed as one [K d][d] matrix (tile (nt, kt) at
+  // kt * ntiles + nt, lane (j, q)'s piece = row j, columns 32 kt + 8 q ..)
+  const uint16_t* wp[1];
+  size_t step = 32;
+  if (W1p) {
+    const int ntiles = total / 16;
+    const int nt = min((int)(blockIdx.x * RS + set), ntiles - 1);
+    step = (size_t)ntiles * 512;
+    wp[0] = W1p + (((size_t)per * part * ntiles + nt) * 64 + lane) * 8;
+  } else {
+    wp[0] = W1 + (size_t)row * d + 32 * per * part + 8 * q;
+  }
   floatx4_t acc[1];
-  tile_stream<1, DS>(wp, 32, hfrag + (size_t)per * part * 64 + lane, per, acc);
+  tile_stream<1, DS>(wp, step, hfrag + (size_t)per * part * 64 + lane, per, acc);
   if constexpr (KS > 1) {
     __shared__ floatx4_t red[RS][KS - 1][64];
     if (part > 0) red[set][part - 1][lane] = acc[0];
@@ -948,7 +960,8 @@ hipError_t launch_heads_tile(const HeadsArgs& a, int b0, int G, hipStream_t st) 
 #define W1_TILE(KS, DS)                                                                        \
   hipLaunchKernelGGL((heads_w1_tile_kernel<KS, DS>),                                           \
                      dim3((total + 16 * (kHeadWaves / KS) - 1) / (16 * (kHeadWaves / KS))),    \
-                     dim3(kHeadWaves * 64), 0, st, a.h, a.B, b0, a.K, d, W1, a.b1, hfrag, a.z, \
+                     dim3(kHeadWaves * 64), 0, st, a.h, a.B, b0, a.K, d, W1,                   \
+                     reinterpret_cast<const uint16_t*>(a.W1_packed), a.b1, hfrag, a.z,          \
                      zf16)
   if (nblk % 32 == 0)
     W1_TILE(4, 8);

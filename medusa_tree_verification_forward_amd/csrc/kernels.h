@@ -29,6 +29,7 @@ struct HeadsArgs {
   int B, d, V, K, S;
   const float* h;
   const void* W1;
+  const void* W1_packed;  // or null: W1 packed as one [K d][d] matrix (plain)
   const float* b1;        // may be null
   const void* W2;
   const void* W2_packed;  // or null: each head's W2_k packed (plain, rows = V), heads in order

@@ -67,7 +67,9 @@ class VerifyStep:
                                                 ("W_lm", L.PACK_PLAIN, V))}
         # batches of 3 or more bf16 sequences stream W2 as packed tiles
         # (a second copy of W2; the per-row passes of 1-2 sequences read W2)
-        self.w2_packed = L.packed_heads_w2(self.shape, dev["W2"]) if (B >= 3 and not f32) else None
+        batched = B >= 3 and not f32
+        self.w2_packed = L.packed_heads_w2(self.shape, dev["W2"]) if batched else None
+        self.w1_packed = L.packed_heads_w1(self.shape, dev["W1"]) if batched else None
         self.kv_len0 = dev["kv_len"].clone()
         kv = np.asarray(inputs["kv_len"])
         self._uniform_kv = int(kv[0]) if np.all(kv == kv[0]) else None
@@ -110,7 +112,7 @@ class VerifyStep:
         o, i = self.out, self.inp
         L.heads_forward(self.shape, i["h"], i["W1"], i["W2"], o["topk_ids"], o["topk_logits"],
                         self.ws, head_lse=o["head_lse"], head_logits=o["head_logits"], z=o["z"],
-                        W2_packed=self.w2_packed, stream=stream)
+                        W1_packed=self.w1_packed, W2_packed=self.w2_packed, stream=stream)
 
     def tree(self, stream=None, topology: bool = False):
         o, i = self.out, self.inp
@@ -174,6 +176,7 @@ class VerifyStep:
         a = L.StepArgs()
         a.h, a.W1, a.W2 = p(i["h"]), p(i["W1"]), p(i["W2"])
         a.W2_packed_or_null = p(self.w2_packed)
+        a.W1_packed_or_null = p(self.w1_packed)
         a.b1_or_null = p(i.get("b1"))
         a.tree_ranks_host = self._ranks_host.ctypes.data if self._ranks_host.size else None
         a.draft_mode = L.DRAFT_SAMPLE if exact else L.DRAFT_TOPK

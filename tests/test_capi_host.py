@@ -116,8 +116,8 @@ def test_heads_workspace_too_small():
     M = _lib()
     shape = _shape(M)
     lib = M._lib._lib
-    rc = lib.medusa_heads_forward(ctypes.byref(shape), FAKE, FAKE, None, FAKE, None, FAKE, FAKE,
-                                  None, None, None, FAKE, 16, None)
+    rc = lib.medusa_heads_forward(ctypes.byref(shape), FAKE, FAKE, None, None, FAKE, None, FAKE,
+                                  FAKE, None, None, None, FAKE, 16, None)
     assert rc == M._lib.ERR_WORKSPACE
 
 

@@ -25,10 +25,11 @@ def _run_heads(w, inp, with_logits=True, packed=False):
     lse = poisoned((B, K), torch.float32)
     logits = poisoned((B, K, w.V), torch.float32) if with_logits else None
     z = poisoned((B, K, w.d), torch.float32)
-    W2 = dev(inp["W2"])
+    W1, W2 = dev(inp["W1"]), dev(inp["W2"])
+    W1p = M.packed_heads_w1(shape, W1) if packed else None
     W2p = M.packed_heads_w2(shape, W2) if packed else None
-    M.heads_forward(shape, dev(inp["h"]), dev(inp["W1"]), W2, ids, vals, ws,
-                    head_lse=lse, head_logits=logits, z=z, W2_packed=W2p)
+    M.heads_forward(shape, dev(inp["h"]), W1, W2, ids, vals, ws,
+                    head_lse=lse, head_logits=logits, z=z, W1_packed=W1p, W2_packed=W2p)
     torch.cuda.synchronize()
     out = dict(ids=host(ids), vals=host(vals), lse=host(lse), z=host(z))
     if with_logits:
@@ -95,9 +96,9 @@ BATCHED = [w for w in SMALL if w.dtype == "bf16" and w.B >= 3]
 
 
 @pytest.mark.parametrize("w", BATCHED, ids=lambda w: f"{w.name}-d{w.d}-V{w.V}-B{w.B}")
-def test_heads_packed_w2_equals_row_major(w):
-    # The batched passes read W2 in packed tiles when given them: the same
-    # fragments in the same order, so every output is bit-identical.
+def test_heads_packed_weights_equal_row_major(w):
+    # The batched passes read W1 and W2 in packed tiles when given them: the
+    # same fragments in the same order, so every output is bit-identical.
     inp = make_inputs(w, only=("W1", "W2"))
     g = _run_heads(w, inp)
     gp = _run_heads(w, inp, packed=True)
@@ -168,7 +169,7 @@ def test_heads_full_size_batch8():
     inp = make_inputs(w, only=("W1", "W2"))
     g = _run_heads(w, inp)
     _check_topk_on_own_logits(g)
-    # the packed-W2 pass (as the step runs it) gives the same bits
+    # the packed-weight passes (as the step runs them) give the same bits
     gp = _run_heads(w, inp, packed=True)
     for key in g:
         assert np.array_equal(g[key], gp[key]), key
