@@ -69,6 +69,8 @@ void w2_grid(int V, int& G, int& rpw) {
 
 
 constexpr size_t kCounterBytes = 64 * 1024;   // workspace bytes reserved at offset 0 for counters
+// the block's last MEDUSA_MAX_B counters belong to the composite step's commit
+constexpr size_t kCommitCounter = kCounterBytes / sizeof(int) - MEDUSA_MAX_B;
 
 int check_shape(const medusa_shape* s) {
   if (!s) return fail(MEDUSA_ERR_ARG, "shape: null pointer");
@@ -89,8 +91,7 @@ int check_shape(const medusa_shape* s) {
   if (s->d % 64 != 0) return fail(MEDUSA_ERR_UNSUPPORTED, "d=%d is not a multiple of 64", s->d);
   if (s->Dh != 64 && s->Dh != 128)
     return fail(MEDUSA_ERR_UNSUPPORTED, "Dh=%d is not 64 or 128", s->Dh);
-  if ((size_t)gemm_groups_max(3 * s->d) * gemm_passes_max(s->B * (s->N + 1)) >
-      kCounterBytes / sizeof(int))
+  if ((size_t)gemm_groups_max(3 * s->d) * gemm_passes_max(s->B * (s->N + 1)) > kCommitCounter)
     return fail(MEDUSA_ERR_UNSUPPORTED, "d=%d with %d tree rows needs too many GEMM counters",
                 s->d, s->B * (s->N + 1));
   return MEDUSA_OK;
@@ -902,6 +903,7 @@ int step_impl(const medusa_shape* shape, const medusa_step_args* x, void* worksp
   c.kv_len = x->kv_len;
   c.kv_len_out = x->kv_len_out_or_null;
   c.h_next = x->h_next;
+  c.counters = at<int>(workspace, layout_for(shape).counters) + kCommitCounter;
   a.row_stats = x->row_stats;
   a.row_argmax = x->row_argmax;
   hipError_t e = launch_posterior_commit(a, c, static_cast<hipStream_t>(stream));

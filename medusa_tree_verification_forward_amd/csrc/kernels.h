@@ -192,7 +192,9 @@ struct CommitArgs {
   int32_t* kv_len;
   int32_t* kv_len_out;         // advanced lengths go here; null: kv_len in place
   float* h_next;
+  int* counters;               // [B] zeroed, left at zero (composite step)
 };
+constexpr int kCommitParts = 16;   // composite step: workgroups per sequence, at most
 hipError_t launch_commit(const CommitArgs& a, hipStream_t st);
 // Composite step (greedy / typical): posterior + commit in one workgroup per
 // sequence.

@@ -269,6 +269,16 @@ struct SliceRows {
   }
 };
 
+// LDS slot of the 16-byte A piece of fragment lane (lq, li) in k-tile kt of
+// a chunk (chunks start at even k-tiles): the lane's own slot within its lq
+// quarter, rotated by 2 lq + 8 (kt % 2). Sixteen consecutive lanes of a
+// fragment read (fixed lq, kt) hit 16 distinct slots mod 16, and so do
+// sixteen consecutive lanes of a row-contiguous store (two rows, both
+// k-tiles of a pair, four pieces).
+__device__ __forceinline__ int a_slot(int kt, int lq, int li) {
+  return 16 * lq + ((li + 2 * lq + 8 * (kt & 1)) & 15);
+}
+
 template <class ET, int WV, int MT, int CH, int D, int EPI>
 __global__ __launch_bounds__(64 * WV, WV <= 3 ? 1 : 2) void node_gemm_kernel(
     GemmParams p) {
@@ -323,15 +333,27 @@ __global__ __launch_bounds__(64 * WV, WV <= 3 ? 1 : 2) void node_gemm_kernel(
     child_raw(ch_node, ch_tok_raw, ch_par_raw);
   }
 
-  // A fragment f = wave + WV i of a chunk is (k-tile f / MT, m-tile f % MT).
+  // A moves in units of 1 KB, unit f = wave + WV i of a chunk covering rows
+  // 8 h .. 8 h + 7 of m-tile mt over the k-tile pair 2 pr, 2 pr + 1, with
+  // (h, mt, pr) = (f % 2, f / 2 % MT, f / (2 MT)): each row's 128 bytes are
+  // read by 8 lanes (row 8 h + ar, k-tile 2 pr + ak, piece ap), so a unit
+  // touches 8 whole cache lines where a fragment-shaped load touches 16
+  // halves. In LDS the fragments are stored with the 16-byte slot of lane
+  // (lq, li) of k-tile kt at a_slot(kt, lq, li), which keeps both the
+  // scattered stores and the fragment reads free of bank conflicts.
   // Gathered rows: every index load is issued before any is used (a load
-  // and its clamp per fragment would put one memory latency per fragment in
-  // front of the weight stream).
+  // and its clamp per unit would put one memory latency per unit in front
+  // of the weight stream).
+  static_assert(CH % 2 == 0, "A units cover k-tile pairs");
+  const int ar = lane >> 3, ak = (lane >> 2) & 1, ap = lane & 3;
   const St* asrc[NAW];
   {
     int src[NAW];
 #pragma unroll
-    for (int i = 0; i < NAW; ++i) src[i] = min(m0 + 16 * ((wave + WV * i) % MT) + li, p.M - 1);
+    for (int i = 0; i < NAW; ++i) {
+      const int f = wave + WV * i;
+      src[i] = min(m0 + 16 * (f / 2 % MT) + 8 * (f % 2) + ar, p.M - 1);
+    }
     if (p.a_rows) {
       int raw[NAW];
 #pragma unroll
@@ -341,15 +363,15 @@ __global__ __launch_bounds__(64 * WV, WV <= 3 ? 1 : 2) void node_gemm_kernel(
     }
 #pragma unroll
     for (int i = 0; i < NAW; ++i)
-      asrc[i] = A + (size_t)src[i] * p.lda + (size_t)kt_lo * KT + PV * lq;
+      asrc[i] = A + (size_t)src[i] * p.lda + (size_t)kt_lo * KT + PV * ap;
   }
-  // A fragments of chunks c+1 and c+2 are in flight in two register sets
+  // A units of chunks c+1 and c+2 are in flight in two register sets
   u32x4_t ra0[NAW], ra1[NAW];
   // Past the slice end the k-tile index is clamped (those values are never read).
   auto load_a = [&](int c, u32x4_t(&ra)[NAW]) {
 #pragma unroll
     for (int i = 0; i < NAW; ++i) {
-      const int kt = min(c * CH + (wave + WV * i) / MT, nloc - 1);
+      const int kt = min(c * CH + 2 * ((wave + WV * i) / (2 * MT)) + ak, nloc - 1);
       ra[i] = load16(asrc[i] + (size_t)kt * KT);
     }
   };
@@ -357,7 +379,8 @@ __global__ __launch_bounds__(64 * WV, WV <= 3 ? 1 : 2) void node_gemm_kernel(
 #pragma unroll
     for (int i = 0; i < NAW; ++i) {
       const int f = wave + WV * i;
-      buf[f / MT][f % MT][lane] = ra[i];
+      const int j = 2 * (f / (2 * MT)) + ak;
+      buf[j][f / 2 % MT][a_slot(j, ap, 8 * (f % 2) + ar)] = ra[i];
     }
   };
   floatx4_t acc[MT];
@@ -401,7 +424,8 @@ __global__ __launch_bounds__(64 * WV, WV <= 3 ? 1 : 2) void node_gemm_kernel(
       if (S || s < nloc) {
         const u32x4_t b = wr[(R0 + j) % D];
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt) acc[mt] = frag_mfma<ET>(cur[j][mt][lane], b, acc[mt]);
+        for (int mt = 0; mt < MT; ++mt)
+          acc[mt] = frag_mfma<ET>(cur[j][mt][a_slot(j, lq, li)], b, acc[mt]);
         if (S || s + D < nloc) wr[(R0 + j) % D] = load16_stream(wtile(s + D));
       }
       // one k-tile at a time: hoisting later LDS reads only raises pressure

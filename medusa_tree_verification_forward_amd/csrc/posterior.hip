@@ -19,6 +19,7 @@
 // to 32768, held in LDS), then a walk over the nodes' decisions; larger
 // vocabularies: one 1024-thread workgroup per sequence walks the tree, each
 // p/q step a block-wide pass over the vocabulary in global memory.
+#include <algorithm>
 #include <type_traits>
 
 #include "cdf.h"
@@ -67,8 +68,10 @@ struct TreeLds {
 // Greedy / typical posterior of sequence b over the workgroup (blockDim.x >=
 // T, a multiple of 64, at most 1024) from sh.parent, sh.tok, sh.stat and
 // thread c's child logit cl: thread 0 writes accept_len, last_node,
-// out_tokens and next_root; on return every thread sees sh.best, sh.depth.
-__device__ void posterior_det_lds(const PostArgs& a, int b, float cl, TreeLds& sh) {
+// out_tokens and next_root (when `publish`); on return every thread sees
+// sh.best, sh.depth.
+__device__ void posterior_det_lds(const PostArgs& a, int b, float cl, TreeLds& sh,
+                                  bool publish = true) {
   const int c = threadIdx.x;
   const int T = a.T;
   if (c < T) {
@@ -106,16 +109,18 @@ __device__ void posterior_det_lds(const PostArgs& a, int b, float cl, TreeLds& s
     for (int w = 1; w < nw; ++w) key = max(key, sh.wmax[w]);
     const int best = 0xffff - (key & 0xffff);
     const int depth = key >> 16;
-    a.accept_len[b] = depth;
-    a.last_node[b] = best;
-    int* out = a.out_tokens + (size_t)b * (a.K + 1);
-    for (int j = depth + 1; j <= a.K; ++j) out[j] = -1;
-    int x = best;
-    for (int j = depth; j >= 0; --j) {
-      out[j] = sh.tok[x];
-      x = sh.parent[x];
+    if (publish) {
+      a.accept_len[b] = depth;
+      a.last_node[b] = best;
+      int* out = a.out_tokens + (size_t)b * (a.K + 1);
+      for (int j = depth + 1; j <= a.K; ++j) out[j] = -1;
+      int x = best;
+      for (int j = depth; j >= 0; --j) {
+        out[j] = sh.tok[x];
+        x = sh.parent[x];
+      }
+      a.next_root[b] = sh.stat[best].am;
     }
-    a.next_root[b] = sh.stat[best].am;
     sh.best = best;
     sh.depth = depth;
     sh.bp = 0x7fffffff;
@@ -134,7 +139,7 @@ __device__ __forceinline__ void load_path_row(const PostArgs& a, int (&ret)[MAXK
 // best_path: the lowest path index whose node at the committed depth is the
 // committed node (0 if none; an LDS minimum over threads c < P).
 __device__ void best_path_lds(const PostArgs& a, int b, const int (&ret)[MAXK + 1],
-                              TreeLds& sh) {
+                              TreeLds& sh, bool publish = true) {
   const int c = threadIdx.x;
   int r = -1;
 #pragma unroll
@@ -142,7 +147,7 @@ __device__ void best_path_lds(const PostArgs& a, int b, const int (&ret)[MAXK + 
     if (j == sh.depth) r = ret[j];
   if (c < a.P && r == sh.best) atomicMin(&sh.bp, c);
   __syncthreads();
-  if (c == 0) a.best_path[b] = sh.bp < a.P ? sh.bp : 0;
+  if (c == 0 && publish) a.best_path[b] = sh.bp < a.P ? sh.bp : 0;
 }
 
 // Tree data of sequence b into LDS (threads c < T), from values the caller
@@ -546,17 +551,22 @@ bool exact_lds_fits() {
 }
 
 // ---- commit ----------------------------------------------------------------------
-// One 1024-thread workgroup per sequence; the path's K/V rows are copied as
+// One or more workgroups per sequence; the path's K/V rows are copied as
 // 16-byte vectors (a node's row [H][Dh] is contiguous in the tree buffers, a
-// head's row Dh is contiguous in the cache), every thread loading all its
-// vectors (up to kCopyBatch per tensor) before it stores any, so the copy
-// costs one round trip to memory.
+// head's row Dh is contiguous in the cache), together with the committed
+// node's output row (h_next), every thread loading all its vectors (up to
+// kCopyBatch) before it stores any, so the copy costs one round trip to
+// memory.
 constexpr int kCopyBatch = 4;
 
 // Commit of sequence b's accepted path ending at node `last`, prefix length
-// L, over the whole workgroup; sh.parent holds the tree.
+// L, by workgroup `part` of `nparts` (each takes every nparts-th block of the
+// vectors); sh.parent holds the tree. Thread 0 writes the advanced length
+// when `write_len` (with several workgroups: the one that every other has
+// read L before, so that an in-place update races with no read).
 template <class ET>
-__device__ void commit_lds(const CommitArgs& a, int b, int last_in, int L, TreeLds& sh) {
+__device__ void commit_lds(const CommitArgs& a, int b, int last_in, int L, TreeLds& sh,
+                           int part = 0, int nparts = 1, bool write_len = true) {
   constexpr int PV = ET::kPerVec;
   const int T = a.T, H = a.H, Dh = a.Dh;
   if (threadIdx.x == 0) {
@@ -573,31 +583,40 @@ __device__ void commit_lds(const CommitArgs& a, int b, int last_in, int L, TreeL
   __syncthreads();
   const int d = sh.depth;
   const bool room = L >= 0 && L + d + 1 <= a.Lmax;
-  const float4* y = reinterpret_cast<const float4*>(a.y + ((size_t)b * T + sh.path[d]) * a.d);
-  float4* hn = reinterpret_cast<float4*>(a.h_next + (size_t)b * a.d);
-  if (room) {
-    const int vec_row = H * Dh / PV;          // 16-byte vectors per node row
-    const int vec_head = Dh / PV;             // per head
-    const int total = (d + 1) * vec_row;
-    const u32x4_t* kt = reinterpret_cast<const u32x4_t*>(a.k_tree);
-    const u32x4_t* vt = reinterpret_cast<const u32x4_t*>(a.v_tree);
-    u32x4_t* kc = reinterpret_cast<u32x4_t*>(a.k_cache);
-    u32x4_t* vc = reinterpret_cast<u32x4_t*>(a.v_cache);
-    for (int e0 = threadIdx.x; e0 < total; e0 += kCopyBatch * blockDim.x) {
-      u32x4_t kv[kCopyBatch], vv[kCopyBatch];
+  const u32x4_t* y = reinterpret_cast<const u32x4_t*>(a.y + ((size_t)b * T + sh.path[d]) * a.d);
+  u32x4_t* hn = reinterpret_cast<u32x4_t*>(a.h_next + (size_t)b * a.d);
+  const int vec_row = H * Dh / PV;          // 16-byte vectors per node row
+  const int vec_head = Dh / PV;             // per head
+  const int ny = a.d / 4;                   // vectors of the h_next row
+  const int total = ny + (room ? (d + 1) * vec_row : 0);   // h_next, then K/V pairs
+  const u32x4_t* kt = reinterpret_cast<const u32x4_t*>(a.k_tree);
+  const u32x4_t* vt = reinterpret_cast<const u32x4_t*>(a.v_tree);
+  u32x4_t* kc = reinterpret_cast<u32x4_t*>(a.k_cache);
+  u32x4_t* vc = reinterpret_cast<u32x4_t*>(a.v_cache);
+  const int stride = nparts * (int)blockDim.x;
+  for (int e0 = part * (int)blockDim.x + (int)threadIdx.x; e0 < total;
+       e0 += kCopyBatch * stride) {
+    u32x4_t kv[kCopyBatch], vv[kCopyBatch];
 #pragma unroll
-      for (int u = 0; u < kCopyBatch; ++u) {
-        const int e = min(e0 + u * (int)blockDim.x, total - 1);
-        const int i = e / vec_row, rem = e - i * vec_row;
+    for (int u = 0; u < kCopyBatch; ++u) {
+      const int e = min(e0 + u * stride, total - 1);
+      if (e < ny) {
+        kv[u] = y[e];
+      } else {
+        const int i = (e - ny) / vec_row, rem = (e - ny) - i * vec_row;
         const size_t src = ((size_t)b * T + sh.path[i]) * vec_row + rem;
         kv[u] = kt[src];
         vv[u] = vt[src];
       }
+    }
 #pragma unroll
-      for (int u = 0; u < kCopyBatch; ++u) {
-        const int e = e0 + u * (int)blockDim.x;
-        if (e >= total) break;
-        const int i = e / vec_row, rem = e - i * vec_row;
+    for (int u = 0; u < kCopyBatch; ++u) {
+      const int e = e0 + u * stride;
+      if (e >= total) break;
+      if (e < ny) {
+        hn[e] = kv[u];
+      } else {
+        const int i = (e - ny) / vec_row, rem = (e - ny) - i * vec_row;
         const int hh = rem / vec_head, x = rem - hh * vec_head;
         const size_t dst = (((size_t)b * H + hh) * a.Lmax + L + i) * vec_head + x;
         kc[dst] = kv[u];
@@ -605,9 +624,8 @@ __device__ void commit_lds(const CommitArgs& a, int b, int last_in, int L, TreeL
       }
     }
   }
-  for (int e = threadIdx.x; e < a.d / 4; e += blockDim.x) hn[e] = y[e];
-  __syncthreads();
-  if (threadIdx.x == 0) (a.kv_len_out ? a.kv_len_out : a.kv_len)[b] = room ? L + d + 1 : -1;
+  if (write_len && threadIdx.x == 0)
+    (a.kv_len_out ? a.kv_len_out : a.kv_len)[b] = room ? L + d + 1 : -1;
 }
 
 template <class ET>
@@ -622,13 +640,17 @@ __global__ __launch_bounds__(1024) void commit_kernel(CommitArgs a) {
   commit_lds<ET>(a, b, last, sh.L, sh);
 }
 
-// Composite step, greedy / typical: one workgroup per sequence evaluates the
-// posterior from the merged row statistics and commits the accepted path.
-// All the loads the decision needs -- row statistics, child logits, tokens,
+// Composite step, greedy / typical: gridDim.x workgroups per sequence
+// (blockIdx.y) each evaluate the posterior from the merged row statistics
+// -- the same inputs and operations, so the same decision -- and copy their
+// share of the accepted path; the first publishes the decision. All the
+// loads the decision needs -- row statistics, child logits, tokens,
 // parents, path rows, the prefix length -- are issued before any is used.
+constexpr int kPostThreads = 256;
+static_assert(kPostThreads >= MAXT, "one thread per tree row");
 template <class ET>
-__global__ __launch_bounds__(1024) void posterior_commit_kernel(PostArgs a, CommitArgs c) {
-  const int b = blockIdx.x, t = threadIdx.x, T = a.T;
+__global__ __launch_bounds__(kPostThreads) void posterior_commit_kernel(PostArgs a, CommitArgs c) {
+  const int b = blockIdx.y, t = threadIdx.x, T = a.T;
   __shared__ TreeLds sh;
   int par = 0, tk = 0;
   float cl = 0.f;
@@ -640,17 +662,36 @@ __global__ __launch_bounds__(1024) void posterior_commit_kernel(PostArgs a, Comm
   }
   int ret[MAXK + 1];
   load_path_row(a, ret);
-  if (t == 0) sh.L = c.kv_len[b];
+  int L = 0;
+  if (t == 0) L = c.kv_len[b];
   if (t < T) {
     const size_t r = (size_t)b * T + t;
     sh.stat[t] = RowStat{a.row_stats[r * 3 + 0], a.row_stats[r * 3 + 1],
                          a.row_stats[r * 3 + 2], a.row_argmax[r]};
   }
+  // Workgroups of several count themselves in on c.counters[b] once their
+  // read of the prefix length is complete (every load of the wave waited
+  // for); the last to count writes the advanced length and leaves the
+  // counter at zero. The count is not waited for until the end.
+  int before = 0;
+  if (t == 0) {
+    sh.L = L;
+    if (gridDim.x > 1) {
+      __atomic_signal_fence(__ATOMIC_SEQ_CST);
+      vmcnt<0>();
+      __atomic_signal_fence(__ATOMIC_SEQ_CST);
+      before = __hip_atomic_fetch_add(c.counters + b, 1, __ATOMIC_RELAXED,
+                                      __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
   stage_tree(T, par, tk, sh);
   __syncthreads();
-  posterior_det_lds(a, b, cl, sh);
-  best_path_lds(a, b, ret, sh);
-  commit_lds<ET>(c, b, sh.best, sh.L, sh);
+  const bool publish = blockIdx.x == 0;
+  posterior_det_lds(a, b, cl, sh, publish);
+  best_path_lds(a, b, ret, sh, publish);
+  const bool last = (int)gridDim.x == 1 || before == (int)gridDim.x - 1;
+  commit_lds<ET>(c, b, sh.best, sh.L, sh, blockIdx.x, gridDim.x, last);
+  if (t == 0 && gridDim.x > 1 && last) coherent_store(c.counters + b, 0);
 }
 
 }  // namespace
@@ -670,10 +711,14 @@ hipError_t launch_posterior(const PostArgs& a, hipStream_t st) {
 }
 
 hipError_t launch_posterior_commit(const PostArgs& a, const CommitArgs& c, hipStream_t st) {
+  // the copy spread over up to kCommitParts workgroups a sequence, about one
+  // workgroup per compute unit in all
+  const int parts = std::max(1, std::min(kCommitParts, device_cus() / std::max(a.B, 1)));
+  const dim3 grid(parts, a.B);
   if (c.f32)
-    hipLaunchKernelGGL(posterior_commit_kernel<F32>, dim3(a.B), dim3(1024), 0, st, a, c);
+    hipLaunchKernelGGL(posterior_commit_kernel<F32>, grid, dim3(kPostThreads), 0, st, a, c);
   else
-    hipLaunchKernelGGL(posterior_commit_kernel<BF16>, dim3(a.B), dim3(1024), 0, st, a, c);
+    hipLaunchKernelGGL(posterior_commit_kernel<BF16>, grid, dim3(kPostThreads), 0, st, a, c);
   return hipGetLastError();
 }
 
