@@ -144,7 +144,7 @@ Layout layout_for(const medusa_shape* s) {
   L.att_ml = take(B * H * L.NS * T * 2 * 4);
   L.q = take(B * T * d * es);
   L.o_elem = take(B * T * d * es);
-  L.y_elem = take(B * T * d * es);
+  L.y_elem = take((B * T + 15) / 16 * 16 * d * es);   // A-fragment order, whole m-tiles
   // LM records [M][stripes][4]
   L.lm_part = take(B * T * (size_t)lm_record_slots(s->V) * 4 * 4);
   {
@@ -535,6 +535,7 @@ int verify_impl(const medusa_shape* shape, const void* E, const void* W_qkv, con
   g.T = T;
   g.H = shape->H;
   g.Dh = shape->Dh;
+  g.a_mtiles = (M + 15) / 16;   // y in the LM head's A-fragment order
   // 1. q, k, v = RoPE(E[tok] Wq^T), RoPE(E[tok] Wk^T), E[tok] Wv^T
   g.M = M;
   g.N = 3 * d;

@@ -186,6 +186,17 @@ __device__ __forceinline__ int coherent_load(const int* p) {
   return __hip_atomic_load(const_cast<int*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// A-fragment order of a [rows][K] operand of v_mfma_f32_16x16x32_bf16 (PV =
+// 8 elements per 16-byte piece) or of four v_mfma_f32_16x16x4_f32 (PV = 4):
+// tile (k-tile kt, m-tile mt) is 64 lane pieces of 16 bytes, lane 16 lq + li
+// holding row 16 mt + li, elements 4 PV kt + PV lq .. + PV - 1; the tiles of
+// a k-tile are adjacent (mtiles of them), so a wave loads one fragment as
+// one contiguous 1 KB. Element index of (row r, column c):
+__device__ __forceinline__ size_t frag_index(int r, int c, int mtiles, int PV) {
+  const int kt = c / (4 * PV), rem = c - kt * 4 * PV, lq = rem / PV;
+  return (((size_t)kt * mtiles + (r >> 4)) * 64 + 16 * lq + (r & 15)) * PV + (rem - lq * PV);
+}
+
 // Counts the calling workgroup in on `counter` and returns, in every thread,
 // whether it is the last of `n` workgroups to arrive; the last one resets the
 // counter to zero for the next launch. Every coherent_store of the workgroup

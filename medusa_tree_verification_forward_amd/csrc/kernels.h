@@ -88,8 +88,9 @@ enum { EPI_QKV = 0, EPI_OPROJ = 1, EPI_LM = 2 };
 struct GemmParams {
   bool f32;
   int M, N, K;                 // C[M][N] = A[M][K] * W[N][K]^T
-  const void* A;
+  const void* A;               // [M][lda] (QKV, OPROJ) or A-fragment order (LM head)
   int lda;
+  int a_mtiles;                // m-tiles of the fragment-ordered LM-head A and OPROJ y_elem
   const int32_t* a_rows;       // optional: A row of output row m is a_rows[m]
   int a_nrows;                 // rows of A (gathered indices are clamped into range)
   const void* W;
@@ -104,7 +105,8 @@ struct GemmParams {
   const void* E;
   const int32_t* tokens;       // [M]
   float* y_out;                // [M][N] fp32
-  void* y_elem;                // [M][N] storage type
+  void* y_elem;                // storage type in A-fragment order over a_mtiles m-tiles
+                               // (frag_index), rows M .. 16 a_mtiles - 1 zero
   // LM epilogue
   float inv_tau;
   float* part;                 // LM: [M][groups][4]; QKV/OPROJ: [groups][M][cols][KS]

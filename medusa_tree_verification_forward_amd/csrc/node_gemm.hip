@@ -175,12 +175,17 @@ struct QkvColumn {
   }
 };
 
-// y = x + acc, x = E[token of row r]: written as fp32 and storage type.
+// y = x + acc, x = E[token of row r]: written as fp32 and, in the LM head's
+// A-fragment order, as storage type. Rows M .. 16 a_mtiles - 1 of the
+// fragment-ordered copy (the padding of its last m-tile) are written as zero.
 template <class ET>
 __device__ __forceinline__ void oproj_store(const GemmParams& p, int r, int n, float y) {
   using St = typename ET::storage;
-  p.y_out[(size_t)r * p.N + n] = y;
-  reinterpret_cast<St*>(p.y_elem)[(size_t)r * p.N + n] = ET::from_float(y);
+  if (r >= 16 * p.a_mtiles) return;
+  const bool live = r < p.M;
+  if (live) p.y_out[(size_t)r * p.N + n] = y;
+  reinterpret_cast<St*>(p.y_elem)[frag_index(r, n, p.a_mtiles, ET::kPerVec)] =
+      ET::from_float(live ? y : 0.f);
 }
 
 // Workgroup coordinates: column group g, K slice ks, row pass pz. With one
@@ -262,7 +267,7 @@ struct SliceRows {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const int r = m0 + 16 * mt + 4 * lq + j;
-          if (r < p.M && col < p.N)
+          if (col < p.N)
             oproj_store<ET>(p, r, col, ET::from_raw(opaque(xr[mt][j])) + acc[mt][j]);
         }
     }
@@ -344,10 +349,20 @@ __global__ __launch_bounds__(64 * WV, WV <= 3 ? 1 : 2) void node_gemm_kernel(
   // Gathered rows: every index load is issued before any is used (a load
   // and its clamp per unit would put one memory latency per unit in front
   // of the weight stream).
+  // The LM head's A (the output projection's y) comes in A-fragment order
+  // (frag_index): there unit f is fragment (k-tile f / MT, m-tile f % MT),
+  // one contiguous 1 KB, stored at its lanes' own slots.
   static_assert(CH % 2 == 0, "A units cover k-tile pairs");
+  constexpr bool kFragA = EPI == EPI_LM;
   const int ar = lane >> 3, ak = (lane >> 2) & 1, ap = lane & 3;
   const St* asrc[NAW];
-  {
+  if constexpr (kFragA) {
+#pragma unroll
+    for (int i = 0; i < NAW; ++i) {
+      const int mt = min(m0 / 16 + (wave + WV * i) % MT, p.a_mtiles - 1);
+      asrc[i] = A + ((size_t)kt_lo * p.a_mtiles * 64 + (size_t)mt * 64 + lane) * PV;
+    }
+  } else {
     int src[NAW];
 #pragma unroll
     for (int i = 0; i < NAW; ++i) {
@@ -371,16 +386,26 @@ __global__ __launch_bounds__(64 * WV, WV <= 3 ? 1 : 2) void node_gemm_kernel(
   auto load_a = [&](int c, u32x4_t(&ra)[NAW]) {
 #pragma unroll
     for (int i = 0; i < NAW; ++i) {
-      const int kt = min(c * CH + 2 * ((wave + WV * i) / (2 * MT)) + ak, nloc - 1);
-      ra[i] = load16(asrc[i] + (size_t)kt * KT);
+      const int f = wave + WV * i;
+      if constexpr (kFragA) {
+        const int kt = min(c * CH + f / MT, nloc - 1);
+        ra[i] = load16(asrc[i] + (size_t)kt * p.a_mtiles * 64 * PV);
+      } else {
+        const int kt = min(c * CH + 2 * (f / (2 * MT)) + ak, nloc - 1);
+        ra[i] = load16(asrc[i] + (size_t)kt * KT);
+      }
     }
   };
   auto store_a = [&](u32x4_t(&buf)[CH][MT][64], const u32x4_t(&ra)[NAW]) {
 #pragma unroll
     for (int i = 0; i < NAW; ++i) {
       const int f = wave + WV * i;
-      const int j = 2 * (f / (2 * MT)) + ak;
-      buf[j][f / 2 % MT][a_slot(j, ap, 8 * (f % 2) + ar)] = ra[i];
+      if constexpr (kFragA) {
+        buf[f / MT][f % MT][a_slot(f / MT, lq, li)] = ra[i];
+      } else {
+        const int j = 2 * (f / (2 * MT)) + ak;
+        buf[j][f / 2 % MT][a_slot(j, ap, 8 * (f % 2) + ar)] = ra[i];
+      }
     }
   };
   floatx4_t acc[MT];
@@ -574,8 +599,7 @@ __global__ __launch_bounds__(64 * WV, WV <= 3 ? 1 : 2) void node_gemm_kernel(
         if (n0 + cl < p.N)
 #pragma unroll
           for (int i = 0; i < RB; ++i) {
-            const int r = m0 + rl + RL * (i0 + i);
-            if (r < p.M) oproj_store<ET>(p, r, n, x[i] + acc_s[i]);
+            oproj_store<ET>(p, m0 + rl + RL * (i0 + i), n, x[i] + acc_s[i]);
           }
       }
     }
@@ -720,9 +744,15 @@ __global__ __launch_bounds__(64 * WV, 1) void node_gemm_rows_kernel(GemmParams p
   const int nkt = p.K / KT, ntiles = (p.N + 15) >> 4;
   const int n0 = g * 16 * NS;
 
-  // A rows of the wave (gathered rows: every index load before any use)
+  // A of the wave: its m-tiles' fragments (LM head: A in A-fragment order,
+  // frag_index) or its rows (gathered rows: every index load before any use)
   const St* arow[MW];
-  {
+  if constexpr (EPI == EPI_LM) {
+#pragma unroll
+    for (int mt = 0; mt < MW; ++mt)
+      arow[mt] = reinterpret_cast<const St*>(p.A) +
+                 ((size_t)min(mw / 16 + mt, p.a_mtiles - 1) * 64 + lane) * PV;
+  } else {
     int src[MW];
 #pragma unroll
     for (int mt = 0; mt < MW; ++mt) src[mt] = min(mw + 16 * mt + li, p.M - 1);
@@ -755,7 +785,7 @@ __global__ __launch_bounds__(64 * WV, 1) void node_gemm_rows_kernel(GemmParams p
     for (int u = 0; u < NPW; ++u) w[u] = load16_stream(wbase[u] + off);
   };
   auto load_a = [&](int kt, u32x4_t(&a)[MW]) {
-    const size_t off = (size_t)min(kt, nkt - 1) * KT;
+    const size_t off = (size_t)min(kt, nkt - 1) * (EPI == EPI_LM ? (size_t)p.a_mtiles * 64 * PV : KT);
 #pragma unroll
     for (int mt = 0; mt < MW; ++mt) a[mt] = load16(arow[mt] + off);
   };
