@@ -1079,8 +1079,20 @@ struct RowsCfg {
 };
 bool rows_config(int M, int N, int epi, bool f32, RowsCfg& c) {
   if (f32 || M <= 48 || (epi != EPI_QKV && epi != EPI_LM)) return false;
-  c.wv = M <= 192 ? 4 : 8;
   const int stripes = (N + 15) / 16, cus = device_cus();
+  if (epi == EPI_QKV && M > 192) {
+    // several passes of 192 rows (the passes of a column group share its
+    // weight reads in L2) when 3, 4 or 6 stripes a workgroup fit one
+    // workgroup per compute unit
+    const int passes = (M + 191) / 192;
+    for (int ns : {3, 4, 6})
+      if ((stripes + ns - 1) / ns * passes <= cus) {
+        c.wv = 4;
+        c.ns = ns;
+        return true;
+      }
+  }
+  c.wv = M <= 192 ? 4 : 8;
   c.ns = 8;
   for (int ns : {3, 4, 8})
     if ((stripes + ns - 1) / ns <= cus) {
@@ -1101,6 +1113,7 @@ hipError_t launch_rows(const GemmParams& p, const RowsCfg& c, hipStream_t st) {
   }
   ROWS_CASE(4, 3)
   ROWS_CASE(4, 4)
+  if constexpr (EPI == EPI_QKV) ROWS_CASE(4, 6)
   ROWS_CASE(4, 8)
   ROWS_CASE(8, 3)
   ROWS_CASE(8, 4)
