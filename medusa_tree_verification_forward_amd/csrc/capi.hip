@@ -816,7 +816,7 @@ int step_impl(const medusa_shape* shape, const medusa_step_args* x, void* worksp
   rc = check_workspace(shape, workspace, workspace_bytes, &L);
   if (rc) return rc;
   const bool fuse_tree = x->draft_mode == MEDUSA_DRAFT_TOPK;
-  // greedy / typical: posterior and commit in one workgroup per sequence
+  // greedy / typical: posterior and commit in one kernel, checked here
   const bool fuse_post = mode != MEDUSA_EXACT;
   if (fuse_post) {
     REQUIRE_PTR(x->accept_len);
@@ -853,18 +853,20 @@ int step_impl(const medusa_shape* shape, const medusa_step_args* x, void* worksp
                    x->child_logit, x->verify_logits_or_null, workspace, workspace_bytes, stream,
                    dry);
   if (rc) return rc;
-  // 4. posterior and commit
+  // 4. posterior and commit (exact mode: the two calls' checks, then the
+  // node-parallel posterior with the walk and the commit in one kernel)
   if (!fuse_post) {
     rc = posterior_impl(shape, mode, x->temperature, x->eps, x->delta, x->row_stats,
                         x->row_argmax, x->child_logit, x->verify_logits_or_null, x->tree_tokens,
                         x->parent, x->retrieve, x->head_logits_or_null, x->head_lse_or_null,
                         x->u_accept_or_null, x->u_resample_or_null, x->accept_len, x->best_path,
                         x->last_node, x->out_tokens, x->next_root, workspace, workspace_bytes,
-                        stream, dry);
+                        stream, true);
     if (rc) return rc;
-    return commit_impl(shape, x->last_node, x->parent, x->k_tree, x->v_tree, x->y,
-                       x->k_cache, x->v_cache, x->kv_len, x->kv_len_out_or_null, x->h_next,
-                       stream, dry);
+    rc = commit_impl(shape, x->last_node, x->parent, x->k_tree, x->v_tree, x->y,
+                     x->k_cache, x->v_cache, x->kv_len, x->kv_len_out_or_null, x->h_next,
+                     stream, true);
+    if (rc) return rc;
   }
   if (dry) return MEDUSA_OK;
   PostArgs a{};
@@ -886,6 +888,13 @@ int step_impl(const medusa_shape* shape, const medusa_step_args* x, void* worksp
   a.last_node = x->last_node;
   a.out_tokens = x->out_tokens;
   a.next_root = x->next_root;
+  a.verify_logits = x->verify_logits_or_null;
+  a.head_logits = x->head_logits_or_null;
+  a.head_lse = x->head_lse_or_null;
+  a.u_accept = x->u_accept_or_null;
+  a.u_resample = x->u_resample_or_null;
+  a.pw = at<float>(workspace, L.pw);
+  a.exact_dec = at<int32_t>(workspace, L.exact_dec);
   CommitArgs c{};
   c.f32 = shape->dtype == MEDUSA_F32;
   c.B = shape->B;
@@ -904,7 +913,7 @@ int step_impl(const medusa_shape* shape, const medusa_step_args* x, void* worksp
   c.kv_len = x->kv_len;
   c.kv_len_out = x->kv_len_out_or_null;
   c.h_next = x->h_next;
-  c.counters = at<int>(workspace, layout_for(shape).counters) + kCommitCounter;
+  c.counters = at<int>(workspace, L.counters) + kCommitCounter;
   a.row_stats = x->row_stats;
   a.row_argmax = x->row_argmax;
   hipError_t e = launch_posterior_commit(a, c, static_cast<hipStream_t>(stream));

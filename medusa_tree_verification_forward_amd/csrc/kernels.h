@@ -198,8 +198,9 @@ struct CommitArgs {
 };
 constexpr int kCommitParts = 16;   // composite step: workgroups per sequence, at most
 hipError_t launch_commit(const CommitArgs& a, hipStream_t st);
-// Composite step (greedy / typical): posterior + commit in one workgroup per
-// sequence.
+// Composite step: greedy / typical posterior + commit in one kernel (several
+// workgroups a sequence); exact mode: the node-parallel posterior, then the
+// walk + commit in one kernel (large vocabularies: the separate kernels).
 hipError_t launch_posterior_commit(const PostArgs& a, const CommitArgs& c, hipStream_t st);
 
 }  // namespace medusa

@@ -694,6 +694,87 @@ __global__ __launch_bounds__(kPostThreads) void posterior_commit_kernel(PostArgs
   if (t == 0 && gridDim.x > 1 && last) coherent_store(c.counters + b, 0);
 }
 
+// Composite step, exact mode, after exact_node_kernel: gridDim.x workgroups
+// per sequence (blockIdx.y) each follow the accepted children from the root,
+// as exact_walk_kernel does, and copy their share of the accepted path; the
+// first publishes the decision. The prefix length is counted in and written
+// as in posterior_commit_kernel.
+template <class ET>
+__global__ __launch_bounds__(kPostThreads) void exact_walk_commit_kernel(PostArgs a,
+                                                                         CommitArgs c) {
+  const int b = blockIdx.y, t = threadIdx.x, T = a.T, K = a.K;
+  __shared__ TreeLds sh;
+  __shared__ int s_taken[MAXT], s_draw[MAXT];
+  int2 dec = make_int2(0, 0);
+  int par = 0, tk = 0;
+  if (t < T) {
+    dec = *reinterpret_cast<const int2*>(a.exact_dec + ((size_t)b * T + t) * 2);
+    par = a.parent[t];
+    tk = a.tokens[(size_t)b * T + t];
+  }
+  int L = 0;
+  if (t == 0) L = c.kv_len[b];
+  int before = 0;
+  if (t == 0) {
+    sh.L = L;
+    if (gridDim.x > 1) {
+      __atomic_signal_fence(__ATOMIC_SEQ_CST);
+      vmcnt<0>();
+      __atomic_signal_fence(__ATOMIC_SEQ_CST);
+      before = __hip_atomic_fetch_add(c.counters + b, 1, __ATOMIC_RELAXED,
+                                      __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+  stage_tree(T, par, tk, sh);
+  if (t < T) {
+    s_taken[t] = dec.x;
+    s_draw[t] = dec.y;
+  }
+  __syncthreads();
+  if (t == 0) {
+    int v = 0;
+    // a taken child is a later node, so the walk ends within T steps
+    for (int i = 0; i < T; ++i) {
+      const int ch = s_taken[v];
+      if (ch <= v || ch >= T) break;
+      v = ch;
+    }
+    sh.best = v;
+  }
+  __syncthreads();
+  const int v = sh.best;
+  if (blockIdx.x == 0 && t < 64) {
+    int depth = 0;
+    for (int x = v; x != 0 && depth < K; x = sh.parent[x]) ++depth;
+    // best path: the lowest path index whose node at this depth is v
+    int bp = 0x7fffffff;
+    for (int q = t; q < a.P; q += 64)
+      if (a.retrieve[(size_t)q * (K + 1) + depth] == v) bp = min(bp, q);
+    bp = -wave_max_i(-bp);
+    if (t == 0) {
+      a.accept_len[b] = depth;
+      a.last_node[b] = v;
+      int* out = a.out_tokens + (size_t)b * (K + 1);
+      for (int j = depth + 1; j <= K; ++j) out[j] = -1;
+      int x = v;
+      for (int j = depth; j >= 0; --j) {
+        out[j] = sh.tok[x];
+        x = sh.parent[x];
+      }
+      a.next_root[b] = s_draw[v];
+      a.best_path[b] = bp == 0x7fffffff ? 0 : bp;
+    }
+  }
+  const bool last = (int)gridDim.x == 1 || before == (int)gridDim.x - 1;
+  commit_lds<ET>(c, b, v, sh.L, sh, blockIdx.x, gridDim.x, last);
+  if (t == 0 && gridDim.x > 1 && last) coherent_store(c.counters + b, 0);
+}
+
+// Workgroups a sequence of the composite posterior + commit kernels: the
+// copy spread over up to kCommitParts, about one workgroup per compute unit
+// in all.
+int commit_parts(int B) { return std::max(1, std::min(kCommitParts, device_cus() / std::max(B, 1))); }
+
 }  // namespace
 
 hipError_t launch_posterior(const PostArgs& a, hipStream_t st) {
@@ -711,10 +792,25 @@ hipError_t launch_posterior(const PostArgs& a, hipStream_t st) {
 }
 
 hipError_t launch_posterior_commit(const PostArgs& a, const CommitArgs& c, hipStream_t st) {
-  // the copy spread over up to kCommitParts workgroups a sequence, about one
-  // workgroup per compute unit in all
-  const int parts = std::max(1, std::min(kCommitParts, device_cus() / std::max(a.B, 1)));
-  const dim3 grid(parts, a.B);
+  if (a.mode == 2) {
+    // exact: the node-parallel posterior, then the walk with the commit;
+    // vocabularies past the LDS kernel take the separate kernels
+    if (a.V <= kExactLdsV && exact_lds_fits()) {
+      hipLaunchKernelGGL(exact_node_kernel, dim3(a.T, a.B), dim3(1024), 0, st, a);
+      hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+      const dim3 grid(commit_parts(a.B), a.B);
+      if (c.f32)
+        hipLaunchKernelGGL(exact_walk_commit_kernel<F32>, grid, dim3(kPostThreads), 0, st, a, c);
+      else
+        hipLaunchKernelGGL(exact_walk_commit_kernel<BF16>, grid, dim3(kPostThreads), 0, st, a, c);
+      return hipGetLastError();
+    }
+    hipError_t e = launch_posterior(a, st);
+    if (e != hipSuccess) return e;
+    return launch_commit(c, st);
+  }
+  const dim3 grid(commit_parts(a.B), a.B);
   if (c.f32)
     hipLaunchKernelGGL(posterior_commit_kernel<F32>, grid, dim3(kPostThreads), 0, st, a, c);
   else

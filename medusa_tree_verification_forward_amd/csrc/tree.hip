@@ -4,7 +4,9 @@
 // The host has validated the rank-path spec and reduced it to (parent, own
 // rank, depth) per node. Per step, one thread per node writes
 //   tokens     = the root token, or head (depth-1)'s token of the node's rank,
-//   positions  = kv_len[b] + depth.
+//   positions  = kv_len[b] + depth
+// (in sampling mode the sampler's depth-1 workgroups write the positions
+// and the root token, and the draws the other tokens).
 // The topology, which only depends on the spec, is written when asked (once
 // per spec is enough), by one workgroup with one thread per node (T <= 256):
 //   mask[i][j] = 1 iff j is i or an ancestor of i,
@@ -36,8 +38,6 @@ __global__ __launch_bounds__(256) void tree_nodes_kernel(TreeArgs a) {
   int tok;
   if (n == 0)
     tok = a.root_tok[b];
-  else if (a.sample)
-    return;   // drawn by tree_sample_kernel
   else
     tok = a.topk_ids[((size_t)b * K + (d - 1)) * a.S + a.plan.last_rank[n]];
   a.tokens[(size_t)b * T + n] = tok;
@@ -91,7 +91,9 @@ __global__ __launch_bounds__(256) void tree_topology_kernel(TreeArgs a) {
 // Inverse-CDF draws for sampling mode. One 1024-thread workgroup per
 // (depth k, sequence b) builds the CDF of head k's softmax weights
 // w_v = exp(l_v - lse) (cdf.h); thread n then draws node n's token with the
-// node's uniform if node n has depth k + 1 (T <= 256 threads).
+// node's uniform if node n has depth k + 1 (T <= 256 threads). The
+// workgroups of depth 1 also write what the node kernel writes in top-s mode
+// for every node: the position ids, and the root token.
 __global__ __launch_bounds__(kCdfThreads) void tree_sample_kernel(TreeArgs a) {
   const int kd = blockIdx.x;     // 0-based head = depth - 1
   const int b = blockIdx.y;
@@ -101,8 +103,13 @@ __global__ __launch_bounds__(kCdfThreads) void tree_sample_kernel(TreeArgs a) {
   const float lse = a.head_lse[(size_t)b * K + kd];
   __shared__ CdfLds sh;
   const ExpRow w{l, lse, V};
-  const bool mine = t >= 1 && t < T && a.plan.depth[min(t, MAXT - 1)] == kd + 1;
+  const int dep = a.plan.depth[min(t, MAXT - 1)];
+  const bool mine = t >= 1 && t < T && dep == kd + 1;
   const float u = mine ? a.u_draft[(size_t)b * T + t] : 0.f;
+  if (kd == 0 && t < T) {
+    a.position_ids[(size_t)b * T + t] = a.kv_len[b] + dep;
+    if (t == 0) a.tokens[(size_t)b * T] = a.root_tok[b];
+  }
   cdf_build<true>(w, V, sh);
   if (mine) a.tokens[(size_t)b * T + t] = cdf_draw(w, V, u, sh);
 }
@@ -110,9 +117,12 @@ __global__ __launch_bounds__(kCdfThreads) void tree_sample_kernel(TreeArgs a) {
 }  // namespace
 
 hipError_t launch_tree(const TreeArgs& a, hipStream_t st) {
-  hipLaunchKernelGGL(tree_nodes_kernel, dim3(a.B), dim3(256), 0, st, a);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  hipError_t e = hipSuccess;
+  if (!a.sample) {
+    hipLaunchKernelGGL(tree_nodes_kernel, dim3(a.B), dim3(256), 0, st, a);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   if (a.mask || a.retrieve || a.parent || a.depth) {
     hipLaunchKernelGGL(tree_topology_kernel, dim3(1), dim3(256), 0, st, a);
     e = hipGetLastError();

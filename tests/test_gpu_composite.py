@@ -1,8 +1,8 @@
 """The composite call (medusa_step) against the five separate calls and the
-oracle. The composite fuses the tree tokens into the head merge and the row
-statistics, posterior and commit into one workgroup per sequence, with the
-same arithmetic in the same order: every output must be bit-identical to the
-separate calls'."""
+oracle. The composite fuses the tree tokens into the head merge, the
+posterior and commit into one kernel (greedy / typical; exact mode: the walk
+over the node decisions and the commit), with the same arithmetic in the
+same order: every output must be bit-identical to the separate calls'."""
 
 import numpy as np
 import pytest
