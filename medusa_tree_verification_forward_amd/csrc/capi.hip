@@ -497,7 +497,7 @@ int verify_impl(const medusa_shape* shape, const void* E, const void* W_qkv, con
                 float temperature, void* k_tree_out, void* v_tree_out, float* y_out,
                 float* row_stats, int32_t* row_argmax, float* child_logit,
                 float* verify_logits_or_null, void* workspace, size_t workspace_bytes,
-                void* stream, bool dry) {
+                void* stream, bool dry, bool merge_rows = true) {
   int rc = check_shape(shape);
   if (rc) return rc;
   REQUIRE_PTR(E);
@@ -602,7 +602,7 @@ int verify_impl(const medusa_shape* shape, const void* E, const void* W_qkv, con
   gl.part = at<float>(workspace, L.lm_part);
   gl.child_logit = child_logit;
   gl.logits_out = verify_logits_or_null;
-  e = launch_lm_head(gl, row_stats, row_argmax, st);
+  e = launch_lm_head(gl, row_stats, row_argmax, st, merge_rows);
   if (e != hipSuccess) return hip_fail(e, "lm head launch");
   return ok();
 }
@@ -851,7 +851,7 @@ int step_impl(const medusa_shape* shape, const medusa_step_args* x, void* worksp
                    x->position_ids, x->tree_mask, x->parent, x->k_cache, x->v_cache, x->kv_len,
                    x->temperature, x->k_tree, x->v_tree, x->y, x->row_stats, x->row_argmax,
                    x->child_logit, x->verify_logits_or_null, workspace, workspace_bytes, stream,
-                   dry);
+                   dry, fuse_post);
   if (rc) return rc;
   // 4. posterior and commit (exact mode: the two calls' checks, then the
   // node-parallel posterior with the walk and the commit in one kernel)
@@ -895,6 +895,13 @@ int step_impl(const medusa_shape* shape, const medusa_step_args* x, void* worksp
   a.u_resample = x->u_resample_or_null;
   a.pw = at<float>(workspace, L.pw);
   a.exact_dec = at<int32_t>(workspace, L.exact_dec);
+  if (!fuse_post) {
+    // exact mode: the LM head's row-statistics merge runs with the posterior
+    a.lm_part = at<float>(workspace, L.lm_part);
+    a.lm_G = lm_head_blocks(shape->V, a.B * a.T, shape->dtype == MEDUSA_F32);
+    a.row_stats_out = x->row_stats;
+    a.row_argmax_out = x->row_argmax;
+  }
   CommitArgs c{};
   c.f32 = shape->dtype == MEDUSA_F32;
   c.B = shape->B;

@@ -311,6 +311,53 @@ __device__ __forceinline__ void rec_merge(float& m, float& s, float& w, int& a, 
   a = an;
 }
 
+// Merge of row r's G records part[r][g][4] (m, S, W, argmax bits) by a group
+// of 256 threads (t = 0..255 within the group, `wr` 4 LDS slots of its own),
+// in a fixed order: thread t its records t, t + 256, ... in turn, a butterfly
+// over each wave, then thread 0 the group's 4 waves in order; it writes
+// row_stats[r] (m, S, W) and row_argmax[r] when `live`. Every thread of the
+// calling workgroup calls it once (one barrier).
+__device__ __forceinline__ void row_records_merge(const float* __restrict__ part, int G,
+                                                  float inv_tau, int r, int t, bool live,
+                                                  floatx4_t* wr, float* __restrict__ row_stats,
+                                                  int* __restrict__ row_argmax) {
+  constexpr int RB = 8;
+  const int lane = t & 63, wave = t >> 6;
+  float m = -__builtin_huge_valf(), s = 0.f, w = 0.f;
+  int a = 0x7fffffff;
+  for (int g0 = 0; g0 < G; g0 += 256 * RB) {
+    floatx4_t rec[RB];
+#pragma unroll
+    for (int u = 0; u < RB; ++u) {
+      const int g = min(g0 + t + 256 * u, G - 1);
+      rec[u] = *reinterpret_cast<const floatx4_t*>(part + ((size_t)r * G + g) * 4);
+    }
+#pragma unroll
+    for (int u = 0; u < RB; ++u)
+      if (g0 + t + 256 * u < G)
+        rec_merge(m, s, w, a, rec[u][0], rec[u][1], rec[u][2], __float_as_int(rec[u][3]),
+                  inv_tau);
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    const float m2 = __shfl_xor(m, off), s2 = __shfl_xor(s, off), w2 = __shfl_xor(w, off);
+    const int a2 = __shfl_xor(a, off);
+    rec_merge(m, s, w, a, m2, s2, w2, a2, inv_tau);
+  }
+  if (lane == 0) wr[wave] = floatx4_t{m, s, w, __int_as_float(a)};
+  __syncthreads();
+  if (t != 0 || !live) return;
+  m = -__builtin_huge_valf();
+  s = w = 0.f;
+  a = 0x7fffffff;
+  for (int i = 0; i < 4; ++i)
+    rec_merge(m, s, w, a, wr[i][0], wr[i][1], wr[i][2], __float_as_int(wr[i][3]), inv_tau);
+  row_stats[(size_t)r * 3 + 0] = m;
+  row_stats[(size_t)r * 3 + 1] = s;
+  row_stats[(size_t)r * 3 + 2] = w;
+  row_argmax[r] = a;
+}
+
 // ---- MFMA ---------------------------------------------------------------------
 // v_mfma_f32_16x16x32_bf16: A 16x32, B 32x16, C 16x16 fp32.
 // Lane l holds A[l%16][8*(l/16) .. +7], B[8*(l/16) .. +7][l%16] and

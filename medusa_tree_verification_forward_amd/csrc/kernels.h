@@ -129,7 +129,13 @@ int lm_record_slots(int N);                // upper bound of lm_head_blocks over
 int gemm_splits(int epi, int N, int K, bool f32, int M);   // K slices of the QKV / output projection of M rows
 hipError_t launch_qkv(const GemmParams& p, hipStream_t st);
 hipError_t launch_oproj(const GemmParams& p, hipStream_t st);
-hipError_t launch_lm_head(GemmParams p, float* row_stats, int* row_argmax, hipStream_t st);
+// merge_rows = false leaves the row-statistics merge of the records in
+// p.part to the caller (the exact-mode composite step runs it beside the
+// node posterior).
+hipError_t launch_lm_head(GemmParams p, float* row_stats, int* row_argmax, hipStream_t st,
+                          bool merge_rows = true);
+hipError_t launch_row_stats_merge(const float* part, int G, int M, float inv_tau,
+                                  float* row_stats, int* row_argmax, hipStream_t st);
 
 // ---- tree attention ---------------------------------------------------------------
 constexpr int kAttnChunk = 256;   // prefix keys per split
@@ -178,6 +184,12 @@ struct PostArgs {
   int32_t* last_node;
   int32_t* out_tokens;         // [B][K+1]
   int32_t* next_root;
+  // exact-mode composite step: the row-statistics merge of the LM head's
+  // records, run by extra workgroups of the node posterior (null: not)
+  const float* lm_part;        // [B T][lm_G][4]
+  int lm_G;
+  float* row_stats_out;        // [B][T][3]
+  int32_t* row_argmax_out;     // [B][T]
 };
 hipError_t launch_posterior(const PostArgs& a, hipStream_t st);
 

@@ -976,42 +976,8 @@ constexpr int kRowMergeThreads = 256;
 __global__ __launch_bounds__(kRowMergeThreads) void row_stats_merge_kernel(
     const float* __restrict__ part, int G, float inv_tau, float* __restrict__ row_stats,
     int* __restrict__ row_argmax) {
-  constexpr int RB = 8;
-  const int r = blockIdx.x, t = threadIdx.x, lane = t & 63, wave = t >> 6;
-  float m = kNegInf, s = 0.f, w = 0.f;
-  int a = 0x7fffffff;
-  for (int g0 = 0; g0 < G; g0 += kRowMergeThreads * RB) {
-    floatx4_t rec[RB];
-#pragma unroll
-    for (int u = 0; u < RB; ++u) {
-      const int g = min(g0 + t + kRowMergeThreads * u, G - 1);
-      rec[u] = *reinterpret_cast<const floatx4_t*>(part + ((size_t)r * G + g) * 4);
-    }
-#pragma unroll
-    for (int u = 0; u < RB; ++u)
-      if (g0 + t + kRowMergeThreads * u < G)
-        rec_merge(m, s, w, a, rec[u][0], rec[u][1], rec[u][2], __float_as_int(rec[u][3]),
-                  inv_tau);
-  }
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) {
-    const float m2 = __shfl_xor(m, off), s2 = __shfl_xor(s, off), w2 = __shfl_xor(w, off);
-    const int a2 = __shfl_xor(a, off);
-    rec_merge(m, s, w, a, m2, s2, w2, a2, inv_tau);
-  }
   __shared__ floatx4_t wr[kRowMergeThreads / 64];
-  if (lane == 0) wr[wave] = floatx4_t{m, s, w, __int_as_float(a)};
-  __syncthreads();
-  if (t != 0) return;
-  m = kNegInf;
-  s = w = 0.f;
-  a = 0x7fffffff;
-  for (int i = 0; i < kRowMergeThreads / 64; ++i)
-    rec_merge(m, s, w, a, wr[i][0], wr[i][1], wr[i][2], __float_as_int(wr[i][3]), inv_tau);
-  row_stats[(size_t)r * 3 + 0] = m;
-  row_stats[(size_t)r * 3 + 1] = s;
-  row_stats[(size_t)r * 3 + 2] = w;
-  row_argmax[r] = a;
+  row_records_merge(part, G, inv_tau, blockIdx.x, threadIdx.x, true, wr, row_stats, row_argmax);
 }
 
 // Tile configuration: waves per workgroup (= 16-column stripes), m-tiles
@@ -1198,7 +1164,15 @@ hipError_t launch_oproj(const GemmParams& p, hipStream_t st) {
   return launch_split<EPI_OPROJ>(p, st);
 }
 
-hipError_t launch_lm_head(GemmParams p, float* row_stats, int* row_argmax, hipStream_t st) {
+hipError_t launch_row_stats_merge(const float* part, int G, int M, float inv_tau,
+                                  float* row_stats, int* row_argmax, hipStream_t st) {
+  hipLaunchKernelGGL(row_stats_merge_kernel, dim3(M), dim3(kRowMergeThreads), 0, st, part, G,
+                     inv_tau, row_stats, row_argmax);
+  return hipGetLastError();
+}
+
+hipError_t launch_lm_head(GemmParams p, float* row_stats, int* row_argmax, hipStream_t st,
+                          bool merge_rows) {
   p.group_cols = 16 * config_for(p.M, p.N, EPI_LM).wv;
   RowsCfg rc;
   hipError_t e;
@@ -1206,7 +1180,7 @@ hipError_t launch_lm_head(GemmParams p, float* row_stats, int* row_argmax, hipSt
     e = launch_rows<EPI_LM>(p, rc, st);
   else
     e = p.f32 ? launch_main<F32, EPI_LM>(p, 1, st) : launch_main<BF16, EPI_LM>(p, 1, st);
-  if (e != hipSuccess) return e;
+  if (e != hipSuccess || !merge_rows) return e;
   hipLaunchKernelGGL(row_stats_merge_kernel, dim3(p.M), dim3(kRowMergeThreads), 0, st, p.part,
                      lm_head_blocks(p.N, p.M, p.f32), p.inv_tau, row_stats, row_argmax);
   return hipGetLastError();

@@ -358,6 +358,15 @@ __device__ __forceinline__ float pick32(const float (&r)[kExactPer], int i) {
 }
 
 __global__ __launch_bounds__(1024) void exact_node_kernel(PostArgs a) {
+  if (blockIdx.x >= a.T) {
+    // workgroups past the nodes (composite step): the row-statistics merge
+    // of the LM head's records, 4 rows a workgroup, beside the nodes' work
+    __shared__ floatx4_t wr[4][4];
+    const int grp = threadIdx.x >> 8, n = 4 * (blockIdx.x - a.T) + grp;
+    row_records_merge(a.lm_part, a.lm_G, a.inv_tau, blockIdx.y * a.T + min(n, a.T - 1),
+                      threadIdx.x & 255, n < a.T, wr[grp], a.row_stats_out, a.row_argmax_out);
+    return;
+  }
   const int v = blockIdx.x, b = blockIdx.y, t = threadIdx.x;
   const int T = a.T, V = a.V, K = a.K;
   const int x0 = kExactPer * t;
@@ -796,7 +805,8 @@ hipError_t launch_posterior_commit(const PostArgs& a, const CommitArgs& c, hipSt
     // exact: the node-parallel posterior, then the walk with the commit;
     // vocabularies past the LDS kernel take the separate kernels
     if (a.V <= kExactLdsV && exact_lds_fits()) {
-      hipLaunchKernelGGL(exact_node_kernel, dim3(a.T, a.B), dim3(1024), 0, st, a);
+      const int rx = a.lm_part ? (a.T + 3) / 4 : 0;   // row-statistics workgroups
+      hipLaunchKernelGGL(exact_node_kernel, dim3(a.T + rx, a.B), dim3(1024), 0, st, a);
       hipError_t e = hipGetLastError();
       if (e != hipSuccess) return e;
       const dim3 grid(commit_parts(a.B), a.B);
@@ -806,7 +816,12 @@ hipError_t launch_posterior_commit(const PostArgs& a, const CommitArgs& c, hipSt
         hipLaunchKernelGGL(exact_walk_commit_kernel<BF16>, grid, dim3(kPostThreads), 0, st, a, c);
       return hipGetLastError();
     }
-    hipError_t e = launch_posterior(a, st);
+    hipError_t e = hipSuccess;
+    if (a.lm_part)
+      e = launch_row_stats_merge(a.lm_part, a.lm_G, a.B * a.T, a.inv_tau, a.row_stats_out,
+                                 a.row_argmax_out, st);
+    if (e != hipSuccess) return e;
+    e = launch_posterior(a, st);
     if (e != hipSuccess) return e;
     return launch_commit(c, st);
   }
