@@ -355,6 +355,240 @@ __global__ __launch_bounds__(64 * kPfxWaves) void prefix_attn_bf16_kernel(AttnAr
   }
 }
 
+// Per-wave split-KV kernel for trees of at most three query tiles and
+// 128-wide heads: wave w of a workgroup takes keys 32 w .. 32 w + 31 of each
+// of the workgroup's chunks and keeps its own running softmax (max, sum,
+// output) for every query, so that a chunk needs no exchange between the
+// waves and no barrier: S^T = K Q^T (K fragments from memory, Q fragments
+// from LDS); P = 2^(s - m) stays in registers, packed in the key order of
+// the transposing read, as the B operand of O^T += V^T P^T (V^T read from
+// the wave's own V rows in LDS); the next chunk's K and V loads go out into
+// the registers the current one has finished with. The eight states are
+// combined once, at the end, into the workgroup's partial: maxima and sums
+// through LDS (each wave then scales its outputs), and the outputs summed
+// over the waves in wave order, wave w owning dh tile w.
+template <int QT>
+__global__ __launch_bounds__(64 * kPfxWaves) void prefix_attn_wave_kernel(AttnArgs a) {
+  using S = uint16_t;
+  constexpr int DH = 128, DS = DH / 32, DT = DH / 16, VP = DH / 8, VL = 32 * VP / 64;
+  constexpr int VSTR = DH + 16, QSTR = DH + 8;
+  static_assert(DT == kPfxWaves, "wave w owns dh tile w of the partial");
+  constexpr int kQBytes = 16 * QT * QSTR * 2, kVBytes = kPfxWaves * 32 * VSTR * 2;
+  constexpr int kXBytes = kPfxWaves * (DT / 2) * QT * 64 * 16;   // half the dh tiles of every wave
+  constexpr int kLdsBytes = kQBytes + kVBytes > kXBytes ? kQBytes + kVBytes : kXBytes;
+  const int h = blockIdx.y, b = blockIdx.z, G = gridDim.x;
+  const int T = a.T, H = a.H;
+  const int L = min(max(a.kv_len[b], 0), a.Lmax);
+  int s = blockIdx.x;   // chunks s, s + G, ... of (b, h)
+  if (s * kAttnChunk >= L) return;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int li = lane & 15, lq = lane >> 4;
+  const float sl2 = a.scale * kLog2e;
+  // the Q rows and each wave's V rows during the chunks; the outputs' exchange after them
+  __shared__ __attribute__((aligned(16))) unsigned char lds[kLdsBytes];
+  __shared__ float st_m[kPfxWaves][16 * QT], st_l[kPfxWaves][16 * QT];
+  S* qs = reinterpret_cast<S*>(lds);                                   // [16 QT][QSTR]
+  S* vw = reinterpret_cast<S*>(lds + kQBytes) + wave * 32 * VSTR;      // this wave's [32][VSTR]
+
+  const size_t head = ((size_t)b * H + h) * a.Lmax;
+  const S* __restrict__ kc = reinterpret_cast<const S*>(a.k_cache) + head * DH;
+  const S* __restrict__ vc = reinterpret_cast<const S*>(a.v_cache) + head * DH;
+  const S* __restrict__ qb = reinterpret_cast<const S*>(a.q);
+  // this wave's 32 keys of a chunk (rows past L are read clamped and masked
+  // later): K fragments (A operand), key 16 kt + li, dh 8 lq + 32 ds .. + 7;
+  // V rows, piece p = lane + 64 i at key p / VP, dh 8 (p % VP)
+  auto load_kv = [&](int chunk, u32x4_t(&kf)[2][DS], u32x4_t(&vv)[VL]) {
+    const int key0 = chunk * kAttnChunk + 32 * wave;
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int ds = 0; ds < DS; ++ds)
+        kf[kt][ds] = load16(kc + (size_t)min(key0 + 16 * kt + li, L - 1) * DH + 8 * lq + 32 * ds);
+#pragma unroll
+    for (int i = 0; i < VL; ++i) {
+      const int p = lane + 64 * i, kk = p / VP, c = p - kk * VP;
+      vv[i] = load16(vc + (size_t)min(key0 + kk, L - 1) * DH + 8 * c);
+    }
+  };
+  u32x4_t kf[2][DS], vv[VL];
+  load_kv(s, kf, vv);
+  {
+    // every query tile's rows, once (rows past T read clamped, never used)
+    constexpr int QP = 16 * QT * VP, QRN = (QP + 64 * kPfxWaves - 1) / (64 * kPfxWaves);
+#pragma unroll
+    for (int r = 0; r < QRN; ++r) {
+      const int p = threadIdx.x + 64 * kPfxWaves * r;
+      const int pc = min(p, QP - 1), qr = pc / VP, c = pc - qr * VP;
+      const u32x4_t v = load16(qb + (((size_t)b * T + min(qr, T - 1)) * H + h) * DH + 8 * c);
+      if (p < QP) *reinterpret_cast<u32x4_t*>(qs + qr * QSTR + 8 * c) = v;
+    }
+  }
+  floatx4_t o[QT][DT];
+  float m_run[QT], l_run[QT];   // of query 16 u + li
+#pragma unroll
+  for (int u = 0; u < QT; ++u) {
+    m_run[u] = kNegInf;
+    l_run[u] = 0.f;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) o[u][dt] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+  }
+  __syncthreads();   // the Q rows are published
+  for (;;) {
+    const int key0 = s * kAttnChunk + 32 * wave;
+    const int sn = s + G;
+    const bool more = sn * kAttnChunk < L;
+    // the V rows into this wave's rows (its reads of the previous chunk's
+    // came first: one wave's LDS operations run in order)
+#pragma unroll
+    for (int i = 0; i < VL; ++i) {
+      const int p = lane + 64 * i, kk = p / VP, c = p - kk * VP;
+      *reinterpret_cast<u32x4_t*>(vw + kk * VSTR + 8 * c) = vv[i];
+    }
+    // ---- S^T: lane holds keys key0 + 16 kt + 4 lq + j of query 16 u + li ----
+    floatx4_t st[2][QT];
+#pragma unroll
+    for (int u = 0; u < QT; ++u) {
+      u32x4_t qf[DS];
+#pragma unroll
+      for (int ds = 0; ds < DS; ++ds)
+        qf[ds] = *reinterpret_cast<const u32x4_t*>(qs + (16 * u + li) * QSTR + 8 * lq + 32 * ds);
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt) {
+        st[kt][u] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ds = 0; ds < DS; ++ds) st[kt][u] = mfma16x16x32_bf16(kf[kt][ds], qf[ds], st[kt][u]);
+      }
+    }
+    // the next chunk's loads, into the registers this one is done with
+    if (more) load_kv(sn, kf, vv);
+    // ---- running softmax of each query over the wave's keys; P^T in registers ----
+    u32x4_t pw[QT];
+#pragma unroll
+    for (int u = 0; u < QT; ++u) {
+      float mc = kNegInf;
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const bool ok = key0 + 16 * kt + 4 * lq + j < L;
+          const float v = ok ? st[kt][u][j] * sl2 : kNegInf;
+          st[kt][u][j] = v;
+          mc = fmaxf(mc, v);
+        }
+      mc = fmaxf(mc, __shfl_xor(mc, 16));
+      mc = fmaxf(mc, __shfl_xor(mc, 32));
+      const float mn = fmaxf(m_run[u], mc);
+      const float alpha = m_run[u] == kNegInf ? 0.f : __builtin_amdgcn_exp2f(m_run[u] - mn);
+      float rs = 0.f;
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const float pv = mn == kNegInf ? 0.f : __builtin_amdgcn_exp2f(st[kt][u][j] - mn);
+          st[kt][u][j] = pv;
+          rs += pv;
+        }
+      rs += __shfl_xor(rs, 16);
+      rs += __shfl_xor(rs, 32);
+      l_run[u] = l_run[u] * alpha + rs;
+      m_run[u] = mn;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) o[u][dt][j] *= alpha;
+      // key 16 kt + 4 lq + j of the wave's 32 at B-operand position 8 lq + 4 kt + j
+      pw[u][0] = pack_bf16x2(st[0][u][0], st[0][u][1]);
+      pw[u][1] = pack_bf16x2(st[0][u][2], st[0][u][3]);
+      pw[u][2] = pack_bf16x2(st[1][u][0], st[1][u][1]);
+      pw[u][3] = pack_bf16x2(st[1][u][2], st[1][u][3]);
+    }
+    // ---- O^T += V^T P^T over the wave's 32 keys ----
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+      // A: lane gets dh 16 dt + li of keys 4 lq + (0..3) and 16 + 4 lq + (0..3)
+      const S* v0 = vw + (4 * lq + (li >> 2)) * VSTR + 16 * dt + 4 * (li & 3);
+      const uint2 lo = lds_read_tr16(v0);
+      const uint2 hi = lds_read_tr16(v0 + 16 * VSTR);
+      u32x4_t vf;
+      vf[0] = lo.x;
+      vf[1] = lo.y;
+      vf[2] = hi.x;
+      vf[3] = hi.y;
+#pragma unroll
+      for (int u = 0; u < QT; ++u) o[u][dt] = mfma16x16x32_bf16(vf, pw[u], o[u][dt]);
+    }
+    if (!more) break;
+    s = sn;
+  }
+  // ---- the eight states into the workgroup's partial (slot blockIdx.x) ----
+  if (lq == 0)
+#pragma unroll
+    for (int u = 0; u < QT; ++u) {
+      st_m[wave][16 * u + li] = m_run[u];
+      st_l[wave][16 * u + li] = l_run[u];
+    }
+  __syncthreads();   // every wave is past its chunks (Q and V rows free) and its state is in
+  float Mq[QT], Lq[QT];
+#pragma unroll
+  for (int u = 0; u < QT; ++u) {
+    const int q = 16 * u + li;
+    float M = kNegInf;
+#pragma unroll
+    for (int w = 0; w < kPfxWaves; ++w) M = fmaxf(M, st_m[w][q]);
+    float l = 0.f;
+#pragma unroll
+    for (int w = 0; w < kPfxWaves; ++w) {
+      const float mw = st_m[w][q];
+      l += mw == kNegInf ? 0.f : st_l[w][q] * __builtin_amdgcn_exp2f(mw - M);
+    }
+    Mq[u] = M;
+    Lq[u] = l;
+    const float c = m_run[u] == kNegInf ? 0.f : __builtin_amdgcn_exp2f(m_run[u] - M);
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) o[u][dt][j] *= c;
+  }
+  const size_t base = ((size_t)b * H + h) * a.NS * T + (size_t)blockIdx.x * T;
+  floatx4_t* xb = reinterpret_cast<floatx4_t*>(lds);   // [wave][DT / 2][QT][64]
+#pragma unroll
+  for (int half = 0; half < 2; ++half) {
+    if (half) __syncthreads();   // the first half's sums are read
+#pragma unroll
+    for (int d4 = 0; d4 < DT / 2; ++d4)
+#pragma unroll
+      for (int u = 0; u < QT; ++u)
+        xb[((wave * (DT / 2) + d4) * QT + u) * 64 + lane] = o[u][(DT / 2) * half + d4];
+    __syncthreads();
+    if (wave / (DT / 2) == half) {
+      const int d4 = wave % (DT / 2), dt = wave;
+#pragma unroll
+      for (int u = 0; u < QT; ++u) {
+        floatx4_t acc = floatx4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int w = 0; w < kPfxWaves; ++w) {
+          const floatx4_t x = xb[((w * (DT / 2) + d4) * QT + u) * 64 + lane];
+#pragma unroll
+          for (int j = 0; j < 4; ++j) acc[j] += x[j];
+        }
+        const int query = 16 * u + li;
+        if (query < T)
+          *reinterpret_cast<float4*>(a.part_o + base * DH + ((size_t)dt * T + query) * 16 +
+                                     4 * lq) = make_float4(acc[0], acc[1], acc[2], acc[3]);
+      }
+    }
+  }
+  if (wave == 0 && lq == 0)
+#pragma unroll
+    for (int u = 0; u < QT; ++u) {
+      const int query = 16 * u + li;
+      if (query < T) {
+        a.part_ml[(base + query) * 2 + 0] = Mq[u];
+        a.part_ml[(base + query) * 2 + 1] = Lq[u];
+      }
+    }
+}
+
 // fp32 prefix kernel: SC keys per round are staged in LDS (K row-major, V
 // transposed); the next round's global loads are in flight while the waves
 // compute the current one. Waves split the query tiles (16 queries each);
@@ -681,6 +915,24 @@ hipError_t launch_bf16(const AttnArgs& a, hipStream_t st) {
   // chunk leaves its own.
   const bool acc = MQ > 4 || a.NS > 2 * G;
   m.NP = acc ? G : a.NS;
+  if constexpr (DH == 128) {
+    // workgroups that loop over chunks, trees of at most three query tiles:
+    // the per-wave kernel (one partial per workgroup). With one chunk a
+    // workgroup its closing exchange costs more than the barriers it saves
+    // (7B: 15.2 against 12.1 us).
+    if (acc && MQ <= 3) {
+      m.NP = G;
+      switch (MQ) {
+        case 1: hipLaunchKernelGGL((prefix_attn_wave_kernel<1>), grid, block, 0, st, a); break;
+        case 2: hipLaunchKernelGGL((prefix_attn_wave_kernel<2>), grid, block, 0, st, a); break;
+        default: hipLaunchKernelGGL((prefix_attn_wave_kernel<3>), grid, block, 0, st, a); break;
+      }
+      hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+      hipLaunchKernelGGL((attn_merge_kernel<BF16, DH>), dim3(a.T, a.H, a.B), dim3(64), 0, st, m);
+      return hipGetLastError();
+    }
+  }
   // 5 to 9 query tiles: all Q rows held in LDS (151 KB with the V and P
   // buffers for 128-wide heads), so no query group is reloaded per chunk
   if (MQ > 4 && MQ <= kHeldTiles && attn_hold_q())
