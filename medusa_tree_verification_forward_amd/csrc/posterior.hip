@@ -348,6 +348,43 @@ __device__ __forceinline__ void load_row32(const float* __restrict__ row, int V,
   }
 }
 
+// Rows of V % 4 == 0 tokens, read coalesced: thread T loads float4s
+// T + 1024 i of the row (clamped into it, as load_row32 does) into its
+// registers r[4 i .. 4 i + 3], and unstage_row32 passes them through LDS
+// (float4 column j of thread t's 32 tokens at column j ^ ((t >> 1) & 7),
+// which keeps the writes of 16 consecutive threads and the reads of their
+// own tokens free of bank conflicts) into the layout of load_row32: thread
+// t holds tokens 32 t .. 32 t + 31, in the same registers.
+__device__ __forceinline__ void stage_row32(const float* __restrict__ row, int V,
+                                            float (&r)[kExactPer]) {
+#pragma unroll
+  for (int i = 0; i < kExactPer / 4; ++i) {
+    const int f = threadIdx.x + 1024 * i;
+    const floatx4_t v = *reinterpret_cast<const floatx4_t*>(row + max(min(4 * f, V - 4), 0));
+#pragma unroll
+    for (int e = 0; e < 4; ++e) r[4 * i + e] = v[e];
+  }
+}
+// Every thread calls it; `buf` (kExactLdsV floats) is free on entry and may
+// be written again after a barrier that follows the call.
+__device__ __forceinline__ void unstage_row32(float (&r)[kExactPer], floatx4_t* buf) {
+  static_assert(kExactPer == 32, "eight float4 columns a thread");
+#pragma unroll
+  for (int i = 0; i < kExactPer / 4; ++i) {
+    const int f = threadIdx.x + 1024 * i, tt = f >> 3, j = f & 7;
+    buf[8 * tt + (j ^ ((tt >> 1) & 7))] =
+        floatx4_t{r[4 * i], r[4 * i + 1], r[4 * i + 2], r[4 * i + 3]};
+  }
+  __syncthreads();
+  const int t = threadIdx.x;
+#pragma unroll
+  for (int j = 0; j < kExactPer / 4; ++j) {
+    const floatx4_t v = buf[8 * t + (j ^ ((t >> 1) & 7))];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) r[4 * j + e] = v[e];
+  }
+}
+
 // Register i of an array, for a runtime i the same in the whole wave
 // (selects, no indexed register access).
 __device__ __forceinline__ float pick32(const float (&r)[kExactPer], int i) {
@@ -376,8 +413,15 @@ __global__ __launch_bounds__(1024) void exact_node_kernel(PostArgs a) {
   __shared__ float s_ua[MAXT];
   __shared__ float s_pq[2];
   __shared__ int s_next;
+  // the rows (V % 4 == 0) are read coalesced and handed out through LDS
+  __shared__ floatx4_t rowbuf[kExactLdsV / 4];
+  const bool coalesced = (V & 3) == 0;
   float p[kExactPer], q[kExactPer];
-  load_row32(a.verify_logits + ((size_t)b * T + v) * V, V, p);
+  const float* prow = a.verify_logits + ((size_t)b * T + v) * V;
+  if (coalesced)
+    stage_row32(prow, V, p);
+  else
+    load_row32(prow, V, p);
   if (t < T) {
     s_par[t] = a.parent[t];
     s_tok[t] = a.tokens[(size_t)b * T + t];
@@ -389,7 +433,16 @@ __global__ __launch_bounds__(1024) void exact_node_kernel(PostArgs a) {
   for (int x = v; x != 0 && dv < K; x = min(max(s_par[x], 0), T - 1)) ++dv;
   const bool kids = dv < K;
   const float* hl = a.head_logits + ((size_t)b * K + min(dv, K - 1)) * V;
-  if (kids) load_row32(hl, V, q);   // in flight during the softmax below
+  if (coalesced) {
+    if (kids) stage_row32(hl, V, q);   // in flight while p is handed out
+    unstage_row32(p, rowbuf);
+    if (kids) {
+      __syncthreads();   // every thread has its p
+      unstage_row32(q, rowbuf);
+    }
+  } else if (kids) {
+    load_row32(hl, V, q);   // in flight during the softmax below
+  }
   // p = softmax(l_v / tau): unnormalised weights and their scale
   float mx = kNegInf;
 #pragma unroll
