@@ -152,6 +152,8 @@ struct AttnArgs {
   float scale;
   int NS;                      // prefix splits per (b, h) (kAttnChunk keys each)
   int NP;                      // partials per (b, h) the merge reads (set by the launcher)
+  int qgroups;                 // per-wave kernel: groups of 3 query tiles
+  int chunk_sets;              // per-wave kernel: workgroups (chunk sets) per (b, h, group)
   float* part_o;               // [B][H][NS][Dh/16][T][16]
   float* part_ml;              // [B][H][NS][T][2]
   float* out;                  // [B][T][H][Dh] fp32 (or null)

@@ -376,10 +376,21 @@ __global__ __launch_bounds__(64 * kPfxWaves) void prefix_attn_wave_kernel(AttnAr
   constexpr int kQBytes = 16 * QT * QSTR * 2, kVBytes = kPfxWaves * 32 * VSTR * 2;
   constexpr int kXBytes = kPfxWaves * (DT / 2) * QT * 64 * 16;   // half the dh tiles of every wave
   constexpr int kLdsBytes = kQBytes + kVBytes > kXBytes ? kQBytes + kVBytes : kXBytes;
-  const int h = blockIdx.y, b = blockIdx.z, G = gridDim.x;
+  // One-dimensional grid over units (b, h, s) -- s the chunk set, the
+  // workgroup taking chunks s, s + G, ... of (b, h) -- and query groups qg
+  // (tiles 3 qg .. 3 qg + QT - 1): linear id 8 nqg j + 8 qg + i is unit
+  // 8 j + i, so that a unit's query groups have ids 8 apart (one XCD, at
+  // about the same time: its chunks are read from HBM once and from the L2
+  // by the others). With one group, unit = linear id.
+  const int nqg = a.qgroups, G = a.chunk_sets;
+  const int lin = blockIdx.x, blk = lin / (8 * nqg), within = lin - blk * 8 * nqg;
+  const int qg = within >> 3, unit = 8 * blk + (within & 7);
+  if (unit >= G * a.H * a.B) return;
+  const int sset = unit % G, h = (unit / G) % a.H, b = unit / (G * a.H);
+  const int q0 = 48 * qg;
   const int T = a.T, H = a.H;
   const int L = min(max(a.kv_len[b], 0), a.Lmax);
-  int s = blockIdx.x;   // chunks s, s + G, ... of (b, h)
+  int s = sset;
   if (s * kAttnChunk >= L) return;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int li = lane & 15, lq = lane >> 4;
@@ -419,7 +430,8 @@ __global__ __launch_bounds__(64 * kPfxWaves) void prefix_attn_wave_kernel(AttnAr
     for (int r = 0; r < QRN; ++r) {
       const int p = threadIdx.x + 64 * kPfxWaves * r;
       const int pc = min(p, QP - 1), qr = pc / VP, c = pc - qr * VP;
-      const u32x4_t v = load16(qb + (((size_t)b * T + min(qr, T - 1)) * H + h) * DH + 8 * c);
+      const u32x4_t v =
+          load16(qb + (((size_t)b * T + min(q0 + qr, T - 1)) * H + h) * DH + 8 * c);
       if (p < QP) *reinterpret_cast<u32x4_t*>(qs + qr * QSTR + 8 * c) = v;
     }
   }
@@ -549,7 +561,7 @@ __global__ __launch_bounds__(64 * kPfxWaves) void prefix_attn_wave_kernel(AttnAr
 #pragma unroll
       for (int j = 0; j < 4; ++j) o[u][dt][j] *= c;
   }
-  const size_t base = ((size_t)b * H + h) * a.NS * T + (size_t)blockIdx.x * T;
+  const size_t base = ((size_t)b * H + h) * a.NS * T + (size_t)sset * T;
   floatx4_t* xb = reinterpret_cast<floatx4_t*>(lds);   // [wave][DT / 2][QT][64]
 #pragma unroll
   for (int half = 0; half < 2; ++half) {
@@ -571,7 +583,7 @@ __global__ __launch_bounds__(64 * kPfxWaves) void prefix_attn_wave_kernel(AttnAr
 #pragma unroll
           for (int j = 0; j < 4; ++j) acc[j] += x[j];
         }
-        const int query = 16 * u + li;
+        const int query = q0 + 16 * u + li;
         if (query < T)
           *reinterpret_cast<float4*>(a.part_o + base * DH + ((size_t)dt * T + query) * 16 +
                                      4 * lq) = make_float4(acc[0], acc[1], acc[2], acc[3]);
@@ -581,7 +593,7 @@ __global__ __launch_bounds__(64 * kPfxWaves) void prefix_attn_wave_kernel(AttnAr
   if (wave == 0 && lq == 0)
 #pragma unroll
     for (int u = 0; u < QT; ++u) {
-      const int query = 16 * u + li;
+      const int query = q0 + 16 * u + li;
       if (query < T) {
         a.part_ml[(base + query) * 2 + 0] = Mq[u];
         a.part_ml[(base + query) * 2 + 1] = Lq[u];
@@ -922,11 +934,33 @@ hipError_t launch_bf16(const AttnArgs& a, hipStream_t st) {
     // (7B: 15.2 against 12.1 us).
     if (acc && MQ <= 3) {
       m.NP = G;
+      AttnArgs w = a;
+      w.qgroups = 1;
+      w.chunk_sets = G;
+      const dim3 wgrid((G * a.H * a.B + 7) / 8 * 8);
       switch (MQ) {
-        case 1: hipLaunchKernelGGL((prefix_attn_wave_kernel<1>), grid, block, 0, st, a); break;
-        case 2: hipLaunchKernelGGL((prefix_attn_wave_kernel<2>), grid, block, 0, st, a); break;
-        default: hipLaunchKernelGGL((prefix_attn_wave_kernel<3>), grid, block, 0, st, a); break;
+        case 1: hipLaunchKernelGGL((prefix_attn_wave_kernel<1>), wgrid, block, 0, st, w); break;
+        case 2: hipLaunchKernelGGL((prefix_attn_wave_kernel<2>), wgrid, block, 0, st, w); break;
+        default: hipLaunchKernelGGL((prefix_attn_wave_kernel<3>), wgrid, block, 0, st, w); break;
       }
+      hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+      hipLaunchKernelGGL((attn_merge_kernel<BF16, DH>), dim3(a.T, a.H, a.B), dim3(64), 0, st, m);
+      return hipGetLastError();
+    }
+    if (MQ > 3) {
+      // larger trees: a set of workgroups per group of three query tiles,
+      // each set reading the same chunks (from L2 or the Infinity Cache for
+      // all but one), as many chunk sets as fill the compute units once
+      const int nqg = (MQ + 2) / 3;
+      int G2 = cus / (nqg * a.B * a.H);
+      G2 = G2 < 1 ? 1 : (G2 > a.NS ? a.NS : G2);
+      AttnArgs w = a;
+      w.qgroups = nqg;
+      w.chunk_sets = G2;
+      m.NP = G2;
+      const dim3 wgrid((G2 * a.H * a.B + 7) / 8 * 8 * nqg);
+      hipLaunchKernelGGL((prefix_attn_wave_kernel<3>), wgrid, block, 0, st, w);
       hipError_t e = hipGetLastError();
       if (e != hipSuccess) return e;
       hipLaunchKernelGGL((attn_merge_kernel<BF16, DH>), dim3(a.T, a.H, a.B), dim3(64), 0, st, m);
