@@ -1011,7 +1011,14 @@ Config config_for(int M, int N, int epi) {
     if (epi == EPI_LM) return Config{8, 3, 8, 16};
     return small_config(N).c;
   }
-  // more rows: 8-wave workgroups of 12 m-tiles (A chunks of 48 KB, double
+  // The output projection of more than 48 rows: passes of 48 rows, 8-wave
+  // workgroups (128 columns) with 16 weight loads in flight per wave; the
+  // passes of a column group run on one XCD and share its weight reads in
+  // L2 (vicuna13b 136 rows: 25.1 us where one 192-row pass took 39.9, its
+  // eight waves each reading twelve A tiles from LDS every k-tile).
+  if (epi == EPI_OPROJ) return Config{8, 3, 8, 16};
+  // QKV and LM head of more rows where the row-split kernel does not apply
+  // (fp32): 8-wave workgroups of 12 m-tiles (A chunks of 48 KB, double
   // buffered) with 4 weight loads in flight per wave (8 spills registers
   // and measured no faster)
   return Config{8, 12, 4, 4};
@@ -1141,10 +1148,10 @@ int gemm_splits(int epi, int N, int K, bool f32, int M) {
   const int nkt = K / (f32 ? 16 : 32);
   int ks = 1;
   if (M > 48) {
-    // workgroups of the 12-m-tile configuration take most of a compute
-    // unit's LDS: split K while the grid still fits one workgroup per unit
+    // split K while the grid still fits one workgroup per compute unit
     const Config c = config_for(M, N, epi);
     const int wgs = (N + 16 * c.wv - 1) / (16 * c.wv) * ((M + 16 * c.mt - 1) / (16 * c.mt));
+    // (two a unit measured slower: 13B output projection 35.5 against 25.0 us)
     while (wgs * ks * 2 <= device_cus() && nkt / (ks * 2) >= 8 && ks < kMaxSplits) ks *= 2;
     return ks;
   }
