@@ -579,21 +579,24 @@ __global__ __launch_bounds__(256) void act_frag_kernel(const float* __restrict__
 // NG tile rows of one wave over nt column blocks, DS blocks (NG DS tiles and
 // DS A fragments) in flight: wp[g] points at the lane's 8 weights of the
 // first block in group g, ap at its A fragment of the first block. Requires
-// nt a positive multiple of DS. The weight loads are plain (cached) loads: a
-// tile reads half of each 128-byte line and the next block the other half,
-// and with the non-temporal hint the line was often gone by then (37% more
-// HBM traffic).
+// nt a positive multiple of DS. STREAM: the weight loads carry the
+// non-temporal hint -- for packed weights, whose tiles are whole 1 KB runs
+// (batch of 8: W2 236 -> 210 us, W1 34.8 -> 30.3). From a row-major W the
+// loads are plain (cached): there a tile reads half of each 128-byte line and
+// the next block the other half, and with the hint the line was often gone
+// by then (37% more HBM traffic).
 // `step`: elements from one column block of a lane's row piece to the next
 // (32 in a row-major W, ntiles * 512 in a packed one).
-template <int NG, int DS>
+template <int NG, int DS, bool STREAM = false>
 __device__ __forceinline__ void tile_stream(const uint16_t* const (&wp)[NG], size_t step,
                                             const u32x4_t* __restrict__ ap, int nt,
                                             floatx4_t (&acc)[NG]) {
+  auto wload = [](const uint16_t* q) { return STREAM ? load16_stream(q) : load16(q); };
   u32x4_t wr[DS][NG], ar[DS];
 #pragma unroll
   for (int j = 0; j < DS; ++j) {
 #pragma unroll
-    for (int g = 0; g < NG; ++g) wr[j][g] = load16(wp[g] + step * j);
+    for (int g = 0; g < NG; ++g) wr[j][g] = wload(wp[g] + step * j);
     ar[j] = load16(ap + 64 * j);
   }
 #pragma unroll
@@ -606,7 +609,7 @@ __device__ __forceinline__ void tile_stream(const uint16_t* const (&wp)[NG], siz
 #pragma unroll
       for (int g = 0; g < NG; ++g) {
         acc[g] = mfma16x16x32_bf16(ar[j], wr[j][g], acc[g]);
-        wr[j][g] = load16(wp[g] + step * tn);
+        wr[j][g] = wload(wp[g] + step * tn);
       }
       ar[j] = load16(ap + 64 * tn);
     }
@@ -622,7 +625,7 @@ __device__ __forceinline__ void tile_stream(const uint16_t* const (&wp)[NG], siz
 // A workgroup takes 16 (4 / KS) consecutive rows of the K d rows: wave w
 // streams rows 16 (w / KS) .. + 15 over column blocks of part w % KS of d,
 // and the KS partial tiles are summed through LDS in part order.
-template <int KS, int DS>
+template <int KS, int DS, bool PACKED>
 __global__ __launch_bounds__(kHeadWaves * 64, 4) void heads_w1_tile_kernel(
     const float* __restrict__ h, int B, int b0, int K, int d, const uint16_t* __restrict__ W1,
     const uint16_t* __restrict__ W1p, const float* __restrict__ b1,
@@ -646,7 +649,7 @@ __global__ __launch_bounds__(kHeadWaves * 64, 4) void heads_w1_tile_kernel(
   // kt * ntiles + nt, lane (j, q)'s piece = row j, columns 32 kt + 8 q ..)
   const uint16_t* wp[1];
   size_t step = 32;
-  if (W1p) {
+  if constexpr (PACKED) {
     const int ntiles = total / 16;
     const int nt = min((int)(blockIdx.x * RS + set), ntiles - 1);
     step = (size_t)ntiles * 512;
@@ -655,7 +658,7 @@ __global__ __launch_bounds__(kHeadWaves * 64, 4) void heads_w1_tile_kernel(
     wp[0] = W1 + (size_t)row * d + 32 * per * part + 8 * q;
   }
   floatx4_t acc[1];
-  tile_stream<1, DS>(wp, step, hfrag + (size_t)per * part * 64 + lane, per, acc);
+  tile_stream<1, DS, PACKED>(wp, step, hfrag + (size_t)per * part * 64 + lane, per, acc);
   if constexpr (KS > 1) {
     __shared__ floatx4_t red[RS][KS - 1][64];
     if (part > 0) red[set][part - 1][lane] = acc[0];
@@ -687,7 +690,7 @@ __global__ __launch_bounds__(kHeadWaves * 64, 4) void heads_w1_tile_kernel(
 // rows of a wave stay within a few pages; rows interleaved over the waves
 // spread every wave over the whole head); the values are moved to lane = row
 // (lane 16 g + j takes row j of tile row g) for the shared top-S epilogue.
-template <int NG, int DS>
+template <int NG, int DS, bool PACKED>
 __global__ __launch_bounds__(kHeadWaves * 64, 4) void heads_w2_tile_kernel(
     int B, int b0, int K, int V, int d, const uint16_t* __restrict__ W2,
     const uint16_t* __restrict__ W2p, const u32x4_t* __restrict__ zfrag, int S,
@@ -708,13 +711,13 @@ __global__ __launch_bounds__(kHeadWaves * 64, 4) void heads_w2_tile_kernel(
   if (nrows > 0) {
     const uint16_t* wp[NG];
     size_t step = 32;
-    if (W2p) {
+    if constexpr (PACKED) {
       // packed tiles (16 rows x 32 columns, 64 lane pieces, k-major within
       // each head): lane (j, q)'s piece of tile (row block, column block t)
       // is row j, columns 32 t + 8 q .. + 7 -- the same fragment
       const int ntiles = (V + 15) / 16;
-      step = (size_t)ntiles * 512;
       const uint16_t* head = W2p + (size_t)k * ntiles * 16 * d;
+      step = (size_t)ntiles * 512;
 #pragma unroll
       for (int tg = 0; tg < NG; ++tg)
         wp[tg] = head + ((size_t)min(rb / 16 + tg, ntiles - 1) * 64 + lane) * 8;
@@ -725,7 +728,7 @@ __global__ __launch_bounds__(kHeadWaves * 64, 4) void heads_w2_tile_kernel(
                  8 * q;
     }
     floatx4_t acc[NG];
-    tile_stream<NG, DS>(wp, step, zfrag + (size_t)k * (d / 32) * 64 + lane, d / 32, acc);
+    tile_stream<NG, DS, PACKED>(wp, step, zfrag + (size_t)k * (d / 32) * 64 + lane, d / 32, acc);
 #pragma unroll
     for (int tg = 0; tg < NG; ++tg) {
       const float v0 = acc[tg][0] + acc[tg][1], v1 = acc[tg][2] + acc[tg][3];
@@ -957,12 +960,17 @@ hipError_t launch_heads_tile(const HeadsArgs& a, int b0, int G, hipStream_t st) 
   const uint16_t* W1 = reinterpret_cast<const uint16_t*>(a.W1);
   uint16_t* zf16 = reinterpret_cast<uint16_t*>(zfrag);
   const int total = a.K * d;
-#define W1_TILE(KS, DS)                                                                        \
-  hipLaunchKernelGGL((heads_w1_tile_kernel<KS, DS>),                                           \
+  const uint16_t* W1p = reinterpret_cast<const uint16_t*>(a.W1_packed);
+#define W1_TILE_P(KS, DS, P)                                                                   \
+  hipLaunchKernelGGL((heads_w1_tile_kernel<KS, DS, P>),                                        \
                      dim3((total + 16 * (kHeadWaves / KS) - 1) / (16 * (kHeadWaves / KS))),    \
-                     dim3(kHeadWaves * 64), 0, st, a.h, a.B, b0, a.K, d, W1,                   \
-                     reinterpret_cast<const uint16_t*>(a.W1_packed), a.b1, hfrag, a.z,          \
-                     zf16)
+                     dim3(kHeadWaves * 64), 0, st, a.h, a.B, b0, a.K, d, W1, W1p, a.b1, hfrag,  \
+                     a.z, zf16)
+#define W1_TILE(KS, DS)     \
+  if (W1p)                  \
+    W1_TILE_P(KS, DS, true); \
+  else                      \
+    W1_TILE_P(KS, DS, false)
   if (nblk % 32 == 0)
     W1_TILE(4, 8);
   else if (nblk % 16 == 0)
@@ -972,6 +980,7 @@ hipError_t launch_heads_tile(const HeadsArgs& a, int b0, int G, hipStream_t st) 
   else
     W1_TILE(1, 2);
 #undef W1_TILE
+#undef W1_TILE_P
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (a.ev_before) {
@@ -980,16 +989,22 @@ hipError_t launch_heads_tile(const HeadsArgs& a, int b0, int G, hipStream_t st) 
   }
   const uint16_t* W2 = reinterpret_cast<const uint16_t*>(a.W2);
   const uint16_t* W2p = reinterpret_cast<const uint16_t*>(a.W2_packed);
-#define W2_TILE(NG, DS)                                                                       \
-  hipLaunchKernelGGL((heads_w2_tile_kernel<NG, DS>), dim3(G, a.K), dim3(kHeadWaves * 64), 0, st, \
-                     a.B, b0, a.K, a.V, d, W2, W2p, zfrag, a.S, a.head_logits, a.part_val,     \
+#define W2_TILE_P(NG, DS, P)                                                                    \
+  hipLaunchKernelGGL((heads_w2_tile_kernel<NG, DS, P>), dim3(G, a.K), dim3(kHeadWaves * 64), 0, \
+                     st, a.B, b0, a.K, a.V, d, W2, W2p, zfrag, a.S, a.head_logits, a.part_val,   \
                      a.part_id, a.part_m, a.part_s, G)
+#define W2_TILE(NG, DS)     \
+  if (W2p)                  \
+    W2_TILE_P(NG, DS, true); \
+  else                      \
+    W2_TILE_P(NG, DS, false)
   // d is a multiple of 64: nblk is even
   if (nblk % 4 == 0)
     W2_TILE(kW2TileNg, 4);
   else
     W2_TILE(kW2TileNg, 2);
 #undef W2_TILE
+#undef W2_TILE_P
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (a.ev_after) e = hipEventRecord(a.ev_after, st);
