@@ -153,13 +153,20 @@ struct AttnArgs {
   int NS;                      // prefix splits per (b, h) (kAttnChunk keys each)
   int NP;                      // partials per (b, h) the merge reads (set by the launcher)
   int qgroups;                 // per-wave kernel: groups of 3 query tiles
-  int chunk_sets;              // per-wave kernel: workgroups (chunk sets) per (b, h, group)
+  int chunk_sets;              // per-wave kernel: units per query group (see `balanced`)
+  int balanced;                // per-wave kernel: units are chunk_sets balanced ranges of all
+                               // (b, h, chunk) in order, else (b, h, chunk set) triples
   float* part_o;               // [B][H][NS][Dh/16][T][16]
   float* part_ml;              // [B][H][NS][T][2]
   float* out;                  // [B][T][H][Dh] fp32 (or null)
   void* out_elem;              // [B][T][H][Dh] storage type (or null)
 };
 int attn_splits(int Lmax);
+// prefix chunks of a sequence whose KV length is `len` (clamped to [0, Lmax])
+__host__ __device__ inline int attn_chunks(int len, int Lmax) {
+  const int L = len < 0 ? 0 : (len > Lmax ? Lmax : len);
+  return (L + kAttnChunk - 1) / kAttnChunk;
+}
 int device_cus();   // compute units of the current device (cached per device)
 hipError_t launch_tree_attention(const AttnArgs& a, hipStream_t st);
 

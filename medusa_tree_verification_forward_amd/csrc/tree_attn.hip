@@ -355,6 +355,17 @@ __global__ __launch_bounds__(64 * kPfxWaves) void prefix_attn_bf16_kernel(AttnAr
   }
 }
 
+// Prefix chunks of sequence `lane` (0 past B; B <= 64, one per lane) and
+// their sum over the wave, for the balanced split of the per-wave kernel.
+__device__ __forceinline__ int lane_chunks(const AttnArgs& a, int lane) {
+  return lane < a.B ? attn_chunks(a.kv_len[lane], a.Lmax) : 0;
+}
+__device__ __forceinline__ int wave_sum_int(int v) {
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) v += __shfl_xor(v, off);
+  return v;
+}
+
 // Per-wave split-KV kernel for trees of at most three query tiles and
 // 128-wide heads: wave w of a workgroup takes keys 32 w .. 32 w + 31 of each
 // of the workgroup's chunks and keeps its own running softmax (max, sum,
@@ -367,7 +378,7 @@ __global__ __launch_bounds__(64 * kPfxWaves) void prefix_attn_bf16_kernel(AttnAr
 // combined once, at the end, into the workgroup's partial: maxima and sums
 // through LDS (each wave then scales its outputs), and the outputs summed
 // over the waves in wave order, wave w owning dh tile w.
-template <int QT>
+template <int QT, bool BAL>
 __global__ __launch_bounds__(64 * kPfxWaves) void prefix_attn_wave_kernel(AttnArgs a) {
   using S = uint16_t;
   constexpr int DH = 128, DS = DH / 32, DT = DH / 16, VP = DH / 8, VL = 32 * VP / 64;
@@ -376,229 +387,276 @@ __global__ __launch_bounds__(64 * kPfxWaves) void prefix_attn_wave_kernel(AttnAr
   constexpr int kQBytes = 16 * QT * QSTR * 2, kVBytes = kPfxWaves * 32 * VSTR * 2;
   constexpr int kXBytes = kPfxWaves * (DT / 2) * QT * 64 * 16;   // half the dh tiles of every wave
   constexpr int kLdsBytes = kQBytes + kVBytes > kXBytes ? kQBytes + kVBytes : kXBytes;
-  // One-dimensional grid over units (b, h, s) -- s the chunk set, the
-  // workgroup taking chunks s, s + G, ... of (b, h) -- and query groups qg
-  // (tiles 3 qg .. 3 qg + QT - 1): linear id 8 nqg j + 8 qg + i is unit
-  // 8 j + i, so that a unit's query groups have ids 8 apart (one XCD, at
-  // about the same time: its chunks are read from HBM once and from the L2
-  // by the others). With one group, unit = linear id.
+  // One-dimensional grid over units and query groups qg (tiles 3 qg ..
+  // 3 qg + QT - 1): linear id 8 nqg j + 8 qg + i is unit 8 j + i, so that a
+  // unit's query groups have ids 8 apart (one XCD, at about the same time:
+  // its chunks are read from HBM once and from the L2 by the others). With
+  // one group, unit = linear id.
+  // Strided units (b, h, s), s < G = chunk_sets: chunks s, s + G, ... of
+  // (b, h), one partial at slot s. Balanced units (several sequences of
+  // ragged prefixes): the C chunks of all (b, h), in (b, h, chunk) order,
+  // are cut into min(G, C) contiguous ranges of floor(C / G) or one more;
+  // unit w takes range w and leaves one partial per (b, h) it meets, at the
+  // slot of its first chunk there (attn_merge_kernel finds the same slots).
   const int nqg = a.qgroups, G = a.chunk_sets;
   const int lin = blockIdx.x, blk = lin / (8 * nqg), within = lin - blk * 8 * nqg;
   const int qg = within >> 3, unit = 8 * blk + (within & 7);
-  if (unit >= G * a.H * a.B) return;
-  const int sset = unit % G, h = (unit / G) % a.H, b = unit / (G * a.H);
   const int q0 = 48 * qg;
   const int T = a.T, H = a.H;
-  const int L = min(max(a.kv_len[b], 0), a.Lmax);
-  int s = sset;
-  if (s * kAttnChunk >= L) return;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int li = lane & 15, lq = lane >> 4;
   const float sl2 = a.scale * kLog2e;
   // the Q rows and each wave's V rows during the chunks; the outputs' exchange after them
   __shared__ __attribute__((aligned(16))) unsigned char lds[kLdsBytes];
   __shared__ float st_m[kPfxWaves][16 * QT], st_l[kPfxWaves][16 * QT];
   S* qs = reinterpret_cast<S*>(lds);                                   // [16 QT][QSTR]
-  S* vw = reinterpret_cast<S*>(lds + kQBytes) + wave * 32 * VSTR;      // this wave's [32][VSTR]
-
-  const size_t head = ((size_t)b * H + h) * a.Lmax;
-  const S* __restrict__ kc = reinterpret_cast<const S*>(a.k_cache) + head * DH;
-  const S* __restrict__ vc = reinterpret_cast<const S*>(a.v_cache) + head * DH;
   const S* __restrict__ qb = reinterpret_cast<const S*>(a.q);
-  // this wave's 32 keys of a chunk (rows past L are read clamped and masked
-  // later): K fragments (A operand), key 16 kt + li, dh 8 lq + 32 ds .. + 7;
-  // V rows, piece p = lane + 64 i at key p / VP, dh 8 (p % VP)
-  auto load_kv = [&](int chunk, u32x4_t(&kf)[2][DS], u32x4_t(&vv)[VL]) {
-    const int key0 = chunk * kAttnChunk + 32 * wave;
+
+  // Chunks first, first + stride, ... (at most through `last`) of (b, h)
+  // into the partial at `slot`. Every thread of the workgroup runs the same
+  // segments; the LDS is free on entry.
+  auto segment = [&](int b, int h, int first, int stride, int last,
+                     int slot) __attribute__((always_inline)) {
+    // lane indices taken afresh in each segment, so that the addressing
+    // built from them is not held in registers across segments
+    const int tid = opaque((int)threadIdx.x);
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+    const int li = lane & 15, lq = lane >> 4;
+    const int L = min(max(a.kv_len[b], 0), a.Lmax);
+    const size_t head = ((size_t)b * H + h) * a.Lmax;
+    const S* __restrict__ kc = reinterpret_cast<const S*>(a.k_cache) + head * DH;
+    const S* __restrict__ vc = reinterpret_cast<const S*>(a.v_cache) + head * DH;
+    S* vw = reinterpret_cast<S*>(lds + kQBytes) + wave * 32 * VSTR;   // this wave's [32][VSTR]
+    // this wave's 32 keys of a chunk (rows past L are read clamped and masked
+    // later): K fragments (A operand), key 16 kt + li, dh 8 lq + 32 ds .. + 7;
+    // V rows, piece p = lane + 64 i at key p / VP, dh 8 (p % VP)
+    auto load_kv = [&](int chunk, u32x4_t(&kf)[2][DS], u32x4_t(&vv)[VL]) {
+      const int key0 = chunk * kAttnChunk + 32 * wave;
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt)
+      for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-      for (int ds = 0; ds < DS; ++ds)
-        kf[kt][ds] = load16(kc + (size_t)min(key0 + 16 * kt + li, L - 1) * DH + 8 * lq + 32 * ds);
+        for (int ds = 0; ds < DS; ++ds)
+          kf[kt][ds] = load16(kc + (size_t)min(key0 + 16 * kt + li, L - 1) * DH + 8 * lq + 32 * ds);
 #pragma unroll
-    for (int i = 0; i < VL; ++i) {
-      const int p = lane + 64 * i, kk = p / VP, c = p - kk * VP;
-      vv[i] = load16(vc + (size_t)min(key0 + kk, L - 1) * DH + 8 * c);
-    }
-  };
-  u32x4_t kf[2][DS], vv[VL];
-  load_kv(s, kf, vv);
-  {
-    // every query tile's rows, once (rows past T read clamped, never used)
-    constexpr int QP = 16 * QT * VP, QRN = (QP + 64 * kPfxWaves - 1) / (64 * kPfxWaves);
+      for (int i = 0; i < VL; ++i) {
+        const int p = lane + 64 * i, kk = p / VP, c = p - kk * VP;
+        vv[i] = load16(vc + (size_t)min(key0 + kk, L - 1) * DH + 8 * c);
+      }
+    };
+    int s = first;
+    u32x4_t kf[2][DS], vv[VL];
+    load_kv(s, kf, vv);
+    {
+      // every query tile's rows, once (rows past T read clamped, never used)
+      constexpr int QP = 16 * QT * VP, QRN = (QP + 64 * kPfxWaves - 1) / (64 * kPfxWaves);
 #pragma unroll
-    for (int r = 0; r < QRN; ++r) {
-      const int p = threadIdx.x + 64 * kPfxWaves * r;
-      const int pc = min(p, QP - 1), qr = pc / VP, c = pc - qr * VP;
-      const u32x4_t v =
-          load16(qb + (((size_t)b * T + min(q0 + qr, T - 1)) * H + h) * DH + 8 * c);
-      if (p < QP) *reinterpret_cast<u32x4_t*>(qs + qr * QSTR + 8 * c) = v;
-    }
-  }
-  floatx4_t o[QT][DT];
-  float m_run[QT], l_run[QT];   // of query 16 u + li
-#pragma unroll
-  for (int u = 0; u < QT; ++u) {
-    m_run[u] = kNegInf;
-    l_run[u] = 0.f;
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt) o[u][dt] = floatx4_t{0.f, 0.f, 0.f, 0.f};
-  }
-  __syncthreads();   // the Q rows are published
-  for (;;) {
-    const int key0 = s * kAttnChunk + 32 * wave;
-    const int sn = s + G;
-    const bool more = sn * kAttnChunk < L;
-    // the V rows into this wave's rows (its reads of the previous chunk's
-    // came first: one wave's LDS operations run in order)
-#pragma unroll
-    for (int i = 0; i < VL; ++i) {
-      const int p = lane + 64 * i, kk = p / VP, c = p - kk * VP;
-      *reinterpret_cast<u32x4_t*>(vw + kk * VSTR + 8 * c) = vv[i];
-    }
-    // ---- S^T: lane holds keys key0 + 16 kt + 4 lq + j of query 16 u + li ----
-    floatx4_t st[2][QT];
-#pragma unroll
-    for (int u = 0; u < QT; ++u) {
-      u32x4_t qf[DS];
-#pragma unroll
-      for (int ds = 0; ds < DS; ++ds)
-        qf[ds] = *reinterpret_cast<const u32x4_t*>(qs + (16 * u + li) * QSTR + 8 * lq + 32 * ds);
-#pragma unroll
-      for (int kt = 0; kt < 2; ++kt) {
-        st[kt][u] = floatx4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int ds = 0; ds < DS; ++ds) st[kt][u] = mfma16x16x32_bf16(kf[kt][ds], qf[ds], st[kt][u]);
+      for (int r = 0; r < QRN; ++r) {
+        const int p = threadIdx.x + 64 * kPfxWaves * r;
+        const int pc = min(p, QP - 1), qr = pc / VP, c = pc - qr * VP;
+        const u32x4_t v =
+            load16(qb + (((size_t)b * T + min(q0 + qr, T - 1)) * H + h) * DH + 8 * c);
+        if (p < QP) *reinterpret_cast<u32x4_t*>(qs + qr * QSTR + 8 * c) = v;
       }
     }
-    // the next chunk's loads, into the registers this one is done with
-    if (more) load_kv(sn, kf, vv);
-    // ---- running softmax of each query over the wave's keys; P^T in registers ----
-    u32x4_t pw[QT];
+    floatx4_t o[QT][DT];
+    float m_run[QT], l_run[QT];   // of query 16 u + li
 #pragma unroll
     for (int u = 0; u < QT; ++u) {
-      float mc = kNegInf;
+      m_run[u] = kNegInf;
+      l_run[u] = 0.f;
 #pragma unroll
-      for (int kt = 0; kt < 2; ++kt)
+      for (int dt = 0; dt < DT; ++dt) o[u][dt] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+    }
+    __syncthreads();   // the Q rows are published
+    for (;;) {
+      const int key0 = s * kAttnChunk + 32 * wave;
+      const int sn = s + stride;
+      const bool more = sn <= last && sn * kAttnChunk < L;
+      // the V rows into this wave's rows (its reads of the previous chunk's
+      // came first: one wave's LDS operations run in order)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const bool ok = key0 + 16 * kt + 4 * lq + j < L;
-          const float v = ok ? st[kt][u][j] * sl2 : kNegInf;
-          st[kt][u][j] = v;
-          mc = fmaxf(mc, v);
+      for (int i = 0; i < VL; ++i) {
+        const int p = lane + 64 * i, kk = p / VP, c = p - kk * VP;
+        *reinterpret_cast<u32x4_t*>(vw + kk * VSTR + 8 * c) = vv[i];
+      }
+      // ---- S^T: lane holds keys key0 + 16 kt + 4 lq + j of query 16 u + li ----
+      floatx4_t st[2][QT];
+#pragma unroll
+      for (int u = 0; u < QT; ++u) {
+        u32x4_t qf[DS];
+#pragma unroll
+        for (int ds = 0; ds < DS; ++ds)
+          qf[ds] = *reinterpret_cast<const u32x4_t*>(qs + (16 * u + li) * QSTR + 8 * lq + 32 * ds);
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt) {
+          st[kt][u] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int ds = 0; ds < DS; ++ds)
+            st[kt][u] = mfma16x16x32_bf16(kf[kt][ds], qf[ds], st[kt][u]);
         }
-      mc = fmaxf(mc, __shfl_xor(mc, 16));
-      mc = fmaxf(mc, __shfl_xor(mc, 32));
-      const float mn = fmaxf(m_run[u], mc);
-      const float alpha = m_run[u] == kNegInf ? 0.f : __builtin_amdgcn_exp2f(m_run[u] - mn);
-      float rs = 0.f;
+      }
+      // the next chunk's loads, into the registers this one is done with
+      if (more) load_kv(sn, kf, vv);
+      // ---- running softmax of each query over the wave's keys; P^T in registers ----
+      u32x4_t pw[QT];
 #pragma unroll
-      for (int kt = 0; kt < 2; ++kt)
+      for (int u = 0; u < QT; ++u) {
+        float mc = kNegInf;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const float pv = mn == kNegInf ? 0.f : __builtin_amdgcn_exp2f(st[kt][u][j] - mn);
-          st[kt][u][j] = pv;
-          rs += pv;
-        }
-      rs += __shfl_xor(rs, 16);
-      rs += __shfl_xor(rs, 32);
-      l_run[u] = l_run[u] * alpha + rs;
-      m_run[u] = mn;
+        for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const bool ok = key0 + 16 * kt + 4 * lq + j < L;
+            const float v = ok ? st[kt][u][j] * sl2 : kNegInf;
+            st[kt][u][j] = v;
+            mc = fmaxf(mc, v);
+          }
+        mc = fmaxf(mc, __shfl_xor(mc, 16));
+        mc = fmaxf(mc, __shfl_xor(mc, 32));
+        const float mn = fmaxf(m_run[u], mc);
+        const float alpha = m_run[u] == kNegInf ? 0.f : __builtin_amdgcn_exp2f(m_run[u] - mn);
+        float rs = 0.f;
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const float pv = mn == kNegInf ? 0.f : __builtin_amdgcn_exp2f(st[kt][u][j] - mn);
+            st[kt][u][j] = pv;
+            rs += pv;
+          }
+        rs += __shfl_xor(rs, 16);
+        rs += __shfl_xor(rs, 32);
+        l_run[u] = l_run[u] * alpha + rs;
+        m_run[u] = mn;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) o[u][dt][j] *= alpha;
+        // key 16 kt + 4 lq + j of the wave's 32 at B-operand position 8 lq + 4 kt + j
+        pw[u][0] = pack_bf16x2(st[0][u][0], st[0][u][1]);
+        pw[u][1] = pack_bf16x2(st[0][u][2], st[0][u][3]);
+        pw[u][2] = pack_bf16x2(st[1][u][0], st[1][u][1]);
+        pw[u][3] = pack_bf16x2(st[1][u][2], st[1][u][3]);
+      }
+      // ---- O^T += V^T P^T over the wave's 32 keys ----
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+        // A: lane gets dh 16 dt + li of keys 4 lq + (0..3) and 16 + 4 lq + (0..3)
+        const S* v0 = vw + (4 * lq + (li >> 2)) * VSTR + 16 * dt + 4 * (li & 3);
+        const uint2 lo = lds_read_tr16(v0);
+        const uint2 hi = lds_read_tr16(v0 + 16 * VSTR);
+        u32x4_t vf;
+        vf[0] = lo.x;
+        vf[1] = lo.y;
+        vf[2] = hi.x;
+        vf[3] = hi.y;
+#pragma unroll
+        for (int u = 0; u < QT; ++u) o[u][dt] = mfma16x16x32_bf16(vf, pw[u], o[u][dt]);
+      }
+      if (!more) break;
+      s = sn;
+    }
+    // ---- the eight states into the partial at `slot` ----
+    if (lq == 0)
+#pragma unroll
+      for (int u = 0; u < QT; ++u) {
+        st_m[wave][16 * u + li] = m_run[u];
+        st_l[wave][16 * u + li] = l_run[u];
+      }
+    __syncthreads();   // every wave is past its chunks (Q and V rows free) and its state is in
+    float Mq[QT], Lq[QT];
+#pragma unroll
+    for (int u = 0; u < QT; ++u) {
+      const int q = 16 * u + li;
+      float M = kNegInf;
+#pragma unroll
+      for (int w = 0; w < kPfxWaves; ++w) M = fmaxf(M, st_m[w][q]);
+      float l = 0.f;
+#pragma unroll
+      for (int w = 0; w < kPfxWaves; ++w) {
+        const float mw = st_m[w][q];
+        l += mw == kNegInf ? 0.f : st_l[w][q] * __builtin_amdgcn_exp2f(mw - M);
+      }
+      Mq[u] = M;
+      Lq[u] = l;
+      const float c = m_run[u] == kNegInf ? 0.f : __builtin_amdgcn_exp2f(m_run[u] - M);
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) o[u][dt][j] *= alpha;
-      // key 16 kt + 4 lq + j of the wave's 32 at B-operand position 8 lq + 4 kt + j
-      pw[u][0] = pack_bf16x2(st[0][u][0], st[0][u][1]);
-      pw[u][1] = pack_bf16x2(st[0][u][2], st[0][u][3]);
-      pw[u][2] = pack_bf16x2(st[1][u][0], st[1][u][1]);
-      pw[u][3] = pack_bf16x2(st[1][u][2], st[1][u][3]);
+        for (int j = 0; j < 4; ++j) o[u][dt][j] *= c;
     }
-    // ---- O^T += V^T P^T over the wave's 32 keys ----
+    const size_t base = ((size_t)b * H + h) * a.NS * T + (size_t)slot * T;
+    floatx4_t* xb = reinterpret_cast<floatx4_t*>(lds);   // [wave][DT / 2][QT][64]
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt) {
-      // A: lane gets dh 16 dt + li of keys 4 lq + (0..3) and 16 + 4 lq + (0..3)
-      const S* v0 = vw + (4 * lq + (li >> 2)) * VSTR + 16 * dt + 4 * (li & 3);
-      const uint2 lo = lds_read_tr16(v0);
-      const uint2 hi = lds_read_tr16(v0 + 16 * VSTR);
-      u32x4_t vf;
-      vf[0] = lo.x;
-      vf[1] = lo.y;
-      vf[2] = hi.x;
-      vf[3] = hi.y;
+    for (int half = 0; half < 2; ++half) {
+      if (half) __syncthreads();   // the first half's sums are read
 #pragma unroll
-      for (int u = 0; u < QT; ++u) o[u][dt] = mfma16x16x32_bf16(vf, pw[u], o[u][dt]);
+      for (int d4 = 0; d4 < DT / 2; ++d4)
+#pragma unroll
+        for (int u = 0; u < QT; ++u)
+          xb[((wave * (DT / 2) + d4) * QT + u) * 64 + lane] = o[u][(DT / 2) * half + d4];
+      __syncthreads();
+      if (wave / (DT / 2) == half) {
+        const int d4 = wave % (DT / 2), dt = wave;
+#pragma unroll
+        for (int u = 0; u < QT; ++u) {
+          floatx4_t acc = floatx4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int w = 0; w < kPfxWaves; ++w) {
+            const floatx4_t x = xb[((w * (DT / 2) + d4) * QT + u) * 64 + lane];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) acc[j] += x[j];
+          }
+          const int query = q0 + 16 * u + li;
+          if (query < T)
+            *reinterpret_cast<float4*>(a.part_o + base * DH + ((size_t)dt * T + query) * 16 +
+                                       4 * lq) = make_float4(acc[0], acc[1], acc[2], acc[3]);
+        }
+      }
     }
-    if (!more) break;
-    s = sn;
-  }
-  // ---- the eight states into the workgroup's partial (slot blockIdx.x) ----
-  if (lq == 0)
-#pragma unroll
-    for (int u = 0; u < QT; ++u) {
-      st_m[wave][16 * u + li] = m_run[u];
-      st_l[wave][16 * u + li] = l_run[u];
-    }
-  __syncthreads();   // every wave is past its chunks (Q and V rows free) and its state is in
-  float Mq[QT], Lq[QT];
-#pragma unroll
-  for (int u = 0; u < QT; ++u) {
-    const int q = 16 * u + li;
-    float M = kNegInf;
-#pragma unroll
-    for (int w = 0; w < kPfxWaves; ++w) M = fmaxf(M, st_m[w][q]);
-    float l = 0.f;
-#pragma unroll
-    for (int w = 0; w < kPfxWaves; ++w) {
-      const float mw = st_m[w][q];
-      l += mw == kNegInf ? 0.f : st_l[w][q] * __builtin_amdgcn_exp2f(mw - M);
-    }
-    Mq[u] = M;
-    Lq[u] = l;
-    const float c = m_run[u] == kNegInf ? 0.f : __builtin_amdgcn_exp2f(m_run[u] - M);
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) o[u][dt][j] *= c;
-  }
-  const size_t base = ((size_t)b * H + h) * a.NS * T + (size_t)sset * T;
-  floatx4_t* xb = reinterpret_cast<floatx4_t*>(lds);   // [wave][DT / 2][QT][64]
-#pragma unroll
-  for (int half = 0; half < 2; ++half) {
-    if (half) __syncthreads();   // the first half's sums are read
-#pragma unroll
-    for (int d4 = 0; d4 < DT / 2; ++d4)
-#pragma unroll
-      for (int u = 0; u < QT; ++u)
-        xb[((wave * (DT / 2) + d4) * QT + u) * 64 + lane] = o[u][(DT / 2) * half + d4];
-    __syncthreads();
-    if (wave / (DT / 2) == half) {
-      const int d4 = wave % (DT / 2), dt = wave;
+    if (wave == 0 && lq == 0)
 #pragma unroll
       for (int u = 0; u < QT; ++u) {
-        floatx4_t acc = floatx4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int w = 0; w < kPfxWaves; ++w) {
-          const floatx4_t x = xb[((w * (DT / 2) + d4) * QT + u) * 64 + lane];
-#pragma unroll
-          for (int j = 0; j < 4; ++j) acc[j] += x[j];
-        }
         const int query = q0 + 16 * u + li;
-        if (query < T)
-          *reinterpret_cast<float4*>(a.part_o + base * DH + ((size_t)dt * T + query) * 16 +
-                                     4 * lq) = make_float4(acc[0], acc[1], acc[2], acc[3]);
+        if (query < T) {
+          a.part_ml[(base + query) * 2 + 0] = Mq[u];
+          a.part_ml[(base + query) * 2 + 1] = Lq[u];
+        }
       }
+  };
+
+  if constexpr (!BAL) {
+    // strided: one segment
+    if (unit >= G * a.H * a.B) return;
+    const int s = unit % G, h = (unit / G) % a.H, b = unit / (G * a.H);
+    if (s * kAttnChunk >= min(max(a.kv_len[b], 0), a.Lmax)) return;
+    segment(b, h, s, G, 0x7fffffff, s);
+  } else {
+    // balanced: each (b, h) the unit's range [pos, hi) meets (the C chunks
+    // in order: sequence b's H nch chunks start at pb)
+    // every sequence's chunk count at once, one a lane (the walk below
+    // reads them back with readlane)
+    const int nl = lane_chunks(a, (int)threadIdx.x & 63);
+    const int C = H * __builtin_amdgcn_readfirstlane(wave_sum_int(nl));
+    const int NWe = min(G, C);
+    if (unit >= NWe) return;
+    // (divisions run on the vector ALUs: their uniform results are moved
+    // back to scalar registers)
+    int pos = __builtin_amdgcn_readfirstlane((int)((long long)unit * C / NWe));
+    const int hi = __builtin_amdgcn_readfirstlane((int)((long long)(unit + 1) * C / NWe));
+    int b = 0, pb = 0, nch = __builtin_amdgcn_readlane(nl, 0);
+    while (pos < hi) {
+      while (pos >= pb + H * nch) {   // the sequence of chunk pos (pos < C)
+        pb += H * nch;
+        ++b;
+        nch = __builtin_amdgcn_readlane(nl, b);
+      }
+      const int h = __builtin_amdgcn_readfirstlane((pos - pb) / nch);
+      const int first = pos - pb - h * nch;
+      const int end = min(hi, pb + (h + 1) * nch);
+      segment(__builtin_amdgcn_readfirstlane(b), h, first, 1, first + (end - pos) - 1, first);
+      pos = end;
+      __syncthreads();   // the segment's exchange is read before the LDS is reused
     }
   }
-  if (wave == 0 && lq == 0)
-#pragma unroll
-    for (int u = 0; u < QT; ++u) {
-      const int query = q0 + 16 * u + li;
-      if (query < T) {
-        a.part_ml[(base + query) * 2 + 0] = Mq[u];
-        a.part_ml[(base + query) * 2 + 1] = Lq[u];
-      }
-    }
 }
 
 // fp32 prefix kernel: SC keys per round are staged in LDS (K row-major, V
@@ -765,15 +823,43 @@ __global__ __launch_bounds__(256) void prefix_attn_f32_kernel(AttnArgs a) {
 // are clamped and given zero weight.
 constexpr int kMergeBatch = 8;
 constexpr int kTreeBatch = 8;
-template <class ET, int DH>
+template <class ET, int DH, bool BAL>
 __global__ __launch_bounds__(64) void attn_merge_kernel(AttnArgs a) {
   using S = typename ET::storage;
   constexpr int E = DH / 64;
   const int i = blockIdx.x, h = blockIdx.y, b = blockIdx.z, lane = threadIdx.x;
   const int T = a.T, H = a.H;
   const int L = min(max(a.kv_len[b], 0), a.Lmax);
-  // partials: one per prefix workgroup that had a chunk
-  const int ns = min(a.NP, (L + kAttnChunk - 1) / kAttnChunk);
+  // partials: one per prefix workgroup that had a chunk (strided units:
+  // slots 0 .. ns - 1). Balanced units: the ns units whose ranges meet this
+  // (b, h)'s chunks [cs, cs + nch) of the C in order, wa the first; unit
+  // wa + j left its partial at the slot of its first chunk here.
+  // (balanced: (NWe + 64) C < 2^32, which the launcher checks, so 32-bit
+  // unsigned products)
+  const int nch = attn_chunks(L, a.Lmax);
+  int ns = min(a.NP, nch);
+  unsigned wa = 0, NWe = 1, C = 1, cs = 0;
+  if constexpr (BAL) {
+    // every sequence's chunks at once, one a lane
+    const int nl = lane_chunks(a, lane);
+    C = H * (unsigned)__builtin_amdgcn_readfirstlane(wave_sum_int(nl));
+    cs = H * (unsigned)__builtin_amdgcn_readfirstlane(wave_sum_int(lane < b ? nl : 0)) + h * nch;
+    NWe = min((unsigned)a.chunk_sets, C);
+    ns = 0;
+    if (nch > 0) {
+      wa = ((cs + 1) * NWe + C - 1) / C - 1;
+      ns = (int)(((cs + nch) * NWe + C - 1) / C - wa);
+    }
+  }
+  // (balanced: lane j computes partial j's slot once)
+  auto slot_of = [&](unsigned j) -> int { return (int)(max((wa + j) * C / NWe, cs) - cs); };
+  const int slot_l = BAL ? slot_of(lane) : 0;
+  auto slot = [&](int j) -> int {
+    if constexpr (BAL)
+      return j < 64 ? __builtin_amdgcn_readlane(slot_l, j) : slot_of(j);
+    else
+      return j;
+  };
   const float sl2 = a.scale * kLog2e;
   const size_t hs = ((size_t)b * H + h) * a.NS;   // split 0 of (b, h)
   // dh E lane + e of query i inside a split's [DT][T][16] block
@@ -788,7 +874,7 @@ __global__ __launch_bounds__(64) void attn_merge_kernel(AttnArgs a) {
   auto load_splits = [&](int s0) {
 #pragma unroll
     for (int j = 0; j < kMergeBatch; ++j) {
-      const size_t sp = hs + min(s0 + j, max(ns - 1, 0));
+      const size_t sp = hs + slot(min(s0 + j, max(ns - 1, 0)));
       ms[j] = a.part_ml[(sp * T + i) * 2];
       lsv[j] = a.part_ml[(sp * T + i) * 2 + 1];
 #pragma unroll
@@ -937,15 +1023,36 @@ hipError_t launch_bf16(const AttnArgs& a, hipStream_t st) {
       AttnArgs w = a;
       w.qgroups = 1;
       w.chunk_sets = G;
-      const dim3 wgrid((G * a.H * a.B + 7) / 8 * 8);
-      switch (MQ) {
-        case 1: hipLaunchKernelGGL((prefix_attn_wave_kernel<1>), wgrid, block, 0, st, w); break;
-        case 2: hipLaunchKernelGGL((prefix_attn_wave_kernel<2>), wgrid, block, 0, st, w); break;
-        default: hipLaunchKernelGGL((prefix_attn_wave_kernel<3>), wgrid, block, 0, st, w); break;
+      w.balanced = 0;
+      if (a.B > 1 && (long long)(cus + 64) * a.B * a.H * a.NS < (1ll << 32)) {
+        // several sequences: one balanced range of the chunks of every
+        // (b, h) per compute unit, so that ragged prefixes leave no unit idle
+        // (batch of 8, 7B: 79.8 -> 70.6 us)
+        w.balanced = 1;
+        w.chunk_sets = cus;
       }
+      m.balanced = w.balanced;
+      m.chunk_sets = w.chunk_sets;
+      const dim3 wgrid(w.balanced ? (cus + 7) / 8 * 8 : (G * a.H * a.B + 7) / 8 * 8);
+#define WAVE_CASES(BAL)                                                                      \
+  switch (MQ) {                                                                              \
+    case 1: hipLaunchKernelGGL((prefix_attn_wave_kernel<1, BAL>), wgrid, block, 0, st, w); break; \
+    case 2: hipLaunchKernelGGL((prefix_attn_wave_kernel<2, BAL>), wgrid, block, 0, st, w); break; \
+    default: hipLaunchKernelGGL((prefix_attn_wave_kernel<3, BAL>), wgrid, block, 0, st, w); break; \
+  }
+      if (w.balanced)
+        WAVE_CASES(true)
+      else
+        WAVE_CASES(false)
+#undef WAVE_CASES
       hipError_t e = hipGetLastError();
       if (e != hipSuccess) return e;
-      hipLaunchKernelGGL((attn_merge_kernel<BF16, DH>), dim3(a.T, a.H, a.B), dim3(64), 0, st, m);
+      if (w.balanced)
+        hipLaunchKernelGGL((attn_merge_kernel<BF16, DH, true>), dim3(a.T, a.H, a.B), dim3(64), 0,
+                           st, m);
+      else
+        hipLaunchKernelGGL((attn_merge_kernel<BF16, DH, false>), dim3(a.T, a.H, a.B), dim3(64), 0,
+                           st, m);
       return hipGetLastError();
     }
     if (MQ > 3) {
@@ -958,12 +1065,13 @@ hipError_t launch_bf16(const AttnArgs& a, hipStream_t st) {
       AttnArgs w = a;
       w.qgroups = nqg;
       w.chunk_sets = G2;
+      w.balanced = 0;
       m.NP = G2;
       const dim3 wgrid((G2 * a.H * a.B + 7) / 8 * 8 * nqg);
-      hipLaunchKernelGGL((prefix_attn_wave_kernel<3>), wgrid, block, 0, st, w);
+      hipLaunchKernelGGL((prefix_attn_wave_kernel<3, false>), wgrid, block, 0, st, w);
       hipError_t e = hipGetLastError();
       if (e != hipSuccess) return e;
-      hipLaunchKernelGGL((attn_merge_kernel<BF16, DH>), dim3(a.T, a.H, a.B), dim3(64), 0, st, m);
+      hipLaunchKernelGGL((attn_merge_kernel<BF16, DH, false>), dim3(a.T, a.H, a.B), dim3(64), 0, st, m);
       return hipGetLastError();
     }
   }
@@ -989,7 +1097,7 @@ hipError_t launch_bf16(const AttnArgs& a, hipStream_t st) {
     }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((attn_merge_kernel<BF16, DH>), dim3(a.T, a.H, a.B), dim3(64), 0, st, m);
+  hipLaunchKernelGGL((attn_merge_kernel<BF16, DH, false>), dim3(a.T, a.H, a.B), dim3(64), 0, st, m);
   return hipGetLastError();
 }
 
@@ -1010,7 +1118,7 @@ hipError_t launch_f32(const AttnArgs& a, hipStream_t st) {
   if (e != hipSuccess) return e;
   AttnArgs m = a;
   m.NP = a.NS;   // one partial per chunk
-  hipLaunchKernelGGL((attn_merge_kernel<F32, DH>), dim3(a.T, a.H, a.B), dim3(64), 0, st, m);
+  hipLaunchKernelGGL((attn_merge_kernel<F32, DH, false>), dim3(a.T, a.H, a.B), dim3(64), 0, st, m);
   return hipGetLastError();
 }
 

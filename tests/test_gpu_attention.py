@@ -83,6 +83,31 @@ def test_tree_attention(case):
     assert np.max(np.abs(g - o)) < (5e-2 if dtype == "bf16" else 1e-4)
 
 
+# Several sequences whose prefix chunks outnumber the workgroups: balanced
+# ranges over every (sequence, head)'s chunks, some ranges spanning several
+# heads or sequences. (tree s, B, H, prefix lengths, Lmax)
+BALANCED = [
+    ((3, 2), 2, 128, [4000, 600], 4200),               # one query tile
+    ((3, 2, 2, 1, 1), 8, 32, [2048, 512, 1700, 900, 64, 2000, 1, 1300], 2120),  # three tiles
+    ((2, 2), 2, 128, [0, 100], 4200),                  # fewer chunks than workgroups, an empty prefix
+    ((4, 3), 3, 96, [0, 2000, 257], 2100),             # two tiles, a sequence with no chunks first
+]
+
+
+@pytest.mark.parametrize("case", BALANCED, ids=lambda c: f"s{c[0]}-B{c[1]}-H{c[2]}-L{c[4]}")
+def test_tree_attention_balanced(case):
+    s, B, H, Ls, Lmax = case
+    Dh = 128
+    rng = np.random.default_rng(sum(s) * 1000 + B * 100 + H)
+    K = len(s)
+    topo, q, kt, vt, kc, vc = _case(rng, cartesian_ranks(s), K, B, H, Dh, Ls, Lmax, "bf16")
+    scale = 1.0 / np.sqrt(Dh)
+    g = _run(topo, q, kt, vt, kc, vc, Ls, K, "bf16", scale)
+    o = _oracle(topo, q, kt, vt, kc, vc, Ls, scale)
+    assert_close(g, o, 2e-2, "attention balanced")
+    assert np.max(np.abs(g - o)) < 5e-2
+
+
 def test_tree_attention_sparse_tree():
     rng = np.random.default_rng(11)
     spec = np.array([[0, -1, -1], [1, -1, -1], [2, -1, -1], [0, 0, -1], [0, 1, -1], [2, 0, -1],
