@@ -690,8 +690,10 @@ __global__ __launch_bounds__(kHeadWaves * 64, 4) void heads_w1_tile_kernel(
 // rows of a wave stay within a few pages; rows interleaved over the waves
 // spread every wave over the whole head); the values are moved to lane = row
 // (lane 16 g + j takes row j of tile row g) for the shared top-S epilogue.
+// three resident workgroups a compute unit: registers for 8 column blocks in flight
+constexpr int kW2TileMinBlocks = 3;
 template <int NG, int DS, bool PACKED>
-__global__ __launch_bounds__(kHeadWaves * 64, 4) void heads_w2_tile_kernel(
+__global__ __launch_bounds__(kHeadWaves * 64, kW2TileMinBlocks) void heads_w2_tile_kernel(
     int B, int b0, int K, int V, int d, const uint16_t* __restrict__ W2,
     const uint16_t* __restrict__ W2p, const u32x4_t* __restrict__ zfrag, int S,
     float* __restrict__ head_logits,
@@ -938,8 +940,9 @@ hipError_t launch_heads_nb(const HeadsArgs& a, int b0, hipStream_t st) {
 
 // Batched passes (3 or more vectors, bf16): W1 split over 4 waves (fewer
 // where d does not allow) with 8 column blocks in flight, W2 in tile rows of
-// two (32 rows a wave) with 4 column blocks in flight (2 where d does not
-// allow). From a row-major W2 the batch-8 step took 746 us with these
+// two (32 rows a wave) with 8 column blocks in flight (4 or 2 where d does
+// not allow; 8 at three workgroups a unit against 4 at four: 206.5 against
+// 208.9 us at a batch of 8). From a row-major W2 the batch-8 step took 746 us with these
 // against 755-779 for 16-64 rows a wave and 4-16 tiles in flight:
 // fragment-shaped reads lose DRAM locality as more of them are outstanding.
 // From packed tiles the W2 pass takes 237 us against 286 (row-major); 3
@@ -999,7 +1002,9 @@ hipError_t launch_heads_tile(const HeadsArgs& a, int b0, int G, hipStream_t st) 
   else                      \
     W2_TILE_P(NG, DS, false)
   // d is a multiple of 64: nblk is even
-  if (nblk % 4 == 0)
+  if (nblk % 8 == 0)
+    W2_TILE(kW2TileNg, 8);
+  else if (nblk % 4 == 0)
     W2_TILE(kW2TileNg, 4);
   else
     W2_TILE(kW2TileNg, 2);
