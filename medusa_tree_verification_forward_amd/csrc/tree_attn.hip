@@ -366,16 +366,18 @@ __device__ __forceinline__ int wave_sum_int(int v) {
   return v;
 }
 
-// Per-wave split-KV kernel for trees of at most three query tiles and
-// 128-wide heads: wave w of a workgroup takes keys 32 w .. 32 w + 31 of each
-// of the workgroup's chunks and keeps its own running softmax (max, sum,
-// output) for every query, so that a chunk needs no exchange between the
-// waves and no barrier: S^T = K Q^T (K fragments from memory, Q fragments
+// Per-wave split-KV kernel for 128-wide heads, one group of at most three
+// query tiles a workgroup (trees of more tiles run a workgroup set per
+// group): wave w of a workgroup takes keys 32 w .. 32 w + 31 of each of its
+// chunks and keeps its own running softmax (max, sum, output) for every
+// query of the group, so that a chunk needs no exchange between the waves
+// and no barrier: S^T = K Q^T (K fragments from memory, Q fragments
 // from LDS); P = 2^(s - m) stays in registers, packed in the key order of
 // the transposing read, as the B operand of O^T += V^T P^T (V^T read from
 // the wave's own V rows in LDS); the next chunk's K and V loads go out into
 // the registers the current one has finished with. The eight states are
-// combined once, at the end, into the workgroup's partial: maxima and sums
+// combined once, at the end of each segment (a run of chunks of one (b, h)),
+// into that segment's partial: maxima and sums
 // through LDS (each wave then scales its outputs), and the outputs summed
 // over the waves in wave order, wave w owning dh tile w.
 template <int QT, bool BAL>
