@@ -91,6 +91,9 @@ BALANCED = [
     ((3, 2, 2, 1, 1), 8, 32, [2048, 512, 1700, 900, 64, 2000, 1, 1300], 2120),  # three tiles
     ((2, 2), 2, 128, [0, 100], 4200),                  # fewer chunks than workgroups, an empty prefix
     ((4, 3), 3, 96, [0, 2000, 257], 2100),             # two tiles, a sequence with no chunks first
+    # the largest batch a call takes (64 sequences, one chunk count a lane),
+    # lengths spread over [0, Lmax] with empty and full prefixes among them
+    ((3, 2, 2, 1, 1), 64, 4, [(37 * i * i + 11 * i) % 2101 for i in range(63)] + [2100], 2100),
 ]
 
 
