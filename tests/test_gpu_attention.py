@@ -56,6 +56,7 @@ CASES = [
     ((3, 2, 2, 1, 1), 1, 4, 128, [2048], "bf16"),
     ((3, 2, 2, 1, 1), 3, 2, 128, [0, 1, 777], "bf16"),     # empty, single-row, ragged prefix
     ((4, 3, 2, 2, 1), 1, 2, 128, [4096], "bf16"),          # 137 rows: 9 query tiles
+    ((4, 3, 2, 2, 1), 2, 3, 128, [3000, 40], "bf16"),      # 9 tiles, two ragged sequences
     ((2, 2), 2, 3, 64, [255, 257], "bf16"),               # Dh 64, around a chunk boundary
     ((16, 14), 1, 1, 128, [100], "bf16"),                  # 241 rows: 16 query tiles
     ((2, 2, 2), 2, 2, 128, [300, 5], "f32"),
