@@ -471,7 +471,9 @@ def main():
         others = []
         for oname in OTHER_WORKLOADS:
             ow = WORKLOADS[oname]
-            n = max(20, args.steps // 4)
+            # at least 50 steps (~25 ms of GPU work): 20-step regions of these
+            # workloads read 2-5 us a step above longer ones
+            n = max(50, args.steps // 4)
             o = time_step(ow, n, max(5, args.warmup // 4), min_warm_s=args.min_warm)
             oalg = algorithmic_bytes(ow, o["T"], o["L_total"])
             ocomb = combined_roofline_us(ow, o["T"], o["L_total"])
