@@ -259,8 +259,8 @@ int heads_impl(const medusa_shape* shape, const float* h, const void* W1,
                float* head_lse_or_null, float* head_logits_or_null, float* z_or_null,
                void* workspace, size_t workspace_bytes, void* stream, const TreePlan* fuse_plan,
                const int32_t* root_tok, const int32_t* kv_len, int32_t* tree_tokens,
-               int32_t* position_ids, bool dry, hipEvent_t ev_w2_start = nullptr,
-               hipEvent_t ev_w2_end = nullptr) {
+               int32_t* position_ids, const float* u_draft_or_null, bool dry,
+               hipEvent_t ev_w2_start = nullptr, hipEvent_t ev_w2_end = nullptr) {
   int rc = check_shape(shape);
   if (rc) return rc;
   REQUIRE_PTR(h);
@@ -274,6 +274,8 @@ int heads_impl(const medusa_shape* shape, const float* h, const void* W1,
   OPTIONAL_PTR(head_lse_or_null);
   OPTIONAL_PTR(head_logits_or_null);
   OPTIONAL_PTR(z_or_null);
+  if (fuse_plan && u_draft_or_null && !head_logits_or_null)
+    return fail(MEDUSA_ERR_ARG, "sampled drafting needs head_logits");
   Layout L;
   rc = check_workspace(shape, workspace, workspace_bytes, &L);
   if (rc) return rc;
@@ -316,6 +318,7 @@ int heads_impl(const medusa_shape* shape, const float* h, const void* W1,
     a.kv_len = kv_len;
     a.tree_tokens = tree_tokens;
     a.position_ids = position_ids;
+    a.u_draft = u_draft_or_null;
   }
   hipError_t e = launch_heads(a, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "heads launch");
@@ -336,7 +339,7 @@ int medusa_heads_forward(const medusa_shape* shape, const float* h, const void* 
                     topk_ids, topk_logits,
                     head_lse_or_null,
                     head_logits_or_null, z_or_null, workspace, workspace_bytes, stream, nullptr,
-                    nullptr, nullptr, nullptr, nullptr, false);
+                    nullptr, nullptr, nullptr, nullptr, nullptr, false);
 }
 
 }  // extern "C"
@@ -829,21 +832,22 @@ int step_impl(const medusa_shape* shape, const medusa_step_args* x, void* worksp
     if (mode == MEDUSA_TYPICAL && (!(x->eps >= 0.f) || !(x->delta >= 0.f)))
       return fail(MEDUSA_ERR_ARG, "eps, delta must be >= 0");
   }
-  // 1. heads (+ tree tokens and positions)
+  // 1. heads, with the tree's tokens and positions: top-s drafting in the
+  // head merge, sampled drafting in workgroups launched beside it
   rc = heads_impl(shape, x->h, x->W1, x->W1_packed_or_null, x->b1_or_null, x->W2,
                   x->W2_packed_or_null, x->topk_ids,
                   x->topk_logits,
                   x->head_lse_or_null, x->head_logits_or_null, x->z_or_null, workspace,
-                  workspace_bytes, stream,
-                  fuse_tree ? &plan : nullptr, x->root_tok, x->kv_len, x->tree_tokens,
-                  x->position_ids, dry, ev_w2_start, ev_w2_end);
+                  workspace_bytes, stream, &plan, x->root_tok, x->kv_len, x->tree_tokens,
+                  x->position_ids, fuse_tree ? nullptr : x->u_draft_or_null, dry, ev_w2_start,
+                  ev_w2_end);
   if (rc) return rc;
-  // 2. tree tokens by sampling
-  if (!fuse_tree) {
+  // 2. sampled drafting: the tree sampler's checks (its draws ran with the heads)
+  if (!fuse_tree && dry) {
     rc = tree_impl(shape, x->tree_ranks_host, x->draft_mode, x->root_tok, x->topk_ids,
                    x->head_logits_or_null, x->head_lse_or_null, x->u_draft_or_null, x->kv_len,
                    x->tree_tokens, nullptr, x->position_ids, nullptr, nullptr, nullptr, stream,
-                   dry);
+                   true);
     if (rc) return rc;
   }
   // 3. verify forward

@@ -14,6 +14,7 @@
 #include <algorithm>
 #include <type_traits>
 
+#include "cdf.h"
 #include "common.h"
 #include "kernels.h"
 #include "select.h"
@@ -756,7 +757,9 @@ __global__ __launch_bounds__(kHeadWaves * 64, kW2TileMinBlocks) void heads_w2_ti
 constexpr int kMergeThreads = 256;
 constexpr int kMergeBatch = 4;
 
-// Tree tokens and positions written by the merge (composite step).
+// Tree tokens and positions written by the merge (composite step): top-s
+// drafting (u_draft null), the merge of head k writes the depth-(k+1) nodes'
+// tokens; sampled drafting, workgroups of their own draw them (below).
 struct MergeTree {
   int on;
   TreePlan plan;
@@ -764,17 +767,23 @@ struct MergeTree {
   const int32_t* kv_len;
   int32_t* tokens;
   int32_t* position_ids;
+  const float* u_draft;       // [B][T] (sampled drafting) or null
+  const float* head_logits;   // [B][K][V] (sampled drafting)
+  int V;
 };
 
+// The merge of head k of sequence b. Threads past the first kMergeThreads
+// (in a larger workgroup) take no part but meet its barrier; `tree`: write
+// the top-s tree tokens and positions.
 template <int SMAX>
-__global__ __launch_bounds__(kMergeThreads) void heads_merge_kernel(
-    int K, int G, int S, const float* __restrict__ part_val, const int* __restrict__ part_id,
-    const float* __restrict__ part_m, const float* __restrict__ part_s,
-    int* __restrict__ topk_ids, float* __restrict__ topk_logits, float* __restrict__ lse,
-    MergeTree tr) {
+__device__ __forceinline__ void merge_head(
+    int k, int b, int K, int G, int S, const float* __restrict__ part_val,
+    const int* __restrict__ part_id, const float* __restrict__ part_m,
+    const float* __restrict__ part_s, int* __restrict__ topk_ids,
+    float* __restrict__ topk_logits, float* __restrict__ lse, const MergeTree& tr, bool tree) {
   constexpr int NW = kMergeThreads / 64;
-  const int k = blockIdx.x, b = blockIdx.y;
   const int t = threadIdx.x, wave = t >> 6, lane = t & 63;
+  const bool act = t < kMergeThreads;   // wave-uniform
   const size_t rec0 = ((size_t)b * K + k) * G;
   __shared__ float sv[NW][MAXS_LDS];
   __shared__ int si[NW][MAXS_LDS];
@@ -788,7 +797,7 @@ __global__ __launch_bounds__(kMergeThreads) void heads_merge_kernel(
   // the plan is a kernel argument), loaded now and used at the end
   constexpr int NQ = MAXT / 64;
   int pdep[NQ], prank[NQ], pkv = 0, proot = 0;
-  if (tr.on && wave == 0) {
+  if (tree && wave == 0) {
 #pragma unroll
     for (int q = 0; q < NQ; ++q) {
       pdep[q] = tr.plan.depth[lane + 64 * q];
@@ -805,7 +814,7 @@ __global__ __launch_bounds__(kMergeThreads) void heads_merge_kernel(
     lv[j] = kNegInf;
     li[j] = kNoId;
   }
-  const int ncand = G * S;
+  const int ncand = act ? G * S : 0;
   for (int base = 0; base < ncand; base += kMergeThreads * kMergeBatch) {
     float v[kMergeBatch];
     int id[kMergeBatch];
@@ -836,10 +845,12 @@ __global__ __launch_bounds__(kMergeThreads) void heads_merge_kernel(
   }
   float wv;
   int wi;
-  wave_select<SMAX>(lv, li, S, wv, wi);
-  if (lane < S) {
-    sv[wave][lane] = wv;
-    si[wave][lane] = wi;
+  if (act) {
+    wave_select<SMAX>(lv, li, S, wv, wi);
+    if (lane < S) {
+      sv[wave][lane] = wv;
+      si[wave][lane] = wi;
+    }
   }
 
   // log-sum-exp of the G (max, sum) records: wave 0, fixed order
@@ -867,7 +878,7 @@ __global__ __launch_bounds__(kMergeThreads) void heads_merge_kernel(
     topk_ids[out + lane] = wi;
     topk_logits[out + lane] = wv;
   }
-  if (!tr.on) return;
+  if (!tree) return;
   // nodes of depth k+1 take rank r's token of this head (held by lane r)
   const int T = tr.plan.T;
 #pragma unroll
@@ -883,6 +894,66 @@ __global__ __launch_bounds__(kMergeThreads) void heads_merge_kernel(
       if (n == 0) tr.tokens[(size_t)b * T] = opaque(proot);
     }
   }
+}
+
+template <int SMAX>
+__global__ __launch_bounds__(kMergeThreads) void heads_merge_kernel(
+    int K, int G, int S, const float* __restrict__ part_val, const int* __restrict__ part_id,
+    const float* __restrict__ part_m, const float* __restrict__ part_s,
+    int* __restrict__ topk_ids, float* __restrict__ topk_logits, float* __restrict__ lse,
+    MergeTree tr) {
+  merge_head<SMAX>(blockIdx.x, blockIdx.y, K, G, S, part_val, part_id, part_m, part_s, topk_ids,
+                   topk_logits, lse, tr, tr.on != 0);
+}
+
+// Sampled drafting (composite step): the draws of the depth-(kd+1) nodes of
+// sequence b from head kd's softmax, as the tree sampler makes them, by one
+// kCdfThreads workgroup. The weights are e^(l - m) with m the row's maximum
+// -- the largest of the W2 workgroups' maxima, an exact maximum -- instead
+// of e^(l - lse): an inverse-CDF draw scales its target by the weights'
+// total, so it needs no log-sum-exp and does not wait for the merge. Depth 1
+// also writes the position ids and the root token.
+__device__ __forceinline__ void sample_head(int kd, int b, int K, int G,
+                                            const float* __restrict__ part_m,
+                                            const MergeTree& tr) {
+  const int t = threadIdx.x, wave = t >> 6, lane = t & 63;
+  const int T = tr.plan.T, V = tr.V;
+  __shared__ CdfLds sh;
+  __shared__ float s_mx;
+  const int dep = tr.plan.depth[min(t, MAXT - 1)];
+  const bool mine = t >= 1 && t < T && dep == kd + 1;
+  const float u = mine ? tr.u_draft[(size_t)b * T + t] : 0.f;
+  if (wave == 0) {
+    const float* pm = part_m + ((size_t)b * K + kd) * G;
+    float m = kNegInf;
+    for (int g = lane; g < G; g += 64) m = fmaxf(m, pm[g]);
+    m = wave_max(m);
+    if (lane == 0) s_mx = m;
+  }
+  if (kd == 0 && t < T) {
+    tr.position_ids[(size_t)b * T + t] = tr.kv_len[b] + dep;
+    if (t == 0) tr.tokens[(size_t)b * T] = tr.root_tok[b];
+  }
+  __syncthreads();
+  const ExpRow w{tr.head_logits + ((size_t)b * K + kd) * V, s_mx, V};
+  cdf_build<true>(w, V, sh);
+  if (mine) tr.tokens[(size_t)b * T + t] = cdf_draw(w, V, u, sh);
+}
+
+// Composite step with sampled drafting: workgroups (k, b), k < K, merge head
+// k (on their first kMergeThreads threads); workgroups (K + kd, b) draw the
+// depth-(kd+1) nodes. Neither waits for the other.
+template <int SMAX>
+__global__ __launch_bounds__(kCdfThreads) void heads_merge_sample_kernel(
+    int K, int G, int S, const float* __restrict__ part_val, const int* __restrict__ part_id,
+    const float* __restrict__ part_m, const float* __restrict__ part_s,
+    int* __restrict__ topk_ids, float* __restrict__ topk_logits, float* __restrict__ lse,
+    MergeTree tr) {
+  if ((int)blockIdx.x < K)
+    merge_head<SMAX>(blockIdx.x, blockIdx.y, K, G, S, part_val, part_id, part_m, part_s,
+                     topk_ids, topk_logits, lse, tr, false);
+  else
+    sample_head(blockIdx.x - K, blockIdx.y, K, G, part_m, tr);
 }
 
 template <class ET, int NB, int SPR>
@@ -1045,11 +1116,21 @@ hipError_t launch_heads_et(const HeadsArgs& a, hipStream_t st) {
     tr.kv_len = a.kv_len;
     tr.tokens = a.tree_tokens;
     tr.position_ids = a.position_ids;
+    tr.u_draft = a.u_draft;
+    tr.head_logits = a.head_logits;
+    tr.V = a.V;
   }
-#define MERGE_LAUNCH(SM)                                                                      \
-  hipLaunchKernelGGL(heads_merge_kernel<SM>, dim3(a.K, a.B), dim3(kMergeThreads), 0, st, a.K, \
-                     G, a.S, a.part_val, a.part_id, a.part_m, a.part_s, a.topk_ids,            \
-                     a.topk_logits, a.lse, tr)
+  // sampled drafting: the merge and the draws in one launch
+  const bool sample = a.fuse_tree && a.u_draft;
+#define MERGE_LAUNCH(SM)                                                                       \
+  if (sample)                                                                                  \
+    hipLaunchKernelGGL(heads_merge_sample_kernel<SM>, dim3(2 * a.K, a.B), dim3(kCdfThreads), 0, \
+                       st, a.K, G, a.S, a.part_val, a.part_id, a.part_m, a.part_s, a.topk_ids, \
+                       a.topk_logits, a.lse, tr);                                              \
+  else                                                                                         \
+    hipLaunchKernelGGL(heads_merge_kernel<SM>, dim3(a.K, a.B), dim3(kMergeThreads), 0, st,     \
+                       a.K, G, a.S, a.part_val, a.part_id, a.part_m, a.part_s, a.topk_ids,     \
+                       a.topk_logits, a.lse, tr)
   if (a.S <= 4)
     MERGE_LAUNCH(4);
   else if (a.S <= 8)

@@ -48,15 +48,18 @@ struct HeadsArgs {
   int w2_rows_per_wave;   // 4..64
   hipEvent_t ev_before;   // optional: recorded around the W2 kernel
   hipEvent_t ev_after;
-  // optional (composite step, top-s drafting): the merge of head k also
-  // writes the tokens of the depth-(k+1) nodes; head 0 writes the root
-  // token and every position id
+  // optional (composite step): the tree's tokens and positions with the
+  // merge -- top-s drafting (u_draft null): the merge of head k writes the
+  // tokens of the depth-(k+1) nodes, head 0 the root token and every
+  // position id; sampled drafting: workgroups beside the merge draw them
+  // from head_logits with u_draft
   bool fuse_tree;
   TreePlan plan;
   const int32_t* root_tok;     // [B]
   const int32_t* kv_len;       // [B]
   int32_t* tree_tokens;        // [B][T]
   int32_t* position_ids;       // [B][T]
+  const float* u_draft;        // [B][T] or null
 };
 hipError_t launch_heads(const HeadsArgs& a, hipStream_t st);
 // Row blocks a head's partial records can need: the per-row streams'
