@@ -138,10 +138,20 @@ def _ptr(t) -> Optional[int]:
     return t.data_ptr()
 
 
+def _current_stream() -> int:
+    """torch's current stream on the current device (the capture stream while
+    a graph is being recorded), without building a Stream object (~3 us a
+    call)."""
+    import torch
+    C = torch._C
+    if hasattr(C, "_cuda_getCurrentRawStream") and hasattr(C, "_cuda_getDevice"):
+        return C._cuda_getCurrentRawStream(C._cuda_getDevice())
+    return torch.cuda.current_stream().cuda_stream
+
+
 def _stream(stream) -> Optional[int]:
     if stream is None:
-        import torch
-        return torch.cuda.current_stream().cuda_stream
+        return _current_stream()
     if isinstance(stream, int):
         return stream
     return stream.cuda_stream

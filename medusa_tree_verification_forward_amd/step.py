@@ -215,7 +215,16 @@ class VerifyStep:
         for keep_kv_len. w2_events = (start, end): medusa_step_timed records
         them around the vocabulary-projection kernel."""
         if w2_events is None:
-            L.step(self.shape, self.step_args(keep_kv_len), self.ws, stream=stream)
+            # the call's marshalled arguments, built once per variant (the
+            # stream is looked up each call: a graph capture changes it)
+            key = "_call_keep" if keep_kv_len else "_call"
+            call = getattr(self, key, None)
+            if call is None:
+                import ctypes
+                call = (ctypes.byref(self.shape), ctypes.byref(self.step_args(keep_kv_len)),
+                        self.ws.data_ptr(), self.ws.numel() * self.ws.element_size())
+                setattr(self, key, call)
+            L._check(L._lib.medusa_step(call[0], call[1], call[2], call[3], L._stream(stream)))
         else:
             L.step_timed(self.shape, self.step_args(keep_kv_len), self.ws, w2_events[0],
                          w2_events[1], stream=stream)
