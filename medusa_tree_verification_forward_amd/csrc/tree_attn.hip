@@ -360,6 +360,19 @@ __global__ __launch_bounds__(64 * kPfxWaves) void prefix_attn_bf16_kernel(AttnAr
 __device__ __forceinline__ int lane_chunks(const AttnArgs& a, int lane) {
   return lane < a.B ? attn_chunks(a.kv_len[lane], a.Lmax) : 0;
 }
+// Weight of one (b, h) segment's start (its Q loads, the first chunk's
+// exposed load latency, the closing exchange and partial store) in the
+// balanced split, in half chunks: a chunk weighs 2. Measured on the batch of
+// 8 (7B): a segment costs about one and a half chunks.
+#ifndef MEDUSA_PROBE
+constexpr int kSegWeight = 3;
+#else
+constexpr int kSegWeight = MEDUSA_PROBE;
+#endif
+// Weight of sequence b's H segments of nch chunks (none without chunks).
+__device__ __forceinline__ int seq_weight(int H, int nch) {
+  return nch > 0 ? H * (kSegWeight + 2 * nch) : 0;
+}
 __device__ __forceinline__ int wave_sum_int(int v) {
 #pragma unroll
   for (int off = 1; off < 64; off <<= 1) v += __shfl_xor(v, off);
@@ -632,30 +645,38 @@ __global__ __launch_bounds__(64 * kPfxWaves) void prefix_attn_wave_kernel(AttnAr
     if (s * kAttnChunk >= min(max(a.kv_len[b], 0), a.Lmax)) return;
     segment(b, h, s, G, 0x7fffffff, s);
   } else {
-    // balanced: each (b, h) the unit's range [pos, hi) meets (the C chunks
-    // in order: sequence b's H nch chunks start at pb)
-    // every sequence's chunk count at once, one a lane (the walk below
-    // reads them back with readlane)
+    // balanced: the (b, h) with chunks lie in order, each weighing
+    // kSegWeight + 2 nch, T in all; unit u takes the weights
+    // [u T / NWe, (u + 1) T / NWe) and each chunk whose last weight falls in
+    // them (chunk j of a (b, h) at P: weight P + kSegWeight + 2 j + 1), so
+    // that every unit carries about the same chunks plus segment starts.
+    // Every sequence's chunk count at once, one a lane (the walk below
+    // reads them back with readlane).
     const int nl = lane_chunks(a, (int)threadIdx.x & 63);
     const int C = H * __builtin_amdgcn_readfirstlane(wave_sum_int(nl));
+    const int Tw = __builtin_amdgcn_readfirstlane(wave_sum_int(seq_weight(H, nl)));
     const int NWe = min(G, C);
     if (unit >= NWe) return;
     // (divisions run on the vector ALUs: their uniform results are moved
     // back to scalar registers)
-    int pos = __builtin_amdgcn_readfirstlane((int)((long long)unit * C / NWe));
-    const int hi = __builtin_amdgcn_readfirstlane((int)((long long)(unit + 1) * C / NWe));
+    int x = __builtin_amdgcn_readfirstlane((int)((long long)unit * Tw / NWe));
+    const int hi = __builtin_amdgcn_readfirstlane((int)((long long)(unit + 1) * Tw / NWe));
     int b = 0, pb = 0, nch = __builtin_amdgcn_readlane(nl, 0);
-    while (pos < hi) {
-      while (pos >= pb + H * nch) {   // the sequence of chunk pos (pos < C)
-        pb += H * nch;
+    while (x < hi) {
+      while (x >= pb + seq_weight(H, nch)) {   // the sequence of weight x (x < Tw)
+        pb += seq_weight(H, nch);
         ++b;
         nch = __builtin_amdgcn_readlane(nl, b);
       }
-      const int h = __builtin_amdgcn_readfirstlane((pos - pb) / nch);
-      const int first = pos - pb - h * nch;
-      const int end = min(hi, pb + (h + 1) * nch);
-      segment(__builtin_amdgcn_readfirstlane(b), h, first, 1, first + (end - pos) - 1, first);
-      pos = end;
+      const int wh = kSegWeight + 2 * nch;
+      const int h = __builtin_amdgcn_readfirstlane((x - pb) / wh);
+      const int P = pb + h * wh;
+      const int off = x - P, e = min(hi - P, wh);
+      const int first = off > kSegWeight ? (off - kSegWeight) / 2 : 0;
+      const int last = e >= kSegWeight + 2 ? (e - kSegWeight - 2) / 2 : -1;
+      x = P + e;
+      if (last < first) continue;   // the range ends before this (b, h)'s first chunk
+      segment(__builtin_amdgcn_readfirstlane(b), h, first, 1, last, first);
       __syncthreads();   // the segment's exchange is read before the LDS is reused
     }
   }
@@ -833,28 +854,37 @@ __global__ __launch_bounds__(64) void attn_merge_kernel(AttnArgs a) {
   const int T = a.T, H = a.H;
   const int L = min(max(a.kv_len[b], 0), a.Lmax);
   // partials: one per prefix workgroup that had a chunk (strided units:
-  // slots 0 .. ns - 1). Balanced units: the ns units whose ranges meet this
-  // (b, h)'s chunks [cs, cs + nch) of the C in order, wa the first; unit
-  // wa + j left its partial at the slot of its first chunk here.
-  // (balanced: (NWe + 64) C < 2^32, which the launcher checks, so 32-bit
-  // unsigned products)
+  // slots 0 .. ns - 1). Balanced units: this (b, h) weighs kSegWeight + 2 nch
+  // from P of the Tw in order, its chunk j's last weight at
+  // P + kSegWeight + 2 j + 1; the unit whose range [u Tw / NWe,
+  // (u + 1) Tw / NWe) holds weight p is ceil((p + 1) NWe / Tw) - 1. The ns
+  // units from wa hold its chunks (each at least one, as a range spans at
+  // least two weights) and left their partials at the slot of their first
+  // chunk here. ((NWe + 64) Tw < 2^32, which the launcher checks, so 32-bit
+  // unsigned products.)
   const int nch = attn_chunks(L, a.Lmax);
   int ns = min(a.NP, nch);
-  unsigned wa = 0, NWe = 1, C = 1, cs = 0;
+  unsigned wa = 0, NWe = 1, Tw = 1, P = 0;
   if constexpr (BAL) {
     // every sequence's chunks at once, one a lane
     const int nl = lane_chunks(a, lane);
-    C = H * (unsigned)__builtin_amdgcn_readfirstlane(wave_sum_int(nl));
-    cs = H * (unsigned)__builtin_amdgcn_readfirstlane(wave_sum_int(lane < b ? nl : 0)) + h * nch;
+    const unsigned C = H * (unsigned)__builtin_amdgcn_readfirstlane(wave_sum_int(nl));
+    Tw = (unsigned)__builtin_amdgcn_readfirstlane(wave_sum_int(seq_weight(H, nl)));
+    P = (unsigned)__builtin_amdgcn_readfirstlane(wave_sum_int(lane < b ? seq_weight(H, nl) : 0)) +
+        h * (unsigned)(kSegWeight + 2 * nch);
     NWe = min((unsigned)a.chunk_sets, C);
     ns = 0;
     if (nch > 0) {
-      wa = ((cs + 1) * NWe + C - 1) / C - 1;
-      ns = (int)(((cs + nch) * NWe + C - 1) / C - wa);
+      wa = ((P + kSegWeight + 2) * NWe + Tw - 1) / Tw - 1;
+      ns = (int)(((P + kSegWeight + 2 * nch) * NWe + Tw - 1) / Tw - wa);
     }
   }
-  // (balanced: lane j computes partial j's slot once)
-  auto slot_of = [&](unsigned j) -> int { return (int)(max((wa + j) * C / NWe, cs) - cs); };
+  // (balanced: lane j computes partial j's slot once: the first chunk whose
+  // last weight is at or past the unit's range start)
+  auto slot_of = [&](unsigned j) -> int {
+    const unsigned lo = (wa + j) * Tw / NWe;
+    return lo <= P + kSegWeight ? 0 : (int)((lo - P - kSegWeight) / 2);
+  };
   const int slot_l = BAL ? slot_of(lane) : 0;
   auto slot = [&](int j) -> int {
     if constexpr (BAL)
@@ -1026,10 +1056,11 @@ hipError_t launch_bf16(const AttnArgs& a, hipStream_t st) {
       w.qgroups = 1;
       w.chunk_sets = G;
       w.balanced = 0;
-      if (a.B > 1 && (long long)(cus + 64) * a.B * a.H * a.NS < (1ll << 32)) {
+      if (a.B > 1 && (long long)(cus + 64) * a.B * a.H * (2 * a.NS + kSegWeight) < (1ll << 32)) {
         // several sequences: one balanced range of the chunks of every
         // (b, h) per compute unit, so that ragged prefixes leave no unit idle
-        // (batch of 8, 7B: 79.8 -> 70.6 us)
+        // (batch of 8, 7B: 79.8 -> 70.6 us; with segment starts weighed in,
+        // 67.7 -> 57.1 us)
         w.balanced = 1;
         w.chunk_sets = cus;
       }
