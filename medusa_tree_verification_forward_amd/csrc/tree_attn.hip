@@ -357,26 +357,26 @@ __global__ __launch_bounds__(64 * kPfxWaves) void prefix_attn_bf16_kernel(AttnAr
 
 // Prefix chunks of sequence `lane` (0 past B; B <= 64, one per lane) and
 // their sum over the wave, for the balanced split of the per-wave kernel.
+// (the load is clamped rather than branched around, so that it issues
+// beside the caller's other loads)
 __device__ __forceinline__ int lane_chunks(const AttnArgs& a, int lane) {
-  return lane < a.B ? attn_chunks(a.kv_len[lane], a.Lmax) : 0;
+  const int n = attn_chunks(a.kv_len[min(lane, a.B - 1)], a.Lmax);
+  return lane < a.B ? n : 0;
 }
 // Weight of one (b, h) segment's start (its Q loads, the first chunk's
 // exposed load latency, the closing exchange and partial store) in the
 // balanced split, in half chunks: a chunk weighs 2. Measured on the batch of
 // 8 (7B): a segment costs about one and a half chunks.
-#ifndef MEDUSA_PROBE
 constexpr int kSegWeight = 3;
-#else
-constexpr int kSegWeight = MEDUSA_PROBE;
-#endif
 // Weight of sequence b's H segments of nch chunks (none without chunks).
 __device__ __forceinline__ int seq_weight(int H, int nch) {
   return nch > 0 ? H * (kSegWeight + 2 * nch) : 0;
 }
+// Sum over the wave of non-negative integers whose total is below 2^24
+// (the launcher bounds the balanced weights far below that): every partial
+// sum is then exact in fp32, and the DPP row sums need no LDS round trips.
 __device__ __forceinline__ int wave_sum_int(int v) {
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) v += __shfl_xor(v, off);
-  return v;
+  return (int)wave_sum((float)v);
 }
 
 // Per-wave split-KV kernel for 128-wide heads, one group of at most three
@@ -845,14 +845,32 @@ __global__ __launch_bounds__(256) void prefix_attn_f32_kernel(AttnArgs a) {
 // prefixes, wide trees) follow the same pattern. Split indices past the last
 // are clamped and given zero weight.
 constexpr int kMergeBatch = 8;
+
 constexpr int kTreeBatch = 8;
-template <class ET, int DH, bool BAL>
-__global__ __launch_bounds__(64) void attn_merge_kernel(AttnArgs a) {
+template <class ET, int DH, bool BAL, int MW>
+__global__ __launch_bounds__(64 * MW) void attn_merge_kernel(AttnArgs a) {
   using S = typename ET::storage;
   constexpr int E = DH / 64;
-  const int i = blockIdx.x, h = blockIdx.y, b = blockIdx.z, lane = threadIdx.x;
+  // (the wave index through readfirstlane, so that the compiler knows i,
+  // and the early exit below, to be uniform)
+  const int i = blockIdx.x * MW + (MW > 1 ? __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6) : 0);
+  const int lane = threadIdx.x & 63;
+  const int h = blockIdx.y, b = blockIdx.z;
   const int T = a.T, H = a.H;
-  const int L = min(max(a.kv_len[b], 0), a.Lmax);
+  if (i >= T) return;   // wave-uniform; the kernel has no barriers
+  // the query row and the first mask window, loaded ahead of the split
+  // bookkeeping below (all three loads in flight together)
+  const S* __restrict__ qp = reinterpret_cast<const S*>(a.q) + (((size_t)b * T + i) * H + h) * DH;
+  const uint8_t* __restrict__ mrow = a.mask + (size_t)i * T;
+  float qv[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) qv[e] = ET::load1(qp + E * lane + e);
+  const bool allow0 = mrow[min(lane, T - 1)] != 0 && lane < T;
+  // every sequence's prefix length, one a lane (B <= 64), by a vector load
+  // that issues beside the query and mask loads above (a scalar load of
+  // kv_len[b] would be waited for before any of them)
+  const int kvl = a.kv_len[min(lane, a.B - 1)];
+  const int L = min(max(__builtin_amdgcn_readlane(kvl, b), 0), a.Lmax);
   // partials: one per prefix workgroup that had a chunk (strided units:
   // slots 0 .. ns - 1). Balanced units: this (b, h) weighs kSegWeight + 2 nch
   // from P of the Tw in order, its chunk j's last weight at
@@ -867,7 +885,7 @@ __global__ __launch_bounds__(64) void attn_merge_kernel(AttnArgs a) {
   unsigned wa = 0, NWe = 1, Tw = 1, P = 0;
   if constexpr (BAL) {
     // every sequence's chunks at once, one a lane
-    const int nl = lane_chunks(a, lane);
+    const int nl = lane < a.B ? attn_chunks(kvl, a.Lmax) : 0;
     const unsigned C = H * (unsigned)__builtin_amdgcn_readfirstlane(wave_sum_int(nl));
     Tw = (unsigned)__builtin_amdgcn_readfirstlane(wave_sum_int(seq_weight(H, nl)));
     P = (unsigned)__builtin_amdgcn_readfirstlane(wave_sum_int(lane < b ? seq_weight(H, nl) : 0)) +
@@ -896,8 +914,6 @@ __global__ __launch_bounds__(64) void attn_merge_kernel(AttnArgs a) {
   const size_t hs = ((size_t)b * H + h) * a.NS;   // split 0 of (b, h)
   // dh E lane + e of query i inside a split's [DT][T][16] block
   const size_t oin = ((size_t)(E * lane / 16) * T + i) * 16 + (E * lane) % 16;
-  const S* __restrict__ qp = reinterpret_cast<const S*>(a.q) + (((size_t)b * T + i) * H + h) * DH;
-  const uint8_t* __restrict__ mrow = a.mask + (size_t)i * T;
   const S* __restrict__ ktr = reinterpret_cast<const S*>(a.k_tree) + ((size_t)b * T * H + h) * DH;
   const S* __restrict__ vtr = reinterpret_cast<const S*>(a.v_tree) + ((size_t)b * T * H + h) * DH;
   const size_t krow = (size_t)H * DH;
@@ -936,10 +952,6 @@ __global__ __launch_bounds__(64) void attn_merge_kernel(AttnArgs a) {
     return nb;
   };
 
-  float qv[E];
-#pragma unroll
-  for (int e = 0; e < E; ++e) qv[e] = ET::load1(qp + E * lane + e);
-  const bool allow0 = lane < T && mrow[lane] != 0;
   if (ns > 0) load_splits(0);
   uint64_t bits = __ballot(allow0);
   int nb = bits ? take_tree(0, bits) : 0;
@@ -1000,6 +1012,19 @@ __global__ __launch_bounds__(64) void attn_merge_kernel(AttnArgs a) {
     if (a.out) a.out[out + e] = ov;
     if (a.out_elem) reinterpret_cast<S*>(a.out_elem)[out + e] = ET::from_float(ov);
   }
+}
+
+// The merge, MW queries (one a wave) a workgroup: four when it has under
+// eight waves a compute unit (7B tree, 1440 waves: 6.3 -> 5.5 us), else one
+// (13B tree and batch of 8, 5440 and 11520 waves: four measured 0.2-0.4 us
+// slower).
+template <class ET, int DH, bool BAL>
+void launch_merge(const AttnArgs& m, hipStream_t st) {
+  if ((long long)m.T * m.H * m.B < 8ll * device_cus())
+    hipLaunchKernelGGL((attn_merge_kernel<ET, DH, BAL, 4>), dim3((m.T + 3) / 4, m.H, m.B), dim3(256),
+                       0, st, m);
+  else
+    hipLaunchKernelGGL((attn_merge_kernel<ET, DH, BAL, 1>), dim3(m.T, m.H, m.B), dim3(64), 0, st, m);
 }
 
 constexpr int kHeldTiles = 9;   // query tiles whose Q rows the bf16 kernel can hold
@@ -1081,11 +1106,9 @@ hipError_t launch_bf16(const AttnArgs& a, hipStream_t st) {
       hipError_t e = hipGetLastError();
       if (e != hipSuccess) return e;
       if (w.balanced)
-        hipLaunchKernelGGL((attn_merge_kernel<BF16, DH, true>), dim3(a.T, a.H, a.B), dim3(64), 0,
-                           st, m);
+        launch_merge<BF16, DH, true>(m, st);
       else
-        hipLaunchKernelGGL((attn_merge_kernel<BF16, DH, false>), dim3(a.T, a.H, a.B), dim3(64), 0,
-                           st, m);
+        launch_merge<BF16, DH, false>(m, st);
       return hipGetLastError();
     }
     if (MQ > 3) {
@@ -1104,7 +1127,7 @@ hipError_t launch_bf16(const AttnArgs& a, hipStream_t st) {
       hipLaunchKernelGGL((prefix_attn_wave_kernel<3, false>), wgrid, block, 0, st, w);
       hipError_t e = hipGetLastError();
       if (e != hipSuccess) return e;
-      hipLaunchKernelGGL((attn_merge_kernel<BF16, DH, false>), dim3(a.T, a.H, a.B), dim3(64), 0, st, m);
+      launch_merge<BF16, DH, false>(m, st);
       return hipGetLastError();
     }
   }
@@ -1130,7 +1153,7 @@ hipError_t launch_bf16(const AttnArgs& a, hipStream_t st) {
     }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((attn_merge_kernel<BF16, DH, false>), dim3(a.T, a.H, a.B), dim3(64), 0, st, m);
+  launch_merge<BF16, DH, false>(m, st);
   return hipGetLastError();
 }
 
@@ -1151,7 +1174,7 @@ hipError_t launch_f32(const AttnArgs& a, hipStream_t st) {
   if (e != hipSuccess) return e;
   AttnArgs m = a;
   m.NP = a.NS;   // one partial per chunk
-  hipLaunchKernelGGL((attn_merge_kernel<F32, DH, false>), dim3(a.T, a.H, a.B), dim3(64), 0, st, m);
+  launch_merge<F32, DH, false>(m, st);
   return hipGetLastError();
 }
 
