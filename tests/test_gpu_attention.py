@@ -95,6 +95,10 @@ BALANCED = [
     # the largest batch a call takes (64 sequences, one chunk count a lane),
     # lengths spread over [0, Lmax] with empty and full prefixes among them
     ((3, 2, 2, 1, 1), 64, 4, [(37 * i * i + 11 * i) % 2101 for i in range(63)] + [2100], 2100),
+    # many short prefixes (one or two chunks a (sequence, head)) beside one
+    # long one: narrow ranges, many of which end inside a (sequence, head)'s
+    # start weight and leave its first chunk to the next range
+    ((3, 2, 2, 1, 1), 16, 32, [(53 * i * i + 29 * i) % 300 + 1 for i in range(15)] + [1300], 1300),
 ]
 
 
